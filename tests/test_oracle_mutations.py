@@ -1,0 +1,62 @@
+"""The oracle's pins catch plausible mistakes.
+
+Each case plants one mistake (a dropped term, a wrong sign, a transposed or
+swapped operand, the wrong tie rule or nibble order, a wrong rounding) in a
+temporary copy of ``oracle/`` and runs the pin tests against that copy; at
+least one pin must fail.  The repository's own files are never modified.
+"""
+import os
+import shutil
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+MUTATIONS = [
+    ("qlora.py", "Y = X @ W.T + s * (XA @ B.T)", "Y = X @ W.T - s * (XA @ B.T)"),
+    ("qlora.py", "dX = dY @ W + s * (T @ A)", "dX = dY @ W + (T @ A)"),
+    ("qlora.py", "dB = s * (dY.T @ XA)", "dB = s * (dY.T @ (X @ A[::-1].T))"),
+    ("qlora.py", "dA = s * (T.T @ X)", "dA = s * (T.T @ X[::-1])"),
+    ("qlora.py", "return sg * (1.0 + g * (1.0 - sg))", "return sg * (1.0 + g * (1.0 + sg))"),
+    ("qlora.py", "dG = dH * U * silu_grad(G)", "dG = dH * U * sigmoid(G)"),
+    ("qlora.py", "dU = dH * silu(G)", "dU = dH * sigmoid(G)"),
+    ("qlora.py", "return float(alpha) / float(r)", "return float(alpha) / float(r + 1)"),
+    ("nf4.py", 'side="left"', 'side="right"'),
+    ("nf4.py", "flat[0::2] | (flat[1::2] << np.uint8(4))", "flat[1::2] | (flat[0::2] << np.uint8(4))"),
+    ("nf4.py", "np.minimum(np.rint(ratio), 255.0)", "np.minimum(np.floor(ratio), 255.0)"),
+    ("nf4.py", "return (cb[:-1] + cb[1:]) / 2.0", "return (cb[:-1] + cb[1:]) / 2.0 + 1e-9"),
+    ("nf4.py", "S = np.float32(seg.max()) / np.float32(255.0)",
+     "S = np.float32(seg.max()) / np.float32(256.0)"),
+    ("nf4.py", "vals = cb[q].reshape(-1, bs) * a[:, None]",
+     "vals = cb[q].reshape(-1, bs) * a.mean()"),
+]
+
+
+@pytest.fixture(scope="module")
+def sandbox(tmp_path_factory):
+    d = tmp_path_factory.mktemp("oracle_mut")
+    shutil.copytree(os.path.join(ROOT, "synth"), d / "synth",
+                    ignore=shutil.ignore_patterns("*.tmp*", "__pycache__"))
+    os.makedirs(d / "tests" / "golden")
+    for f in ("conftest.py", "test_oracle_nf4.py", "test_oracle_qlora.py"):
+        shutil.copy(os.path.join(ROOT, "tests", f), d / "tests" / f)
+    shutil.copy(os.path.join(ROOT, "tests", "golden", "nf4_codebook.txt"),
+                d / "tests" / "golden" / "nf4_codebook.txt")
+    return d
+
+
+@pytest.mark.parametrize("fname,old,new", MUTATIONS, ids=[m[2][:40] for m in MUTATIONS])
+def test_pins_catch_mutation(sandbox, fname, old, new):
+    od = sandbox / "oracle"
+    if od.exists():
+        shutil.rmtree(od)
+    shutil.copytree(os.path.join(ROOT, "oracle"), od, ignore=shutil.ignore_patterns("__pycache__"))
+    src = (od / fname).read_text()
+    assert old in src
+    (od / fname).write_text(src.replace(old, new))
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        "tests/test_oracle_nf4.py", "tests/test_oracle_qlora.py"],
+                       cwd=str(sandbox), capture_output=True, text=True, timeout=300)
+    assert r.returncode == 1, "mutation survived: %s\n%s" % (new, r.stdout[-2000:])
