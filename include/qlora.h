@@ -1,0 +1,235 @@
+/*
+ * qlora.h - C ABI of the MI355X (gfx950) QLoRA linear / SwiGLU-MLP library.
+ *
+ * The layer: a frozen base weight W0 [N, K] stored as 4-bit NormalFloat
+ * (NF4) codes with per-block absmax scales, plus a trainable LoRA pair
+ * A [r, K], B [N, r] ("LLM Fine-Tuning in 2026: Unsloth vs QLoRA vs
+ * Liger-Kernel", section 1: h = W0 x + (alpha/r) B A x; FAQ: QLoRA keeps the
+ * base weight in 4-bit NormalFloat).  No dropout and no bias (section 5's
+ * adapter settings), so the ABI has neither.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Tokens are rows.  All matrices are row-major and contiguous.
+ *   bf16 tensors are passed as pointers to 16-bit bf16 bit patterns.
+ * - Every pointer argument that names a tensor is a DEVICE pointer (memory
+ *   of the current HIP device), except where stated.  The caller owns all
+ *   memory, including workspaces; the library never allocates, frees or
+ *   synchronises.  It keeps no state between calls and is re-entrant.
+ * - `stream` is a hipStream_t (NULL = the default stream).  All work is
+ *   enqueued on it in order; a call returns once the work is enqueued.
+ * - bf16 and fp32 tensor pointers must be 16-byte aligned.
+ * - Arguments are validated before anything is enqueued; a failed check
+ *   returns a negative status and enqueues nothing.  Device-side faults
+ *   surface on a later synchronisation and map to QLORA_ERR_HIP when a
+ *   launch itself reports an error.
+ * - Gradients are written (overwritten), never accumulated.
+ * - M (tokens) may be any value >= 0; M == 0 is a no-op that returns OK.
+ * - Shapes: K % 64 == 0 and N % 64 == 0 (whole absmax blocks, whole tiles
+ *   of 64), 1 <= r <= 128, blocksize == 64, dq_group in {0, 256}.
+ */
+#ifndef QLORA_H
+#define QLORA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QLORA_ABI_VERSION 1u
+
+/* Status codes. */
+#define QLORA_OK 0
+#define QLORA_ERR_INVALID_ARG (-1)         /* null pointer, negative size, bad enum, non-finite alpha */
+#define QLORA_ERR_UNSUPPORTED_SHAPE (-2)   /* K or N not a multiple of 64, r out of [1,128], ... */
+#define QLORA_ERR_MISALIGNED (-3)          /* a tensor pointer not 16-byte aligned */
+#define QLORA_ERR_WORKSPACE_TOO_SMALL (-4) /* ws_bytes below the matching *_workspace_bytes() */
+#define QLORA_ERR_UNSUPPORTED_DEVICE (-5)  /* current device is not gfx950 */
+#define QLORA_ERR_HIP (-6)                 /* a HIP runtime call or launch failed */
+
+/* Output element types of nf4_dequantize. */
+#define QLORA_DTYPE_BF16 0
+#define QLORA_DTYPE_F32 1
+
+/*
+ * An NF4-quantized frozen weight W0 [N, K] (QLoRA base weight; the pages name
+ * the format, its parameters are fixed here).
+ *
+ *   codes        u8 [N*K/2]: element e = n*K + k of the row-major weight has
+ *                its 4-bit code in byte e/2, bits 0-3 for even e, bits 4-7
+ *                for odd e.
+ *   blocksize    64: absmax block b covers elements [64b, 64b+64), i.e. 64
+ *                consecutive elements of one row.
+ *   dq_group 0   absmax       fp32 [N*K/64]: max |w| of each block.
+ *   dq_group 256 absmax_q     u8   [N*K/64]: 8-bit linear code of each absmax,
+ *                absmax_scale fp32 [ceil(N*K/64/256)]: one scale S per group
+ *                of 256 consecutive blocks; absmax' = fp32(code8 * S).
+ *   codebook     fp32 [16], device memory: strictly increasing, -1 and +1 at
+ *                the ends, exactly one 0.0 entry.
+ *
+ * Element value: fp32(codebook[code] * absmax'), absmax' = absmax when
+ * dq_group == 0.  Unused pointers (absmax or absmax_q/absmax_scale) may be
+ * NULL.
+ */
+typedef struct qlora_nf4 {
+  const uint8_t* codes;
+  const float* absmax;
+  const uint8_t* absmax_q;
+  const float* absmax_scale;
+  const float* codebook;
+  int64_t N;
+  int64_t K;
+  int32_t blocksize;
+  int32_t dq_group;
+} qlora_nf4;
+
+/*
+ * One QLoRA linear layer: Y = X W0^T + s (X A^T) B^T with s = alpha / r
+ * computed in fp32.  A bf16 [r, K], B bf16 [N, r] (orientation of B A x in
+ * "LLM Fine-Tuning in 2026", section 1).  W0.N, W0.K give N and K.
+ */
+typedef struct qlora_linear {
+  qlora_nf4 W0;
+  const void* A;
+  const void* B;
+  int32_t r;
+  float alpha;
+} qlora_linear;
+
+/*
+ * SwiGLU MLP block of three QLoRA linears: gate and up map D -> I, down maps
+ * I -> D.  Y = down(silu(gate(X)) * up(X)), silu(g) = g / (1 + e^-g)
+ * ("MLP SwiGLU" among the hand-derived kernels, "LLM Fine-Tuning in 2026",
+ * section 2).  gate and up must have the same r and alpha; down may differ.
+ */
+typedef struct qlora_mlp {
+  qlora_linear gate;
+  qlora_linear up;
+  qlora_linear down;
+} qlora_mlp;
+
+/*
+ * What the MLP forward saves for the backward.  Only the gate and up
+ * pre-activations are kept; sigma(G), silu(G) and H = silu(G) * U are
+ * recomputed in the backward ("What is Unsloth", "Recompute instead of store").
+ *   G, U   bf16 [M, I]   gate / up outputs
+ *   XA_g   fp32 [M, r_g] X A_g^T      XA_u  fp32 [M, r_u] X A_u^T
+ *   HA_d   fp32 [M, r_d] H A_d^T
+ */
+typedef struct qlora_mlp_saved {
+  void* G;
+  void* U;
+  float* XA_g;
+  float* XA_u;
+  float* HA_d;
+} qlora_mlp_saved;
+
+/* LoRA gradients of the MLP, bf16, shapes of the matching A / B. */
+typedef struct qlora_mlp_grads {
+  void* dA_g;
+  void* dB_g;
+  void* dA_u;
+  void* dB_u;
+  void* dA_d;
+  void* dB_d;
+} qlora_mlp_grads;
+
+/* ABI version of the loaded library (QLORA_ABI_VERSION it was built with). */
+uint32_t qlora_abi_version(void);
+
+/* Static message for a status code; never NULL. */
+const char* qlora_strerror(int status);
+
+/*
+ * nf4_quantize: blockwise-absmax NF4 quantization of W [N, K] fp32.
+ *
+ * Per block of 64: a = max |w|; if a == 0 every code is the index of the
+ * codebook's 0.0; otherwise q = the nearest codebook entry to the correctly
+ * rounded fp32 quotient w / a, ties to the lower index.  With dq_group == 256
+ * the absmax vector is then quantized in groups of 256 blocks (last group may
+ * be shorter): S = fp32(max / 255), code8 = min(255, round_half_even(fp32(a/S)))
+ * (0 if S == 0).  The 4-bit codes always use the exact absmax.
+ *
+ *   W            fp32 [N, K] device, input (finite values; others are
+ *                memory-safe but give unspecified codes)
+ *   codebook16   fp32 [16] device
+ *   blocksize    must be 64
+ *   dq_group     0 or 256
+ *   codes        u8 [N*K/2] device, output
+ *   absmax       fp32 [N*K/64] device, output when dq_group == 0 (else unused)
+ *   absmax_q     u8 [N*K/64] device, output when dq_group == 256
+ *   absmax_scale fp32 [ceil(N*K/64/256)] device, output when dq_group == 256
+ * Needs no workspace.  N == 0 is a no-op.
+ */
+int nf4_quantize(const float* W, int64_t N, int64_t K, const float* codebook16,
+                 int32_t blocksize, int32_t dq_group, uint8_t* codes, float* absmax,
+                 uint8_t* absmax_q, float* absmax_scale, void* stream);
+
+/*
+ * nf4_dequantize: writes every element fp32(codebook[q] * absmax') of w as
+ * out_dtype QLORA_DTYPE_BF16 (round to nearest even) or QLORA_DTYPE_F32,
+ * into out [N, K] (device).  Bit-exact with the definition above.
+ */
+int nf4_dequantize(const qlora_nf4* w, int32_t out_dtype, void* out, void* stream);
+
+/* Workspace bytes the linear forward and backward need for M tokens. */
+size_t qlora_linear_workspace_bytes(const qlora_linear* L, int64_t M);
+
+/*
+ * qlora_linear_fwd: Y = X W0^T + s XA B^T, XA = X A^T.
+ *   X        bf16 [M, K] input
+ *   Y        bf16 [M, N] output
+ *   XA_saved fp32 [M, r] output, kept by the caller for qlora_linear_bwd
+ *   ws       device workspace of ws_bytes >= qlora_linear_workspace_bytes(L, M)
+ * fp32 accumulation throughout; the dequantized weight enters the matrix
+ * cores as bf16(fp32(codebook[q] * absmax')).
+ */
+int qlora_linear_fwd(const qlora_linear* L, const void* X, int64_t M, void* Y,
+                     float* XA_saved, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * qlora_linear_bwd: gradients of <Y, dY> ("LLM Fine-Tuning in 2026",
+ * section 2: analytic gradients instead of autograd; W0 is frozen).
+ *   T  = dY B                      (fp32, in the workspace)
+ *   dX = dY W0 + s T A             bf16 [M, K] output
+ *   dA = s T^T X                   bf16 [r, K] output
+ *   dB = s dY^T XA_saved           bf16 [N, r] output
+ *   dY bf16 [M, N], X bf16 [M, K], XA_saved fp32 [M, r]: inputs.
+ * The reductions over M run in a fixed order, so results are bitwise
+ * reproducible from run to run.  With M == 0, dA and dB are set to zero.
+ */
+int qlora_linear_bwd(const qlora_linear* L, const void* dY, const void* X,
+                     const float* XA_saved, int64_t M, void* dX, void* dA, void* dB,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes the MLP forward and backward need for M tokens. */
+size_t qlora_mlp_workspace_bytes(const qlora_mlp* P, int64_t M);
+
+/*
+ * qlora_mlp_fwd: G = gate(X), U = up(X), H = silu(G) * U (transient, in the
+ * workspace), Y = down(H).
+ *   X bf16 [M, D] input;  Y bf16 [M, D] output;  S: saved tensors (outputs).
+ */
+int qlora_mlp_fwd(const qlora_mlp* P, const void* X, int64_t M, void* Y,
+                  const qlora_mlp_saved* S, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * qlora_mlp_bwd: gradients of <Y, dY> with sigma, silu and H recomputed from
+ * the saved G and U:
+ *   dH = dY Wd + s_d (dY Bd) Ad
+ *   dU = dH * silu(G),  dG = dH * U * sigma(G) (1 + G (1 - sigma(G)))
+ *   dX = dG Wg + s_g (dG Bg) Ag + dU Wu + s_u (dU Bu) Au      bf16 [M, D]
+ *   LoRA gradients of the three layers as in qlora_linear_bwd (G_out).
+ *   dG and dU live in the workspace.
+ */
+int qlora_mlp_bwd(const qlora_mlp* P, const void* dY, const void* X,
+                  const qlora_mlp_saved* S, int64_t M, void* dX, const qlora_mlp_grads* G_out,
+                  void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QLORA_H */

@@ -1,0 +1,312 @@
+"""Thin Python binding of libqlora.so (include/qlora.h) for MI355X / gfx950.
+
+Argument marshalling only: torch supplies device memory (``torch.empty``) and
+the current HIP stream; every step of the computation runs in the library's
+HIP kernels.  Each function carries the name of the C entry point it calls.
+If the compiled library is missing, importing the ABI raises immediately:
+there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqlora.so")
+
+QLORA_OK = 0
+QLORA_DTYPE_BF16 = 0
+QLORA_DTYPE_F32 = 1
+
+EXPORTED = (
+    "qlora_abi_version", "qlora_strerror", "nf4_quantize", "nf4_dequantize",
+    "qlora_linear_workspace_bytes", "qlora_linear_fwd", "qlora_linear_bwd",
+    "qlora_mlp_workspace_bytes", "qlora_mlp_fwd", "qlora_mlp_bwd",
+)
+
+
+class QloraError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__("%s failed: %d (%s)" % (fn, status, msg))
+        self.status = status
+
+
+# ------------------------------------------------------------------ C structs
+
+class CNf4(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("absmax", ctypes.c_void_p),
+                ("absmax_q", ctypes.c_void_p), ("absmax_scale", ctypes.c_void_p),
+                ("codebook", ctypes.c_void_p), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
+                ("blocksize", ctypes.c_int32), ("dq_group", ctypes.c_int32)]
+
+
+class CLinear(ctypes.Structure):
+    _fields_ = [("W0", CNf4), ("A", ctypes.c_void_p), ("B", ctypes.c_void_p),
+                ("r", ctypes.c_int32), ("alpha", ctypes.c_float)]
+
+
+class CMlp(ctypes.Structure):
+    _fields_ = [("gate", CLinear), ("up", CLinear), ("down", CLinear)]
+
+
+class CMlpSaved(ctypes.Structure):
+    _fields_ = [("G", ctypes.c_void_p), ("U", ctypes.c_void_p), ("XA_g", ctypes.c_void_p),
+                ("XA_u", ctypes.c_void_p), ("HA_d", ctypes.c_void_p)]
+
+
+class CMlpGrads(ctypes.Structure):
+    _fields_ = [("dA_g", ctypes.c_void_p), ("dB_g", ctypes.c_void_p), ("dA_u", ctypes.c_void_p),
+                ("dB_u", ctypes.c_void_p), ("dA_d", ctypes.c_void_p), ("dB_d", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libqlora.so and declare its signatures (no GPU needed)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError("libqlora.so not built (%s); run `python -m qlora_fine_tuning_linear_amd.build`"
+                           % path)
+    lib = ctypes.CDLL(path)
+    vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+    P = ctypes.POINTER
+    sig = {
+        "qlora_abi_version": (ctypes.c_uint32, []),
+        "qlora_strerror": (ctypes.c_char_p, [ctypes.c_int]),
+        "nf4_quantize": (ctypes.c_int, [vp, i64, i64, vp, i32, i32, vp, vp, vp, vp, vp]),
+        "nf4_dequantize": (ctypes.c_int, [P(CNf4), i32, vp, vp]),
+        "qlora_linear_workspace_bytes": (sz, [P(CLinear), i64]),
+        "qlora_linear_fwd": (ctypes.c_int, [P(CLinear), vp, i64, vp, vp, vp, sz, vp]),
+        "qlora_linear_bwd": (ctypes.c_int, [P(CLinear), vp, vp, vp, i64, vp, vp, vp, vp, sz, vp]),
+        "qlora_mlp_workspace_bytes": (sz, [P(CMlp), i64]),
+        "qlora_mlp_fwd": (ctypes.c_int, [P(CMlp), vp, i64, vp, P(CMlpSaved), vp, sz, vp]),
+        "qlora_mlp_bwd": (ctypes.c_int, [P(CMlp), vp, vp, P(CMlpSaved), i64, vp, P(CMlpGrads), vp, sz,
+                                         vp]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(fn: str, st: int):
+    if st != QLORA_OK:
+        raise QloraError(fn, st, load_library().qlora_strerror(st).decode())
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device=None) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _need(t: torch.Tensor, dtype, shape, name):
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if t.dtype != dtype or tuple(t.shape) != tuple(shape) or not t.is_contiguous():
+        raise ValueError("%s: expected contiguous %s %s, got %s %s" % (name, dtype, tuple(shape), t.dtype,
+                                                                     tuple(t.shape)))
+
+
+# ------------------------------------------------------------------ NF4 weight
+
+@dataclass
+class Nf4Weight:
+    codes: torch.Tensor                 # uint8 [N*K/2]
+    absmax: Optional[torch.Tensor]      # fp32 [N*K/64]         (dq_group == 0)
+    absmax_q: Optional[torch.Tensor]    # uint8 [N*K/64]        (dq_group == 256)
+    absmax_scale: Optional[torch.Tensor]  # fp32 [ceil(nb/256)] (dq_group == 256)
+    codebook: torch.Tensor              # fp32 [16]
+    N: int
+    K: int
+    dq_group: int = 0
+    blocksize: int = 64
+
+    def c(self) -> CNf4:
+        return CNf4(_ptr(self.codes), _ptr(self.absmax), _ptr(self.absmax_q), _ptr(self.absmax_scale),
+                    _ptr(self.codebook), self.N, self.K, self.blocksize, self.dq_group)
+
+
+def nf4_quantize(W: torch.Tensor, codebook: torch.Tensor, dq_group: int = 0, blocksize: int = 64) -> Nf4Weight:
+    """nf4_quantize: fp32 [N, K] device weight -> NF4 codes + absmax (or DQ absmax)."""
+    lib = load_library()
+    N, K = W.shape
+    _need(W, torch.float32, (N, K), "W")
+    _need(codebook, torch.float32, (16,), "codebook")
+    dev = W.device
+    nb = N * K // blocksize
+    codes = torch.empty(N * K // 2, dtype=torch.uint8, device=dev)
+    absmax = absmax_q = scale = None
+    if dq_group:
+        absmax_q = torch.empty(nb, dtype=torch.uint8, device=dev)
+        scale = torch.empty(-(-nb // dq_group), dtype=torch.float32, device=dev)
+    else:
+        absmax = torch.empty(nb, dtype=torch.float32, device=dev)
+    st = lib.nf4_quantize(W.data_ptr(), N, K, codebook.data_ptr(), blocksize, dq_group, codes.data_ptr(),
+                          _ptr(absmax), _ptr(absmax_q), _ptr(scale), _stream(dev))
+    _check("nf4_quantize", st)
+    return Nf4Weight(codes, absmax, absmax_q, scale, codebook, N, K, dq_group, blocksize)
+
+
+def nf4_dequantize(w: Nf4Weight, dtype: torch.dtype = torch.bfloat16, out: Optional[torch.Tensor] = None):
+    """nf4_dequantize: NF4 weight -> bf16 or fp32 [N, K]."""
+    lib = load_library()
+    if out is None:
+        out = torch.empty(w.N, w.K, dtype=dtype, device=w.codes.device)
+    code = QLORA_DTYPE_F32 if out.dtype == torch.float32 else QLORA_DTYPE_BF16
+    cw = w.c()
+    _check("nf4_dequantize", lib.nf4_dequantize(ctypes.byref(cw), code, out.data_ptr(), _stream(out.device)))
+    return out
+
+
+# ------------------------------------------------------------------ linear
+
+@dataclass
+class QLoraLinear:
+    W0: Nf4Weight
+    A: torch.Tensor   # bf16 [r, K]
+    B: torch.Tensor   # bf16 [N, r]
+    alpha: float
+
+    @property
+    def r(self) -> int:
+        return int(self.A.shape[0])
+
+    def c(self) -> CLinear:
+        return CLinear(self.W0.c(), self.A.data_ptr(), self.B.data_ptr(), self.r, float(self.alpha))
+
+
+def qlora_linear_workspace_bytes(L: QLoraLinear, M: int) -> int:
+    cl = L.c()
+    return int(load_library().qlora_linear_workspace_bytes(ctypes.byref(cl), M))
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def qlora_linear_fwd(L: QLoraLinear, X: torch.Tensor, Y=None, XA=None, ws=None):
+    """qlora_linear_fwd: returns (Y bf16 [M, N], XA fp32 [M, r])."""
+    lib = load_library()
+    M = X.shape[0]
+    dev = X.device
+    _need(X, torch.bfloat16, (M, L.W0.K), "X")
+    Y = torch.empty(M, L.W0.N, dtype=torch.bfloat16, device=dev) if Y is None else Y
+    XA = torch.empty(M, L.r, dtype=torch.float32, device=dev) if XA is None else XA
+    ws = _workspace(qlora_linear_workspace_bytes(L, M), dev) if ws is None else ws
+    cl = L.c()
+    st = lib.qlora_linear_fwd(ctypes.byref(cl), X.data_ptr(), M, Y.data_ptr(), XA.data_ptr(), ws.data_ptr(),
+                              ws.numel(), _stream(dev))
+    _check("qlora_linear_fwd", st)
+    return Y, XA
+
+
+def qlora_linear_bwd(L: QLoraLinear, dY: torch.Tensor, X: torch.Tensor, XA: torch.Tensor, dX=None, dA=None,
+                     dB=None, ws=None):
+    """qlora_linear_bwd: returns (dX bf16 [M, K], dA bf16 [r, K], dB bf16 [N, r])."""
+    lib = load_library()
+    M = X.shape[0]
+    dev = X.device
+    _need(dY, torch.bfloat16, (M, L.W0.N), "dY")
+    dX = torch.empty(M, L.W0.K, dtype=torch.bfloat16, device=dev) if dX is None else dX
+    dA = torch.empty_like(L.A) if dA is None else dA
+    dB = torch.empty_like(L.B) if dB is None else dB
+    ws = _workspace(qlora_linear_workspace_bytes(L, M), dev) if ws is None else ws
+    cl = L.c()
+    st = lib.qlora_linear_bwd(ctypes.byref(cl), dY.data_ptr(), X.data_ptr(), XA.data_ptr(), M, dX.data_ptr(),
+                              dA.data_ptr(), dB.data_ptr(), ws.data_ptr(), ws.numel(), _stream(dev))
+    _check("qlora_linear_bwd", st)
+    return dX, dA, dB
+
+
+# ------------------------------------------------------------------ MLP
+
+@dataclass
+class QLoraMlp:
+    gate: QLoraLinear
+    up: QLoraLinear
+    down: QLoraLinear
+
+    def c(self) -> CMlp:
+        return CMlp(self.gate.c(), self.up.c(), self.down.c())
+
+    @property
+    def D(self) -> int:
+        return self.gate.W0.K
+
+    @property
+    def I(self) -> int:  # noqa: E743
+        return self.gate.W0.N
+
+
+@dataclass
+class MlpSaved:
+    G: torch.Tensor
+    U: torch.Tensor
+    XA_g: torch.Tensor
+    XA_u: torch.Tensor
+    HA_d: torch.Tensor
+
+    def c(self) -> CMlpSaved:
+        return CMlpSaved(self.G.data_ptr(), self.U.data_ptr(), self.XA_g.data_ptr(), self.XA_u.data_ptr(),
+                         self.HA_d.data_ptr())
+
+
+def qlora_mlp_workspace_bytes(P: QLoraMlp, M: int) -> int:
+    cm = P.c()
+    return int(load_library().qlora_mlp_workspace_bytes(ctypes.byref(cm), M))
+
+
+def alloc_mlp_saved(P: QLoraMlp, M: int, device) -> MlpSaved:
+    f32, bf = torch.float32, torch.bfloat16
+    return MlpSaved(torch.empty(M, P.I, dtype=bf, device=device), torch.empty(M, P.I, dtype=bf, device=device),
+                    torch.empty(M, P.gate.r, dtype=f32, device=device),
+                    torch.empty(M, P.up.r, dtype=f32, device=device),
+                    torch.empty(M, P.down.r, dtype=f32, device=device))
+
+
+def qlora_mlp_fwd(P: QLoraMlp, X: torch.Tensor, Y=None, saved: Optional[MlpSaved] = None, ws=None):
+    """qlora_mlp_fwd: returns (Y bf16 [M, D], MlpSaved)."""
+    lib = load_library()
+    M = X.shape[0]
+    dev = X.device
+    _need(X, torch.bfloat16, (M, P.D), "X")
+    Y = torch.empty(M, P.D, dtype=torch.bfloat16, device=dev) if Y is None else Y
+    saved = alloc_mlp_saved(P, M, dev) if saved is None else saved
+    ws = _workspace(qlora_mlp_workspace_bytes(P, M), dev) if ws is None else ws
+    cm, cs = P.c(), saved.c()
+    st = lib.qlora_mlp_fwd(ctypes.byref(cm), X.data_ptr(), M, Y.data_ptr(), ctypes.byref(cs), ws.data_ptr(),
+                           ws.numel(), _stream(dev))
+    _check("qlora_mlp_fwd", st)
+    return Y, saved
+
+
+def qlora_mlp_bwd(P: QLoraMlp, dY: torch.Tensor, X: torch.Tensor, saved: MlpSaved, dX=None, grads=None, ws=None):
+    """qlora_mlp_bwd: returns (dX bf16 [M, D], dict of the six LoRA gradients)."""
+    lib = load_library()
+    M = X.shape[0]
+    dev = X.device
+    _need(dY, torch.bfloat16, (M, P.D), "dY")
+    dX = torch.empty(M, P.D, dtype=torch.bfloat16, device=dev) if dX is None else dX
+    if grads is None:
+        grads = dict(dA_g=torch.empty_like(P.gate.A), dB_g=torch.empty_like(P.gate.B),
+                     dA_u=torch.empty_like(P.up.A), dB_u=torch.empty_like(P.up.B),
+                     dA_d=torch.empty_like(P.down.A), dB_d=torch.empty_like(P.down.B))
+    ws = _workspace(qlora_mlp_workspace_bytes(P, M), dev) if ws is None else ws
+    cm, cs = P.c(), saved.c()
+    cg = CMlpGrads(*[grads[k].data_ptr() for k in ("dA_g", "dB_g", "dA_u", "dB_u", "dA_d", "dB_d")])
+    st = lib.qlora_mlp_bwd(ctypes.byref(cm), dY.data_ptr(), X.data_ptr(), ctypes.byref(cs), M, dX.data_ptr(),
+                           ctypes.byref(cg), ws.data_ptr(), ws.numel(), _stream(dev))
+    _check("qlora_mlp_bwd", st)
+    return dX, grads

@@ -1,0 +1,60 @@
+"""Builds libqlora.so (HIP for gfx950) in-tree with hipcc.
+
+    python -m qlora_fine_tuning_linear_amd.build
+
+Flags: -O3, no fast-math and no denormal flushing (the NF4 encoder relies on
+IEEE fp32 division and subnormals), packed-fp32 instruction forms disabled.
+The argument-validation unit is plain C++ compiled by the host compiler.
+"""
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(HERE, "libqlora.so")
+ARCH = "gfx950"
+
+HIP_FLAGS = [
+    "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
+    "-fno-gpu-flush-denormals-to-zero", "-fno-fast-math",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-I" + INCLUDE, "-I" + CSRC, "-Wall", "-Wno-unused-result",
+]
+
+
+def build(verbose: bool = False) -> str:
+    bdir = os.path.join(HERE, "_build")
+    os.makedirs(bdir, exist_ok=True)
+    objs = []
+    for src in ("qlora_kernels.hip", "qlora_api.hip"):
+        obj = os.path.join(bdir, src + ".o")
+        cmd = ["hipcc", "-c"] + HIP_FLAGS + [os.path.join(CSRC, src), "-o", obj]
+        _run(cmd, verbose)
+        objs.append(obj)
+    vobj = os.path.join(bdir, "qlora_validate.o")
+    _run(["g++", "-c", "-O2", "-std=c++17", "-fPIC", "-Wall", "-I" + INCLUDE, "-I" + CSRC,
+          os.path.join(CSRC, "qlora_validate.cpp"), "-o", vobj], verbose)
+    objs.append(vobj)
+    tmp = LIB + ".tmp%d" % os.getpid()
+    _run(["hipcc", "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs, verbose)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    noise = "is not a recognized feature for this target"
+    err = "\n".join(l for l in (r.stderr or "").splitlines() if noise not in l)
+    if r.returncode != 0:
+        raise RuntimeError("build step failed: %s\n%s" % (" ".join(cmd), err))
+    if verbose and err.strip():
+        print(err, file=sys.stderr)
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,311 @@
+// C ABI entry points (include/qlora.h): validate, then enqueue the kernels of
+// one pass on the caller's stream.  No allocation, no synchronisation.
+#include <hip/hip_runtime.h>
+#include <string.h>
+
+#include <atomic>
+
+#include "qlora.h"
+#include "qlora_launch.h"
+#include "qlora_plan.h"
+#include "qlora_validate.h"
+
+namespace {
+
+// Per-device answer to "is this a gfx950": 0 unknown, 1 yes, 2 no.
+std::atomic<int> g_dev_ok[64];
+
+int check_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return QLORA_ERR_HIP;
+  if (dev < 0 || dev >= 64) return QLORA_ERR_UNSUPPORTED_DEVICE;
+  int s = g_dev_ok[dev].load(std::memory_order_relaxed);
+  if (s == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return QLORA_ERR_HIP;
+    s = (strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    g_dev_ok[dev].store(s, std::memory_order_relaxed);
+  }
+  return s == 1 ? QLORA_OK : QLORA_ERR_UNSUPPORTED_DEVICE;
+}
+
+inline int hip_status(hipError_t e) { return e == hipSuccess ? QLORA_OK : QLORA_ERR_HIP; }
+
+Nf4Dev to_dev(const qlora_nf4& w) {
+  Nf4Dev d;
+  d.codes = w.codes;
+  d.absmax = w.absmax;
+  d.absmax_q = w.absmax_q;
+  d.absmax_scale = w.absmax_scale;
+  d.N = w.N;
+  d.K = w.K;
+  d.dq = w.dq_group;
+  return d;
+}
+
+float lora_s(const qlora_linear& L) { return L.alpha / (float)L.r; }
+
+// LoRA term with the B [N, r] matrix (forward side).
+LoraSide side_B(const qlora_linear& L, const float* V) {
+  return LoraSide{V, static_cast<const uint16_t*>(L.B), (int64_t)L.r, 1, L.r, lora_s(L)};
+}
+// LoRA term with the A [r, K] matrix (backward side).
+LoraSide side_A(const qlora_linear& L, const float* V) {
+  return LoraSide{V, static_cast<const uint16_t*>(L.A), 1, L.W0.K, L.r, lora_s(L)};
+}
+
+GemmArgs gemm_args() {
+  GemmArgs a;
+  memset(&a, 0, sizeof(a));
+  return a;
+}
+
+#define QTRY(expr)                  \
+  do {                              \
+    const int _st = (expr);         \
+    if (_st != QLORA_OK) return _st; \
+  } while (0)
+#define QHIP(expr) QTRY(hip_status(expr))
+
+const uint16_t* u16(const void* p) { return static_cast<const uint16_t*>(p); }
+uint16_t* u16m(void* p) { return static_cast<uint16_t*>(p); }
+char* bytes(void* p) { return static_cast<char*>(p); }
+
+}  // namespace
+
+extern "C" {
+
+int nf4_quantize(const float* W, int64_t N, int64_t K, const float* codebook16, int32_t blocksize, int32_t dq_group,
+                 uint8_t* codes, float* absmax, uint8_t* absmax_q, float* absmax_scale, void* stream) {
+  QTRY(qv_quantize(W, N, K, codebook16, blocksize, dq_group, codes, absmax, absmax_q, absmax_scale));
+  if (N == 0 || K == 0) return QLORA_OK;
+  QTRY(check_device());
+  return hip_status(launch_nf4_quantize(W, N * K / 64, codebook16, dq_group, codes, absmax, absmax_q, absmax_scale,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+int nf4_dequantize(const qlora_nf4* w, int32_t out_dtype, void* out, void* stream) {
+  QTRY(qv_dequantize(w, out_dtype, out));
+  QTRY(check_device());
+  return hip_status(launch_nf4_dequantize(to_dev(*w), w->codebook, out_dtype == QLORA_DTYPE_F32 ? 1 : 0, out,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+int qlora_linear_fwd(const qlora_linear* L, const void* X, int64_t M, void* Y, float* XA_saved, void* ws,
+                     size_t ws_bytes, void* stream) {
+  QTRY(qv_linear_fwd(L, X, M, Y, XA_saved, ws, ws_bytes));
+  if (M == 0) return QLORA_OK;
+  QTRY(check_device());
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t N = L->W0.N, K = L->W0.K;
+  const qplan::LinearWs w = qplan::linear_ws(M, N, K, L->r);
+  float* part = reinterpret_cast<float*>(bytes(ws));
+  float* down_part = reinterpret_cast<float*>(bytes(ws) + w.fwd_part);
+
+  // XA = X A^T (kept for the backward)
+  QHIP(launch_lora_down(true, u16(X), M, K, u16(L->A), L->r, nullptr, 0, XA_saved, nullptr,
+                        qplan::plan_down_splits(M, K), down_part, st));
+  // Y = X W0^T + s XA B^T
+  const qplan::GemmPlan pl = qplan::plan_gemm(M, N, K, true);
+  GemmArgs a = gemm_args();
+  a.act0 = u16(X);
+  a.M = M;
+  a.Nout = N;
+  a.Kred0 = K;
+  a.w0 = to_dev(L->W0);
+  a.codebook = L->W0.codebook;
+  a.l0 = side_B(*L, XA_saved);
+  a.out0 = u16m(Y);
+  a.partial = part;
+  QHIP(launch_qgemm(MODE_FWD, a, pl, st));
+  if (pl.splits > 1) QHIP(launch_splitk_finish(part, pl.splits, M, N, a.l0, u16m(Y), st));
+  return QLORA_OK;
+}
+
+int qlora_linear_bwd(const qlora_linear* L, const void* dY, const void* X, const float* XA_saved, int64_t M, void* dX,
+                     void* dA, void* dB, void* ws, size_t ws_bytes, void* stream) {
+  QTRY(qv_linear_bwd(L, dY, X, XA_saved, M, dX, dA, dB, ws, ws_bytes));
+  QTRY(check_device());
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t N = L->W0.N, K = L->W0.K;
+  const int r = L->r;
+  const float s = lora_s(*L);
+  if (M == 0) {
+    QHIP(launch_lora_grad(0, nullptr, nullptr, 0, N, nullptr, r, s, 1, nullptr, 0, u16m(dB), st));
+    QHIP(launch_lora_grad(0, nullptr, nullptr, 0, K, nullptr, r, s, 1, nullptr, 1, u16m(dA), st));
+    return QLORA_OK;
+  }
+  const qplan::LinearWs w = qplan::linear_ws(M, N, K, r);
+  char* base = bytes(ws);
+  float* T = reinterpret_cast<float*>(base);
+  float* part = reinterpret_cast<float*>(base + w.bwd_T);
+  float* down_part = reinterpret_cast<float*>(base + w.bwd_T + w.bwd_part);
+  float* grad_part = reinterpret_cast<float*>(base + w.bwd_T + w.bwd_part + w.bwd_down);
+
+  // T = dY B
+  QHIP(launch_lora_down(false, u16(dY), M, N, u16(L->B), r, nullptr, 0, T, nullptr, qplan::plan_down_splits(M, N),
+                        down_part, st));
+  // dX = dY W0 + s T A
+  const qplan::GemmPlan pl = qplan::plan_gemm(M, K, N, true);
+  GemmArgs a = gemm_args();
+  a.act0 = u16(dY);
+  a.M = M;
+  a.Nout = K;
+  a.Kred0 = N;
+  a.w0 = to_dev(L->W0);
+  a.codebook = L->W0.codebook;
+  a.l0 = side_A(*L, T);
+  a.out0 = u16m(dX);
+  a.partial = part;
+  QHIP(launch_qgemm(MODE_BWD, a, pl, st));
+  if (pl.splits > 1) QHIP(launch_splitk_finish(part, pl.splits, M, K, a.l0, u16m(dX), st));
+  // dB = s dY^T XA  ([N, r]);  dA = s T^T X  ([r, K])
+  QHIP(launch_lora_grad(0, u16(dY), nullptr, M, N, XA_saved, r, s, qplan::plan_grad_msplits(M, N, r), grad_part, 0,
+                        u16m(dB), st));
+  QHIP(launch_lora_grad(0, u16(X), nullptr, M, K, T, r, s, qplan::plan_grad_msplits(M, K, r), grad_part, 1, u16m(dA),
+                        st));
+  return QLORA_OK;
+}
+
+int qlora_mlp_fwd(const qlora_mlp* P, const void* X, int64_t M, void* Y, const qlora_mlp_saved* S, void* ws,
+                  size_t ws_bytes, void* stream) {
+  QTRY(qv_mlp_fwd(P, X, M, Y, S, ws, ws_bytes));
+  if (M == 0) return QLORA_OK;
+  QTRY(check_device());
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t I = P->gate.W0.N, D = P->gate.W0.K;
+  const qplan::MlpWs w = qplan::mlp_ws(M, D, I, P->gate.r, P->up.r, P->down.r);
+  uint16_t* H = reinterpret_cast<uint16_t*>(bytes(ws));
+  float* down_part = reinterpret_cast<float*>(bytes(ws) + w.fwd_H);
+
+  // XA_g | XA_u in one pass over X
+  QHIP(launch_lora_down(true, u16(X), M, D, u16(P->gate.A), P->gate.r, u16(P->up.A), P->up.r, S->XA_g, S->XA_u,
+                        qplan::plan_down_splits(M, D), down_part, st));
+  // G, U = gate/up(X) and H = silu(G) * U in one dual GEMM
+  {
+    GemmArgs a = gemm_args();
+    a.act0 = u16(X);
+    a.M = M;
+    a.Nout = I;
+    a.Kred0 = D;
+    a.w0 = to_dev(P->gate.W0);
+    a.w1 = to_dev(P->up.W0);
+    a.codebook = P->gate.W0.codebook;
+    a.l0 = side_B(P->gate, S->XA_g);
+    a.l1 = side_B(P->up, S->XA_u);
+    a.out0 = u16m(S->G);
+    a.out1 = u16m(S->U);
+    a.out2 = H;
+    QHIP(launch_qgemm(MODE_FWD_SWIGLU, a, qplan::plan_gemm(M, I, D, false), st));
+  }
+  // HA_d = H A_d^T
+  QHIP(launch_lora_down(true, H, M, I, u16(P->down.A), P->down.r, nullptr, 0, S->HA_d, nullptr,
+                        qplan::plan_down_splits(M, I), down_part, st));
+  // Y = H W_d^T + s_d HA_d B_d^T
+  {
+    GemmArgs a = gemm_args();
+    a.act0 = H;
+    a.M = M;
+    a.Nout = D;
+    a.Kred0 = I;
+    a.w0 = to_dev(P->down.W0);
+    a.codebook = P->down.W0.codebook;
+    a.l0 = side_B(P->down, S->HA_d);
+    a.out0 = u16m(Y);
+    QHIP(launch_qgemm(MODE_FWD, a, qplan::plan_gemm(M, D, I, false), st));
+  }
+  return QLORA_OK;
+}
+
+int qlora_mlp_bwd(const qlora_mlp* P, const void* dY, const void* X, const qlora_mlp_saved* S, int64_t M, void* dX,
+                  const qlora_mlp_grads* G, void* ws, size_t ws_bytes, void* stream) {
+  QTRY(qv_mlp_bwd(P, dY, X, S, M, dX, G, ws, ws_bytes));
+  QTRY(check_device());
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t I = P->gate.W0.N, D = P->gate.W0.K;
+  const int rg = P->gate.r, ru = P->up.r, rd = P->down.r;
+  const float sg = lora_s(P->gate), su = lora_s(P->up), sd = lora_s(P->down);
+  if (M == 0) {
+    QHIP(launch_lora_grad(0, nullptr, nullptr, 0, D, nullptr, rd, sd, 1, nullptr, 0, u16m(G->dB_d), st));
+    QHIP(launch_lora_grad(0, nullptr, nullptr, 0, I, nullptr, rd, sd, 1, nullptr, 1, u16m(G->dA_d), st));
+    QHIP(launch_lora_grad(0, nullptr, nullptr, 0, I, nullptr, rg, sg, 1, nullptr, 0, u16m(G->dB_g), st));
+    QHIP(launch_lora_grad(0, nullptr, nullptr, 0, D, nullptr, rg, sg, 1, nullptr, 1, u16m(G->dA_g), st));
+    QHIP(launch_lora_grad(0, nullptr, nullptr, 0, I, nullptr, ru, su, 1, nullptr, 0, u16m(G->dB_u), st));
+    QHIP(launch_lora_grad(0, nullptr, nullptr, 0, D, nullptr, ru, su, 1, nullptr, 1, u16m(G->dA_u), st));
+    return QLORA_OK;
+  }
+  const qplan::MlpWs w = qplan::mlp_ws(M, D, I, rg, ru, rd);
+  char* b = bytes(ws);
+  float* Td = reinterpret_cast<float*>(b);
+  b += w.bwd_Td;
+  uint16_t* dG = reinterpret_cast<uint16_t*>(b);
+  b += w.bwd_dG;
+  uint16_t* dU = reinterpret_cast<uint16_t*>(b);
+  b += w.bwd_dU;
+  float* Tg = reinterpret_cast<float*>(b);
+  b += w.bwd_Tg;
+  float* Tu = reinterpret_cast<float*>(b);
+  b += w.bwd_Tu;
+  float* down_part = reinterpret_cast<float*>(b);
+  b += w.bwd_down;
+  float* grad_part = reinterpret_cast<float*>(b);
+
+  // Td = dY B_d
+  QHIP(launch_lora_down(false, u16(dY), M, D, u16(P->down.B), rd, nullptr, 0, Td, nullptr,
+                        qplan::plan_down_splits(M, D), down_part, st));
+  // dH = dY W_d + s_d Td A_d, with the SwiGLU backward in the epilogue -> dG, dU
+  {
+    GemmArgs a = gemm_args();
+    a.act0 = u16(dY);
+    a.M = M;
+    a.Nout = I;
+    a.Kred0 = D;
+    a.w0 = to_dev(P->down.W0);
+    a.codebook = P->down.W0.codebook;
+    a.l0 = side_A(P->down, Td);
+    a.in0 = u16(S->G);
+    a.in1 = u16(S->U);
+    a.out0 = dG;
+    a.out1 = dU;
+    QHIP(launch_qgemm(MODE_BWD_SWIGLU, a, qplan::plan_gemm(M, I, D, false), st));
+  }
+  // down-layer LoRA gradients: dB_d = s_d dY^T HA_d, dA_d = s_d Td^T H (H recomputed)
+  QHIP(launch_lora_grad(0, u16(dY), nullptr, M, D, S->HA_d, rd, sd, qplan::plan_grad_msplits(M, D, rd), grad_part, 0,
+                        u16m(G->dB_d), st));
+  QHIP(launch_lora_grad(1, u16(S->G), u16(S->U), M, I, Td, rd, sd, qplan::plan_grad_msplits(M, I, rd), grad_part, 1,
+                        u16m(G->dA_d), st));
+  // Tg = dG B_g, Tu = dU B_u
+  QHIP(launch_lora_down(false, dG, M, I, u16(P->gate.B), rg, nullptr, 0, Tg, nullptr, qplan::plan_down_splits(M, I),
+                        down_part, st));
+  QHIP(launch_lora_down(false, dU, M, I, u16(P->up.B), ru, nullptr, 0, Tu, nullptr, qplan::plan_down_splits(M, I),
+                        down_part, st));
+  // dX = dG W_g + dU W_u + s_g Tg A_g + s_u Tu A_u  (one GEMM, reduction over 2I)
+  {
+    GemmArgs a = gemm_args();
+    a.act0 = dG;
+    a.act1 = dU;
+    a.M = M;
+    a.Nout = D;
+    a.Kred0 = I;
+    a.Kred1 = I;
+    a.w0 = to_dev(P->gate.W0);
+    a.w1 = to_dev(P->up.W0);
+    a.codebook = P->gate.W0.codebook;
+    a.l0 = side_A(P->gate, Tg);
+    a.l1 = side_A(P->up, Tu);
+    a.out0 = u16m(dX);
+    QHIP(launch_qgemm(MODE_BWD_DUAL, a, qplan::plan_gemm(M, D, 2 * I, false), st));
+  }
+  // gate / up LoRA gradients
+  QHIP(launch_lora_grad(0, dG, nullptr, M, I, S->XA_g, rg, sg, qplan::plan_grad_msplits(M, I, rg), grad_part, 0,
+                        u16m(G->dB_g), st));
+  QHIP(launch_lora_grad(0, u16(X), nullptr, M, D, Tg, rg, sg, qplan::plan_grad_msplits(M, D, rg), grad_part, 1,
+                        u16m(G->dA_g), st));
+  QHIP(launch_lora_grad(0, dU, nullptr, M, I, S->XA_u, ru, su, qplan::plan_grad_msplits(M, I, ru), grad_part, 0,
+                        u16m(G->dB_u), st));
+  QHIP(launch_lora_grad(0, u16(X), nullptr, M, D, Tu, ru, su, qplan::plan_grad_msplits(M, D, ru), grad_part, 1,
+                        u16m(G->dA_u), st));
+  return QLORA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,851 @@
+// gfx950 (MI355X, CDNA4) kernels of the QLoRA linear / SwiGLU-MLP library.
+//
+// The method: a frozen NF4 base weight plus a trainable rank-r LoRA pair,
+// h = W0 x + (alpha/r) B A x ("LLM Fine-Tuning in 2026: Unsloth vs QLoRA vs
+// Liger-Kernel", section 1), with forward and backward written by hand
+// (section 2 of that page) and the SwiGLU activation recomputed in the
+// backward pass ("What is Unsloth", "Recompute instead of store").  The
+// kernel design below is this library's own, for CDNA4:
+//
+// * qgemm_kernel - the hot path.  A dequant-staged bf16 MFMA GEMM
+//   (v_mfma_f32_32x32x16_bf16, fp32 accumulation).  Per 64-wide reduction
+//   tile, all threads of the workgroup expand the NF4 codes of the weight
+//   tile (codebook lookup in LDS, times the block absmax, round to bf16) and
+//   write them into a double-buffered LDS tile; for the backward pass the
+//   tile is written transposed so that both passes read it the same way.
+//   Activations (X or dY) go from HBM straight into registers in MFMA operand
+//   layout.  The LoRA term is one more MFMA step on the same accumulators in
+//   the epilogue; SwiGLU (forward) and its analytic backward are epilogue
+//   variants, so G, U, H and dG, dU are produced without another pass.
+// * lora_down_kernel - V = Z A^T (and T = dY B), the skinny rank-r products.
+// * lora_grad_kernel - dB = s dY^T XA and dA = s T^T X: reductions over the
+//   tokens, with the token-major operand transposed in registers and fed to
+//   the matrix cores; fixed-order partial sums, so results are reproducible.
+// * nf4_quantize_kernel / nf4_dequantize_kernel - the bit-exact encoding.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "qlora_device.h"
+#include "qlora_launch.h"
+
+namespace qk {
+
+// ------------------------------------------------------------------------
+// NF4 quantization.  One workgroup per group of 256 consecutive absmax
+// blocks (64 elements each); thread t owns block t of the group.  With
+// double quantization the group is exactly one DQ group.
+// ------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void nf4_quantize_kernel(
+    const float* __restrict__ W, int64_t nblocks, const float* __restrict__ codebook, int dq,
+    uint8_t* __restrict__ codes, float* __restrict__ absmax, uint8_t* __restrict__ absmax_q,
+    float* __restrict__ absmax_scale) {
+  __shared__ double mids[15];
+  __shared__ int zidx;
+  __shared__ float wmax[4];
+  const int t = threadIdx.x;
+  if (t < 15) mids[t] = ((double)codebook[t] + (double)codebook[t + 1]) * 0.5;
+  if (t < 16 && codebook[t] == 0.0f) zidx = t;
+  __syncthreads();
+  const int64_t b = (int64_t)blockIdx.x * 256 + t;
+  const bool valid = b < nblocks;
+  float a = 0.0f;
+  f32x4 v[16];
+  if (valid) {
+    const f32x4* src = reinterpret_cast<const f32x4*>(W + b * 64);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = src[i];
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) a = fmaxf(a, fabsf(v[i][e]));
+    u32x4 out[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
+    const int z = zidx;
+#pragma unroll
+    for (int e = 0; e < 64; ++e) {
+      int q = z;
+      if (a != 0.0f) {
+        const float n = v[e >> 2][e & 3] / a;  // correctly rounded fp32 quotient
+        const double nd = (double)n;
+        q = 0;
+#pragma unroll
+        for (int j = 0; j < 15; ++j) q += (nd > mids[j]) ? 1 : 0;
+      }
+      out[e >> 5][(e & 31) >> 3] |= (uint32_t)q << (4 * (e & 7));
+    }
+    u32x4* dst = reinterpret_cast<u32x4*>(codes + b * 32);
+    dst[0] = out[0];
+    dst[1] = out[1];
+    if (!dq) absmax[b] = a;
+  }
+  if (dq) {
+    float g = a;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) g = fmaxf(g, __shfl_xor(g, off));
+    if ((t & 63) == 0) wmax[t >> 6] = g;
+    __syncthreads();
+    g = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+    const float S = g / 255.0f;
+    if (valid) {
+      uint32_t c8 = 0;
+      if (S != 0.0f) c8 = (uint32_t)fminf(255.0f, rintf(a / S));
+      absmax_q[b] = (uint8_t)c8;
+    }
+    if (t == 0) absmax_scale[blockIdx.x] = S;
+  }
+}
+
+__device__ __forceinline__ float block_absmax(const Nf4Dev& w, int64_t blk) {
+  if (w.dq) return (float)w.absmax_q[blk] * w.absmax_scale[blk / w.dq];
+  return w.absmax[blk];
+}
+
+// ------------------------------------------------------------------------
+// NF4 dequantization (export): 8 elements per thread.
+// ------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void nf4_dequantize_kernel(Nf4Dev w, const float* __restrict__ codebook,
+                                                             int64_t n_groups8, int out_f32, void* out) {
+  __shared__ float cb[16];
+  if (threadIdx.x < 16) cb[threadIdx.x] = codebook[threadIdx.x];
+  __syncthreads();
+  const int64_t i8 = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i8 >= n_groups8) return;
+  const uint32_t c = reinterpret_cast<const uint32_t*>(w.codes)[i8];
+  const float a = block_absmax(w, i8 >> 3);
+  float v[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = cb[(c >> (4 * e)) & 15u] * a;
+  if (out_f32) {
+    f32x4* o = reinterpret_cast<f32x4*>(static_cast<float*>(out) + i8 * 8);
+    o[0] = f32x4{v[0], v[1], v[2], v[3]};
+    o[1] = f32x4{v[4], v[5], v[6], v[7]};
+  } else {
+    u32x4 o;
+    o[0] = pack_bf16x2(v[0], v[1]);
+    o[1] = pack_bf16x2(v[2], v[3]);
+    o[2] = pack_bf16x2(v[4], v[5]);
+    o[3] = pack_bf16x2(v[6], v[7]);
+    reinterpret_cast<u32x4*>(static_cast<uint16_t*>(out) + i8 * 8)[0] = o;
+  }
+}
+
+// ------------------------------------------------------------------------
+// The dequant-staged MFMA GEMM.
+//
+// Output tile: BM tokens x BN output columns; WM x WN waves, each FM x FN
+// frags of 32 x 32.  The MFMA's "A" operand is the weight side (rows = output
+// columns, from LDS), its "B" operand the activations (columns = tokens, from
+// registers), so each lane ends up with 4 consecutive output columns of one
+// token per accumulator quad and stores them as one 8-byte write.
+//
+// LDS weight tile: [BN rows][64 reduction values] bf16, rows = output columns,
+// 16-byte chunks XOR-swizzled by swz(row); two buffers.
+// ------------------------------------------------------------------------
+template <int MODE>
+struct ModeTraits {
+  static constexpr bool trans = (MODE == MODE_BWD || MODE == MODE_BWD_SWIGLU || MODE == MODE_BWD_DUAL);
+  static constexpr bool swiglu_fwd = (MODE == MODE_FWD_SWIGLU);
+};
+
+template <int WM, int WN, int FM, int FN>
+struct TileCfg {
+  static constexpr int NT = WM * WN * 64;
+  static constexpr int BM = WM * FM * 32;
+  static constexpr int BN = WN * FN * 32;
+  static constexpr int EPT = 64 * BN / NT;  // forward fill: elements per thread
+  static constexpr int TPR = 64 / EPT;      // forward fill: threads per LDS row
+  static constexpr int RPT = 8 * BN / NT;   // transposed fill: weight rows per thread
+};
+
+// LDS row (= output column within the tile) of frag f of wave column wn.
+template <int MODE, int WN, int FN>
+__device__ __forceinline__ int frag_row(int wn, int f) {
+  if (ModeTraits<MODE>::swiglu_fwd) {
+    constexpr int H = FN / 2;
+    constexpr int BNH = WN * H * 32;
+    return (f < H) ? (wn * H + f) * 32 : BNH + (wn * H + (f - H)) * 32;
+  }
+  return (wn * FN + f) * 32;
+}
+
+// Forward (non-transposed) fill: LDS row r <- weight row; registers first.
+template <int EPT>
+struct FillFwd {
+  uint32_t c[EPT / 8];
+  float a;
+};
+
+// Transposed fill: LDS row (output column) <- 8 weight columns x RPT rows.
+template <int RPT>
+struct FillTr {
+  uint32_t c[RPT];
+  float a[RPT];
+};
+
+__device__ __forceinline__ u32x4 deq8(uint32_t c, float a, const float* cb) {
+  u32x4 o;
+  o[0] = pack_bf16x2(cb[c & 15u] * a, cb[(c >> 4) & 15u] * a);
+  o[1] = pack_bf16x2(cb[(c >> 8) & 15u] * a, cb[(c >> 12) & 15u] * a);
+  o[2] = pack_bf16x2(cb[(c >> 16) & 15u] * a, cb[(c >> 20) & 15u] * a);
+  o[3] = pack_bf16x2(cb[(c >> 24) & 15u] * a, cb[(c >> 28) & 15u] * a);
+  return o;
+}
+
+template <int MODE, int WM, int WN, int FM, int FN, bool SPLIT>
+__global__ __launch_bounds__(WM* WN * 64) void qgemm_kernel(GemmArgs p) {
+  using C = TileCfg<WM, WN, FM, FN>;
+  constexpr int NT = C::NT, BM = C::BM, BN = C::BN;
+  constexpr bool TR = ModeTraits<MODE>::trans;
+
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2][BN * 64];
+  __shared__ float cb[16];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  const int l32 = lane & 31, g = lane >> 5;
+
+  // output columns per tile: the SwiGLU forward stacks gate and up rows of the
+  // same BN/2 intermediate columns in one LDS tile
+  constexpr int BNO = ModeTraits<MODE>::swiglu_fwd ? BN / 2 : BN;
+  const int64_t tm = blockIdx.x % p.tiles_m;
+  const int64_t tn = blockIdx.x / p.tiles_m;
+  const int64_t m0 = tm * BM;
+  const int64_t n0 = tn * BNO;  // first output column (I-index for the SwiGLU forward)
+
+  const int KT0 = (int)(p.Kred0 / 64);
+  const int KT = KT0 + (int)(p.Kred1 / 64);
+  int kt_begin = 0, kt_end = KT;
+  if (SPLIT) {
+    kt_begin = blockIdx.y * p.ktiles_per_split;
+    kt_end = min(KT, kt_begin + p.ktiles_per_split);
+  }
+
+  if (tid < 16) cb[tid] = p.codebook[tid];
+
+  // ---- activation operand: rows of this lane, clamped into [0, M)
+  int64_t arow[FM];
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    int64_t r = m0 + (int64_t)(wm * FM + i) * 32 + l32;
+    arow[i] = r < p.M ? r : p.M - 1;
+  }
+  auto load_act = [&](int kt, u32x4 (&dst)[FM][4]) {
+    const uint16_t* act = p.act0;
+    int64_t lda = p.Kred0, kk = (int64_t)kt * 64;
+    if (kt >= KT0) {
+      act = p.act1;
+      lda = p.Kred1;
+      kk -= p.Kred0;
+    }
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        dst[i][s] = *reinterpret_cast<const u32x4*>(act + arow[i] * lda + kk + 16 * s + 8 * g);
+  };
+
+  // ---- weight tile fill
+  FillFwd<C::EPT> ff;
+  FillTr<C::RPT> ft;
+  auto fill_load = [&](int kt) {
+    if constexpr (!TR) {
+      const int r = tid / C::TPR, part = tid % C::TPR;
+      const Nf4Dev* w = &p.w0;
+      int64_t wrow = n0 + r;
+      if (ModeTraits<MODE>::swiglu_fwd && r >= BN / 2) {
+        w = &p.w1;
+        wrow = n0 + (r - BN / 2);
+      }
+      if (wrow >= w->N) wrow = w->N - 1;
+      const uint8_t* src = w->codes + wrow * (w->K / 2) + (int64_t)kt * 32 + part * (C::EPT / 2);
+      if constexpr (C::EPT == 64) {
+        u32x4 x0 = reinterpret_cast<const u32x4*>(src)[0], x1 = reinterpret_cast<const u32x4*>(src)[1];
+        ff.c[0] = x0[0]; ff.c[1] = x0[1]; ff.c[2] = x0[2]; ff.c[3] = x0[3];
+        ff.c[4] = x1[0]; ff.c[5] = x1[1]; ff.c[6] = x1[2]; ff.c[7] = x1[3];
+      } else if constexpr (C::EPT == 32) {
+        u32x4 x0 = reinterpret_cast<const u32x4*>(src)[0];
+        ff.c[0] = x0[0]; ff.c[1] = x0[1]; ff.c[2] = x0[2]; ff.c[3] = x0[3];
+      } else {
+        u32x2 x0 = reinterpret_cast<const u32x2*>(src)[0];
+        ff.c[0] = x0[0]; ff.c[1] = x0[1];
+      }
+      ff.a = block_absmax(*w, wrow * (w->K / 64) + kt);
+    } else {
+      constexpr int KC = BN / 8;
+      const int kc = tid % KC, rg = tid / KC;
+      const Nf4Dev* w = &p.w0;
+      int64_t nb = (int64_t)kt * 64;
+      if (kt >= KT0) {
+        w = &p.w1;
+        nb -= p.Kred0;
+      }
+      int64_t col = n0 + 8 * kc;
+      if (col > w->K - 8) col = w->K - 8;
+#pragma unroll
+      for (int i = 0; i < C::RPT; ++i) {
+        const int64_t wrow = nb + rg * C::RPT + i;
+        ft.c[i] = *reinterpret_cast<const uint32_t*>(w->codes + wrow * (w->K / 2) + col / 2);
+        ft.a[i] = block_absmax(*w, wrow * (w->K / 64) + col / 64);
+      }
+    }
+  };
+  auto fill_store = [&](uint16_t* buf) {
+    if constexpr (!TR) {
+      const int r = tid / C::TPR, part = tid % C::TPR;
+#pragma unroll
+      for (int d = 0; d < C::EPT / 8; ++d) {
+        const int chunk = part * (C::EPT / 8) + d;
+        const u32x4 v = deq8(ff.c[d], ff.a, cb);
+        *reinterpret_cast<u32x4*>(buf + r * 64 + ((chunk ^ swz(r)) * 8)) = v;
+      }
+    } else {
+      constexpr int KC = BN / 8;
+      constexpr int RPT = C::RPT;
+      const int kc = tid % KC, rg = tid / KC;
+      const int n_off = rg * RPT;
+      const int chunk = n_off >> 3, sub = n_off & 7;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        float v[RPT];
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) v[i] = cb[(ft.c[i] >> (4 * c)) & 15u] * ft.a[i];
+        const int row = 8 * kc + c;
+        uint16_t* dst = buf + row * 64 + ((chunk ^ swz(row)) * 8) + sub;
+        if constexpr (RPT == 8) {
+          u32x4 o{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                  pack_bf16x2(v[6], v[7])};
+          *reinterpret_cast<u32x4*>(dst) = o;
+        } else if constexpr (RPT == 4) {
+          u32x2 o{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+          *reinterpret_cast<u32x2*>(dst) = o;
+        } else {
+          *reinterpret_cast<uint32_t*>(dst) = pack_bf16x2(v[0], v[1]);
+        }
+      }
+    }
+  };
+
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int f = 0; f < FN; ++f)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][f][v] = 0.0f;
+
+  u32x4 actA[FM][4], actB[FM][4];
+  __syncthreads();  // codebook in LDS
+  if (kt_begin < kt_end) {
+    load_act(kt_begin, actA);
+    fill_load(kt_begin);
+    fill_store(lds[kt_begin & 1]);
+  }
+  __syncthreads();
+
+  for (int kt = kt_begin; kt < kt_end; ++kt) {
+    const bool more = kt + 1 < kt_end;
+    if (more) {
+      load_act(kt + 1, actB);
+      fill_load(kt + 1);
+    }
+    const uint16_t* buf = lds[kt & 1];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      u32x4 wa[FN];
+#pragma unroll
+      for (int f = 0; f < FN; ++f) {
+        const int row = frag_row<MODE, WN, FN>(wn, f) + l32;
+        wa[f] = *reinterpret_cast<const u32x4*>(buf + row * 64 + (((2 * s + g) ^ swz(row)) * 8));
+      }
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int f = 0; f < FN; ++f) acc[i][f] = mfma32(wa[f], actA[i][s], acc[i][f]);
+    }
+    if (more) fill_store(lds[(kt + 1) & 1]);
+    __syncthreads();
+    if (more) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) actA[i][s] = actB[i][s];
+    }
+  }
+
+  // ---- output column of lane-row l32 in frag f, and the LoRA side it uses
+  auto out_col = [&](int f) -> int64_t {
+    if (ModeTraits<MODE>::swiglu_fwd) {
+      constexpr int H = FN / 2;
+      return n0 + (int64_t)(wn * H + (f % H)) * 32;
+    }
+    return n0 + (int64_t)frag_row<MODE, WN, FN>(wn, f);
+  };
+
+  if constexpr (SPLIT) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int64_t m = m0 + (int64_t)(wm * FM + i) * 32 + l32;
+      if (m >= p.M) continue;
+#pragma unroll
+      for (int f = 0; f < FN; ++f) {
+        const int64_t cb0 = out_col(f);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int64_t n = cb0 + 8 * q + 4 * g;
+          if (n >= p.Nout) continue;
+          f32x4 o{acc[i][f][4 * q], acc[i][f][4 * q + 1], acc[i][f][4 * q + 2], acc[i][f][4 * q + 3]};
+          *reinterpret_cast<f32x4*>(p.partial + ((int64_t)blockIdx.y * p.M + m) * p.Nout + n) = o;
+        }
+      }
+    }
+    return;
+  } else {
+    // ---- LoRA epilogue: acc += s * V[m, :] Wl(col, :)^T as extra MFMA steps.
+    auto lora = [&](const LoraSide& L, int f_lo, int f_hi) {
+      const int steps = (L.r + 15) / 16;
+      for (int t = 0; t < steps; ++t) {
+        u32x4 vop[FM];
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+          float x[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int j = 16 * t + 8 * g + e;
+            x[e] = (j < L.r) ? L.s * L.V[arow[i] * L.r + j] : 0.0f;
+          }
+          vop[i] = u32x4{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
+                         pack_bf16x2(x[6], x[7])};
+        }
+#pragma unroll
+        for (int f = 0; f < FN; ++f) {
+          if (f < f_lo || f >= f_hi) continue;
+          int64_t c = out_col(f) + l32;
+          if (c >= p.Nout) c = p.Nout - 1;
+          uint32_t h[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int j = 16 * t + 8 * g + e;
+            h[e] = (j < L.r) ? (uint32_t)L.Wl[c * L.wl_sc + (int64_t)j * L.wl_sj] : 0u;
+          }
+          const u32x4 wop{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+#pragma unroll
+          for (int i = 0; i < FM; ++i) acc[i][f] = mfma32(wop, vop[i], acc[i][f]);
+        }
+      }
+    };
+    if constexpr (MODE == MODE_FWD_SWIGLU) {
+      lora(p.l0, 0, FN / 2);
+      lora(p.l1, FN / 2, FN);
+    } else if constexpr (MODE == MODE_BWD_DUAL) {
+      lora(p.l0, 0, FN);
+      lora(p.l1, 0, FN);
+    } else {
+      lora(p.l0, 0, FN);
+    }
+
+    // ---- stores
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int64_t m = m0 + (int64_t)(wm * FM + i) * 32 + l32;
+      if (m >= p.M) continue;
+      constexpr int FO = ModeTraits<MODE>::swiglu_fwd ? FN / 2 : FN;
+#pragma unroll
+      for (int f = 0; f < FO; ++f) {
+        const int64_t cb0 = out_col(f);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int64_t n = cb0 + 8 * q + 4 * g;
+          if (n >= p.Nout) continue;
+          const int64_t off = m * p.Nout + n;
+          if constexpr (MODE == MODE_FWD_SWIGLU) {
+            float G[4], U[4], H[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              G[e] = acc[i][f][4 * q + e];
+              U[e] = acc[i][f + FN / 2][4 * q + e];
+              H[e] = G[e] * sigmoidf_(G[e]) * U[e];
+            }
+            *reinterpret_cast<u32x2*>(p.out0 + off) = u32x2{pack_bf16x2(G[0], G[1]), pack_bf16x2(G[2], G[3])};
+            *reinterpret_cast<u32x2*>(p.out1 + off) = u32x2{pack_bf16x2(U[0], U[1]), pack_bf16x2(U[2], U[3])};
+            *reinterpret_cast<u32x2*>(p.out2 + off) = u32x2{pack_bf16x2(H[0], H[1]), pack_bf16x2(H[2], H[3])};
+          } else if constexpr (MODE == MODE_BWD_SWIGLU) {
+            const u32x2 gg = *reinterpret_cast<const u32x2*>(p.in0 + off);
+            const u32x2 uu = *reinterpret_cast<const u32x2*>(p.in1 + off);
+            const float G[4] = {bf16_lo(gg[0]), bf16_hi(gg[0]), bf16_lo(gg[1]), bf16_hi(gg[1])};
+            const float U[4] = {bf16_lo(uu[0]), bf16_hi(uu[0]), bf16_lo(uu[1]), bf16_hi(uu[1])};
+            float dG[4], dU[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float dH = acc[i][f][4 * q + e];
+              const float sg = sigmoidf_(G[e]);
+              dU[e] = dH * G[e] * sg;
+              dG[e] = dH * U[e] * sg * (1.0f + G[e] * (1.0f - sg));
+            }
+            *reinterpret_cast<u32x2*>(p.out0 + off) = u32x2{pack_bf16x2(dG[0], dG[1]), pack_bf16x2(dG[2], dG[3])};
+            *reinterpret_cast<u32x2*>(p.out1 + off) = u32x2{pack_bf16x2(dU[0], dU[1]), pack_bf16x2(dU[2], dU[3])};
+          } else {
+            const f32x16& a = acc[i][f];
+            *reinterpret_cast<u32x2*>(p.out0 + off) =
+                u32x2{pack_bf16x2(a[4 * q], a[4 * q + 1]), pack_bf16x2(a[4 * q + 2], a[4 * q + 3])};
+          }
+        }
+      }
+    }
+  }
+}
+
+// Split-reduction finish for the linear GEMMs: out = bf16(sum_z part[z] + LoRA).
+// One thread per 4 consecutive output columns of one token, fixed z order.
+__global__ __launch_bounds__(256) void splitk_finish_kernel(const float* __restrict__ part, int splits,
+                                                            int64_t M, int64_t Nout, LoraSide L,
+                                                            uint16_t* __restrict__ out) {
+  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t per_row = Nout / 4;
+  if (q >= M * per_row) return;
+  const int64_t m = q / per_row, n = (q % per_row) * 4;
+  f32x4 s = {0.f, 0.f, 0.f, 0.f};
+  for (int z = 0; z < splits; ++z) s += *reinterpret_cast<const f32x4*>(part + ((int64_t)z * M + m) * Nout + n);
+  for (int j = 0; j < L.r; ++j) {
+    const float v = L.s * L.V[m * L.r + j];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) s[e] += v * bf16_to_f32(L.Wl[(n + e) * L.wl_sc + (int64_t)j * L.wl_sj]);
+  }
+  *reinterpret_cast<u32x2*>(out + m * Nout + n) = u32x2{pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3])};
+}
+
+// ------------------------------------------------------------------------
+// LoRA down-projection V[M, r] = Z[M, K] Aw^T on the matrix cores.
+//   AW_ROWS: Aw is [r, K] (rows = j)            -> V = Z A^T   (XA, HA_d)
+//   else   : Aw is [K, r] (Aw = B, K = N)       -> V = Z B     (T = dY B)
+// Workgroup: 32 tokens, 4 waves dealing the k16 steps round-robin; the four
+// partials are summed in LDS in wave order.  blockIdx.y = reduction split.
+// Two outputs (for gate | up) when V1 != null: columns [0, r0) from A0 into
+// V0 and [r0, r0 + r1) from A1 into V1.
+// ------------------------------------------------------------------------
+template <bool AW_ROWS>
+__global__ __launch_bounds__(256) void lora_down_kernel(const uint16_t* __restrict__ Z, int64_t M, int64_t Kred,
+                                                        const uint16_t* __restrict__ A0, int r0,
+                                                        const uint16_t* __restrict__ A1, int r1,
+                                                        float* __restrict__ V0, float* __restrict__ V1,
+                                                        int64_t k_per_split, float* __restrict__ part) {
+  __shared__ float red[4][4 * 16 * 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, g = lane >> 5;
+  const int rt = r0 + r1;
+  const int JF = (rt + 31) / 32;
+  const int64_t m0 = (int64_t)blockIdx.x * 32;
+  int64_t m = m0 + l32;
+  if (m >= M) m = M - 1;
+  const int64_t kb = (int64_t)blockIdx.y * k_per_split;
+  const int64_t ke = min(Kred, kb + k_per_split);
+
+  f32x16 acc[4];
+#pragma unroll
+  for (int jf = 0; jf < 4; ++jf)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[jf][v] = 0.0f;
+
+  for (int64_t k = kb + 16 * wave; k < ke; k += 64) {
+    const u32x4 zb = *reinterpret_cast<const u32x4*>(Z + m * Kred + k + 8 * g);
+#pragma unroll
+    for (int jf = 0; jf < 4; ++jf) {
+      if (jf >= JF) break;
+      const int j = 32 * jf + l32;
+      u32x4 aop = {0u, 0u, 0u, 0u};
+      if (j < rt) {
+        const uint16_t* Aw = (j < r0) ? A0 : A1;
+        const int jj = (j < r0) ? j : j - r0;
+        const int rr = (j < r0) ? r0 : r1;
+        if (AW_ROWS) {
+          aop = *reinterpret_cast<const u32x4*>(Aw + (int64_t)jj * Kred + k + 8 * g);
+        } else {
+          uint32_t h[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) h[e] = Aw[(k + 8 * g + e) * rr + jj];
+          aop = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+        }
+      }
+      acc[jf] = mfma32(aop, zb, acc[jf]);
+    }
+  }
+  // acc[jf][v] = C[j = 32 jf + 8(v/4) + 4g + v%4][token l32]
+#pragma unroll
+  for (int jf = 0; jf < 4; ++jf)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) red[wave][(jf * 16 + v) * 64 + lane] = acc[jf][v];
+  __syncthreads();
+  // each thread finishes (jf, v, lane) slots in fixed wave order
+  for (int idx = tid; idx < JF * 16 * 64; idx += 256) {
+    const float s = ((red[0][idx] + red[1][idx]) + red[2][idx]) + red[3][idx];
+    const int ln = idx & 63, vv = (idx >> 6) & 15, jf = idx >> 10;
+    const int j = 32 * jf + 8 * (vv >> 2) + 4 * (ln >> 5) + (vv & 3);
+    const int64_t mm = m0 + (ln & 31);
+    if (j >= rt || mm >= M) continue;
+    if (part) {
+      part[((int64_t)blockIdx.y * M + mm) * rt + j] = s;
+    } else if (j < r0) {
+      V0[mm * r0 + j] = s;
+    } else {
+      V1[mm * r1 + (j - r0)] = s;
+    }
+  }
+}
+
+// Sum of split partials [S][M][r0 + r1] in split order into V0 | V1.
+__global__ __launch_bounds__(256) void down_finish_kernel(const float* __restrict__ part, int S, int64_t M,
+                                                          int r0, int r1, float* __restrict__ V0,
+                                                          float* __restrict__ V1) {
+  const int rt = r0 + r1;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= M * rt) return;
+  float s = 0.0f;
+  for (int z = 0; z < S; ++z) s += part[(int64_t)z * M * rt + i];
+  const int64_t m = i / rt;
+  const int j = (int)(i % rt);
+  if (j < r0)
+    V0[m * r0 + j] = s;
+  else
+    V1[m * r1 + (j - r0)] = s;
+}
+
+// ------------------------------------------------------------------------
+// LoRA gradient reduction over tokens: part[z][p][j] = sum_{m in split z}
+// Z[m, p] V[m, j], for p in [0, P), j in [jb, jb + 32*JF).
+//   ZMODE 0: Z is a bf16 [M, P] tensor.
+//   ZMODE 1: Z = silu(G) * U recomputed from bf16 G, U [M, P].
+// One wave per 256 columns p: per 16 tokens each lane loads 8 tokens x 8
+// columns (16 B per token, coalesced along p), transposes them in registers
+// (v_perm) into eight 32x16 operands whose row i is column p0 + 8 i + t,
+// and runs 8 MFMAs per 32-wide j frag against V (rounded to bf16).
+// ------------------------------------------------------------------------
+template <int ZMODE, int JF>
+__global__ __launch_bounds__(256) void lora_grad_kernel(const uint16_t* __restrict__ Z0,
+                                                        const uint16_t* __restrict__ Z1, int64_t M,
+                                                        int64_t P, const float* __restrict__ V, int r, int jb,
+                                                        int64_t m_per_split, float* __restrict__ part) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, g = lane >> 5;
+  const int64_t p0 = ((int64_t)blockIdx.x * 4 + wave) * 256;
+  if (p0 >= P) return;
+  const int z = blockIdx.y;
+  const int64_t mb = (int64_t)z * m_per_split;
+  const int64_t me = min(M, mb + m_per_split);
+  int64_t pc = p0 + 8 * l32;
+  if (pc > P - 8) pc = P - 8;
+
+  f32x16 acc[8][JF];
+#pragma unroll
+  for (int t = 0; t < 8; ++t)
+#pragma unroll
+    for (int jf = 0; jf < JF; ++jf)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[t][jf][v] = 0.0f;
+
+  for (int64_t ms = mb; ms < me; ms += 16) {
+    u32x4 rows[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int64_t mm = ms + 8 * g + e;
+      if (mm < me) {
+        if constexpr (ZMODE == 0) {
+          rows[e] = *reinterpret_cast<const u32x4*>(Z0 + mm * P + pc);
+        } else {
+          const u32x4 gg = *reinterpret_cast<const u32x4*>(Z0 + mm * P + pc);
+          const u32x4 uu = *reinterpret_cast<const u32x4*>(Z1 + mm * P + pc);
+#pragma unroll
+          for (int d = 0; d < 4; ++d) {
+            const float g0 = bf16_lo(gg[d]), g1 = bf16_hi(gg[d]);
+            const float h0 = g0 * sigmoidf_(g0) * bf16_lo(uu[d]);
+            const float h1 = g1 * sigmoidf_(g1) * bf16_hi(uu[d]);
+            rows[e][d] = pack_bf16x2(h0, h1);
+          }
+        }
+      } else {
+        rows[e] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+    // operand t: lane (i, g) holds Z[ms + 8g + e][p0 + 8 i + t], e = 0..7
+    u32x4 aop[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const uint32_t sel = (t & 1) ? 0x07060302u : 0x05040100u;
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+        aop[t][d] = __builtin_amdgcn_perm(rows[2 * d + 1][t >> 1], rows[2 * d][t >> 1], sel);
+    }
+#pragma unroll
+    for (int jf = 0; jf < JF; ++jf) {
+      const int j = jb + 32 * jf + l32;
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int64_t mm = ms + 8 * g + e;
+        x[e] = (j < r && mm < me) ? V[mm * r + j] : 0.0f;
+      }
+      const u32x4 vop{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
+                      pack_bf16x2(x[6], x[7])};
+#pragma unroll
+      for (int t = 0; t < 8; ++t) acc[t][jf] = mfma32(aop[t], vop, acc[t][jf]);
+    }
+  }
+  // acc[t][jf][v] = C[i = 8(v/4) + 4g + v%4][j = jb + 32 jf + l32], column p = p0 + 8 i + t
+#pragma unroll
+  for (int jf = 0; jf < JF; ++jf) {
+    const int j = jb + 32 * jf + l32;
+    if (j >= r) continue;
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int i = 8 * (v >> 2) + 4 * g + (v & 3);
+        const int64_t pp = p0 + 8 * i + t;
+        if (pp < P) part[((int64_t)z * P + pp) * r + j] = acc[t][jf][v];
+      }
+  }
+}
+
+// out = bf16(s * sum_z part[z]), layout [P, r] (dB) or [r, P] (dA).
+__global__ __launch_bounds__(256) void grad_finish_kernel(const float* __restrict__ part, int S, int64_t P, int r,
+                                                          float s, int out_rp, uint16_t* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= P * r) return;
+  float acc = 0.0f;
+  for (int z = 0; z < S; ++z) acc += part[(int64_t)z * P * r + i];
+  acc *= s;
+  const int64_t pp = i / r;
+  const int j = (int)(i % r);
+  const uint32_t b = pack_bf16x2(acc, 0.0f) & 0xFFFFu;
+  if (out_rp)
+    out[(int64_t)j * P + pp] = (uint16_t)b;
+  else
+    out[i] = (uint16_t)b;
+}
+
+__global__ __launch_bounds__(256) void zero_u16_kernel(uint16_t* __restrict__ out, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) out[i] = 0;
+}
+
+}  // namespace qk
+
+// ==========================================================================
+// Launchers (called by the C ABI in qlora_api.hip)
+// ==========================================================================
+using namespace qk;
+
+static inline unsigned grid1(int64_t n, int per) { return (unsigned)((n + per - 1) / per); }
+
+hipError_t launch_nf4_quantize(const float* W, int64_t nblocks, const float* codebook, int dq, uint8_t* codes,
+                               float* absmax, uint8_t* absmax_q, float* absmax_scale, hipStream_t st) {
+  if (nblocks == 0) return hipSuccess;
+  nf4_quantize_kernel<<<grid1(nblocks, 256), 256, 0, st>>>(W, nblocks, codebook, dq, codes, absmax, absmax_q,
+                                                           absmax_scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_nf4_dequantize(const Nf4Dev& w, const float* codebook, int out_f32, void* out, hipStream_t st) {
+  const int64_t n8 = w.N * w.K / 8;
+  if (n8 == 0) return hipSuccess;
+  nf4_dequantize_kernel<<<grid1(n8, 256), 256, 0, st>>>(w, codebook, n8, out_f32, out);
+  return hipGetLastError();
+}
+
+template <int MODE, int WM, int WN, int FM, int FN>
+static hipError_t run_gemm(GemmArgs a, const qplan::GemmPlan& pl, hipStream_t st) {
+  constexpr int NT = WM * WN * 64;
+  constexpr int BM = WM * FM * 32;
+  constexpr int BNO = (MODE == MODE_FWD_SWIGLU ? WN * FN * 16 : WN * FN * 32);
+  a.tiles_m = (a.M + BM - 1) / BM;
+  a.tiles_n = (a.Nout + BNO - 1) / BNO;
+  a.ktiles_per_split = pl.ktiles_per_split;
+  dim3 grid((unsigned)(a.tiles_m * a.tiles_n), (unsigned)pl.splits);
+  if (pl.splits > 1) {
+    if constexpr (MODE == MODE_FWD || MODE == MODE_BWD) {
+      qgemm_kernel<MODE, WM, WN, FM, FN, true><<<grid, NT, 0, st>>>(a);
+    } else {
+      return hipErrorInvalidValue;
+    }
+  } else {
+    qgemm_kernel<MODE, WM, WN, FM, FN, false><<<grid, NT, 0, st>>>(a);
+  }
+  return hipGetLastError();
+}
+
+template <int MODE>
+static hipError_t run_gemm_cfg(const GemmArgs& a, const qplan::GemmPlan& pl, hipStream_t st) {
+  if (pl.cfg == qplan::CFG_BIG) return run_gemm<MODE, 2, 2, 4, 4>(a, pl, st);
+  if constexpr (MODE == MODE_FWD_SWIGLU) {
+    return run_gemm<MODE, 1, 2, 2, 2>(a, pl, st);
+  } else {
+    return run_gemm<MODE, 1, 2, 2, 1>(a, pl, st);
+  }
+}
+
+hipError_t launch_qgemm(int mode, const GemmArgs& a, const qplan::GemmPlan& pl, hipStream_t st) {
+  switch (mode) {
+    case MODE_FWD: return run_gemm_cfg<MODE_FWD>(a, pl, st);
+    case MODE_FWD_SWIGLU: return run_gemm_cfg<MODE_FWD_SWIGLU>(a, pl, st);
+    case MODE_BWD: return run_gemm_cfg<MODE_BWD>(a, pl, st);
+    case MODE_BWD_SWIGLU: return run_gemm_cfg<MODE_BWD_SWIGLU>(a, pl, st);
+    case MODE_BWD_DUAL: return run_gemm_cfg<MODE_BWD_DUAL>(a, pl, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_splitk_finish(const float* part, int splits, int64_t M, int64_t Nout, const LoraSide& L,
+                                uint16_t* out, hipStream_t st) {
+  const int64_t n = M * (Nout / 4);
+  if (n == 0) return hipSuccess;
+  splitk_finish_kernel<<<grid1(n, 256), 256, 0, st>>>(part, splits, M, Nout, L, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_lora_down(bool aw_rows, const uint16_t* Z, int64_t M, int64_t Kred, const uint16_t* A0, int r0,
+                            const uint16_t* A1, int r1, float* V0, float* V1, int splits, float* part,
+                            hipStream_t st) {
+  if (M == 0) return hipSuccess;
+  const int64_t k16 = Kred / 16;
+  const int64_t per = ((k16 + splits - 1) / splits) * 16;
+  const int S = (int)((Kred + per - 1) / per);
+  dim3 grid(grid1(M, 32), (unsigned)S);
+  float* pp = S > 1 ? part : nullptr;
+  if (aw_rows)
+    lora_down_kernel<true><<<grid, 256, 0, st>>>(Z, M, Kred, A0, r0, A1, r1, V0, V1, per, pp);
+  else
+    lora_down_kernel<false><<<grid, 256, 0, st>>>(Z, M, Kred, A0, r0, A1, r1, V0, V1, per, pp);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || S == 1) return e;
+  down_finish_kernel<<<grid1(M * (r0 + r1), 256), 256, 0, st>>>(part, S, M, r0, r1, V0, V1);
+  return hipGetLastError();
+}
+
+hipError_t launch_lora_grad(int zmode, const uint16_t* Z0, const uint16_t* Z1, int64_t M, int64_t P,
+                            const float* V, int r, float s, int msplits, float* part, int out_rp, uint16_t* out,
+                            hipStream_t st) {
+  if (M == 0) {
+    zero_u16_kernel<<<grid1(P * r, 256), 256, 0, st>>>(out, P * r);
+    return hipGetLastError();
+  }
+  const int64_t mps = (((M + msplits - 1) / msplits) + 15) / 16 * 16;
+  const int S = (int)((M + mps - 1) / mps);
+  for (int jb = 0; jb < r; jb += 64) {
+    const int jf = (r - jb) > 32 ? 2 : 1;
+    dim3 grid(grid1(P, 1024), (unsigned)S);
+    if (zmode == 0) {
+      if (jf == 2)
+        lora_grad_kernel<0, 2><<<grid, 256, 0, st>>>(Z0, Z1, M, P, V, r, jb, mps, part);
+      else
+        lora_grad_kernel<0, 1><<<grid, 256, 0, st>>>(Z0, Z1, M, P, V, r, jb, mps, part);
+    } else {
+      if (jf == 2)
+        lora_grad_kernel<1, 2><<<grid, 256, 0, st>>>(Z0, Z1, M, P, V, r, jb, mps, part);
+      else
+        lora_grad_kernel<1, 1><<<grid, 256, 0, st>>>(Z0, Z1, M, P, V, r, jb, mps, part);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  grad_finish_kernel<<<grid1(P * r, 256), 256, 0, st>>>(part, S, P, r, s, out_rp, out);
+  return hipGetLastError();
+}

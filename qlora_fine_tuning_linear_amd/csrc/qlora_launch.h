@@ -1,0 +1,65 @@
+// Kernel launchers and their argument blocks (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "qlora_plan.h"
+
+// GEMM modes of qgemm_kernel.
+enum {
+  MODE_FWD = 0,         // Y  = X W^T + LoRA                 (weight [N, K], reduce over K)
+  MODE_FWD_SWIGLU = 1,  // G, U = X Wg^T, X Wu^T + LoRA; H = silu(G) * U
+  MODE_BWD = 2,         // dX = dY W + LoRA                  (weight [N, K], reduce over N)
+  MODE_BWD_SWIGLU = 3,  // dH = dY Wd + LoRA; dG, dU from G, U
+  MODE_BWD_DUAL = 4,    // dX = dG Wg + dU Wu + both LoRA terms (reduce over 2I)
+};
+
+struct Nf4Dev {
+  const uint8_t* codes;
+  const float* absmax;        // dq == 0
+  const uint8_t* absmax_q;    // dq > 0
+  const float* absmax_scale;  // dq > 0
+  int64_t N, K;
+  int32_t dq;
+};
+
+// One LoRA epilogue term: out[m, c] += s * sum_j V[m, j] * Wl(c, j),
+// Wl(c, j) = Wl[c * wl_sc + j * wl_sj]  (B [N, r]: (r, 1); A [r, K]: (1, K)).
+struct LoraSide {
+  const float* V;
+  const uint16_t* Wl;
+  int64_t wl_sc, wl_sj;
+  int32_t r;
+  float s;
+};
+
+struct GemmArgs {
+  const uint16_t* act0;
+  const uint16_t* act1;
+  int64_t M, Nout, Kred0, Kred1;
+  Nf4Dev w0, w1;
+  const float* codebook;
+  LoraSide l0, l1;
+  uint16_t* out0;
+  uint16_t* out1;
+  uint16_t* out2;
+  const uint16_t* in0;
+  const uint16_t* in1;
+  float* partial;
+  int64_t tiles_m, tiles_n;
+  int32_t ktiles_per_split;
+};
+
+hipError_t launch_nf4_quantize(const float* W, int64_t nblocks, const float* codebook, int dq, uint8_t* codes,
+                               float* absmax, uint8_t* absmax_q, float* absmax_scale, hipStream_t st);
+hipError_t launch_nf4_dequantize(const Nf4Dev& w, const float* codebook, int out_f32, void* out, hipStream_t st);
+hipError_t launch_qgemm(int mode, const GemmArgs& a, const qplan::GemmPlan& pl, hipStream_t st);
+hipError_t launch_splitk_finish(const float* part, int splits, int64_t M, int64_t Nout, const LoraSide& L,
+                                uint16_t* out, hipStream_t st);
+hipError_t launch_lora_down(bool aw_rows, const uint16_t* Z, int64_t M, int64_t Kred, const uint16_t* A0, int r0,
+                            const uint16_t* A1, int r1, float* V0, float* V1, int splits, float* part,
+                            hipStream_t st);
+hipError_t launch_lora_grad(int zmode, const uint16_t* Z0, const uint16_t* Z1, int64_t M, int64_t P,
+                            const float* V, int r, float s, int msplits, float* part, int out_rp, uint16_t* out,
+                            hipStream_t st);

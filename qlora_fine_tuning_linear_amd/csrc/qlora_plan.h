@@ -1,0 +1,148 @@
+// Host-side planning shared by the launch code and the workspace queries.
+// No HIP types here: this header is also compiled into the HIP-free
+// argument-validation translation unit.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace qplan {
+
+// Tile configurations of the dequant-staged MFMA GEMM (32x32x16 bf16 frags).
+//   BIG     : 2x2 waves, 4x4 frags per wave -> 256 tokens x 256 output columns
+//   SKINNY  : 1x2 waves, 2x1 frags per wave ->  64 tokens x  64 output columns
+enum GemmCfg { CFG_BIG = 0, CFG_SKINNY = 1 };
+
+constexpr int kNumCUs = 256;
+constexpr int64_t kBK = 64;  // reduction tile = one absmax block
+
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct GemmPlan {
+  int cfg;
+  int64_t bm, bn;
+  int64_t tiles_m, tiles_n;
+  int splits;            // reduction splits (fp32 partials + a reduce pass when > 1)
+  int ktiles_per_split;  // 64-wide reduction tiles per split
+};
+
+// M tokens, Nout output columns, Kred reduction length (multiple of 64).
+inline GemmPlan plan_gemm(int64_t M, int64_t Nout, int64_t Kred, bool allow_split) {
+  GemmPlan p{};
+  p.cfg = (M <= 128) ? CFG_SKINNY : CFG_BIG;
+  p.bm = (p.cfg == CFG_BIG) ? 256 : 64;
+  p.bn = (p.cfg == CFG_BIG) ? 256 : 64;
+  p.tiles_m = cdiv(M, p.bm);
+  p.tiles_n = cdiv(Nout, p.bn);
+  const int64_t kt = Kred / kBK;
+  int64_t splits = 1;
+  const int64_t tiles = p.tiles_m * p.tiles_n;
+  if (allow_split && tiles < 2 * kNumCUs) {
+    splits = cdiv(2 * kNumCUs, tiles);
+    const int64_t max_splits = kt / 8 > 0 ? kt / 8 : 1;  // keep >= 8 tiles per split
+    if (splits > max_splits) splits = max_splits;
+    if (splits < 1) splits = 1;
+  }
+  int64_t per = cdiv(kt, splits);
+  splits = cdiv(kt, per);
+  p.splits = (int)splits;
+  p.ktiles_per_split = (int)per;
+  return p;
+}
+
+// Reduction splits of the LoRA down-projection V = Z A^T (M x r, reduce over Kred).
+inline int plan_down_splits(int64_t M, int64_t Kred) {
+  const int64_t wgs = cdiv(M, 32);
+  if (wgs >= kNumCUs) return 1;
+  int64_t s = cdiv(kNumCUs, wgs);
+  const int64_t max_s = Kred / 512 > 0 ? Kred / 512 : 1;  // >= 32 k16-steps per split
+  if (s > max_s) s = max_s;
+  return (int)(s < 1 ? 1 : s);
+}
+
+// Token splits of a LoRA-gradient reduction out[p, j] = sum_m Z[m, p] V[m, j].
+// Each split writes an fp32 [P, r] partial; keep the partials small next to Z.
+inline int plan_grad_msplits(int64_t M, int64_t P, int r) {
+  const int64_t waves = cdiv(P, 256);
+  int64_t s = cdiv(4 * kNumCUs, waves);
+  // partial bytes 4 * s * P * r must stay below ~1/8 of the Z bytes 2 * M * P
+  int64_t cap = (M / (16 * (int64_t)r));
+  if (cap < 1) cap = 1;
+  if (s > cap) s = cap;
+  const int64_t max_by_rows = cdiv(M, 64);  // >= 64 tokens per split
+  if (s > max_by_rows) s = max_by_rows;
+  return (int)(s < 1 ? 1 : s);
+}
+
+struct LinearWs {
+  size_t fwd_part, fwd_down;             // forward: split-K partials, down-proj partials
+  size_t bwd_T, bwd_part, bwd_down, bwd_grad;
+  size_t fwd_total, bwd_total, total;
+};
+
+inline LinearWs linear_ws(int64_t M, int64_t N, int64_t K, int r) {
+  LinearWs w{};
+  GemmPlan pf = plan_gemm(M, N, K, true);
+  w.fwd_part = pf.splits > 1 ? align256((size_t)pf.splits * M * N * 4) : 0;
+  const int ds = plan_down_splits(M, K);
+  w.fwd_down = ds > 1 ? align256((size_t)ds * M * r * 4) : 0;
+  w.fwd_total = w.fwd_part + w.fwd_down;
+
+  GemmPlan pb = plan_gemm(M, K, N, true);
+  w.bwd_T = align256((size_t)M * r * 4);
+  w.bwd_part = pb.splits > 1 ? align256((size_t)pb.splits * M * K * 4) : 0;
+  const int ts = plan_down_splits(M, N);
+  w.bwd_down = ts > 1 ? align256((size_t)ts * M * r * 4) : 0;
+  const int gs_b = plan_grad_msplits(M, N, r);
+  const int gs_a = plan_grad_msplits(M, K, r);
+  size_t gb = align256((size_t)gs_b * N * r * 4), ga = align256((size_t)gs_a * K * r * 4);
+  w.bwd_grad = gb > ga ? gb : ga;
+  w.bwd_total = w.bwd_T + w.bwd_part + w.bwd_down + w.bwd_grad;
+  w.total = w.fwd_total > w.bwd_total ? w.fwd_total : w.bwd_total;
+  if (w.total == 0) w.total = 256;
+  return w;
+}
+
+struct MlpWs {
+  size_t fwd_H, fwd_down;                            // H bf16 [M, I], down-proj partials
+  size_t bwd_Td, bwd_dG, bwd_dU, bwd_Tg, bwd_Tu, bwd_down, bwd_grad;
+  size_t fwd_total, bwd_total, total;
+};
+
+inline MlpWs mlp_ws(int64_t M, int64_t D, int64_t I, int rg, int ru, int rd) {
+  MlpWs w{};
+  int rmax = rg > ru ? rg : ru;
+  if (rd > rmax) rmax = rd;
+  w.fwd_H = align256((size_t)M * I * 2);
+  const int s1 = plan_down_splits(M, D), s2 = plan_down_splits(M, I);
+  size_t d1 = s1 > 1 ? align256((size_t)s1 * M * (rg + ru) * 4) : 0;
+  size_t d2 = s2 > 1 ? align256((size_t)s2 * M * rd * 4) : 0;
+  w.fwd_down = d1 > d2 ? d1 : d2;
+  w.fwd_total = w.fwd_H + w.fwd_down;
+
+  w.bwd_Td = align256((size_t)M * rd * 4);
+  w.bwd_dG = align256((size_t)M * I * 2);
+  w.bwd_dU = align256((size_t)M * I * 2);
+  w.bwd_Tg = align256((size_t)M * rg * 4);
+  w.bwd_Tu = align256((size_t)M * ru * 4);
+  const int t1 = plan_down_splits(M, D), t2 = plan_down_splits(M, I);
+  size_t e1 = t1 > 1 ? align256((size_t)t1 * M * rd * 4) : 0;
+  size_t e2 = t2 > 1 ? align256((size_t)t2 * M * rmax * 4) : 0;
+  w.bwd_down = e1 > e2 ? e1 : e2;
+  size_t g = 0;
+  const int64_t Ps[6] = {D, I, I, D, I, D};
+  const int Rs[6] = {rd, rd, rg, rg, ru, ru};
+  for (int i = 0; i < 6; ++i) {
+    const int ms = plan_grad_msplits(M, Ps[i], Rs[i]);
+    size_t b = align256((size_t)ms * Ps[i] * Rs[i] * 4);
+    if (b > g) g = b;
+  }
+  w.bwd_grad = g;
+  w.bwd_total = w.bwd_Td + w.bwd_dG + w.bwd_dU + w.bwd_Tg + w.bwd_Tu + w.bwd_down + w.bwd_grad;
+  w.total = w.fwd_total > w.bwd_total ? w.fwd_total : w.bwd_total;
+  if (w.total == 0) w.total = 256;
+  return w;
+}
+
+}  // namespace qplan

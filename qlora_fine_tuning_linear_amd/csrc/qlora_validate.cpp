@@ -1,0 +1,168 @@
+// Argument validation and workspace sizing of the C ABI (include/qlora.h).
+// This translation unit uses no HIP: every check here runs before anything
+// touches the GPU, so the rejection paths can be exercised on a host without
+// one.
+#include <math.h>
+#include <stdint.h>
+
+#include "qlora.h"
+#include "qlora_plan.h"
+#include "qlora_validate.h"
+
+namespace {
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int check_nf4(const qlora_nf4* w) {
+  if (!w || !w->codes || !w->codebook) return QLORA_ERR_INVALID_ARG;
+  if (w->N < 0 || w->K < 0) return QLORA_ERR_INVALID_ARG;
+  if (w->blocksize != 64) return QLORA_ERR_UNSUPPORTED_SHAPE;
+  if (w->dq_group != 0 && w->dq_group != 256) return QLORA_ERR_UNSUPPORTED_SHAPE;
+  if (w->dq_group == 0 && !w->absmax) return QLORA_ERR_INVALID_ARG;
+  if (w->dq_group != 0 && (!w->absmax_q || !w->absmax_scale)) return QLORA_ERR_INVALID_ARG;
+  if (w->N == 0 || w->K == 0) return QLORA_ERR_UNSUPPORTED_SHAPE;
+  if (w->K % 64 != 0 || w->N % 64 != 0) return QLORA_ERR_UNSUPPORTED_SHAPE;
+  if (!aligned16(w->codes) || !aligned16(w->codebook)) return QLORA_ERR_MISALIGNED;
+  if (w->dq_group == 0 && !aligned16(w->absmax)) return QLORA_ERR_MISALIGNED;
+  if (w->dq_group != 0 && !aligned16(w->absmax_scale)) return QLORA_ERR_MISALIGNED;
+  return QLORA_OK;
+}
+
+int check_linear(const qlora_linear* L) {
+  if (!L) return QLORA_ERR_INVALID_ARG;
+  int st = check_nf4(&L->W0);
+  if (st) return st;
+  if (!L->A || !L->B) return QLORA_ERR_INVALID_ARG;
+  if (!isfinite(L->alpha)) return QLORA_ERR_INVALID_ARG;
+  if (L->r < 1 || L->r > 128) return QLORA_ERR_UNSUPPORTED_SHAPE;
+  if (!aligned16(L->A) || !aligned16(L->B)) return QLORA_ERR_MISALIGNED;
+  return QLORA_OK;
+}
+
+int check_ptr(const void* p) {
+  if (!p) return QLORA_ERR_INVALID_ARG;
+  if (!aligned16(p)) return QLORA_ERR_MISALIGNED;
+  return QLORA_OK;
+}
+
+int check_ws(const void* ws, size_t ws_bytes, size_t need) {
+  if (need == 0) return QLORA_OK;
+  if (ws_bytes < need) return QLORA_ERR_WORKSPACE_TOO_SMALL;
+  return check_ptr(ws);
+}
+
+}  // namespace
+
+int qv_quantize(const float* W, int64_t N, int64_t K, const float* codebook16, int32_t blocksize, int32_t dq_group,
+                const uint8_t* codes, const float* absmax, const uint8_t* absmax_q, const float* absmax_scale) {
+  if (N < 0 || K < 0) return QLORA_ERR_INVALID_ARG;
+  if (blocksize != 64) return QLORA_ERR_UNSUPPORTED_SHAPE;
+  if (dq_group != 0 && dq_group != 256) return QLORA_ERR_UNSUPPORTED_SHAPE;
+  if (K % 64 != 0) return QLORA_ERR_UNSUPPORTED_SHAPE;
+  if (N == 0 || K == 0) return QLORA_OK;
+  if (!W || !codebook16 || !codes) return QLORA_ERR_INVALID_ARG;
+  if (dq_group == 0 && !absmax) return QLORA_ERR_INVALID_ARG;
+  if (dq_group != 0 && (!absmax_q || !absmax_scale)) return QLORA_ERR_INVALID_ARG;
+  if (!aligned16(W) || !aligned16(codebook16) || !aligned16(codes)) return QLORA_ERR_MISALIGNED;
+  if (dq_group == 0 && !aligned16(absmax)) return QLORA_ERR_MISALIGNED;
+  if (dq_group != 0 && !aligned16(absmax_scale)) return QLORA_ERR_MISALIGNED;
+  return QLORA_OK;
+}
+
+int qv_dequantize(const qlora_nf4* w, int32_t out_dtype, const void* out) {
+  int st = check_nf4(w);
+  if (st) return st;
+  if (out_dtype != QLORA_DTYPE_BF16 && out_dtype != QLORA_DTYPE_F32) return QLORA_ERR_INVALID_ARG;
+  return check_ptr(out);
+}
+
+int qv_linear_fwd(const qlora_linear* L, const void* X, int64_t M, const void* Y, const float* XA, const void* ws,
+                  size_t ws_bytes) {
+  int st = check_linear(L);
+  if (st) return st;
+  if (M < 0) return QLORA_ERR_INVALID_ARG;
+  if (M == 0) return QLORA_OK;
+  if ((st = check_ptr(X)) || (st = check_ptr(Y)) || (st = check_ptr(XA))) return st;
+  const qplan::LinearWs w = qplan::linear_ws(M, L->W0.N, L->W0.K, L->r);
+  return check_ws(ws, ws_bytes, w.fwd_total);
+}
+
+int qv_linear_bwd(const qlora_linear* L, const void* dY, const void* X, const float* XA, int64_t M, const void* dX,
+                  const void* dA, const void* dB, const void* ws, size_t ws_bytes) {
+  int st = check_linear(L);
+  if (st) return st;
+  if (M < 0) return QLORA_ERR_INVALID_ARG;
+  if ((st = check_ptr(dA)) || (st = check_ptr(dB))) return st;
+  if (M == 0) return QLORA_OK;
+  if ((st = check_ptr(dY)) || (st = check_ptr(X)) || (st = check_ptr(XA)) || (st = check_ptr(dX))) return st;
+  const qplan::LinearWs w = qplan::linear_ws(M, L->W0.N, L->W0.K, L->r);
+  return check_ws(ws, ws_bytes, w.bwd_total);
+}
+
+static int check_mlp(const qlora_mlp* P) {
+  if (!P) return QLORA_ERR_INVALID_ARG;
+  int st;
+  if ((st = check_linear(&P->gate)) || (st = check_linear(&P->up)) || (st = check_linear(&P->down))) return st;
+  const int64_t I = P->gate.W0.N, D = P->gate.W0.K;
+  if (P->up.W0.N != I || P->up.W0.K != D) return QLORA_ERR_UNSUPPORTED_SHAPE;
+  if (P->down.W0.N != D || P->down.W0.K != I) return QLORA_ERR_UNSUPPORTED_SHAPE;
+  return QLORA_OK;
+}
+
+int qv_mlp_fwd(const qlora_mlp* P, const void* X, int64_t M, const void* Y, const qlora_mlp_saved* S, const void* ws,
+               size_t ws_bytes) {
+  int st = check_mlp(P);
+  if (st) return st;
+  if (M < 0 || !S) return QLORA_ERR_INVALID_ARG;
+  if (M == 0) return QLORA_OK;
+  if ((st = check_ptr(X)) || (st = check_ptr(Y)) || (st = check_ptr(S->G)) || (st = check_ptr(S->U)) ||
+      (st = check_ptr(S->XA_g)) || (st = check_ptr(S->XA_u)) || (st = check_ptr(S->HA_d)))
+    return st;
+  const qplan::MlpWs w = qplan::mlp_ws(M, P->gate.W0.K, P->gate.W0.N, P->gate.r, P->up.r, P->down.r);
+  return check_ws(ws, ws_bytes, w.fwd_total);
+}
+
+int qv_mlp_bwd(const qlora_mlp* P, const void* dY, const void* X, const qlora_mlp_saved* S, int64_t M, const void* dX,
+               const qlora_mlp_grads* G, const void* ws, size_t ws_bytes) {
+  int st = check_mlp(P);
+  if (st) return st;
+  if (M < 0 || !S || !G) return QLORA_ERR_INVALID_ARG;
+  if ((st = check_ptr(G->dA_g)) || (st = check_ptr(G->dB_g)) || (st = check_ptr(G->dA_u)) ||
+      (st = check_ptr(G->dB_u)) || (st = check_ptr(G->dA_d)) || (st = check_ptr(G->dB_d)))
+    return st;
+  if (M == 0) return QLORA_OK;
+  if ((st = check_ptr(dY)) || (st = check_ptr(X)) || (st = check_ptr(dX)) || (st = check_ptr(S->G)) ||
+      (st = check_ptr(S->U)) || (st = check_ptr(S->XA_g)) || (st = check_ptr(S->XA_u)) || (st = check_ptr(S->HA_d)))
+    return st;
+  const qplan::MlpWs w = qplan::mlp_ws(M, P->gate.W0.K, P->gate.W0.N, P->gate.r, P->up.r, P->down.r);
+  return check_ws(ws, ws_bytes, w.bwd_total);
+}
+
+extern "C" {
+
+uint32_t qlora_abi_version(void) { return QLORA_ABI_VERSION; }
+
+const char* qlora_strerror(int status) {
+  switch (status) {
+    case QLORA_OK: return "ok";
+    case QLORA_ERR_INVALID_ARG: return "invalid argument";
+    case QLORA_ERR_UNSUPPORTED_SHAPE: return "unsupported shape";
+    case QLORA_ERR_MISALIGNED: return "tensor pointer not 16-byte aligned";
+    case QLORA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case QLORA_ERR_UNSUPPORTED_DEVICE: return "unsupported device (needs gfx950)";
+    case QLORA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+size_t qlora_linear_workspace_bytes(const qlora_linear* L, int64_t M) {
+  if (!L || M <= 0 || L->r < 1) return 0;
+  return qplan::linear_ws(M, L->W0.N, L->W0.K, L->r).total;
+}
+
+size_t qlora_mlp_workspace_bytes(const qlora_mlp* P, int64_t M) {
+  if (!P || M <= 0) return 0;
+  return qplan::mlp_ws(M, P->gate.W0.K, P->gate.W0.N, P->gate.r, P->up.r, P->down.r).total;
+}
+
+}  // extern "C"

@@ -1,0 +1,112 @@
+"""GPU parity of qlora_linear_fwd / qlora_linear_bwd against the fp64 oracle.
+
+Every floating-point output (Y, XA, dX, dA, dB) must be within relative
+Frobenius error 1e-2 of the oracle.  Cases: the single-linear workloads at
+their full sizes (M=256 512->512 r=8; M=4096 4096->4096 r=16; M=64
+8192->28672 r=16 with double-quantized absmax), ragged token counts and
+output widths that leave partial tiles, every rank from 1 to 128, and the
+degenerate cases (M=0, alpha=0, B=0).  Launch shapes are the library's own
+(the same ones bench.py times).
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import qlora as oq
+
+from gpu_util import assert_close, bf16_dev, f64_host, make_linear
+
+pytestmark = pytest.mark.gpu
+
+q = pytest.importorskip("qlora_fine_tuning_linear_amd")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    q.load_library()
+
+
+def run_case(cfg, seed, codebook, zero_B=False, alpha=None):
+    alpha = cfg.alpha if alpha is None else alpha
+    inp = synth.linear_inputs(cfg, seed)
+    if zero_B:
+        inp["B"] = np.zeros_like(inp["B"])
+    L, Wh = make_linear(q, inp["W0"], inp["A"], inp["B"], alpha, codebook, cfg.dq_group)
+    X, dY = bf16_dev(inp["X"]), bf16_dev(inp["dY"])
+    Y, XA = q.qlora_linear_fwd(L, X)
+    dX, dA, dB = q.qlora_linear_bwd(L, dY, X, XA)
+    torch.cuda.synchronize()
+    Yr, XAr = oq.linear_forward(inp["X"], Wh, inp["A"], inp["B"], alpha)
+    dXr, dAr, dBr = oq.linear_backward(inp["dY"], inp["X"], Wh, inp["A"], inp["B"], alpha)
+    return dict(Y=(Y, Yr), XA=(XA, XAr), dX=(dX, dXr), dA=(dA, dAr), dB=(dB, dBr)), L, X, dY
+
+
+CASES = [
+    # the single-linear workloads at full size
+    synth.CONFIGS[0],
+    synth.CONFIGS[1],
+    synth.CONFIGS[4],
+    # ragged and odd shapes: partial token tiles, partial column tiles, all ranks
+    synth.LinearCfg("m1_64x64_r1", M=1, K=64, N=64, r=1, alpha=2.0, dq_group=0),
+    synth.LinearCfg("m33_128x192_r3", M=33, K=128, N=192, r=3, alpha=5.0, dq_group=256),
+    synth.LinearCfg("m300_512x320_r16", M=300, K=512, N=320, r=16, alpha=16.0, dq_group=0),
+    synth.LinearCfg("m257_256x576_r64", M=257, K=256, N=576, r=64, alpha=16.0, dq_group=256),
+    synth.LinearCfg("m129_640x128_r128", M=129, K=640, N=128, r=128, alpha=32.0, dq_group=0),
+    synth.LinearCfg("m100_2048x4160_r8", M=100, K=2048, N=4160, r=8, alpha=16.0, dq_group=256),
+    synth.LinearCfg("m520_1024x1088_r24", M=520, K=1024, N=1088, r=24, alpha=8.0, dq_group=0),
+]
+
+
+@pytest.mark.parametrize("cfg", CASES, ids=[c.name for c in CASES])
+def test_linear_parity(cfg, codebook):
+    print("case", cfg.name, flush=True)
+    out, *_ = run_case(cfg, 2000 + CASES.index(cfg), codebook)
+    for k, (g, r) in out.items():
+        assert_close(k, g, r)
+
+
+def test_alpha_zero_is_base_matmul(codebook):
+    cfg = synth.LinearCfg("a0", M=96, K=256, N=192, r=8, alpha=0.0, dq_group=0)
+    out, *_ = run_case(cfg, 77, codebook)
+    assert_close("Y", *out["Y"])
+    # with alpha == 0 the LoRA gradients are exactly zero
+    for k in ("dA", "dB"):
+        assert np.all(f64_host(out[k][0]) == 0)
+
+
+def test_b_zero_gives_exact_zero_dA(codebook):
+    cfg = synth.LinearCfg("b0", M=200, K=256, N=320, r=16, alpha=16.0, dq_group=256)
+    out, *_ = run_case(cfg, 78, codebook, zero_B=True)
+    assert np.all(f64_host(out["dA"][0]) == 0)
+    for k in ("Y", "XA", "dX", "dB"):
+        assert_close(k, *out[k])
+
+
+def test_m_zero(codebook):
+    cfg = synth.LinearCfg("m0", M=4, K=128, N=128, r=4, alpha=4.0, dq_group=0)
+    inp = synth.linear_inputs(cfg, 5)
+    L, _ = make_linear(q, inp["W0"], inp["A"], inp["B"], 4.0, codebook, 0)
+    X = torch.empty(0, 128, dtype=torch.bfloat16, device="cuda")
+    Y, XA = q.qlora_linear_fwd(L, X)
+    assert Y.shape == (0, 128)
+    dA = torch.full_like(L.A, 3.0)
+    dB = torch.full_like(L.B, 3.0)
+    q.qlora_linear_bwd(L, torch.empty(0, 128, dtype=torch.bfloat16, device="cuda"), X, XA, dA=dA, dB=dB)
+    torch.cuda.synchronize()
+    assert torch.all(dA == 0) and torch.all(dB == 0)
+
+
+def test_backward_is_bitwise_deterministic(codebook):
+    cfg = synth.LinearCfg("det", M=1000, K=1024, N=768, r=16, alpha=16.0, dq_group=0)
+    out, L, X, dY = run_case(cfg, 9, codebook)
+    XA = out["XA"][0]
+    a = q.qlora_linear_bwd(L, dY, X, XA)
+    b = q.qlora_linear_bwd(L, dY, X, XA)
+    for x, y in zip(a, b):
+        assert torch.equal(x.view(torch.int16), y.view(torch.int16))
+    Y2, XA2 = q.qlora_linear_fwd(L, X)
+    assert torch.equal(Y2.view(torch.int16), out["Y"][0].view(torch.int16))
+    assert torch.equal(XA2, XA)
