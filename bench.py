@@ -1,0 +1,305 @@
+#!/usr/bin/env python3
+"""Throughput of the QLoRA hot path on one MI355X.
+
+A step is one forward + backward pass of the Llama-3-8B-shaped QLoRA SwiGLU
+MLP block (M = 8192 tokens, i.e. batch 2 x sequence 4096, hidden 4096,
+intermediate 14336, LoRA rank 16, alpha 16, NF4 block 64 with fp32 absmax):
+three QLoRA linears with the SwiGLU activation fused into the GEMM epilogues
+and recomputed in the backward pass, plus every LoRA gradient.  Inputs are
+seeded synthetic data of that shape, resident in HBM before timing starts.
+
+Prints ONE JSON line: fwd+bwd TFLOP/s (model FLOPs 12 M D I + 18 M r (D+I)),
+tokens/s, the roofline of the dominant GEMM kernel (timed with HIP events on
+the library's stream through qlora_trace_install), the CPU oracle timed on a
+bounded token sample of the same workload, and secondary lines for the
+single-linear workloads (Llama-3-8B q_proj, and the skinny M=64 gate_proj
+against the HBM roofline with its NF4 weights rotated to defeat the 256 MB
+last-level cache).
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+BF16_PEAK_TFLOPS = 2516.6   # MI355X dense bf16 MFMA
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0, help="target oracle work for the CPU baseline")
+    return ap.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def dev_bf16(u16):
+    import numpy as np
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(u16).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def kernel_source_sha():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "qlora_fine_tuning_linear_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h", ".cpp")):
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(kind):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s.txt" % kind)
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.loads("".join(l for l in open(path) if not l.startswith("#")))
+    except ValueError:
+        return None
+    if rec.get("source_sha") != kernel_source_sha():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def gemm_flops(kind, M, D, I, r):
+    """Algorithmic FLOPs of one launch of each GEMM kind of the MLP step
+    (main product + the rank-r LoRA epilogue product)."""
+    return {
+        "fwd_swiglu": 2 * M * D * (2 * I) + 2 * M * (2 * I) * r,
+        "fwd": 2 * M * I * D + 2 * M * D * r,
+        "bwd_dh_swiglu": 2 * M * D * I + 2 * M * I * r,
+        "bwd_dx_dual": 2 * M * (2 * I) * D + 2 * M * D * (2 * r),
+    }[kind]
+
+
+def mlp_step_bench(q, synth, steps, warmup):
+    import torch
+    idx = 2
+    cfg = synth.CONFIGS[idx]
+    M, D, I, r = cfg.M, cfg.D, cfg.I, cfg.r
+    log("building %s inputs" % cfg.name)
+    inp = synth.mlp_inputs(cfg, synth.seed_of(idx))
+    cb = torch.from_numpy(synth.nf4_codebook()).cuda()
+
+    def lin(W, A, B):
+        Wd = torch.from_numpy(W).cuda()
+        w = q.nf4_quantize(Wd, cb, dq_group=cfg.dq_group)
+        del Wd
+        return q.QLoraLinear(w, dev_bf16(A), dev_bf16(B), cfg.alpha)
+
+    P = q.QLoraMlp(lin(inp["Wg"], inp["Ag"], inp["Bg"]), lin(inp["Wu"], inp["Au"], inp["Bu"]),
+                   lin(inp["Wd"], inp["Ad"], inp["Bd"]))
+    X, dY = dev_bf16(inp["X"]), dev_bf16(inp["dY"])
+    del inp
+    Y = torch.empty(M, D, dtype=torch.bfloat16, device="cuda")
+    dX = torch.empty_like(Y)
+    S = q.alloc_mlp_saved(P, M, "cuda")
+    grads = dict(dA_g=torch.empty_like(P.gate.A), dB_g=torch.empty_like(P.gate.B),
+                 dA_u=torch.empty_like(P.up.A), dB_u=torch.empty_like(P.up.B),
+                 dA_d=torch.empty_like(P.down.A), dB_d=torch.empty_like(P.down.B))
+    ws = torch.empty(q.qlora_mlp_workspace_bytes(P, M), dtype=torch.uint8, device="cuda")
+
+    def step():
+        q.qlora_mlp_fwd(P, X, Y=Y, saved=S, ws=ws)
+        q.qlora_mlp_bwd(P, dY, X, S, dX=dX, grads=grads, ws=ws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    trace = q.LaunchTrace(capacity=8 * steps + 8)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    with trace:
+        e0.record()
+        for _ in range(steps):
+            step()
+        e1.record()
+        torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / steps
+    per_kind = {}
+    for kind, d in trace.durations():
+        per_kind.setdefault(kind, []).append(d)
+    trace.close()
+    flops = 12 * M * D * I + 18 * M * r * (D + I)
+    dom = max(per_kind, key=lambda k: sum(per_kind[k]))
+    dom_ms = sum(per_kind[dom]) / len(per_kind[dom])
+    dom_flops = gemm_flops(dom, M, D, I, r)
+    achieved = dom_flops / (dom_ms * 1e-3) / 1e12
+    traffic = stored_traffic(dom)
+    kernels = {k: {"launches_per_step": len(v) / steps, "avg_ms": sum(v) / len(v),
+                   "tflops": gemm_flops(k, M, D, I, r) / (sum(v) / len(v) * 1e-3) / 1e12}
+               for k, v in per_kind.items()}
+    return dict(cfg=cfg, ms=ms, wall=wall, flops=flops, dom=dom, dom_ms=dom_ms, dom_flops=dom_flops,
+                achieved=achieved, traffic=traffic, kernels=kernels)
+
+
+def linear_bench(q, synth, idx, steps, warmup, rotate=1):
+    """fwd+bwd of one QLoRA linear; with rotate > 1 the NF4 weight is cycled
+    over that many copies so that it streams from HBM every step."""
+    import torch
+    cfg = synth.CONFIGS[idx]
+    M, K, N, r = cfg.M, cfg.K, cfg.N, cfg.r
+    inp = synth.linear_inputs(cfg, synth.seed_of(idx))
+    cb = torch.from_numpy(synth.nf4_codebook()).cuda()
+    Wd = torch.from_numpy(inp["W0"]).cuda()
+    w = q.nf4_quantize(Wd, cb, dq_group=cfg.dq_group)
+    del Wd
+    A, B = dev_bf16(inp["A"]), dev_bf16(inp["B"])
+    Ls = [q.QLoraLinear(w, A, B, cfg.alpha)]
+    for _ in range(rotate - 1):
+        w2 = q.Nf4Weight(w.codes.clone(), None if w.absmax is None else w.absmax.clone(),
+                         None if w.absmax_q is None else w.absmax_q.clone(),
+                         None if w.absmax_scale is None else w.absmax_scale.clone(), cb, N, K, cfg.dq_group)
+        Ls.append(q.QLoraLinear(w2, A, B, cfg.alpha))
+    X, dY = dev_bf16(inp["X"]), dev_bf16(inp["dY"])
+    Y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    XA = torch.empty(M, r, dtype=torch.float32, device="cuda")
+    dX = torch.empty(M, K, dtype=torch.bfloat16, device="cuda")
+    dA, dB = torch.empty_like(A), torch.empty_like(B)
+    ws = torch.empty(q.qlora_linear_workspace_bytes(Ls[0], M), dtype=torch.uint8, device="cuda")
+
+    def step(i):
+        L = Ls[i % len(Ls)]
+        q.qlora_linear_fwd(L, X, Y=Y, XA=XA, ws=ws)
+        q.qlora_linear_bwd(L, dY, X, XA, dX=dX, dA=dA, dB=dB, ws=ws)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    flops = 4 * M * N * K + 6 * M * r * (N + K)
+    wbytes = N * K // 2 + (N * K // 64) * (1 if cfg.dq_group else 4) + \
+        (4 * (-(-(N * K // 64) // cfg.dq_group)) if cfg.dq_group else 0)
+    # algorithmic bytes: the NF4 weight once per pass; activations, LoRA
+    # parameters and gradients read or written once
+    fwd_bytes = wbytes + 2 * M * K + 2 * r * K + 2 * N * r + 2 * M * N + 4 * M * r
+    bwd_bytes = wbytes + 2 * M * N + 2 * M * K + 4 * M * r + 2 * r * K + 2 * N * r + \
+        2 * M * K + 2 * r * K + 2 * N * r
+    total_bytes = fwd_bytes + bwd_bytes
+    return dict(workload=cfg.name, ms_per_step=ms, tflops=flops / (ms * 1e-3) / 1e12,
+                frac_bf16_peak=flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                tokens_per_s=M / (ms * 1e-3), algorithmic_bytes=total_bytes,
+                hbm_gbs=total_bytes / (ms * 1e-3) / 1e9,
+                frac_hbm_peak=total_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, weight_copies=rotate)
+
+
+def cpu_baseline(synth, target_s):
+    """The oracle (fp64 numpy) on the first tokens of the same MLP workload."""
+    import numpy as np
+    from oracle import nf4 as onf4
+    from oracle import qlora as oq
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # noqa: BLE001
+        cores = os.cpu_count() or 1
+    cfg = synth.CONFIGS[2]
+    cb = synth.nf4_codebook()
+    log("cpu baseline: oracle quantization of the three weights")
+    inp = synth.mlp_inputs(cfg, synth.seed_of(2), M=256)
+    W = {}
+    for k in ("Wg", "Wu", "Wd"):
+        W[k] = onf4.dequantize(onf4.quantize(inp[k], cb, dq_group=cfg.dq_group), cb).astype(np.float64)
+        del inp[k]
+    args = (W["Wg"], W["Wu"], W["Wd"], inp["Ag"], inp["Bg"], inp["Au"], inp["Bu"], inp["Ad"], inp["Bd"])
+
+    def run(m):
+        x, dy = inp_rows["X"][:m], inp_rows["dY"][:m]
+        t = time.perf_counter()
+        f = oq.mlp_forward(x, *args, cfg.alpha)
+        oq.mlp_backward(dy, x, f["G"], f["U"], *args, cfg.alpha)
+        return time.perf_counter() - t
+
+    probe_m = 128
+    inp_rows = synth.mlp_inputs(cfg, synth.seed_of(2), M=probe_m, with_weights=False)
+    t_probe = run(probe_m)
+    m = int(min(cfg.M, max(probe_m, probe_m * target_s / max(t_probe, 1e-3))))
+    m = max(64, (m // 64) * 64)
+    inp_rows = synth.mlp_inputs(cfg, synth.seed_of(2), M=m, with_weights=False)
+    t = run(m)
+    flops = 12 * m * cfg.D * cfg.I + 18 * m * cfg.r * (cfg.D + cfg.I)
+    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": "first %d of %d tokens of %s, fwd+bwd, fp64 numpy oracle (weights dequantized by the "
+                      "oracle), %.1f s" % (m, cfg.M, cfg.name, t),
+            "tokens_per_s": m / t}
+
+
+def main():
+    a = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if a.gpus != 1 or world != 1:
+        print("bench.py measures one MI355X: the QLoRA linear / MLP path here runs on a single GPU "
+              "(data-parallel sharding over tokens is described in DESIGN.md, not launched). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import synth
+    import qlora_fine_tuning_linear_amd as q
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    q.load_library()
+    r = mlp_step_bench(q, synth, a.steps, a.warmup)
+    cfg = r["cfg"]
+    value = r["flops"] / (r["ms"] * 1e-3) / 1e12
+    out = {
+        "metric": "QLoRA fwd+bwd TFLOP/s (SwiGLU MLP block, all three projections QLoRA)",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(r["ms"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "tokens": cfg.M, "hidden": cfg.D, "intermediate": cfg.I,
+                   "lora_rank": cfg.r, "lora_alpha": cfg.alpha, "nf4_block": cfg.blocksize,
+                   "double_quant": bool(cfg.dq_group), "parallelism": "single-gpu"},
+        "tokens_per_s": round(cfg.M / (r["ms"] * 1e-3), 1),
+        "frac_bf16_peak": round(value / BF16_PEAK_TFLOPS, 4),
+        "roofline": {"bound": "mfma", "kernel": "qgemm_" + r["dom"],
+                     "achieved": round(r["achieved"], 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(r["achieved"] / BF16_PEAK_TFLOPS, 4), "traffic": r["traffic"],
+                     "flops_per_launch": r["dom_flops"], "avg_launch_ms": round(r["dom_ms"], 4)},
+        "kernels": {k: {kk: round(vv, 4) for kk, vv in v.items()} for k, v in r["kernels"].items()},
+    }
+    if not a.no_secondary:
+        sec = []
+        for idx, steps, rot in ((1, max(5, a.steps), 1), (4, max(10, a.steps), 4)):
+            log("secondary: %s" % synth.CONFIGS[idx].name)
+            s = linear_bench(q, synth, idx, steps, a.warmup, rotate=rot)
+            sec.append({k: (round(v, 4) if isinstance(v, float) else v) for k, v in s.items()})
+        out["secondary"] = sec
+    out["cpu_baseline"] = None if a.no_cpu_baseline else cpu_baseline(synth, a.cpu_seconds)
+    if out["cpu_baseline"]:
+        out["cpu_baseline"]["value"] = round(out["cpu_baseline"]["value"], 5)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -228,6 +228,21 @@ int qlora_mlp_bwd(const qlora_mlp* P, const void* dY, const void* X,
                   const qlora_mlp_saved* S, int64_t M, void* dX, const qlora_mlp_grads* G_out,
                   void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * qlora_trace_install: optional launch tracing, a profiling aid (off by
+ * default).  While installed, every launch of the dequant-staged GEMM kernel
+ * records the caller-created events begin_events[i] and end_events[i]
+ * (hipEvent_t handles) on its stream immediately before and after itself,
+ * and stores its GEMM kind in kinds[i] (0 forward, 1 gate/up + SwiGLU
+ * forward, 2 backward dX, 3 dH + SwiGLU backward, 4 dual-weight dX), for the
+ * first `capacity` launches; *count is incremented for every launch seen.
+ * Recording an event allocates nothing.  Pass capacity 0 (or NULL arrays)
+ * to uninstall.  Process-wide and not thread-safe: install, run, uninstall
+ * from one host thread.
+ */
+int qlora_trace_install(void** begin_events, void** end_events, int32_t* kinds, int32_t capacity,
+                        int32_t* count);
+
 #ifdef __cplusplus
 }
 #endif

@@ -25,7 +25,7 @@ QLORA_DTYPE_F32 = 1
 EXPORTED = (
     "qlora_abi_version", "qlora_strerror", "nf4_quantize", "nf4_dequantize",
     "qlora_linear_workspace_bytes", "qlora_linear_fwd", "qlora_linear_bwd",
-    "qlora_mlp_workspace_bytes", "qlora_mlp_fwd", "qlora_mlp_bwd",
+    "qlora_mlp_workspace_bytes", "qlora_mlp_fwd", "qlora_mlp_bwd", "qlora_trace_install",
 )
 
 
@@ -89,6 +89,7 @@ def load_library(path: str = LIB_PATH):
         "qlora_mlp_fwd": (ctypes.c_int, [P(CMlp), vp, i64, vp, P(CMlpSaved), vp, sz, vp]),
         "qlora_mlp_bwd": (ctypes.c_int, [P(CMlp), vp, vp, P(CMlpSaved), i64, vp, P(CMlpGrads), vp, sz,
                                          vp]),
+        "qlora_trace_install": (ctypes.c_int, [P(vp), P(vp), P(i32), i32, P(i32)]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -310,3 +311,58 @@ def qlora_mlp_bwd(P: QLoraMlp, dY: torch.Tensor, X: torch.Tensor, saved: MlpSave
                            ctypes.byref(cg), ws.data_ptr(), ws.numel(), _stream(dev))
     _check("qlora_mlp_bwd", st)
     return dX, grads
+
+
+# ------------------------------------------------------------------ tracing
+
+GEMM_KINDS = {0: "fwd", 1: "fwd_swiglu", 2: "bwd_dx", 3: "bwd_dh_swiglu", 4: "bwd_dx_dual"}
+
+
+class LaunchTrace:
+    """qlora_trace_install: HIP-event timing of every GEMM launch on its stream.
+
+    Events are created with hipEventCreate from the HIP runtime that torch
+    already loaded; ``durations()`` returns (kind, milliseconds) per launch.
+    """
+
+    def __init__(self, capacity: int = 4096):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.cap = capacity
+        self.begin = (ctypes.c_void_p * capacity)()
+        self.end = (ctypes.c_void_p * capacity)()
+        for arr in (self.begin, self.end):
+            for i in range(capacity):
+                h = ctypes.c_void_p()
+                if self.hip.hipEventCreate(ctypes.byref(h)) != 0:
+                    raise RuntimeError("hipEventCreate failed")
+                arr[i] = h
+        self.kinds = (ctypes.c_int32 * capacity)()
+        self.count = ctypes.c_int32(0)
+
+    def __enter__(self):
+        self.count.value = 0
+        _check("qlora_trace_install", load_library().qlora_trace_install(
+            self.begin, self.end, self.kinds, self.cap, ctypes.byref(self.count)))
+        return self
+
+    def __exit__(self, *exc):
+        load_library().qlora_trace_install(None, None, None, 0, None)
+        return False
+
+    def durations(self):
+        out = []
+        for i in range(min(self.count.value, self.cap)):
+            ms = ctypes.c_float()
+            if self.hip.hipEventElapsedTime(ctypes.byref(ms), self.begin[i], self.end[i]) != 0:
+                raise RuntimeError("hipEventElapsedTime failed")
+            out.append((GEMM_KINDS.get(self.kinds[i], str(self.kinds[i])), float(ms.value)))
+        return out
+
+    def close(self):
+        for arr in (self.begin, self.end):
+            for h in arr:
+                self.hip.hipEventDestroy(h)

@@ -31,6 +31,32 @@ int check_device() {
 
 inline int hip_status(hipError_t e) { return e == hipSuccess ? QLORA_OK : QLORA_ERR_HIP; }
 
+// Launch tracing (qlora_trace_install): caller-owned event arrays.
+struct Trace {
+  void** begin = nullptr;
+  void** end = nullptr;
+  int32_t* kinds = nullptr;
+  int32_t capacity = 0;
+  int32_t* count = nullptr;
+} g_trace;
+
+hipError_t traced_qgemm(int mode, const GemmArgs& a, const qplan::GemmPlan& pl, hipStream_t st) {
+  int32_t idx = -1;
+  if (g_trace.capacity > 0 && g_trace.count) {
+    idx = (*g_trace.count)++;
+    if (idx < g_trace.capacity) {
+      hipError_t e = hipEventRecord(static_cast<hipEvent_t>(g_trace.begin[idx]), st);
+      if (e != hipSuccess) return e;
+      g_trace.kinds[idx] = mode;
+    } else {
+      idx = -1;
+    }
+  }
+  hipError_t e = launch_qgemm(mode, a, pl, st);
+  if (e == hipSuccess && idx >= 0) e = hipEventRecord(static_cast<hipEvent_t>(g_trace.end[idx]), st);
+  return e;
+}
+
 Nf4Dev to_dev(const qlora_nf4& w) {
   Nf4Dev d;
   d.codes = w.codes;
@@ -75,6 +101,19 @@ char* bytes(void* p) { return static_cast<char*>(p); }
 
 extern "C" {
 
+int qlora_trace_install(void** begin_events, void** end_events, int32_t* kinds, int32_t capacity, int32_t* count) {
+  if (capacity <= 0 || !begin_events || !end_events || !kinds || !count) {
+    g_trace = Trace{};
+    return QLORA_OK;
+  }
+  g_trace.begin = begin_events;
+  g_trace.end = end_events;
+  g_trace.kinds = kinds;
+  g_trace.capacity = capacity;
+  g_trace.count = count;
+  return QLORA_OK;
+}
+
 int nf4_quantize(const float* W, int64_t N, int64_t K, const float* codebook16, int32_t blocksize, int32_t dq_group,
                  uint8_t* codes, float* absmax, uint8_t* absmax_q, float* absmax_scale, void* stream) {
   QTRY(qv_quantize(W, N, K, codebook16, blocksize, dq_group, codes, absmax, absmax_q, absmax_scale));
@@ -117,8 +156,8 @@ int qlora_linear_fwd(const qlora_linear* L, const void* X, int64_t M, void* Y, f
   a.l0 = side_B(*L, XA_saved);
   a.out0 = u16m(Y);
   a.partial = part;
-  QHIP(launch_qgemm(MODE_FWD, a, pl, st));
-  if (pl.splits > 1) QHIP(launch_splitk_finish(part, pl.splits, M, N, a.l0, u16m(Y), st));
+  QHIP(traced_qgemm(MODE_FWD, a, pl, st));
+  if (pl.splits > 1) QHIP(launch_splitk_finish(part, pl.splits, M, N, u16m(Y), st));
   return QLORA_OK;
 }
 
@@ -157,8 +196,8 @@ int qlora_linear_bwd(const qlora_linear* L, const void* dY, const void* X, const
   a.l0 = side_A(*L, T);
   a.out0 = u16m(dX);
   a.partial = part;
-  QHIP(launch_qgemm(MODE_BWD, a, pl, st));
-  if (pl.splits > 1) QHIP(launch_splitk_finish(part, pl.splits, M, K, a.l0, u16m(dX), st));
+  QHIP(traced_qgemm(MODE_BWD, a, pl, st));
+  if (pl.splits > 1) QHIP(launch_splitk_finish(part, pl.splits, M, K, u16m(dX), st));
   // dB = s dY^T XA  ([N, r]);  dA = s T^T X  ([r, K])
   QHIP(launch_lora_grad(0, u16(dY), nullptr, M, N, XA_saved, r, s, qplan::plan_grad_msplits(M, N, r), grad_part, 0,
                         u16m(dB), st));
@@ -196,7 +235,7 @@ int qlora_mlp_fwd(const qlora_mlp* P, const void* X, int64_t M, void* Y, const q
     a.out0 = u16m(S->G);
     a.out1 = u16m(S->U);
     a.out2 = H;
-    QHIP(launch_qgemm(MODE_FWD_SWIGLU, a, qplan::plan_gemm(M, I, D, false), st));
+    QHIP(traced_qgemm(MODE_FWD_SWIGLU, a, qplan::plan_gemm(M, I, D, false), st));
   }
   // HA_d = H A_d^T
   QHIP(launch_lora_down(true, H, M, I, u16(P->down.A), P->down.r, nullptr, 0, S->HA_d, nullptr,
@@ -212,7 +251,7 @@ int qlora_mlp_fwd(const qlora_mlp* P, const void* X, int64_t M, void* Y, const q
     a.codebook = P->down.W0.codebook;
     a.l0 = side_B(P->down, S->HA_d);
     a.out0 = u16m(Y);
-    QHIP(launch_qgemm(MODE_FWD, a, qplan::plan_gemm(M, D, I, false), st));
+    QHIP(traced_qgemm(MODE_FWD, a, qplan::plan_gemm(M, D, I, false), st));
   }
   return QLORA_OK;
 }
@@ -267,7 +306,7 @@ int qlora_mlp_bwd(const qlora_mlp* P, const void* dY, const void* X, const qlora
     a.in1 = u16(S->U);
     a.out0 = dG;
     a.out1 = dU;
-    QHIP(launch_qgemm(MODE_BWD_SWIGLU, a, qplan::plan_gemm(M, I, D, false), st));
+    QHIP(traced_qgemm(MODE_BWD_SWIGLU, a, qplan::plan_gemm(M, I, D, false), st));
   }
   // down-layer LoRA gradients: dB_d = s_d dY^T HA_d, dA_d = s_d Td^T H (H recomputed)
   QHIP(launch_lora_grad(0, u16(dY), nullptr, M, D, S->HA_d, rd, sd, qplan::plan_grad_msplits(M, D, rd), grad_part, 0,
@@ -294,7 +333,7 @@ int qlora_mlp_bwd(const qlora_mlp* P, const void* dY, const void* X, const qlora
     a.l0 = side_A(P->gate, Tg);
     a.l1 = side_A(P->up, Tu);
     a.out0 = u16m(dX);
-    QHIP(launch_qgemm(MODE_BWD_DUAL, a, qplan::plan_gemm(M, D, 2 * I, false), st));
+    QHIP(traced_qgemm(MODE_BWD_DUAL, a, qplan::plan_gemm(M, D, 2 * I, false), st));
   }
   // gate / up LoRA gradients
   QHIP(launch_lora_grad(0, dG, nullptr, M, I, S->XA_g, rg, sg, qplan::plan_grad_msplits(M, I, rg), grad_part, 0,

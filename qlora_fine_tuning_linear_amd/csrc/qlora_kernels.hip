@@ -26,6 +26,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "qlora_device.h"
 #include "qlora_launch.h"
 
@@ -168,20 +170,23 @@ __device__ __forceinline__ int frag_row(int wn, int f) {
   return (wn * FN + f) * 32;
 }
 
-// Forward (non-transposed) fill: LDS row r <- weight row; registers first.
-template <int EPT>
-struct FillFwd {
-  uint32_t c[EPT / 8];
-  float a;
+// Per-thread expansion state of one weight tile: packed codes and the absmax
+// of every weight row the thread expands, loaded one tile before expansion.
+//   forward fill   : one weight row, EPT consecutive elements (one absmax)
+//   transposed fill: RPT weight rows x 8 columns (RPT absmax values)
+template <int NC, int NA>
+struct FillRegs {
+  uint32_t c[NC];
+  float a[NA];
 };
 
-// Transposed fill: LDS row (output column) <- 8 weight columns x RPT rows.
-template <int RPT>
-struct FillTr {
-  uint32_t c[RPT];
-  float a[RPT];
-};
+template <bool DQ>
+__device__ __forceinline__ float absmax_at(const Nf4Dev& w, int64_t blk) {
+  if constexpr (DQ) return (float)w.absmax_q[blk] * w.absmax_scale[blk >> 8];
+  return w.absmax[blk];
+}
 
+// Expand 8 codes of one block into 8 bf16 values (4 packed dwords).
 __device__ __forceinline__ u32x4 deq8(uint32_t c, float a, const float* cb) {
   u32x4 o;
   o[0] = pack_bf16x2(cb[c & 15u] * a, cb[(c >> 4) & 15u] * a);
@@ -191,11 +196,22 @@ __device__ __forceinline__ u32x4 deq8(uint32_t c, float a, const float* cb) {
   return o;
 }
 
-template <int MODE, int WM, int WN, int FM, int FN, bool SPLIT>
+#define SCHED_GROUP(mask, n) __builtin_amdgcn_sched_group_barrier(mask, n, 0)
+#define SG_VALU 0x002
+#define SG_MFMA 0x008
+#define SG_VMEM_READ 0x020
+#define SG_DS_READ 0x100
+#define SG_DS_WRITE 0x200
+
+template <int MODE, int WM, int WN, int FM, int FN, bool SPLIT, bool DQ>
 __global__ __launch_bounds__(WM* WN * 64) void qgemm_kernel(GemmArgs p) {
   using C = TileCfg<WM, WN, FM, FN>;
-  constexpr int NT = C::NT, BM = C::BM, BN = C::BN;
+  constexpr int BM = C::BM, BN = C::BN;
   constexpr bool TR = ModeTraits<MODE>::trans;
+  constexpr int NC = TR ? C::RPT : C::EPT / 8;  // code dwords per thread per tile
+  constexpr int NA = TR ? C::RPT : 1;           // absmax values per thread per tile
+  static_assert(NC == 8 || NC == 4 || NC == 2, "fill shape");
+  using Fill = FillRegs<NC, NA>;
 
   __shared__ __attribute__((aligned(16))) uint16_t lds[2][BN * 64];
   __shared__ float cb[16];
@@ -223,105 +239,119 @@ __global__ __launch_bounds__(WM* WN * 64) void qgemm_kernel(GemmArgs p) {
 
   if (tid < 16) cb[tid] = p.codebook[tid];
 
-  // ---- activation operand: rows of this lane, clamped into [0, M)
+  // ---- activation operand: per-lane row pointers (rows clamped into [0, M))
   int64_t arow[FM];
+  const uint16_t* aptr0[FM];
+  const uint16_t* aptr1[FM];
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
     int64_t r = m0 + (int64_t)(wm * FM + i) * 32 + l32;
     arow[i] = r < p.M ? r : p.M - 1;
+    aptr0[i] = p.act0 + arow[i] * p.Kred0 + 8 * g;
+    aptr1[i] = (p.act1 ? p.act1 + arow[i] * p.Kred1 + 8 * g : aptr0[i]) - p.Kred0;
   }
   auto load_act = [&](int kt, u32x4 (&dst)[FM][4]) {
-    const uint16_t* act = p.act0;
-    int64_t lda = p.Kred0, kk = (int64_t)kt * 64;
-    if (kt >= KT0) {
-      act = p.act1;
-      lda = p.Kred1;
-      kk -= p.Kred0;
+    const bool second = kt >= KT0;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const uint16_t* src = (second ? aptr1[i] : aptr0[i]) + (int64_t)kt * 64;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) dst[i][s] = *reinterpret_cast<const u32x4*>(src + 16 * s);
     }
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-        dst[i][s] = *reinterpret_cast<const u32x4*>(act + arow[i] * lda + kk + 16 * s + 8 * g);
   };
 
-  // ---- weight tile fill
-  FillFwd<C::EPT> ff;
-  FillTr<C::RPT> ft;
-  auto fill_load = [&](int kt) {
+  // ---- weight tile expansion: per-thread source pointers
+  // forward: thread -> (LDS row r, part); weight row clamped into [0, N)
+  // transposed: thread -> (8 output columns kc, RPT reduction rows rg)
+  const int fr = TR ? 0 : tid / C::TPR, fpart = TR ? 0 : tid % C::TPR;
+  constexpr int KC = BN / 8;
+  const int kc = tid % KC, rg = tid / KC;
+  const uint8_t* csrc0;
+  const uint8_t* csrc1;
+  int64_t ablk0, ablk1, cstride0, cstride1, astride0, astride1;
+  {
     if constexpr (!TR) {
-      const int r = tid / C::TPR, part = tid % C::TPR;
-      const Nf4Dev* w = &p.w0;
-      int64_t wrow = n0 + r;
-      if (ModeTraits<MODE>::swiglu_fwd && r >= BN / 2) {
-        w = &p.w1;
-        wrow = n0 + (r - BN / 2);
-      }
-      if (wrow >= w->N) wrow = w->N - 1;
-      const uint8_t* src = w->codes + wrow * (w->K / 2) + (int64_t)kt * 32 + part * (C::EPT / 2);
-      if constexpr (C::EPT == 64) {
-        u32x4 x0 = reinterpret_cast<const u32x4*>(src)[0], x1 = reinterpret_cast<const u32x4*>(src)[1];
-        ff.c[0] = x0[0]; ff.c[1] = x0[1]; ff.c[2] = x0[2]; ff.c[3] = x0[3];
-        ff.c[4] = x1[0]; ff.c[5] = x1[1]; ff.c[6] = x1[2]; ff.c[7] = x1[3];
-      } else if constexpr (C::EPT == 32) {
-        u32x4 x0 = reinterpret_cast<const u32x4*>(src)[0];
-        ff.c[0] = x0[0]; ff.c[1] = x0[1]; ff.c[2] = x0[2]; ff.c[3] = x0[3];
-      } else {
-        u32x2 x0 = reinterpret_cast<const u32x2*>(src)[0];
-        ff.c[0] = x0[0]; ff.c[1] = x0[1];
-      }
-      ff.a = block_absmax(*w, wrow * (w->K / 64) + kt);
+      const Nf4Dev& w = (ModeTraits<MODE>::swiglu_fwd && fr >= BN / 2) ? p.w1 : p.w0;
+      int64_t wrow = n0 + (fr % (ModeTraits<MODE>::swiglu_fwd ? BN / 2 : BN));
+      if (wrow >= w.N) wrow = w.N - 1;
+      csrc0 = csrc1 = w.codes + wrow * (w.K / 2) + fpart * (C::EPT / 2);
+      ablk0 = ablk1 = wrow * (w.K / 64);
+      cstride0 = cstride1 = astride0 = astride1 = 0;
     } else {
-      constexpr int KC = BN / 8;
-      const int kc = tid % KC, rg = tid / KC;
-      const Nf4Dev* w = &p.w0;
-      int64_t nb = (int64_t)kt * 64;
-      if (kt >= KT0) {
-        w = &p.w1;
-        nb -= p.Kred0;
-      }
       int64_t col = n0 + 8 * kc;
-      if (col > w->K - 8) col = w->K - 8;
+      if (col > p.w0.K - 8) col = p.w0.K - 8;
+      csrc0 = p.w0.codes + (int64_t)(rg * C::RPT) * (p.w0.K / 2) + col / 2;
+      ablk0 = (int64_t)(rg * C::RPT) * (p.w0.K / 64) + col / 64;
+      cstride0 = p.w0.K / 2;
+      astride0 = p.w0.K / 64;
+      const Nf4Dev& w1 = p.act1 ? p.w1 : p.w0;
+      csrc1 = w1.codes + (int64_t)(rg * C::RPT) * (w1.K / 2) + col / 2 - (int64_t)KT0 * 64 * (w1.K / 2);
+      ablk1 = (int64_t)(rg * C::RPT) * (w1.K / 64) + col / 64 - (int64_t)KT0 * 64 * (w1.K / 64);
+      cstride1 = w1.K / 2;
+      astride1 = w1.K / 64;
+    }
+  }
+  const Nf4Dev& wsel1 = (TR && p.act1) ? p.w1 : p.w0;
+
+  auto fill_load = [&](int kt, Fill& F) {
+    if constexpr (!TR) {
+      // the SwiGLU forward's second half of the rows reads the up weight
+      const Nf4Dev& w = (ModeTraits<MODE>::swiglu_fwd && fr >= BN / 2) ? p.w1 : p.w0;
+      const uint8_t* src = csrc0 + (int64_t)kt * 32;
+      if constexpr (NC == 8) {
+        const u32x4 x0 = reinterpret_cast<const u32x4*>(src)[0], x1 = reinterpret_cast<const u32x4*>(src)[1];
+        F.c[0] = x0[0]; F.c[1] = x0[1]; F.c[2] = x0[2]; F.c[3] = x0[3];
+        F.c[4] = x1[0]; F.c[5] = x1[1]; F.c[6] = x1[2]; F.c[7] = x1[3];
+      } else if constexpr (NC == 4) {
+        const u32x4 x0 = reinterpret_cast<const u32x4*>(src)[0];
+        F.c[0] = x0[0]; F.c[1] = x0[1]; F.c[2] = x0[2]; F.c[3] = x0[3];
+      } else {
+        const u32x2 x0 = reinterpret_cast<const u32x2*>(src)[0];
+        F.c[0] = x0[0]; F.c[1] = x0[1];
+      }
+      F.a[0] = absmax_at<DQ>(w, ablk0 + kt);
+    } else {
+      const bool second = kt >= KT0;
+      const Nf4Dev& w = second ? wsel1 : p.w0;
+      const uint8_t* src = second ? csrc1 : csrc0;
+      const int64_t cs = second ? cstride1 : cstride0;
+      const int64_t ab = second ? ablk1 : ablk0;
+      const int64_t as = second ? astride1 : astride0;
+      const int64_t row = (int64_t)kt * 64;
 #pragma unroll
       for (int i = 0; i < C::RPT; ++i) {
-        const int64_t wrow = nb + rg * C::RPT + i;
-        ft.c[i] = *reinterpret_cast<const uint32_t*>(w->codes + wrow * (w->K / 2) + col / 2);
-        ft.a[i] = block_absmax(*w, wrow * (w->K / 64) + col / 64);
+        F.c[i] = *reinterpret_cast<const uint32_t*>(src + (row + i) * cs);
+        F.a[i] = absmax_at<DQ>(w, ab + (row + i) * as);
       }
     }
   };
-  auto fill_store = [&](uint16_t* buf) {
+
+  // Expand part `d` (of 8) of the thread's tile into LDS buffer `buf`.
+  auto fill_part = [&](const Fill& F, uint16_t* buf, int d) {
     if constexpr (!TR) {
-      const int r = tid / C::TPR, part = tid % C::TPR;
-#pragma unroll
-      for (int d = 0; d < C::EPT / 8; ++d) {
-        const int chunk = part * (C::EPT / 8) + d;
-        const u32x4 v = deq8(ff.c[d], ff.a, cb);
-        *reinterpret_cast<u32x4*>(buf + r * 64 + ((chunk ^ swz(r)) * 8)) = v;
+      constexpr int PER = NC;  // code dwords = LDS chunks of this thread
+      if (d < PER) {
+        const int chunk = fpart * PER + d;
+        const u32x4 v = deq8(F.c[d], F.a[0], cb);
+        *reinterpret_cast<u32x4*>(buf + fr * 64 + ((chunk ^ swz(fr)) * 8)) = v;
       }
     } else {
-      constexpr int KC = BN / 8;
       constexpr int RPT = C::RPT;
-      const int kc = tid % KC, rg = tid / KC;
       const int n_off = rg * RPT;
       const int chunk = n_off >> 3, sub = n_off & 7;
+      const int c = d;  // output column 8 kc + c
+      float v[RPT];
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        float v[RPT];
-#pragma unroll
-        for (int i = 0; i < RPT; ++i) v[i] = cb[(ft.c[i] >> (4 * c)) & 15u] * ft.a[i];
-        const int row = 8 * kc + c;
-        uint16_t* dst = buf + row * 64 + ((chunk ^ swz(row)) * 8) + sub;
-        if constexpr (RPT == 8) {
-          u32x4 o{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
-                  pack_bf16x2(v[6], v[7])};
-          *reinterpret_cast<u32x4*>(dst) = o;
-        } else if constexpr (RPT == 4) {
-          u32x2 o{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-          *reinterpret_cast<u32x2*>(dst) = o;
-        } else {
-          *reinterpret_cast<uint32_t*>(dst) = pack_bf16x2(v[0], v[1]);
-        }
+      for (int i = 0; i < RPT; ++i) v[i] = cb[(F.c[i] >> (4 * c)) & 15u] * F.a[i];
+      const int row = 8 * kc + c;
+      uint16_t* dst = buf + row * 64 + ((chunk ^ swz(row)) * 8) + sub;
+      if constexpr (RPT == 8) {
+        *reinterpret_cast<u32x4*>(dst) = u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                                               pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
+      } else if constexpr (RPT == 4) {
+        *reinterpret_cast<u32x2*>(dst) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+      } else {
+        *reinterpret_cast<uint32_t*>(dst) = pack_bf16x2(v[0], v[1]);
       }
     }
   };
@@ -334,44 +364,76 @@ __global__ __launch_bounds__(WM* WN * 64) void qgemm_kernel(GemmArgs p) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][f][v] = 0.0f;
 
-  u32x4 actA[FM][4], actB[FM][4];
-  __syncthreads();  // codebook in LDS
-  if (kt_begin < kt_end) {
-    load_act(kt_begin, actA);
-    fill_load(kt_begin);
-    fill_store(lds[kt_begin & 1]);
-  }
-  __syncthreads();
-
-  for (int kt = kt_begin; kt < kt_end; ++kt) {
-    const bool more = kt + 1 < kt_end;
-    if (more) {
-      load_act(kt + 1, actB);
-      fill_load(kt + 1);
+  // MFMAs of one reduction tile from LDS buffer `cur` with activations A.
+  // With a next tile (`nxt` != null): each activation substep slot is
+  // refilled from tile kt_next as soon as its MFMAs have been issued, and the
+  // expansion of the next weight tile (codes F) into `nxt` is spread over the
+  // four substeps, so the vector and LDS work overlaps the matrix cores.
+  auto mma_tile = [&](auto has_next, const uint16_t* cur, u32x4 (&A)[FM][4], int kt_next, const Fill& F,
+                      uint16_t* nxt) {
+    constexpr bool NEXT = decltype(has_next)::value;
+    const uint16_t* asrc[FM];
+    if constexpr (NEXT) {
+      const bool second = kt_next >= KT0;
+#pragma unroll
+      for (int i = 0; i < FM; ++i) asrc[i] = (second ? aptr1[i] : aptr0[i]) + (int64_t)kt_next * 64;
     }
-    const uint16_t* buf = lds[kt & 1];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       u32x4 wa[FN];
 #pragma unroll
       for (int f = 0; f < FN; ++f) {
         const int row = frag_row<MODE, WN, FN>(wn, f) + l32;
-        wa[f] = *reinterpret_cast<const u32x4*>(buf + row * 64 + (((2 * s + g) ^ swz(row)) * 8));
+        wa[f] = *reinterpret_cast<const u32x4*>(cur + row * 64 + (((2 * s + g) ^ swz(row)) * 8));
       }
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int f = 0; f < FN; ++f) acc[i][f] = mfma32(wa[f], actA[i][s], acc[i][f]);
-    }
-    if (more) fill_store(lds[(kt + 1) & 1]);
-    __syncthreads();
-    if (more) {
+        for (int f = 0; f < FN; ++f) acc[i][f] = mfma32(wa[f], A[i][s], acc[i][f]);
+      if constexpr (NEXT) {
+        // refill activation slots in pairs: substeps (0,1) and (2,3) of a row
+        // are one contiguous 64-byte segment, fetched by back-to-back loads
+        if (s & 1) {
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
+          for (int i = 0; i < FM; ++i) {
+            A[i][s - 1] = *reinterpret_cast<const u32x4*>(asrc[i] + 16 * (s - 1));
+            A[i][s] = *reinterpret_cast<const u32x4*>(asrc[i] + 16 * s);
+          }
+          // keep the refill here: sinking it to the end of the tile would
+          // expose its latency at the start of the next tile
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        // this substep's share of the expansion parts
+        constexpr int NP = TR ? 8 : NC;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) actA[i][s] = actB[i][s];
+        for (int d = 0; d < NP; ++d)
+          if (d * 4 / NP == s) fill_part(F, nxt, d);
+      }
     }
+  };
+
+  u32x4 A[FM][4];
+  Fill Fa, Fb;
+  __syncthreads();  // codebook in LDS
+  if (kt_begin < kt_end) {
+    load_act(kt_begin, A);
+    fill_load(kt_begin, Fa);
+#pragma unroll
+    for (int d = 0; d < 8; ++d) fill_part(Fa, lds[kt_begin & 1], d);
+    fill_load(min(kt_begin + 1, kt_end - 1), Fa);
   }
+  __syncthreads();
+
+  // steady state: tile kt computes from LDS while tile kt+1 is expanded into
+  // the other buffer; activations are fetched one tile ahead, codes two.
+  for (int kt = kt_begin; kt + 1 < kt_end; ++kt) {
+    fill_load(min(kt + 2, kt_end - 1), Fb);
+    __builtin_amdgcn_sched_barrier(0);  // issue the code loads first
+    mma_tile(std::true_type{}, lds[kt & 1], A, kt + 1, Fa, lds[(kt + 1) & 1]);
+    __syncthreads();
+    Fa = Fb;
+  }
+  if (kt_begin < kt_end) mma_tile(std::false_type{}, lds[(kt_end - 1) & 1], A, 0, Fa, lds[0]);
 
   // ---- output column of lane-row l32 in frag f, and the LoRA side it uses
   auto out_col = [&](int f) -> int64_t {
@@ -382,25 +444,7 @@ __global__ __launch_bounds__(WM* WN * 64) void qgemm_kernel(GemmArgs p) {
     return n0 + (int64_t)frag_row<MODE, WN, FN>(wn, f);
   };
 
-  if constexpr (SPLIT) {
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      const int64_t m = m0 + (int64_t)(wm * FM + i) * 32 + l32;
-      if (m >= p.M) continue;
-#pragma unroll
-      for (int f = 0; f < FN; ++f) {
-        const int64_t cb0 = out_col(f);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int64_t n = cb0 + 8 * q + 4 * g;
-          if (n >= p.Nout) continue;
-          f32x4 o{acc[i][f][4 * q], acc[i][f][4 * q + 1], acc[i][f][4 * q + 2], acc[i][f][4 * q + 3]};
-          *reinterpret_cast<f32x4*>(p.partial + ((int64_t)blockIdx.y * p.M + m) * p.Nout + n) = o;
-        }
-      }
-    }
-    return;
-  } else {
+  {
     // ---- LoRA epilogue: acc += s * V[m, :] Wl(col, :)^T as extra MFMA steps.
     auto lora = [&](const LoraSide& L, int f_lo, int f_hi) {
       const int steps = (L.r + 15) / 16;
@@ -441,7 +485,27 @@ __global__ __launch_bounds__(WM* WN * 64) void qgemm_kernel(GemmArgs p) {
       lora(p.l0, 0, FN);
       lora(p.l1, 0, FN);
     } else {
-      lora(p.l0, 0, FN);
+      if (!SPLIT || blockIdx.y == 0) lora(p.l0, 0, FN);  // split runs: the LoRA term goes into split 0
+    }
+
+    if constexpr (SPLIT) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int64_t m = m0 + (int64_t)(wm * FM + i) * 32 + l32;
+        if (m >= p.M) continue;
+#pragma unroll
+        for (int f = 0; f < FN; ++f) {
+          const int64_t cb0 = out_col(f);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int64_t n = cb0 + 8 * q + 4 * g;
+            if (n >= p.Nout) continue;
+            f32x4 o{acc[i][f][4 * q], acc[i][f][4 * q + 1], acc[i][f][4 * q + 2], acc[i][f][4 * q + 3]};
+            *reinterpret_cast<f32x4*>(p.partial + ((int64_t)blockIdx.y * p.M + m) * p.Nout + n) = o;
+          }
+        }
+      }
+      return;
     }
 
     // ---- stores
@@ -495,23 +559,15 @@ __global__ __launch_bounds__(WM* WN * 64) void qgemm_kernel(GemmArgs p) {
   }
 }
 
-// Split-reduction finish for the linear GEMMs: out = bf16(sum_z part[z] + LoRA).
-// One thread per 4 consecutive output columns of one token, fixed z order.
+// Split-reduction finish for the linear GEMMs: out = bf16(sum_z part[z]) in
+// split order (split 0 already holds the LoRA term).  4 columns per thread.
 __global__ __launch_bounds__(256) void splitk_finish_kernel(const float* __restrict__ part, int splits,
-                                                            int64_t M, int64_t Nout, LoraSide L,
-                                                            uint16_t* __restrict__ out) {
-  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t per_row = Nout / 4;
-  if (q >= M * per_row) return;
-  const int64_t m = q / per_row, n = (q % per_row) * 4;
-  f32x4 s = {0.f, 0.f, 0.f, 0.f};
-  for (int z = 0; z < splits; ++z) s += *reinterpret_cast<const f32x4*>(part + ((int64_t)z * M + m) * Nout + n);
-  for (int j = 0; j < L.r; ++j) {
-    const float v = L.s * L.V[m * L.r + j];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) s[e] += v * bf16_to_f32(L.Wl[(n + e) * L.wl_sc + (int64_t)j * L.wl_sj]);
-  }
-  *reinterpret_cast<u32x2*>(out + m * Nout + n) = u32x2{pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3])};
+                                                            int64_t MN, uint16_t* __restrict__ out) {
+  const int64_t q = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (q >= MN) return;
+  f32x4 s = *reinterpret_cast<const f32x4*>(part + q);
+  for (int z = 1; z < splits; ++z) s += *reinterpret_cast<const f32x4*>(part + (int64_t)z * MN + q);
+  *reinterpret_cast<u32x2*>(out + q) = u32x2{pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3])};
 }
 
 // ------------------------------------------------------------------------
@@ -751,7 +807,7 @@ hipError_t launch_nf4_dequantize(const Nf4Dev& w, const float* codebook, int out
   return hipGetLastError();
 }
 
-template <int MODE, int WM, int WN, int FM, int FN>
+template <int MODE, int WM, int WN, int FM, int FN, bool DQ>
 static hipError_t run_gemm(GemmArgs a, const qplan::GemmPlan& pl, hipStream_t st) {
   constexpr int NT = WM * WN * 64;
   constexpr int BM = WM * FM * 32;
@@ -762,42 +818,48 @@ static hipError_t run_gemm(GemmArgs a, const qplan::GemmPlan& pl, hipStream_t st
   dim3 grid((unsigned)(a.tiles_m * a.tiles_n), (unsigned)pl.splits);
   if (pl.splits > 1) {
     if constexpr (MODE == MODE_FWD || MODE == MODE_BWD) {
-      qgemm_kernel<MODE, WM, WN, FM, FN, true><<<grid, NT, 0, st>>>(a);
+      qgemm_kernel<MODE, WM, WN, FM, FN, true, DQ><<<grid, NT, 0, st>>>(a);
     } else {
       return hipErrorInvalidValue;
     }
   } else {
-    qgemm_kernel<MODE, WM, WN, FM, FN, false><<<grid, NT, 0, st>>>(a);
+    qgemm_kernel<MODE, WM, WN, FM, FN, false, DQ><<<grid, NT, 0, st>>>(a);
   }
   return hipGetLastError();
 }
 
-template <int MODE>
+template <int MODE, bool DQ>
 static hipError_t run_gemm_cfg(const GemmArgs& a, const qplan::GemmPlan& pl, hipStream_t st) {
-  if (pl.cfg == qplan::CFG_BIG) return run_gemm<MODE, 2, 2, 4, 4>(a, pl, st);
+  if (pl.cfg == qplan::CFG_BIG8) return run_gemm<MODE, 8, 1, 2, 4, DQ>(a, pl, st);
+  if (pl.cfg == qplan::CFG_BIG) return run_gemm<MODE, 2, 2, 4, 4, DQ>(a, pl, st);
   if constexpr (MODE == MODE_FWD_SWIGLU) {
-    return run_gemm<MODE, 1, 2, 2, 2>(a, pl, st);
+    return run_gemm<MODE, 1, 2, 2, 2, DQ>(a, pl, st);
   } else {
-    return run_gemm<MODE, 1, 2, 2, 1>(a, pl, st);
+    return run_gemm<MODE, 1, 2, 2, 1, DQ>(a, pl, st);
   }
+}
+
+template <int MODE>
+static hipError_t run_mode(const GemmArgs& a, const qplan::GemmPlan& pl, hipStream_t st) {
+  return a.w0.dq ? run_gemm_cfg<MODE, true>(a, pl, st) : run_gemm_cfg<MODE, false>(a, pl, st);
 }
 
 hipError_t launch_qgemm(int mode, const GemmArgs& a, const qplan::GemmPlan& pl, hipStream_t st) {
   switch (mode) {
-    case MODE_FWD: return run_gemm_cfg<MODE_FWD>(a, pl, st);
-    case MODE_FWD_SWIGLU: return run_gemm_cfg<MODE_FWD_SWIGLU>(a, pl, st);
-    case MODE_BWD: return run_gemm_cfg<MODE_BWD>(a, pl, st);
-    case MODE_BWD_SWIGLU: return run_gemm_cfg<MODE_BWD_SWIGLU>(a, pl, st);
-    case MODE_BWD_DUAL: return run_gemm_cfg<MODE_BWD_DUAL>(a, pl, st);
+    case MODE_FWD: return run_mode<MODE_FWD>(a, pl, st);
+    case MODE_FWD_SWIGLU: return run_mode<MODE_FWD_SWIGLU>(a, pl, st);
+    case MODE_BWD: return run_mode<MODE_BWD>(a, pl, st);
+    case MODE_BWD_SWIGLU: return run_mode<MODE_BWD_SWIGLU>(a, pl, st);
+    case MODE_BWD_DUAL: return run_mode<MODE_BWD_DUAL>(a, pl, st);
     default: return hipErrorInvalidValue;
   }
 }
 
-hipError_t launch_splitk_finish(const float* part, int splits, int64_t M, int64_t Nout, const LoraSide& L,
-                                uint16_t* out, hipStream_t st) {
-  const int64_t n = M * (Nout / 4);
-  if (n == 0) return hipSuccess;
-  splitk_finish_kernel<<<grid1(n, 256), 256, 0, st>>>(part, splits, M, Nout, L, out);
+hipError_t launch_splitk_finish(const float* part, int splits, int64_t M, int64_t Nout, uint16_t* out,
+                                hipStream_t st) {
+  const int64_t mn = M * Nout;
+  if (mn == 0) return hipSuccess;
+  splitk_finish_kernel<<<grid1(mn / 4, 256), 256, 0, st>>>(part, splits, mn, out);
   return hipGetLastError();
 }
 

@@ -55,8 +55,8 @@ hipError_t launch_nf4_quantize(const float* W, int64_t nblocks, const float* cod
                                float* absmax, uint8_t* absmax_q, float* absmax_scale, hipStream_t st);
 hipError_t launch_nf4_dequantize(const Nf4Dev& w, const float* codebook, int out_f32, void* out, hipStream_t st);
 hipError_t launch_qgemm(int mode, const GemmArgs& a, const qplan::GemmPlan& pl, hipStream_t st);
-hipError_t launch_splitk_finish(const float* part, int splits, int64_t M, int64_t Nout, const LoraSide& L,
-                                uint16_t* out, hipStream_t st);
+hipError_t launch_splitk_finish(const float* part, int splits, int64_t M, int64_t Nout, uint16_t* out,
+                                hipStream_t st);
 hipError_t launch_lora_down(bool aw_rows, const uint16_t* Z, int64_t M, int64_t Kred, const uint16_t* A0, int r0,
                             const uint16_t* A1, int r1, float* V0, float* V1, int splits, float* part,
                             hipStream_t st);

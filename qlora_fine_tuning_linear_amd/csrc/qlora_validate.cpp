@@ -106,6 +106,7 @@ static int check_mlp(const qlora_mlp* P) {
   const int64_t I = P->gate.W0.N, D = P->gate.W0.K;
   if (P->up.W0.N != I || P->up.W0.K != D) return QLORA_ERR_UNSUPPORTED_SHAPE;
   if (P->down.W0.N != D || P->down.W0.K != I) return QLORA_ERR_UNSUPPORTED_SHAPE;
+  if (P->gate.W0.dq_group != P->up.W0.dq_group) return QLORA_ERR_UNSUPPORTED_SHAPE;
   return QLORA_OK;
 }
 

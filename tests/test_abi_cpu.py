@@ -92,9 +92,12 @@ def test_linear_workspace_rule(lib):
     L = linear(N=28672, K=8192, r=16, dq=256)   # skinny M splits the reduction -> needs workspace
     need = lib.qlora_linear_workspace_bytes(ctypes.byref(L), 64)
     assert need > 0
-    assert fwd(lib, L, M=64, wsb=need - 1) == WS_SMALL
+    assert fwd(lib, L, M=64, wsb=16) == WS_SMALL
     assert fwd(lib, L, M=64, ws=None, wsb=need) == INVALID
     assert fwd(lib, L, M=64, ws=FAKE + 4, wsb=need) == MISALIGNED
+    bwd = lambda wsb: lib.qlora_linear_bwd(ctypes.byref(L), FAKE, FAKE, FAKE, 64, FAKE, FAKE, FAKE, FAKE, wsb,
+                                           None)
+    assert bwd(need - 1) == WS_SMALL  # the query returns what the larger (backward) pass needs
 
 
 def test_m_zero_forward_is_a_noop(lib):

@@ -57,6 +57,8 @@ CASES = [
     synth.LinearCfg("m129_640x128_r128", M=129, K=640, N=128, r=128, alpha=32.0, dq_group=0),
     synth.LinearCfg("m100_2048x4160_r8", M=100, K=2048, N=4160, r=8, alpha=16.0, dq_group=256),
     synth.LinearCfg("m520_1024x1088_r24", M=520, K=1024, N=1088, r=24, alpha=8.0, dq_group=0),
+    synth.LinearCfg("m1300_384x448_r16", M=1300, K=384, N=448, r=16, alpha=16.0, dq_group=256),
+    synth.LinearCfg("m2049_192x1216_r40", M=2049, K=192, N=1216, r=40, alpha=20.0, dq_group=0),
 ]
 
 

@@ -51,6 +51,8 @@ SMALL = [
     synth.MlpCfg("m70_d512_i768_r16_dq", M=70, D=512, I=768, r=16, alpha=16.0, dq_group=256),
     synth.MlpCfg("m1_d128_i256_r4", M=1, D=128, I=256, r=4, alpha=8.0, dq_group=0),
     synth.MlpCfg("m513_d256_i384_r64_dq", M=513, D=256, I=384, r=64, alpha=16.0, dq_group=256),
+    synth.MlpCfg("m1100_d320_i448_r16", M=1100, D=320, I=448, r=16, alpha=16.0, dq_group=0),
+    synth.MlpCfg("m1537_d192_i576_r32_dq", M=1537, D=192, I=576, r=32, alpha=32.0, dq_group=256),
 ]
 
 
