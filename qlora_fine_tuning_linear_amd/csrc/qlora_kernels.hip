@@ -203,10 +203,16 @@ __device__ __forceinline__ u32x4 deq8(uint32_t c, float a, const float* cb) {
 #define SG_DS_READ 0x100
 #define SG_DS_WRITE 0x200
 
-template <int MODE, int WM, int WN, int FM, int FN, bool SPLIT, bool DQ>
+// ALDS: activations are staged through LDS.  Each 64-wide reduction tile of
+// the BM token rows is fetched with direct global->LDS loads in whole 128-byte
+// row segments (8 lanes per row), the 16-byte chunk each lane fetches chosen
+// so that the LDS image is the swz()-swizzled [BM][64] layout; the MFMA
+// operands are then read from LDS.  Without ALDS each lane loads its own
+// operand rows straight into registers (fine when the token tile is small).
+template <int MODE, int WM, int WN, int FM, int FN, bool SPLIT, bool DQ, bool ALDS>
 __global__ __launch_bounds__(WM* WN * 64) void qgemm_kernel(GemmArgs p) {
   using C = TileCfg<WM, WN, FM, FN>;
-  constexpr int BM = C::BM, BN = C::BN;
+  constexpr int BM = C::BM, BN = C::BN, NT = C::NT;
   constexpr bool TR = ModeTraits<MODE>::trans;
   constexpr int NC = TR ? C::RPT : C::EPT / 8;  // code dwords per thread per tile
   constexpr int NA = TR ? C::RPT : 1;           // absmax values per thread per tile
@@ -214,6 +220,7 @@ __global__ __launch_bounds__(WM* WN * 64) void qgemm_kernel(GemmArgs p) {
   using Fill = FillRegs<NC, NA>;
 
   __shared__ __attribute__((aligned(16))) uint16_t lds[2][BN * 64];
+  __shared__ __attribute__((aligned(16))) uint16_t alds[ALDS ? 2 : 1][ALDS ? BM * 64 : 8];
   __shared__ float cb[16];
 
   const int tid = threadIdx.x;
@@ -260,6 +267,43 @@ __global__ __launch_bounds__(WM* WN * 64) void qgemm_kernel(GemmArgs p) {
     }
   };
 
+  // ---- ALDS staging: per tile, NI coalesced 16-byte loads per thread into
+  // registers (8 lanes read one 128-byte row segment), written to LDS later
+  // in the tile at the swz()-swizzled position.  Load i of wave w covers rows
+  // (i*W + w)*8 + lane/8, chunk lane%8.  Rows past M are clamped.
+  constexpr int NW = NT / 64;
+  constexpr int NI = ALDS ? BM * 8 / NT : 1;
+  uint32_t soff[NI];  // element offsets of the lane's chunks from the tile's first row
+  int srow[NI];
+  if constexpr (ALDS) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int row = (i * NW + wave) * 8 + (lane >> 3);
+      int r = row;
+      if (m0 + r >= p.M) r = (int)(p.M - 1 - m0);
+      srow[i] = row;
+      soff[i] = (uint32_t)r * (uint32_t)p.Kred0 + (uint32_t)(lane & 7) * 8;
+    }
+  }
+  // the dual-reduction GEMM reads act0 then act1, both with row length Kred0
+  const uint16_t* sbase0 = p.act0 + m0 * p.Kred0;
+  const uint16_t* sbase1 = (p.act1 ? p.act1 + m0 * p.Kred0 : sbase0) - p.Kred0;
+  auto stage_load = [&](int kt, u32x4 (&S)[NI]) {
+    if constexpr (ALDS) {
+      const uint16_t* base = (kt >= KT0 ? sbase1 : sbase0) + (int64_t)kt * 64;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) S[i] = *reinterpret_cast<const u32x4*>(base + soff[i]);
+    }
+  };
+  auto stage_store = [&](const u32x4 (&S)[NI], uint16_t* buf) {
+    if constexpr (ALDS) {
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int row = srow[i];
+        *reinterpret_cast<u32x4*>(buf + row * 64 + (((lane & 7) ^ swz(row)) * 8)) = S[i];
+      }
+    }
+  };
   // ---- weight tile expansion: per-thread source pointers
   // forward: thread -> (LDS row r, part); weight row clamped into [0, N)
   // transposed: thread -> (8 output columns kc, RPT reduction rows rg)
@@ -369,11 +413,12 @@ __global__ __launch_bounds__(WM* WN * 64) void qgemm_kernel(GemmArgs p) {
   // refilled from tile kt_next as soon as its MFMAs have been issued, and the
   // expansion of the next weight tile (codes F) into `nxt` is spread over the
   // four substeps, so the vector and LDS work overlaps the matrix cores.
-  auto mma_tile = [&](auto has_next, const uint16_t* cur, u32x4 (&A)[FM][4], int kt_next, const Fill& F,
-                      uint16_t* nxt) {
+  u32x4 S[NI];
+  auto mma_tile = [&](auto has_next, const uint16_t* cur, const uint16_t* acur, u32x4 (&A)[FM][4], int kt_next,
+                      const Fill& F, uint16_t* nxt, uint16_t* anxt) {
     constexpr bool NEXT = decltype(has_next)::value;
     const uint16_t* asrc[FM];
-    if constexpr (NEXT) {
+    if constexpr (NEXT && !ALDS) {
       const bool second = kt_next >= KT0;
 #pragma unroll
       for (int i = 0; i < FM; ++i) asrc[i] = (second ? aptr1[i] : aptr0[i]) + (int64_t)kt_next * 64;
@@ -386,6 +431,13 @@ __global__ __launch_bounds__(WM* WN * 64) void qgemm_kernel(GemmArgs p) {
         const int row = frag_row<MODE, WN, FN>(wn, f) + l32;
         wa[f] = *reinterpret_cast<const u32x4*>(cur + row * 64 + (((2 * s + g) ^ swz(row)) * 8));
       }
+      if constexpr (ALDS) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+          const int row = (wm * FM + i) * 32 + l32;
+          A[i][s] = *reinterpret_cast<const u32x4*>(acur + row * 64 + (((2 * s + g) ^ swz(row)) * 8));
+        }
+      }
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -393,7 +445,7 @@ __global__ __launch_bounds__(WM* WN * 64) void qgemm_kernel(GemmArgs p) {
       if constexpr (NEXT) {
         // refill activation slots in pairs: substeps (0,1) and (2,3) of a row
         // are one contiguous 64-byte segment, fetched by back-to-back loads
-        if (s & 1) {
+        if (!ALDS && (s & 1)) {
 #pragma unroll
           for (int i = 0; i < FM; ++i) {
             A[i][s - 1] = *reinterpret_cast<const u32x4*>(asrc[i] + 16 * (s - 1));
@@ -408,6 +460,7 @@ __global__ __launch_bounds__(WM* WN * 64) void qgemm_kernel(GemmArgs p) {
 #pragma unroll
         for (int d = 0; d < NP; ++d)
           if (d * 4 / NP == s) fill_part(F, nxt, d);
+        if (ALDS && s == 3) stage_store(S, anxt);  // next tile's activations, loaded at the tile start
       }
     }
   };
@@ -416,7 +469,12 @@ __global__ __launch_bounds__(WM* WN * 64) void qgemm_kernel(GemmArgs p) {
   Fill Fa, Fb;
   __syncthreads();  // codebook in LDS
   if (kt_begin < kt_end) {
-    load_act(kt_begin, A);
+    if constexpr (ALDS) {
+      stage_load(kt_begin, S);
+      stage_store(S, alds[kt_begin & 1]);
+    } else {
+      load_act(kt_begin, A);
+    }
     fill_load(kt_begin, Fa);
 #pragma unroll
     for (int d = 0; d < 8; ++d) fill_part(Fa, lds[kt_begin & 1], d);
@@ -426,14 +484,28 @@ __global__ __launch_bounds__(WM* WN * 64) void qgemm_kernel(GemmArgs p) {
 
   // steady state: tile kt computes from LDS while tile kt+1 is expanded into
   // the other buffer; activations are fetched one tile ahead, codes two.
-  for (int kt = kt_begin; kt + 1 < kt_end; ++kt) {
-    fill_load(min(kt + 2, kt_end - 1), Fb);
-    __builtin_amdgcn_sched_barrier(0);  // issue the code loads first
-    mma_tile(std::true_type{}, lds[kt & 1], A, kt + 1, Fa, lds[(kt + 1) & 1]);
+  // Two code-register sets alternate between consecutive tiles (unrolled by
+  // two), so a prefetch is never copied - a copy would wait for the load.
+  auto step = [&](int kt, const Fill& Fuse, Fill& Fload) {
+    stage_load(kt + 1, S);
+    fill_load(min(kt + 2, kt_end - 1), Fload);
+    __builtin_amdgcn_sched_barrier(0);  // issue the global loads first
+    mma_tile(std::true_type{}, lds[kt & 1], alds[ALDS ? (kt & 1) : 0], A, kt + 1, Fuse, lds[(kt + 1) & 1],
+             alds[ALDS ? ((kt + 1) & 1) : 0]);
     __syncthreads();
-    Fa = Fb;
+  };
+  int kt = kt_begin;
+  for (; kt + 2 < kt_end; kt += 2) {
+    step(kt, Fa, Fb);
+    step(kt + 1, Fb, Fa);
   }
-  if (kt_begin < kt_end) mma_tile(std::false_type{}, lds[(kt_end - 1) & 1], A, 0, Fa, lds[0]);
+  if (kt + 1 < kt_end) {
+    step(kt, Fa, Fb);
+    ++kt;
+  }
+  if (kt_begin < kt_end)
+    mma_tile(std::false_type{}, lds[(kt_end - 1) & 1], alds[ALDS ? ((kt_end - 1) & 1) : 0], A, 0, Fa, lds[0],
+             alds[0]);
 
   // ---- output column of lane-row l32 in frag f, and the LoRA side it uses
   auto out_col = [&](int f) -> int64_t {
@@ -807,7 +879,7 @@ hipError_t launch_nf4_dequantize(const Nf4Dev& w, const float* codebook, int out
   return hipGetLastError();
 }
 
-template <int MODE, int WM, int WN, int FM, int FN, bool DQ>
+template <int MODE, int WM, int WN, int FM, int FN, bool DQ, bool ALDS>
 static hipError_t run_gemm(GemmArgs a, const qplan::GemmPlan& pl, hipStream_t st) {
   constexpr int NT = WM * WN * 64;
   constexpr int BM = WM * FM * 32;
@@ -818,24 +890,23 @@ static hipError_t run_gemm(GemmArgs a, const qplan::GemmPlan& pl, hipStream_t st
   dim3 grid((unsigned)(a.tiles_m * a.tiles_n), (unsigned)pl.splits);
   if (pl.splits > 1) {
     if constexpr (MODE == MODE_FWD || MODE == MODE_BWD) {
-      qgemm_kernel<MODE, WM, WN, FM, FN, true, DQ><<<grid, NT, 0, st>>>(a);
+      qgemm_kernel<MODE, WM, WN, FM, FN, true, DQ, ALDS><<<grid, NT, 0, st>>>(a);
     } else {
       return hipErrorInvalidValue;
     }
   } else {
-    qgemm_kernel<MODE, WM, WN, FM, FN, false, DQ><<<grid, NT, 0, st>>>(a);
+    qgemm_kernel<MODE, WM, WN, FM, FN, false, DQ, ALDS><<<grid, NT, 0, st>>>(a);
   }
   return hipGetLastError();
 }
 
 template <int MODE, bool DQ>
 static hipError_t run_gemm_cfg(const GemmArgs& a, const qplan::GemmPlan& pl, hipStream_t st) {
-  if (pl.cfg == qplan::CFG_BIG8) return run_gemm<MODE, 8, 1, 2, 4, DQ>(a, pl, st);
-  if (pl.cfg == qplan::CFG_BIG) return run_gemm<MODE, 2, 2, 4, 4, DQ>(a, pl, st);
+  if (pl.cfg == qplan::CFG_L256) return run_gemm<MODE, 4, 2, 2, 4, DQ, true>(a, pl, st);
   if constexpr (MODE == MODE_FWD_SWIGLU) {
-    return run_gemm<MODE, 1, 2, 2, 2, DQ>(a, pl, st);
+    return run_gemm<MODE, 1, 2, 2, 2, DQ, false>(a, pl, st);
   } else {
-    return run_gemm<MODE, 1, 2, 2, 1, DQ>(a, pl, st);
+    return run_gemm<MODE, 1, 2, 2, 1, DQ, false>(a, pl, st);
   }
 }
 

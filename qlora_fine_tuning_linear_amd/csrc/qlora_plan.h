@@ -9,11 +9,11 @@
 namespace qplan {
 
 // Tile configurations of the dequant-staged MFMA GEMM (32x32x16 bf16 frags).
-//   BIG8    : 8x1 waves, 2x4 frags per wave -> 512 tokens x 128 output columns
-//             (2 waves per SIMD)
-//   BIG     : 2x2 waves, 4x4 frags per wave -> 256 tokens x 256 output columns
-//   SKINNY  : 1x2 waves, 2x1 frags per wave ->  64 tokens x  64 output columns
-enum GemmCfg { CFG_BIG = 0, CFG_SKINNY = 1, CFG_BIG8 = 2 };
+//   L256    : 4x2 waves, 2x4 frags per wave -> 256 tokens x 256 output columns,
+//             activations staged through LDS (2 waves per SIMD)
+//   SKINNY  : 1x2 waves, 2x1 frags per wave ->  64 tokens x  64 output columns,
+//             activations loaded straight into registers
+enum GemmCfg { CFG_L256 = 0, CFG_SKINNY = 1 };
 
 constexpr int kNumCUs = 256;
 constexpr int64_t kBK = 64;  // reduction tile = one absmax block
@@ -32,9 +32,9 @@ struct GemmPlan {
 // M tokens, Nout output columns, Kred reduction length (multiple of 64).
 inline GemmPlan plan_gemm(int64_t M, int64_t Nout, int64_t Kred, bool allow_split) {
   GemmPlan p{};
-  p.cfg = (M <= 128) ? CFG_SKINNY : (M >= 1024 ? CFG_BIG8 : CFG_BIG);
-  p.bm = (p.cfg == CFG_BIG8) ? 512 : (p.cfg == CFG_BIG) ? 256 : 64;
-  p.bn = (p.cfg == CFG_BIG8) ? 128 : (p.cfg == CFG_BIG) ? 256 : 64;
+  p.cfg = (M <= 128) ? CFG_SKINNY : CFG_L256;
+  p.bm = (p.cfg == CFG_L256) ? 256 : 64;
+  p.bn = (p.cfg == CFG_L256) ? 256 : 64;
   p.tiles_m = cdiv(M, p.bm);
   p.tiles_n = cdiv(Nout, p.bn);
   const int64_t kt = Kred / kBK;
