@@ -102,7 +102,9 @@ typedef struct qlora_linear {
  * SwiGLU MLP block of three QLoRA linears: gate and up map D -> I, down maps
  * I -> D.  Y = down(silu(gate(X)) * up(X)), silu(g) = g / (1 + e^-g)
  * ("MLP SwiGLU" among the hand-derived kernels, "LLM Fine-Tuning in 2026",
- * section 2).  gate and up must have the same r and alpha; down may differ.
+ * section 2).  gate and up must have the same dq_group
+ * (QLORA_ERR_UNSUPPORTED_SHAPE otherwise); r, alpha and the codebook buffer
+ * may differ per layer.
  */
 typedef struct qlora_mlp {
   qlora_linear gate;
@@ -174,7 +176,12 @@ int nf4_quantize(const float* W, int64_t N, int64_t K, const float* codebook16,
  */
 int nf4_dequantize(const qlora_nf4* w, int32_t out_dtype, void* out, void* stream);
 
-/* Workspace bytes the linear forward and backward need for M tokens. */
+/*
+ * Workspace bytes the linear forward and backward need for M tokens.  From
+ * M = 512 tokens on, the GEMMs expand the NF4 weight once per call into a
+ * bf16 copy held in the workspace (N*K*2 bytes) instead of expanding it in
+ * every 256-token tile; below that the expansion happens inside the GEMM.
+ */
 size_t qlora_linear_workspace_bytes(const qlora_linear* L, int64_t M);
 
 /*
@@ -204,7 +211,11 @@ int qlora_linear_bwd(const qlora_linear* L, const void* dY, const void* X,
                      const float* XA_saved, int64_t M, void* dX, void* dA, void* dB,
                      void* ws, size_t ws_bytes, void* stream);
 
-/* Workspace bytes the MLP forward and backward need for M tokens. */
+/*
+ * Workspace bytes the MLP forward and backward need for M tokens (with
+ * M >= 512 this includes a bf16 copy of the expanded weights of one GEMM,
+ * up to 2*I*D*2 bytes, as for the linear layer).
+ */
 size_t qlora_mlp_workspace_bytes(const qlora_mlp* P, int64_t M);
 
 /*
@@ -230,8 +241,8 @@ int qlora_mlp_bwd(const qlora_mlp* P, const void* dY, const void* X,
 
 /*
  * qlora_trace_install: optional launch tracing, a profiling aid (off by
- * default).  While installed, every launch of the dequant-staged GEMM kernel
- * records the caller-created events begin_events[i] and end_events[i]
+ * default).  While installed, every launch of a GEMM kernel (dequant-staged
+ * or bf16-staged) records the caller-created events begin_events[i] and end_events[i]
  * (hipEvent_t handles) on its stream immediately before and after itself,
  * and stores its GEMM kind in kinds[i] (0 forward, 1 gate/up + SwiGLU
  * forward, 2 backward dX, 3 dH + SwiGLU backward, 4 dual-weight dX), for the

@@ -40,7 +40,9 @@ struct Trace {
   int32_t* count = nullptr;
 } g_trace;
 
-hipError_t traced_qgemm(int mode, const GemmArgs& a, const qplan::GemmPlan& pl, hipStream_t st) {
+// One GEMM launch, bracketed by trace events when tracing is installed.
+// bf16: the bf16-staged kernel (the weight already expanded into a.wb).
+hipError_t traced_gemm(int mode, bool bf16, const GemmArgs& a, const qplan::GemmPlan& pl, hipStream_t st) {
   int32_t idx = -1;
   if (g_trace.capacity > 0 && g_trace.count) {
     idx = (*g_trace.count)++;
@@ -52,9 +54,16 @@ hipError_t traced_qgemm(int mode, const GemmArgs& a, const qplan::GemmPlan& pl, 
       idx = -1;
     }
   }
-  hipError_t e = launch_qgemm(mode, a, pl, st);
+  hipError_t e = bf16 ? launch_bgemm(mode, a, st) : launch_qgemm(mode, a, pl, st);
   if (e == hipSuccess && idx >= 0) e = hipEventRecord(static_cast<hipEvent_t>(g_trace.end[idx]), st);
   return e;
+}
+
+hipError_t traced_gemm_q(int mode, const GemmArgs& a, const qplan::GemmPlan& pl, hipStream_t st) {
+  return traced_gemm(mode, false, a, pl, st);
+}
+hipError_t traced_gemm_b(int mode, const GemmArgs& a, hipStream_t st) {
+  return traced_gemm(mode, true, a, qplan::GemmPlan{}, st);
 }
 
 Nf4Dev to_dev(const qlora_nf4& w) {
@@ -156,7 +165,15 @@ int qlora_linear_fwd(const qlora_linear* L, const void* X, int64_t M, void* Y, f
   a.l0 = side_B(*L, XA_saved);
   a.out0 = u16m(Y);
   a.partial = part;
-  QHIP(traced_qgemm(MODE_FWD, a, pl, st));
+  if (qplan::use_bgemm(M)) {
+    uint16_t* wbuf = reinterpret_cast<uint16_t*>(bytes(ws) + w.fwd_part + w.fwd_down);
+    QHIP(launch_dequant_rows(a.w0, nullptr, a.codebook, nullptr, N, wbuf, st));
+    a.wb = wbuf;
+    a.ldw = K;
+    a.wrows = N;
+    return hip_status(traced_gemm_b(MODE_FWD, a, st));
+  }
+  QHIP(traced_gemm_q(MODE_FWD, a, pl, st));
   if (pl.splits > 1) QHIP(launch_splitk_finish(part, pl.splits, M, N, u16m(Y), st));
   return QLORA_OK;
 }
@@ -196,8 +213,18 @@ int qlora_linear_bwd(const qlora_linear* L, const void* dY, const void* X, const
   a.l0 = side_A(*L, T);
   a.out0 = u16m(dX);
   a.partial = part;
-  QHIP(traced_qgemm(MODE_BWD, a, pl, st));
-  if (pl.splits > 1) QHIP(launch_splitk_finish(part, pl.splits, M, K, u16m(dX), st));
+  if (qplan::use_bgemm(M)) {
+    // W0^T expanded to bf16 [K, N]: the reduction over N becomes row-contiguous
+    uint16_t* wbuf = reinterpret_cast<uint16_t*>(base + w.bwd_T + w.bwd_part + w.bwd_down + w.bwd_grad);
+    QHIP(launch_dequant_trans(a.w0, a.codebook, wbuf, N, 0, st));
+    a.wb = wbuf;
+    a.ldw = N;
+    a.wrows = K;
+    QHIP(traced_gemm_b(MODE_BWD, a, st));
+  } else {
+    QHIP(traced_gemm_q(MODE_BWD, a, pl, st));
+    if (pl.splits > 1) QHIP(launch_splitk_finish(part, pl.splits, M, K, u16m(dX), st));
+  }
   // dB = s dY^T XA  ([N, r]);  dA = s T^T X  ([r, K])
   QHIP(launch_lora_grad(0, u16(dY), nullptr, M, N, XA_saved, r, s, qplan::plan_grad_msplits(M, N, r), grad_part, 0,
                         u16m(dB), st));
@@ -216,6 +243,7 @@ int qlora_mlp_fwd(const qlora_mlp* P, const void* X, int64_t M, void* Y, const q
   const qplan::MlpWs w = qplan::mlp_ws(M, D, I, P->gate.r, P->up.r, P->down.r);
   uint16_t* H = reinterpret_cast<uint16_t*>(bytes(ws));
   float* down_part = reinterpret_cast<float*>(bytes(ws) + w.fwd_H);
+  uint16_t* wbuf = w.fwd_wbuf ? reinterpret_cast<uint16_t*>(bytes(ws) + w.fwd_H + w.fwd_down) : nullptr;
 
   // XA_g | XA_u in one pass over X
   QHIP(launch_lora_down(true, u16(X), M, D, u16(P->gate.A), P->gate.r, u16(P->up.A), P->up.r, S->XA_g, S->XA_u,
@@ -230,12 +258,21 @@ int qlora_mlp_fwd(const qlora_mlp* P, const void* X, int64_t M, void* Y, const q
     a.w0 = to_dev(P->gate.W0);
     a.w1 = to_dev(P->up.W0);
     a.codebook = P->gate.W0.codebook;
+    a.codebook1 = P->up.W0.codebook;
     a.l0 = side_B(P->gate, S->XA_g);
     a.l1 = side_B(P->up, S->XA_u);
     a.out0 = u16m(S->G);
     a.out1 = u16m(S->U);
     a.out2 = H;
-    QHIP(traced_qgemm(MODE_FWD_SWIGLU, a, qplan::plan_gemm(M, I, D, false), st));
+    if (wbuf) {
+      QHIP(launch_dequant_rows(a.w0, &a.w1, a.codebook, a.codebook1, qplan::pair_rows(I), wbuf, st));
+      a.wb = wbuf;
+      a.ldw = D;
+      a.wrows = qplan::pair_rows(I);
+      QHIP(traced_gemm_b(MODE_FWD_SWIGLU, a, st));
+    } else {
+      QHIP(traced_gemm_q(MODE_FWD_SWIGLU, a, qplan::plan_gemm(M, I, D, false), st));
+    }
   }
   // HA_d = H A_d^T
   QHIP(launch_lora_down(true, H, M, I, u16(P->down.A), P->down.r, nullptr, 0, S->HA_d, nullptr,
@@ -251,7 +288,15 @@ int qlora_mlp_fwd(const qlora_mlp* P, const void* X, int64_t M, void* Y, const q
     a.codebook = P->down.W0.codebook;
     a.l0 = side_B(P->down, S->HA_d);
     a.out0 = u16m(Y);
-    QHIP(traced_qgemm(MODE_FWD, a, qplan::plan_gemm(M, D, I, false), st));
+    if (wbuf) {
+      QHIP(launch_dequant_rows(a.w0, nullptr, a.codebook, nullptr, D, wbuf, st));
+      a.wb = wbuf;
+      a.ldw = I;
+      a.wrows = D;
+      QHIP(traced_gemm_b(MODE_FWD, a, st));
+    } else {
+      QHIP(traced_gemm_q(MODE_FWD, a, qplan::plan_gemm(M, D, I, false), st));
+    }
   }
   return QLORA_OK;
 }
@@ -288,6 +333,8 @@ int qlora_mlp_bwd(const qlora_mlp* P, const void* dY, const void* X, const qlora
   float* down_part = reinterpret_cast<float*>(b);
   b += w.bwd_down;
   float* grad_part = reinterpret_cast<float*>(b);
+  b += w.bwd_grad;
+  uint16_t* wbuf = w.bwd_wbuf ? reinterpret_cast<uint16_t*>(b) : nullptr;
 
   // Td = dY B_d
   QHIP(launch_lora_down(false, u16(dY), M, D, u16(P->down.B), rd, nullptr, 0, Td, nullptr,
@@ -306,7 +353,16 @@ int qlora_mlp_bwd(const qlora_mlp* P, const void* dY, const void* X, const qlora
     a.in1 = u16(S->U);
     a.out0 = dG;
     a.out1 = dU;
-    QHIP(traced_qgemm(MODE_BWD_SWIGLU, a, qplan::plan_gemm(M, I, D, false), st));
+    if (wbuf) {
+      // W_d^T as bf16 [I, D]
+      QHIP(launch_dequant_trans(a.w0, a.codebook, wbuf, D, 0, st));
+      a.wb = wbuf;
+      a.ldw = D;
+      a.wrows = I;
+      QHIP(traced_gemm_b(MODE_BWD_SWIGLU, a, st));
+    } else {
+      QHIP(traced_gemm_q(MODE_BWD_SWIGLU, a, qplan::plan_gemm(M, I, D, false), st));
+    }
   }
   // down-layer LoRA gradients: dB_d = s_d dY^T HA_d, dA_d = s_d Td^T H (H recomputed)
   QHIP(launch_lora_grad(0, u16(dY), nullptr, M, D, S->HA_d, rd, sd, qplan::plan_grad_msplits(M, D, rd), grad_part, 0,
@@ -330,10 +386,21 @@ int qlora_mlp_bwd(const qlora_mlp* P, const void* dY, const void* X, const qlora
     a.w0 = to_dev(P->gate.W0);
     a.w1 = to_dev(P->up.W0);
     a.codebook = P->gate.W0.codebook;
+    a.codebook1 = P->up.W0.codebook;
     a.l0 = side_A(P->gate, Tg);
     a.l1 = side_A(P->up, Tu);
     a.out0 = u16m(dX);
-    QHIP(traced_qgemm(MODE_BWD_DUAL, a, qplan::plan_gemm(M, D, 2 * I, false), st));
+    if (wbuf) {
+      // [W_g^T | W_u^T] as bf16 [D, 2I]
+      QHIP(launch_dequant_trans(a.w0, a.codebook, wbuf, 2 * I, 0, st));
+      QHIP(launch_dequant_trans(a.w1, a.codebook1, wbuf, 2 * I, I, st));
+      a.wb = wbuf;
+      a.ldw = 2 * I;
+      a.wrows = D;
+      QHIP(traced_gemm_b(MODE_BWD_DUAL, a, st));
+    } else {
+      QHIP(traced_gemm_q(MODE_BWD_DUAL, a, qplan::plan_gemm(M, D, 2 * I, false), st));
+    }
   }
   // gate / up LoRA gradients
   QHIP(launch_lora_grad(0, dG, nullptr, M, I, S->XA_g, rg, sg, qplan::plan_grad_msplits(M, I, rg), grad_part, 0,

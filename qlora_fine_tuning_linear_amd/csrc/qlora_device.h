@@ -4,6 +4,15 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+// Instruction-class masks for __builtin_amdgcn_sched_group_barrier: pin the
+// interleave of matrix, LDS and global instructions in a scheduling region.
+#define SCHED_GROUP(mask, n) __builtin_amdgcn_sched_group_barrier(mask, n, 0)
+#define SG_VALU 0x002
+#define SG_MFMA 0x008
+#define SG_VMEM_READ 0x020
+#define SG_DS_READ 0x100
+#define SG_DS_WRITE 0x200
+
 namespace qk {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -38,6 +47,16 @@ __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
 // 8 lanes that read one chunk column of 8 consecutive rows, and the 8 lanes
 // that write one chunk of rows 8 apart, all hit different bank groups.
 __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 7); }
+
+// Workgroup barrier that orders LDS only: LDS writes before it are complete
+// and visible to the workgroup after it, while global loads issued before it
+// (register prefetches of later tiles) may still be in flight.  A plain
+// __syncthreads() also waits for every outstanding global load.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 
 __device__ __forceinline__ float sigmoidf_(float g) { return 1.0f / (1.0f + __expf(-g)); }
 

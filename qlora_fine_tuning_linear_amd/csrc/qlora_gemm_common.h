@@ -1,0 +1,219 @@
+// Tile geometry, mode traits and the shared epilogue of the MFMA GEMM
+// kernels (the dequant-staged qgemm_kernel and the bf16-staged
+// bgemm_kernel): LoRA term as extra MFMA steps on the accumulators, split
+// partials, and the stores with the SwiGLU forward / backward variants.
+#pragma once
+
+#include "qlora_device.h"
+#include "qlora_launch.h"
+
+namespace qk {
+
+// Absmax of NF4 block `blk`: fp32, or with double quantization the 8-bit code
+// times the fp32 scale of its group of 256 blocks.
+template <bool DQ>
+__device__ __forceinline__ float absmax_at(const Nf4Dev& w, int64_t blk) {
+  if constexpr (DQ) return (float)w.absmax_q[blk] * w.absmax_scale[blk >> 8];
+  return w.absmax[blk];
+}
+
+// Expand 8 codes of one block into 8 bf16 values (4 packed dwords).
+__device__ __forceinline__ u32x4 deq8(uint32_t c, float a, const float* cb) {
+  u32x4 o;
+  o[0] = pack_bf16x2(cb[c & 15u] * a, cb[(c >> 4) & 15u] * a);
+  o[1] = pack_bf16x2(cb[(c >> 8) & 15u] * a, cb[(c >> 12) & 15u] * a);
+  o[2] = pack_bf16x2(cb[(c >> 16) & 15u] * a, cb[(c >> 20) & 15u] * a);
+  o[3] = pack_bf16x2(cb[(c >> 24) & 15u] * a, cb[(c >> 28) & 15u] * a);
+  return o;
+}
+
+template <int MODE>
+struct ModeTraits {
+  static constexpr bool trans = (MODE == MODE_BWD || MODE == MODE_BWD_SWIGLU || MODE == MODE_BWD_DUAL);
+  static constexpr bool swiglu_fwd = (MODE == MODE_FWD_SWIGLU);
+};
+
+template <int WM, int WN, int FM, int FN>
+struct TileCfg {
+  static constexpr int NT = WM * WN * 64;
+  static constexpr int BM = WM * FM * 32;
+  static constexpr int BN = WN * FN * 32;
+  static constexpr int EPT = 64 * BN / NT;  // forward fill: elements per thread
+  static constexpr int TPR = 64 / EPT;      // forward fill: threads per LDS row
+  static constexpr int RPT = 8 * BN / NT;   // transposed fill: weight rows per thread
+};
+
+// LDS row (= output column within the tile) of frag f of wave column wn.
+template <int MODE, int WN, int FN>
+__device__ __forceinline__ int frag_row(int wn, int f) {
+  if (ModeTraits<MODE>::swiglu_fwd) {
+    constexpr int H = FN / 2;
+    constexpr int BNH = WN * H * 32;
+    return (f < H) ? (wn * H + f) * 32 : BNH + (wn * H + (f - H)) * 32;
+  }
+  return (wn * FN + f) * 32;
+}
+
+// Epilogue of one output tile.  acc[i][f]: token frag i (rows
+// m0 + (wm*FM + i)*32 + l32, clamped copy in arow[i]) x output frag f of wave
+// column wn; element v of lane (l32, g) is output column
+// out_col(f) + 8*(v/4) + 4*g + v%4.
+template <int MODE, int WM, int WN, int FM, int FN, bool SPLIT>
+__device__ __forceinline__ void gemm_epilogue(const GemmArgs& p, f32x16 (&acc)[FM][FN], const int64_t (&arow)[FM],
+                                              int64_t m0, int64_t n0, int wm, int wn, int l32, int g) {
+  // ---- output column of lane-row l32 in frag f, and the LoRA side it uses
+  auto out_col = [&](int f) -> int64_t {
+    if (ModeTraits<MODE>::swiglu_fwd) {
+      constexpr int H = FN / 2;
+      return n0 + (int64_t)(wn * H + (f % H)) * 32;
+    }
+    return n0 + (int64_t)frag_row<MODE, WN, FN>(wn, f);
+  };
+
+  {
+    // ---- LoRA epilogue: acc += s * V[m, :] Wl(col, :)^T as extra MFMA steps.
+    auto lora = [&](const LoraSide& L, int f_lo, int f_hi) {
+      const int steps = (L.r + 15) / 16;
+      for (int t = 0; t < steps; ++t) {
+        u32x4 vop[FM];
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+          float x[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int j = 16 * t + 8 * g + e;
+            x[e] = (j < L.r) ? L.s * L.V[arow[i] * L.r + j] : 0.0f;
+          }
+          vop[i] = u32x4{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
+                         pack_bf16x2(x[6], x[7])};
+        }
+#pragma unroll
+        for (int f = 0; f < FN; ++f) {
+          if (f < f_lo || f >= f_hi) continue;
+          int64_t c = out_col(f) + l32;
+          if (c >= p.Nout) c = p.Nout - 1;
+          uint32_t h[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int j = 16 * t + 8 * g + e;
+            h[e] = (j < L.r) ? (uint32_t)L.Wl[c * L.wl_sc + (int64_t)j * L.wl_sj] : 0u;
+          }
+          const u32x4 wop{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+#pragma unroll
+          for (int i = 0; i < FM; ++i) acc[i][f] = mfma32(wop, vop[i], acc[i][f]);
+        }
+      }
+    };
+    if constexpr (MODE == MODE_FWD_SWIGLU) {
+      lora(p.l0, 0, FN / 2);
+      lora(p.l1, FN / 2, FN);
+    } else if constexpr (MODE == MODE_BWD_DUAL) {
+      lora(p.l0, 0, FN);
+      lora(p.l1, 0, FN);
+    } else {
+      if (!SPLIT || blockIdx.y == 0) lora(p.l0, 0, FN);  // split runs: the LoRA term goes into split 0
+    }
+
+    if constexpr (SPLIT) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int64_t m = m0 + (int64_t)(wm * FM + i) * 32 + l32;
+        if (m >= p.M) continue;
+#pragma unroll
+        for (int f = 0; f < FN; ++f) {
+          const int64_t cb0 = out_col(f);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int64_t n = cb0 + 8 * q + 4 * g;
+            if (n >= p.Nout) continue;
+            f32x4 o{acc[i][f][4 * q], acc[i][f][4 * q + 1], acc[i][f][4 * q + 2], acc[i][f][4 * q + 3]};
+            *reinterpret_cast<f32x4*>(p.partial + ((int64_t)blockIdx.y * p.M + m) * p.Nout + n) = o;
+          }
+        }
+      }
+      return;
+    }
+
+    // ---- SwiGLU backward: per token frag, every G / U load of the frag is
+    // issued before any of them is used (one memory latency per frag, not
+    // one per 4-column group); columns past Nout load a clamped address and
+    // are not stored.
+    if constexpr (MODE == MODE_BWD_SWIGLU) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int64_t m = m0 + (int64_t)(wm * FM + i) * 32 + l32;
+        const int64_t mr = arow[i];
+        u32x2 gg[FN][4], uu[FN][4];
+#pragma unroll
+        for (int f = 0; f < FN; ++f)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            int64_t n = out_col(f) + 8 * q + 4 * g;
+            if (n >= p.Nout) n = p.Nout - 4;
+            gg[f][q] = *reinterpret_cast<const u32x2*>(p.in0 + mr * p.Nout + n);
+            uu[f][q] = *reinterpret_cast<const u32x2*>(p.in1 + mr * p.Nout + n);
+          }
+        if (m >= p.M) continue;
+#pragma unroll
+        for (int f = 0; f < FN; ++f)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int64_t n = out_col(f) + 8 * q + 4 * g;
+            if (n >= p.Nout) continue;
+            const int64_t off = m * p.Nout + n;
+            const float G[4] = {bf16_lo(gg[f][q][0]), bf16_hi(gg[f][q][0]), bf16_lo(gg[f][q][1]),
+                                bf16_hi(gg[f][q][1])};
+            const float U[4] = {bf16_lo(uu[f][q][0]), bf16_hi(uu[f][q][0]), bf16_lo(uu[f][q][1]),
+                                bf16_hi(uu[f][q][1])};
+            float dG[4], dU[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float dH = acc[i][f][4 * q + e];
+              const float sg = sigmoidf_(G[e]);
+              dU[e] = dH * G[e] * sg;
+              dG[e] = dH * U[e] * sg * (1.0f + G[e] * (1.0f - sg));
+            }
+            *reinterpret_cast<u32x2*>(p.out0 + off) = u32x2{pack_bf16x2(dG[0], dG[1]), pack_bf16x2(dG[2], dG[3])};
+            *reinterpret_cast<u32x2*>(p.out1 + off) = u32x2{pack_bf16x2(dU[0], dU[1]), pack_bf16x2(dU[2], dU[3])};
+          }
+      }
+      return;
+    }
+
+    // ---- stores
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int64_t m = m0 + (int64_t)(wm * FM + i) * 32 + l32;
+      if (m >= p.M) continue;
+      constexpr int FO = ModeTraits<MODE>::swiglu_fwd ? FN / 2 : FN;
+#pragma unroll
+      for (int f = 0; f < FO; ++f) {
+        const int64_t cb0 = out_col(f);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int64_t n = cb0 + 8 * q + 4 * g;
+          if (n >= p.Nout) continue;
+          const int64_t off = m * p.Nout + n;
+          if constexpr (MODE == MODE_FWD_SWIGLU) {
+            float G[4], U[4], H[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              G[e] = acc[i][f][4 * q + e];
+              U[e] = acc[i][f + FN / 2][4 * q + e];
+              H[e] = G[e] * sigmoidf_(G[e]) * U[e];
+            }
+            *reinterpret_cast<u32x2*>(p.out0 + off) = u32x2{pack_bf16x2(G[0], G[1]), pack_bf16x2(G[2], G[3])};
+            *reinterpret_cast<u32x2*>(p.out1 + off) = u32x2{pack_bf16x2(U[0], U[1]), pack_bf16x2(U[2], U[3])};
+            *reinterpret_cast<u32x2*>(p.out2 + off) = u32x2{pack_bf16x2(H[0], H[1]), pack_bf16x2(H[2], H[3])};
+          } else {
+            const f32x16& a = acc[i][f];
+            *reinterpret_cast<u32x2*>(p.out0 + off) =
+                u32x2{pack_bf16x2(a[4 * q], a[4 * q + 1]), pack_bf16x2(a[4 * q + 2], a[4 * q + 3])};
+          }
+        }
+      }
+    }
+  }
+}
+
+}  // namespace qk

@@ -29,6 +29,7 @@
 #include <type_traits>
 
 #include "qlora_device.h"
+#include "qlora_gemm_common.h"
 #include "qlora_launch.h"
 
 namespace qk {
@@ -143,33 +144,6 @@ __global__ __launch_bounds__(256) void nf4_dequantize_kernel(Nf4Dev w, const flo
 // LDS weight tile: [BN rows][64 reduction values] bf16, rows = output columns,
 // 16-byte chunks XOR-swizzled by swz(row); two buffers.
 // ------------------------------------------------------------------------
-template <int MODE>
-struct ModeTraits {
-  static constexpr bool trans = (MODE == MODE_BWD || MODE == MODE_BWD_SWIGLU || MODE == MODE_BWD_DUAL);
-  static constexpr bool swiglu_fwd = (MODE == MODE_FWD_SWIGLU);
-};
-
-template <int WM, int WN, int FM, int FN>
-struct TileCfg {
-  static constexpr int NT = WM * WN * 64;
-  static constexpr int BM = WM * FM * 32;
-  static constexpr int BN = WN * FN * 32;
-  static constexpr int EPT = 64 * BN / NT;  // forward fill: elements per thread
-  static constexpr int TPR = 64 / EPT;      // forward fill: threads per LDS row
-  static constexpr int RPT = 8 * BN / NT;   // transposed fill: weight rows per thread
-};
-
-// LDS row (= output column within the tile) of frag f of wave column wn.
-template <int MODE, int WN, int FN>
-__device__ __forceinline__ int frag_row(int wn, int f) {
-  if (ModeTraits<MODE>::swiglu_fwd) {
-    constexpr int H = FN / 2;
-    constexpr int BNH = WN * H * 32;
-    return (f < H) ? (wn * H + f) * 32 : BNH + (wn * H + (f - H)) * 32;
-  }
-  return (wn * FN + f) * 32;
-}
-
 // Per-thread expansion state of one weight tile: packed codes and the absmax
 // of every weight row the thread expands, loaded one tile before expansion.
 //   forward fill   : one weight row, EPT consecutive elements (one absmax)
@@ -178,30 +152,9 @@ template <int NC, int NA>
 struct FillRegs {
   uint32_t c[NC];
   float a[NA];
+  int cbo;  // transposed fill: codebook of the tile (0: w0, 16: w1)
 };
 
-template <bool DQ>
-__device__ __forceinline__ float absmax_at(const Nf4Dev& w, int64_t blk) {
-  if constexpr (DQ) return (float)w.absmax_q[blk] * w.absmax_scale[blk >> 8];
-  return w.absmax[blk];
-}
-
-// Expand 8 codes of one block into 8 bf16 values (4 packed dwords).
-__device__ __forceinline__ u32x4 deq8(uint32_t c, float a, const float* cb) {
-  u32x4 o;
-  o[0] = pack_bf16x2(cb[c & 15u] * a, cb[(c >> 4) & 15u] * a);
-  o[1] = pack_bf16x2(cb[(c >> 8) & 15u] * a, cb[(c >> 12) & 15u] * a);
-  o[2] = pack_bf16x2(cb[(c >> 16) & 15u] * a, cb[(c >> 20) & 15u] * a);
-  o[3] = pack_bf16x2(cb[(c >> 24) & 15u] * a, cb[(c >> 28) & 15u] * a);
-  return o;
-}
-
-#define SCHED_GROUP(mask, n) __builtin_amdgcn_sched_group_barrier(mask, n, 0)
-#define SG_VALU 0x002
-#define SG_MFMA 0x008
-#define SG_VMEM_READ 0x020
-#define SG_DS_READ 0x100
-#define SG_DS_WRITE 0x200
 
 // ALDS: activations are staged through LDS.  Each 64-wide reduction tile of
 // the BM token rows is fetched with direct global->LDS loads in whole 128-byte
@@ -221,7 +174,7 @@ __global__ __launch_bounds__(WM* WN * 64) void qgemm_kernel(GemmArgs p) {
 
   __shared__ __attribute__((aligned(16))) uint16_t lds[2][BN * 64];
   __shared__ __attribute__((aligned(16))) uint16_t alds[ALDS ? 2 : 1][ALDS ? BM * 64 : 8];
-  __shared__ float cb[16];
+  __shared__ float cb[32];  // [0, 16): table of w0, [16, 32): table of w1
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -244,7 +197,7 @@ __global__ __launch_bounds__(WM* WN * 64) void qgemm_kernel(GemmArgs p) {
     kt_end = min(KT, kt_begin + p.ktiles_per_split);
   }
 
-  if (tid < 16) cb[tid] = p.codebook[tid];
+  if (tid < 32) cb[tid] = (tid < 16 || !p.codebook1) ? p.codebook[tid & 15] : p.codebook1[tid & 15];
 
   // ---- activation operand: per-lane row pointers (rows clamped into [0, M))
   int64_t arow[FM];
@@ -354,6 +307,7 @@ __global__ __launch_bounds__(WM* WN * 64) void qgemm_kernel(GemmArgs p) {
         F.c[0] = x0[0]; F.c[1] = x0[1];
       }
       F.a[0] = absmax_at<DQ>(w, ablk0 + kt);
+      F.cbo = 0;
     } else {
       const bool second = kt >= KT0;
       const Nf4Dev& w = second ? wsel1 : p.w0;
@@ -362,6 +316,7 @@ __global__ __launch_bounds__(WM* WN * 64) void qgemm_kernel(GemmArgs p) {
       const int64_t ab = second ? ablk1 : ablk0;
       const int64_t as = second ? astride1 : astride0;
       const int64_t row = (int64_t)kt * 64;
+      F.cbo = second ? 16 : 0;
 #pragma unroll
       for (int i = 0; i < C::RPT; ++i) {
         F.c[i] = *reinterpret_cast<const uint32_t*>(src + (row + i) * cs);
@@ -376,7 +331,7 @@ __global__ __launch_bounds__(WM* WN * 64) void qgemm_kernel(GemmArgs p) {
       constexpr int PER = NC;  // code dwords = LDS chunks of this thread
       if (d < PER) {
         const int chunk = fpart * PER + d;
-        const u32x4 v = deq8(F.c[d], F.a[0], cb);
+        const u32x4 v = deq8(F.c[d], F.a[0], (ModeTraits<MODE>::swiglu_fwd && fr >= BN / 2) ? cb + 16 : cb);
         *reinterpret_cast<u32x4*>(buf + fr * 64 + ((chunk ^ swz(fr)) * 8)) = v;
       }
     } else {
@@ -385,8 +340,9 @@ __global__ __launch_bounds__(WM* WN * 64) void qgemm_kernel(GemmArgs p) {
       const int chunk = n_off >> 3, sub = n_off & 7;
       const int c = d;  // output column 8 kc + c
       float v[RPT];
+      const float* tcb = cb + F.cbo;
 #pragma unroll
-      for (int i = 0; i < RPT; ++i) v[i] = cb[(F.c[i] >> (4 * c)) & 15u] * F.a[i];
+      for (int i = 0; i < RPT; ++i) v[i] = tcb[(F.c[i] >> (4 * c)) & 15u] * F.a[i];
       const int row = 8 * kc + c;
       uint16_t* dst = buf + row * 64 + ((chunk ^ swz(row)) * 8) + sub;
       if constexpr (RPT == 8) {
@@ -492,7 +448,7 @@ __global__ __launch_bounds__(WM* WN * 64) void qgemm_kernel(GemmArgs p) {
     __builtin_amdgcn_sched_barrier(0);  // issue the global loads first
     mma_tile(std::true_type{}, lds[kt & 1], alds[ALDS ? (kt & 1) : 0], A, kt + 1, Fuse, lds[(kt + 1) & 1],
              alds[ALDS ? ((kt + 1) & 1) : 0]);
-    __syncthreads();
+    lds_barrier();  // global prefetches stay in flight across it
   };
   int kt = kt_begin;
   for (; kt + 2 < kt_end; kt += 2) {
@@ -507,128 +463,7 @@ __global__ __launch_bounds__(WM* WN * 64) void qgemm_kernel(GemmArgs p) {
     mma_tile(std::false_type{}, lds[(kt_end - 1) & 1], alds[ALDS ? ((kt_end - 1) & 1) : 0], A, 0, Fa, lds[0],
              alds[0]);
 
-  // ---- output column of lane-row l32 in frag f, and the LoRA side it uses
-  auto out_col = [&](int f) -> int64_t {
-    if (ModeTraits<MODE>::swiglu_fwd) {
-      constexpr int H = FN / 2;
-      return n0 + (int64_t)(wn * H + (f % H)) * 32;
-    }
-    return n0 + (int64_t)frag_row<MODE, WN, FN>(wn, f);
-  };
-
-  {
-    // ---- LoRA epilogue: acc += s * V[m, :] Wl(col, :)^T as extra MFMA steps.
-    auto lora = [&](const LoraSide& L, int f_lo, int f_hi) {
-      const int steps = (L.r + 15) / 16;
-      for (int t = 0; t < steps; ++t) {
-        u32x4 vop[FM];
-#pragma unroll
-        for (int i = 0; i < FM; ++i) {
-          float x[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int j = 16 * t + 8 * g + e;
-            x[e] = (j < L.r) ? L.s * L.V[arow[i] * L.r + j] : 0.0f;
-          }
-          vop[i] = u32x4{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
-                         pack_bf16x2(x[6], x[7])};
-        }
-#pragma unroll
-        for (int f = 0; f < FN; ++f) {
-          if (f < f_lo || f >= f_hi) continue;
-          int64_t c = out_col(f) + l32;
-          if (c >= p.Nout) c = p.Nout - 1;
-          uint32_t h[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int j = 16 * t + 8 * g + e;
-            h[e] = (j < L.r) ? (uint32_t)L.Wl[c * L.wl_sc + (int64_t)j * L.wl_sj] : 0u;
-          }
-          const u32x4 wop{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
-#pragma unroll
-          for (int i = 0; i < FM; ++i) acc[i][f] = mfma32(wop, vop[i], acc[i][f]);
-        }
-      }
-    };
-    if constexpr (MODE == MODE_FWD_SWIGLU) {
-      lora(p.l0, 0, FN / 2);
-      lora(p.l1, FN / 2, FN);
-    } else if constexpr (MODE == MODE_BWD_DUAL) {
-      lora(p.l0, 0, FN);
-      lora(p.l1, 0, FN);
-    } else {
-      if (!SPLIT || blockIdx.y == 0) lora(p.l0, 0, FN);  // split runs: the LoRA term goes into split 0
-    }
-
-    if constexpr (SPLIT) {
-#pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const int64_t m = m0 + (int64_t)(wm * FM + i) * 32 + l32;
-        if (m >= p.M) continue;
-#pragma unroll
-        for (int f = 0; f < FN; ++f) {
-          const int64_t cb0 = out_col(f);
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int64_t n = cb0 + 8 * q + 4 * g;
-            if (n >= p.Nout) continue;
-            f32x4 o{acc[i][f][4 * q], acc[i][f][4 * q + 1], acc[i][f][4 * q + 2], acc[i][f][4 * q + 3]};
-            *reinterpret_cast<f32x4*>(p.partial + ((int64_t)blockIdx.y * p.M + m) * p.Nout + n) = o;
-          }
-        }
-      }
-      return;
-    }
-
-    // ---- stores
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      const int64_t m = m0 + (int64_t)(wm * FM + i) * 32 + l32;
-      if (m >= p.M) continue;
-      constexpr int FO = ModeTraits<MODE>::swiglu_fwd ? FN / 2 : FN;
-#pragma unroll
-      for (int f = 0; f < FO; ++f) {
-        const int64_t cb0 = out_col(f);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int64_t n = cb0 + 8 * q + 4 * g;
-          if (n >= p.Nout) continue;
-          const int64_t off = m * p.Nout + n;
-          if constexpr (MODE == MODE_FWD_SWIGLU) {
-            float G[4], U[4], H[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              G[e] = acc[i][f][4 * q + e];
-              U[e] = acc[i][f + FN / 2][4 * q + e];
-              H[e] = G[e] * sigmoidf_(G[e]) * U[e];
-            }
-            *reinterpret_cast<u32x2*>(p.out0 + off) = u32x2{pack_bf16x2(G[0], G[1]), pack_bf16x2(G[2], G[3])};
-            *reinterpret_cast<u32x2*>(p.out1 + off) = u32x2{pack_bf16x2(U[0], U[1]), pack_bf16x2(U[2], U[3])};
-            *reinterpret_cast<u32x2*>(p.out2 + off) = u32x2{pack_bf16x2(H[0], H[1]), pack_bf16x2(H[2], H[3])};
-          } else if constexpr (MODE == MODE_BWD_SWIGLU) {
-            const u32x2 gg = *reinterpret_cast<const u32x2*>(p.in0 + off);
-            const u32x2 uu = *reinterpret_cast<const u32x2*>(p.in1 + off);
-            const float G[4] = {bf16_lo(gg[0]), bf16_hi(gg[0]), bf16_lo(gg[1]), bf16_hi(gg[1])};
-            const float U[4] = {bf16_lo(uu[0]), bf16_hi(uu[0]), bf16_lo(uu[1]), bf16_hi(uu[1])};
-            float dG[4], dU[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const float dH = acc[i][f][4 * q + e];
-              const float sg = sigmoidf_(G[e]);
-              dU[e] = dH * G[e] * sg;
-              dG[e] = dH * U[e] * sg * (1.0f + G[e] * (1.0f - sg));
-            }
-            *reinterpret_cast<u32x2*>(p.out0 + off) = u32x2{pack_bf16x2(dG[0], dG[1]), pack_bf16x2(dG[2], dG[3])};
-            *reinterpret_cast<u32x2*>(p.out1 + off) = u32x2{pack_bf16x2(dU[0], dU[1]), pack_bf16x2(dU[2], dU[3])};
-          } else {
-            const f32x16& a = acc[i][f];
-            *reinterpret_cast<u32x2*>(p.out0 + off) =
-                u32x2{pack_bf16x2(a[4 * q], a[4 * q + 1]), pack_bf16x2(a[4 * q + 2], a[4 * q + 3])};
-          }
-        }
-      }
-    }
-  }
+  gemm_epilogue<MODE, WM, WN, FM, FN, SPLIT>(p, acc, arow, m0, n0, wm, wn, l32, g);
 }
 
 // Split-reduction finish for the linear GEMMs: out = bf16(sum_z part[z]) in

@@ -39,7 +39,8 @@ struct GemmArgs {
   const uint16_t* act1;
   int64_t M, Nout, Kred0, Kred1;
   Nf4Dev w0, w1;
-  const float* codebook;
+  const float* codebook;   // table of w0
+  const float* codebook1;  // table of w1 (dual-weight modes)
   LoraSide l0, l1;
   uint16_t* out0;
   uint16_t* out1;
@@ -49,12 +50,26 @@ struct GemmArgs {
   float* partial;
   int64_t tiles_m, tiles_n;
   int32_t ktiles_per_split;
+  // bgemm_kernel: the weight operand as bf16 rows (row = output column,
+  // contiguous along the reduction), row stride ldw, rows [0, wrows) valid
+  const uint16_t* wb;
+  int64_t ldw, wrows;
 };
 
 hipError_t launch_nf4_quantize(const float* W, int64_t nblocks, const float* codebook, int dq, uint8_t* codes,
                                float* absmax, uint8_t* absmax_q, float* absmax_scale, hipStream_t st);
 hipError_t launch_nf4_dequantize(const Nf4Dev& w, const float* codebook, int out_f32, void* out, hipStream_t st);
 hipError_t launch_qgemm(int mode, const GemmArgs& a, const qplan::GemmPlan& pl, hipStream_t st);
+hipError_t launch_bgemm(int mode, const GemmArgs& a, hipStream_t st);
+// bf16 copy of the dequantized weight(s) for bgemm_kernel.
+//   rows : out[R, 0:K] = deq(W)[src(R), :]; with w1 (SwiGLU pair) rows come in
+//          blocks of 256 = 128 gate rows then the 128 up rows of the same
+//          columns (rows past N are zero), else src(R) = R.
+//   trans: out[k, col0 + n] = deq(W)[n, k] (row stride ldo).
+hipError_t launch_dequant_rows(const Nf4Dev& w0, const Nf4Dev* w1, const float* codebook0, const float* codebook1,
+                               int64_t rows_out, uint16_t* out, hipStream_t st);
+hipError_t launch_dequant_trans(const Nf4Dev& w, const float* codebook, uint16_t* out, int64_t ldo, int64_t col0,
+                                hipStream_t st);
 hipError_t launch_splitk_finish(const float* part, int splits, int64_t M, int64_t Nout, uint16_t* out,
                                 hipStream_t st);
 hipError_t launch_lora_down(bool aw_rows, const uint16_t* Z, int64_t M, int64_t Kred, const uint16_t* A0, int r0,

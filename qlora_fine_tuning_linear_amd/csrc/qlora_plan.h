@@ -77,30 +77,41 @@ inline int plan_grad_msplits(int64_t M, int64_t P, int r) {
   return (int)(s < 1 ? 1 : s);
 }
 
+// Token count from which a GEMM runs as "expand the NF4 weight once into a
+// bf16 workspace, then bf16 GEMM" (bgemm) instead of expanding it inside
+// every 256-token tile (qgemm).
+constexpr int64_t kBgemmMinTokens = 512;
+inline bool use_bgemm(int64_t M) { return M >= kBgemmMinTokens; }
+// Rows of the bf16 gate|up workspace: blocks of 128 gate rows + 128 up rows.
+inline int64_t pair_rows(int64_t I) { return 256 * cdiv(I, 128); }
+
 struct LinearWs {
   size_t fwd_part, fwd_down;             // forward: split-K partials, down-proj partials
   size_t bwd_T, bwd_part, bwd_down, bwd_grad;
+  size_t wbuf;                           // bf16 weight copy (bgemm only), at the end
   size_t fwd_total, bwd_total, total;
 };
 
 inline LinearWs linear_ws(int64_t M, int64_t N, int64_t K, int r) {
   LinearWs w{};
+  const bool bg = use_bgemm(M);
   GemmPlan pf = plan_gemm(M, N, K, true);
-  w.fwd_part = pf.splits > 1 ? align256((size_t)pf.splits * M * N * 4) : 0;
+  w.fwd_part = (!bg && pf.splits > 1) ? align256((size_t)pf.splits * M * N * 4) : 0;
   const int ds = plan_down_splits(M, K);
   w.fwd_down = ds > 1 ? align256((size_t)ds * M * r * 4) : 0;
-  w.fwd_total = w.fwd_part + w.fwd_down;
+  w.wbuf = bg ? align256((size_t)N * K * 2) : 0;
+  w.fwd_total = w.fwd_part + w.fwd_down + w.wbuf;
 
   GemmPlan pb = plan_gemm(M, K, N, true);
   w.bwd_T = align256((size_t)M * r * 4);
-  w.bwd_part = pb.splits > 1 ? align256((size_t)pb.splits * M * K * 4) : 0;
+  w.bwd_part = (!bg && pb.splits > 1) ? align256((size_t)pb.splits * M * K * 4) : 0;
   const int ts = plan_down_splits(M, N);
   w.bwd_down = ts > 1 ? align256((size_t)ts * M * r * 4) : 0;
   const int gs_b = plan_grad_msplits(M, N, r);
   const int gs_a = plan_grad_msplits(M, K, r);
   size_t gb = align256((size_t)gs_b * N * r * 4), ga = align256((size_t)gs_a * K * r * 4);
   w.bwd_grad = gb > ga ? gb : ga;
-  w.bwd_total = w.bwd_T + w.bwd_part + w.bwd_down + w.bwd_grad;
+  w.bwd_total = w.bwd_T + w.bwd_part + w.bwd_down + w.bwd_grad + w.wbuf;
   w.total = w.fwd_total > w.bwd_total ? w.fwd_total : w.bwd_total;
   if (w.total == 0) w.total = 256;
   return w;
@@ -109,6 +120,7 @@ inline LinearWs linear_ws(int64_t M, int64_t N, int64_t K, int r) {
 struct MlpWs {
   size_t fwd_H, fwd_down;                            // H bf16 [M, I], down-proj partials
   size_t bwd_Td, bwd_dG, bwd_dU, bwd_Tg, bwd_Tu, bwd_down, bwd_grad;
+  size_t fwd_wbuf, bwd_wbuf;                         // bf16 weight copies (bgemm only), at the end
   size_t fwd_total, bwd_total, total;
 };
 
@@ -121,7 +133,12 @@ inline MlpWs mlp_ws(int64_t M, int64_t D, int64_t I, int rg, int ru, int rd) {
   size_t d1 = s1 > 1 ? align256((size_t)s1 * M * (rg + ru) * 4) : 0;
   size_t d2 = s2 > 1 ? align256((size_t)s2 * M * rd * 4) : 0;
   w.fwd_down = d1 > d2 ? d1 : d2;
-  w.fwd_total = w.fwd_H + w.fwd_down;
+  if (use_bgemm(M)) {
+    const size_t gu = (size_t)pair_rows(I) * D * 2, dn = (size_t)D * I * 2;
+    w.fwd_wbuf = align256(gu > dn ? gu : dn);
+    w.bwd_wbuf = align256((size_t)2 * I * D * 2);
+  }
+  w.fwd_total = w.fwd_H + w.fwd_down + w.fwd_wbuf;
 
   w.bwd_Td = align256((size_t)M * rd * 4);
   w.bwd_dG = align256((size_t)M * I * 2);
@@ -141,7 +158,7 @@ inline MlpWs mlp_ws(int64_t M, int64_t D, int64_t I, int rg, int ru, int rd) {
     if (b > g) g = b;
   }
   w.bwd_grad = g;
-  w.bwd_total = w.bwd_Td + w.bwd_dG + w.bwd_dU + w.bwd_Tg + w.bwd_Tu + w.bwd_down + w.bwd_grad;
+  w.bwd_total = w.bwd_Td + w.bwd_dG + w.bwd_dU + w.bwd_Tg + w.bwd_Tu + w.bwd_down + w.bwd_grad + w.bwd_wbuf;
   w.total = w.fwd_total > w.bwd_total ? w.fwd_total : w.bwd_total;
   if (w.total == 0) w.total = 256;
   return w;
