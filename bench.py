@@ -38,6 +38,12 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0, help="target oracle work for the CPU baseline")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="first run one plain device-to-device copy of this many MiB (the known-size kernel "
+                         "that calibrates the FETCH_SIZE / WRITE_SIZE counters)")
+    ap.add_argument("--summarize-traffic", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_MIB"),
+                    help="no GPU: turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, "
+                         "WRITE_SIZE) of a --copy-probe-mib run into profiles/traffic_<kernel>.txt")
     return ap.parse_args()
 
 
@@ -60,10 +66,10 @@ def kernel_source_sha():
     return h.hexdigest()[:16]
 
 
-def stored_traffic(kind):
+def stored_traffic(key):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it
     was taken on the current kernel sources (else None)."""
-    path = os.path.join(ROOT, "profiles", "traffic_%s.txt" % kind)
+    path = os.path.join(ROOT, "profiles", "traffic_%s.txt" % key)
     if not os.path.exists(path):
         return None
     try:
@@ -73,6 +79,66 @@ def stored_traffic(kind):
     if rec.get("source_sha") != kernel_source_sha():
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+KIND_OF_MODE = {0: "fwd", 1: "fwd_swiglu", 2: "bwd_dx", 3: "bwd_dh_swiglu", 4: "bwd_dx_dual"}
+
+
+def kernel_key(csv_name):
+    """'void qk::bgemm_kernel<1>(GemmArgs)' -> 'bgemm_fwd_swiglu' (None for other kernels)."""
+    import re
+    m = re.search(r"\b([qb]gemm)_kernel<(\d+)", csv_name)
+    return None if not m else "%s_%s" % (m.group(1), KIND_OF_MODE[int(m.group(2))])
+
+
+def summarize_traffic(fetch_csv, write_csv, copy_mib, command):
+    """Per-launch HBM bytes of every GEMM kernel in a profiled bench run.
+
+    FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are scaled by what they read
+    for the plain copy of copy_mib MiB in the same run (the copy moves exactly
+    that many bytes each way); the factors are recorded with the result."""
+    import csv
+    import statistics
+
+    def per_kernel(path, counter):
+        vals = {}
+        for row in csv.DictReader(open(path)):
+            if row["Counter_Name"] != counter:
+                continue
+            vals.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
+        return vals
+
+    f = per_kernel(fetch_csv, "FETCH_SIZE")
+    w = per_kernel(write_csv, "WRITE_SIZE")
+    copy_kib = copy_mib * 1024.0
+
+    def calib(vals):
+        c = [v for k, vs in vals.items() if "copyBuffer" in k or "copy" in k.lower() for v in vs
+             if v > 0.5 * copy_kib]
+        if not c:
+            raise SystemExit("no copy dispatch of about %d MiB in the counter file" % copy_mib)
+        return copy_kib / statistics.median(c)
+
+    cf, cw = calib(f), calib(w)
+    sha = kernel_source_sha()
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    written = []
+    for name in sorted(set(f) & set(w)):
+        key = kernel_key(name)
+        if key is None:
+            continue
+        fk, wk = statistics.median(f[name]), statistics.median(w[name])
+        rec = {"kernel": name, "launches": len(f[name]), "fetch_kib_per_launch": fk, "write_kib_per_launch": wk,
+               "copy_probe_mib": copy_mib, "calib_fetch": cf, "calib_write": cw,
+               "hbm_bytes_per_launch": int(round((fk * cf + wk * cw) * 1024)), "source_sha": sha}
+        path = os.path.join(ROOT, "profiles", "traffic_%s.txt" % key)
+        with open(path, "w") as fh:
+            fh.write("# HBM traffic per launch of %s (median over launches), from two rocprofv3 --pmc runs\n" % name)
+            fh.write("# of the command below (FETCH_SIZE, then WRITE_SIZE), each scaled by the counter value\n")
+            fh.write("# of the %d MiB plain copy in the same run.\n# command: %s\n" % (copy_mib, command))
+            fh.write(json.dumps(rec, indent=1) + "\n")
+        written.append(path)
+    return written
 
 
 def gemm_flops(kind, M, D, I, r):
@@ -132,21 +198,23 @@ def mlp_step_bench(q, synth, steps, warmup):
         torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = e0.elapsed_time(e1) / steps
-    per_kind = {}
-    for kind, d in trace.durations():
+    per_kind, kname = {}, {}
+    for kind, kernel, d in trace.launches():
         per_kind.setdefault(kind, []).append(d)
+        kname[kind] = kernel
     trace.close()
     flops = 12 * M * D * I + 18 * M * r * (D + I)
     dom = max(per_kind, key=lambda k: sum(per_kind[k]))
     dom_ms = sum(per_kind[dom]) / len(per_kind[dom])
     dom_flops = gemm_flops(dom, M, D, I, r)
     achieved = dom_flops / (dom_ms * 1e-3) / 1e12
-    traffic = stored_traffic(dom)
-    kernels = {k: {"launches_per_step": len(v) / steps, "avg_ms": sum(v) / len(v),
-                   "tflops": gemm_flops(k, M, D, I, r) / (sum(v) / len(v) * 1e-3) / 1e12}
+    dom_kernel = "%s<%s>" % (kname[dom], dom)
+    traffic = stored_traffic("%s_%s" % (kname[dom].split("_")[0], dom))
+    kernels = {"%s<%s>" % (kname[k], k): {"launches_per_step": len(v) / steps, "avg_ms": sum(v) / len(v),
+                                          "tflops": gemm_flops(k, M, D, I, r) / (sum(v) / len(v) * 1e-3) / 1e12}
                for k, v in per_kind.items()}
-    return dict(cfg=cfg, ms=ms, wall=wall, flops=flops, dom=dom, dom_ms=dom_ms, dom_flops=dom_flops,
-                achieved=achieved, traffic=traffic, kernels=kernels)
+    return dict(cfg=cfg, ms=ms, wall=wall, flops=flops, dom=dom, dom_kernel=dom_kernel, dom_ms=dom_ms,
+                dom_flops=dom_flops, achieved=achieved, traffic=traffic, kernels=kernels)
 
 
 def linear_bench(q, synth, idx, steps, warmup, rotate=1):
@@ -248,6 +316,12 @@ def cpu_baseline(synth, target_s):
 
 def main():
     a = parse()
+    if a.summarize_traffic:
+        fetch_csv, write_csv, mib = a.summarize_traffic
+        cmd = os.environ.get("TRAFFIC_COMMAND", "(see the profiles README)")
+        for p in summarize_traffic(fetch_csv, write_csv, int(mib), cmd):
+            print(p)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if a.gpus != 1 or world != 1:
         print("bench.py measures one MI355X: the QLoRA linear / MLP path here runs on a single GPU "
@@ -261,6 +335,13 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     q.load_library()
+    if a.copy_probe_mib > 0:
+        n = a.copy_probe_mib * (1 << 20) // 2
+        src = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     r = mlp_step_bench(q, synth, a.steps, a.warmup)
     cfg = r["cfg"]
     value = r["flops"] / (r["ms"] * 1e-3) / 1e12
@@ -282,7 +363,7 @@ def main():
                    "double_quant": bool(cfg.dq_group), "parallelism": "single-gpu"},
         "tokens_per_s": round(cfg.M / (r["ms"] * 1e-3), 1),
         "frac_bf16_peak": round(value / BF16_PEAK_TFLOPS, 4),
-        "roofline": {"bound": "mfma", "kernel": "qgemm_" + r["dom"],
+        "roofline": {"bound": "mfma", "kernel": r["dom_kernel"],
                      "achieved": round(r["achieved"], 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(r["achieved"] / BF16_PEAK_TFLOPS, 4), "traffic": r["traffic"],
                      "flops_per_launch": r["dom_flops"], "avg_launch_ms": round(r["dom_ms"], 4)},

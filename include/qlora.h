@@ -245,7 +245,8 @@ int qlora_mlp_bwd(const qlora_mlp* P, const void* dY, const void* X,
  * or bf16-staged) records the caller-created events begin_events[i] and end_events[i]
  * (hipEvent_t handles) on its stream immediately before and after itself,
  * and stores its GEMM kind in kinds[i] (0 forward, 1 gate/up + SwiGLU
- * forward, 2 backward dX, 3 dH + SwiGLU backward, 4 dual-weight dX), for the
+ * forward, 2 backward dX, 3 dH + SwiGLU backward, 4 dual-weight dX; plus 8
+ * when the bf16-staged kernel ran, i.e. from 512 tokens on), for the
  * first `capacity` launches; *count is incremented for every launch seen.
  * Recording an event allocates nothing.  Pass capacity 0 (or NULL arrays)
  * to uninstall.  Process-wide and not thread-safe: install, run, uninstall

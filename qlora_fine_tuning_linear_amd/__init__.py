@@ -316,6 +316,9 @@ def qlora_mlp_bwd(P: QLoraMlp, dY: torch.Tensor, X: torch.Tensor, saved: MlpSave
 # ------------------------------------------------------------------ tracing
 
 GEMM_KINDS = {0: "fwd", 1: "fwd_swiglu", 2: "bwd_dx", 3: "bwd_dh_swiglu", 4: "bwd_dx_dual"}
+# trace kind = GEMM kind + 8 when the bf16-staged kernel (bgemm_kernel) ran
+GEMM_KERNELS = {k: "qgemm_kernel" for k in GEMM_KINDS}
+GEMM_KERNELS.update({k + 8: "bgemm_kernel" for k in GEMM_KINDS})
 
 
 class LaunchTrace:
@@ -359,8 +362,13 @@ class LaunchTrace:
             ms = ctypes.c_float()
             if self.hip.hipEventElapsedTime(ctypes.byref(ms), self.begin[i], self.end[i]) != 0:
                 raise RuntimeError("hipEventElapsedTime failed")
-            out.append((GEMM_KINDS.get(self.kinds[i], str(self.kinds[i])), float(ms.value)))
+            out.append((GEMM_KINDS.get(self.kinds[i] & 7, str(self.kinds[i])), float(ms.value)))
         return out
+
+    def launches(self):
+        """(kind, kernel name, milliseconds) per traced GEMM launch."""
+        return [(kind, GEMM_KERNELS.get(self.kinds[i], "?"), ms)
+                for i, (kind, ms) in enumerate(self.durations())]
 
     def close(self):
         for arr in (self.begin, self.end):

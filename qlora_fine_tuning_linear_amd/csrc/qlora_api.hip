@@ -49,7 +49,7 @@ hipError_t traced_gemm(int mode, bool bf16, const GemmArgs& a, const qplan::Gemm
     if (idx < g_trace.capacity) {
       hipError_t e = hipEventRecord(static_cast<hipEvent_t>(g_trace.begin[idx]), st);
       if (e != hipSuccess) return e;
-      g_trace.kinds[idx] = mode;
+      g_trace.kinds[idx] = mode + (bf16 ? 8 : 0);
     } else {
       idx = -1;
     }
