@@ -151,7 +151,7 @@ int qlora_linear_fwd(const qlora_linear* L, const void* X, int64_t M, void* Y, f
   float* down_part = reinterpret_cast<float*>(bytes(ws) + w.fwd_part);
 
   // XA = X A^T (kept for the backward)
-  QHIP(launch_lora_down(true, u16(X), M, K, u16(L->A), L->r, nullptr, 0, XA_saved, nullptr,
+  QHIP(launch_lora_down(u16(X), M, K, u16(L->A), L->r, nullptr, 0, XA_saved, nullptr,
                         qplan::plan_down_splits(M, K), down_part, st));
   // Y = X W0^T + s XA B^T
   const qplan::GemmPlan pl = qplan::plan_gemm(M, N, K, true);
@@ -194,13 +194,15 @@ int qlora_linear_bwd(const qlora_linear* L, const void* dY, const void* X, const
   const qplan::LinearWs w = qplan::linear_ws(M, N, K, r);
   char* base = bytes(ws);
   float* T = reinterpret_cast<float*>(base);
-  float* part = reinterpret_cast<float*>(base + w.bwd_T);
-  float* down_part = reinterpret_cast<float*>(base + w.bwd_T + w.bwd_part);
-  float* grad_part = reinterpret_cast<float*>(base + w.bwd_T + w.bwd_part + w.bwd_down);
+  uint16_t* BT = reinterpret_cast<uint16_t*>(base + w.bwd_T);
+  char* after_bt = base + w.bwd_T + w.bwd_BT;
+  float* part = reinterpret_cast<float*>(after_bt);
+  float* down_part = reinterpret_cast<float*>(after_bt + w.bwd_part);
+  float* grad_part = reinterpret_cast<float*>(after_bt + w.bwd_part + w.bwd_down);
 
-  // T = dY B
-  QHIP(launch_lora_down(false, u16(dY), M, N, u16(L->B), r, nullptr, 0, T, nullptr, qplan::plan_down_splits(M, N),
-                        down_part, st));
+  // T = dY B  (B^T first, so that the product reads rows)
+  QHIP(launch_transpose_rn(u16(L->B), N, r, BT, st));
+  QHIP(launch_lora_down(u16(dY), M, N, BT, r, nullptr, 0, T, nullptr, qplan::plan_down_splits(M, N), down_part, st));
   // dX = dY W0 + s T A
   const qplan::GemmPlan pl = qplan::plan_gemm(M, K, N, true);
   GemmArgs a = gemm_args();
@@ -215,7 +217,7 @@ int qlora_linear_bwd(const qlora_linear* L, const void* dY, const void* X, const
   a.partial = part;
   if (qplan::use_bgemm(M)) {
     // W0^T expanded to bf16 [K, N]: the reduction over N becomes row-contiguous
-    uint16_t* wbuf = reinterpret_cast<uint16_t*>(base + w.bwd_T + w.bwd_part + w.bwd_down + w.bwd_grad);
+    uint16_t* wbuf = reinterpret_cast<uint16_t*>(after_bt + w.bwd_part + w.bwd_down + w.bwd_grad);
     QHIP(launch_dequant_trans(a.w0, a.codebook, wbuf, N, 0, st));
     a.wb = wbuf;
     a.ldw = N;
@@ -246,7 +248,7 @@ int qlora_mlp_fwd(const qlora_mlp* P, const void* X, int64_t M, void* Y, const q
   uint16_t* wbuf = w.fwd_wbuf ? reinterpret_cast<uint16_t*>(bytes(ws) + w.fwd_H + w.fwd_down) : nullptr;
 
   // XA_g | XA_u in one pass over X
-  QHIP(launch_lora_down(true, u16(X), M, D, u16(P->gate.A), P->gate.r, u16(P->up.A), P->up.r, S->XA_g, S->XA_u,
+  QHIP(launch_lora_down(u16(X), M, D, u16(P->gate.A), P->gate.r, u16(P->up.A), P->up.r, S->XA_g, S->XA_u,
                         qplan::plan_down_splits(M, D), down_part, st));
   // G, U = gate/up(X) and H = silu(G) * U in one dual GEMM
   {
@@ -275,7 +277,7 @@ int qlora_mlp_fwd(const qlora_mlp* P, const void* X, int64_t M, void* Y, const q
     }
   }
   // HA_d = H A_d^T
-  QHIP(launch_lora_down(true, H, M, I, u16(P->down.A), P->down.r, nullptr, 0, S->HA_d, nullptr,
+  QHIP(launch_lora_down(H, M, I, u16(P->down.A), P->down.r, nullptr, 0, S->HA_d, nullptr,
                         qplan::plan_down_splits(M, I), down_part, st));
   // Y = H W_d^T + s_d HA_d B_d^T
   {
@@ -330,6 +332,11 @@ int qlora_mlp_bwd(const qlora_mlp* P, const void* dY, const void* X, const qlora
   b += w.bwd_Tg;
   float* Tu = reinterpret_cast<float*>(b);
   b += w.bwd_Tu;
+  uint16_t* BdT = reinterpret_cast<uint16_t*>(b);
+  uint16_t* BgT = reinterpret_cast<uint16_t*>(b + qplan::align256((size_t)rd * D * 2));
+  uint16_t* BuT = reinterpret_cast<uint16_t*>(b + qplan::align256((size_t)rd * D * 2) +
+                                              qplan::align256((size_t)rg * I * 2));
+  b += w.bwd_BT;
   float* down_part = reinterpret_cast<float*>(b);
   b += w.bwd_down;
   float* grad_part = reinterpret_cast<float*>(b);
@@ -337,8 +344,11 @@ int qlora_mlp_bwd(const qlora_mlp* P, const void* dY, const void* X, const qlora
   uint16_t* wbuf = w.bwd_wbuf ? reinterpret_cast<uint16_t*>(b) : nullptr;
 
   // Td = dY B_d
-  QHIP(launch_lora_down(false, u16(dY), M, D, u16(P->down.B), rd, nullptr, 0, Td, nullptr,
-                        qplan::plan_down_splits(M, D), down_part, st));
+  QHIP(launch_transpose_rn(u16(P->down.B), D, rd, BdT, st));
+  QHIP(launch_transpose_rn(u16(P->gate.B), I, rg, BgT, st));
+  QHIP(launch_transpose_rn(u16(P->up.B), I, ru, BuT, st));
+  QHIP(launch_lora_down(u16(dY), M, D, BdT, rd, nullptr, 0, Td, nullptr, qplan::plan_down_splits(M, D), down_part,
+                        st));
   // dH = dY W_d + s_d Td A_d, with the SwiGLU backward in the epilogue -> dG, dU
   {
     GemmArgs a = gemm_args();
@@ -370,10 +380,8 @@ int qlora_mlp_bwd(const qlora_mlp* P, const void* dY, const void* X, const qlora
   QHIP(launch_lora_grad(1, u16(S->G), u16(S->U), M, I, Td, rd, sd, qplan::plan_grad_msplits(M, I, rd), grad_part, 1,
                         u16m(G->dA_d), st));
   // Tg = dG B_g, Tu = dU B_u
-  QHIP(launch_lora_down(false, dG, M, I, u16(P->gate.B), rg, nullptr, 0, Tg, nullptr, qplan::plan_down_splits(M, I),
-                        down_part, st));
-  QHIP(launch_lora_down(false, dU, M, I, u16(P->up.B), ru, nullptr, 0, Tu, nullptr, qplan::plan_down_splits(M, I),
-                        down_part, st));
+  QHIP(launch_lora_down(dG, M, I, BgT, rg, nullptr, 0, Tg, nullptr, qplan::plan_down_splits(M, I), down_part, st));
+  QHIP(launch_lora_down(dU, M, I, BuT, ru, nullptr, 0, Tu, nullptr, qplan::plan_down_splits(M, I), down_part, st));
   // dX = dG W_g + dU W_u + s_g Tg A_g + s_u Tu A_u  (one GEMM, reduction over 2I)
   {
     GemmArgs a = gemm_args();

@@ -60,4 +60,8 @@ __device__ __forceinline__ void lds_barrier() {
 
 __device__ __forceinline__ float sigmoidf_(float g) { return 1.0f / (1.0f + __expf(-g)); }
 
+// sigmoid with the hardware reciprocal (v_rcp_f32, about 1 ulp) instead of
+// the correctly rounded division: for values that are rounded to bf16 next.
+__device__ __forceinline__ float sigmoid_fast(float g) { return __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
+
 }  // namespace qk

@@ -478,81 +478,113 @@ __global__ __launch_bounds__(256) void splitk_finish_kernel(const float* __restr
 }
 
 // ------------------------------------------------------------------------
-// LoRA down-projection V[M, r] = Z[M, K] Aw^T on the matrix cores.
-//   AW_ROWS: Aw is [r, K] (rows = j)            -> V = Z A^T   (XA, HA_d)
-//   else   : Aw is [K, r] (Aw = B, K = N)       -> V = Z B     (T = dY B)
-// Workgroup: 32 tokens, 4 waves dealing the k16 steps round-robin; the four
-// partials are summed in LDS in wave order.  blockIdx.y = reduction split.
-// Two outputs (for gate | up) when V1 != null: columns [0, r0) from A0 into
-// V0 and [r0, r0 + r1) from A1 into V1.
+// LoRA down-projection V[M, j] = sum_k Z[M, k] W[j, k] on the matrix cores,
+// for the rank-r products X A^T, H A_d^T and (with W = B^T) dY B.  W rows
+// j < r0 come from W0 into V0, rows r0 <= j < r0 + r1 from W1 into V1 (gate |
+// up share one pass over Z).  Both W are [r, Kred] bf16, rows contiguous.
+//
+// Workgroup: 32 tokens, 8 waves taking the 64-wide reduction chunks of their
+// split in turn (consecutive chunks stream side by side).  Within a chunk
+// lane (token l32, half h) loads the 64 contiguous bytes k0 + 32h .. +31 of
+// its token row, and the W lane (row l32 of the frag, half h) the same
+// columns of its row: MFMA step t multiplies columns k0 + 32h + 8t + e, a
+// permutation of the chunk shared by both operands.  The next chunk's loads
+// are issued before the current chunk's MFMAs.  The 8 wave partials are
+// summed in LDS in wave order; with several splits (blockIdx.y) the sums go
+// to part[split][M][r0 + r1] for down_finish_kernel.
 // ------------------------------------------------------------------------
-template <bool AW_ROWS>
-__global__ __launch_bounds__(256) void lora_down_kernel(const uint16_t* __restrict__ Z, int64_t M, int64_t Kred,
-                                                        const uint16_t* __restrict__ A0, int r0,
-                                                        const uint16_t* __restrict__ A1, int r1,
+template <int JF>
+__global__ __launch_bounds__(512) void lora_down_kernel(const uint16_t* __restrict__ Z, int64_t M, int64_t Kred,
+                                                        const uint16_t* __restrict__ W0, int r0,
+                                                        const uint16_t* __restrict__ W1, int r1,
                                                         float* __restrict__ V0, float* __restrict__ V1,
-                                                        int64_t k_per_split, float* __restrict__ part) {
-  __shared__ float red[4][4 * 16 * 64];
+                                                        int64_t chunks_per_split, float* __restrict__ part) {
+  __shared__ float red[8][JF * 16 * 64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int l32 = lane & 31, g = lane >> 5;
+  const int l32 = lane & 31, h = lane >> 5;
   const int rt = r0 + r1;
-  const int JF = (rt + 31) / 32;
   const int64_t m0 = (int64_t)blockIdx.x * 32;
-  int64_t m = m0 + l32;
-  if (m >= M) m = M - 1;
-  const int64_t kb = (int64_t)blockIdx.y * k_per_split;
-  const int64_t ke = min(Kred, kb + k_per_split);
-
-  f32x16 acc[4];
+  const int64_t m = (m0 + l32 < M) ? m0 + l32 : M - 1;
+  const uint16_t* zrow = Z + m * Kred + 32 * h;
+  const uint16_t* wrow[JF];
+  bool wok[JF];
 #pragma unroll
-  for (int jf = 0; jf < 4; ++jf)
+  for (int jf = 0; jf < JF; ++jf) {
+    const int j = 32 * jf + l32;
+    wok[jf] = j < rt;
+    wrow[jf] = (j < r0 ? W0 + (int64_t)j * Kred : W1 + (int64_t)(j - r0) * Kred) + 32 * h;
+    if (!wok[jf]) wrow[jf] = zrow;  // any valid address; the operand is zeroed
+  }
+  const int64_t C = Kred / 64;
+  const int64_t cb = (int64_t)blockIdx.y * chunks_per_split;
+  const int64_t ce = (cb + chunks_per_split < C) ? cb + chunks_per_split : C;
+
+  f32x16 acc[JF];
+#pragma unroll
+  for (int jf = 0; jf < JF; ++jf)
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[jf][v] = 0.0f;
 
-  for (int64_t k = kb + 16 * wave; k < ke; k += 64) {
-    const u32x4 zb = *reinterpret_cast<const u32x4*>(Z + m * Kred + k + 8 * g);
+  u32x4 za[4], wa[JF][4], zb[4], wb[JF][4];
+  auto load = [&](int64_t c, u32x4 (&z)[4], u32x4 (&w)[JF][4]) {
 #pragma unroll
-    for (int jf = 0; jf < 4; ++jf) {
-      if (jf >= JF) break;
-      const int j = 32 * jf + l32;
-      u32x4 aop = {0u, 0u, 0u, 0u};
-      if (j < rt) {
-        const uint16_t* Aw = (j < r0) ? A0 : A1;
-        const int jj = (j < r0) ? j : j - r0;
-        const int rr = (j < r0) ? r0 : r1;
-        if (AW_ROWS) {
-          aop = *reinterpret_cast<const u32x4*>(Aw + (int64_t)jj * Kred + k + 8 * g);
-        } else {
-          uint32_t h[8];
+    for (int t = 0; t < 4; ++t) z[t] = *reinterpret_cast<const u32x4*>(zrow + c * 64 + 8 * t);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) h[e] = Aw[(k + 8 * g + e) * rr + jj];
-          aop = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
-        }
+    for (int jf = 0; jf < JF; ++jf)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) w[jf][t] = *reinterpret_cast<const u32x4*>(wrow[jf] + c * 64 + 8 * t);
+  };
+  auto mul = [&](const u32x4 (&z)[4], const u32x4 (&w)[JF][4]) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int jf = 0; jf < JF; ++jf) {
+        const u32x4 wz = wok[jf] ? w[jf][t] : u32x4{0u, 0u, 0u, 0u};
+        acc[jf] = mfma32(wz, z[t], acc[jf]);
       }
-      acc[jf] = mfma32(aop, zb, acc[jf]);
-    }
+  };
+  int64_t c = cb + wave;
+  if (c < ce) load(c, za, wa);
+  // two register sets alternate (a copy of a prefetch would wait for it)
+  for (; c + 8 < ce; c += 16) {
+    load(c + 8, zb, wb);
+    mul(za, wa);
+    if (c + 16 < ce) load(c + 16, za, wa);
+    mul(zb, wb);
   }
-  // acc[jf][v] = C[j = 32 jf + 8(v/4) + 4g + v%4][token l32]
+  if (c < ce) mul(za, wa);
+
+  // acc[jf][v] = C[j = 32 jf + 8(v/4) + 4h + v%4][token l32]
 #pragma unroll
-  for (int jf = 0; jf < 4; ++jf)
+  for (int jf = 0; jf < JF; ++jf)
 #pragma unroll
     for (int v = 0; v < 16; ++v) red[wave][(jf * 16 + v) * 64 + lane] = acc[jf][v];
   __syncthreads();
-  // each thread finishes (jf, v, lane) slots in fixed wave order
-  for (int idx = tid; idx < JF * 16 * 64; idx += 256) {
-    const float s = ((red[0][idx] + red[1][idx]) + red[2][idx]) + red[3][idx];
+  for (int idx = tid; idx < JF * 16 * 64; idx += 512) {
+    float sum = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) sum += red[w][idx];
     const int ln = idx & 63, vv = (idx >> 6) & 15, jf = idx >> 10;
     const int j = 32 * jf + 8 * (vv >> 2) + 4 * (ln >> 5) + (vv & 3);
     const int64_t mm = m0 + (ln & 31);
     if (j >= rt || mm >= M) continue;
     if (part) {
-      part[((int64_t)blockIdx.y * M + mm) * rt + j] = s;
+      part[((int64_t)blockIdx.y * M + mm) * rt + j] = sum;
     } else if (j < r0) {
-      V0[mm * r0 + j] = s;
+      V0[mm * r0 + j] = sum;
     } else {
-      V1[mm * r1 + (j - r0)] = s;
+      V1[mm * r1 + (j - r0)] = sum;
     }
   }
+}
+
+// B [N, r] -> B^T [r, N] (bf16), so that dY B runs as a row-layout product.
+__global__ __launch_bounds__(256) void transpose_rn_kernel(const uint16_t* __restrict__ B, int64_t N, int r,
+                                                           uint16_t* __restrict__ BT) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // index into BT
+  if (i >= N * r) return;
+  const int64_t j = i / N, n = i % N;
+  BT[i] = B[n * r + j];
 }
 
 // Sum of split partials [S][M][r0 + r1] in split order into V0 | V1.
@@ -605,27 +637,44 @@ __global__ __launch_bounds__(256) void lora_grad_kernel(const uint16_t* __restri
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[t][jf][v] = 0.0f;
 
-  for (int64_t ms = mb; ms < me; ms += 16) {
+  // raw rows of one 16-token slab: token ms + 8 g + e, columns pc .. pc + 7
+  // (ZMODE 1: G and U); tokens past the split are clamped and masked later
+  constexpr int NZ = ZMODE == 0 ? 1 : 2;
+  struct Slab {
+    u32x4 raw[NZ][8];
+    float x[JF][8];  // V[token][j] of the slab's tokens
+  };
+  auto load = [&](int64_t ms, Slab& S) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      int64_t mm = ms + 8 * g + e;
+      if (mm >= me) mm = me - 1;
+      S.raw[0][e] = *reinterpret_cast<const u32x4*>(Z0 + mm * P + pc);
+      if constexpr (ZMODE == 1) S.raw[NZ - 1][e] = *reinterpret_cast<const u32x4*>(Z1 + mm * P + pc);
+#pragma unroll
+      for (int jf = 0; jf < JF; ++jf) {
+        int j = jb + 32 * jf + l32;
+        if (j >= r) j = r - 1;
+        S.x[jf][e] = V[mm * r + j];
+      }
+    }
+  };
+  auto slab = [&](int64_t ms, const Slab& S) {
+    const auto& raw = S.raw;
     u32x4 rows[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const int64_t mm = ms + 8 * g + e;
-      if (mm < me) {
-        if constexpr (ZMODE == 0) {
-          rows[e] = *reinterpret_cast<const u32x4*>(Z0 + mm * P + pc);
-        } else {
-          const u32x4 gg = *reinterpret_cast<const u32x4*>(Z0 + mm * P + pc);
-          const u32x4 uu = *reinterpret_cast<const u32x4*>(Z1 + mm * P + pc);
-#pragma unroll
-          for (int d = 0; d < 4; ++d) {
-            const float g0 = bf16_lo(gg[d]), g1 = bf16_hi(gg[d]);
-            const float h0 = g0 * sigmoidf_(g0) * bf16_lo(uu[d]);
-            const float h1 = g1 * sigmoidf_(g1) * bf16_hi(uu[d]);
-            rows[e][d] = pack_bf16x2(h0, h1);
-          }
-        }
+      const bool ok = ms + 8 * g + e < me;
+      if constexpr (ZMODE == 0) {
+        rows[e] = ok ? raw[0][e] : u32x4{0u, 0u, 0u, 0u};
       } else {
-        rows[e] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const float g0 = bf16_lo(raw[0][e][d]), g1 = bf16_hi(raw[0][e][d]);
+          const float h0 = g0 * sigmoid_fast(g0) * bf16_lo(raw[1][e][d]);
+          const float h1 = g1 * sigmoid_fast(g1) * bf16_hi(raw[1][e][d]);
+          rows[e][d] = ok ? pack_bf16x2(h0, h1) : 0u;
+        }
       }
     }
     // operand t: lane (i, g) holds Z[ms + 8g + e][p0 + 8 i + t], e = 0..7
@@ -644,14 +693,26 @@ __global__ __launch_bounds__(256) void lora_grad_kernel(const uint16_t* __restri
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int64_t mm = ms + 8 * g + e;
-        x[e] = (j < r && mm < me) ? V[mm * r + j] : 0.0f;
+        x[e] = (j < r && mm < me) ? S.x[jf][e] : 0.0f;
       }
       const u32x4 vop{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
                       pack_bf16x2(x[6], x[7])};
 #pragma unroll
       for (int t = 0; t < 8; ++t) acc[t][jf] = mfma32(aop[t], vop, acc[t][jf]);
     }
+  };
+  // two register sets alternate; the next slab is in flight during the current one
+  Slab ra, rb;
+  int64_t ms = mb;
+  if (ms < me) load(ms, ra);
+  for (; ms + 16 < me; ms += 32) {
+    load(ms + 16, rb);
+    slab(ms, ra);
+    if (ms + 32 < me) load(ms + 32, ra);
+    slab(ms + 16, rb);
   }
+  if (ms < me) slab(ms, ra);
+
   // acc[t][jf][v] = C[i = 8(v/4) + 4g + v%4][j = jb + 32 jf + l32], column p = p0 + 8 i + t
 #pragma unroll
   for (int jf = 0; jf < JF; ++jf) {
@@ -769,22 +830,32 @@ hipError_t launch_splitk_finish(const float* part, int splits, int64_t M, int64_
   return hipGetLastError();
 }
 
-hipError_t launch_lora_down(bool aw_rows, const uint16_t* Z, int64_t M, int64_t Kred, const uint16_t* A0, int r0,
-                            const uint16_t* A1, int r1, float* V0, float* V1, int splits, float* part,
+hipError_t launch_lora_down(const uint16_t* Z, int64_t M, int64_t Kred, const uint16_t* W0, int r0,
+                            const uint16_t* W1, int r1, float* V0, float* V1, int splits, float* part,
                             hipStream_t st) {
   if (M == 0) return hipSuccess;
-  const int64_t k16 = Kred / 16;
-  const int64_t per = ((k16 + splits - 1) / splits) * 16;
-  const int S = (int)((Kred + per - 1) / per);
+  const int64_t C = Kred / 64;
+  const int64_t per = (C + splits - 1) / splits;
+  const int S = (int)((C + per - 1) / per);
   dim3 grid(grid1(M, 32), (unsigned)S);
   float* pp = S > 1 ? part : nullptr;
-  if (aw_rows)
-    lora_down_kernel<true><<<grid, 256, 0, st>>>(Z, M, Kred, A0, r0, A1, r1, V0, V1, per, pp);
-  else
-    lora_down_kernel<false><<<grid, 256, 0, st>>>(Z, M, Kred, A0, r0, A1, r1, V0, V1, per, pp);
+  const int jf = (r0 + r1 + 31) / 32;
+  switch (jf) {
+    case 1: lora_down_kernel<1><<<grid, 512, 0, st>>>(Z, M, Kred, W0, r0, W1, r1, V0, V1, per, pp); break;
+    case 2: lora_down_kernel<2><<<grid, 512, 0, st>>>(Z, M, Kred, W0, r0, W1, r1, V0, V1, per, pp); break;
+    case 3: lora_down_kernel<3><<<grid, 512, 0, st>>>(Z, M, Kred, W0, r0, W1, r1, V0, V1, per, pp); break;
+    case 4: lora_down_kernel<4><<<grid, 512, 0, st>>>(Z, M, Kred, W0, r0, W1, r1, V0, V1, per, pp); break;
+    default: return hipErrorInvalidValue;
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || S == 1) return e;
   down_finish_kernel<<<grid1(M * (r0 + r1), 256), 256, 0, st>>>(part, S, M, r0, r1, V0, V1);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose_rn(const uint16_t* B, int64_t N, int r, uint16_t* BT, hipStream_t st) {
+  if (N * r == 0) return hipSuccess;
+  transpose_rn_kernel<<<grid1(N * r, 256), 256, 0, st>>>(B, N, r, BT);
   return hipGetLastError();
 }
 

@@ -72,9 +72,12 @@ hipError_t launch_dequant_trans(const Nf4Dev& w, const float* codebook, uint16_t
                                 hipStream_t st);
 hipError_t launch_splitk_finish(const float* part, int splits, int64_t M, int64_t Nout, uint16_t* out,
                                 hipStream_t st);
-hipError_t launch_lora_down(bool aw_rows, const uint16_t* Z, int64_t M, int64_t Kred, const uint16_t* A0, int r0,
-                            const uint16_t* A1, int r1, float* V0, float* V1, int splits, float* part,
+// V0 | V1 = Z W0^T | Z W1^T, W0 [r0, Kred], W1 [r1, Kred] (r0 + r1 <= 128).
+hipError_t launch_lora_down(const uint16_t* Z, int64_t M, int64_t Kred, const uint16_t* W0, int r0,
+                            const uint16_t* W1, int r1, float* V0, float* V1, int splits, float* part,
                             hipStream_t st);
+// B [N, r] -> B^T [r, N]
+hipError_t launch_transpose_rn(const uint16_t* B, int64_t N, int r, uint16_t* BT, hipStream_t st);
 hipError_t launch_lora_grad(int zmode, const uint16_t* Z0, const uint16_t* Z1, int64_t M, int64_t P,
                             const float* V, int r, float s, int msplits, float* part, int out_rp, uint16_t* out,
                             hipStream_t st);

@@ -53,12 +53,14 @@ inline GemmPlan plan_gemm(int64_t M, int64_t Nout, int64_t Kred, bool allow_spli
   return p;
 }
 
-// Reduction splits of the LoRA down-projection V = Z A^T (M x r, reduce over Kred).
+// Reduction splits of the LoRA down-projection V = Z W^T (M x r, reduce over
+// Kred): one 8-wave workgroup per 32 tokens and split; enough splits to put
+// one workgroup on every CU, each split keeping >= 2 64-wide chunks per wave.
 inline int plan_down_splits(int64_t M, int64_t Kred) {
   const int64_t wgs = cdiv(M, 32);
   if (wgs >= kNumCUs) return 1;
   int64_t s = cdiv(kNumCUs, wgs);
-  const int64_t max_s = Kred / 512 > 0 ? Kred / 512 : 1;  // >= 32 k16-steps per split
+  const int64_t max_s = Kred / 1024 > 0 ? Kred / 1024 : 1;
   if (s > max_s) s = max_s;
   return (int)(s < 1 ? 1 : s);
 }
@@ -67,9 +69,9 @@ inline int plan_down_splits(int64_t M, int64_t Kred) {
 // Each split writes an fp32 [P, r] partial; keep the partials small next to Z.
 inline int plan_grad_msplits(int64_t M, int64_t P, int r) {
   const int64_t waves = cdiv(P, 256);
-  int64_t s = cdiv(4 * kNumCUs, waves);
-  // partial bytes 4 * s * P * r must stay below ~1/8 of the Z bytes 2 * M * P
-  int64_t cap = (M / (16 * (int64_t)r));
+  int64_t s = cdiv(8 * kNumCUs, waves);  // ~8 waves per CU
+  // partial bytes 4 * s * P * r must stay below ~1/4 of the Z bytes 2 * M * P
+  int64_t cap = (M / (8 * (int64_t)r));
   if (cap < 1) cap = 1;
   if (s > cap) s = cap;
   const int64_t max_by_rows = cdiv(M, 64);  // >= 64 tokens per split
@@ -87,7 +89,7 @@ inline int64_t pair_rows(int64_t I) { return 256 * cdiv(I, 128); }
 
 struct LinearWs {
   size_t fwd_part, fwd_down;             // forward: split-K partials, down-proj partials
-  size_t bwd_T, bwd_part, bwd_down, bwd_grad;
+  size_t bwd_T, bwd_BT, bwd_part, bwd_down, bwd_grad;
   size_t wbuf;                           // bf16 weight copy (bgemm only), at the end
   size_t fwd_total, bwd_total, total;
 };
@@ -104,6 +106,7 @@ inline LinearWs linear_ws(int64_t M, int64_t N, int64_t K, int r) {
 
   GemmPlan pb = plan_gemm(M, K, N, true);
   w.bwd_T = align256((size_t)M * r * 4);
+  w.bwd_BT = align256((size_t)N * r * 2);
   w.bwd_part = (!bg && pb.splits > 1) ? align256((size_t)pb.splits * M * K * 4) : 0;
   const int ts = plan_down_splits(M, N);
   w.bwd_down = ts > 1 ? align256((size_t)ts * M * r * 4) : 0;
@@ -111,7 +114,7 @@ inline LinearWs linear_ws(int64_t M, int64_t N, int64_t K, int r) {
   const int gs_a = plan_grad_msplits(M, K, r);
   size_t gb = align256((size_t)gs_b * N * r * 4), ga = align256((size_t)gs_a * K * r * 4);
   w.bwd_grad = gb > ga ? gb : ga;
-  w.bwd_total = w.bwd_T + w.bwd_part + w.bwd_down + w.bwd_grad + w.wbuf;
+  w.bwd_total = w.bwd_T + w.bwd_BT + w.bwd_part + w.bwd_down + w.bwd_grad + w.wbuf;
   w.total = w.fwd_total > w.bwd_total ? w.fwd_total : w.bwd_total;
   if (w.total == 0) w.total = 256;
   return w;
@@ -119,7 +122,7 @@ inline LinearWs linear_ws(int64_t M, int64_t N, int64_t K, int r) {
 
 struct MlpWs {
   size_t fwd_H, fwd_down;                            // H bf16 [M, I], down-proj partials
-  size_t bwd_Td, bwd_dG, bwd_dU, bwd_Tg, bwd_Tu, bwd_down, bwd_grad;
+  size_t bwd_Td, bwd_dG, bwd_dU, bwd_Tg, bwd_Tu, bwd_BT, bwd_down, bwd_grad;
   size_t fwd_wbuf, bwd_wbuf;                         // bf16 weight copies (bgemm only), at the end
   size_t fwd_total, bwd_total, total;
 };
@@ -145,6 +148,8 @@ inline MlpWs mlp_ws(int64_t M, int64_t D, int64_t I, int rg, int ru, int rd) {
   w.bwd_dU = align256((size_t)M * I * 2);
   w.bwd_Tg = align256((size_t)M * rg * 4);
   w.bwd_Tu = align256((size_t)M * ru * 4);
+  // B_d^T [rd, D], B_g^T [rg, I], B_u^T [ru, I]
+  w.bwd_BT = align256((size_t)rd * D * 2) + align256((size_t)rg * I * 2) + align256((size_t)ru * I * 2);
   const int t1 = plan_down_splits(M, D), t2 = plan_down_splits(M, I);
   size_t e1 = t1 > 1 ? align256((size_t)t1 * M * rd * 4) : 0;
   size_t e2 = t2 > 1 ? align256((size_t)t2 * M * rmax * 4) : 0;
@@ -158,7 +163,8 @@ inline MlpWs mlp_ws(int64_t M, int64_t D, int64_t I, int rg, int ru, int rd) {
     if (b > g) g = b;
   }
   w.bwd_grad = g;
-  w.bwd_total = w.bwd_Td + w.bwd_dG + w.bwd_dU + w.bwd_Tg + w.bwd_Tu + w.bwd_down + w.bwd_grad + w.bwd_wbuf;
+  w.bwd_total = w.bwd_Td + w.bwd_dG + w.bwd_dU + w.bwd_Tg + w.bwd_Tu + w.bwd_BT + w.bwd_down + w.bwd_grad +
+                w.bwd_wbuf;
   w.total = w.fwd_total > w.bwd_total ? w.fwd_total : w.bwd_total;
   if (w.total == 0) w.total = 256;
   return w;
