@@ -25,15 +25,31 @@ namespace qk {
 // ------------------------------------------------------------------------
 // bgemm_kernel: output tile 256 tokens x 256 weight rows, 4 waves (one per
 // SIMD) in a 2 x 2 grid, each 128 x 128 = 4 x 4 frags of 32x32, fp32
-// accumulators.  Per 64-wide reduction tile both operand tiles ([256][64]
-// bf16, 16-byte chunks swizzled by swz(row)) are double-buffered in LDS
-// (128 KB).  Each thread stages 8 + 8 16-byte chunks of the next tile in
-// registers: loaded right after the barrier that opens a tile, written to
-// the other LDS buffer after the tile's MFMAs, so the global latency hides
-// behind one tile of matrix work and one LDS-only barrier per tile suffices.
+// accumulators.  Reduction tiles of 64 columns.
+//
+// Operands move global -> LDS by direct loads (global_load_lds, 16 bytes per
+// lane, no registers, no LDS write instructions).  Each direct load fills
+// 1 KB of LDS with 8 rows x 128 bytes, i.e. whole cache lines; a tile
+// operand ([256][64] bf16, chunk c of row r stored at c ^ swz(r)) is 32 KB,
+// 8 direct loads per wave.  The two operands of tile kt ("halves" 2kt and
+// 2kt+1) rotate through five 32 KB buffers (all 160 KB of LDS; each buffer
+// its own __shared__ object, so the compiler's dependency tracking adds no
+// waits of its own).  While tile kt multiplies from its two buffers, the
+// other three hold the next tile's halves and the following A half, in
+// flight or landed: 96 KB per CU stays in flight, which is what the L2-to-CU
+// path needs (measured: about 9 TB/s with 64 KB in flight or half-line
+// segments, 17-20 TB/s with 96-128 KB of whole lines).
+//
+// Per tile: steps 0-2 multiply while reading the next step's operands; then
+// wait until this wave's loads of tile kt+1 have landed (explicit vmcnt: the
+// A half of kt+2 may stay in flight) and barrier, after which every wave has
+// read its last operands of tile kt and every load of tile kt+1 has landed;
+// step 3 then multiplies while the two freed buffers are refilled (B of
+// kt+2, A of kt+3) and tile kt+1's first operands are read.
 // ------------------------------------------------------------------------
 constexpr int BG_WM = 2, BG_WN = 2, BG_FM = 4, BG_FN = 4;
 constexpr int BG_BM = 256, BG_BN = 256;
+constexpr int BG_HE = 256 * 64;  // elements per half (one operand of one tile)
 
 // Block -> tile.  Workgroups are dealt round-robin over the 8 XCDs; the
 // first part of the mapping gives each XCD a contiguous run of tile ids, the
@@ -53,14 +69,33 @@ __device__ __forceinline__ void bg_tile(int64_t bid, int64_t tiles_m, int64_t ti
   tn = in / gs;
 }
 
+// s_waitcnt with only the vector-memory counter: wait until at most N of this
+// wave's vector memory operations are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier for LDS data written by direct loads: LDS accesses of
+// this wave complete (lgkmcnt), then s_barrier.  The memory clobber keeps the
+// compiler from moving memory accesses across it.  The caller has already
+// waited (vmcnt) for the direct loads that must be visible after it.
+__device__ __forceinline__ void stage_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+#define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
+
 template <int MODE>
 __global__ __launch_bounds__(256) void bgemm_kernel(GemmArgs p) {
   constexpr int WM = BG_WM, WN = BG_WN, FM = BG_FM, FN = BG_FN;
   constexpr int BM = BG_BM, BN = BG_BN;
   constexpr int BNO = ModeTraits<MODE>::swiglu_fwd ? BN / 2 : BN;
 
-  __shared__ __attribute__((aligned(16))) uint16_t sa[2][BM * 64];
-  __shared__ __attribute__((aligned(16))) uint16_t sb[2][BN * 64];
+  __shared__ __attribute__((aligned(16))) uint16_t hb0[BG_HE];
+  __shared__ __attribute__((aligned(16))) uint16_t hb1[BG_HE];
+  __shared__ __attribute__((aligned(16))) uint16_t hb2[BG_HE];
+  __shared__ __attribute__((aligned(16))) uint16_t hb3[BG_HE];
+  __shared__ __attribute__((aligned(16))) uint16_t hb4[BG_HE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -70,53 +105,51 @@ __global__ __launch_bounds__(256) void bgemm_kernel(GemmArgs p) {
   int64_t tm, tn;
   bg_tile(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
   const int64_t m0 = tm * BM;
-  const int64_t n0 = tn * BNO;        // first output column
-  const int64_t wr0 = tn * BN;        // first weight row of the tile
+  const int64_t n0 = tn * BNO;  // first output column
+  const int64_t wr0 = tn * BN;  // first weight row of the tile
   const int KT0 = (int)(p.Kred0 / 64);
   const int KT = KT0 + (int)(p.Kred1 / 64);
 
-  // staging chunk i of this thread: tile row 32 i + 8 wave + lane/8, 16-byte
-  // chunk lane%8 (8 lanes cover one 128-byte row segment)
+  // direct load i (0..7) of this wave: tile rows 8 (8 wave + i) + lane/8,
+  // physical chunk lane%8 <- logical chunk (lane%8) ^ swz(row)
   uint32_t aoff[8], boff[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const int row = 32 * i + 8 * wave + (lane >> 3);
+    const int row = 8 * (8 * wave + i) + (lane >> 3);
+    const int c = (lane & 7) ^ swz(row);
     int64_t ra = m0 + row;
     if (ra >= p.M) ra = p.M - 1;
     int64_t rb = wr0 + row;
     if (rb >= p.wrows) rb = p.wrows - 1;
-    aoff[i] = (uint32_t)((ra - m0) * p.Kred0) + (uint32_t)(lane & 7) * 8;
-    boff[i] = (uint32_t)((rb - wr0) * p.ldw) + (uint32_t)(lane & 7) * 8;
+    aoff[i] = (uint32_t)((ra - m0) * p.Kred0) + (uint32_t)c * 8;
+    boff[i] = (uint32_t)((rb - wr0) * p.ldw) + (uint32_t)c * 8;
   }
   // the dual-reduction GEMM reads act0 for the first KT0 tiles, then act1
   const uint16_t* abase0 = p.act0 + m0 * p.Kred0;
   const uint16_t* abase1 = (p.act1 ? p.act1 + m0 * p.Kred0 : abase0) - (int64_t)KT0 * 64;
   const uint16_t* bbase = p.wb + wr0 * p.ldw;
 
-  u32x4 ra[8], rb[8];
-  auto gload = [&](int kt) {
-    const uint16_t* a = (kt < KT0 ? abase0 : abase1) + (int64_t)kt * 64;
-    const uint16_t* b = bbase + (int64_t)kt * 64;
+  // 8 direct loads of one operand half of tile kt (clamped to the last tile:
+  // the tail re-loads it into a free buffer, which keeps vmcnt uniform).
+  // Uniform base + 32-bit lane byte offset: the scalar-base addressing form.
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {  // same order as the refills in lstore
-      ra[i] = *reinterpret_cast<const u32x4*>(a + aoff[i]);
-      rb[i] = *reinterpret_cast<const u32x4*>(b + boff[i]);
-    }
+  for (int i = 0; i < 8; ++i) {
+    aoff[i] *= 2;
+    boff[i] *= 2;
+  }
+  auto load_a = [&](uint16_t* buf, int kt) {
+    kt = kt < KT ? kt : KT - 1;
+    const char* a = reinterpret_cast<const char*>((kt < KT0 ? abase0 : abase1) + (int64_t)kt * 64);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      __builtin_amdgcn_global_load_lds(a + aoff[i], LDS_PTR(buf + (8 * wave + i) * 512), 16, 0, 0);
   };
-  // staged chunks [4h, 4h + 4) of both operands into LDS buffer `buf`; with
-  // `reload`, each register is refilled from tile kt right after its store
-  auto lstore = [&](int buf, int h, bool reload, int kt) {
-    const uint16_t* a = (kt < KT0 ? abase0 : abase1) + (int64_t)kt * 64;
-    const uint16_t* b = bbase + (int64_t)kt * 64;
+  auto load_b = [&](uint16_t* buf, int kt) {
+    kt = kt < KT ? kt : KT - 1;
+    const char* b = reinterpret_cast<const char*>(bbase + (int64_t)kt * 64);
 #pragma unroll
-    for (int i = 4 * h; i < 4 * h + 4; ++i) {
-      const int row = 32 * i + 8 * wave + (lane >> 3);
-      const int off = row * 64 + (((lane & 7) ^ swz(row)) * 8);
-      *reinterpret_cast<u32x4*>(&sa[buf][off]) = ra[i];
-      if (reload) ra[i] = *reinterpret_cast<const u32x4*>(a + aoff[i]);
-      *reinterpret_cast<u32x4*>(&sb[buf][off]) = rb[i];
-      if (reload) rb[i] = *reinterpret_cast<const u32x4*>(b + boff[i]);
-    }
+    for (int i = 0; i < 8; ++i)
+      __builtin_amdgcn_global_load_lds(b + boff[i], LDS_PTR(buf + (8 * wave + i) * 512), 16, 0, 0);
   };
 
   f32x16 acc[FM][FN];
@@ -127,25 +160,28 @@ __global__ __launch_bounds__(256) void bgemm_kernel(GemmArgs p) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][f][v] = 0.0f;
 
-  // LDS offsets (elements) of this lane's operand rows
-  int arow_l[FM], brow_l[FN];
+  // element offsets of this lane's operands within a half, per frag and
+  // step (the same for every buffer, whose base goes to the read's offset)
+  uint32_t aro[FM][4], bro[FN][4];
 #pragma unroll
-  for (int i = 0; i < FM; ++i) arow_l[i] = (wm * FM + i) * 32 + l32;
+  for (int i = 0; i < FM; ++i) {
+    const int row = (wm * FM + i) * 32 + l32;
 #pragma unroll
-  for (int f = 0; f < FN; ++f) brow_l[f] = frag_row<MODE, WN, FN>(wn, f) + l32;
+    for (int s = 0; s < 4; ++s) aro[i][s] = row * 64 + (((2 * s + g) ^ swz(row)) * 8);
+  }
+#pragma unroll
+  for (int f = 0; f < FN; ++f) {
+    const int row = frag_row<MODE, WN, FN>(wn, f) + l32;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) bro[f][s] = row * 64 + (((2 * s + g) ^ swz(row)) * 8);
+  }
 
-  // operands of one 16-wide reduction step s of LDS buffer `buf`
-  auto rd = [&](int buf, int s, u32x4 (&xa)[FM], u32x4 (&wa)[FN]) {
+  // operands of 16-wide step s (0..3) of a tile held in halves (ha, hb)
+  auto rd = [&](const uint16_t* ha, const uint16_t* hb, int s, u32x4 (&xa)[FM], u32x4 (&wa)[FN]) {
 #pragma unroll
-    for (int f = 0; f < FN; ++f) {
-      const int row = brow_l[f];
-      wa[f] = *reinterpret_cast<const u32x4*>(&sb[buf][row * 64 + (((2 * s + g) ^ swz(row)) * 8)]);
-    }
+    for (int f = 0; f < FN; ++f) wa[f] = *reinterpret_cast<const u32x4*>(hb + bro[f][s]);
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      const int row = arow_l[i];
-      xa[i] = *reinterpret_cast<const u32x4*>(&sa[buf][row * 64 + (((2 * s + g) ^ swz(row)) * 8)]);
-    }
+    for (int i = 0; i < FM; ++i) xa[i] = *reinterpret_cast<const u32x4*>(ha + aro[i][s]);
   };
   auto mm = [&](const u32x4 (&xa)[FM], const u32x4 (&wa)[FN]) {
 #pragma unroll
@@ -153,26 +189,7 @@ __global__ __launch_bounds__(256) void bgemm_kernel(GemmArgs p) {
 #pragma unroll
       for (int f = 0; f < FN; ++f) acc[i][f] = mfma32(wa[f], xa[i], acc[i][f]);
   };
-  auto mm_half = [&](const u32x4 (&xa)[FM], const u32x4 (&wa)[FN], int h) {
-#pragma unroll
-    for (int i = 2 * h; i < 2 * h + 2; ++i)
-#pragma unroll
-      for (int f = 0; f < FN; ++f) acc[i][f] = mfma32(wa[f], xa[i], acc[i][f]);
-  };
-
-  // Software pipeline over one reduction tile (4 steps x 16 MFMAs): the
-  // operands of step s+1 are read while step s multiplies (two register
-  // sets); during steps 2 and 3 the staged next tile goes to the other LDS
-  // buffer, each staging register being refilled from the tile after that
-  // right after its store, so every global load has one whole tile of matrix
-  // work to arrive.  The group barriers pin the interleave: one LDS access
-  // (and one global load) next to each MFMA.
-  u32x4 x0[FM], w0[FN], x1[FM], w1[FN];
-  auto tile = [&](int kt, auto more) {
-    constexpr bool MORE = decltype(more)::value;  // a next tile exists
-    const int cur = kt & 1, nxt = cur ^ 1;
-    rd(cur, 1, x1, w1);
-    mm(x0, w0);
+  auto interleave_reads = [&]() {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       SCHED_GROUP(SG_MFMA, 1);
@@ -180,75 +197,69 @@ __global__ __launch_bounds__(256) void bgemm_kernel(GemmArgs p) {
     }
     SCHED_GROUP(SG_MFMA, 8);
     __builtin_amdgcn_sched_barrier(0);
-    rd(cur, 2, x0, w0);
+  };
+
+  u32x4 x0[FM], w0[FN], x1[FM], w1[FN];
+  // tile kt in halves (ca, cb); tile kt+1 in (na, nb)
+  auto tile = [&](int kt, uint16_t* ca, uint16_t* cb, const uint16_t* na, const uint16_t* nb) {
+    rd(ca, cb, 1, x1, w1);
+    mm(x0, w0);
+    interleave_reads();
+    rd(ca, cb, 2, x0, w0);
+    mm(x1, w1);
+    interleave_reads();
+    rd(ca, cb, 3, x1, w1);
+    mm(x0, w0);
+    interleave_reads();
+    wait_vmcnt<8>();  // tile kt+1 landed; the A half of kt+2 may be in flight
+    stage_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    load_b(ca, kt + 2);
+    load_a(cb, kt + 3);
+    rd(na, nb, 0, x0, w0);
     mm(x1, w1);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       SCHED_GROUP(SG_MFMA, 1);
+      SCHED_GROUP(SG_VMEM_READ, 2);
       SCHED_GROUP(SG_DS_READ, 1);
     }
     SCHED_GROUP(SG_MFMA, 8);
     __builtin_amdgcn_sched_barrier(0);
-    rd(cur, 3, x1, w1);
-    if constexpr (MORE) lstore(nxt, 0, true, min(kt + 2, KT - 1));
-    mm(x0, w0);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      SCHED_GROUP(SG_MFMA, 1);
-      SCHED_GROUP(SG_DS_READ, 1);
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      SCHED_GROUP(SG_MFMA, 1);
-      if (MORE) {
-        SCHED_GROUP(SG_DS_WRITE, 1);
-        SCHED_GROUP(SG_VMEM_READ, 1);
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    if constexpr (MORE) lstore(nxt, 1, true, min(kt + 2, KT - 1));
-    mm_half(x1, w1, 0);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      SCHED_GROUP(SG_MFMA, 1);
-      if (MORE) {
-        SCHED_GROUP(SG_DS_WRITE, 1);
-        SCHED_GROUP(SG_VMEM_READ, 1);
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    // Every LDS access of this wave to buffer `cur` and every store into
-    // `nxt` is complete at this barrier, so the next tile's first operands
-    // are read while the last MFMAs of this tile run.
-    if constexpr (MORE) {
-      lds_barrier();
-      rd(nxt, 0, x0, w0);
-    }
-    mm_half(x1, w1, 1);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      SCHED_GROUP(SG_MFMA, 1);
-      if (MORE) SCHED_GROUP(SG_DS_READ, 1);
-    }
-    __builtin_amdgcn_sched_barrier(0);
   };
-
-  if (KT > 0) {
-    gload(0);
-    lstore(0, 0, true, min(1, KT - 1));
-    lstore(0, 1, true, min(1, KT - 1));
-    lds_barrier();
-    rd(0, 0, x0, w0);
-    int kt = 0;
-    for (; kt + 1 < KT; ++kt) tile(kt, std::true_type{});
-    tile(kt, std::false_type{});
-  }
 
   int64_t arow[FM];
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
     const int64_t r = m0 + (int64_t)(wm * FM + i) * 32 + l32;
     arow[i] = r < p.M ? r : p.M - 1;
+  }
+  if (KT > 0) {
+    load_a(hb0, 0);
+    load_b(hb1, 0);
+    load_a(hb2, 1);
+    load_b(hb3, 1);
+    load_a(hb4, 2);
+    // the LoRA term first: its loads overlap the pipeline fill
+    gemm_lora<MODE, WN, FM, FN, false>(p, acc, arow, n0, wn, l32, g);
+    wait_vmcnt<24>();  // tile 0 landed
+    stage_barrier();
+    rd(hb0, hb1, 0, x0, w0);
+    // half h of the sequence A0 B0 A1 B1 ... lives in buffer h % 5
+    int kt = 0;
+    for (; kt + 5 <= KT; kt += 5) {
+      tile(kt, hb0, hb1, hb2, hb3);
+      tile(kt + 1, hb2, hb3, hb4, hb0);
+      tile(kt + 2, hb4, hb0, hb1, hb2);
+      tile(kt + 3, hb1, hb2, hb3, hb4);
+      tile(kt + 4, hb3, hb4, hb0, hb1);
+    }
+    const int rem = KT - kt;  // 0 .. 4
+    if (rem > 0) tile(kt, hb0, hb1, hb2, hb3);
+    if (rem > 1) tile(kt + 1, hb2, hb3, hb4, hb0);
+    if (rem > 2) tile(kt + 2, hb4, hb0, hb1, hb2);
+    if (rem > 3) tile(kt + 3, hb1, hb2, hb3, hb4);
+    wait_vmcnt<0>();  // no direct load may still target LDS past this point
   }
   gemm_epilogue<MODE, WM, WN, FM, FN, false>(p, acc, arow, m0, n0, wm, wn, l32, g);
 }

@@ -54,66 +54,88 @@ __device__ __forceinline__ int frag_row(int wn, int f) {
   return (wn * FN + f) * 32;
 }
 
-// Epilogue of one output tile.  acc[i][f]: token frag i (rows
+// Output column of lane-row l32 in output frag f of wave column wn (for the
+// SwiGLU forward, frags f and f + FN/2 are the gate and up columns of the
+// same intermediate column).
+template <int MODE, int WN, int FN>
+__device__ __forceinline__ int64_t out_col_of(int64_t n0, int wn, int f) {
+  if (ModeTraits<MODE>::swiglu_fwd) {
+    constexpr int H = FN / 2;
+    return n0 + (int64_t)(wn * H + (f % H)) * 32;
+  }
+  return n0 + (int64_t)frag_row<MODE, WN, FN>(wn, f);
+}
+
+// LoRA term acc += s * V[m, :] Wl(col, :)^T as extra MFMA steps (rank r in
+// steps of 16; s V rounded to bf16).  Called before the main reduction, so
+// that its operand loads overlap the pipeline fill: every load of a step is
+// issued unconditionally (indices clamped, values masked) before any use.
+template <int MODE, int WN, int FM, int FN, bool SPLIT>
+__device__ __forceinline__ void gemm_lora(const GemmArgs& p, f32x16 (&acc)[FM][FN], const int64_t (&arow)[FM],
+                                          int64_t n0, int wn, int l32, int g) {
+  auto lora = [&](const LoraSide& L, int f_lo, int f_hi) {
+    const int steps = (L.r + 15) / 16;
+    for (int t = 0; t < steps; ++t) {
+      float x[FM][8];
+      uint32_t h[FN][8];
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int j = 16 * t + 8 * g + e;
+          x[i][e] = L.V[arow[i] * L.r + (j < L.r ? j : L.r - 1)];
+        }
+#pragma unroll
+      for (int f = 0; f < FN; ++f) {
+        int64_t c = out_col_of<MODE, WN, FN>(n0, wn, f) + l32;
+        if (c >= p.Nout) c = p.Nout - 1;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int j = 16 * t + 8 * g + e;
+          h[f][e] = L.Wl[c * L.wl_sc + (int64_t)(j < L.r ? j : L.r - 1) * L.wl_sj];
+        }
+      }
+      u32x4 vop[FM];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        float y[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[e] = (16 * t + 8 * g + e < L.r) ? L.s * x[i][e] : 0.0f;
+        vop[i] = u32x4{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]), pack_bf16x2(y[4], y[5]),
+                       pack_bf16x2(y[6], y[7])};
+      }
+#pragma unroll
+      for (int f = 0; f < FN; ++f) {
+        if (f < f_lo || f >= f_hi) continue;
+        uint32_t hh[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) hh[e] = (16 * t + 8 * g + e < L.r) ? h[f][e] : 0u;
+        const u32x4 wop{hh[0] | (hh[1] << 16), hh[2] | (hh[3] << 16), hh[4] | (hh[5] << 16), hh[6] | (hh[7] << 16)};
+#pragma unroll
+        for (int i = 0; i < FM; ++i) acc[i][f] = mfma32(wop, vop[i], acc[i][f]);
+      }
+    }
+  };
+  if constexpr (MODE == MODE_FWD_SWIGLU) {
+    lora(p.l0, 0, FN / 2);
+    lora(p.l1, FN / 2, FN);
+  } else if constexpr (MODE == MODE_BWD_DUAL) {
+    lora(p.l0, 0, FN);
+    lora(p.l1, 0, FN);
+  } else {
+    if (!SPLIT || blockIdx.y == 0) lora(p.l0, 0, FN);  // split runs: the LoRA term goes into split 0
+  }
+}
+
+// Stores of one output tile.  acc[i][f]: token frag i (rows
 // m0 + (wm*FM + i)*32 + l32, clamped copy in arow[i]) x output frag f of wave
 // column wn; element v of lane (l32, g) is output column
 // out_col(f) + 8*(v/4) + 4*g + v%4.
 template <int MODE, int WM, int WN, int FM, int FN, bool SPLIT>
 __device__ __forceinline__ void gemm_epilogue(const GemmArgs& p, f32x16 (&acc)[FM][FN], const int64_t (&arow)[FM],
                                               int64_t m0, int64_t n0, int wm, int wn, int l32, int g) {
-  // ---- output column of lane-row l32 in frag f, and the LoRA side it uses
-  auto out_col = [&](int f) -> int64_t {
-    if (ModeTraits<MODE>::swiglu_fwd) {
-      constexpr int H = FN / 2;
-      return n0 + (int64_t)(wn * H + (f % H)) * 32;
-    }
-    return n0 + (int64_t)frag_row<MODE, WN, FN>(wn, f);
-  };
-
+  auto out_col = [&](int f) -> int64_t { return out_col_of<MODE, WN, FN>(n0, wn, f); };
   {
-    // ---- LoRA epilogue: acc += s * V[m, :] Wl(col, :)^T as extra MFMA steps.
-    auto lora = [&](const LoraSide& L, int f_lo, int f_hi) {
-      const int steps = (L.r + 15) / 16;
-      for (int t = 0; t < steps; ++t) {
-        u32x4 vop[FM];
-#pragma unroll
-        for (int i = 0; i < FM; ++i) {
-          float x[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int j = 16 * t + 8 * g + e;
-            x[e] = (j < L.r) ? L.s * L.V[arow[i] * L.r + j] : 0.0f;
-          }
-          vop[i] = u32x4{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
-                         pack_bf16x2(x[6], x[7])};
-        }
-#pragma unroll
-        for (int f = 0; f < FN; ++f) {
-          if (f < f_lo || f >= f_hi) continue;
-          int64_t c = out_col(f) + l32;
-          if (c >= p.Nout) c = p.Nout - 1;
-          uint32_t h[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int j = 16 * t + 8 * g + e;
-            h[e] = (j < L.r) ? (uint32_t)L.Wl[c * L.wl_sc + (int64_t)j * L.wl_sj] : 0u;
-          }
-          const u32x4 wop{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
-#pragma unroll
-          for (int i = 0; i < FM; ++i) acc[i][f] = mfma32(wop, vop[i], acc[i][f]);
-        }
-      }
-    };
-    if constexpr (MODE == MODE_FWD_SWIGLU) {
-      lora(p.l0, 0, FN / 2);
-      lora(p.l1, FN / 2, FN);
-    } else if constexpr (MODE == MODE_BWD_DUAL) {
-      lora(p.l0, 0, FN);
-      lora(p.l1, 0, FN);
-    } else {
-      if (!SPLIT || blockIdx.y == 0) lora(p.l0, 0, FN);  // split runs: the LoRA term goes into split 0
-    }
-
     if constexpr (SPLIT) {
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
@@ -134,25 +156,28 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& p, f32x16 (&acc)[F
       return;
     }
 
-    // ---- SwiGLU backward: per token frag, every G / U load of the frag is
-    // issued before any of them is used (one memory latency per frag, not
-    // one per 4-column group); columns past Nout load a clamped address and
-    // are not stored.
+    // ---- SwiGLU backward: the G / U loads of token frag i+1 are issued
+    // before frag i is computed and stored (one exposed memory latency per
+    // tile); columns past Nout load a clamped address and are not stored.
     if constexpr (MODE == MODE_BWD_SWIGLU) {
-#pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const int64_t m = m0 + (int64_t)(wm * FM + i) * 32 + l32;
-        const int64_t mr = arow[i];
-        u32x2 gg[FN][4], uu[FN][4];
+      u32x2 gg[2][FN][4], uu[2][FN][4];
+      auto load = [&](int i, int b) {
 #pragma unroll
         for (int f = 0; f < FN; ++f)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             int64_t n = out_col(f) + 8 * q + 4 * g;
             if (n >= p.Nout) n = p.Nout - 4;
-            gg[f][q] = *reinterpret_cast<const u32x2*>(p.in0 + mr * p.Nout + n);
-            uu[f][q] = *reinterpret_cast<const u32x2*>(p.in1 + mr * p.Nout + n);
+            gg[b][f][q] = *reinterpret_cast<const u32x2*>(p.in0 + arow[i] * p.Nout + n);
+            uu[b][f][q] = *reinterpret_cast<const u32x2*>(p.in1 + arow[i] * p.Nout + n);
           }
+      };
+      load(0, 0);
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        if (i + 1 < FM) load(i + 1, (i + 1) & 1);
+        const int b = i & 1;
+        const int64_t m = m0 + (int64_t)(wm * FM + i) * 32 + l32;
         if (m >= p.M) continue;
 #pragma unroll
         for (int f = 0; f < FN; ++f)
@@ -161,15 +186,15 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& p, f32x16 (&acc)[F
             const int64_t n = out_col(f) + 8 * q + 4 * g;
             if (n >= p.Nout) continue;
             const int64_t off = m * p.Nout + n;
-            const float G[4] = {bf16_lo(gg[f][q][0]), bf16_hi(gg[f][q][0]), bf16_lo(gg[f][q][1]),
-                                bf16_hi(gg[f][q][1])};
-            const float U[4] = {bf16_lo(uu[f][q][0]), bf16_hi(uu[f][q][0]), bf16_lo(uu[f][q][1]),
-                                bf16_hi(uu[f][q][1])};
+            const float G[4] = {bf16_lo(gg[b][f][q][0]), bf16_hi(gg[b][f][q][0]), bf16_lo(gg[b][f][q][1]),
+                                bf16_hi(gg[b][f][q][1])};
+            const float U[4] = {bf16_lo(uu[b][f][q][0]), bf16_hi(uu[b][f][q][0]), bf16_lo(uu[b][f][q][1]),
+                                bf16_hi(uu[b][f][q][1])};
             float dG[4], dU[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const float dH = acc[i][f][4 * q + e];
-              const float sg = sigmoidf_(G[e]);
+              const float sg = sigmoid_fast(G[e]);
               dU[e] = dH * G[e] * sg;
               dG[e] = dH * U[e] * sg * (1.0f + G[e] * (1.0f - sg));
             }
@@ -200,7 +225,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& p, f32x16 (&acc)[F
             for (int e = 0; e < 4; ++e) {
               G[e] = acc[i][f][4 * q + e];
               U[e] = acc[i][f + FN / 2][4 * q + e];
-              H[e] = G[e] * sigmoidf_(G[e]) * U[e];
+              H[e] = G[e] * sigmoid_fast(G[e]) * U[e];
             }
             *reinterpret_cast<u32x2*>(p.out0 + off) = u32x2{pack_bf16x2(G[0], G[1]), pack_bf16x2(G[2], G[3])};
             *reinterpret_cast<u32x2*>(p.out1 + off) = u32x2{pack_bf16x2(U[0], U[1]), pack_bf16x2(U[2], U[3])};

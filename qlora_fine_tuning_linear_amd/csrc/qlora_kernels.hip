@@ -421,6 +421,9 @@ __global__ __launch_bounds__(WM* WN * 64) void qgemm_kernel(GemmArgs p) {
     }
   };
 
+  // the LoRA term first: its loads are issued before the main reduction
+  gemm_lora<MODE, WN, FM, FN, SPLIT>(p, acc, arow, n0, wn, l32, g);
+
   u32x4 A[FM][4];
   Fill Fa, Fb;
   __syncthreads();  // codebook in LDS
