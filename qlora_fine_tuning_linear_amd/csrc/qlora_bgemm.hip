@@ -47,7 +47,7 @@ namespace qk {
 // step 3 then multiplies while the two freed buffers are refilled (B of
 // kt+2, A of kt+3) and tile kt+1's first operands are read.
 // ------------------------------------------------------------------------
-constexpr int BG_WM = 2, BG_WN = 2, BG_FM = 4, BG_FN = 4;
+constexpr int BG_WN = 2, BG_FM = 4, BG_FN = 4;  // 2 x 2 waves
 constexpr int BG_BM = 256, BG_BN = 256;
 constexpr int BG_HE = 256 * 64;  // elements per half (one operand of one tile)
 
@@ -85,9 +85,157 @@ __device__ __forceinline__ void stage_barrier() { asm volatile("s_waitcnt lgkmcn
 
 #define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 
+// Epilogue through LDS.  After the reduction each wave owns one 32 KB LDS
+// buffer.  Its 128 x 128 results are written there in accumulator layout and
+// read back as 16-byte row chunks, so that every global load and store of
+// the epilogue covers whole row segments (16 lanes per 256-byte row),
+// instead of 8-byte pieces of 32 different rows per instruction.  Chunk c of
+// row r sits at c ^ (r mod #chunks), which keeps both the writes and the
+// row-chunk reads free of bank conflicts.
+template <int MODE>
+__device__ __forceinline__ void bg_epilogue(const GemmArgs& p, f32x16 (&acc)[BG_FM][BG_FN], int64_t m0, int64_t n0,
+                                            int wm, int wn, int lane, uint16_t* reg) {
+  constexpr int FM = BG_FM, FN = BG_FN;
+  const int l32 = lane & 31, g = lane >> 5;
+  const int64_t mw = m0 + wm * 128;  // first token of the wave
+  if constexpr (MODE == MODE_FWD_SWIGLU) {
+    // G = acc[.][0..1], U = acc[.][2..3]: 64 intermediate columns per wave
+    const int64_t cw = n0 + wn * 64;
+    uint16_t* lg = reg;
+    uint16_t* lu = reg + 128 * 64;
+    auto wr = [&](uint16_t* t, int i, int f, int q, const float (&v)[4]) {
+      const int row = i * 32 + l32;
+      const int c = 4 * f + q;
+      *reinterpret_cast<u32x2*>(t + row * 64 + ((c ^ (row & 7)) * 8) + 4 * g) =
+          u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+    };
+    auto flush = [&](const uint16_t* t, uint16_t* out) {
+#pragma unroll
+      for (int it = 0; it < 16; ++it) {
+        const int row = it * 8 + (lane >> 3), c = lane & 7;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(t + row * 64 + ((c ^ (row & 7)) * 8));
+        const int64_t m = mw + row, n = cw + c * 8;
+        if (m < p.M && n < p.Nout) *reinterpret_cast<u32x4*>(out + m * p.Nout + n) = v;
+      }
+    };
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int f = 0; f < 2; ++f)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float G[4] = {acc[i][f][4 * q], acc[i][f][4 * q + 1], acc[i][f][4 * q + 2], acc[i][f][4 * q + 3]};
+          const float U[4] = {acc[i][f + 2][4 * q], acc[i][f + 2][4 * q + 1], acc[i][f + 2][4 * q + 2],
+                              acc[i][f + 2][4 * q + 3]};
+          wr(lg, i, f, q, G);
+          wr(lu, i, f, q, U);
+        }
+    flush(lg, p.out0);
+    flush(lu, p.out1);
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int f = 0; f < 2; ++f)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          float H[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float Gv = acc[i][f][4 * q + e], Uv = acc[i][f + 2][4 * q + e];
+            H[e] = Gv * sigmoid_fast(Gv) * Uv;
+          }
+          wr(lg, i, f, q, H);
+        }
+    flush(lg, p.out2);
+  } else if constexpr (MODE == MODE_BWD_SWIGLU) {
+    // dH (fp32) one token frag (32 rows x 128 columns, 16 KB) at a time; the
+    // G / U chunks of frag i+1 are loaded while frag i is finished
+    const int64_t cw = n0 + wn * 128;
+    const int c16 = lane & 15;  // this lane's 8-column group
+    const int64_t ncol = cw + 8 * c16;
+    const bool col_ok = ncol < p.Nout;
+    const int64_t nc = col_ok ? ncol : p.Nout - 8;
+    u32x4 gg[2][8], uu[2][8];
+    auto load = [&](int i, int b) {
+#pragma unroll
+      for (int it = 0; it < 8; ++it) {
+        int64_t m = mw + i * 32 + it * 4 + (lane >> 4);
+        if (m >= p.M) m = p.M - 1;
+        gg[b][it] = *reinterpret_cast<const u32x4*>(p.in0 + m * p.Nout + nc);
+        uu[b][it] = *reinterpret_cast<const u32x4*>(p.in1 + m * p.Nout + nc);
+      }
+    };
+    float* lf = reinterpret_cast<float*>(reg);
+    load(0, 0);
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      if (i + 1 < FM) load(i + 1, (i + 1) & 1);
+      const int b = i & 1;
+#pragma unroll
+      for (int f = 0; f < FN; ++f)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int row = l32, c = 8 * f + 2 * q + g;  // 16-byte fp32 chunk of 32 per row
+          *reinterpret_cast<f32x4*>(lf + row * 128 + ((c ^ (row & 31)) * 4)) =
+              f32x4{acc[i][f][4 * q], acc[i][f][4 * q + 1], acc[i][f][4 * q + 2], acc[i][f][4 * q + 3]};
+        }
+#pragma unroll
+      for (int it = 0; it < 8; ++it) {
+        const int row = it * 4 + (lane >> 4);
+        const int c0 = 2 * c16;
+        const f32x4 d0 = *reinterpret_cast<const f32x4*>(lf + row * 128 + ((c0 ^ (row & 31)) * 4));
+        const f32x4 d1 = *reinterpret_cast<const f32x4*>(lf + row * 128 + (((c0 + 1) ^ (row & 31)) * 4));
+        const float dH[8] = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
+        u32x4 og, ou;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          float dG2[2], dU2[2];
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const float G = e ? bf16_hi(gg[b][it][d]) : bf16_lo(gg[b][it][d]);
+            const float U = e ? bf16_hi(uu[b][it][d]) : bf16_lo(uu[b][it][d]);
+            const float sg = sigmoid_fast(G);
+            const float h = dH[2 * d + e];
+            dU2[e] = h * G * sg;
+            dG2[e] = h * U * sg * (1.0f + G * (1.0f - sg));
+          }
+          og[d] = pack_bf16x2(dG2[0], dG2[1]);
+          ou[d] = pack_bf16x2(dU2[0], dU2[1]);
+        }
+        const int64_t m = mw + i * 32 + row;
+        if (m < p.M && col_ok) {
+          *reinterpret_cast<u32x4*>(p.out0 + m * p.Nout + ncol) = og;
+          *reinterpret_cast<u32x4*>(p.out1 + m * p.Nout + ncol) = ou;
+        }
+      }
+    }
+  } else {
+    // plain bf16 output: 128 tokens x 128 columns per wave, one pass
+    const int64_t cw = n0 + wn * 128;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int f = 0; f < FN; ++f)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int row = i * 32 + l32, c = 4 * f + q;
+          *reinterpret_cast<u32x2*>(reg + row * 128 + ((c ^ (row & 15)) * 8) + 4 * g) =
+              u32x2{pack_bf16x2(acc[i][f][4 * q], acc[i][f][4 * q + 1]),
+                    pack_bf16x2(acc[i][f][4 * q + 2], acc[i][f][4 * q + 3])};
+        }
+#pragma unroll
+    for (int it = 0; it < 32; ++it) {
+      const int row = it * 4 + (lane >> 4), c = lane & 15;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(reg + row * 128 + ((c ^ (row & 15)) * 8));
+      const int64_t m = mw + row, n = cw + c * 8;
+      if (m < p.M && n < p.Nout) *reinterpret_cast<u32x4*>(p.out0 + m * p.Nout + n) = v;
+    }
+  }
+}
+
 template <int MODE>
 __global__ __launch_bounds__(256) void bgemm_kernel(GemmArgs p) {
-  constexpr int WM = BG_WM, WN = BG_WN, FM = BG_FM, FN = BG_FN;
+  constexpr int WN = BG_WN, FM = BG_FM, FN = BG_FN;
   constexpr int BM = BG_BM, BN = BG_BN;
   constexpr int BNO = ModeTraits<MODE>::swiglu_fwd ? BN / 2 : BN;
 
@@ -261,7 +409,9 @@ __global__ __launch_bounds__(256) void bgemm_kernel(GemmArgs p) {
     if (rem > 3) tile(kt + 3, hb1, hb2, hb3, hb4);
     wait_vmcnt<0>();  // no direct load may still target LDS past this point
   }
-  gemm_epilogue<MODE, WM, WN, FM, FN, false>(p, acc, arow, m0, n0, wm, wn, l32, g);
+  stage_barrier();  // every wave is done reading operands: LDS is free
+  uint16_t* reg = wave == 0 ? hb0 : wave == 1 ? hb1 : wave == 2 ? hb2 : hb3;
+  bg_epilogue<MODE>(p, acc, m0, n0, wm, wn, lane, reg);
 }
 
 // ------------------------------------------------------------------------
