@@ -84,9 +84,10 @@ float lora_s(const qlora_linear& L) { return L.alpha / (float)L.r; }
 LoraSide side_B(const qlora_linear& L, const float* V) {
   return LoraSide{V, static_cast<const uint16_t*>(L.B), (int64_t)L.r, 1, L.r, lora_s(L)};
 }
-// LoRA term with the A [r, K] matrix (backward side).
-LoraSide side_A(const qlora_linear& L, const float* V) {
-  return LoraSide{V, static_cast<const uint16_t*>(L.A), 1, L.W0.K, L.r, lora_s(L)};
+// LoRA term with the A [r, K] matrix (backward side), read from its
+// transposed copy AT [K, r] (rows contiguous in j, as the GEMM wants).
+LoraSide side_AT(const qlora_linear& L, const float* V, const uint16_t* AT) {
+  return LoraSide{V, AT, (int64_t)L.r, 1, L.r, lora_s(L)};
 }
 
 GemmArgs gemm_args() {
@@ -195,6 +196,7 @@ int qlora_linear_bwd(const qlora_linear* L, const void* dY, const void* X, const
   char* base = bytes(ws);
   float* T = reinterpret_cast<float*>(base);
   uint16_t* BT = reinterpret_cast<uint16_t*>(base + w.bwd_T);
+  uint16_t* AT = reinterpret_cast<uint16_t*>(base + w.bwd_T + qplan::align256((size_t)N * r * 2));
   char* after_bt = base + w.bwd_T + w.bwd_BT;
   float* part = reinterpret_cast<float*>(after_bt);
   float* down_part = reinterpret_cast<float*>(after_bt + w.bwd_part);
@@ -202,6 +204,7 @@ int qlora_linear_bwd(const qlora_linear* L, const void* dY, const void* X, const
 
   // T = dY B  (B^T first, so that the product reads rows)
   QHIP(launch_transpose_rn(u16(L->B), N, r, BT, st));
+  QHIP(launch_transpose_rn(u16(L->A), r, (int)K, AT, st));  // A [r, K] -> A^T [K, r]
   QHIP(launch_lora_down(u16(dY), M, N, BT, r, nullptr, 0, T, nullptr, qplan::plan_down_splits(M, N), down_part, st));
   // dX = dY W0 + s T A
   const qplan::GemmPlan pl = qplan::plan_gemm(M, K, N, true);
@@ -212,7 +215,7 @@ int qlora_linear_bwd(const qlora_linear* L, const void* dY, const void* X, const
   a.Kred0 = N;
   a.w0 = to_dev(L->W0);
   a.codebook = L->W0.codebook;
-  a.l0 = side_A(*L, T);
+  a.l0 = side_AT(*L, T, AT);
   a.out0 = u16m(dX);
   a.partial = part;
   if (qplan::use_bgemm(M)) {
@@ -336,6 +339,12 @@ int qlora_mlp_bwd(const qlora_mlp* P, const void* dY, const void* X, const qlora
   uint16_t* BgT = reinterpret_cast<uint16_t*>(b + qplan::align256((size_t)rd * D * 2));
   uint16_t* BuT = reinterpret_cast<uint16_t*>(b + qplan::align256((size_t)rd * D * 2) +
                                               qplan::align256((size_t)rg * I * 2));
+  char* at0 = b + qplan::align256((size_t)rd * D * 2) + qplan::align256((size_t)rg * I * 2) +
+              qplan::align256((size_t)ru * I * 2);
+  uint16_t* AdT = reinterpret_cast<uint16_t*>(at0);                                        // [I, rd]
+  uint16_t* AgT = reinterpret_cast<uint16_t*>(at0 + qplan::align256((size_t)I * rd * 2));  // [D, rg]
+  uint16_t* AuT = reinterpret_cast<uint16_t*>(at0 + qplan::align256((size_t)I * rd * 2) +
+                                              qplan::align256((size_t)D * rg * 2));       // [D, ru]
   b += w.bwd_BT;
   float* down_part = reinterpret_cast<float*>(b);
   b += w.bwd_down;
@@ -347,6 +356,9 @@ int qlora_mlp_bwd(const qlora_mlp* P, const void* dY, const void* X, const qlora
   QHIP(launch_transpose_rn(u16(P->down.B), D, rd, BdT, st));
   QHIP(launch_transpose_rn(u16(P->gate.B), I, rg, BgT, st));
   QHIP(launch_transpose_rn(u16(P->up.B), I, ru, BuT, st));
+  QHIP(launch_transpose_rn(u16(P->down.A), rd, (int)I, AdT, st));
+  QHIP(launch_transpose_rn(u16(P->gate.A), rg, (int)D, AgT, st));
+  QHIP(launch_transpose_rn(u16(P->up.A), ru, (int)D, AuT, st));
   QHIP(launch_lora_down(u16(dY), M, D, BdT, rd, nullptr, 0, Td, nullptr, qplan::plan_down_splits(M, D), down_part,
                         st));
   // dH = dY W_d + s_d Td A_d, with the SwiGLU backward in the epilogue -> dG, dU
@@ -358,7 +370,7 @@ int qlora_mlp_bwd(const qlora_mlp* P, const void* dY, const void* X, const qlora
     a.Kred0 = D;
     a.w0 = to_dev(P->down.W0);
     a.codebook = P->down.W0.codebook;
-    a.l0 = side_A(P->down, Td);
+    a.l0 = side_AT(P->down, Td, AdT);
     a.in0 = u16(S->G);
     a.in1 = u16(S->U);
     a.out0 = dG;
@@ -395,8 +407,8 @@ int qlora_mlp_bwd(const qlora_mlp* P, const void* dY, const void* X, const qlora
     a.w1 = to_dev(P->up.W0);
     a.codebook = P->gate.W0.codebook;
     a.codebook1 = P->up.W0.codebook;
-    a.l0 = side_A(P->gate, Tg);
-    a.l1 = side_A(P->up, Tu);
+    a.l0 = side_AT(P->gate, Tg, AgT);
+    a.l1 = side_AT(P->up, Tu, AuT);
     a.out0 = u16m(dX);
     if (wbuf) {
       // [W_g^T | W_u^T] as bf16 [D, 2I]

@@ -383,13 +383,36 @@ __global__ __launch_bounds__(256) void bgemm_kernel(GemmArgs p) {
     arow[i] = r < p.M ? r : p.M - 1;
   }
   if (KT > 0) {
+    // The LoRA term first.  Fast form: step 0 of every side is loaded before
+    // the pipeline fill is issued (so the compiler's wait for it lets the
+    // fill stay in flight) and applied after; remaining steps (rank > 16)
+    // and the scalar form follow the fill.
+    const LoraSide* L[2];
+    int lo[2], hi[2];
+    const int ns = lora_sides<MODE, FN, false>(p, L, lo, hi);
+    const bool fast = lora_fast(*L[0]) && (ns < 2 || lora_fast(*L[1]));
+    LoraRegs<FM, FN> R0, R1;
+    if (fast) {
+      if (ns > 0) lora_load<MODE, WN, FM, FN>(p, *L[0], 0, arow, n0, wn, l32, g, R0);
+      if (ns > 1) lora_load<MODE, WN, FM, FN>(p, *L[1], 0, arow, n0, wn, l32, g, R1);
+    }
     load_a(hb0, 0);
     load_b(hb1, 0);
     load_a(hb2, 1);
     load_b(hb3, 1);
     load_a(hb4, 2);
-    // the LoRA term first: its loads overlap the pipeline fill
-    gemm_lora<MODE, WN, FM, FN, false>(p, acc, arow, n0, wn, l32, g);
+    if (fast) {
+      if (ns > 0) lora_apply<FM, FN>(*L[0], 0, g, lo[0], hi[0], acc, R0);
+      if (ns > 1) lora_apply<FM, FN>(*L[1], 0, g, lo[1], hi[1], acc, R1);
+      for (int k = 0; k < ns; ++k)
+        for (int t = 1; t < (L[k]->r + 15) / 16; ++t) {
+          lora_load<MODE, WN, FM, FN>(p, *L[k], t, arow, n0, wn, l32, g, R0);
+          lora_apply<FM, FN>(*L[k], t, g, lo[k], hi[k], acc, R0);
+        }
+    } else {
+      for (int k = 0; k < ns; ++k)
+        lora_scalar<MODE, WN, FM, FN>(p, *L[k], 0, acc, arow, n0, wn, l32, g, lo[k], hi[k]);
+    }
     wait_vmcnt<24>();  // tile 0 landed
     stage_barrier();
     rd(hb0, hb1, 0, x0, w0);

@@ -67,64 +67,137 @@ __device__ __forceinline__ int64_t out_col_of(int64_t n0, int wn, int f) {
 }
 
 // LoRA term acc += s * V[m, :] Wl(col, :)^T as extra MFMA steps (rank r in
-// steps of 16; s V rounded to bf16).  Called before the main reduction, so
-// that its operand loads overlap the pipeline fill: every load of a step is
-// issued unconditionally (indices clamped, values masked) before any use.
+// steps of 16; s V rounded to bf16), done before the main reduction.
+//
+// Fast form (r a multiple of 8 and Wl rows contiguous in j, wl_sj == 1): the
+// operands of a step are 16-byte vector loads (per lane two of V, one of Wl
+// per frag), issued by lora_load; lora_apply packs and multiplies.  Callers
+// issue step 0's loads before their own prologue loads so that the LoRA
+// latency hides behind them.  Otherwise gemm_lora_scalar: clamped scalar
+// loads, all issued before any use.
+template <int FM, int FN>
+struct LoraRegs {
+  u32x4 v[FM][2];  // fp32 V[token][j .. j+7]
+  u32x4 h[FN];     // bf16 Wl[col][j .. j+7]
+};
+
+__device__ __forceinline__ bool lora_fast(const LoraSide& L) { return (L.r & 7) == 0 && L.wl_sj == 1; }
+
+template <int MODE, int WN, int FM, int FN>
+__device__ __forceinline__ void lora_load(const GemmArgs& p, const LoraSide& L, int t, const int64_t (&arow)[FM],
+                                          int64_t n0, int wn, int l32, int g, LoraRegs<FM, FN>& R) {
+  int j0 = 16 * t + 8 * g;
+  if (j0 > L.r - 8) j0 = L.r - 8;  // out-of-range group: any valid address, masked in lora_apply
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    const u32x4* src = reinterpret_cast<const u32x4*>(L.V + arow[i] * L.r + j0);
+    R.v[i][0] = src[0];
+    R.v[i][1] = src[1];
+  }
+#pragma unroll
+  for (int f = 0; f < FN; ++f) {
+    int64_t c = out_col_of<MODE, WN, FN>(n0, wn, f) + l32;
+    if (c >= p.Nout) c = p.Nout - 1;
+    R.h[f] = *reinterpret_cast<const u32x4*>(L.Wl + c * L.wl_sc + j0);
+  }
+}
+
+template <int FM, int FN>
+__device__ __forceinline__ void lora_apply(const LoraSide& L, int t, int g, int f_lo, int f_hi,
+                                           f32x16 (&acc)[FM][FN], const LoraRegs<FM, FN>& R) {
+  const bool ok = 16 * t + 8 * g < L.r;
+  u32x4 vop[FM];
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    float y[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) y[e] = ok ? L.s * __uint_as_float(R.v[i][e >> 2][e & 3]) : 0.0f;
+    vop[i] = u32x4{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]), pack_bf16x2(y[4], y[5]),
+                   pack_bf16x2(y[6], y[7])};
+  }
+#pragma unroll
+  for (int f = 0; f < FN; ++f) {
+    if (f < f_lo || f >= f_hi) continue;
+    const u32x4 wop = ok ? R.h[f] : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < FM; ++i) acc[i][f] = mfma32(wop, vop[i], acc[i][f]);
+  }
+}
+
+template <int MODE, int WN, int FM, int FN>
+__device__ __forceinline__ void lora_scalar(const GemmArgs& p, const LoraSide& L, int t0, f32x16 (&acc)[FM][FN],
+                                            const int64_t (&arow)[FM], int64_t n0, int wn, int l32, int g, int f_lo,
+                                            int f_hi) {
+  const int steps = (L.r + 15) / 16;
+  for (int t = t0; t < steps; ++t) {
+    float x[FM][8];
+    uint32_t h[FN][8];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int j = 16 * t + 8 * g + e;
+        x[i][e] = L.V[arow[i] * L.r + (j < L.r ? j : L.r - 1)];
+      }
+#pragma unroll
+    for (int f = 0; f < FN; ++f) {
+      int64_t c = out_col_of<MODE, WN, FN>(n0, wn, f) + l32;
+      if (c >= p.Nout) c = p.Nout - 1;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int j = 16 * t + 8 * g + e;
+        h[f][e] = L.Wl[c * L.wl_sc + (int64_t)(j < L.r ? j : L.r - 1) * L.wl_sj];
+      }
+    }
+    u32x4 vop[FM];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      float y[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) y[e] = (16 * t + 8 * g + e < L.r) ? L.s * x[i][e] : 0.0f;
+      vop[i] = u32x4{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]), pack_bf16x2(y[4], y[5]),
+                     pack_bf16x2(y[6], y[7])};
+    }
+#pragma unroll
+    for (int f = 0; f < FN; ++f) {
+      if (f < f_lo || f >= f_hi) continue;
+      uint32_t hh[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) hh[e] = (16 * t + 8 * g + e < L.r) ? h[f][e] : 0u;
+      const u32x4 wop{hh[0] | (hh[1] << 16), hh[2] | (hh[3] << 16), hh[4] | (hh[5] << 16), hh[6] | (hh[7] << 16)};
+#pragma unroll
+      for (int i = 0; i < FM; ++i) acc[i][f] = mfma32(wop, vop[i], acc[i][f]);
+    }
+  }
+}
+
+// The LoRA sides of a mode: (side, output frags it adds to).  Split runs add
+// the LoRA term in split 0 only.
+template <int MODE, int FN, bool SPLIT>
+__device__ __forceinline__ int lora_sides(const GemmArgs& p, const LoraSide* (&L)[2], int (&lo)[2], int (&hi)[2]) {
+  if constexpr (MODE == MODE_FWD_SWIGLU) {
+    L[0] = &p.l0; lo[0] = 0; hi[0] = FN / 2;
+    L[1] = &p.l1; lo[1] = FN / 2; hi[1] = FN;
+    return 2;
+  } else if constexpr (MODE == MODE_BWD_DUAL) {
+    L[0] = &p.l0; lo[0] = 0; hi[0] = FN;
+    L[1] = &p.l1; lo[1] = 0; hi[1] = FN;
+    return 2;
+  } else {
+    L[0] = &p.l0; lo[0] = 0; hi[0] = FN;
+    L[1] = &p.l0; lo[1] = 0; hi[1] = 0;
+    return (!SPLIT || blockIdx.y == 0) ? 1 : 0;
+  }
+}
+
+// The whole LoRA term in one call (loads, then use).
 template <int MODE, int WN, int FM, int FN, bool SPLIT>
 __device__ __forceinline__ void gemm_lora(const GemmArgs& p, f32x16 (&acc)[FM][FN], const int64_t (&arow)[FM],
                                           int64_t n0, int wn, int l32, int g) {
-  auto lora = [&](const LoraSide& L, int f_lo, int f_hi) {
-    const int steps = (L.r + 15) / 16;
-    for (int t = 0; t < steps; ++t) {
-      float x[FM][8];
-      uint32_t h[FN][8];
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int j = 16 * t + 8 * g + e;
-          x[i][e] = L.V[arow[i] * L.r + (j < L.r ? j : L.r - 1)];
-        }
-#pragma unroll
-      for (int f = 0; f < FN; ++f) {
-        int64_t c = out_col_of<MODE, WN, FN>(n0, wn, f) + l32;
-        if (c >= p.Nout) c = p.Nout - 1;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int j = 16 * t + 8 * g + e;
-          h[f][e] = L.Wl[c * L.wl_sc + (int64_t)(j < L.r ? j : L.r - 1) * L.wl_sj];
-        }
-      }
-      u32x4 vop[FM];
-#pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        float y[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) y[e] = (16 * t + 8 * g + e < L.r) ? L.s * x[i][e] : 0.0f;
-        vop[i] = u32x4{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]), pack_bf16x2(y[4], y[5]),
-                       pack_bf16x2(y[6], y[7])};
-      }
-#pragma unroll
-      for (int f = 0; f < FN; ++f) {
-        if (f < f_lo || f >= f_hi) continue;
-        uint32_t hh[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) hh[e] = (16 * t + 8 * g + e < L.r) ? h[f][e] : 0u;
-        const u32x4 wop{hh[0] | (hh[1] << 16), hh[2] | (hh[3] << 16), hh[4] | (hh[5] << 16), hh[6] | (hh[7] << 16)};
-#pragma unroll
-        for (int i = 0; i < FM; ++i) acc[i][f] = mfma32(wop, vop[i], acc[i][f]);
-      }
-    }
-  };
-  if constexpr (MODE == MODE_FWD_SWIGLU) {
-    lora(p.l0, 0, FN / 2);
-    lora(p.l1, FN / 2, FN);
-  } else if constexpr (MODE == MODE_BWD_DUAL) {
-    lora(p.l0, 0, FN);
-    lora(p.l1, 0, FN);
-  } else {
-    if (!SPLIT || blockIdx.y == 0) lora(p.l0, 0, FN);  // split runs: the LoRA term goes into split 0
-  }
+  const LoraSide* L[2];
+  int lo[2], hi[2];
+  const int ns = lora_sides<MODE, FN, SPLIT>(p, L, lo, hi);
+  for (int k = 0; k < ns; ++k) lora_scalar<MODE, WN, FM, FN>(p, *L[k], 0, acc, arow, n0, wn, l32, g, lo[k], hi[k]);
 }
 
 // Stores of one output tile.  acc[i][f]: token frag i (rows

@@ -106,7 +106,7 @@ inline LinearWs linear_ws(int64_t M, int64_t N, int64_t K, int r) {
 
   GemmPlan pb = plan_gemm(M, K, N, true);
   w.bwd_T = align256((size_t)M * r * 4);
-  w.bwd_BT = align256((size_t)N * r * 2);
+  w.bwd_BT = align256((size_t)N * r * 2) + align256((size_t)K * r * 2);  // B^T [r, N], A^T [K, r]
   w.bwd_part = (!bg && pb.splits > 1) ? align256((size_t)pb.splits * M * K * 4) : 0;
   const int ts = plan_down_splits(M, N);
   w.bwd_down = ts > 1 ? align256((size_t)ts * M * r * 4) : 0;
@@ -148,8 +148,9 @@ inline MlpWs mlp_ws(int64_t M, int64_t D, int64_t I, int rg, int ru, int rd) {
   w.bwd_dU = align256((size_t)M * I * 2);
   w.bwd_Tg = align256((size_t)M * rg * 4);
   w.bwd_Tu = align256((size_t)M * ru * 4);
-  // B_d^T [rd, D], B_g^T [rg, I], B_u^T [ru, I]
-  w.bwd_BT = align256((size_t)rd * D * 2) + align256((size_t)rg * I * 2) + align256((size_t)ru * I * 2);
+  // B_d^T [rd, D], B_g^T [rg, I], B_u^T [ru, I]; A_d^T [I, rd], A_g^T [D, rg], A_u^T [D, ru]
+  w.bwd_BT = align256((size_t)rd * D * 2) + align256((size_t)rg * I * 2) + align256((size_t)ru * I * 2) +
+             align256((size_t)I * rd * 2) + align256((size_t)D * rg * 2) + align256((size_t)D * ru * 2);
   const int t1 = plan_down_splits(M, D), t2 = plan_down_splits(M, I);
   size_t e1 = t1 > 1 ? align256((size_t)t1 * M * rd * 4) : 0;
   size_t e2 = t2 > 1 ? align256((size_t)t2 * M * rmax * 4) : 0;
