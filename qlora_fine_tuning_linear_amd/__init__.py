@@ -319,6 +319,7 @@ GEMM_KINDS = {0: "fwd", 1: "fwd_swiglu", 2: "bwd_dx", 3: "bwd_dh_swiglu", 4: "bw
 # trace kind = GEMM kind + 8 when the bf16-staged kernel (bgemm_kernel) ran
 GEMM_KERNELS = {k: "qgemm_kernel" for k in GEMM_KINDS}
 GEMM_KERNELS.update({k + 8: "bgemm_kernel" for k in GEMM_KINDS})
+GEMM_KERNELS.update({k + 16: "skinny_kernel" for k in GEMM_KINDS})
 
 
 class LaunchTrace:

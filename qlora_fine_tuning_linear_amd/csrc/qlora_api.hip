@@ -59,6 +59,29 @@ hipError_t traced_gemm(int mode, bool bf16, const GemmArgs& a, const qplan::Gemm
   return e;
 }
 
+// Trace slot around one launch (-1: not traced).
+int32_t trace_begin(int32_t kind, hipStream_t st, hipError_t* err) {
+  *err = hipSuccess;
+  if (g_trace.capacity <= 0 || !g_trace.count) return -1;
+  const int32_t idx = (*g_trace.count)++;
+  if (idx >= g_trace.capacity) return -1;
+  *err = hipEventRecord(static_cast<hipEvent_t>(g_trace.begin[idx]), st);
+  g_trace.kinds[idx] = kind;
+  return idx;
+}
+hipError_t trace_end(int32_t idx, hipError_t e, hipStream_t st) {
+  if (e == hipSuccess && idx >= 0) e = hipEventRecord(static_cast<hipEvent_t>(g_trace.end[idx]), st);
+  return e;
+}
+
+// Skinny-M forward GEMM, traced as kind mode + 16.
+hipError_t traced_skinny_fwd(const SkinnyArgs& a, const qplan::SkinnyPlan& pl, hipStream_t st) {
+  hipError_t e;
+  const int32_t idx = trace_begin(MODE_FWD + 16, st, &e);
+  if (e != hipSuccess) return e;
+  return trace_end(idx, launch_skinny_fwd(a, pl, st), st);
+}
+
 hipError_t traced_gemm_q(int mode, const GemmArgs& a, const qplan::GemmPlan& pl, hipStream_t st) {
   return traced_gemm(mode, false, a, pl, st);
 }
@@ -151,6 +174,35 @@ int qlora_linear_fwd(const qlora_linear* L, const void* X, int64_t M, void* Y, f
   float* part = reinterpret_cast<float*>(bytes(ws));
   float* down_part = reinterpret_cast<float*>(bytes(ws) + w.fwd_part);
 
+  if (qplan::use_skinny_fwd(M, L->r)) {
+    // XA partials; the skinny GEMM sums them, writes XA and adds s XA B^T
+    const int ds = qplan::plan_down_splits(M, K);
+    const int dsu = qplan::down_splits_used(K, ds);
+    QHIP(launch_lora_down(u16(X), M, K, u16(L->A), L->r, nullptr, 0, XA_saved, nullptr, ds, down_part, st, false));
+    const qplan::SkinnyPlan sp = qplan::plan_skinny_fwd(N, K);
+    SkinnyArgs a;
+    memset(&a, 0, sizeof(a));
+    a.X = u16(X);
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    a.w = to_dev(L->W0);
+    a.codebook = L->W0.codebook;
+    a.vpart = dsu > 1 ? down_part : XA_saved;
+    a.vsplits = dsu;
+    a.vout = dsu > 1 ? XA_saved : nullptr;
+    a.Wl = static_cast<const uint16_t*>(L->B);
+    a.wl_sc = L->r;
+    a.wl_sj = 1;
+    a.r = L->r;
+    a.s = lora_s(*L);
+    a.out = u16m(Y);
+    a.part = sp.splits > 1 ? part : nullptr;
+    a.kps = sp.kps;
+    QHIP(traced_skinny_fwd(a, sp, st));
+    if (sp.splits > 1) QHIP(launch_splitk_finish(part, sp.splits, M, N, u16m(Y), st));
+    return QLORA_OK;
+  }
   // XA = X A^T (kept for the backward)
   QHIP(launch_lora_down(u16(X), M, K, u16(L->A), L->r, nullptr, 0, XA_saved, nullptr,
                         qplan::plan_down_splits(M, K), down_part, st));
@@ -207,7 +259,7 @@ int qlora_linear_bwd(const qlora_linear* L, const void* dY, const void* X, const
   QHIP(launch_transpose_rn(u16(L->A), r, (int)K, AT, st));  // A [r, K] -> A^T [K, r]
   QHIP(launch_lora_down(u16(dY), M, N, BT, r, nullptr, 0, T, nullptr, qplan::plan_down_splits(M, N), down_part, st));
   // dX = dY W0 + s T A
-  const qplan::GemmPlan pl = qplan::plan_gemm(M, K, N, true);
+  const qplan::GemmPlan pl = qplan::plan_gemm(M, K, N, true, true);
   GemmArgs a = gemm_args();
   a.act0 = u16(dY);
   a.M = M;

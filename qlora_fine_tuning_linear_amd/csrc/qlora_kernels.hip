@@ -802,6 +802,9 @@ static hipError_t run_gemm(GemmArgs a, const qplan::GemmPlan& pl, hipStream_t st
 template <int MODE, bool DQ>
 static hipError_t run_gemm_cfg(const GemmArgs& a, const qplan::GemmPlan& pl, hipStream_t st) {
   if (pl.cfg == qplan::CFG_L256) return run_gemm<MODE, 4, 2, 2, 4, DQ, true>(a, pl, st);
+  if constexpr (MODE == MODE_BWD) {
+    if (pl.cfg == qplan::CFG_SKINNY_TR) return run_gemm<MODE, 1, 8, 2, 1, DQ, true>(a, pl, st);
+  }
   if constexpr (MODE == MODE_FWD_SWIGLU) {
     return run_gemm<MODE, 1, 2, 2, 2, DQ, false>(a, pl, st);
   } else {
@@ -835,7 +838,7 @@ hipError_t launch_splitk_finish(const float* part, int splits, int64_t M, int64_
 
 hipError_t launch_lora_down(const uint16_t* Z, int64_t M, int64_t Kred, const uint16_t* W0, int r0,
                             const uint16_t* W1, int r1, float* V0, float* V1, int splits, float* part,
-                            hipStream_t st) {
+                            hipStream_t st, bool finish) {
   if (M == 0) return hipSuccess;
   const int64_t C = Kred / 64;
   const int64_t per = (C + splits - 1) / splits;
@@ -851,7 +854,7 @@ hipError_t launch_lora_down(const uint16_t* Z, int64_t M, int64_t Kred, const ui
     default: return hipErrorInvalidValue;
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || S == 1) return e;
+  if (e != hipSuccess || S == 1 || !finish) return e;
   down_finish_kernel<<<grid1(M * (r0 + r1), 256), 256, 0, st>>>(part, S, M, r0, r1, V0, V1);
   return hipGetLastError();
 }

@@ -56,6 +56,28 @@ struct GemmArgs {
   int64_t ldw, wrows;
 };
 
+// Skinny-M forward GEMM (qlora_skinny.hip): out[m, n] = sum_k X[m, k]
+// deq(w)[n, k] + s sum_j V[m, j] Wl(n, j), V = sum_z vpart[z] ([M, r] fp32
+// partials of the down-projection, vsplits of them; when vout is set, V is
+// also written there).  With part set, split z of the reduction writes fp32
+// partials part[z][M][N] instead of out (LoRA term in split 0 only).
+struct SkinnyArgs {
+  const uint16_t* X;
+  int64_t M, N, K;
+  Nf4Dev w;
+  const float* codebook;
+  const float* vpart;
+  int32_t vsplits;
+  float* vout;
+  const uint16_t* Wl;
+  int64_t wl_sc, wl_sj;
+  int32_t r;
+  float s;
+  uint16_t* out;
+  float* part;
+  int32_t kps;  // 64-wide reduction tiles per split
+};
+
 hipError_t launch_nf4_quantize(const float* W, int64_t nblocks, const float* codebook, int dq, uint8_t* codes,
                                float* absmax, uint8_t* absmax_q, float* absmax_scale, hipStream_t st);
 hipError_t launch_nf4_dequantize(const Nf4Dev& w, const float* codebook, int out_f32, void* out, hipStream_t st);
@@ -72,10 +94,14 @@ hipError_t launch_dequant_trans(const Nf4Dev& w, const float* codebook, uint16_t
                                 hipStream_t st);
 hipError_t launch_splitk_finish(const float* part, int splits, int64_t M, int64_t Nout, uint16_t* out,
                                 hipStream_t st);
+bool skinny_fwd_supported(int64_t M, int r);
+hipError_t launch_skinny_fwd(const SkinnyArgs& a, const qplan::SkinnyPlan& pl, hipStream_t st);
 // V0 | V1 = Z W0^T | Z W1^T, W0 [r0, Kred], W1 [r1, Kred] (r0 + r1 <= 128).
+// With finish = false and more than one split (qplan::down_splits_used) the
+// fp32 partials stay in part[split][M][r0 + r1] for the consumer to sum.
 hipError_t launch_lora_down(const uint16_t* Z, int64_t M, int64_t Kred, const uint16_t* W0, int r0,
                             const uint16_t* W1, int r1, float* V0, float* V1, int splits, float* part,
-                            hipStream_t st);
+                            hipStream_t st, bool finish = true);
 // B [N, r] -> B^T [r, N]
 hipError_t launch_transpose_rn(const uint16_t* B, int64_t N, int r, uint16_t* BT, hipStream_t st);
 hipError_t launch_lora_grad(int zmode, const uint16_t* Z0, const uint16_t* Z1, int64_t M, int64_t P,

@@ -13,7 +13,10 @@ namespace qplan {
 //             activations staged through LDS (2 waves per SIMD)
 //   SKINNY  : 1x2 waves, 2x1 frags per wave ->  64 tokens x  64 output columns,
 //             activations loaded straight into registers
-enum GemmCfg { CFG_L256 = 0, CFG_SKINNY = 1 };
+//   SKINNY_TR: 1x4 waves, 2x2 frags per wave -> 64 tokens x 256 output columns
+//             of the transposed (backward) product, activations staged through
+//             LDS: each weight row segment of a tile is one 128-byte line
+enum GemmCfg { CFG_L256 = 0, CFG_SKINNY = 1, CFG_SKINNY_TR = 2 };
 
 constexpr int kNumCUs = 256;
 constexpr int64_t kBK = 64;  // reduction tile = one absmax block
@@ -29,12 +32,15 @@ struct GemmPlan {
   int ktiles_per_split;  // 64-wide reduction tiles per split
 };
 
-// M tokens, Nout output columns, Kred reduction length (multiple of 64).
-inline GemmPlan plan_gemm(int64_t M, int64_t Nout, int64_t Kred, bool allow_split) {
+// M tokens, Nout output columns, Kred reduction length (multiple of 64);
+// trans: the single-linear backward product (the one transposed mode that
+// may split its reduction).
+inline GemmPlan plan_gemm(int64_t M, int64_t Nout, int64_t Kred, bool allow_split, bool trans = false) {
   GemmPlan p{};
   p.cfg = (M <= 128) ? CFG_SKINNY : CFG_L256;
+  if (M <= 64 && trans && allow_split) p.cfg = CFG_SKINNY_TR;
   p.bm = (p.cfg == CFG_L256) ? 256 : 64;
-  p.bn = (p.cfg == CFG_L256) ? 256 : 64;
+  p.bn = (p.cfg == CFG_SKINNY) ? 64 : 256;
   p.tiles_m = cdiv(M, p.bm);
   p.tiles_n = cdiv(Nout, p.bn);
   const int64_t kt = Kred / kBK;
@@ -64,6 +70,51 @@ inline int plan_down_splits(int64_t M, int64_t Kred) {
   if (s > max_s) s = max_s;
   return (int)(s < 1 ? 1 : s);
 }
+
+// Splits that launch_lora_down actually runs for a requested split count.
+inline int down_splits_used(int64_t Kred, int splits) {
+  const int64_t C = Kred / 64;
+  if (C == 0 || splits <= 1) return 1;
+  const int64_t per = cdiv(C, splits);
+  return (int)cdiv(C, per);
+}
+
+// Skinny-M forward GEMM (M <= 64): one 4-wave workgroup per 16 * fn weight
+// rows, fn from {1, 2, 4, 7, 8} the smallest that puts at most one
+// workgroup on each CU; with fewer tiles than CUs the reduction is split
+// (each wave keeping >= 2 of the 64-wide tiles), and it is split further
+// while the workgroup's fp32 block absmax (16 fn rows x tiles) exceeds the
+// 64 KB it stages in LDS.
+struct SkinnyPlan {
+  int fn;
+  int splits;
+  int kps;  // reduction tiles per split
+};
+
+inline SkinnyPlan plan_skinny_fwd(int64_t N, int64_t K) {
+  static const int kFn[] = {1, 2, 4, 7, 8};
+  SkinnyPlan p{8, 1, 0};
+  for (int f : kFn)
+    if (cdiv(N, 16 * f) <= kNumCUs) {
+      p.fn = f;
+      break;
+    }
+  const int64_t tiles = cdiv(N, 16 * p.fn);
+  const int64_t kt = K / kBK;
+  int64_t s = 1;
+  if (tiles < kNumCUs) {
+    s = kNumCUs / tiles;
+    const int64_t max_s = kt / 8 > 0 ? kt / 8 : 1;
+    if (s > max_s) s = max_s;
+  }
+  const int64_t max_tiles = (64 * 1024) / (4 * 16 * p.fn);
+  if (s < cdiv(kt, max_tiles)) s = cdiv(kt, max_tiles);
+  const int64_t per = cdiv(kt, s > 0 ? s : 1);
+  p.kps = (int)(per > 0 ? per : 1);
+  p.splits = (int)(kt > 0 ? cdiv(kt, p.kps) : 1);
+  return p;
+}
+inline bool use_skinny_fwd(int64_t M, int r) { return M >= 1 && M <= 64 && r <= 64; }
 
 // Token splits of a LoRA-gradient reduction out[p, j] = sum_m Z[m, p] V[m, j].
 // Each split writes an fp32 [P, r] partial; keep the partials small next to Z.
@@ -99,12 +150,16 @@ inline LinearWs linear_ws(int64_t M, int64_t N, int64_t K, int r) {
   const bool bg = use_bgemm(M);
   GemmPlan pf = plan_gemm(M, N, K, true);
   w.fwd_part = (!bg && pf.splits > 1) ? align256((size_t)pf.splits * M * N * 4) : 0;
+  if (use_skinny_fwd(M, r)) {
+    const SkinnyPlan sp = plan_skinny_fwd(N, K);
+    w.fwd_part = sp.splits > 1 ? align256((size_t)sp.splits * M * N * 4) : 0;
+  }
   const int ds = plan_down_splits(M, K);
   w.fwd_down = ds > 1 ? align256((size_t)ds * M * r * 4) : 0;
   w.wbuf = bg ? align256((size_t)N * K * 2) : 0;
   w.fwd_total = w.fwd_part + w.fwd_down + w.wbuf;
 
-  GemmPlan pb = plan_gemm(M, K, N, true);
+  GemmPlan pb = plan_gemm(M, K, N, true, true);
   w.bwd_T = align256((size_t)M * r * 4);
   w.bwd_BT = align256((size_t)N * r * 2) + align256((size_t)K * r * 2);  // B^T [r, N], A^T [K, r]
   w.bwd_part = (!bg && pb.splits > 1) ? align256((size_t)pb.splits * M * K * 4) : 0;

@@ -59,6 +59,14 @@ CASES = [
     synth.LinearCfg("m520_1024x1088_r24", M=520, K=1024, N=1088, r=24, alpha=8.0, dq_group=0),
     synth.LinearCfg("m1300_384x448_r16", M=1300, K=384, N=448, r=16, alpha=16.0, dq_group=256),
     synth.LinearCfg("m2049_192x1216_r40", M=2049, K=192, N=1216, r=40, alpha=20.0, dq_group=0),
+    # skinny (M <= 64) forward: reduction splits, ragged rows / tokens, wave
+    # ranges that leave a partial load ring, the largest rank it takes
+    synth.LinearCfg("m16_4096x192_r64", M=16, K=4096, N=192, r=64, alpha=16.0, dq_group=256),
+    synth.LinearCfg("m16_256x20032_r8", M=16, K=256, N=20032, r=8, alpha=16.0, dq_group=0),
+    synth.LinearCfg("m64_1024x1088_r48", M=64, K=1024, N=1088, r=48, alpha=12.0, dq_group=0),
+    synth.LinearCfg("m50_640x4096_r16", M=50, K=640, N=4096, r=16, alpha=16.0, dq_group=256),
+    synth.LinearCfg("m7_8192x1024_r32", M=7, K=8192, N=1024, r=32, alpha=8.0, dq_group=0),
+    synth.LinearCfg("m64_1024x512_r65", M=64, K=1024, N=512, r=65, alpha=13.0, dq_group=0),
 ]
 
 
@@ -99,6 +107,15 @@ def test_m_zero(codebook):
     q.qlora_linear_bwd(L, torch.empty(0, 128, dtype=torch.bfloat16, device="cuda"), X, XA, dA=dA, dB=dB)
     torch.cuda.synchronize()
     assert torch.all(dA == 0) and torch.all(dB == 0)
+
+
+def test_skinny_forward_is_bitwise_deterministic(codebook):
+    cfg = synth.LinearCfg("det_skinny", M=48, K=2048, N=640, r=16, alpha=16.0, dq_group=256)
+    out, L, X, dY = run_case(cfg, 10, codebook)
+    for _ in range(2):
+        Y2, XA2 = q.qlora_linear_fwd(L, X)
+        assert torch.equal(Y2.view(torch.int16), out["Y"][0].view(torch.int16))
+        assert torch.equal(XA2, out["XA"][0])
 
 
 def test_backward_is_bitwise_deterministic(codebook):
