@@ -254,12 +254,48 @@ int qlora_linear_bwd(const qlora_linear* L, const void* dY, const void* X, const
   float* down_part = reinterpret_cast<float*>(after_bt + w.bwd_part);
   float* grad_part = reinterpret_cast<float*>(after_bt + w.bwd_part + w.bwd_down);
 
+  const qplan::GemmPlan pl = qplan::plan_gemm(M, K, N, true, true);
+  if (!qplan::use_bgemm(M) && pl.cfg == qplan::CFG_SKINNY_TR && pl.splits > 1 && skinny_finish_supported(M, r)) {
+    // Skinny M: T partials, the split transposed product without its LoRA
+    // term, then one finish launch for dX (+ s T A), dA and dB.
+    QHIP(launch_transpose_rn(u16(L->B), N, r, BT, st));
+    const int ds = qplan::plan_down_splits(M, N);
+    const int dsu = qplan::down_splits_used(N, ds);
+    QHIP(launch_lora_down(u16(dY), M, N, BT, r, nullptr, 0, T, nullptr, ds, down_part, st, false));
+    GemmArgs a = gemm_args();
+    a.act0 = u16(dY);
+    a.M = M;
+    a.Nout = K;
+    a.Kred0 = N;
+    a.w0 = to_dev(L->W0);
+    a.codebook = L->W0.codebook;
+    a.partial = part;
+    QHIP(traced_gemm_q(MODE_BWD, a, pl, st));
+    SkinnyFinishArgs f;
+    memset(&f, 0, sizeof(f));
+    f.M = M;
+    f.N = N;
+    f.K = K;
+    f.r = r;
+    f.s = s;
+    f.part = part;
+    f.splits = pl.splits;
+    f.tpart = dsu > 1 ? down_part : T;
+    f.tsplits = dsu;
+    f.XA = XA_saved;
+    f.X = u16(X);
+    f.dY = u16(dY);
+    f.A = u16(L->A);
+    f.dX = u16m(dX);
+    f.dA = u16m(dA);
+    f.dB = u16m(dB);
+    return hip_status(launch_skinny_bwd_finish(f, st));
+  }
   // T = dY B  (B^T first, so that the product reads rows)
   QHIP(launch_transpose_rn(u16(L->B), N, r, BT, st));
   QHIP(launch_transpose_rn(u16(L->A), r, (int)K, AT, st));  // A [r, K] -> A^T [K, r]
   QHIP(launch_lora_down(u16(dY), M, N, BT, r, nullptr, 0, T, nullptr, qplan::plan_down_splits(M, N), down_part, st));
   // dX = dY W0 + s T A
-  const qplan::GemmPlan pl = qplan::plan_gemm(M, K, N, true, true);
   GemmArgs a = gemm_args();
   a.act0 = u16(dY);
   a.M = M;

@@ -78,6 +78,26 @@ struct SkinnyArgs {
   int32_t kps;  // 64-wide reduction tiles per split
 };
 
+// Skinny-M backward finish (qlora_skinny.hip): dX = sum of the split
+// partials + s T A, dA = s T^T X, dB = s dY^T XA (T = sum of tpart), bf16
+// outputs; M <= 64, r <= 128, K and N multiples of 64.
+struct SkinnyFinishArgs {
+  int64_t M, N, K;
+  int32_t r;
+  float s;
+  const float* part;   // [splits][M][K]
+  int32_t splits;
+  const float* tpart;  // [tsplits][M][r]
+  int32_t tsplits;
+  const float* XA;     // [M][r]
+  const uint16_t* X;   // [M][K]
+  const uint16_t* dY;  // [M][N]
+  const uint16_t* A;   // [r][K]
+  uint16_t* dX;
+  uint16_t* dA;
+  uint16_t* dB;
+};
+
 hipError_t launch_nf4_quantize(const float* W, int64_t nblocks, const float* codebook, int dq, uint8_t* codes,
                                float* absmax, uint8_t* absmax_q, float* absmax_scale, hipStream_t st);
 hipError_t launch_nf4_dequantize(const Nf4Dev& w, const float* codebook, int out_f32, void* out, hipStream_t st);
@@ -95,6 +115,8 @@ hipError_t launch_dequant_trans(const Nf4Dev& w, const float* codebook, uint16_t
 hipError_t launch_splitk_finish(const float* part, int splits, int64_t M, int64_t Nout, uint16_t* out,
                                 hipStream_t st);
 bool skinny_fwd_supported(int64_t M, int r);
+bool skinny_finish_supported(int64_t M, int r);
+hipError_t launch_skinny_bwd_finish(const SkinnyFinishArgs& a, hipStream_t st);
 hipError_t launch_skinny_fwd(const SkinnyArgs& a, const qplan::SkinnyPlan& pl, hipStream_t st);
 // V0 | V1 = Z W0^T | Z W1^T, W0 [r0, Kred], W1 [r1, Kred] (r0 + r1 <= 128).
 // With finish = false and more than one split (qplan::down_splits_used) the

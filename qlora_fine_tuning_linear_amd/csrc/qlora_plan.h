@@ -107,7 +107,7 @@ inline SkinnyPlan plan_skinny_fwd(int64_t N, int64_t K) {
     const int64_t max_s = kt / 8 > 0 ? kt / 8 : 1;
     if (s > max_s) s = max_s;
   }
-  const int64_t max_tiles = (64 * 1024) / (4 * 16 * p.fn);
+  const int64_t max_tiles = (64 * 1024) / (4 * 16 * p.fn) - 4;  // row stride tiles + 4
   if (s < cdiv(kt, max_tiles)) s = cdiv(kt, max_tiles);
   const int64_t per = cdiv(kt, s > 0 ? s : 1);
   p.kps = (int)(per > 0 ? per : 1);

@@ -48,20 +48,64 @@ __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
 
 constexpr int SK_WAVES = 4;   // one wave per SIMD: 512 registers each
 constexpr int SK_TF = 4;      // token frags of 16: up to 64 tokens
-constexpr int SK_DEPTH = 4;   // register sets of the load ring (tiles in flight + 1)
+constexpr int SK_DEPTH = 3;   // register sets of the load ring (tiles in flight + 1)
 constexpr int SK_ABS_LDS = 64 * 1024;  // bytes of block absmax staged per workgroup
+
+// Byte offset of a codebook entry: 4 * (bits [8B + 2, 8B + 6) of x), i.e.
+// with x = c << 2 the low nibble of byte B of c, with x = c >> 2 its high
+// nibble, selected and masked by one SDWA instruction (the codebook sits at
+// LDS address 0, so this is the lookup's address).
+#define SK_NIB(B)                                                                                             \
+  __device__ __forceinline__ uint32_t nib_off##B(uint32_t x) {                                                \
+    uint32_t r;                                                                                               \
+    asm("v_and_b32_sdwa %0, 60, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_" #B \
+        : "=v"(r)                                                                                             \
+        : "v"(x));                                                                                            \
+    return r;                                                                                                 \
+  }
+SK_NIB(0)
+SK_NIB(1)
+SK_NIB(2)
+SK_NIB(3)
+#undef SK_NIB
+
+// 8 codes of one dword -> their 8 fp32 codebook values, element order (cb
+// is the codebook at LDS address 0)
+__device__ __forceinline__ void sk_lookup8(const float* cb, uint32_t c, float* v) {
+  const uint32_t lo = c << 2, hi = c >> 2;
+  const char* t = reinterpret_cast<const char*>(cb);
+  v[0] = *reinterpret_cast<const float*>(t + nib_off0(lo));
+  v[1] = *reinterpret_cast<const float*>(t + nib_off0(hi));
+  v[2] = *reinterpret_cast<const float*>(t + nib_off1(lo));
+  v[3] = *reinterpret_cast<const float*>(t + nib_off1(hi));
+  v[4] = *reinterpret_cast<const float*>(t + nib_off2(lo));
+  v[5] = *reinterpret_cast<const float*>(t + nib_off2(hi));
+  v[6] = *reinterpret_cast<const float*>(t + nib_off3(lo));
+  v[7] = *reinterpret_cast<const float*>(t + nib_off3(hi));
+}
+
+// LDS of the forward kernel, the codebook first (LDS address 0, which the
+// lookups above rely on: it is the kernel's only LDS object).
+struct SkFwdSmem {
+  float cb[16];
+  float vs[64 * 64];  // V = sum of the down-projection partials, [M][r]
+  // block absmax [row - n0][tile - kb] (row stride ntile + 4) during the main
+  // loop; afterwards the per-wave partial tiles of the reduction
+  float absl[SK_ABS_LDS / 4];
+};
 
 template <int FN, bool DQ>
 __global__ __launch_bounds__(256) void skinny_fwd_kernel(SkinnyArgs p) {
   constexpr int TF = SK_TF;
   constexpr int R = 16 * FN;
   constexpr int D = SK_DEPTH;
-  __shared__ float cb[16];
-  __shared__ float red[SK_WAVES][TF * 4 * 64];
-  __shared__ float vs[64 * 64];                 // V = sum of the down-projection partials, [M][r]
-  __shared__ float absl[SK_ABS_LDS / 4];        // block absmax, [tile - kb][row - n0]
+  __shared__ SkFwdSmem sm;
+  float* cb = sm.cb;
+  float* vs = sm.vs;
+  float* absl = sm.absl;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, q = lane >> 4;
   const int64_t n0 = (int64_t)blockIdx.x * R;
   const int KT = (int)(p.K / 64);
@@ -71,21 +115,20 @@ __global__ __launch_bounds__(256) void skinny_fwd_kernel(SkinnyArgs p) {
   const int nt = we - wb;  // this wave's tiles
   const bool lora_here = blockIdx.y == 0 && p.r > 0;
 
-  // ---- operand pointers (rows clamped into range; clamped rows are not stored)
-  const uint8_t* cptr[FN];
+  // ---- operands through buffer resources (the workgroup's code rows, the
+  // activations) with 32-bit lane offsets and the tile offset in the scalar
+  // offset; rows are clamped into range (clamped rows are not stored)
+  const int rows = (int)min((int64_t)R, p.N - n0);
+  const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(p.w.codes + n0 * (p.K / 2)), (short)0, (int)(rows * (p.K / 2)), 0x00020000);
+  const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.X), (short)0,
+                                                                      (int)(p.M * p.K * 2), 0x00020000);
+  uint32_t coff[FN];
 #pragma unroll
-  for (int f = 0; f < FN; ++f) {
-    int64_t row = n0 + 16 * f + l16;
-    if (row >= p.N) row = p.N - 1;
-    cptr[f] = p.w.codes + row * (p.K / 2) + 8 * q;
-  }
-  const uint16_t* xptr[TF];
+  for (int f = 0; f < FN; ++f) coff[f] = (uint32_t)(min(16 * f + l16, rows - 1) * (p.K / 2) + 8 * q);
+  uint32_t xoff[TF];
 #pragma unroll
-  for (int i = 0; i < TF; ++i) {
-    int64_t m = 16 * i + l16;
-    if (m >= p.M) m = p.M - 1;
-    xptr[i] = p.X + m * p.K + 16 * q;
-  }
+  for (int i = 0; i < TF; ++i) xoff[i] = (uint32_t)(min(16 * i + l16, (int)p.M - 1) * p.K * 2 + 32 * q);
 
   struct Regs {
     u32x4 x[TF][2];
@@ -93,11 +136,14 @@ __global__ __launch_bounds__(256) void skinny_fwd_kernel(SkinnyArgs p) {
   };
   auto load = [&](int kt, Regs& g) {
 #pragma unroll
-    for (int f = 0; f < FN; ++f) g.c[f] = *reinterpret_cast<const u32x2*>(cptr[f] + (int64_t)kt * 32);
+    for (int f = 0; f < FN; ++f)
+      g.c[f] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(crs, coff[f], kt * 32, 0));
 #pragma unroll
     for (int i = 0; i < TF; ++i)
 #pragma unroll
-      for (int s = 0; s < 2; ++s) g.x[i][s] = *reinterpret_cast<const u32x4*>(xptr[i] + (int64_t)kt * 64 + 8 * s);
+      for (int s = 0; s < 2; ++s)
+        g.x[i][s] =
+            __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xrs, xoff[i], kt * 128 + 16 * s, 0));
   };
 
   // the first D - 1 tiles are requested before anything else
@@ -107,14 +153,16 @@ __global__ __launch_bounds__(256) void skinny_fwd_kernel(SkinnyArgs p) {
     for (int u = 0; u < D - 1; ++u) load(wb + min(u, nt - 1), g[u]);
   }
 
-  // ---- block absmax of the workgroup's rows and tiles into LDS (fp32).
-  // Row rr's tiles are contiguous in memory; when they start and end on a
-  // 4-tile boundary they are read 4 at a time (one 4-byte load of codes with
-  // double quantization, one 16-byte load otherwise), all of a thread's
-  // loads issued before the first is used.
+  // ---- block absmax of the workgroup's rows and tiles into LDS as fp32,
+  // row-major with row stride ntile + 4.  Row rr's tiles are contiguous in
+  // memory; when they start and end on a 4-tile boundary they are read 4 at a
+  // time (a 4-byte load of codes with double quantization, a 16-byte load
+  // otherwise) and written as one 16-byte LDS store, all of a thread's loads
+  // issued before the first is used.
   if (tid < 16) cb[tid] = p.codebook[tid];
+  const int ntile = ke - kb;
+  const int astr = ntile + 4;
   {
-    const int ntile = ke - kb;
     if (((KT | kb | ntile) & 3) == 0) {
       const int nq = ntile >> 2, total = R * nq;  // 4-tile groups
       constexpr int PER = SK_ABS_LDS / 16 / 256;     // groups per thread at most
@@ -142,15 +190,14 @@ __global__ __launch_bounds__(256) void skinny_fwd_kernel(SkinnyArgs p) {
         const int e = tid + 256 * j;
         if (e < total) {
           const int rr = e / nq, g4 = e - rr * nq;
+          f32x4 a4;
+          if constexpr (DQ) {
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            float a;
-            if constexpr (DQ)
-              a = (float)((cq[j] >> (8 * u)) & 0xFFu) * sc[j];
-            else
-              a = af[j][u];
-            absl[(4 * g4 + u) * R + rr] = a;
+            for (int u = 0; u < 4; ++u) a4[u] = (float)((cq[j] >> (8 * u)) & 0xFFu) * sc[j];
+          } else {
+            a4 = af[j];
           }
+          *reinterpret_cast<f32x4*>(absl + rr * astr + 4 * g4) = a4;
         }
       }
     } else {
@@ -169,7 +216,7 @@ __global__ __launch_bounds__(256) void skinny_fwd_kernel(SkinnyArgs p) {
           const int e = e0 + tid + 256 * j;
           if (e < R * ntile) {
             const int rr = e / ntile, t = e - rr * ntile;
-            absl[t * R + rr] = a[j];
+            absl[rr * astr + t] = a[j];
           }
         }
       }
@@ -182,39 +229,26 @@ __global__ __launch_bounds__(256) void skinny_fwd_kernel(SkinnyArgs p) {
 #pragma unroll
     for (int i = 0; i < TF; ++i) acc[f][i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  // Expansion of one tile: the 16 codebook lookups of frag f + 1 are issued
-  // before frag f is scaled, rounded and multiplied, so that their LDS
-  // latency overlaps the matrix work of frag f.
-  auto look = [&](const u32x2 c, float (&v)[16]) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      v[e] = cb[(c[0] >> (4 * e)) & 15u];
-      v[8 + e] = cb[(c[1] >> (4 * e)) & 15u];
-    }
-  };
+  // Expansion and products of one tile, frag by frag: 16 codebook lookups,
+  // times the block absmax, rounded to bf16, then step 0 of all token frags
+  // and step 1 (dependent MFMAs TF apart).
   auto compute = [&](int kt, const Regs& gg) {
-    const float* arow = absl + (kt - kb) * R + l16;
-    float a[FN];
-#pragma unroll
-    for (int f = 0; f < FN; ++f) a[f] = arow[16 * f];
-    float lv[2][16];
-    look(gg.c[0], lv[0]);
+    const float* arow = absl + l16 * astr + (kt - kb);
 #pragma unroll
     for (int f = 0; f < FN; ++f) {
-      if (f + 1 < FN) look(gg.c[f + 1], lv[(f + 1) & 1]);
-      const float* v = lv[f & 1];
+      const float a = arow[16 * f * astr];
+      float v[16];
+      sk_lookup8(cb, gg.c[f][0], v);
+      sk_lookup8(cb, gg.c[f][1], v + 8);
       u32x4 w[2];
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2)
-        w[s2] = u32x4{pack_bf16x2(v[8 * s2 + 0] * a[f], v[8 * s2 + 1] * a[f]),
-                      pack_bf16x2(v[8 * s2 + 2] * a[f], v[8 * s2 + 3] * a[f]),
-                      pack_bf16x2(v[8 * s2 + 4] * a[f], v[8 * s2 + 5] * a[f]),
-                      pack_bf16x2(v[8 * s2 + 6] * a[f], v[8 * s2 + 7] * a[f])};
+        w[s2] = u32x4{pack_bf16x2(v[8 * s2 + 0] * a, v[8 * s2 + 1] * a), pack_bf16x2(v[8 * s2 + 2] * a, v[8 * s2 + 3] * a),
+                      pack_bf16x2(v[8 * s2 + 4] * a, v[8 * s2 + 5] * a), pack_bf16x2(v[8 * s2 + 6] * a, v[8 * s2 + 7] * a)};
 #pragma unroll
-      for (int i = 0; i < TF; ++i) {
-        acc[f][i] = mfma16(gg.x[i][0], w[0], acc[f][i]);
-        acc[f][i] = mfma16(gg.x[i][1], w[1], acc[f][i]);
-      }
+      for (int i = 0; i < TF; ++i) acc[f][i] = mfma16(gg.x[i][0], w[0], acc[f][i]);
+#pragma unroll
+      for (int i = 0; i < TF; ++i) acc[f][i] = mfma16(gg.x[i][1], w[1], acc[f][i]);
     }
   };
 
@@ -304,33 +338,163 @@ __global__ __launch_bounds__(256) void skinny_fwd_kernel(SkinnyArgs p) {
     }
   }
 
-  // ---- sum the wave partials of each frag in wave order and store.
-  // Value e = 256 i + 64 v + lane of a frag is token 16 i + 4 (lane/16) + v,
-  // weight row n0 + 16 f + lane%16.
+  // ---- sum the wave partials in wave order and store, up to 4 frags per
+  // round through the (now free) absmax region: per frag and wave 1024 values,
+  // value e = 256 i + 64 v + lane of a frag being token 16 i + 4 (lane/16) + v,
+  // weight row n0 + 16 f + lane%16.  A thread sums 4 consecutive values (4
+  // consecutive rows of one token) and stores them as one 8-byte write.
+  float* red = absl;
+  constexpr int FR = 4;
 #pragma unroll
-  for (int f = 0; f < FN; ++f) {
+  for (int f0 = 0; f0 < FN; f0 += FR) {
+    __syncthreads();  // the region is free: main loop (or the previous round) done
 #pragma unroll
-    for (int i = 0; i < TF; ++i)
+    for (int fl = 0; fl < FR; ++fl) {
+      if (f0 + fl < FN) {
 #pragma unroll
-      for (int v = 0; v < 4; ++v) red[wave][256 * i + 64 * v + lane] = acc[f][i][v];
-    __syncthreads();
+        for (int i = 0; i < TF; ++i)
 #pragma unroll
-    for (int h = 0; h < TF; ++h) {
-      const int e = tid + 256 * h;
-      float sum = 0.0f;
-#pragma unroll
-      for (int w = 0; w < SK_WAVES; ++w) sum += red[w][e];
-      const int ln = e & 63;
-      const int64_t m = 16 * (e >> 8) + 4 * (ln >> 4) + ((e >> 6) & 3);
-      const int64_t n = n0 + 16 * f + (ln & 15);
-      if (m < p.M && n < p.N) {
-        if (p.part)
-          p.part[((int64_t)blockIdx.y * p.M + m) * p.N + n] = sum;
-        else
-          p.out[m * p.N + n] = (uint16_t)(pack_bf16x2(sum, 0.0f) & 0xFFFFu);
+          for (int v = 0; v < 4; ++v) red[(fl * SK_WAVES + wave) * 1024 + 256 * i + 64 * v + lane] = acc[f0 + fl][i][v];
       }
     }
     __syncthreads();
+#pragma unroll
+    for (int fl = 0; fl < FR; ++fl) {
+      if (f0 + fl >= FN) continue;
+      const int e = 4 * tid;  // values e .. e + 3 of frag f0 + fl
+      f32x4 sum = *reinterpret_cast<const f32x4*>(red + (fl * SK_WAVES) * 1024 + e);
+#pragma unroll
+      for (int w = 1; w < SK_WAVES; ++w) sum += *reinterpret_cast<const f32x4*>(red + (fl * SK_WAVES + w) * 1024 + e);
+      const int ln = e & 63;
+      const int64_t m = 16 * (e >> 8) + 4 * (ln >> 4) + ((e >> 6) & 3);
+      const int64_t n = n0 + 16 * (f0 + fl) + (ln & 15);  // first of 4 consecutive rows
+      if (m < p.M) {
+        if (p.part) {
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            if (n + u < p.N) p.part[((int64_t)blockIdx.y * p.M + m) * p.N + n + u] = sum[u];
+        } else if (n + 3 < p.N) {
+          *reinterpret_cast<u32x2*>(p.out + m * p.N + n) =
+              u32x2{pack_bf16x2(sum[0], sum[1]), pack_bf16x2(sum[2], sum[3])};
+        } else {
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            if (n + u < p.N) p.out[m * p.N + n + u] = (uint16_t)(pack_bf16x2(sum[u], 0.0f) & 0xFFFFu);
+        }
+      }
+    }
+  }
+
+}
+
+
+// ------------------------------------------------------------------------
+// Skinny-M backward finish ("LLM Fine-Tuning in 2026: Unsloth vs QLoRA vs
+// Liger-Kernel", section 2): one launch after the split transposed product.
+// Workgroups [0, K/64) own 64 columns k of the input side:
+//   dX[:, k] = sum_z part[z][:, k] + s T A[:, k]     (T = sum_z tpart[z])
+//   dA[:, k] = s T^T X[:, k]
+// workgroups [K/64, K/64 + N/64) own 64 rows n of B:
+//   dB[n, :] = s dY[:, n]^T XA
+// Every sum runs in fp32 in a fixed order.
+// ------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void skinny_bwd_finish_kernel(SkinnyFinishArgs p) {
+  __shared__ float vs[64 * 128];  // T or XA, [M][r]
+  __shared__ float zs[64 * 68];   // 64-column block of X or dY, [M][64] (+4 pad)
+  __shared__ float as[128 * 64];  // 64-column block of A, [r][64]
+  const int tid = threadIdx.x;
+  const int M = (int)p.M, r = p.r;
+  const int nkb = (int)(p.K / 64);
+  // bf16 [M][64] block at src (row stride ld) -> zs as fp32, 8 columns per load
+  auto stage_block = [&](const uint16_t* src, int64_t ld) {
+    for (int e = tid; e < M * 8; e += 256) {
+      const int m = e >> 3, c8 = (e & 7) * 8;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(src + (int64_t)m * ld + c8);
+      float* d = zs + m * 68 + c8;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        d[2 * u] = bf16_lo(v[u]);
+        d[2 * u + 1] = bf16_hi(v[u]);
+      }
+    }
+  };
+  if ((int)blockIdx.x < nkb) {
+    const int64_t k0 = (int64_t)blockIdx.x * 64;
+    // T = sum_z tpart[z] (split order), loads of 8 splits in flight
+    for (int e0 = tid; e0 < M * r; e0 += 256 * 4) {
+      float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      for (int z0 = 0; z0 < p.tsplits; z0 += 8) {
+        float t[4][8];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int zz = 0; zz < 8; ++zz)
+            t[j][zz] = p.tpart[(int64_t)min(z0 + zz, p.tsplits - 1) * M * r + min(e0 + 256 * j, M * r - 1)];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int zz = 0; zz < 8; ++zz)
+            if (z0 + zz < p.tsplits) v[j] += t[j][zz];
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (e0 + 256 * j < M * r) vs[e0 + 256 * j] = v[j];
+    }
+    stage_block(p.X + k0, p.K);
+    for (int e = tid; e < r * 8; e += 256) {
+      const int j = e >> 3, c8 = (e & 7) * 8;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(p.A + (int64_t)j * p.K + k0 + c8);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        as[j * 64 + c8 + 2 * u] = bf16_lo(v[u]);
+        as[j * 64 + c8 + 2 * u + 1] = bf16_hi(v[u]);
+      }
+    }
+    __syncthreads();
+    // dX: 16 threads per row, 4 columns each; the split partials of a row
+    // are loaded 8 splits at a time and added in split order
+    const int cq = (tid & 15) * 4;
+    for (int m = tid >> 4; m < M; m += 16) {
+      const float* src = p.part + (int64_t)m * p.K + k0 + cq;
+      f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+      for (int z0 = 0; z0 < p.splits; z0 += 8) {
+        f32x4 t[8];
+#pragma unroll
+        for (int zz = 0; zz < 8; ++zz)
+          t[zz] = *reinterpret_cast<const f32x4*>(src + (int64_t)min(z0 + zz, p.splits - 1) * M * p.K);
+#pragma unroll
+        for (int zz = 0; zz < 8; ++zz)
+          if (z0 + zz < p.splits) acc += t[zz];
+      }
+      float lo[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      for (int j = 0; j < r; ++j) {
+        const float v = vs[m * r + j];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) lo[u] += v * as[j * 64 + cq + u];
+      }
+      *reinterpret_cast<u32x2*>(p.dX + (int64_t)m * p.K + k0 + cq) =
+          u32x2{pack_bf16x2(acc[0] + p.s * lo[0], acc[1] + p.s * lo[1]),
+                pack_bf16x2(acc[2] + p.s * lo[2], acc[3] + p.s * lo[3])};
+    }
+    // dA[j, k0 + c] = s sum_m T[m, j] X[m, k0 + c]
+    const int c = tid & 63;
+    for (int j = tid >> 6; j < r; j += 4) {
+      float acc = 0.0f;
+      for (int m = 0; m < M; ++m) acc += vs[m * r + j] * zs[m * 68 + c];
+      p.dA[(int64_t)j * p.K + k0 + c] = (uint16_t)(pack_bf16x2(p.s * acc, 0.0f) & 0xFFFFu);
+    }
+  } else {
+    const int64_t n0 = (int64_t)(blockIdx.x - nkb) * 64;
+    for (int e = tid; e < M * r; e += 256) vs[e] = p.XA[e];
+    stage_block(p.dY + n0, p.N);
+    __syncthreads();
+    // consecutive threads write consecutive ranks of one row of dB
+    for (int e = tid; e < 64 * r; e += 256) {
+      const int nl = e / r, j = e - nl * r;
+      float acc = 0.0f;
+      for (int m = 0; m < M; ++m) acc += zs[m * 68 + nl] * vs[m * r + j];
+      p.dB[(n0 + nl) * r + j] = (uint16_t)(pack_bf16x2(p.s * acc, 0.0f) & 0xFFFFu);
+    }
   }
 }
 
@@ -360,4 +524,14 @@ hipError_t launch_skinny_fwd(const SkinnyArgs& a, const qplan::SkinnyPlan& pl, h
     case 8: return run_skinny_fwd<8>(a, pl.splits, st);
     default: return hipErrorInvalidValue;
   }
+}
+
+bool skinny_finish_supported(int64_t M, int r) { return M >= 1 && M <= 64 && r >= 1 && r <= 128; }
+
+hipError_t launch_skinny_bwd_finish(const SkinnyFinishArgs& a, hipStream_t st) {
+  if (!skinny_finish_supported(a.M, a.r) || a.K % 64 != 0 || a.N % 64 != 0) return hipErrorInvalidValue;
+  const unsigned grid = (unsigned)(a.K / 64 + a.N / 64);
+  if (grid == 0) return hipSuccess;
+  skinny_bwd_finish_kernel<<<grid, 256, 0, st>>>(a);
+  return hipGetLastError();
 }
