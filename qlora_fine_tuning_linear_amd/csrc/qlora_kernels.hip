@@ -369,9 +369,11 @@ __global__ __launch_bounds__(WM* WN * 64) void qgemm_kernel(GemmArgs p) {
   // refilled from tile kt_next as soon as its MFMAs have been issued, and the
   // expansion of the next weight tile (codes F) into `nxt` is spread over the
   // four substeps, so the vector and LDS work overlaps the matrix cores.
-  u32x4 S[NI];
+  // staged activations of the next tiles: two register sets, loaded two tiles
+  // ahead of their LDS store
+  u32x4 Sa[NI], Sb[NI];
   auto mma_tile = [&](auto has_next, const uint16_t* cur, const uint16_t* acur, u32x4 (&A)[FM][4], int kt_next,
-                      const Fill& F, uint16_t* nxt, uint16_t* anxt) {
+                      const Fill& F, uint16_t* nxt, uint16_t* anxt, const u32x4 (&Sst)[NI]) {
     constexpr bool NEXT = decltype(has_next)::value;
     const uint16_t* asrc[FM];
     if constexpr (NEXT && !ALDS) {
@@ -416,7 +418,7 @@ __global__ __launch_bounds__(WM* WN * 64) void qgemm_kernel(GemmArgs p) {
 #pragma unroll
         for (int d = 0; d < NP; ++d)
           if (d * 4 / NP == s) fill_part(F, nxt, d);
-        if (ALDS && s == 3) stage_store(S, anxt);  // next tile's activations, loaded at the tile start
+        if (ALDS && s == 3) stage_store(Sst, anxt);  // next tile's activations, loaded two tiles ahead
       }
     }
   };
@@ -429,8 +431,9 @@ __global__ __launch_bounds__(WM* WN * 64) void qgemm_kernel(GemmArgs p) {
   __syncthreads();  // codebook in LDS
   if (kt_begin < kt_end) {
     if constexpr (ALDS) {
-      stage_load(kt_begin, S);
-      stage_store(S, alds[kt_begin & 1]);
+      stage_load(kt_begin, Sa);
+      stage_store(Sa, alds[kt_begin & 1]);
+      stage_load(min(kt_begin + 1, kt_end - 1), Sa);
     } else {
       load_act(kt_begin, A);
     }
@@ -445,26 +448,28 @@ __global__ __launch_bounds__(WM* WN * 64) void qgemm_kernel(GemmArgs p) {
   // the other buffer; activations are fetched one tile ahead, codes two.
   // Two code-register sets alternate between consecutive tiles (unrolled by
   // two), so a prefetch is never copied - a copy would wait for the load.
-  auto step = [&](int kt, const Fill& Fuse, Fill& Fload) {
-    stage_load(kt + 1, S);
+  // (the staged activations of tile kt + 1 sit in Suse, those of kt + 2 are
+  // requested into Sload; tiles past the end are clamped: redundant loads)
+  auto step = [&](int kt, const Fill& Fuse, Fill& Fload, const u32x4 (&Suse)[NI], u32x4 (&Sload)[NI]) {
+    stage_load(min(kt + 2, kt_end - 1), Sload);
     fill_load(min(kt + 2, kt_end - 1), Fload);
     __builtin_amdgcn_sched_barrier(0);  // issue the global loads first
     mma_tile(std::true_type{}, lds[kt & 1], alds[ALDS ? (kt & 1) : 0], A, kt + 1, Fuse, lds[(kt + 1) & 1],
-             alds[ALDS ? ((kt + 1) & 1) : 0]);
+             alds[ALDS ? ((kt + 1) & 1) : 0], Suse);
     lds_barrier();  // global prefetches stay in flight across it
   };
   int kt = kt_begin;
   for (; kt + 2 < kt_end; kt += 2) {
-    step(kt, Fa, Fb);
-    step(kt + 1, Fb, Fa);
+    step(kt, Fa, Fb, Sa, Sb);
+    step(kt + 1, Fb, Fa, Sb, Sa);
   }
   if (kt + 1 < kt_end) {
-    step(kt, Fa, Fb);
+    step(kt, Fa, Fb, Sa, Sb);
     ++kt;
   }
   if (kt_begin < kt_end)
     mma_tile(std::false_type{}, lds[(kt_end - 1) & 1], alds[ALDS ? ((kt_end - 1) & 1) : 0], A, 0, Fa, lds[0],
-             alds[0]);
+             alds[0], Sa);
 
   gemm_epilogue<MODE, WM, WN, FM, FN, SPLIT>(p, acc, arow, m0, n0, wm, wn, l32, g);
 }
