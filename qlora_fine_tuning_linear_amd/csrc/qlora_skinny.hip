@@ -391,24 +391,25 @@ __global__ __launch_bounds__(256) void skinny_fwd_kernel(SkinnyArgs p) {
 // ------------------------------------------------------------------------
 // Skinny-M backward finish ("LLM Fine-Tuning in 2026: Unsloth vs QLoRA vs
 // Liger-Kernel", section 2): one launch after the split transposed product.
-// Workgroups [0, K/64) own 64 columns k of the input side:
+// Workgroups [0, K/32) own 32 columns k of the input side:
 //   dX[:, k] = sum_z part[z][:, k] + s T A[:, k]     (T = sum_z tpart[z])
 //   dA[:, k] = s T^T X[:, k]
-// workgroups [K/64, K/64 + N/64) own 64 rows n of B:
+// workgroups [K/32, K/32 + N/64) own 64 rows n of B:
 //   dB[n, :] = s dY[:, n]^T XA
 // Every sum runs in fp32 in a fixed order.
 // ------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void skinny_bwd_finish_kernel(SkinnyFinishArgs p) {
   __shared__ float vs[64 * 128];  // T or XA, [M][r]
   __shared__ float zs[64 * 68];   // 64-column block of X or dY, [M][64] (+4 pad)
-  __shared__ float as[128 * 64];  // 64-column block of A, [r][64]
+  __shared__ float as[128 * 32];  // 32-column block of A, [r][32]
   const int tid = threadIdx.x;
   const int M = (int)p.M, r = p.r;
-  const int nkb = (int)(p.K / 64);
-  // bf16 [M][64] block at src (row stride ld) -> zs as fp32, 8 columns per load
-  auto stage_block = [&](const uint16_t* src, int64_t ld) {
-    for (int e = tid; e < M * 8; e += 256) {
-      const int m = e >> 3, c8 = (e & 7) * 8;
+  const int nkb = (int)(p.K / 32);
+  // bf16 [M][cols] block at src (row stride ld) -> zs as fp32, 8 columns per load
+  auto stage_block = [&](const uint16_t* src, int64_t ld, int cols) {
+    const int n8 = cols / 8;
+    for (int e = tid; e < M * n8; e += 256) {
+      const int m = e / n8, c8 = (e - m * n8) * 8;
       const u32x4 v = *reinterpret_cast<const u32x4*>(src + (int64_t)m * ld + c8);
       float* d = zs + m * 68 + c8;
 #pragma unroll
@@ -419,7 +420,7 @@ __global__ __launch_bounds__(256) void skinny_bwd_finish_kernel(SkinnyFinishArgs
     }
   };
   if ((int)blockIdx.x < nkb) {
-    const int64_t k0 = (int64_t)blockIdx.x * 64;
+    const int64_t k0 = (int64_t)blockIdx.x * 32;
     // T = sum_z tpart[z] (split order), loads of 8 splits in flight
     for (int e0 = tid; e0 < M * r; e0 += 256 * 4) {
       float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -440,21 +441,21 @@ __global__ __launch_bounds__(256) void skinny_bwd_finish_kernel(SkinnyFinishArgs
       for (int j = 0; j < 4; ++j)
         if (e0 + 256 * j < M * r) vs[e0 + 256 * j] = v[j];
     }
-    stage_block(p.X + k0, p.K);
-    for (int e = tid; e < r * 8; e += 256) {
-      const int j = e >> 3, c8 = (e & 7) * 8;
+    stage_block(p.X + k0, p.K, 32);
+    for (int e = tid; e < r * 4; e += 256) {
+      const int j = e >> 2, c8 = (e & 3) * 8;
       const u32x4 v = *reinterpret_cast<const u32x4*>(p.A + (int64_t)j * p.K + k0 + c8);
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        as[j * 64 + c8 + 2 * u] = bf16_lo(v[u]);
-        as[j * 64 + c8 + 2 * u + 1] = bf16_hi(v[u]);
+        as[j * 32 + c8 + 2 * u] = bf16_lo(v[u]);
+        as[j * 32 + c8 + 2 * u + 1] = bf16_hi(v[u]);
       }
     }
     __syncthreads();
-    // dX: 16 threads per row, 4 columns each; the split partials of a row
+    // dX: 8 threads per row, 4 columns each; the split partials of a row
     // are loaded 8 splits at a time and added in split order
-    const int cq = (tid & 15) * 4;
-    for (int m = tid >> 4; m < M; m += 16) {
+    const int cq = (tid & 7) * 4;
+    for (int m = tid >> 3; m < M; m += 32) {
       const float* src = p.part + (int64_t)m * p.K + k0 + cq;
       f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
       for (int z0 = 0; z0 < p.splits; z0 += 8) {
@@ -470,15 +471,15 @@ __global__ __launch_bounds__(256) void skinny_bwd_finish_kernel(SkinnyFinishArgs
       for (int j = 0; j < r; ++j) {
         const float v = vs[m * r + j];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) lo[u] += v * as[j * 64 + cq + u];
+        for (int u = 0; u < 4; ++u) lo[u] += v * as[j * 32 + cq + u];
       }
       *reinterpret_cast<u32x2*>(p.dX + (int64_t)m * p.K + k0 + cq) =
           u32x2{pack_bf16x2(acc[0] + p.s * lo[0], acc[1] + p.s * lo[1]),
                 pack_bf16x2(acc[2] + p.s * lo[2], acc[3] + p.s * lo[3])};
     }
     // dA[j, k0 + c] = s sum_m T[m, j] X[m, k0 + c]
-    const int c = tid & 63;
-    for (int j = tid >> 6; j < r; j += 4) {
+    const int c = tid & 31;
+    for (int j = tid >> 5; j < r; j += 8) {
       float acc = 0.0f;
       for (int m = 0; m < M; ++m) acc += vs[m * r + j] * zs[m * 68 + c];
       p.dA[(int64_t)j * p.K + k0 + c] = (uint16_t)(pack_bf16x2(p.s * acc, 0.0f) & 0xFFFFu);
@@ -486,7 +487,7 @@ __global__ __launch_bounds__(256) void skinny_bwd_finish_kernel(SkinnyFinishArgs
   } else {
     const int64_t n0 = (int64_t)(blockIdx.x - nkb) * 64;
     for (int e = tid; e < M * r; e += 256) vs[e] = p.XA[e];
-    stage_block(p.dY + n0, p.N);
+    stage_block(p.dY + n0, p.N, 64);
     __syncthreads();
     // consecutive threads write consecutive ranks of one row of dB
     for (int e = tid; e < 64 * r; e += 256) {
@@ -530,7 +531,7 @@ bool skinny_finish_supported(int64_t M, int r) { return M >= 1 && M <= 64 && r >
 
 hipError_t launch_skinny_bwd_finish(const SkinnyFinishArgs& a, hipStream_t st) {
   if (!skinny_finish_supported(a.M, a.r) || a.K % 64 != 0 || a.N % 64 != 0) return hipErrorInvalidValue;
-  const unsigned grid = (unsigned)(a.K / 64 + a.N / 64);
+  const unsigned grid = (unsigned)(a.K / 32 + a.N / 64);
   if (grid == 0) return hipSuccess;
   skinny_bwd_finish_kernel<<<grid, 256, 0, st>>>(a);
   return hipGetLastError();
