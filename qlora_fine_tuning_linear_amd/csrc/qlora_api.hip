@@ -82,6 +82,14 @@ hipError_t traced_skinny_fwd(const SkinnyArgs& a, const qplan::SkinnyPlan& pl, h
   return trace_end(idx, launch_skinny_fwd(a, pl, st), st);
 }
 
+// Skinny-M transposed product, traced as kind MODE_BWD + 16.
+hipError_t traced_skinny_bwd(const SkinnyBwdArgs& a, int splits, hipStream_t st) {
+  hipError_t e;
+  const int32_t idx = trace_begin(MODE_BWD + 16, st, &e);
+  if (e != hipSuccess) return e;
+  return trace_end(idx, launch_skinny_bwd(a, splits, st), st);
+}
+
 hipError_t traced_gemm_q(int mode, const GemmArgs& a, const qplan::GemmPlan& pl, hipStream_t st) {
   return traced_gemm(mode, false, a, pl, st);
 }
@@ -255,22 +263,39 @@ int qlora_linear_bwd(const qlora_linear* L, const void* dY, const void* X, const
   float* grad_part = reinterpret_cast<float*>(after_bt + w.bwd_part + w.bwd_down);
 
   const qplan::GemmPlan pl = qplan::plan_gemm(M, K, N, true, true);
-  if (!qplan::use_bgemm(M) && pl.cfg == qplan::CFG_SKINNY_TR && pl.splits > 1 && skinny_finish_supported(M, r)) {
+  const bool sk_bwd = skinny_bwd_supported(M, N, K);
+  if (!qplan::use_bgemm(M) && pl.cfg == qplan::CFG_SKINNY_TR && skinny_finish_supported(M, r) &&
+      (sk_bwd || pl.splits > 1)) {
     // Skinny M: T partials, the split transposed product without its LoRA
-    // term, then one finish launch for dX (+ s T A), dA and dB.
+    // term (the skinny kernel when the shape allows, else the dequant-staged
+    // GEMM), then one finish launch for dX (+ s T A), dA and dB.
     QHIP(launch_transpose_rn(u16(L->B), N, r, BT, st));
     const int ds = qplan::plan_down_splits(M, N);
     const int dsu = qplan::down_splits_used(N, ds);
     QHIP(launch_lora_down(u16(dY), M, N, BT, r, nullptr, 0, T, nullptr, ds, down_part, st, false));
-    GemmArgs a = gemm_args();
-    a.act0 = u16(dY);
-    a.M = M;
-    a.Nout = K;
-    a.Kred0 = N;
-    a.w0 = to_dev(L->W0);
-    a.codebook = L->W0.codebook;
-    a.partial = part;
-    QHIP(traced_gemm_q(MODE_BWD, a, pl, st));
+    if (sk_bwd) {
+      SkinnyBwdArgs b;
+      memset(&b, 0, sizeof(b));
+      b.dY = u16(dY);
+      b.M = M;
+      b.N = N;
+      b.K = K;
+      b.w = to_dev(L->W0);
+      b.codebook = L->W0.codebook;
+      b.part = part;
+      b.kps = pl.ktiles_per_split;
+      QHIP(traced_skinny_bwd(b, pl.splits, st));
+    } else {
+      GemmArgs a = gemm_args();
+      a.act0 = u16(dY);
+      a.M = M;
+      a.Nout = K;
+      a.Kred0 = N;
+      a.w0 = to_dev(L->W0);
+      a.codebook = L->W0.codebook;
+      a.partial = part;
+      QHIP(traced_gemm_q(MODE_BWD, a, pl, st));
+    }
     SkinnyFinishArgs f;
     memset(&f, 0, sizeof(f));
     f.M = M;

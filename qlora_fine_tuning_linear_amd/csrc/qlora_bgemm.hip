@@ -69,22 +69,6 @@ __device__ __forceinline__ void bg_tile(int64_t bid, int64_t tiles_m, int64_t ti
   tn = in / gs;
 }
 
-// s_waitcnt with only the vector-memory counter: wait until at most N of this
-// wave's vector memory operations are outstanding.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// Workgroup barrier for LDS data written by direct loads: LDS accesses of
-// this wave complete (lgkmcnt), then s_barrier.  The memory clobber keeps the
-// compiler from moving memory accesses across it.  The caller has already
-// waited (vmcnt) for the direct loads that must be visible after it.
-__device__ __forceinline__ void stage_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
-#define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
-
 // Epilogue through LDS.  After the reduction each wave owns one 32 KB LDS
 // buffer.  Its 128 x 128 results are written there in accumulator layout and
 // read back as 16-byte row chunks, so that every global load and store of

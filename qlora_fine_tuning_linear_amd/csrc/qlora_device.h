@@ -58,6 +58,22 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// s_waitcnt with only the vector-memory counter: wait until at most N of this
+// wave's vector memory operations are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier for LDS data written by direct loads: LDS accesses of
+// this wave complete (lgkmcnt), then s_barrier.  The memory clobber keeps the
+// compiler from moving memory accesses across it.  The caller has already
+// waited (vmcnt) for the direct loads that must be visible after it.
+__device__ __forceinline__ void stage_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+#define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
+
 __device__ __forceinline__ float sigmoidf_(float g) { return 1.0f / (1.0f + __expf(-g)); }
 
 // sigmoid with the hardware reciprocal (v_rcp_f32, about 1 ulp) instead of

@@ -98,6 +98,17 @@ struct SkinnyFinishArgs {
   uint16_t* dB;
 };
 
+// Skinny-M transposed product (qlora_skinny.hip): part[z][M][K] =
+// dY[:, tiles of split z] deq(w)[those rows, :], 64-row tiles, kps per split.
+struct SkinnyBwdArgs {
+  const uint16_t* dY;  // [M][N]
+  int64_t M, N, K;     // weight [N, K]
+  Nf4Dev w;
+  const float* codebook;
+  float* part;
+  int32_t kps;
+};
+
 hipError_t launch_nf4_quantize(const float* W, int64_t nblocks, const float* codebook, int dq, uint8_t* codes,
                                float* absmax, uint8_t* absmax_q, float* absmax_scale, hipStream_t st);
 hipError_t launch_nf4_dequantize(const Nf4Dev& w, const float* codebook, int out_f32, void* out, hipStream_t st);
@@ -116,6 +127,8 @@ hipError_t launch_splitk_finish(const float* part, int splits, int64_t M, int64_
                                 hipStream_t st);
 bool skinny_fwd_supported(int64_t M, int r);
 bool skinny_finish_supported(int64_t M, int r);
+bool skinny_bwd_supported(int64_t M, int64_t N, int64_t K);
+hipError_t launch_skinny_bwd(const SkinnyBwdArgs& a, int splits, hipStream_t st);
 hipError_t launch_skinny_bwd_finish(const SkinnyFinishArgs& a, hipStream_t st);
 hipError_t launch_skinny_fwd(const SkinnyArgs& a, const qplan::SkinnyPlan& pl, hipStream_t st);
 // V0 | V1 = Z W0^T | Z W1^T, W0 [r0, Kred], W1 [r1, Kred] (r0 + r1 <= 128).

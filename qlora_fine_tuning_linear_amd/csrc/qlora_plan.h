@@ -163,6 +163,8 @@ inline LinearWs linear_ws(int64_t M, int64_t N, int64_t K, int r) {
   w.bwd_T = align256((size_t)M * r * 4);
   w.bwd_BT = align256((size_t)N * r * 2) + align256((size_t)K * r * 2);  // B^T [r, N], A^T [K, r]
   w.bwd_part = (!bg && pb.splits > 1) ? align256((size_t)pb.splits * M * K * 4) : 0;
+  // skinny backward: the transposed product always writes split partials
+  if (pb.cfg == CFG_SKINNY_TR) w.bwd_part = align256((size_t)pb.splits * M * K * 4);
   const int ts = plan_down_splits(M, N);
   w.bwd_down = ts > 1 ? align256((size_t)ts * M * r * 4) : 0;
   const int gs_b = plan_grad_msplits(M, N, r);

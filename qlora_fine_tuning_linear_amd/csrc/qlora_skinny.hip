@@ -499,6 +499,210 @@ __global__ __launch_bounds__(256) void skinny_bwd_finish_kernel(SkinnyFinishArgs
   }
 }
 
+// ------------------------------------------------------------------------
+// Skinny-M transposed product: the dequantized-weight part of dX = dY W0
+// ("LLM Fine-Tuning in 2026: Unsloth vs QLoRA vs Liger-Kernel", section 2)
+// for M <= 64 tokens, as split partials part[z] = dY[:, n-range z]
+// deq(W0)[n-range z, :] (the finish kernel adds them and the LoRA term).
+//
+// Workgroup: 256 output columns k x the 64-row reduction tiles of one split,
+// 8 waves (two per SIMD, so one wave's LDS waits overlap the other's work).
+// Waves w and w + 4 own columns 64 (w % 4) .. + 63 and take reduction rows
+// 0..31 and 32..63 of every tile; their sums are added at the end.  Per tile,
+// the code rows (64 x 128 bytes), the dY tile (64 tokens x 64 reduction rows)
+// and the absmax of the tile's rows arrive by direct global->LDS loads (whole
+// 128-byte lines for codes and dY) in a 4-stage ring with one barrier per
+// tile; every load of the kernel is a direct load, so each wait is the
+// explicit vmcnt below.  Lane (l16, q) owns columns 4 l16 .. 4 l16 + 3 of its
+// wave's 64 (frag f holds column 4 l16 + f): it reads 2 bytes of codes per
+// reduction row and expands them straight into the B operands of
+// v_mfma_f32_16x16x32_bf16 (reduction rows 32 h + 8 q + e, e < 8), so the
+// expanded weight never goes through LDS.  Code rows are stored with 16-byte
+// chunk c of row r at position c ^ ((r >> 3) & 7), dY rows with chunk c at
+// c ^ (r & 7): the lanes of one LDS read then hit different banks.
+// ------------------------------------------------------------------------
+constexpr int SB_D = 4;  // stages of the load ring
+
+struct __attribute__((aligned(16))) SkBwdStage {
+  uint8_t codes[64 * 128];  // 64 reduction rows x 256 columns
+  uint16_t dy[64 * 64];     // 64 tokens x 64 reduction rows
+  // per row of the tile, one region per wave: DQ: waves 0..3 the row's 4
+  // absmax codes (one dword), waves 4..7 the fp32 scale of those blocks;
+  // else the fp32 absmax of the wave's block (waves 4..7: a copy)
+  uint32_t aux[8 * 64];
+};
+
+// The codebook; the most strictly aligned LDS object, so that it sits at LDS
+// address 0 (the lookups use the SDWA result as the address).
+struct __attribute__((aligned(256))) SkBwdHead {
+  float cb[16];
+};
+
+template <bool DQ>
+__global__ __launch_bounds__(512) void skinny_bwd_kernel(SkinnyBwdArgs p) {
+  __shared__ SkBwdHead hd;
+  __shared__ SkBwdStage st0, st1, st2, st3;
+  __shared__ f32x4 red[4 * 16 * 64];  // second-half sums of waves 4..7
+  constexpr int TF = SK_TF;
+  // direct loads per wave per tile: codes, dY and one absmax part, the same
+  // three in every wave and without branches (a direct load under a branch
+  // makes the compiler wait for all loads before every LDS read)
+  constexpr int PT = 3;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int cw = wave & 3, hh = wave >> 2;
+  const int l16 = lane & 15, q = lane >> 4;
+  const int64_t c0 = (int64_t)blockIdx.x * 256;
+  const int64_t KB = p.K / 64;
+  const int64_t kb0 = c0 / 64;
+  const int NTL = (int)(p.N / 64);
+  const int tb = blockIdx.y * p.kps, te = min(NTL, tb + p.kps);
+  const int nt = te - tb;
+  if (tid < 16) hd.cb[tid] = p.codebook[tid];
+
+  // direct-load lane addresses for tile 0 (the tile offset is added per load):
+  // wave w brings code rows and dY tokens 8 w .. 8 w + 7
+  const int lrow = 8 * wave + (lane >> 3);
+  const uint8_t* cg = p.w.codes + (int64_t)lrow * (p.K / 2) + c0 / 2 + 16 * ((lane & 7) ^ wave);
+  // token rows past M read row M - 1 (never stored)
+  const uint16_t* yg = p.dY + (int64_t)min(lrow, (int)p.M - 1) * p.N + 8 * ((lane & 7) ^ (lrow & 7));
+  auto dma = [&](int t, SkBwdStage& S) {
+    const int64_t n0 = (int64_t)t * 64;
+    __builtin_amdgcn_global_load_lds(cg + n0 * (p.K / 2), LDS_PTR(S.codes + 8 * wave * 128), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(yg + n0, LDS_PTR(S.dy + 8 * wave * 64), 16, 0, 0);
+    const int64_t blk = (n0 + lane) * KB + kb0;  // row lane's first block of the 256 columns
+    const void* src;
+    if constexpr (DQ)
+      src = hh == 0 ? (const void*)(p.w.absmax_q + blk) : (const void*)(p.w.absmax_scale + ((blk + cw) >> 8));
+    else
+      src = p.w.absmax + blk + cw;
+    __builtin_amdgcn_global_load_lds(src, LDS_PTR(S.aux + 64 * wave), 4, 0, 0);
+  };
+
+  f32x4 acc[4][TF];
+#pragma unroll
+  for (int f = 0; f < 4; ++f)
+#pragma unroll
+    for (int i = 0; i < TF; ++i) acc[f][i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  const int r0 = 32 * hh + 8 * q;         // the lane's 8 reduction rows within a tile
+  const int cbyte = 32 * cw + 2 * l16;    // the lane's 2 code bytes within a row
+  const int pc = ((cbyte >> 4) ^ ((4 * hh + q) & 7)) * 16 + (cbyte & 15);
+  // the operands of one tile: built from its stage in one step, multiplied
+  // in the next (interleaved with the next tile's LDS and VALU work)
+  u32x4 wp[4], xp[TF];
+#pragma unroll
+  for (int f = 0; f < 4; ++f) wp[f] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int i = 0; i < TF; ++i) xp[i] = u32x4{0u, 0u, 0u, 0u};
+  auto mma = [&]() {
+#pragma unroll
+    for (int f = 0; f < 4; ++f)
+#pragma unroll
+      for (int i = 0; i < TF; ++i) acc[f][i] = mfma16(xp[i], wp[f], acc[f][i]);
+  };
+  auto prepare = [&](const SkBwdStage& S, u32x4 (&w)[4], u32x4 (&x)[TF]) {
+    // absmax of this wave's block for the tile's rows: lane r computes row r,
+    // the lanes that need it read it with a cross-lane move
+    float arow;
+    if constexpr (DQ)
+      arow = (float)((S.aux[64 * cw + lane] >> (8 * cw)) & 0xFFu) * __uint_as_float(S.aux[256 + 64 * cw + lane]);
+    else
+      arow = __uint_as_float(S.aux[64 * cw + lane]);
+    float v[8][4];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const uint32_t lo16 = *reinterpret_cast<const uint16_t*>(S.codes + (r0 + 2 * h) * 128 + pc);
+      const uint32_t hi16 = *reinterpret_cast<const uint16_t*>(S.codes + (r0 + 2 * h + 1) * 128 + pc);
+      const uint32_t d = lo16 | (hi16 << 16);
+      float t8[8];
+      sk_lookup8(hd.cb, d, t8);  // rows 2h (cols 0..3), 2h + 1 (cols 0..3)
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        v[2 * h][f] = t8[f];
+        v[2 * h + 1][f] = t8[4 + f];
+      }
+    }
+    float a[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) a[e] = __shfl(arow, r0 + e);
+#pragma unroll
+    for (int f = 0; f < 4; ++f)
+      w[f] = u32x4{pack_bf16x2(v[0][f] * a[0], v[1][f] * a[1]), pack_bf16x2(v[2][f] * a[2], v[3][f] * a[3]),
+                   pack_bf16x2(v[4][f] * a[4], v[5][f] * a[5]), pack_bf16x2(v[6][f] * a[6], v[7][f] * a[7])};
+#pragma unroll
+    for (int i = 0; i < TF; ++i) {
+      const int tok = 16 * i + l16;
+      x[i] = *reinterpret_cast<const u32x4*>(S.dy + tok * 64 + (((4 * hh + q) ^ (tok & 7)) * 8));
+    }
+  };
+
+  // ring: tile t in stage t % 4; D - 1 tiles requested ahead (clamped to the
+  // last tile, so every wave issues the same number of loads)
+  if (nt > 0) {
+    dma(tb + 0, st0);
+    dma(tb + min(1, nt - 1), st1);
+    dma(tb + min(2, nt - 1), st2);
+  }
+  auto step = [&](int t, SkBwdStage& cur, SkBwdStage& fill) {
+    wait_vmcnt<(SB_D - 2) * PT>();  // tile t landed (this wave's part)
+    stage_barrier();  // every wave's part landed; every wave done reading tile t - 1
+    dma(tb + min(t + SB_D - 1, nt - 1), fill);
+    u32x4 wn[4], xn[TF];
+    prepare(cur, wn, xn);
+    mma();  // tile t - 1 (zero operands before the first tile)
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      SCHED_GROUP(SG_DS_READ, 3);
+      SCHED_GROUP(SG_VALU, 6);
+      SCHED_GROUP(SG_MFMA, 1);
+    }
+#pragma unroll
+    for (int f = 0; f < 4; ++f) wp[f] = wn[f];
+#pragma unroll
+    for (int i = 0; i < TF; ++i) xp[i] = xn[i];
+  };
+  int t = 0;
+  for (; t + 4 <= nt; t += 4) {
+    step(t, st0, st3);
+    step(t + 1, st1, st0);
+    step(t + 2, st2, st1);
+    step(t + 3, st3, st2);
+  }
+  if (t < nt) step(t, st0, st3);
+  if (t + 1 < nt) step(t + 1, st1, st0);
+  if (t + 2 < nt) step(t + 2, st2, st1);
+  wait_vmcnt<0>();  // no direct load may still target LDS at the end
+  mma();            // the last tile
+
+  // waves 4..7 hand their sums to waves 0..3 (lane-contiguous 16-byte slots)
+  f32x4* rw = red + cw * 16 * 64 + lane;
+  if (hh == 1) {
+#pragma unroll
+    for (int f = 0; f < 4; ++f)
+#pragma unroll
+      for (int i = 0; i < TF; ++i) rw[(4 * f + i) * 64] = acc[f][i];
+  }
+  __syncthreads();
+  if (hh == 1) return;
+#pragma unroll
+  for (int f = 0; f < 4; ++f)
+#pragma unroll
+    for (int i = 0; i < TF; ++i) acc[f][i] += rw[(4 * f + i) * 64];
+
+  // split partial: value v of acc[f][i] is token 16 i + 4 q + v, column
+  // c0 + 64 cw + 4 l16 + f: 4 adjacent columns per (i, v), one 16-byte store
+  float* dst = p.part + (int64_t)blockIdx.y * p.M * p.K + c0 + 64 * cw + 4 * l16;
+#pragma unroll
+  for (int i = 0; i < TF; ++i)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int64_t m = 16 * i + 4 * q + v;
+      if (m < p.M)
+        *reinterpret_cast<f32x4*>(dst + m * p.K) = f32x4{acc[0][i][v], acc[1][i][v], acc[2][i][v], acc[3][i][v]};
+    }
+}
+
 template <int FN>
 static hipError_t run_skinny_fwd(const SkinnyArgs& a, int splits, hipStream_t st) {
   dim3 grid((unsigned)((a.N + 16 * FN - 1) / (16 * FN)), (unsigned)splits);
@@ -534,5 +738,19 @@ hipError_t launch_skinny_bwd_finish(const SkinnyFinishArgs& a, hipStream_t st) {
   const unsigned grid = (unsigned)(a.K / 32 + a.N / 64);
   if (grid == 0) return hipSuccess;
   skinny_bwd_finish_kernel<<<grid, 256, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+bool skinny_bwd_supported(int64_t M, int64_t N, int64_t K) {
+  return M >= 1 && M <= 64 && K % 256 == 0 && N % 64 == 0 && N > 0;
+}
+
+hipError_t launch_skinny_bwd(const SkinnyBwdArgs& a, int splits, hipStream_t st) {
+  if (!skinny_bwd_supported(a.M, a.N, a.K) || splits < 1) return hipErrorInvalidValue;
+  dim3 grid((unsigned)(a.K / 256), (unsigned)splits);
+  if (a.w.dq)
+    skinny_bwd_kernel<true><<<grid, 512, 0, st>>>(a);
+  else
+    skinny_bwd_kernel<false><<<grid, 512, 0, st>>>(a);
   return hipGetLastError();
 }
