@@ -27,25 +27,31 @@ namespace qk {
 // SIMD) in a 2 x 2 grid, each 128 x 128 = 4 x 4 frags of 32x32, fp32
 // accumulators.  Reduction tiles of 64 columns.
 //
-// Operands move global -> LDS by direct loads (global_load_lds, 16 bytes per
-// lane, no registers, no LDS write instructions).  Each direct load fills
-// 1 KB of LDS with 8 rows x 128 bytes, i.e. whole cache lines; a tile
-// operand ([256][64] bf16, chunk c of row r stored at c ^ swz(r)) is 32 KB,
-// 8 direct loads per wave.  The two operands of tile kt ("halves" 2kt and
-// 2kt+1) rotate through five 32 KB buffers (all 160 KB of LDS; each buffer
-// its own __shared__ object, so the compiler's dependency tracking adds no
-// waits of its own).  While tile kt multiplies from its two buffers, the
-// other three hold the next tile's halves and the following A half, in
-// flight or landed: 96 KB per CU stays in flight, which is what the L2-to-CU
-// path needs (measured: about 9 TB/s with 64 KB in flight or half-line
-// segments, 17-20 TB/s with 96-128 KB of whole lines).
+// Operands move global -> LDS by direct loads (buffer loads with the lds
+// flag, 16 bytes per lane, no registers, no LDS write instructions; a fixed
+// 32-bit lane offset, the tile's column offset in the scalar offset).  Each
+// direct load fills 1 KB of LDS with 8 rows x 128 bytes, i.e. whole cache
+// lines; a tile operand ([256][64] bf16, chunk c of row r stored at
+// c ^ swz(r)) is 32 KB, 8 direct loads per wave.  The two operands of tile kt
+// ("halves" 2kt and 2kt+1: the first half is the weight when the weight is
+// the larger matrix, else the activations) rotate through five 32 KB buffers
+// (all 160 KB of LDS; each buffer its own __shared__ object, so the
+// compiler's dependency tracking adds no waits of its own).  While tile kt
+// multiplies from its two buffers, the other three hold the next tile's
+// halves and the following first half, in flight or landed: 96 KB per CU
+// stays in flight, which is what the L2-to-CU path needs (measured: about
+// 9 TB/s with 64 KB in flight or half-line segments, 17-20 TB/s with
+// 96-128 KB of whole lines).  A first half is requested 1.5 tiles before its
+// use, a second half one tile before; giving the longer lead to the operand
+// that more often misses L2 shortens the waits at the per-tile barrier.
 //
 // Per tile: steps 0-2 multiply while reading the next step's operands; then
 // wait until this wave's loads of tile kt+1 have landed (explicit vmcnt: the
-// A half of kt+2 may stay in flight) and barrier, after which every wave has
-// read its last operands of tile kt and every load of tile kt+1 has landed;
-// step 3 then multiplies while the two freed buffers are refilled (B of
-// kt+2, A of kt+3) and tile kt+1's first operands are read.
+// first half of kt+2 may stay in flight) and barrier, after which every wave
+// has read its last operands of tile kt and every load of tile kt+1 has
+// landed; step 3 then multiplies while the two freed buffers are refilled
+// (second half of kt+2, first half of kt+3) and tile kt+1's first operands
+// are read.
 // ------------------------------------------------------------------------
 constexpr int BG_WN = 2, BG_FM = 4, BG_FN = 4;  // 2 x 2 waves
 constexpr int BG_BM = 256, BG_BN = 256;
@@ -217,7 +223,7 @@ __device__ __forceinline__ void bg_epilogue(const GemmArgs& p, f32x16 (&acc)[BG_
   }
 }
 
-template <int MODE>
+template <int MODE, bool WLEAD>
 __global__ __launch_bounds__(256) void bgemm_kernel(GemmArgs p) {
   constexpr int WN = BG_WN, FM = BG_FM, FN = BG_FN;
   constexpr int BM = BG_BM, BN = BG_BN;
@@ -230,7 +236,8 @@ __global__ __launch_bounds__(256) void bgemm_kernel(GemmArgs p) {
   __shared__ __attribute__((aligned(16))) uint16_t hb4[BG_HE];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
   const int l32 = lane & 31, g = lane >> 5;
 
@@ -256,14 +263,21 @@ __global__ __launch_bounds__(256) void bgemm_kernel(GemmArgs p) {
     aoff[i] = (uint32_t)((ra - m0) * p.Kred0) + (uint32_t)c * 8;
     boff[i] = (uint32_t)((rb - wr0) * p.ldw) + (uint32_t)c * 8;
   }
-  // the dual-reduction GEMM reads act0 for the first KT0 tiles, then act1
-  const uint16_t* abase0 = p.act0 + m0 * p.Kred0;
-  const uint16_t* abase1 = (p.act1 ? p.act1 + m0 * p.Kred0 : abase0) - (int64_t)KT0 * 64;
-  const uint16_t* bbase = p.wb + wr0 * p.ldw;
+  // Buffer resources over the tile's rows: the dual-reduction GEMM reads
+  // act0 for the first KT0 tiles, then act1 (same row stride).  A direct load
+  // is then one buffer load: fixed 32-bit lane offset, the tile's column
+  // offset in the scalar offset, the LDS destination in M0.
+  auto rsrc = [](const void* base, int64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0,
+                                             (int)(bytes < 0x7FFFFFFF ? bytes : 0x7FFFFFFF), 0x00020000);
+  };
+  const int64_t abytes = (p.M - m0) * p.Kred0 * 2;
+  const __amdgpu_buffer_rsrc_t ra0 = rsrc(p.act0 + m0 * p.Kred0, abytes);
+  const __amdgpu_buffer_rsrc_t ra1 = rsrc((p.act1 ? p.act1 : p.act0) + m0 * p.Kred0, abytes);
+  const __amdgpu_buffer_rsrc_t rb = rsrc(p.wb + wr0 * p.ldw, (p.wrows - wr0) * p.ldw * 2);
 
   // 8 direct loads of one operand half of tile kt (clamped to the last tile:
-  // the tail re-loads it into a free buffer, which keeps vmcnt uniform).
-  // Uniform base + 32-bit lane byte offset: the scalar-base addressing form.
+  // the tail re-loads it into a free buffer, which keeps vmcnt uniform)
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     aoff[i] *= 2;
@@ -271,17 +285,18 @@ __global__ __launch_bounds__(256) void bgemm_kernel(GemmArgs p) {
   }
   auto load_a = [&](uint16_t* buf, int kt) {
     kt = kt < KT ? kt : KT - 1;
-    const char* a = reinterpret_cast<const char*>((kt < KT0 ? abase0 : abase1) + (int64_t)kt * 64);
+    const bool second = kt >= KT0;
+    const int so = (second ? kt - KT0 : kt) * 128;
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      __builtin_amdgcn_global_load_lds(a + aoff[i], LDS_PTR(buf + (8 * wave + i) * 512), 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(second ? ra1 : ra0, LDS_PTR(buf + (8 * wave + i) * 512), 16, aoff[i],
+                                               so, 0, 0);
   };
   auto load_b = [&](uint16_t* buf, int kt) {
     kt = kt < KT ? kt : KT - 1;
-    const char* b = reinterpret_cast<const char*>(bbase + (int64_t)kt * 64);
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      __builtin_amdgcn_global_load_lds(b + boff[i], LDS_PTR(buf + (8 * wave + i) * 512), 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, LDS_PTR(buf + (8 * wave + i) * 512), 16, boff[i], kt * 128, 0, 0);
   };
 
   f32x16 acc[FM][FN];
@@ -309,7 +324,24 @@ __global__ __launch_bounds__(256) void bgemm_kernel(GemmArgs p) {
   }
 
   // operands of 16-wide step s (0..3) of a tile held in halves (ha, hb)
-  auto rd = [&](const uint16_t* ha, const uint16_t* hb, int s, u32x4 (&xa)[FM], u32x4 (&wa)[FN]) {
+  // The first half of each tile in the ring is requested half a tile earlier
+  // than the second: WLEAD puts the weight operand first (chosen when it is
+  // the larger matrix, whose tiles more often come from beyond L2).
+  auto load_first = [&](uint16_t* buf, int kt) {
+    if constexpr (WLEAD)
+      load_b(buf, kt);
+    else
+      load_a(buf, kt);
+  };
+  auto load_second = [&](uint16_t* buf, int kt) {
+    if constexpr (WLEAD)
+      load_a(buf, kt);
+    else
+      load_b(buf, kt);
+  };
+  auto rd = [&](const uint16_t* h1, const uint16_t* h2, int s, u32x4 (&xa)[FM], u32x4 (&wa)[FN]) {
+    const uint16_t* ha = WLEAD ? h2 : h1;
+    const uint16_t* hb = WLEAD ? h1 : h2;
 #pragma unroll
     for (int f = 0; f < FN; ++f) wa[f] = *reinterpret_cast<const u32x4*>(hb + bro[f][s]);
 #pragma unroll
@@ -346,8 +378,8 @@ __global__ __launch_bounds__(256) void bgemm_kernel(GemmArgs p) {
     wait_vmcnt<8>();  // tile kt+1 landed; the A half of kt+2 may be in flight
     stage_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    load_b(ca, kt + 2);
-    load_a(cb, kt + 3);
+    load_second(ca, kt + 2);
+    load_first(cb, kt + 3);
     rd(na, nb, 0, x0, w0);
     mm(x1, w1);
 #pragma unroll
@@ -380,11 +412,11 @@ __global__ __launch_bounds__(256) void bgemm_kernel(GemmArgs p) {
       if (ns > 0) lora_load<MODE, WN, FM, FN>(p, *L[0], 0, arow, n0, wn, l32, g, R0);
       if (ns > 1) lora_load<MODE, WN, FM, FN>(p, *L[1], 0, arow, n0, wn, l32, g, R1);
     }
-    load_a(hb0, 0);
-    load_b(hb1, 0);
-    load_a(hb2, 1);
-    load_b(hb3, 1);
-    load_a(hb4, 2);
+    load_first(hb0, 0);
+    load_second(hb1, 0);
+    load_first(hb2, 1);
+    load_second(hb3, 1);
+    load_first(hb4, 2);
     if (fast) {
       if (ns > 0) lora_apply<FM, FN>(*L[0], 0, g, lo[0], hi[0], acc, R0);
       if (ns > 1) lora_apply<FM, FN>(*L[1], 0, g, lo[1], hi[1], acc, R1);
@@ -422,43 +454,46 @@ __global__ __launch_bounds__(256) void bgemm_kernel(GemmArgs p) {
 }
 
 // ------------------------------------------------------------------------
-// Weight expansion into bf16 rows.  Thread -> 32 consecutive elements of one
-// output row (16-byte code load, four 16-byte stores).  With a SwiGLU pair
-// the output rows come in blocks of 256: 128 gate rows, then the up rows of
-// the same 128 columns; rows past N are written as zeros.
+// Weight expansion into bf16 rows.  The output is cut into 8-element
+// chunks (16 bytes, one code dword); wave w expands chunks 256 w .. 256 w +
+// 255, lane l taking chunks 256 w + 64 j + l (j < 4), so that every store
+// instruction of a wave writes 1 KB of consecutive output and every code load
+// reads 256 consecutive bytes.  With a SwiGLU pair the output rows come in
+// blocks of 256: 128 gate rows, then the up rows of the same 128 columns;
+// rows past N are written as zeros.
 // ------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void dequant_rows_kernel(Nf4Dev w0, Nf4Dev w1, int pair,
                                                            const float* __restrict__ codebook0,
-                                                           const float* __restrict__ codebook1, int64_t rows_out,
-                                                           uint16_t* __restrict__ out) {
+                                                           const float* __restrict__ codebook1, uint32_t cpr,
+                                                           uint32_t nchunks, uint16_t* __restrict__ out) {
   __shared__ float cb[32];  // tables of w0, w1
   if (threadIdx.x < 32) cb[threadIdx.x] = threadIdx.x < 16 ? codebook0[threadIdx.x] : codebook1[threadIdx.x & 15];
   __syncthreads();
   const int64_t K = w0.K;
-  const int64_t per_row = K / 32;
-  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (t >= rows_out * per_row) return;
-  const int64_t R = t / per_row;
-  const int64_t k0 = (t % per_row) * 32;
-  bool up = false;
-  int64_t src = R;
-  if (pair) {
-    const int64_t within = R & 255;
-    up = within >= 128;
-    src = (R >> 8) * 128 + (within & 127);
-  }
-  const Nf4Dev& w = up ? w1 : w0;
-  u32x4 o[4] = {};
-  if (src < w.N) {
-    const u32x4 c = *reinterpret_cast<const u32x4*>(w.codes + src * (K / 2) + k0 / 2);
-    const int64_t blk = (src * K + k0) / 64;
-    const float a = w.dq ? absmax_at<true>(w, blk) : absmax_at<false>(w, blk);
+  const uint32_t g0 = blockIdx.x * 1024u + (threadIdx.x >> 6) * 256u + (threadIdx.x & 63);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) o[j] = deq8(c[j], a, up ? cb + 16 : cb);
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t g = g0 + 64u * j;
+    if (g >= nchunks) break;
+    const uint32_t R = g / cpr;
+    const int64_t k0 = (int64_t)(g - R * cpr) * 8;
+    bool up = false;
+    int64_t src = R;
+    if (pair) {
+      const uint32_t within = R & 255u;
+      up = within >= 128u;
+      src = (int64_t)(R >> 8) * 128 + (within & 127u);
+    }
+    const Nf4Dev& w = up ? w1 : w0;
+    u32x4 o = {0u, 0u, 0u, 0u};
+    if (src < w.N) {
+      const uint32_t c = *reinterpret_cast<const uint32_t*>(w.codes + src * (K / 2) + k0 / 2);
+      const int64_t blk = (src * K + k0) / 64;
+      const float a = w.dq ? absmax_at<true>(w, blk) : absmax_at<false>(w, blk);
+      o = deq8(c, a, up ? cb + 16 : cb);
+    }
+    *reinterpret_cast<u32x4*>(out + (int64_t)R * K + k0) = o;
   }
-  uint16_t* dst = out + R * K + k0;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) reinterpret_cast<u32x4*>(dst)[j] = o[j];
 }
 
 // ------------------------------------------------------------------------
@@ -522,7 +557,10 @@ static hipError_t run_bgemm(GemmArgs a, hipStream_t st) {
   a.tiles_n = (a.Nout + BNO - 1) / BNO;
   const int64_t n = a.tiles_m * a.tiles_n;
   if (n == 0) return hipSuccess;
-  bgemm_kernel<MODE><<<dim3((unsigned)n), 256, 0, st>>>(a);
+  if (a.wrows > a.M)
+    bgemm_kernel<MODE, true><<<dim3((unsigned)n), 256, 0, st>>>(a);
+  else
+    bgemm_kernel<MODE, false><<<dim3((unsigned)n), 256, 0, st>>>(a);
   return hipGetLastError();
 }
 
@@ -539,10 +577,12 @@ hipError_t launch_bgemm(int mode, const GemmArgs& a, hipStream_t st) {
 
 hipError_t launch_dequant_rows(const Nf4Dev& w0, const Nf4Dev* w1, const float* codebook0, const float* codebook1,
                                int64_t rows_out, uint16_t* out, hipStream_t st) {
-  const int64_t threads = rows_out * (w0.K / 32);
-  if (threads == 0) return hipSuccess;
-  dequant_rows_kernel<<<dim3((unsigned)((threads + 255) / 256)), 256, 0, st>>>(
-      w0, w1 ? *w1 : w0, w1 ? 1 : 0, codebook0, codebook1 ? codebook1 : codebook0, rows_out, out);
+  const int64_t cpr = w0.K / 8, chunks = rows_out * cpr;
+  if (chunks == 0) return hipSuccess;
+  if (chunks >= ((int64_t)1 << 32) - 1024) return hipErrorInvalidValue;  // 32-bit chunk index
+  dequant_rows_kernel<<<dim3((unsigned)((chunks + 1023) / 1024)), 256, 0, st>>>(
+      w0, w1 ? *w1 : w0, w1 ? 1 : 0, codebook0, codebook1 ? codebook1 : codebook0, (uint32_t)cpr, (uint32_t)chunks,
+      out);
   return hipGetLastError();
 }
 
