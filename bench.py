@@ -41,6 +41,9 @@ def parse():
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="first run one plain device-to-device copy of this many MiB (the known-size kernel "
                          "that calibrates the FETCH_SIZE / WRITE_SIZE counters)")
+    ap.add_argument("--only", type=int, default=None, metavar="IDX",
+                    help="profiling aid: time only workload config IDX (0-4; the skinny linear with 4 rotated "
+                         "weight copies) and print its own JSON line instead of the metric line")
     ap.add_argument("--summarize-traffic", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_MIB"),
                     help="no GPU: turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, "
                          "WRITE_SIZE) of a --copy-probe-mib run into profiles/traffic_<kernel>.txt")
@@ -152,9 +155,8 @@ def gemm_flops(kind, M, D, I, r):
     }[kind]
 
 
-def mlp_step_bench(q, synth, steps, warmup):
+def mlp_step_bench(q, synth, steps, warmup, idx=2):
     import torch
-    idx = 2
     cfg = synth.CONFIGS[idx]
     M, D, I, r = cfg.M, cfg.D, cfg.I, cfg.r
     log("building %s inputs" % cfg.name)
@@ -342,6 +344,20 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    if a.only is not None:
+        cfg = synth.CONFIGS[a.only]
+        if cfg.kind == "mlp":
+            r = mlp_step_bench(q, synth, a.steps, a.warmup, idx=a.only)
+            line = {"workload": cfg.name, "ms_per_step": round(r["ms"], 4),
+                    "tflops": round(r["flops"] / (r["ms"] * 1e-3) / 1e12, 2),
+                    "frac_bf16_peak": round(r["flops"] / (r["ms"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                    "tokens_per_s": round(cfg.M / (r["ms"] * 1e-3), 1),
+                    "kernels": {k: {kk: round(vv, 4) for kk, vv in v.items()} for k, v in r["kernels"].items()}}
+        else:
+            s = linear_bench(q, synth, a.only, a.steps, a.warmup, rotate=4 if a.only == 4 else 1)
+            line = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in s.items()}
+        print(json.dumps(line), flush=True)
+        return
     r = mlp_step_bench(q, synth, a.steps, a.warmup)
     cfg = r["cfg"]
     value = r["flops"] / (r["ms"] * 1e-3) / 1e12
