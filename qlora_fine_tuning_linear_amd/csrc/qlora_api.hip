@@ -317,8 +317,12 @@ int qlora_linear_bwd(const qlora_linear* L, const void* dY, const void* X, const
     return hip_status(launch_skinny_bwd_finish(f, st));
   }
   // T = dY B  (B^T first, so that the product reads rows)
-  QHIP(launch_transpose_rn(u16(L->B), N, r, BT, st));
-  QHIP(launch_transpose_rn(u16(L->A), r, (int)K, AT, st));  // A [r, K] -> A^T [K, r]
+  {
+    TransposeBatch tb;
+    tb.add(u16(L->B), N, r, BT);  // B [N, r] -> B^T [r, N]
+    tb.add(u16(L->A), r, K, AT);  // A [r, K] -> A^T [K, r]
+    QHIP(launch_transpose_multi(tb.J, st));
+  }
   QHIP(launch_lora_down(u16(dY), M, N, BT, r, nullptr, 0, T, nullptr, qplan::plan_down_splits(M, N), down_part, st));
   // dX = dY W0 + s T A
   GemmArgs a = gemm_args();
@@ -466,12 +470,16 @@ int qlora_mlp_bwd(const qlora_mlp* P, const void* dY, const void* X, const qlora
   uint16_t* wbuf = w.bwd_wbuf ? reinterpret_cast<uint16_t*>(b) : nullptr;
 
   // Td = dY B_d
-  QHIP(launch_transpose_rn(u16(P->down.B), D, rd, BdT, st));
-  QHIP(launch_transpose_rn(u16(P->gate.B), I, rg, BgT, st));
-  QHIP(launch_transpose_rn(u16(P->up.B), I, ru, BuT, st));
-  QHIP(launch_transpose_rn(u16(P->down.A), rd, (int)I, AdT, st));
-  QHIP(launch_transpose_rn(u16(P->gate.A), rg, (int)D, AgT, st));
-  QHIP(launch_transpose_rn(u16(P->up.A), ru, (int)D, AuT, st));
+  {
+    TransposeBatch tb;
+    tb.add(u16(P->down.B), D, rd, BdT);
+    tb.add(u16(P->gate.B), I, rg, BgT);
+    tb.add(u16(P->up.B), I, ru, BuT);
+    tb.add(u16(P->down.A), rd, I, AdT);
+    tb.add(u16(P->gate.A), rg, D, AgT);
+    tb.add(u16(P->up.A), ru, D, AuT);
+    QHIP(launch_transpose_multi(tb.J, st));
+  }
   QHIP(launch_lora_down(u16(dY), M, D, BdT, rd, nullptr, 0, Td, nullptr, qplan::plan_down_splits(M, D), down_part,
                         st));
   // dH = dY W_d + s_d Td A_d, with the SwiGLU backward in the epilogue -> dG, dU

@@ -375,7 +375,7 @@ __global__ __launch_bounds__(256) void bgemm_kernel(GemmArgs p) {
     rd(ca, cb, 3, x1, w1);
     mm(x0, w0);
     interleave_reads();
-    wait_vmcnt<8>();  // tile kt+1 landed; the A half of kt+2 may be in flight
+    wait_vmcnt<8>();  // tile kt+1 landed; the first half of kt+2 may be in flight
     stage_barrier();
     __builtin_amdgcn_sched_barrier(0);
     load_second(ca, kt + 2);

@@ -595,6 +595,20 @@ __global__ __launch_bounds__(256) void transpose_rn_kernel(const uint16_t* __res
   BT[i] = B[n * r + j];
 }
 
+// Up to six transposes in one launch: job k turns src[k] [rows, cols] into
+// dst[k] [cols, rows]; the elements of all jobs are numbered one after the
+// other, job k owning [end[k-1], end[k]).
+__global__ __launch_bounds__(256) void transpose_multi_kernel(TransposeJobs J) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  int k = 0;
+  while (k < J.n - 1 && i >= J.end[k]) ++k;
+  if (i >= J.end[k]) return;
+  const int64_t li = i - (k ? J.end[k - 1] : 0);  // index into dst[k]
+  const int64_t R = J.rows[k];
+  const int64_t j = li / R, n = li % R;
+  J.dst[k][li] = J.src[k][n * J.cols[k] + j];
+}
+
 // Sum of split partials [S][M][r0 + r1] in split order into V0 | V1.
 __global__ __launch_bounds__(256) void down_finish_kernel(const float* __restrict__ part, int S, int64_t M,
                                                           int r0, int r1, float* __restrict__ V0,
@@ -743,7 +757,16 @@ __global__ __launch_bounds__(256) void grad_finish_kernel(const float* __restric
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= P * r) return;
   float acc = 0.0f;
-  for (int z = 0; z < S; ++z) acc += part[(int64_t)z * P * r + i];
+  const int64_t stride = P * r;
+  int z = 0;
+  for (; z + 8 <= S; z += 8) {  // 8 loads in flight, added in split order
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = part[(int64_t)(z + u) * stride + i];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc += v[u];
+  }
+  for (; z < S; ++z) acc += part[(int64_t)z * stride + i];
   acc *= s;
   const int64_t pp = i / r;
   const int j = (int)(i % r);
@@ -861,6 +884,14 @@ hipError_t launch_lora_down(const uint16_t* Z, int64_t M, int64_t Kred, const ui
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || S == 1 || !finish) return e;
   down_finish_kernel<<<grid1(M * (r0 + r1), 256), 256, 0, st>>>(part, S, M, r0, r1, V0, V1);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose_multi(const TransposeJobs& J, hipStream_t st) {
+  if (J.n < 1 || J.n > 6) return hipErrorInvalidValue;
+  const int64_t total = J.end[J.n - 1];
+  if (total == 0) return hipSuccess;
+  transpose_multi_kernel<<<grid1(total, 256), 256, 0, st>>>(J);
   return hipGetLastError();
 }
 

@@ -139,6 +139,27 @@ hipError_t launch_lora_down(const uint16_t* Z, int64_t M, int64_t Kred, const ui
                             hipStream_t st, bool finish = true);
 // B [N, r] -> B^T [r, N]
 hipError_t launch_transpose_rn(const uint16_t* B, int64_t N, int r, uint16_t* BT, hipStream_t st);
+// Several transposes in one launch: job k, src [rows, cols] -> dst [cols, rows].
+struct TransposeJobs {
+  const uint16_t* src[6];
+  uint16_t* dst[6];
+  int64_t rows[6];
+  int64_t cols[6];
+  int64_t end[6];  // running element count through job k
+  int32_t n;
+};
+struct TransposeBatch {
+  TransposeJobs J{};
+  void add(const uint16_t* src, int64_t rows, int64_t cols, uint16_t* dst) {
+    const int k = J.n++;
+    J.src[k] = src;
+    J.dst[k] = dst;
+    J.rows[k] = rows;
+    J.cols[k] = cols;
+    J.end[k] = (k ? J.end[k - 1] : 0) + rows * cols;
+  }
+};
+hipError_t launch_transpose_multi(const TransposeJobs& J, hipStream_t st);
 hipError_t launch_lora_grad(int zmode, const uint16_t* Z0, const uint16_t* Z1, int64_t M, int64_t P,
                             const float* V, int r, float s, int msplits, float* part, int out_rp, uint16_t* out,
                             hipStream_t st);
