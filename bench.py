@@ -41,9 +41,10 @@ def parse():
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="first run one plain device-to-device copy of this many MiB (the known-size kernel "
                          "that calibrates the FETCH_SIZE / WRITE_SIZE counters)")
-    ap.add_argument("--only", type=int, default=None, metavar="IDX",
+    ap.add_argument("--only", default=None, metavar="IDX|merge",
                     help="profiling aid: time only workload config IDX (0-4; the skinny linear with 4 rotated "
-                         "weight copies) and print its own JSON line instead of the metric line")
+                         "weight copies), or the 16-bit merge, and print its own JSON line instead of the "
+                         "metric line")
     ap.add_argument("--summarize-traffic", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_MIB"),
                     help="no GPU: turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, "
                          "WRITE_SIZE) of a --copy-probe-mib run into profiles/traffic_<kernel>.txt")
@@ -275,6 +276,45 @@ def linear_bench(q, synth, idx, steps, warmup, rotate=1):
                 frac_hbm_peak=total_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, weight_copies=rotate)
 
 
+def merge_bench(q, synth, steps, warmup, copies=3):
+    """qlora_merge of the Llama-3-8B gate weight (14336 x 4096, r = 16) into
+    bf16, cycled over `copies` weights and outputs (more bytes than the 256 MB
+    last-level cache); HBM-bound: algorithmic bytes = codes + absmax + A + B
+    read once, the 16-bit weight written once."""
+    import torch
+    idx = 2
+    cfg = synth.CONFIGS[idx]
+    inp = synth.mlp_inputs(cfg, synth.seed_of(idx), M=1)
+    N, K, r = cfg.I, cfg.D, cfg.r
+    cb = torch.from_numpy(synth.nf4_codebook()).cuda()
+    Wd = torch.from_numpy(inp["Wg"]).cuda()
+    w = q.nf4_quantize(Wd, cb, dq_group=cfg.dq_group)
+    del Wd
+    A, B = dev_bf16(inp["Ag"]), dev_bf16(inp["Bg"])
+    del inp
+    Ls = [q.QLoraLinear(w, A, B, cfg.alpha)]
+    for _ in range(copies - 1):
+        w2 = q.Nf4Weight(w.codes.clone(), None if w.absmax is None else w.absmax.clone(),
+                         None if w.absmax_q is None else w.absmax_q.clone(),
+                         None if w.absmax_scale is None else w.absmax_scale.clone(), cb, N, K, cfg.dq_group)
+        Ls.append(q.QLoraLinear(w2, A, B, cfg.alpha))
+    outs = [torch.empty(N, K, dtype=torch.bfloat16, device="cuda") for _ in range(copies)]
+    for i in range(warmup):
+        q.qlora_merge(Ls[i % copies], out=outs[i % copies])
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        q.qlora_merge(Ls[i % copies], out=outs[i % copies])
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    nbytes = N * K // 2 + (N * K // 64) * (1 if cfg.dq_group else 4) + 2 * r * K + 2 * N * r + 2 * N * K
+    return dict(workload="merge_16bit_llama3_8b_gate_14336x4096_r16", ms_per_call=ms, algorithmic_bytes=nbytes,
+                hbm_gbs=nbytes / (ms * 1e-3) / 1e9, frac_hbm_peak=nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                weight_copies=copies)
+
+
 def cpu_baseline(synth, target_s):
     """The oracle (fp64 numpy) on the first tokens of the same MLP workload."""
     import numpy as np
@@ -344,7 +384,12 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    if a.only == "merge":
+        s = merge_bench(q, synth, max(10, a.steps), a.warmup)
+        print(json.dumps({k: (round(v, 4) if isinstance(v, float) else v) for k, v in s.items()}), flush=True)
+        return
     if a.only is not None:
+        a.only = int(a.only)
         cfg = synth.CONFIGS[a.only]
         if cfg.kind == "mlp":
             r = mlp_step_bench(q, synth, a.steps, a.warmup, idx=a.only)
@@ -391,6 +436,9 @@ def main():
             log("secondary: %s" % synth.CONFIGS[idx].name)
             s = linear_bench(q, synth, idx, steps, a.warmup, rotate=rot)
             sec.append({k: (round(v, 4) if isinstance(v, float) else v) for k, v in s.items()})
+        log("secondary: merge")
+        s = merge_bench(q, synth, max(10, a.steps), a.warmup)
+        sec.append({k: (round(v, 4) if isinstance(v, float) else v) for k, v in s.items()})
         out["secondary"] = sec
     out["cpu_baseline"] = None if a.no_cpu_baseline else cpu_baseline(synth, a.cpu_seconds)
     if out["cpu_baseline"]:

@@ -49,9 +49,10 @@ extern "C" {
 #define QLORA_ERR_UNSUPPORTED_DEVICE (-5)  /* current device is not gfx950 */
 #define QLORA_ERR_HIP (-6)                 /* a HIP runtime call or launch failed */
 
-/* Output element types of nf4_dequantize. */
+/* Output element types of nf4_dequantize (BF16, F32) and qlora_merge (BF16, F16). */
 #define QLORA_DTYPE_BF16 0
 #define QLORA_DTYPE_F32 1
+#define QLORA_DTYPE_F16 2
 
 /*
  * An NF4-quantized frozen weight W0 [N, K] (QLoRA base weight; the pages name
@@ -175,6 +176,26 @@ int nf4_quantize(const float* W, int64_t N, int64_t K, const float* codebook16,
  * into out [N, K] (device).  Bit-exact with the definition above.
  */
 int nf4_dequantize(const qlora_nf4* w, int32_t out_dtype, void* out, void* stream);
+
+/*
+ * qlora_merge: the adapted layer as one 16-bit weight, for export after
+ * training ("LLM Fine-Tuning in 2026", the listing's 16-bit merge save step;
+ * the update h = W0 x + (alpha/r) B A x of section 1 folded into the weight):
+ *
+ *   out[n, k] = round16( fp32(codebook[q] * absmax')[n, k] + s * (B A)[n, k] ),
+ *   evaluated in fp32 (the scaled product may be fused into the add):
+ *   s = alpha / r in fp32, (B A)[n, k] = sum_j B[n, j] A[j, k] with exact
+ *   products of the bf16 values accumulated in fp32; round16 = round to
+ *   nearest even into out_dtype QLORA_DTYPE_BF16 or QLORA_DTYPE_F16 (fp16
+ *   overflow gives +-inf).
+ *
+ *   L    the layer (W0, A, B, r, alpha as for qlora_linear_fwd)
+ *   out  16-bit [N, K] device output, 16-byte aligned
+ * With B == 0 the result equals nf4_dequantize(W0, QLORA_DTYPE_BF16) bit for
+ * bit.  Needs no workspace; N == 0 is a no-op.  Errors as for the other entry
+ * points (QLORA_ERR_INVALID_ARG for another out_dtype).
+ */
+int qlora_merge(const qlora_linear* L, int32_t out_dtype, void* out, void* stream);
 
 /*
  * Workspace bytes the linear forward and backward need for M tokens.  From

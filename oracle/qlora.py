@@ -21,6 +21,9 @@ hand instead of by autograd; W0 is frozen, so it gets no gradient):
     dB = s dY^T XA                  [N, r]
     dA = s T^T X                    [r, K]
 
+Merge (the listing's 16-bit merge save step): W' = W0 + s B A in float64,
+rounded once to bf16 or fp16 (nearest, ties to even).
+
 SwiGLU MLP built from three such layers (gate, up: D -> I; down: I -> D;
 "MLP SwiGLU" among the hand-derived kernels in section 2; the variant is
 silu(gate) * up):
@@ -57,6 +60,40 @@ def as_f64(x) -> np.ndarray:
 
 def lora_scale(alpha: float, r: int) -> float:
     return float(alpha) / float(r)
+
+
+# ------------------------------------------------------------------ merge
+
+def merge_weight(W, A, B, alpha):
+    """W + (alpha/r) B A in float64: the update h = W0 x + (alpha/r) B A x of
+    "LLM Fine-Tuning in 2026", section 1, folded into one weight, as the
+    listing's 16-bit merge save step does after training."""
+    W, A, B = as_f64(W), as_f64(A), as_f64(B)
+    return W + lora_scale(alpha, A.shape[0]) * (B @ A)
+
+
+def f64_to_bf16_bits(x) -> np.ndarray:
+    """float64 -> bf16 bit patterns in one rounding, to nearest, ties to even
+    (no intermediate fp32).  bf16 keeps 8 significant bits; below its smallest
+    normal 2^-126 the spacing is 2^-133.  Finite values within bf16 range."""
+    x = np.asarray(x, np.float64)
+    _, e = np.frexp(x)                      # |x| in [2^(e-1), 2^e)
+    q = np.maximum(e - 8, -133)             # exponent of the last kept bit
+    y = np.ldexp(np.rint(np.ldexp(x, -q)), q)  # rint: nearest, ties to even
+    return (y.astype(np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+def f64_to_f16_bits(x) -> np.ndarray:
+    """float64 -> fp16 bit patterns in one rounding, to nearest, ties to even
+    (numpy's direct double -> half conversion)."""
+    return np.asarray(x, np.float64).astype(np.float16).view(np.uint16)
+
+
+def merge_16bit(W, A, B, alpha, dtype: str = "bf16") -> np.ndarray:
+    """The merged weight rounded once to 16 bits ("bf16" or "f16"): uint16
+    bit patterns [N, K]."""
+    Wm = merge_weight(W, A, B, alpha)
+    return f64_to_bf16_bits(Wm) if dtype == "bf16" else f64_to_f16_bits(Wm)
 
 
 # ------------------------------------------------------------------ linear

@@ -21,11 +21,12 @@ LIB_PATH = os.path.join(_HERE, "libqlora.so")
 QLORA_OK = 0
 QLORA_DTYPE_BF16 = 0
 QLORA_DTYPE_F32 = 1
+QLORA_DTYPE_F16 = 2
 
 EXPORTED = (
     "qlora_abi_version", "qlora_strerror", "nf4_quantize", "nf4_dequantize",
     "qlora_linear_workspace_bytes", "qlora_linear_fwd", "qlora_linear_bwd",
-    "qlora_mlp_workspace_bytes", "qlora_mlp_fwd", "qlora_mlp_bwd", "qlora_trace_install",
+    "qlora_mlp_workspace_bytes", "qlora_mlp_fwd", "qlora_mlp_bwd", "qlora_trace_install", "qlora_merge",
 )
 
 
@@ -90,6 +91,7 @@ def load_library(path: str = LIB_PATH):
         "qlora_mlp_bwd": (ctypes.c_int, [P(CMlp), vp, vp, P(CMlpSaved), i64, vp, P(CMlpGrads), vp, sz,
                                          vp]),
         "qlora_trace_install": (ctypes.c_int, [P(vp), P(vp), P(i32), i32, P(i32)]),
+        "qlora_merge": (ctypes.c_int, [P(CLinear), i32, vp, vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -229,6 +231,17 @@ def qlora_linear_bwd(L: QLoraLinear, dY: torch.Tensor, X: torch.Tensor, XA: torc
                               dA.data_ptr(), dB.data_ptr(), ws.data_ptr(), ws.numel(), _stream(dev))
     _check("qlora_linear_bwd", st)
     return dX, dA, dB
+
+
+def qlora_merge(L: QLoraLinear, dtype: torch.dtype = torch.bfloat16, out: Optional[torch.Tensor] = None):
+    """qlora_merge: the layer as one 16-bit weight [N, K], round16(deq(W0) + s B A)."""
+    lib = load_library()
+    if out is None:
+        out = torch.empty(L.W0.N, L.W0.K, dtype=dtype, device=L.A.device)
+    code = QLORA_DTYPE_F16 if out.dtype == torch.float16 else QLORA_DTYPE_BF16
+    cl = L.c()
+    _check("qlora_merge", lib.qlora_merge(ctypes.byref(cl), code, out.data_ptr(), _stream(out.device)))
+    return out
 
 
 # ------------------------------------------------------------------ MLP

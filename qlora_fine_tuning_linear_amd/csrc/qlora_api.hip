@@ -171,6 +171,13 @@ int nf4_dequantize(const qlora_nf4* w, int32_t out_dtype, void* out, void* strea
                                           static_cast<hipStream_t>(stream)));
 }
 
+int qlora_merge(const qlora_linear* L, int32_t out_dtype, void* out, void* stream) {
+  QTRY(qv_merge(L, out_dtype, out));
+  QTRY(check_device());
+  return hip_status(launch_merge(to_dev(L->W0), L->W0.codebook, u16(L->A), u16(L->B), L->r, lora_s(*L),
+                                 out_dtype == QLORA_DTYPE_F16 ? 1 : 0, u16m(out), static_cast<hipStream_t>(stream)));
+}
+
 int qlora_linear_fwd(const qlora_linear* L, const void* X, int64_t M, void* Y, float* XA_saved, void* ws,
                      size_t ws_bytes, void* stream) {
   QTRY(qv_linear_fwd(L, X, M, Y, XA_saved, ws, ws_bytes));

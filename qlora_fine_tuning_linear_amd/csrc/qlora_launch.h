@@ -111,6 +111,9 @@ struct SkinnyBwdArgs {
 
 hipError_t launch_nf4_quantize(const float* W, int64_t nblocks, const float* codebook, int dq, uint8_t* codes,
                                float* absmax, uint8_t* absmax_q, float* absmax_scale, hipStream_t st);
+// out [N, K] 16-bit = round16(deq(w) + s B A) (f16: fp16, else bf16).
+hipError_t launch_merge(const Nf4Dev& w, const float* codebook, const uint16_t* A, const uint16_t* B, int r,
+                        float s, int f16, uint16_t* out, hipStream_t st);
 hipError_t launch_nf4_dequantize(const Nf4Dev& w, const float* codebook, int out_f32, void* out, hipStream_t st);
 hipError_t launch_qgemm(int mode, const GemmArgs& a, const qplan::GemmPlan& pl, hipStream_t st);
 hipError_t launch_bgemm(int mode, const GemmArgs& a, hipStream_t st);

@@ -76,6 +76,13 @@ int qv_dequantize(const qlora_nf4* w, int32_t out_dtype, const void* out) {
   return check_ptr(out);
 }
 
+int qv_merge(const qlora_linear* L, int32_t out_dtype, const void* out) {
+  int st = check_linear(L);
+  if (st) return st;
+  if (out_dtype != QLORA_DTYPE_BF16 && out_dtype != QLORA_DTYPE_F16) return QLORA_ERR_INVALID_ARG;
+  return check_ptr(out);
+}
+
 int qv_linear_fwd(const qlora_linear* L, const void* X, int64_t M, const void* Y, const float* XA, const void* ws,
                   size_t ws_bytes) {
   int st = check_linear(L);

@@ -9,6 +9,7 @@
 int qv_quantize(const float* W, int64_t N, int64_t K, const float* codebook16, int32_t blocksize, int32_t dq_group,
                 const uint8_t* codes, const float* absmax, const uint8_t* absmax_q, const float* absmax_scale);
 int qv_dequantize(const qlora_nf4* w, int32_t out_dtype, const void* out);
+int qv_merge(const qlora_linear* L, int32_t out_dtype, const void* out);
 int qv_linear_fwd(const qlora_linear* L, const void* X, int64_t M, const void* Y, const float* XA, const void* ws,
                   size_t ws_bytes);
 int qv_linear_bwd(const qlora_linear* L, const void* dY, const void* X, const float* XA, int64_t M, const void* dX,

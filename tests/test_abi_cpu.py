@@ -161,3 +161,17 @@ def test_workspace_grows_with_tokens(lib):
     b = lib.qlora_mlp_workspace_bytes(ctypes.byref(P), 8192)
     assert 0 < a < b
     assert lib.qlora_mlp_workspace_bytes(ctypes.byref(P), 0) == 0
+
+
+def test_merge_rejections(lib):
+    call = lambda L, dt=0, out=FAKE: lib.qlora_merge(ctypes.byref(L), dt, out, None)
+    assert call(linear(), dt=1) == INVALID          # fp32 is not a merge output type
+    assert call(linear(), dt=7) == INVALID
+    assert call(linear(), out=None) == INVALID
+    assert call(linear(), out=FAKE + 2) == MISALIGNED
+    assert call(linear(K=96)) == SHAPE
+    assert call(linear(r=0)) == SHAPE
+    assert call(linear(r=129)) == SHAPE
+    assert call(linear(alpha=float("nan"))) == INVALID
+    assert call(linear(codes=FAKE + 8)) == MISALIGNED
+    assert lib.qlora_merge(None, 0, FAKE, None) == INVALID

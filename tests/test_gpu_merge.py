@@ -1,0 +1,130 @@
+"""GPU parity of qlora_merge (the adapted layer as one 16-bit weight) against
+the oracle's merge_16bit.
+
+The kernel evaluates deq(W0) + s B A in fp32 (B A accumulated in fp32 on the
+matrix cores), the oracle in fp64; both round once to 16 bits.  The two can
+differ only where the exact value lies within about 1e-7 (relative) of a
+rounding boundary, so the bar is: every element within one unit in the last
+place of the 16-bit type, and at least 99.9% of them bit-identical.  With
+B = 0 the result is the dequantized weight and must match bit for bit.
+
+Cases: ragged shapes (rows not a multiple of the 128-row workgroup, a
+64-column tail tile, rank 65 and 128), both absmax modes, both 16-bit types,
+and full-size weights of the Llama-3-8B gate projection and the skinny
+gate_proj on sampled rows.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import nf4 as onf4
+from oracle import qlora as oq
+
+from gpu_util import bf16_dev, make_linear, u16_host
+
+pytestmark = pytest.mark.gpu
+
+q = pytest.importorskip("qlora_fine_tuning_linear_amd")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    q.load_library()
+
+
+def _bits_to_f64(bits, dtype):
+    bits = np.asarray(bits, np.uint16)
+    if dtype == "bf16":
+        return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    return bits.view(np.float16).astype(np.float64)
+
+
+def _assert_merge_close(got, ref, dtype):
+    """Every element within one 16-bit ulp of the oracle; >= 99.9% identical."""
+    g, r = _bits_to_f64(got, dtype), _bits_to_f64(ref, dtype)
+    assert np.all(np.isfinite(g))
+    # spacing of the 16-bit type at the reference value (subnormal floor)
+    mant, tiny = (7, 2.0 ** -133) if dtype == "bf16" else (10, 2.0 ** -24)
+    _, e = np.frexp(r)
+    ulp = np.maximum(np.ldexp(1.0, e - 1 - mant), tiny)
+    bad = np.abs(g - r) > ulp
+    assert not bad.any(), (np.argwhere(bad)[:5], g[bad][:5], r[bad][:5])
+    same = np.mean(got == ref)
+    assert same >= 0.999, same
+
+
+def _inputs(N, K, r, seed):
+    rng = np.random.default_rng(seed)
+    W = synth.weight_rows(seed, 2, K, 0, N)
+    A = onf4.to_bf16_bits(rng.uniform(-1.0 / np.sqrt(K), 1.0 / np.sqrt(K), (r, K)).astype(np.float32))
+    B = onf4.to_bf16_bits((rng.standard_normal((N, r)) * 0.01).astype(np.float32))
+    return W, A, B
+
+
+# (name, N, K, r, dq, alpha, dtype, seed)
+CASES = [
+    ("c0_512x512_r8", 512, 512, 8, 0, 16.0, "bf16", 1000),
+    ("ragged_192x320_r65_dq", 192, 320, 65, 256, 16.0, "bf16", 31),
+    ("r128_256x512_f16", 256, 512, 128, 0, 16.0, "f16", 32),
+    ("1024x4096_r16_dq_f16", 1024, 4096, 16, 256, 32.0, "f16", 33),
+    ("64x64_r1", 64, 64, 1, 0, 2.0, "bf16", 34),
+]
+
+
+@pytest.mark.parametrize("name,N,K,r,dq,alpha,dtype,seed", CASES, ids=[c[0] for c in CASES])
+def test_merge_matches_oracle(name, N, K, r, dq, alpha, dtype, seed, codebook):
+    print("case", name, flush=True)
+    W, A, B = _inputs(N, K, r, seed)
+    L, Wh = make_linear(q, W, A, B, alpha, codebook, dq)
+    out = q.qlora_merge(L, torch.bfloat16 if dtype == "bf16" else torch.float16)
+    torch.cuda.synchronize()
+    ref = oq.merge_16bit(Wh, A, B, alpha, dtype)
+    _assert_merge_close(u16_host(out), ref, dtype)
+
+
+@pytest.mark.parametrize("dq", [0, 256])
+def test_merge_b_zero_is_dequantize_bitexact(dq, codebook):
+    print("case b0 dq", dq, flush=True)
+    N, K, r = 320, 640, 16
+    W, A, _ = _inputs(N, K, r, seed=77)
+    L, Wh = make_linear(q, W, A, np.zeros((N, r), np.uint16), 16.0, codebook, dq)
+    got = u16_host(q.qlora_merge(L))
+    deq = u16_host(q.nf4_dequantize(L.W0, torch.bfloat16))
+    assert np.array_equal(got, deq)
+    assert np.array_equal(got, oq.merge_16bit(Wh, A, np.zeros((N, r)), 16.0, "bf16"))
+
+
+# full-size weights, sampled rows: (name, config index, weight stream)
+FULL = [("c2_gate_14336x4096", 2, "Wg"), ("c4_gate_28672x8192_dq", 4, "W0")]
+
+
+@pytest.mark.parametrize("name,idx,wname", FULL, ids=[f[0] for f in FULL])
+def test_merge_full_size_sampled_rows(name, idx, wname, codebook):
+    print("case", name, flush=True)
+    cfg = synth.CONFIGS[idx]
+    seed = synth.seed_of(idx)
+    if cfg.kind == "mlp":
+        inp = synth.mlp_inputs(cfg, seed, M=1)
+        W, A, B = inp["Wg"], inp["Ag"], inp["Bg"]
+    else:
+        inp = synth.linear_inputs(cfg, seed, M=1)
+        W, A, B = inp["W0"], inp["A"], inp["B"]
+    del inp
+    Wd = torch.from_numpy(W).cuda()
+    cbd = torch.from_numpy(codebook).cuda()
+    qw = q.nf4_quantize(Wd, cbd, dq_group=cfg.dq_group)
+    del Wd
+    L = q.QLoraLinear(qw, bf16_dev(A), bf16_dev(B), cfg.alpha)
+    out = q.qlora_merge(L)
+    torch.cuda.synchronize()
+    N, K = W.shape
+    ow = onf4.quantize(W, codebook, dq_group=cfg.dq_group)
+    rows = np.unique(np.concatenate([np.arange(0, N, N // 48), [N - 1]]))
+    got = u16_host(out)[rows]
+    for i, n in enumerate(rows):
+        Wh = onf4.dequantize(ow, codebook, rows=slice(int(n), int(n) + 1)).astype(np.float64)
+        ref = oq.merge_16bit(Wh, A, B[n:n + 1], cfg.alpha, "bf16")
+        _assert_merge_close(got[i:i + 1], ref, "bf16")

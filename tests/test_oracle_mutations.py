@@ -23,6 +23,11 @@ MUTATIONS = [
     ("qlora.py", "dG = dH * U * silu_grad(G)", "dG = dH * U * sigmoid(G)"),
     ("qlora.py", "dU = dH * silu(G)", "dU = dH * sigmoid(G)"),
     ("qlora.py", "return float(alpha) / float(r)", "return float(alpha) / float(r + 1)"),
+    ("qlora.py", "return W + lora_scale(alpha, A.shape[0]) * (B @ A)", "return W + alpha * (B @ A)"),
+    ("qlora.py", "return W + lora_scale(alpha, A.shape[0]) * (B @ A)",
+     "return W + lora_scale(alpha, A.shape[0]) * (B @ A[:, ::-1])"),
+    ("qlora.py", "q = np.maximum(e - 8, -133)", "q = np.maximum(e - 9, -133)"),
+    ("qlora.py", "y = np.ldexp(np.rint(np.ldexp(x, -q)), q)", "y = np.ldexp(np.floor(np.ldexp(x, -q) + 0.5), q)"),
     ("nf4.py", 'side="left"', 'side="right"'),
     ("nf4.py", "flat[0::2] | (flat[1::2] << np.uint8(4))", "flat[1::2] | (flat[0::2] << np.uint8(4))"),
     ("nf4.py", "np.minimum(np.rint(ratio), 255.0)", "np.minimum(np.floor(ratio), 255.0)"),

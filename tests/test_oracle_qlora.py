@@ -193,3 +193,65 @@ def test_mlp_row_chunks_equal_whole():
     np.testing.assert_allclose(c["G"], f["G"], rtol=1e-13, atol=1e-13)
     for k in ("dX", "dA_g", "dB_g", "dA_u", "dB_u", "dA_d", "dB_d"):
         np.testing.assert_allclose(c[k], b[k], rtol=1e-12, atol=1e-12)
+
+
+# ------------------------------------------------------------------ merge
+
+def test_merge_weight_is_the_forward_weight():
+    """The merged weight reproduces the layer's forward (linear_forward is a
+    separate function): a wrong scale or a transposed B A fails here."""
+    X, Wh, A, B, _ = _small_linear(M=4, K=64, N=7, r=3)
+    for alpha in (3.0, 16.0):
+        Y, _ = qlora.linear_forward(X, Wh, A, B, alpha)
+        np.testing.assert_allclose(X @ qlora.merge_weight(Wh, A, B, alpha).T, Y, rtol=1e-12, atol=1e-12)
+
+
+def test_merge_b_zero_is_dequantize_bits():
+    rng = np.random.default_rng(5)
+    cb = synth.nf4_codebook()
+    W = (rng.standard_normal((8, 128)) * 0.02).astype(np.float32)
+    for dq in (0, 256):
+        qw = nf4.quantize(W, cb, dq_group=dq)
+        Wh = nf4.dequantize(qw, cb)
+        A = rng.uniform(-0.1, 0.1, (4, 128))
+        got = qlora.merge_16bit(Wh, A, np.zeros((8, 4)), 16.0, "bf16")
+        assert np.array_equal(got, nf4.dequantize_bf16(qw, cb))
+
+
+def _bits_to_f64(bits, dtype):
+    bits = np.asarray(bits, np.uint16)
+    if dtype == "bf16":
+        return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    return bits.view(np.float16).astype(np.float64)
+
+
+def _check_nearest_even(x, bits, dtype):
+    """Brute force: the rounded value is at least as close to x as both 16-bit
+    neighbours, and on an exact tie its last mantissa bit is 0."""
+    y = _bits_to_f64(bits, dtype)
+    for step in (-1, 1):
+        nb = (bits.astype(np.int32) + step * np.where(y >= 0, 1, -1)).astype(np.uint16)
+        z = _bits_to_f64(nb, dtype)
+        dy, dz = np.abs(y - x), np.abs(z - x)
+        assert np.all(dy <= dz), (x[dy > dz][:5], y[dy > dz][:5])
+        tie = dy == dz
+        assert np.all((bits[tie] & 1) == 0)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_one_step_16bit_rounding(dtype):
+    rng = np.random.default_rng(9)
+    conv = qlora.f64_to_bf16_bits if dtype == "bf16" else qlora.f64_to_f16_bits
+    # random values of several magnitudes
+    x = rng.standard_normal(20000) * np.exp2(rng.integers(-12, 12, 20000))
+    _check_nearest_even(x, conv(x), dtype)
+    # exact ties between neighbours, and values a hair above a tie (below fp32
+    # resolution there, so a rounding through fp32 would treat them as ties)
+    b = conv(rng.standard_normal(4000))
+    lo = _bits_to_f64(b, dtype)
+    hi = _bits_to_f64((b.astype(np.int32) + np.where(lo >= 0, 1, -1)).astype(np.uint16), dtype)
+    tie = (lo + hi) / 2
+    _check_nearest_even(tie, conv(tie), dtype)
+    above = tie + (hi - lo) * 2.0 ** -40
+    got = conv(above)
+    assert np.array_equal(_bits_to_f64(got, dtype), hi)
