@@ -24,10 +24,14 @@ What it computes, and from where:
   instead of store").  These have plain definitions, so the oracle is the
   definition evaluated in float64 with no intermediate rounding.
 
+* ``rmsnorm`` - the RMSNorm in front of the MLP block with one saved inverse
+  RMS per row (the fused-RMSNorm part of section 2 of "LLM Fine-Tuning in
+  2026"), forward and hand-derived backward, the definition in float64.
+
 Pins (``tests/test_oracle_*.py``) tie every function to something other than
 itself: exact-rational brute force for the code search, codebook-exact blocks,
 idempotence, error bounds, the B = 0 reduction to the plain base matmul, the
 pages' column-vector form of the update, the merged-weight form, and central
 finite differences of <Y, dY> for every gradient.
 """
-from . import nf4, qlora  # noqa: F401
+from . import nf4, qlora, rmsnorm  # noqa: F401

@@ -28,6 +28,11 @@ MUTATIONS = [
      "return W + lora_scale(alpha, A.shape[0]) * (B @ A[:, ::-1])"),
     ("qlora.py", "q = np.maximum(e - 8, -133)", "q = np.maximum(e - 9, -133)"),
     ("qlora.py", "y = np.ldexp(np.rint(np.ldexp(x, -q)), q)", "y = np.ldexp(np.floor(np.ldexp(x, -q) + 0.5), q)"),
+    ("rmsnorm.py", "dX = rstd[:, None] * g - (rstd ** 3 / D * c)[:, None] * X",
+     "dX = rstd[:, None] * g + (rstd ** 3 / D * c)[:, None] * X"),
+    ("rmsnorm.py", "rstd ** 3 / D", "rstd ** 2 / D"),
+    ("rmsnorm.py", "dw = np.sum(dY * X * rstd[:, None], axis=0)", "dw = np.sum(dY * X, axis=0)"),
+    ("rmsnorm.py", "ms = np.mean(X * X, axis=1)", "ms = np.sum(X * X, axis=1)"),
     ("nf4.py", 'side="left"', 'side="right"'),
     ("nf4.py", "flat[0::2] | (flat[1::2] << np.uint8(4))", "flat[1::2] | (flat[0::2] << np.uint8(4))"),
     ("nf4.py", "np.minimum(np.rint(ratio), 255.0)", "np.minimum(np.floor(ratio), 255.0)"),
@@ -45,7 +50,7 @@ def sandbox(tmp_path_factory):
     shutil.copytree(os.path.join(ROOT, "synth"), d / "synth",
                     ignore=shutil.ignore_patterns("*.tmp*", "__pycache__"))
     os.makedirs(d / "tests" / "golden")
-    for f in ("conftest.py", "test_oracle_nf4.py", "test_oracle_qlora.py"):
+    for f in ("conftest.py", "test_oracle_nf4.py", "test_oracle_qlora.py", "test_oracle_rmsnorm.py"):
         shutil.copy(os.path.join(ROOT, "tests", f), d / "tests" / f)
     shutil.copy(os.path.join(ROOT, "tests", "golden", "nf4_codebook.txt"),
                 d / "tests" / "golden" / "nf4_codebook.txt")
@@ -62,6 +67,6 @@ def test_pins_catch_mutation(sandbox, fname, old, new):
     assert old in src
     (od / fname).write_text(src.replace(old, new))
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                        "tests/test_oracle_nf4.py", "tests/test_oracle_qlora.py"],
+                        "tests/test_oracle_nf4.py", "tests/test_oracle_qlora.py", "tests/test_oracle_rmsnorm.py"],
                        cwd=str(sandbox), capture_output=True, text=True, timeout=300)
     assert r.returncode == 1, "mutation survived: %s\n%s" % (new, r.stdout[-2000:])
