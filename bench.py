@@ -41,10 +41,10 @@ def parse():
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="first run one plain device-to-device copy of this many MiB (the known-size kernel "
                          "that calibrates the FETCH_SIZE / WRITE_SIZE counters)")
-    ap.add_argument("--only", default=None, metavar="IDX|merge",
+    ap.add_argument("--only", default=None, metavar="IDX|merge|rmsnorm",
                     help="profiling aid: time only workload config IDX (0-4; the skinny linear with 4 rotated "
-                         "weight copies), or the 16-bit merge, and print its own JSON line instead of the "
-                         "metric line")
+                         "weight copies), the 16-bit merge or RMSNorm, and print its own JSON line instead of "
+                         "the metric line")
     ap.add_argument("--summarize-traffic", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_MIB"),
                     help="no GPU: turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, "
                          "WRITE_SIZE) of a --copy-probe-mib run into profiles/traffic_<kernel>.txt")
@@ -315,6 +315,42 @@ def merge_bench(q, synth, steps, warmup, copies=3):
                 weight_copies=copies)
 
 
+def rmsnorm_bench(q, synth, steps, warmup, M=8192, D=4096, eps=1e-5):
+    """rmsnorm_fwd and rmsnorm_bwd (with dw) at the Llama-3-8B hidden size and
+    the MLP workload's token count; HBM-bound.  Algorithmic bytes: forward
+    reads X and writes Y (+ rstd); backward reads dY and X and writes dX (+ rstd,
+    w, dw)."""
+    import torch
+    X = dev_bf16(synth.normal_bf16(1, 40, M * D).reshape(M, D))
+    dY = dev_bf16(synth.normal_bf16(1, 41, M * D).reshape(M, D))
+    w = dev_bf16(synth.normal_bf16(1, 42, D, 1.0, 0.1))
+    Y, rstd = torch.empty_like(X), torch.empty(M, dtype=torch.float32, device="cuda")
+    dX, dw = torch.empty_like(X), torch.empty(D, dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(int(q.load_library().rmsnorm_bwd_workspace_bytes(M, D)), 256), dtype=torch.uint8,
+                     device="cuda")
+
+    def timed(f):
+        for _ in range(warmup):
+            f()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            f()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    f_ms = timed(lambda: q.rmsnorm_fwd(X, w, eps, Y=Y, rstd=rstd))
+    b_ms = timed(lambda: q.rmsnorm_bwd(dY, X, w, rstd, dX=dX, dw=dw, ws=ws))
+    fb = 2 * M * D * 2 + 4 * M + 2 * D
+    bb = 3 * M * D * 2 + 4 * M + 2 * D + 4 * D
+    return dict(workload="rmsnorm_m%d_d%d" % (M, D), fwd_ms=f_ms, bwd_ms=b_ms,
+                fwd_hbm_gbs=fb / (f_ms * 1e-3) / 1e9, bwd_hbm_gbs=bb / (b_ms * 1e-3) / 1e9,
+                fwd_frac_hbm_peak=fb / (f_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                bwd_frac_hbm_peak=bb / (b_ms * 1e-3) / 1e9 / HBM_PEAK_GBS)
+
+
 def cpu_baseline(synth, target_s):
     """The oracle (fp64 numpy) on the first tokens of the same MLP workload."""
     import numpy as np
@@ -384,8 +420,8 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    if a.only == "merge":
-        s = merge_bench(q, synth, max(10, a.steps), a.warmup)
+    if a.only in ("merge", "rmsnorm"):
+        s = (merge_bench if a.only == "merge" else rmsnorm_bench)(q, synth, max(10, a.steps), a.warmup)
         print(json.dumps({k: (round(v, 4) if isinstance(v, float) else v) for k, v in s.items()}), flush=True)
         return
     if a.only is not None:
@@ -438,6 +474,9 @@ def main():
             sec.append({k: (round(v, 4) if isinstance(v, float) else v) for k, v in s.items()})
         log("secondary: merge")
         s = merge_bench(q, synth, max(10, a.steps), a.warmup)
+        sec.append({k: (round(v, 4) if isinstance(v, float) else v) for k, v in s.items()})
+        log("secondary: rmsnorm")
+        s = rmsnorm_bench(q, synth, max(20, a.steps), a.warmup)
         sec.append({k: (round(v, 4) if isinstance(v, float) else v) for k, v in s.items()})
         out["secondary"] = sec
     out["cpu_baseline"] = None if a.no_cpu_baseline else cpu_baseline(synth, a.cpu_seconds)

@@ -198,6 +198,43 @@ int nf4_dequantize(const qlora_nf4* w, int32_t out_dtype, void* out, void* strea
 int qlora_merge(const qlora_linear* L, int32_t out_dtype, void* out, void* stream);
 
 /*
+ * rmsnorm_fwd: the RMSNorm in front of the MLP block ("LLM Fine-Tuning in
+ * 2026", the fused RMSNorm of section 2: the forward keeps one inverse RMS per
+ * row for the backward and no full-size intermediate).  Per row m of X:
+ *
+ *   rstd[m] = 1 / sqrt(mean_j X[m, j]^2 + eps),  Y[m, j] = X[m, j] rstd[m] w[j]
+ *
+ * fp32 arithmetic, Y rounded to bf16 (nearest even).
+ *   X     bf16 [M, D] input          w     bf16 [D] input
+ *   Y     bf16 [M, D] output         rstd  fp32 [M] output, kept for rmsnorm_bwd
+ *   D % 8 == 0 and 8 <= D <= 8192 (QLORA_ERR_UNSUPPORTED_SHAPE otherwise);
+ *   eps finite and >= 0 (QLORA_ERR_INVALID_ARG otherwise; with eps == 0 an
+ *   all-zero row gives non-finite values).  Needs no workspace; M == 0 is a
+ *   no-op.  All pointers 16-byte aligned.
+ */
+int rmsnorm_fwd(const void* X, const void* w, int64_t M, int64_t D, float eps, void* Y, float* rstd,
+                void* stream);
+
+/* Workspace bytes rmsnorm_bwd needs with dw requested (0 without dw). */
+size_t rmsnorm_bwd_workspace_bytes(int64_t M, int64_t D);
+
+/*
+ * rmsnorm_bwd: gradients of <Y, dY> for rmsnorm_fwd, derived by hand.  With
+ * g = dY[m] * w (elementwise):
+ *
+ *   dX[m] = rstd[m] g - rstd[m]^3 / D (sum_j g_j X[m, j]) X[m]     (bf16 out)
+ *   dw    = sum_m dY[m] X[m] rstd[m]                                (fp32 out)
+ *
+ * fp32 arithmetic; dw is summed in a fixed order (bitwise reproducible) and is
+ * optional: dw == NULL skips it, and then ws may be NULL.
+ *   dY, X bf16 [M, D]; w bf16 [D]; rstd fp32 [M] from rmsnorm_fwd; dX bf16
+ *   [M, D] output; ws of ws_bytes >= rmsnorm_bwd_workspace_bytes(M, D).
+ * Shapes and errors as for rmsnorm_fwd.  M == 0 writes dw = 0.
+ */
+int rmsnorm_bwd(const void* dY, const void* X, const void* w, const float* rstd, int64_t M, int64_t D,
+                void* dX, float* dw, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Workspace bytes the linear forward and backward need for M tokens.  From
  * M = 512 tokens on, the GEMMs expand the NF4 weight once per call into a
  * bf16 copy held in the workspace (N*K*2 bytes) instead of expanding it in

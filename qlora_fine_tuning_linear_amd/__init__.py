@@ -27,6 +27,7 @@ EXPORTED = (
     "qlora_abi_version", "qlora_strerror", "nf4_quantize", "nf4_dequantize",
     "qlora_linear_workspace_bytes", "qlora_linear_fwd", "qlora_linear_bwd",
     "qlora_mlp_workspace_bytes", "qlora_mlp_fwd", "qlora_mlp_bwd", "qlora_trace_install", "qlora_merge",
+    "rmsnorm_fwd", "rmsnorm_bwd", "rmsnorm_bwd_workspace_bytes",
 )
 
 
@@ -92,6 +93,9 @@ def load_library(path: str = LIB_PATH):
                                          vp]),
         "qlora_trace_install": (ctypes.c_int, [P(vp), P(vp), P(i32), i32, P(i32)]),
         "qlora_merge": (ctypes.c_int, [P(CLinear), i32, vp, vp]),
+        "rmsnorm_fwd": (ctypes.c_int, [vp, vp, i64, i64, ctypes.c_float, vp, vp, vp]),
+        "rmsnorm_bwd": (ctypes.c_int, [vp, vp, vp, vp, i64, i64, vp, vp, vp, sz, vp]),
+        "rmsnorm_bwd_workspace_bytes": (sz, [i64, i64]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -231,6 +235,36 @@ def qlora_linear_bwd(L: QLoraLinear, dY: torch.Tensor, X: torch.Tensor, XA: torc
                               dA.data_ptr(), dB.data_ptr(), ws.data_ptr(), ws.numel(), _stream(dev))
     _check("qlora_linear_bwd", st)
     return dX, dA, dB
+
+
+def rmsnorm_fwd(X: torch.Tensor, w: torch.Tensor, eps: float, Y: Optional[torch.Tensor] = None,
+                rstd: Optional[torch.Tensor] = None):
+    """rmsnorm_fwd: returns (Y bf16 [M, D], rstd fp32 [M])."""
+    lib = load_library()
+    M, D = X.shape
+    Y = torch.empty_like(X) if Y is None else Y
+    rstd = torch.empty(M, dtype=torch.float32, device=X.device) if rstd is None else rstd
+    _check("rmsnorm_fwd", lib.rmsnorm_fwd(_ptr(X), _ptr(w), M, D, float(eps), _ptr(Y), _ptr(rstd),
+                                          _stream(X.device)))
+    return Y, rstd
+
+
+def rmsnorm_bwd(dY: torch.Tensor, X: torch.Tensor, w: torch.Tensor, rstd: torch.Tensor, want_dw: bool = True,
+                dX: Optional[torch.Tensor] = None, dw: Optional[torch.Tensor] = None,
+                ws: Optional[torch.Tensor] = None):
+    """rmsnorm_bwd: returns (dX bf16 [M, D], dw fp32 [D] or None)."""
+    lib = load_library()
+    M, D = X.shape
+    dX = torch.empty_like(X) if dX is None else dX
+    if want_dw and dw is None:
+        dw = torch.empty(D, dtype=torch.float32, device=X.device)
+    nbytes = lib.rmsnorm_bwd_workspace_bytes(M, D) if want_dw else 0
+    if ws is None:
+        ws = torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=X.device)
+    _check("rmsnorm_bwd", lib.rmsnorm_bwd(_ptr(dY), _ptr(X), _ptr(w), _ptr(rstd), M, D, _ptr(dX),
+                                          _ptr(dw) if want_dw else None, _ptr(ws), ws.numel(),
+                                          _stream(X.device)))
+    return dX, (dw if want_dw else None)
 
 
 def qlora_merge(L: QLoraLinear, dtype: torch.dtype = torch.bfloat16, out: Optional[torch.Tensor] = None):

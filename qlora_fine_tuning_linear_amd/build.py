@@ -29,7 +29,8 @@ def build(verbose: bool = False) -> str:
     bdir = os.path.join(HERE, "_build")
     os.makedirs(bdir, exist_ok=True)
     objs = []
-    for src in ("qlora_kernels.hip", "qlora_bgemm.hip", "qlora_skinny.hip", "qlora_merge.hip", "qlora_api.hip"):
+    for src in ("qlora_kernels.hip", "qlora_bgemm.hip", "qlora_skinny.hip", "qlora_merge.hip", "qlora_rmsnorm.hip",
+                "qlora_api.hip"):
         obj = os.path.join(bdir, src + ".o")
         cmd = ["hipcc", "-c"] + HIP_FLAGS + [os.path.join(CSRC, src), "-o", obj]
         _run(cmd, verbose)

@@ -171,6 +171,25 @@ int nf4_dequantize(const qlora_nf4* w, int32_t out_dtype, void* out, void* strea
                                           static_cast<hipStream_t>(stream)));
 }
 
+int rmsnorm_fwd(const void* X, const void* w, int64_t M, int64_t D, float eps, void* Y, float* rstd,
+                void* stream) {
+  QTRY(qv_rmsnorm_fwd(X, w, M, D, eps, Y, rstd));
+  if (M == 0) return QLORA_OK;
+  QTRY(check_device());
+  return hip_status(launch_rmsnorm_fwd(u16(X), u16(w), M, D, eps, u16m(Y), rstd, static_cast<hipStream_t>(stream)));
+}
+
+size_t rmsnorm_bwd_workspace_bytes(int64_t M, int64_t D) { return qv_rmsnorm_ws(M, D); }
+
+int rmsnorm_bwd(const void* dY, const void* X, const void* w, const float* rstd, int64_t M, int64_t D, void* dX,
+                float* dw, void* ws, size_t ws_bytes, void* stream) {
+  QTRY(qv_rmsnorm_bwd(dY, X, w, rstd, M, D, dX, dw, ws, ws_bytes));
+  if (M == 0 && !dw) return QLORA_OK;
+  QTRY(check_device());
+  return hip_status(launch_rmsnorm_bwd(u16(dY), u16(X), u16(w), rstd, M, D, u16m(dX), dw,
+                                       reinterpret_cast<float*>(ws), static_cast<hipStream_t>(stream)));
+}
+
 int qlora_merge(const qlora_linear* L, int32_t out_dtype, void* out, void* stream) {
   QTRY(qv_merge(L, out_dtype, out));
   QTRY(check_device());

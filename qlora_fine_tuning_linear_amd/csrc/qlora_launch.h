@@ -114,6 +114,13 @@ hipError_t launch_nf4_quantize(const float* W, int64_t nblocks, const float* cod
 // out [N, K] 16-bit = round16(deq(w) + s B A) (f16: fp16, else bf16).
 hipError_t launch_merge(const Nf4Dev& w, const float* codebook, const uint16_t* A, const uint16_t* B, int r,
                         float s, int f16, uint16_t* out, hipStream_t st);
+// RMSNorm: Y = X rstd w (rstd saved per row) and its backward; D % 8 == 0,
+// D <= 8192.  The backward with dw needs part fp32 [rmsnorm_bwd_groups(M)][D].
+int rmsnorm_bwd_groups(int64_t M);
+hipError_t launch_rmsnorm_fwd(const uint16_t* X, const uint16_t* w, int64_t M, int64_t D, float eps, uint16_t* Y,
+                              float* rstd, hipStream_t st);
+hipError_t launch_rmsnorm_bwd(const uint16_t* dY, const uint16_t* X, const uint16_t* w, const float* rstd,
+                              int64_t M, int64_t D, uint16_t* dX, float* dw, float* part, hipStream_t st);
 hipError_t launch_nf4_dequantize(const Nf4Dev& w, const float* codebook, int out_f32, void* out, hipStream_t st);
 hipError_t launch_qgemm(int mode, const GemmArgs& a, const qplan::GemmPlan& pl, hipStream_t st);
 hipError_t launch_bgemm(int mode, const GemmArgs& a, hipStream_t st);

@@ -76,6 +76,39 @@ int qv_dequantize(const qlora_nf4* w, int32_t out_dtype, const void* out) {
   return check_ptr(out);
 }
 
+static int check_rms(int64_t M, int64_t D) {
+  if (M < 0) return QLORA_ERR_INVALID_ARG;
+  if (D < 8 || D > 8192 || D % 8 != 0) return QLORA_ERR_UNSUPPORTED_SHAPE;
+  return QLORA_OK;
+}
+
+size_t qv_rmsnorm_ws(int64_t M, int64_t D) {
+  if (check_rms(M, D) || M == 0) return 0;
+  const int64_t g = (M + 3) / 4;
+  return (size_t)(g < 256 ? g : 256) * (size_t)D * 4;
+}
+
+int qv_rmsnorm_fwd(const void* X, const void* w, int64_t M, int64_t D, float eps, const void* Y, const float* rstd) {
+  int st = check_rms(M, D);
+  if (st) return st;
+  if (!isfinite(eps) || eps < 0.0f) return QLORA_ERR_INVALID_ARG;
+  if (M == 0) return QLORA_OK;
+  if ((st = check_ptr(X)) || (st = check_ptr(w)) || (st = check_ptr(Y)) || (st = check_ptr(rstd))) return st;
+  return QLORA_OK;
+}
+
+int qv_rmsnorm_bwd(const void* dY, const void* X, const void* w, const float* rstd, int64_t M, int64_t D,
+                   const void* dX, const float* dw, const void* ws, size_t ws_bytes) {
+  int st = check_rms(M, D);
+  if (st) return st;
+  if (dw && (st = check_ptr(dw))) return st;
+  if (M == 0) return QLORA_OK;
+  if ((st = check_ptr(dY)) || (st = check_ptr(X)) || (st = check_ptr(w)) || (st = check_ptr(rstd)) ||
+      (st = check_ptr(dX)))
+    return st;
+  return dw ? check_ws(ws, ws_bytes, qv_rmsnorm_ws(M, D)) : QLORA_OK;
+}
+
 int qv_merge(const qlora_linear* L, int32_t out_dtype, const void* out) {
   int st = check_linear(L);
   if (st) return st;

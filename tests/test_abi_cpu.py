@@ -175,3 +175,26 @@ def test_merge_rejections(lib):
     assert call(linear(alpha=float("nan"))) == INVALID
     assert call(linear(codes=FAKE + 8)) == MISALIGNED
     assert lib.qlora_merge(None, 0, FAKE, None) == INVALID
+
+
+def test_rmsnorm_rejections(lib):
+    fwd = lambda M=16, D=64, eps=1e-5, X=FAKE, w=FAKE, Y=FAKE, r=FAKE: lib.rmsnorm_fwd(X, w, M, D, eps, Y, r, None)
+    assert fwd(D=4) == SHAPE
+    assert fwd(D=12) == SHAPE
+    assert fwd(D=8200) == SHAPE
+    assert fwd(M=-1) == INVALID
+    assert fwd(eps=-1.0) == INVALID
+    assert fwd(eps=float("nan")) == INVALID
+    assert fwd(X=None) == INVALID
+    assert fwd(Y=FAKE + 2) == MISALIGNED
+    assert fwd(M=0, X=None, Y=None) == OK            # empty batch: nothing to check or launch
+    assert lib.rmsnorm_bwd_workspace_bytes(16, 64) == 4 * 64 * 4
+    assert lib.rmsnorm_bwd_workspace_bytes(10 ** 6, 64) == 256 * 64 * 4
+    assert lib.rmsnorm_bwd_workspace_bytes(16, 12) == 0
+    bwd = lambda M=16, D=64, dw=FAKE, ws=FAKE, wsb=1 << 20, dX=FAKE: lib.rmsnorm_bwd(
+        FAKE, FAKE, FAKE, FAKE, M, D, dX, dw, ws, wsb, None)
+    assert bwd(D=12) == SHAPE
+    assert bwd(dX=None) == INVALID
+    assert bwd(wsb=16) == WS_SMALL
+    assert bwd(ws=FAKE + 4) == MISALIGNED
+    assert bwd(dw=FAKE + 4) == MISALIGNED
