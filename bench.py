@@ -41,10 +41,10 @@ def parse():
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="first run one plain device-to-device copy of this many MiB (the known-size kernel "
                          "that calibrates the FETCH_SIZE / WRITE_SIZE counters)")
-    ap.add_argument("--only", default=None, metavar="IDX|merge|rmsnorm",
+    ap.add_argument("--only", default=None, metavar="IDX|merge|rmsnorm|qkv",
                     help="profiling aid: time only workload config IDX (0-4; the skinny linear with 4 rotated "
-                         "weight copies), the 16-bit merge or RMSNorm, and print its own JSON line instead of "
-                         "the metric line")
+                         "weight copies), the 16-bit merge, RMSNorm or the packed q/k/v adapters, and print its "
+                         "own JSON line instead of the metric line")
     ap.add_argument("--summarize-traffic", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_MIB"),
                     help="no GPU: turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, "
                          "WRITE_SIZE) of a --copy-probe-mib run into profiles/traffic_<kernel>.txt")
@@ -315,6 +315,60 @@ def merge_bench(q, synth, steps, warmup, copies=3):
                 weight_copies=copies)
 
 
+def grouped_bench(q, synth, steps, warmup, M=4096, K=4096, Ns=(4096, 1024, 1024), r=16, alpha=16.0):
+    """Packed q/k/v adapters of Llama-3-8B (K=4096; q 4096, k and v 1024 rows
+    each, r=16) at 4096 tokens, fwd+bwd through qlora_grouped_fwd/_bwd; the
+    same work as three separate linear calls is timed beside it for context."""
+    import torch
+    cb = torch.from_numpy(synth.nf4_codebook()).cuda()
+    Nt, G = sum(Ns), len(Ns)
+    Wd = torch.from_numpy(synth.weight_rows(7, 2, K, 0, Nt)).cuda()
+    w = q.nf4_quantize(Wd, cb)
+    bound = 1.0 / K ** 0.5
+    A = dev_bf16(synth.uniform_bf16(7, 3, G * r * K, -bound, bound).reshape(G * r, K))
+    Bs = [dev_bf16(synth.normal_bf16(7, 10 + g, Ns[g] * r, 0.0, 0.01).reshape(Ns[g], r)) for g in range(G)]
+    X = dev_bf16(synth.normal_bf16(7, 4, M * K).reshape(M, K))
+    dY = dev_bf16(synth.normal_bf16(7, 5, M * Nt).reshape(M, Nt))
+    Q = q.QLoraGrouped(w, A, Bs, [alpha] * G)
+    ws = torch.empty(q.qlora_grouped_workspace_bytes(Q, M), dtype=torch.uint8, device="cuda")
+    # the separate layers: each group's rows quantized on their own (same codes)
+    Ls, off = [], 0
+    for g in range(G):
+        wg = q.nf4_quantize(Wd[off:off + Ns[g]].contiguous(), cb)
+        Ls.append(q.QLoraLinear(wg, A[g * r:(g + 1) * r].contiguous(), Bs[g], alpha))
+        off += Ns[g]
+    del Wd
+    dYs = [dY[:, sum(Ns[:g]):sum(Ns[:g + 1])].contiguous() for g in range(G)]
+    wss = [torch.empty(q.qlora_linear_workspace_bytes(L, M), dtype=torch.uint8, device="cuda") for L in Ls]
+
+    def grouped_step():
+        Y, XA = q.qlora_grouped_fwd(Q, X, ws=ws)
+        q.qlora_grouped_bwd(Q, dY, X, XA, ws=ws)
+
+    def separate_step():
+        for g in range(G):
+            Y, XA = q.qlora_linear_fwd(Ls[g], X, ws=wss[g])
+            q.qlora_linear_bwd(Ls[g], dYs[g], X, XA, ws=wss[g])
+
+    def timed(f):
+        for _ in range(warmup):
+            f()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            f()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    g_ms, s_ms = timed(grouped_step), timed(separate_step)
+    flops = sum(4 * M * n * K + 6 * M * r * (n + K) for n in Ns)
+    return dict(workload="grouped_qkv_llama3_8b_m%d_r%d" % (M, r), ms_per_step=g_ms,
+                tflops=flops / (g_ms * 1e-3) / 1e12, frac_bf16_peak=flops / (g_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                separate_layers_ms=s_ms)
+
+
 def rmsnorm_bench(q, synth, steps, warmup, M=8192, D=4096, eps=1e-5):
     """rmsnorm_fwd and rmsnorm_bwd (with dw) at the Llama-3-8B hidden size and
     the MLP workload's token count; HBM-bound.  Algorithmic bytes: forward
@@ -420,8 +474,9 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    if a.only in ("merge", "rmsnorm"):
-        s = (merge_bench if a.only == "merge" else rmsnorm_bench)(q, synth, max(10, a.steps), a.warmup)
+    if a.only in ("merge", "rmsnorm", "qkv"):
+        fn = {"merge": merge_bench, "rmsnorm": rmsnorm_bench, "qkv": grouped_bench}[a.only]
+        s = fn(q, synth, max(10, a.steps), a.warmup)
         print(json.dumps({k: (round(v, 4) if isinstance(v, float) else v) for k, v in s.items()}), flush=True)
         return
     if a.only is not None:
@@ -474,6 +529,9 @@ def main():
             sec.append({k: (round(v, 4) if isinstance(v, float) else v) for k, v in s.items()})
         log("secondary: merge")
         s = merge_bench(q, synth, max(10, a.steps), a.warmup)
+        sec.append({k: (round(v, 4) if isinstance(v, float) else v) for k, v in s.items()})
+        log("secondary: grouped q/k/v")
+        s = grouped_bench(q, synth, max(5, a.steps), a.warmup)
         sec.append({k: (round(v, 4) if isinstance(v, float) else v) for k, v in s.items()})
         log("secondary: rmsnorm")
         s = rmsnorm_bench(q, synth, max(20, a.steps), a.warmup)

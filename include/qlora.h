@@ -198,6 +198,47 @@ int nf4_dequantize(const qlora_nf4* w, int32_t out_dtype, void* out, void* strea
 int qlora_merge(const qlora_linear* L, int32_t out_dtype, void* out, void* stream);
 
 /*
+ * Several LoRA adapters over one input, packed into one layer ("Speed Up
+ * Fine-Tuning 2x with Unsloth", item 3 "Memory Management": multiple LoRA
+ * adapters packed into a single tensor; the q/k/v projections of attention
+ * are the typical group).  Group g (g < G <= 8) is the QLoRA linear
+ * Y_g = X W_g^T + s_g (X A_g^T) B_g^T with s_g = alpha[g] / r[g]; the groups
+ * share X [M, K] and are stored packed:
+ *
+ *   W0   the NF4 weight of the row-concatenation [W_0; W_1; ...] [N_total, K]
+ *        (N_total = sum N[g], a multiple of 64)
+ *   A    bf16 [r_total, K], the A_g stacked (r_total = sum r[g] <= 128)
+ *   B[g] bf16 [N[g], r[g]], one tensor per group
+ *
+ * Y, dY are [M, N_total] with group g in columns [sum_{h<g} N[h], +N[g]).
+ * XA_saved is [M, r_total] fp32 (X A^T of the stacked A); dA is [r_total, K]
+ * (the dA_g stacked); dB[g] is bf16 [N[g], r[g]].  Internally the groups run
+ * as one layer with a block-diagonal B whose blocks are s_g B_g (rounded to
+ * bf16) and s = 1, so each output is within the tolerance of the separate
+ * layers (exactly them when every s_g is a power of two).
+ */
+typedef struct qlora_grouped {
+  qlora_nf4 W0;
+  const void* A;
+  const void* B[8];
+  int32_t N[8];
+  int32_t r[8];
+  float alpha[8];
+  int32_t G;
+} qlora_grouped;
+
+size_t qlora_grouped_workspace_bytes(const qlora_grouped* Q, int64_t M);
+
+/* qlora_grouped_fwd / _bwd: as qlora_linear_fwd / _bwd for the packed groups
+ * (arguments as in the comment above; same errors, plus
+ * QLORA_ERR_UNSUPPORTED_SHAPE for G outside [1, 8], an N[g] < 1, a sum of N
+ * other than W0.N, or r_total outside [1, 128]). */
+int qlora_grouped_fwd(const qlora_grouped* Q, const void* X, int64_t M, void* Y, float* XA_saved, void* ws,
+                      size_t ws_bytes, void* stream);
+int qlora_grouped_bwd(const qlora_grouped* Q, const void* dY, const void* X, const float* XA_saved, int64_t M,
+                      void* dX, void* dA, void* const* dB, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * rmsnorm_fwd: the RMSNorm in front of the MLP block ("LLM Fine-Tuning in
  * 2026", the fused RMSNorm of section 2: the forward keeps one inverse RMS per
  * row for the backward and no full-size intermediate).  Per row m of X:

@@ -28,6 +28,7 @@ EXPORTED = (
     "qlora_linear_workspace_bytes", "qlora_linear_fwd", "qlora_linear_bwd",
     "qlora_mlp_workspace_bytes", "qlora_mlp_fwd", "qlora_mlp_bwd", "qlora_trace_install", "qlora_merge",
     "rmsnorm_fwd", "rmsnorm_bwd", "rmsnorm_bwd_workspace_bytes",
+    "qlora_grouped_workspace_bytes", "qlora_grouped_fwd", "qlora_grouped_bwd",
 )
 
 
@@ -49,6 +50,11 @@ class CNf4(ctypes.Structure):
 class CLinear(ctypes.Structure):
     _fields_ = [("W0", CNf4), ("A", ctypes.c_void_p), ("B", ctypes.c_void_p),
                 ("r", ctypes.c_int32), ("alpha", ctypes.c_float)]
+
+
+class CGrouped(ctypes.Structure):
+    _fields_ = [("W0", CNf4), ("A", ctypes.c_void_p), ("B", ctypes.c_void_p * 8), ("N", ctypes.c_int32 * 8),
+                ("r", ctypes.c_int32 * 8), ("alpha", ctypes.c_float * 8), ("G", ctypes.c_int32)]
 
 
 class CMlp(ctypes.Structure):
@@ -96,6 +102,9 @@ def load_library(path: str = LIB_PATH):
         "rmsnorm_fwd": (ctypes.c_int, [vp, vp, i64, i64, ctypes.c_float, vp, vp, vp]),
         "rmsnorm_bwd": (ctypes.c_int, [vp, vp, vp, vp, i64, i64, vp, vp, vp, sz, vp]),
         "rmsnorm_bwd_workspace_bytes": (sz, [i64, i64]),
+        "qlora_grouped_workspace_bytes": (sz, [P(CGrouped), i64]),
+        "qlora_grouped_fwd": (ctypes.c_int, [P(CGrouped), vp, i64, vp, vp, vp, sz, vp]),
+        "qlora_grouped_bwd": (ctypes.c_int, [P(CGrouped), vp, vp, vp, i64, vp, vp, P(vp), vp, sz, vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -235,6 +244,71 @@ def qlora_linear_bwd(L: QLoraLinear, dY: torch.Tensor, X: torch.Tensor, XA: torc
                               dA.data_ptr(), dB.data_ptr(), ws.data_ptr(), ws.numel(), _stream(dev))
     _check("qlora_linear_bwd", st)
     return dX, dA, dB
+
+
+@dataclass
+class QLoraGrouped:
+    """Several adapters over one input, packed: W0 the NF4 weight of the stacked
+    rows [W_0; W_1; ...], A the stacked A_g [r_total, K], Bs one B_g [N_g, r_g]
+    per group, alphas one alpha per group."""
+    W0: Nf4Weight
+    A: torch.Tensor
+    Bs: list
+    alphas: list
+
+    @property
+    def rs(self):
+        return [int(B.shape[1]) for B in self.Bs]
+
+    @property
+    def Ns(self):
+        return [int(B.shape[0]) for B in self.Bs]
+
+    def c(self) -> CGrouped:
+        q = CGrouped()
+        q.W0 = self.W0.c()
+        q.A = self.A.data_ptr()
+        q.G = len(self.Bs)
+        for g, B in enumerate(self.Bs):
+            q.B[g] = B.data_ptr()
+            q.N[g] = int(B.shape[0])
+            q.r[g] = int(B.shape[1])
+            q.alpha[g] = float(self.alphas[g])
+        return q
+
+
+def qlora_grouped_workspace_bytes(Q: QLoraGrouped, M: int) -> int:
+    cq = Q.c()
+    return int(load_library().qlora_grouped_workspace_bytes(ctypes.byref(cq), M))
+
+
+def qlora_grouped_fwd(Q: QLoraGrouped, X: torch.Tensor, Y=None, XA=None, ws=None):
+    """qlora_grouped_fwd: returns (Y bf16 [M, N_total], XA fp32 [M, r_total])."""
+    lib = load_library()
+    M, dev = X.shape[0], X.device
+    Y = torch.empty(M, Q.W0.N, dtype=torch.bfloat16, device=dev) if Y is None else Y
+    XA = torch.empty(M, sum(Q.rs), dtype=torch.float32, device=dev) if XA is None else XA
+    ws = _workspace(qlora_grouped_workspace_bytes(Q, M), dev) if ws is None else ws
+    cq = Q.c()
+    _check("qlora_grouped_fwd", lib.qlora_grouped_fwd(ctypes.byref(cq), X.data_ptr(), M, Y.data_ptr(),
+                                                      XA.data_ptr(), ws.data_ptr(), ws.numel(), _stream(dev)))
+    return Y, XA
+
+
+def qlora_grouped_bwd(Q: QLoraGrouped, dY: torch.Tensor, X: torch.Tensor, XA: torch.Tensor, ws=None):
+    """qlora_grouped_bwd: returns (dX bf16 [M, K], dA bf16 [r_total, K], [dB_g bf16 [N_g, r_g]])."""
+    lib = load_library()
+    M, dev = X.shape[0], X.device
+    dX = torch.empty(M, Q.W0.K, dtype=torch.bfloat16, device=dev)
+    dA = torch.empty_like(Q.A)
+    dBs = [torch.empty_like(B) for B in Q.Bs]
+    ptrs = (ctypes.c_void_p * 8)(*[b.data_ptr() for b in dBs])
+    ws = _workspace(qlora_grouped_workspace_bytes(Q, M), dev) if ws is None else ws
+    cq = Q.c()
+    _check("qlora_grouped_bwd", lib.qlora_grouped_bwd(ctypes.byref(cq), dY.data_ptr(), X.data_ptr(), XA.data_ptr(),
+                                                      M, dX.data_ptr(), dA.data_ptr(), ptrs, ws.data_ptr(),
+                                                      ws.numel(), _stream(dev)))
+    return dX, dA, dBs
 
 
 def rmsnorm_fwd(X: torch.Tensor, w: torch.Tensor, eps: float, Y: Optional[torch.Tensor] = None,

@@ -171,6 +171,79 @@ int nf4_dequantize(const qlora_nf4* w, int32_t out_dtype, void* out, void* strea
                                           static_cast<hipStream_t>(stream)));
 }
 
+// ------------------------------------------------------------------ groups
+// The packed groups as one layer: W0 and the stacked A as given, B the
+// block-diagonal of bf16(s_g B_g) held in the workspace, s = 1.
+static qlora_linear grouped_layer(const qlora_grouped* Q, GroupDesc* d) {
+  memset(d, 0, sizeof(*d));
+  d->G = Q->G;
+  for (int g = 0; g < Q->G; ++g) {
+    d->B[g] = static_cast<const uint16_t*>(Q->B[g]);
+    d->noff[g + 1] = d->noff[g] + Q->N[g];
+    d->roff[g + 1] = d->roff[g] + Q->r[g];
+    d->s[g] = Q->alpha[g] / (float)Q->r[g];
+  }
+  qlora_linear L;
+  memset(&L, 0, sizeof(L));
+  L.W0 = Q->W0;
+  L.A = Q->A;
+  L.B = nullptr;  // set to the block-diagonal copy
+  L.r = d->roff[Q->G];
+  L.alpha = (float)L.r;  // s = alpha / r = 1
+  return L;
+}
+
+static size_t grouped_bcat_bytes(const qlora_grouped* Q, int r) {
+  return qplan::align256((size_t)Q->W0.N * (size_t)r * 2);
+}
+
+size_t qlora_grouped_workspace_bytes(const qlora_grouped* Q, int64_t M) {
+  if (qv_grouped(Q)) return 0;
+  GroupDesc d;
+  qlora_linear L = grouped_layer(Q, &d);
+  L.B = L.A;  // any non-null pointer: only the shapes matter for sizing
+  return 2 * grouped_bcat_bytes(Q, L.r) + qlora_linear_workspace_bytes(&L, M);
+}
+
+int qlora_grouped_fwd(const qlora_grouped* Q, const void* X, int64_t M, void* Y, float* XA_saved, void* ws,
+                      size_t ws_bytes, void* stream) {
+  QTRY(qv_grouped(Q));
+  GroupDesc d;
+  qlora_linear L = grouped_layer(Q, &d);
+  const size_t bc = grouped_bcat_bytes(Q, L.r);
+  if (M > 0 && ws_bytes < 2 * bc) return QLORA_ERR_WORKSPACE_TOO_SMALL;
+  L.B = M > 0 ? ws : Q->A;  // where the block-diagonal B goes; validated with the rest first
+  QTRY(qv_linear_fwd(&L, X, M, Y, XA_saved, M > 0 ? bytes(ws) + 2 * bc : ws, M > 0 ? ws_bytes - 2 * bc : 0));
+  if (M == 0) return QLORA_OK;
+  QTRY(check_device());
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  uint16_t* bcat = reinterpret_cast<uint16_t*>(bytes(ws));
+  QHIP(launch_grouped_bcat(d, (int)Q->W0.N, L.r, bcat, st));
+  L.B = bcat;
+  return qlora_linear_fwd(&L, X, M, Y, XA_saved, bytes(ws) + 2 * bc, ws_bytes - 2 * bc, stream);
+}
+
+int qlora_grouped_bwd(const qlora_grouped* Q, const void* dY, const void* X, const float* XA_saved, int64_t M,
+                      void* dX, void* dA, void* const* dB, void* ws, size_t ws_bytes, void* stream) {
+  QTRY(qv_grouped(Q));
+  QTRY(qv_grouped_dB(Q, dB));
+  GroupDesc d;
+  qlora_linear L = grouped_layer(Q, &d);
+  for (int g = 0; g < Q->G; ++g) d.dB[g] = static_cast<uint16_t*>(dB[g]);
+  const size_t bc = grouped_bcat_bytes(Q, L.r);
+  if (ws_bytes < 2 * bc) return QLORA_ERR_WORKSPACE_TOO_SMALL;
+  L.B = ws;  // where the block-diagonal B goes; validated with the rest first
+  QTRY(qv_linear_bwd(&L, dY, X, XA_saved, M, dX, dA, bytes(ws) + bc, bytes(ws) + 2 * bc, ws_bytes - 2 * bc));
+  QTRY(check_device());
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  uint16_t* bcat = reinterpret_cast<uint16_t*>(bytes(ws));
+  uint16_t* dbcat = reinterpret_cast<uint16_t*>(bytes(ws) + bc);
+  QHIP(launch_grouped_bcat(d, (int)Q->W0.N, L.r, bcat, st));
+  L.B = bcat;
+  QTRY(qlora_linear_bwd(&L, dY, X, XA_saved, M, dX, dA, dbcat, bytes(ws) + 2 * bc, ws_bytes - 2 * bc, stream));
+  return hip_status(launch_grouped_db(d, (int)Q->W0.N, L.r, dbcat, st));
+}
+
 int rmsnorm_fwd(const void* X, const void* w, int64_t M, int64_t D, float eps, void* Y, float* rstd,
                 void* stream) {
   QTRY(qv_rmsnorm_fwd(X, w, M, D, eps, Y, rstd));

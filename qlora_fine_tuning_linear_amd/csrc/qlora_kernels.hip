@@ -595,6 +595,39 @@ __global__ __launch_bounds__(256) void transpose_rn_kernel(const uint16_t* __res
   BT[i] = B[n * r + j];
 }
 
+// Packed LoRA groups run as one layer whose B is block-diagonal: element
+// (n, j) of the [Nt, Rt] matrix belongs to the group whose row range holds n.
+__device__ __forceinline__ int group_of(const GroupDesc& d, int n) {
+  int g = 0;
+  while (g < d.G - 1 && n >= d.noff[g + 1]) ++g;
+  return g;
+}
+
+__global__ __launch_bounds__(256) void grouped_bcat_kernel(GroupDesc d, int Nt, int Rt, uint16_t* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)Nt * Rt) return;
+  const int n = (int)(i / Rt), j = (int)(i % Rt);
+  const int g = group_of(d, n);
+  float v = 0.0f;
+  if (j >= d.roff[g] && j < d.roff[g + 1]) {
+    const int rg = d.roff[g + 1] - d.roff[g];
+    v = bf16_to_f32(d.B[g][(int64_t)(n - d.noff[g]) * rg + (j - d.roff[g])]) * d.s[g];
+  }
+  out[i] = (uint16_t)(pack_bf16x2(v, 0.0f) & 0xFFFFu);
+}
+
+__global__ __launch_bounds__(256) void grouped_db_kernel(GroupDesc d, int Nt, int Rt,
+                                                         const uint16_t* __restrict__ dbcat) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)Nt * Rt) return;
+  const int n = (int)(i / Rt), j = (int)(i % Rt);
+  const int g = group_of(d, n);
+  if (j < d.roff[g] || j >= d.roff[g + 1]) return;
+  const int rg = d.roff[g + 1] - d.roff[g];
+  const float v = bf16_to_f32(dbcat[i]) * d.s[g];
+  d.dB[g][(int64_t)(n - d.noff[g]) * rg + (j - d.roff[g])] = (uint16_t)(pack_bf16x2(v, 0.0f) & 0xFFFFu);
+}
+
 // Up to six transposes in one launch: job k turns src[k] [rows, cols] into
 // dst[k] [cols, rows]; the elements of all jobs are numbered one after the
 // other, job k owning [end[k-1], end[k]).
@@ -884,6 +917,20 @@ hipError_t launch_lora_down(const uint16_t* Z, int64_t M, int64_t Kred, const ui
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || S == 1 || !finish) return e;
   down_finish_kernel<<<grid1(M * (r0 + r1), 256), 256, 0, st>>>(part, S, M, r0, r1, V0, V1);
+  return hipGetLastError();
+}
+
+hipError_t launch_grouped_bcat(const GroupDesc& d, int Nt, int Rt, uint16_t* out, hipStream_t st) {
+  const int64_t n = (int64_t)Nt * Rt;
+  if (n == 0) return hipSuccess;
+  grouped_bcat_kernel<<<grid1(n, 256), 256, 0, st>>>(d, Nt, Rt, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_grouped_db(const GroupDesc& d, int Nt, int Rt, const uint16_t* dbcat, hipStream_t st) {
+  const int64_t n = (int64_t)Nt * Rt;
+  if (n == 0) return hipSuccess;
+  grouped_db_kernel<<<grid1(n, 256), 256, 0, st>>>(d, Nt, Rt, dbcat);
   return hipGetLastError();
 }
 

@@ -114,6 +114,19 @@ hipError_t launch_nf4_quantize(const float* W, int64_t nblocks, const float* cod
 // out [N, K] 16-bit = round16(deq(w) + s B A) (f16: fp16, else bf16).
 hipError_t launch_merge(const Nf4Dev& w, const float* codebook, const uint16_t* A, const uint16_t* B, int r,
                         float s, int f16, uint16_t* out, hipStream_t st);
+// Packed LoRA groups: row ranges noff[g] .. noff[g+1] of the packed weight and
+// rank columns roff[g] .. roff[g+1] belong to group g.
+struct GroupDesc {
+  const uint16_t* B[8];
+  uint16_t* dB[8];
+  int32_t noff[9], roff[9];
+  float s[8];
+  int32_t G;
+};
+// out [Nt, Rt] bf16 = block-diagonal of the bf16(s_g B_g)
+hipError_t launch_grouped_bcat(const GroupDesc& d, int Nt, int Rt, uint16_t* out, hipStream_t st);
+// dB_g = bf16(s_g * diagonal block g of dbcat [Nt, Rt])
+hipError_t launch_grouped_db(const GroupDesc& d, int Nt, int Rt, const uint16_t* dbcat, hipStream_t st);
 // RMSNorm: Y = X rstd w (rstd saved per row) and its backward; D % 8 == 0,
 // D <= 8192.  The backward with dw needs part fp32 [rmsnorm_bwd_groups(M)][D].
 int rmsnorm_bwd_groups(int64_t M);

@@ -76,6 +76,35 @@ int qv_dequantize(const qlora_nf4* w, int32_t out_dtype, const void* out) {
   return check_ptr(out);
 }
 
+int qv_grouped(const qlora_grouped* Q) {
+  if (!Q) return QLORA_ERR_INVALID_ARG;
+  int st = check_nf4(&Q->W0);
+  if (st) return st;
+  if (Q->G < 1 || Q->G > 8) return QLORA_ERR_UNSUPPORTED_SHAPE;
+  if (!Q->A) return QLORA_ERR_INVALID_ARG;
+  if (!aligned16(Q->A)) return QLORA_ERR_MISALIGNED;
+  int64_t nsum = 0, rsum = 0;
+  for (int g = 0; g < Q->G; ++g) {
+    if (!Q->B[g]) return QLORA_ERR_INVALID_ARG;
+    if (!aligned16(Q->B[g])) return QLORA_ERR_MISALIGNED;
+    if (!isfinite(Q->alpha[g])) return QLORA_ERR_INVALID_ARG;
+    if (Q->N[g] < 1 || Q->r[g] < 1) return QLORA_ERR_UNSUPPORTED_SHAPE;
+    nsum += Q->N[g];
+    rsum += Q->r[g];
+  }
+  if (nsum != Q->W0.N || rsum > 128) return QLORA_ERR_UNSUPPORTED_SHAPE;
+  return QLORA_OK;
+}
+
+int qv_grouped_dB(const qlora_grouped* Q, void* const* dB) {
+  if (!dB) return QLORA_ERR_INVALID_ARG;
+  for (int g = 0; g < Q->G; ++g) {
+    const int st = check_ptr(dB[g]);
+    if (st) return st;
+  }
+  return QLORA_OK;
+}
+
 static int check_rms(int64_t M, int64_t D) {
   if (M < 0) return QLORA_ERR_INVALID_ARG;
   if (D < 8 || D > 8192 || D % 8 != 0) return QLORA_ERR_UNSUPPORTED_SHAPE;

@@ -9,6 +9,8 @@
 int qv_quantize(const float* W, int64_t N, int64_t K, const float* codebook16, int32_t blocksize, int32_t dq_group,
                 const uint8_t* codes, const float* absmax, const uint8_t* absmax_q, const float* absmax_scale);
 int qv_dequantize(const qlora_nf4* w, int32_t out_dtype, const void* out);
+int qv_grouped(const qlora_grouped* Q);
+int qv_grouped_dB(const qlora_grouped* Q, void* const* dB);
 size_t qv_rmsnorm_ws(int64_t M, int64_t D);
 int qv_rmsnorm_fwd(const void* X, const void* w, int64_t M, int64_t D, float eps, const void* Y, const float* rstd);
 int qv_rmsnorm_bwd(const void* dY, const void* X, const void* w, const float* rstd, int64_t M, int64_t D,

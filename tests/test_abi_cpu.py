@@ -198,3 +198,34 @@ def test_rmsnorm_rejections(lib):
     assert bwd(wsb=16) == WS_SMALL
     assert bwd(ws=FAKE + 4) == MISALIGNED
     assert bwd(dw=FAKE + 4) == MISALIGNED
+
+
+def grouped(Ns=(64, 64), rs=(8, 8), N=None, K=128, G=None):
+    Q = q.CGrouped()
+    Q.W0 = nf4(sum(Ns) if N is None else N, K)
+    Q.A = FAKE
+    Q.G = len(Ns) if G is None else G
+    for g, (n, r) in enumerate(zip(Ns, rs)):
+        Q.B[g], Q.N[g], Q.r[g], Q.alpha[g] = FAKE, n, r, 16.0
+    return Q
+
+
+def test_grouped_rejections(lib):
+    fwd = lambda Q, M=16: lib.qlora_grouped_fwd(ctypes.byref(Q), FAKE, M, FAKE, FAKE, FAKE, 1 << 30, None)
+    assert fwd(grouped(G=0)) == SHAPE
+    assert fwd(grouped(G=9)) == SHAPE
+    assert fwd(grouped(N=192)) == SHAPE                     # sum of N != W0.N
+    assert fwd(grouped(rs=(100, 29))) == SHAPE              # r_total > 128
+    Q = grouped()
+    Q.B[1] = None
+    assert fwd(Q) == INVALID
+    Q = grouped()
+    Q.B[0] = FAKE + 2
+    assert fwd(Q) == MISALIGNED
+    assert fwd(grouped(), M=-1) == INVALID
+    assert lib.qlora_grouped_fwd(ctypes.byref(grouped()), FAKE, 16, FAKE, FAKE, FAKE, 16, None) == WS_SMALL
+    dB = (ctypes.c_void_p * 8)(FAKE, None)
+    assert lib.qlora_grouped_bwd(ctypes.byref(grouped()), FAKE, FAKE, FAKE, 16, FAKE, FAKE, dB, FAKE, 1 << 30,
+                                 None) == INVALID
+    assert lib.qlora_grouped_workspace_bytes(ctypes.byref(grouped()), 64) > 0
+    assert lib.qlora_grouped_workspace_bytes(ctypes.byref(grouped(G=0)), 64) == 0
