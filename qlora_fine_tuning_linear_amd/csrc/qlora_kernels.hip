@@ -5,23 +5,33 @@
 // Liger-Kernel", section 1), with forward and backward written by hand
 // (section 2 of that page) and the SwiGLU activation recomputed in the
 // backward pass ("What is Unsloth", "Recompute instead of store").  The
-// kernel design below is this library's own, for CDNA4:
+// kernel design is this library's own, for CDNA4.  The GEMMs are split by
+// token count M over three files:
 //
-// * qgemm_kernel - the hot path.  A dequant-staged bf16 MFMA GEMM
-//   (v_mfma_f32_32x32x16_bf16, fp32 accumulation).  Per 64-wide reduction
-//   tile, all threads of the workgroup expand the NF4 codes of the weight
-//   tile (codebook lookup in LDS, times the block absmax, round to bf16) and
-//   write them into a double-buffered LDS tile; for the backward pass the
-//   tile is written transposed so that both passes read it the same way.
-//   Activations (X or dY) go from HBM straight into registers in MFMA operand
-//   layout.  The LoRA term is one more MFMA step on the same accumulators in
-//   the epilogue; SwiGLU (forward) and its analytic backward are epilogue
-//   variants, so G, U, H and dG, dU are produced without another pass.
+//   M <= 64      qlora_skinny.hip: codes expanded straight into MFMA operand
+//                registers (weight-streaming forward, split transposed
+//                product + finish for the backward);
+//   64 < M < 512 this file, qgemm_kernel: a dequant-staged bf16 MFMA GEMM
+//                (v_mfma_f32_32x32x16_bf16, fp32 accumulation).  Per 64-wide
+//                reduction tile all threads expand the NF4 codes of the
+//                weight tile (codebook lookup in LDS, times the block absmax,
+//                round to bf16) into a double-buffered LDS tile, written
+//                transposed for the backward so both passes read it alike;
+//                activations are staged through LDS (256 x 256 tiles) or
+//                loaded straight in MFMA layout (64-wide tiles);
+//   M >= 512     qlora_bgemm.hip: the weight expanded once per call into a
+//                bf16 workspace, then a bf16 GEMM with direct-to-LDS loads.
+//
+// All GEMMs share the fused epilogue (qlora_gemm_common.h): the LoRA term as
+// extra MFMA steps on the accumulators, and the SwiGLU forward / analytic
+// backward variants, so G, U, H and dG, dU need no extra pass.  Also here:
+//
 // * lora_down_kernel - V = Z A^T (and T = dY B), the skinny rank-r products.
 // * lora_grad_kernel - dB = s dY^T XA and dA = s T^T X: reductions over the
 //   tokens, with the token-major operand transposed in registers and fed to
 //   the matrix cores; fixed-order partial sums, so results are reproducible.
 // * nf4_quantize_kernel / nf4_dequantize_kernel - the bit-exact encoding.
+// * transpose and packed-adapter helpers of the backward.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
