@@ -23,16 +23,20 @@
 namespace qk {
 
 // ------------------------------------------------------------------------
-// bgemm_kernel: output tile 256 tokens x 256 weight rows, 4 waves (one per
-// SIMD) in a 2 x 2 grid, each 128 x 128 = 4 x 4 frags of 32x32, fp32
-// accumulators.  Reduction tiles of 64 columns.
+// bgemm_kernel: output tile 256 tokens x 256 weight rows, 8 waves (two per
+// SIMD) in a 2 x 4 grid, each 128 tokens x 64 weight rows = 4 x 2 frags of
+// 32x32, fp32 accumulators.  Reduction tiles of 64 columns.  Two waves per
+// SIMD let one wave's matrix instructions run while the other waits for its
+// operands or at the barrier (measured against one 128 x 128 wave per SIMD:
+// 3-9% less time per GEMM; the chip runs at a lower clock under the denser
+// matrix work, so the gain in cycles is larger than the gain in time).
 //
 // Operands move global -> LDS by direct loads (buffer loads with the lds
 // flag, 16 bytes per lane, no registers, no LDS write instructions; a fixed
 // 32-bit lane offset, the tile's column offset in the scalar offset).  Each
 // direct load fills 1 KB of LDS with 8 rows x 128 bytes, i.e. whole cache
 // lines; a tile operand ([256][64] bf16, chunk c of row r stored at
-// c ^ swz(r)) is 32 KB, 8 direct loads per wave.  The two operands of tile kt
+// c ^ swz(r)) is 32 KB, 4 direct loads per wave.  The two operands of tile kt
 // ("halves" 2kt and 2kt+1: the first half is the weight when the weight is
 // the larger matrix, else the activations) rotate through five 32 KB buffers
 // (all 160 KB of LDS; each buffer its own __shared__ object, so the
@@ -53,7 +57,8 @@ namespace qk {
 // (second half of kt+2, first half of kt+3) and tile kt+1's first operands
 // are read.
 // ------------------------------------------------------------------------
-constexpr int BG_WN = 2, BG_FM = 4, BG_FN = 4;  // 2 x 2 waves
+constexpr int BG_WN = 4, BG_FM = 4, BG_FN = 2;  // 2 x 4 waves
+constexpr int BG_LPH = 4;                        // direct loads per wave per operand half
 constexpr int BG_BM = 256, BG_BN = 256;
 constexpr int BG_HE = 256 * 64;  // elements per half (one operand of one tile)
 
@@ -75,35 +80,34 @@ __device__ __forceinline__ void bg_tile(int64_t bid, int64_t tiles_m, int64_t ti
   tn = in / gs;
 }
 
-// Epilogue through LDS.  After the reduction each wave owns one 32 KB LDS
-// buffer.  Its 128 x 128 results are written there in accumulator layout and
-// read back as 16-byte row chunks, so that every global load and store of
-// the epilogue covers whole row segments (16 lanes per 256-byte row),
-// instead of 8-byte pieces of 32 different rows per instruction.  Chunk c of
-// row r sits at c ^ (r mod #chunks), which keeps both the writes and the
-// row-chunk reads free of bank conflicts.
+// Epilogue through LDS.  After the reduction each wave owns 128 tokens x 64
+// weight rows (2 frags of 32) and a 16 KB LDS region.  Its results are
+// written there in accumulator layout and read back as 16-byte row chunks,
+// so that every global load and store of the epilogue covers whole row
+// segments instead of 8-byte pieces of 32 different rows per instruction.
+// Chunk c of row r sits at c ^ (r mod #chunks), which keeps both the writes
+// and the row-chunk reads free of bank conflicts.
 template <int MODE>
-__device__ __forceinline__ void bg_epilogue(const GemmArgs& p, f32x16 (&acc)[BG_FM][BG_FN], int64_t m0, int64_t n0,
-                                            int wm, int wn, int lane, uint16_t* reg) {
-  constexpr int FM = BG_FM, FN = BG_FN;
+__device__ __forceinline__ void bg_epilogue(const GemmArgs& p, f32x16 (&acc)[BG_FM][2], int64_t m0, int64_t n0,
+                                             int wm, int wn, int lane, uint16_t* reg) {
+  constexpr int FM = BG_FM;
   const int l32 = lane & 31, g = lane >> 5;
   const int64_t mw = m0 + wm * 128;  // first token of the wave
   if constexpr (MODE == MODE_FWD_SWIGLU) {
-    // G = acc[.][0..1], U = acc[.][2..3]: 64 intermediate columns per wave
-    const int64_t cw = n0 + wn * 64;
+    // G = acc[.][0], U = acc[.][1]: 32 intermediate columns per wave
+    const int64_t cw = n0 + wn * 32;
     uint16_t* lg = reg;
-    uint16_t* lu = reg + 128 * 64;
-    auto wr = [&](uint16_t* t, int i, int f, int q, const float (&v)[4]) {
+    uint16_t* lu = reg + 128 * 32;
+    auto wr = [&](uint16_t* t, int i, int q, const float (&v)[4]) {
       const int row = i * 32 + l32;
-      const int c = 4 * f + q;
-      *reinterpret_cast<u32x2*>(t + row * 64 + ((c ^ (row & 7)) * 8) + 4 * g) =
+      *reinterpret_cast<u32x2*>(t + row * 32 + ((q ^ (row & 3)) * 8) + 4 * g) =
           u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
     };
     auto flush = [&](const uint16_t* t, uint16_t* out) {
 #pragma unroll
-      for (int it = 0; it < 16; ++it) {
-        const int row = it * 8 + (lane >> 3), c = lane & 7;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(t + row * 64 + ((c ^ (row & 7)) * 8));
+      for (int it = 0; it < 8; ++it) {
+        const int row = it * 16 + (lane >> 2), c = lane & 3;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(t + row * 32 + ((c ^ (row & 3)) * 8));
         const int64_t m = mw + row, n = cw + c * 8;
         if (m < p.M && n < p.Nout) *reinterpret_cast<u32x4*>(out + m * p.Nout + n) = v;
       }
@@ -111,45 +115,40 @@ __device__ __forceinline__ void bg_epilogue(const GemmArgs& p, f32x16 (&acc)[BG_
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int f = 0; f < 2; ++f)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float G[4] = {acc[i][f][4 * q], acc[i][f][4 * q + 1], acc[i][f][4 * q + 2], acc[i][f][4 * q + 3]};
-          const float U[4] = {acc[i][f + 2][4 * q], acc[i][f + 2][4 * q + 1], acc[i][f + 2][4 * q + 2],
-                              acc[i][f + 2][4 * q + 3]};
-          wr(lg, i, f, q, G);
-          wr(lu, i, f, q, U);
-        }
+      for (int q = 0; q < 4; ++q) {
+        const float G[4] = {acc[i][0][4 * q], acc[i][0][4 * q + 1], acc[i][0][4 * q + 2], acc[i][0][4 * q + 3]};
+        const float U[4] = {acc[i][1][4 * q], acc[i][1][4 * q + 1], acc[i][1][4 * q + 2], acc[i][1][4 * q + 3]};
+        wr(lg, i, q, G);
+        wr(lu, i, q, U);
+      }
     flush(lg, p.out0);
     flush(lu, p.out1);
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int f = 0; f < 2; ++f)
+      for (int q = 0; q < 4; ++q) {
+        float H[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          float H[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float Gv = acc[i][f][4 * q + e], Uv = acc[i][f + 2][4 * q + e];
-            H[e] = Gv * sigmoid_fast(Gv) * Uv;
-          }
-          wr(lg, i, f, q, H);
+        for (int e = 0; e < 4; ++e) {
+          const float Gv = acc[i][0][4 * q + e], Uv = acc[i][1][4 * q + e];
+          H[e] = Gv * sigmoid_fast(Gv) * Uv;
         }
+        wr(lg, i, q, H);
+      }
     flush(lg, p.out2);
   } else if constexpr (MODE == MODE_BWD_SWIGLU) {
-    // dH (fp32) one token frag (32 rows x 128 columns, 16 KB) at a time; the
+    // dH (fp32) one token frag (32 rows x 64 columns, 8 KB) at a time; the
     // G / U chunks of frag i+1 are loaded while frag i is finished
-    const int64_t cw = n0 + wn * 128;
-    const int c16 = lane & 15;  // this lane's 8-column group
-    const int64_t ncol = cw + 8 * c16;
+    const int64_t cw = n0 + wn * 64;
+    const int c8 = lane & 7;  // this lane's 8-column group
+    const int64_t ncol = cw + 8 * c8;
     const bool col_ok = ncol < p.Nout;
     const int64_t nc = col_ok ? ncol : p.Nout - 8;
-    u32x4 gg[2][8], uu[2][8];
+    u32x4 gg[2][4], uu[2][4];
     auto load = [&](int i, int b) {
 #pragma unroll
-      for (int it = 0; it < 8; ++it) {
-        int64_t m = mw + i * 32 + it * 4 + (lane >> 4);
+      for (int it = 0; it < 4; ++it) {
+        int64_t m = mw + i * 32 + it * 8 + (lane >> 3);
         if (m >= p.M) m = p.M - 1;
         gg[b][it] = *reinterpret_cast<const u32x4*>(p.in0 + m * p.Nout + nc);
         uu[b][it] = *reinterpret_cast<const u32x4*>(p.in1 + m * p.Nout + nc);
@@ -162,19 +161,19 @@ __device__ __forceinline__ void bg_epilogue(const GemmArgs& p, f32x16 (&acc)[BG_
       if (i + 1 < FM) load(i + 1, (i + 1) & 1);
       const int b = i & 1;
 #pragma unroll
-      for (int f = 0; f < FN; ++f)
+      for (int f = 0; f < 2; ++f)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int row = l32, c = 8 * f + 2 * q + g;  // 16-byte fp32 chunk of 32 per row
-          *reinterpret_cast<f32x4*>(lf + row * 128 + ((c ^ (row & 31)) * 4)) =
+          const int row = l32, c = 8 * f + 2 * q + g;  // 16-byte fp32 chunk of 16 per row
+          *reinterpret_cast<f32x4*>(lf + row * 64 + ((c ^ (row & 15)) * 4)) =
               f32x4{acc[i][f][4 * q], acc[i][f][4 * q + 1], acc[i][f][4 * q + 2], acc[i][f][4 * q + 3]};
         }
 #pragma unroll
-      for (int it = 0; it < 8; ++it) {
-        const int row = it * 4 + (lane >> 4);
-        const int c0 = 2 * c16;
-        const f32x4 d0 = *reinterpret_cast<const f32x4*>(lf + row * 128 + ((c0 ^ (row & 31)) * 4));
-        const f32x4 d1 = *reinterpret_cast<const f32x4*>(lf + row * 128 + (((c0 + 1) ^ (row & 31)) * 4));
+      for (int it = 0; it < 4; ++it) {
+        const int row = it * 8 + (lane >> 3);
+        const int c0 = 2 * c8;
+        const f32x4 d0 = *reinterpret_cast<const f32x4*>(lf + row * 64 + ((c0 ^ (row & 15)) * 4));
+        const f32x4 d1 = *reinterpret_cast<const f32x4*>(lf + row * 64 + (((c0 + 1) ^ (row & 15)) * 4));
         const float dH[8] = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
         u32x4 og, ou;
 #pragma unroll
@@ -200,23 +199,23 @@ __device__ __forceinline__ void bg_epilogue(const GemmArgs& p, f32x16 (&acc)[BG_
       }
     }
   } else {
-    // plain bf16 output: 128 tokens x 128 columns per wave, one pass
-    const int64_t cw = n0 + wn * 128;
+    // plain bf16 output: 128 tokens x 64 columns per wave, one pass
+    const int64_t cw = n0 + wn * 64;
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int f = 0; f < FN; ++f)
+      for (int f = 0; f < 2; ++f)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int row = i * 32 + l32, c = 4 * f + q;
-          *reinterpret_cast<u32x2*>(reg + row * 128 + ((c ^ (row & 15)) * 8) + 4 * g) =
+          *reinterpret_cast<u32x2*>(reg + row * 64 + ((c ^ (row & 7)) * 8) + 4 * g) =
               u32x2{pack_bf16x2(acc[i][f][4 * q], acc[i][f][4 * q + 1]),
                     pack_bf16x2(acc[i][f][4 * q + 2], acc[i][f][4 * q + 3])};
         }
 #pragma unroll
-    for (int it = 0; it < 32; ++it) {
-      const int row = it * 4 + (lane >> 4), c = lane & 15;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(reg + row * 128 + ((c ^ (row & 15)) * 8));
+    for (int it = 0; it < 16; ++it) {
+      const int row = it * 8 + (lane >> 3), c = lane & 7;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(reg + row * 64 + ((c ^ (row & 7)) * 8));
       const int64_t m = mw + row, n = cw + c * 8;
       if (m < p.M && n < p.Nout) *reinterpret_cast<u32x4*>(p.out0 + m * p.Nout + n) = v;
     }
@@ -224,8 +223,9 @@ __device__ __forceinline__ void bg_epilogue(const GemmArgs& p, f32x16 (&acc)[BG_
 }
 
 template <int MODE, bool WLEAD>
-__global__ __launch_bounds__(256) void bgemm_kernel(GemmArgs p) {
+__global__ __launch_bounds__(512) void bgemm_kernel(GemmArgs p) {
   constexpr int WN = BG_WN, FM = BG_FM, FN = BG_FN;
+  constexpr int LPH = BG_LPH;
   constexpr int BM = BG_BM, BN = BG_BN;
   constexpr int BNO = ModeTraits<MODE>::swiglu_fwd ? BN / 2 : BN;
 
@@ -251,10 +251,10 @@ __global__ __launch_bounds__(256) void bgemm_kernel(GemmArgs p) {
 
   // direct load i (0..7) of this wave: tile rows 8 (8 wave + i) + lane/8,
   // physical chunk lane%8 <- logical chunk (lane%8) ^ swz(row)
-  uint32_t aoff[8], boff[8];
+  uint32_t aoff[LPH], boff[LPH];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int row = 8 * (8 * wave + i) + (lane >> 3);
+  for (int i = 0; i < LPH; ++i) {
+    const int row = 8 * (LPH * wave + i) + (lane >> 3);
     const int c = (lane & 7) ^ swz(row);
     int64_t ra = m0 + row;
     if (ra >= p.M) ra = p.M - 1;
@@ -279,7 +279,7 @@ __global__ __launch_bounds__(256) void bgemm_kernel(GemmArgs p) {
   // 8 direct loads of one operand half of tile kt (clamped to the last tile:
   // the tail re-loads it into a free buffer, which keeps vmcnt uniform)
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < LPH; ++i) {
     aoff[i] *= 2;
     boff[i] *= 2;
   }
@@ -288,15 +288,15 @@ __global__ __launch_bounds__(256) void bgemm_kernel(GemmArgs p) {
     const bool second = kt >= KT0;
     const int so = (second ? kt - KT0 : kt) * 128;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(second ? ra1 : ra0, LDS_PTR(buf + (8 * wave + i) * 512), 16, aoff[i],
+    for (int i = 0; i < LPH; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(second ? ra1 : ra0, LDS_PTR(buf + (LPH * wave + i) * 512), 16, aoff[i],
                                                so, 0, 0);
   };
   auto load_b = [&](uint16_t* buf, int kt) {
     kt = kt < KT ? kt : KT - 1;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, LDS_PTR(buf + (8 * wave + i) * 512), 16, boff[i], kt * 128, 0, 0);
+    for (int i = 0; i < LPH; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, LDS_PTR(buf + (LPH * wave + i) * 512), 16, boff[i], kt * 128, 0, 0);
   };
 
   f32x16 acc[FM][FN];
@@ -355,11 +355,11 @@ __global__ __launch_bounds__(256) void bgemm_kernel(GemmArgs p) {
   };
   auto interleave_reads = [&]() {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < FM + FN; ++j) {
       SCHED_GROUP(SG_MFMA, 1);
       SCHED_GROUP(SG_DS_READ, 1);
     }
-    SCHED_GROUP(SG_MFMA, 8);
+    SCHED_GROUP(SG_MFMA, FM * FN - FM - FN);
     __builtin_amdgcn_sched_barrier(0);
   };
 
@@ -375,7 +375,7 @@ __global__ __launch_bounds__(256) void bgemm_kernel(GemmArgs p) {
     rd(ca, cb, 3, x1, w1);
     mm(x0, w0);
     interleave_reads();
-    wait_vmcnt<8>();  // tile kt+1 landed; the first half of kt+2 may be in flight
+    wait_vmcnt<LPH>();  // tile kt+1 landed; the first half of kt+2 may be in flight
     stage_barrier();
     __builtin_amdgcn_sched_barrier(0);
     load_second(ca, kt + 2);
@@ -383,12 +383,12 @@ __global__ __launch_bounds__(256) void bgemm_kernel(GemmArgs p) {
     rd(na, nb, 0, x0, w0);
     mm(x1, w1);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < FM + FN; ++j) {
       SCHED_GROUP(SG_MFMA, 1);
-      SCHED_GROUP(SG_VMEM_READ, 2);
+      if (j < LPH) SCHED_GROUP(SG_VMEM_READ, 2);
       SCHED_GROUP(SG_DS_READ, 1);
     }
-    SCHED_GROUP(SG_MFMA, 8);
+    SCHED_GROUP(SG_MFMA, FM * FN - FM - FN);
     __builtin_amdgcn_sched_barrier(0);
   };
 
@@ -429,7 +429,7 @@ __global__ __launch_bounds__(256) void bgemm_kernel(GemmArgs p) {
       for (int k = 0; k < ns; ++k)
         lora_scalar<MODE, WN, FM, FN>(p, *L[k], 0, acc, arow, n0, wn, l32, g, lo[k], hi[k]);
     }
-    wait_vmcnt<24>();  // tile 0 landed
+    wait_vmcnt<3 * LPH>();  // tile 0 landed
     stage_barrier();
     rd(hb0, hb1, 0, x0, w0);
     // half h of the sequence A0 B0 A1 B1 ... lives in buffer h % 5
@@ -449,8 +449,8 @@ __global__ __launch_bounds__(256) void bgemm_kernel(GemmArgs p) {
     wait_vmcnt<0>();  // no direct load may still target LDS past this point
   }
   stage_barrier();  // every wave is done reading operands: LDS is free
-  uint16_t* reg = wave == 0 ? hb0 : wave == 1 ? hb1 : wave == 2 ? hb2 : hb3;
-  bg_epilogue<MODE>(p, acc, m0, n0, wm, wn, lane, reg);
+  uint16_t* buf = wave < 2 ? hb0 : wave < 4 ? hb1 : wave < 6 ? hb2 : hb3;
+  bg_epilogue<MODE>(p, acc, m0, n0, wm, wn, lane, buf + (wave & 1) * 8192);
 }
 
 // ------------------------------------------------------------------------
@@ -558,9 +558,9 @@ static hipError_t run_bgemm(GemmArgs a, hipStream_t st) {
   const int64_t n = a.tiles_m * a.tiles_n;
   if (n == 0) return hipSuccess;
   if (a.wrows > a.M)
-    bgemm_kernel<MODE, true><<<dim3((unsigned)n), 256, 0, st>>>(a);
+    bgemm_kernel<MODE, true><<<dim3((unsigned)n), 512, 0, st>>>(a);
   else
-    bgemm_kernel<MODE, false><<<dim3((unsigned)n), 256, 0, st>>>(a);
+    bgemm_kernel<MODE, false><<<dim3((unsigned)n), 512, 0, st>>>(a);
   return hipGetLastError();
 }
 
