@@ -27,6 +27,10 @@ What it computes, and from where:
 * ``rmsnorm`` - the RMSNorm in front of the MLP block with one saved inverse
   RMS per row (the fused-RMSNorm part of section 2 of "LLM Fine-Tuning in
   2026"), forward and hand-derived backward, the definition in float64.
+* ``linear_ce`` - the output head's linear projection followed by the
+  cross-entropy loss, and the loss gradient with respect to the hidden states
+  (section 3 of "LLM Fine-Tuning in 2026", the fused cross-entropy), the
+  definition in float64.
 
 Pins (``tests/test_oracle_*.py``) tie every function to something other than
 itself: exact-rational brute force for the code search, codebook-exact blocks,
@@ -34,4 +38,4 @@ idempotence, error bounds, the B = 0 reduction to the plain base matmul, the
 pages' column-vector form of the update, the merged-weight form, and central
 finite differences of <Y, dY> for every gradient.
 """
-from . import nf4, qlora, rmsnorm  # noqa: F401
+from . import linear_ce, nf4, qlora, rmsnorm  # noqa: F401

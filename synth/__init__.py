@@ -86,6 +86,16 @@ def uniform_bf16(seed, stream, n, lo, hi, offset=0):
     return out
 
 
+def targets(seed, stream, n, V, ignore_every=0, ignore_index=-100):
+    """n class indices in [0, V) from the counter-based bits (bits mod V);
+    with ignore_every = k > 0, every k-th index (i % k == k - 1) is the
+    ignore value instead."""
+    out = np.empty(int(n), np.int32)
+    for i in range(int(n)):
+        out[i] = ignore_index if ignore_every and i % ignore_every == ignore_every - 1 else bits(seed, stream, i) % V
+    return out
+
+
 def bf16_to_f32(u16: np.ndarray) -> np.ndarray:
     """Exact widening of bf16 bit patterns to fp32."""
     return (np.asarray(u16, np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)

@@ -33,6 +33,14 @@ MUTATIONS = [
     ("rmsnorm.py", "rstd ** 3 / D", "rstd ** 2 / D"),
     ("rmsnorm.py", "dw = np.sum(dY * X * rstd[:, None], axis=0)", "dw = np.sum(dY * X, axis=0)"),
     ("rmsnorm.py", "ms = np.mean(X * X, axis=1)", "ms = np.sum(X * X, axis=1)"),
+    ("linear_ce.py", "lse = zmax + np.log(S)", "lse = np.log(S)"),
+    ("linear_ce.py", "G[np.arange(T), tgt] -= 1.0", "G[np.arange(T), tgt] += 1.0"),
+    ("linear_ce.py", "loss = float(token_loss.sum() / n) if n > 0 else 0.0",
+     "loss = float(token_loss.sum() / T) if n > 0 else 0.0"),
+    ("linear_ce.py", "dX = (G @ W) / n if n > 0 else np.zeros_like(X)",
+     "dX = (G @ W[::-1]) / n if n > 0 else np.zeros_like(X)"),
+    ("linear_ce.py", "G[~valid] = 0.0", "G[~valid] *= 1.0"),
+    ("linear_ce.py", "E = np.exp(Z - zmax[:, None])", "E = np.exp(Z - zmax[::-1, None])"),
     ("nf4.py", 'side="left"', 'side="right"'),
     ("nf4.py", "flat[0::2] | (flat[1::2] << np.uint8(4))", "flat[1::2] | (flat[0::2] << np.uint8(4))"),
     ("nf4.py", "np.minimum(np.rint(ratio), 255.0)", "np.minimum(np.floor(ratio), 255.0)"),
@@ -50,7 +58,8 @@ def sandbox(tmp_path_factory):
     shutil.copytree(os.path.join(ROOT, "synth"), d / "synth",
                     ignore=shutil.ignore_patterns("*.tmp*", "__pycache__"))
     os.makedirs(d / "tests" / "golden")
-    for f in ("conftest.py", "test_oracle_nf4.py", "test_oracle_qlora.py", "test_oracle_rmsnorm.py"):
+    for f in ("conftest.py", "test_oracle_nf4.py", "test_oracle_qlora.py", "test_oracle_rmsnorm.py",
+              "test_oracle_linear_ce.py"):
         shutil.copy(os.path.join(ROOT, "tests", f), d / "tests" / f)
     shutil.copy(os.path.join(ROOT, "tests", "golden", "nf4_codebook.txt"),
                 d / "tests" / "golden" / "nf4_codebook.txt")
@@ -67,6 +76,7 @@ def test_pins_catch_mutation(sandbox, fname, old, new):
     assert old in src
     (od / fname).write_text(src.replace(old, new))
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                        "tests/test_oracle_nf4.py", "tests/test_oracle_qlora.py", "tests/test_oracle_rmsnorm.py"],
+                        "tests/test_oracle_nf4.py", "tests/test_oracle_qlora.py", "tests/test_oracle_rmsnorm.py",
+                        "tests/test_oracle_linear_ce.py"],
                        cwd=str(sandbox), capture_output=True, text=True, timeout=300)
     assert r.returncode == 1, "mutation survived: %s\n%s" % (new, r.stdout[-2000:])
