@@ -276,6 +276,48 @@ int rmsnorm_bwd(const void* dY, const void* X, const void* w, const float* rstd,
                 void* dX, float* dw, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Workspace bytes qlora_linear_ce needs for T tokens, hidden size D, V classes
+ * and the given chunk (0 when the shape is not supported): one chunk of
+ * logits (min(chunk, T) * V bf16), T per-token fp32 losses and, with
+ * want_dx != 0, the head transposed (V * D bf16) plus the fp32 partials of
+ * the dX product.
+ */
+size_t qlora_linear_ce_workspace_bytes(int64_t T, int64_t D, int64_t V, int64_t chunk, int32_t want_dx);
+
+/*
+ * qlora_linear_ce: the output head's linear projection and the cross-entropy
+ * loss in one call ("LLM Fine-Tuning in 2026", section 3, the fused
+ * cross-entropy), token chunk by token chunk, so that no [T, V] logit matrix
+ * is held: the only [*, V] buffer is one chunk of logits in the workspace.
+ * With n the number of tokens whose target is a class index in [0, V) other
+ * than ignore_index (any other value marks a token without a target):
+ *
+ *   z_t   = W x_t                  V logits, fp32 accumulation, rounded to bf16
+ *   l_t   = logsumexp(z_t) - z_t[target_t]     (fp32; 0 without a target)
+ *   loss  = (1/n) sum_t l_t                     (fixed-order sum; 0 if n == 0)
+ *   dX_t  = sum_v g_tv W_v,  g_tv = bf16((softmax(z_t)_v - [v == target_t]) / n)
+ *           (fp32 accumulation, bf16 out; 0 rows without a target)
+ *
+ *   X          bf16 [T, D]  hidden states
+ *   W          bf16 [V, D]  frozen head, row v = class v
+ *   targets    int32 [T]    device
+ *   loss       fp32 [1]     output (device)
+ *   token_loss fp32 [T]     output l_t, or NULL
+ *   dX         bf16 [T, D]  output, or NULL for the loss alone
+ *   chunk      tokens per chunk, >= 1 (QLORA_ERR_INVALID_ARG otherwise)
+ *   ws         ws_bytes >= qlora_linear_ce_workspace_bytes(T, D, V, chunk,
+ *              dX != NULL); with dX the head is transposed into it once per
+ *              call (V * D * 2 bytes)
+ * D and V multiples of 64, D <= 65536, V <= 2^24
+ * (QLORA_ERR_UNSUPPORTED_SHAPE otherwise).  T == 0 writes loss = 0 and needs
+ * no workspace.  All pointers 16-byte aligned.  Results are bitwise
+ * reproducible from run to run.
+ */
+int qlora_linear_ce(const void* X, int64_t T, int64_t D, const void* W, int64_t V, const int32_t* targets,
+                    int32_t ignore_index, int64_t chunk, float* loss, float* token_loss, void* dX, void* ws,
+                    size_t ws_bytes, void* stream);
+
+/*
  * Workspace bytes the linear forward and backward need for M tokens.  From
  * M = 512 tokens on, the GEMMs expand the NF4 weight once per call into a
  * bf16 copy held in the workspace (N*K*2 bytes) instead of expanding it in

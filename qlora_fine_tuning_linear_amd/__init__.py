@@ -29,6 +29,7 @@ EXPORTED = (
     "qlora_mlp_workspace_bytes", "qlora_mlp_fwd", "qlora_mlp_bwd", "qlora_trace_install", "qlora_merge",
     "rmsnorm_fwd", "rmsnorm_bwd", "rmsnorm_bwd_workspace_bytes",
     "qlora_grouped_workspace_bytes", "qlora_grouped_fwd", "qlora_grouped_bwd",
+    "qlora_linear_ce_workspace_bytes", "qlora_linear_ce",
 )
 
 
@@ -105,6 +106,8 @@ def load_library(path: str = LIB_PATH):
         "qlora_grouped_workspace_bytes": (sz, [P(CGrouped), i64]),
         "qlora_grouped_fwd": (ctypes.c_int, [P(CGrouped), vp, i64, vp, vp, vp, sz, vp]),
         "qlora_grouped_bwd": (ctypes.c_int, [P(CGrouped), vp, vp, vp, i64, vp, vp, P(vp), vp, sz, vp]),
+        "qlora_linear_ce_workspace_bytes": (sz, [i64, i64, i64, i64, i32]),
+        "qlora_linear_ce": (ctypes.c_int, [vp, i64, i64, vp, i64, vp, i32, i64, vp, vp, vp, vp, sz, vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -339,6 +342,34 @@ def rmsnorm_bwd(dY: torch.Tensor, X: torch.Tensor, w: torch.Tensor, rstd: torch.
                                           _ptr(dw) if want_dw else None, _ptr(ws), ws.numel(),
                                           _stream(X.device)))
     return dX, (dw if want_dw else None)
+
+
+IGNORE_INDEX = -100
+
+
+def qlora_linear_ce_workspace_bytes(T: int, D: int, V: int, chunk: int, want_dx: bool = True) -> int:
+    return int(load_library().qlora_linear_ce_workspace_bytes(T, D, V, chunk, 1 if want_dx else 0))
+
+
+def qlora_linear_ce(X: torch.Tensor, W: torch.Tensor, targets: torch.Tensor, ignore_index: int = IGNORE_INDEX,
+                    chunk: int = 1024, want_dx: bool = True, want_token_loss: bool = False,
+                    dX: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None):
+    """qlora_linear_ce: returns (loss fp32 [1], token_loss fp32 [T] or None, dX bf16 [T, D] or None)."""
+    lib = load_library()
+    T, D = X.shape
+    V = W.shape[0]
+    loss = torch.empty(1, dtype=torch.float32, device=X.device)
+    tl = torch.empty(T, dtype=torch.float32, device=X.device) if want_token_loss else None
+    if want_dx and dX is None:
+        dX = torch.empty_like(X)
+    if ws is None:
+        nbytes = lib.qlora_linear_ce_workspace_bytes(T, D, V, chunk, 1 if want_dx else 0)
+        ws = torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=X.device)
+    _check("qlora_linear_ce", lib.qlora_linear_ce(_ptr(X), T, D, _ptr(W), V, _ptr(targets), int(ignore_index),
+                                                  int(chunk), _ptr(loss), _ptr(tl) if tl is not None else None,
+                                                  _ptr(dX) if want_dx else None, _ptr(ws), ws.numel(),
+                                                  _stream(X.device)))
+    return loss, tl, (dX if want_dx else None)
 
 
 def qlora_merge(L: QLoraLinear, dtype: torch.dtype = torch.bfloat16, out: Optional[torch.Tensor] = None):

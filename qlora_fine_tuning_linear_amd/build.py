@@ -30,6 +30,7 @@ def build(verbose: bool = False) -> str:
     os.makedirs(bdir, exist_ok=True)
     objs = []
     for src in ("qlora_kernels.hip", "qlora_bgemm.hip", "qlora_skinny.hip", "qlora_merge.hip", "qlora_rmsnorm.hip",
+                "qlora_ce.hip",
                 "qlora_api.hip"):
         obj = os.path.join(bdir, src + ".o")
         cmd = ["hipcc", "-c"] + HIP_FLAGS + [os.path.join(CSRC, src), "-o", obj]

@@ -263,6 +263,64 @@ int rmsnorm_bwd(const void* dY, const void* X, const void* w, const float* rstd,
                                        reinterpret_cast<float*>(ws), static_cast<hipStream_t>(stream)));
 }
 
+size_t qlora_linear_ce_workspace_bytes(int64_t T, int64_t D, int64_t V, int64_t chunk, int32_t want_dx) {
+  return qv_linear_ce_ws(T, D, V, chunk, want_dx);
+}
+
+int qlora_linear_ce(const void* X, int64_t T, int64_t D, const void* W, int64_t V, const int32_t* targets,
+                    int32_t ignore_index, int64_t chunk, float* loss, float* token_loss, void* dX, void* ws,
+                    size_t ws_bytes, void* stream) {
+  QTRY(qv_linear_ce(X, T, D, W, V, targets, chunk, loss, token_loss, dX, ws, ws_bytes));
+  QTRY(check_device());
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (T == 0) return hip_status(launch_ce_loss(nullptr, 0, nullptr, loss, st));
+  const bool want_dx = dX != nullptr;
+  const qplan::CeWs w = qplan::ce_ws(T, D, V, chunk, want_dx);
+  char* b = bytes(ws);
+  int32_t* nvalid = reinterpret_cast<int32_t*>(b);
+  float* tl = token_loss ? token_loss : reinterpret_cast<float*>(b + w.nvalid);
+  uint16_t* z = reinterpret_cast<uint16_t*>(b + w.nvalid + w.tloss);
+  uint16_t* wt = reinterpret_cast<uint16_t*>(b + w.nvalid + w.tloss + w.logits);
+  float* part = reinterpret_cast<float*>(b + w.nvalid + w.tloss + w.logits + w.wt);
+  QHIP(launch_ce_count(targets, T, V, ignore_index, nvalid, st));
+  // the head as [D, V] rows, so that the dX product reduces over contiguous rows
+  if (want_dx) QHIP(launch_transpose_bf16(u16(W), V, D, wt, st));
+  for (int64_t c0 = 0; c0 < T; c0 += w.C) {
+    const int64_t C = (T - c0) < w.C ? (T - c0) : w.C;
+    // logits of the chunk: z = X_c W^T, bf16 [C, V]
+    GemmArgs a = gemm_args();
+    a.act0 = u16(X) + c0 * D;
+    a.M = C;
+    a.Nout = V;
+    a.Kred0 = D;
+    a.wb = u16(W);
+    a.ldw = D;
+    a.wrows = V;
+    a.out0 = z;
+    QHIP(traced_gemm_b(MODE_FWD, a, st));
+    // loss terms; with dX wanted, z becomes (softmax - onehot) / n
+    QHIP(launch_ce_rows(z, C, V, targets + c0, ignore_index, nvalid, want_dx ? 1 : 0, tl + c0, st));
+    if (!want_dx) continue;
+    // dX_c = z W, the vocabulary reduction split into fp32 partials
+    GemmArgs g = gemm_args();
+    g.act0 = z;
+    g.M = C;
+    g.Nout = D;
+    g.Kred0 = V;
+    g.wb = wt;
+    g.ldw = V;
+    g.wrows = D;
+    g.out0 = u16m(dX) + c0 * D;
+    if (w.splits > 1) {
+      g.partial = part;
+      g.ktiles_per_split = w.kps;
+    }
+    QHIP(traced_gemm_b(MODE_FWD, g, st));
+    if (w.splits > 1) QHIP(launch_splitk_finish(part, w.splits, C, D, u16m(dX) + c0 * D, st));
+  }
+  return hip_status(launch_ce_loss(tl, T, nvalid, loss, st));
+}
+
 int qlora_merge(const qlora_linear* L, int32_t out_dtype, void* out, void* stream) {
   QTRY(qv_merge(L, out_dtype, out));
   QTRY(check_device());

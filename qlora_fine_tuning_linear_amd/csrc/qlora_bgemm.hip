@@ -247,7 +247,11 @@ __global__ __launch_bounds__(512) void bgemm_kernel(GemmArgs p) {
   const int64_t n0 = tn * BNO;  // first output column
   const int64_t wr0 = tn * BN;  // first weight row of the tile
   const int KT0 = (int)(p.Kred0 / 64);
-  const int KT = KT0 + (int)(p.Kred1 / 64);
+  // Reduction split (plain forward mode only, gridDim.y > 1): workgroup
+  // (x, y) takes reduction tiles [kb, kb + KT) and writes fp32 partials.
+  const int kb = gridDim.y > 1 ? (int)blockIdx.y * p.ktiles_per_split : 0;
+  const int KTall = KT0 + (int)(p.Kred1 / 64);
+  const int KT = gridDim.y > 1 ? min(KTall, kb + p.ktiles_per_split) - kb : KTall;
 
   // direct load i (0..7) of this wave: tile rows 8 (8 wave + i) + lane/8,
   // physical chunk lane%8 <- logical chunk (lane%8) ^ swz(row)
@@ -284,7 +288,7 @@ __global__ __launch_bounds__(512) void bgemm_kernel(GemmArgs p) {
     boff[i] *= 2;
   }
   auto load_a = [&](uint16_t* buf, int kt) {
-    kt = kt < KT ? kt : KT - 1;
+    kt = (kt < KT ? kt : KT - 1) + kb;
     const bool second = kt >= KT0;
     const int so = (second ? kt - KT0 : kt) * 128;
 #pragma unroll
@@ -293,7 +297,7 @@ __global__ __launch_bounds__(512) void bgemm_kernel(GemmArgs p) {
                                                so, 0, 0);
   };
   auto load_b = [&](uint16_t* buf, int kt) {
-    kt = kt < KT ? kt : KT - 1;
+    kt = (kt < KT ? kt : KT - 1) + kb;
 #pragma unroll
     for (int i = 0; i < LPH; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, LDS_PTR(buf + (LPH * wave + i) * 512), 16, boff[i], kt * 128, 0, 0);
@@ -405,7 +409,7 @@ __global__ __launch_bounds__(512) void bgemm_kernel(GemmArgs p) {
     // and the scalar form follow the fill.
     const LoraSide* L[2];
     int lo[2], hi[2];
-    const int ns = lora_sides<MODE, FN, false>(p, L, lo, hi);
+    const int ns = lora_sides<MODE, FN, true>(p, L, lo, hi);  // split runs: split 0 only
     const bool fast = lora_fast(*L[0]) && (ns < 2 || lora_fast(*L[1]));
     LoraRegs<FM, FN> R0, R1;
     if (fast) {
@@ -449,6 +453,12 @@ __global__ __launch_bounds__(512) void bgemm_kernel(GemmArgs p) {
     wait_vmcnt<0>();  // no direct load may still target LDS past this point
   }
   stage_barrier();  // every wave is done reading operands: LDS is free
+  if constexpr (MODE == MODE_FWD) {
+    if (gridDim.y > 1) {
+      gemm_epilogue<MODE, 2, WN, FM, FN, true>(p, acc, arow, m0, n0, wm, wn, l32, g);
+      return;
+    }
+  }
   uint16_t* buf = wave < 2 ? hb0 : wave < 4 ? hb1 : wave < 6 ? hb2 : hb3;
   bg_epilogue<MODE>(p, acc, m0, n0, wm, wn, lane, buf + (wave & 1) * 8192);
 }
@@ -557,10 +567,16 @@ static hipError_t run_bgemm(GemmArgs a, hipStream_t st) {
   a.tiles_n = (a.Nout + BNO - 1) / BNO;
   const int64_t n = a.tiles_m * a.tiles_n;
   if (n == 0) return hipSuccess;
+  // reduction splits (plain forward only): fp32 partials [splits][M][Nout]
+  unsigned splits = 1;
+  if (MODE == MODE_FWD && a.ktiles_per_split > 0 && a.partial) {
+    const int64_t kt = (a.Kred0 + a.Kred1) / 64;
+    splits = (unsigned)((kt + a.ktiles_per_split - 1) / a.ktiles_per_split);
+  }
   if (a.wrows > a.M)
-    bgemm_kernel<MODE, true><<<dim3((unsigned)n), 512, 0, st>>>(a);
+    bgemm_kernel<MODE, true><<<dim3((unsigned)n, splits), 512, 0, st>>>(a);
   else
-    bgemm_kernel<MODE, false><<<dim3((unsigned)n), 512, 0, st>>>(a);
+    bgemm_kernel<MODE, false><<<dim3((unsigned)n, splits), 512, 0, st>>>(a);
   return hipGetLastError();
 }
 

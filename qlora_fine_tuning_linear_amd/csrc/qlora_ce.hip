@@ -1,0 +1,204 @@
+// Output head + cross-entropy for gfx950: the fused linear / cross-entropy
+// step of "LLM Fine-Tuning in 2026: Unsloth vs QLoRA vs Liger-Kernel"
+// (section 3), computed one token chunk at a time so that no [tokens, vocab]
+// logit matrix is ever held.  Per chunk the entry point runs the bf16 GEMM
+// for the chunk's logits, ce_rows_kernel for the loss terms and the logit
+// gradient (in place), and the bf16 GEMM again (reduction over the vocabulary,
+// split into fp32 partials) for dX.  The helpers here:
+//   * ce_count_kernel      - number of tokens that carry a target;
+//   * transpose_bf16_kernel - the head [V, D] -> [D, V], so that the dX product
+//     reduces over contiguous rows like every other GEMM of the library;
+//   * ce_rows_kernel       - one workgroup per token row of logits: log-sum-exp
+//     (one pass, running maximum), the token's loss term and, in a second pass,
+//     (softmax - onehot) / n rounded to bf16 in place of the logits;
+//   * ce_loss_kernel       - the mean of the per-token terms in a fixed order.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "qlora_device.h"
+#include "qlora_launch.h"
+
+namespace qk {
+
+// A target counts when it is a class index; ignore_index and any value
+// outside [0, V) mark a token without a target.
+__device__ __forceinline__ bool ce_valid(int32_t t, int64_t V, int32_t ignore) {
+  return t != ignore && t >= 0 && (int64_t)t < V;
+}
+
+__global__ __launch_bounds__(1024) void ce_count_kernel(const int32_t* __restrict__ targets, int64_t T, int64_t V,
+                                                        int32_t ignore, int32_t* __restrict__ n_valid) {
+  __shared__ int32_t red[1024];
+  int32_t c = 0;
+  for (int64_t i = threadIdx.x; i < T; i += 1024) c += ce_valid(targets[i], V, ignore) ? 1 : 0;
+  red[threadIdx.x] = c;
+  __syncthreads();
+  for (int s = 512; s > 0; s >>= 1) {
+    if ((int)threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) *n_valid = red[0];
+}
+
+// out[d, v] = in[v, d] for a [V, D] bf16 matrix, 64 x 64 tiles through LDS
+// (rows read and written as 16-byte chunks).  V, D multiples of 64.
+constexpr int TR_LD = 72;  // LDS row stride (elements)
+
+__global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __restrict__ in, int64_t V, int64_t D,
+                                                             uint16_t* __restrict__ out) {
+  __shared__ __attribute__((aligned(16))) uint16_t tile[64 * TR_LD];
+  const int64_t d0 = (int64_t)blockIdx.x * 64, v0 = (int64_t)blockIdx.y * 64;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int c = threadIdx.x + 256 * j, row = c >> 3, ch = c & 7;
+    *reinterpret_cast<u32x4*>(tile + row * TR_LD + ch * 8) =
+        *reinterpret_cast<const u32x4*>(in + (v0 + row) * D + d0 + ch * 8);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int c = threadIdx.x + 256 * j, drow = c >> 3, vch = c & 7;
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      w[e] = (uint32_t)tile[(vch * 8 + 2 * e) * TR_LD + drow] |
+             ((uint32_t)tile[(vch * 8 + 2 * e + 1) * TR_LD + drow] << 16);
+    *reinterpret_cast<u32x4*>(out + (d0 + drow) * V + v0 + vch * 8) = u32x4{w[0], w[1], w[2], w[3]};
+  }
+}
+
+// Running (max, sum of exp(x - max)) pairs, combined in a fixed order.
+__device__ __forceinline__ void lse_combine(float& m, float& s, float m2, float s2) {
+  if (s2 == 0.0f) return;
+  if (s == 0.0f) {
+    m = m2;
+    s = s2;
+    return;
+  }
+  const float mm = fmaxf(m, m2);
+  s = s * __expf(m - mm) + s2 * __expf(m2 - mm);
+  m = mm;
+}
+
+// One workgroup of 256 threads per token row of the chunk's logits z [rows, V]
+// (bf16, V % 8 == 0).  Thread i takes the 16-byte chunks i, i + 256, ...;
+// partial (max, sum) pairs are combined across lanes with a fixed xor pattern
+// and across the four waves in wave order, so the result does not depend on
+// timing.  Then token_loss[row] = lse - z[target] (0 without a target) and,
+// with want_grad, z is overwritten by bf16((softmax(z) - onehot) / n) (0 rows
+// for tokens without a target).
+__global__ __launch_bounds__(256) void ce_rows_kernel(uint16_t* __restrict__ z, int64_t V,
+                                                      const int32_t* __restrict__ targets, int32_t ignore,
+                                                      const int32_t* __restrict__ n_valid, int want_grad,
+                                                      float* __restrict__ token_loss) {
+  __shared__ float wm[4], wsum[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t row = blockIdx.x;
+  uint16_t* zr = z + row * V;
+  const int32_t tgt = targets[row];
+  const bool valid = ce_valid(tgt, V, ignore);
+  // the target's logit, read before any thread overwrites the row
+  const float zt = valid ? bf16_to_f32(zr[tgt]) : 0.0f;
+  const int64_t nch = V / 8;
+
+  float m = 0.0f, s = 0.0f;
+  for (int64_t c = tid; c < nch; c += 256) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(zr + c * 8);
+    float x[8];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      x[2 * d] = bf16_lo(v[d]);
+      x[2 * d + 1] = bf16_hi(v[d]);
+    }
+    float cm = x[0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) cm = fmaxf(cm, x[e]);
+    float cs = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) cs += __expf(x[e] - cm);
+    lse_combine(m, s, cm, cs);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float m2 = __shfl_xor(m, o), s2 = __shfl_xor(s, o);
+    lse_combine(m, s, m2, s2);
+  }
+  if (lane == 0) {
+    wm[wave] = m;
+    wsum[wave] = s;
+  }
+  __syncthreads();
+  float M = wm[0], S = wsum[0];
+#pragma unroll
+  for (int w = 1; w < 4; ++w) lse_combine(M, S, wm[w], wsum[w]);
+  const float lse = M + __logf(S);
+  if (tid == 0) token_loss[row] = valid ? lse - zt : 0.0f;
+  if (!want_grad) return;
+
+  const int32_t n = *n_valid;
+  const float inv_n = (valid && n > 0) ? 1.0f / (float)n : 0.0f;
+  for (int64_t c = tid; c < nch; c += 256) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(zr + c * 8);
+    u32x4 o;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      float g[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const float x = e ? bf16_hi(v[d]) : bf16_lo(v[d]);
+        const int64_t col = c * 8 + 2 * d + e;
+        g[e] = (__expf(x - lse) - (col == tgt ? 1.0f : 0.0f)) * inv_n;
+      }
+      o[d] = pack_bf16x2(g[0], g[1]);
+    }
+    *reinterpret_cast<u32x4*>(zr + c * 8) = o;
+  }
+}
+
+// loss = (1/n) sum_t token_loss[t] (0 when n == 0 or n_valid is null):
+// thread i adds t = i, i + 1024, ... in order, then a fixed tree over the
+// threads.
+__global__ __launch_bounds__(1024) void ce_loss_kernel(const float* __restrict__ token_loss, int64_t T,
+                                                       const int32_t* __restrict__ n_valid, float* __restrict__ loss) {
+  __shared__ float red[1024];
+  float s = 0.0f;
+  for (int64_t i = threadIdx.x; i < T; i += 1024) s += token_loss[i];
+  red[threadIdx.x] = s;
+  __syncthreads();
+  for (int k = 512; k > 0; k >>= 1) {
+    if ((int)threadIdx.x < k) red[threadIdx.x] += red[threadIdx.x + k];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const int32_t n = n_valid ? *n_valid : 0;
+    *loss = n > 0 ? red[0] / (float)n : 0.0f;
+  }
+}
+
+}  // namespace qk
+
+using namespace qk;
+
+hipError_t launch_ce_count(const int32_t* targets, int64_t T, int64_t V, int32_t ignore, int32_t* n_valid,
+                           hipStream_t st) {
+  ce_count_kernel<<<1, 1024, 0, st>>>(targets, T, V, ignore, n_valid);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose_bf16(const uint16_t* in, int64_t V, int64_t D, uint16_t* out, hipStream_t st) {
+  if (V == 0 || D == 0) return hipSuccess;
+  transpose_bf16_kernel<<<dim3((unsigned)(D / 64), (unsigned)(V / 64)), 256, 0, st>>>(in, V, D, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_ce_rows(uint16_t* z, int64_t rows, int64_t V, const int32_t* targets, int32_t ignore,
+                          const int32_t* n_valid, int want_grad, float* token_loss, hipStream_t st) {
+  if (rows == 0) return hipSuccess;
+  ce_rows_kernel<<<dim3((unsigned)rows), 256, 0, st>>>(z, V, targets, ignore, n_valid, want_grad, token_loss);
+  return hipGetLastError();
+}
+
+hipError_t launch_ce_loss(const float* token_loss, int64_t T, const int32_t* n_valid, float* loss, hipStream_t st) {
+  ce_loss_kernel<<<1, 1024, 0, st>>>(token_loss, T, n_valid, loss);
+  return hipGetLastError();
+}

@@ -137,6 +137,13 @@ hipError_t launch_rmsnorm_bwd(const uint16_t* dY, const uint16_t* X, const uint1
 hipError_t launch_nf4_dequantize(const Nf4Dev& w, const float* codebook, int out_f32, void* out, hipStream_t st);
 hipError_t launch_qgemm(int mode, const GemmArgs& a, const qplan::GemmPlan& pl, hipStream_t st);
 hipError_t launch_bgemm(int mode, const GemmArgs& a, hipStream_t st);
+// Output head + cross-entropy helpers (qlora_ce.hip).
+hipError_t launch_ce_count(const int32_t* targets, int64_t T, int64_t V, int32_t ignore, int32_t* n_valid,
+                           hipStream_t st);
+hipError_t launch_transpose_bf16(const uint16_t* in, int64_t V, int64_t D, uint16_t* out, hipStream_t st);
+hipError_t launch_ce_rows(uint16_t* z, int64_t rows, int64_t V, const int32_t* targets, int32_t ignore,
+                          const int32_t* n_valid, int want_grad, float* token_loss, hipStream_t st);
+hipError_t launch_ce_loss(const float* token_loss, int64_t T, const int32_t* n_valid, float* loss, hipStream_t st);
 // bf16 copy of the dequantized weight(s) for bgemm_kernel.
 //   rows : out[R, 0:K] = deq(W)[src(R), :]; with w1 (SwiGLU pair) rows come in
 //          blocks of 256 = 128 gate rows then the 128 up rows of the same

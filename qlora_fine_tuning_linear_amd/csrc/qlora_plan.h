@@ -228,4 +228,35 @@ inline MlpWs mlp_ws(int64_t M, int64_t D, int64_t I, int rg, int ru, int rd) {
   return w;
 }
 
+// Output head + cross-entropy: C tokens per chunk; the dX product of a chunk
+// ([C, V] x [V, D]) splits its vocabulary reduction so that tiles x splits
+// covers the chip about twice, with at least 32 vocabulary tiles per split.
+struct CeWs {
+  int64_t C;
+  int splits, kps;
+  size_t nvalid, tloss, logits, wt, part, total;
+};
+
+inline CeWs ce_ws(int64_t T, int64_t D, int64_t V, int64_t chunk, bool want_dx) {
+  CeWs w{};
+  w.C = T < chunk ? T : chunk;
+  if (w.C < 1) w.C = 1;
+  const int64_t kt = V / 64;
+  const int64_t tiles = cdiv(w.C, 256) * cdiv(D, 256);
+  int64_t splits = cdiv(2 * kNumCUs, tiles);
+  const int64_t max_splits = kt / 32 > 0 ? kt / 32 : 1;
+  if (splits > max_splits) splits = max_splits;
+  if (splits < 1) splits = 1;
+  const int64_t per = cdiv(kt, splits);
+  w.splits = (int)cdiv(kt, per);
+  w.kps = (int)per;
+  w.nvalid = 256;
+  w.tloss = align256((size_t)T * 4);
+  w.logits = align256((size_t)w.C * V * 2);
+  w.wt = want_dx ? align256((size_t)V * D * 2) : 0;
+  w.part = (want_dx && w.splits > 1) ? align256((size_t)w.splits * w.C * D * 4) : 0;
+  w.total = w.nvalid + w.tloss + w.logits + w.wt + w.part;
+  return w;
+}
+
 }  // namespace qplan

@@ -236,3 +236,22 @@ size_t qlora_mlp_workspace_bytes(const qlora_mlp* P, int64_t M) {
 }
 
 }  // extern "C"
+
+size_t qv_linear_ce_ws(int64_t T, int64_t D, int64_t V, int64_t chunk, int32_t want_dx) {
+  if (T < 0 || D <= 0 || V <= 0 || chunk < 1 || D % 64 != 0 || V % 64 != 0) return 0;
+  return qplan::ce_ws(T, D, V, chunk, want_dx != 0).total;
+}
+
+int qv_linear_ce(const void* X, int64_t T, int64_t D, const void* W, int64_t V, const int32_t* targets,
+                 int64_t chunk, const float* loss, const float* token_loss, const void* dX, const void* ws,
+                 size_t ws_bytes) {
+  if (T < 0 || D <= 0 || V <= 0 || chunk < 1) return QLORA_ERR_INVALID_ARG;
+  if (D % 64 != 0 || V % 64 != 0 || D > 65536 || V > ((int64_t)1 << 24)) return QLORA_ERR_UNSUPPORTED_SHAPE;
+  int st;
+  if ((st = check_ptr(loss))) return st;
+  if (token_loss && (st = check_ptr(token_loss))) return st;
+  if (T == 0) return QLORA_OK;
+  if ((st = check_ptr(X)) || (st = check_ptr(W)) || (st = check_ptr(targets))) return st;
+  if (dX && (st = check_ptr(dX))) return st;
+  return check_ws(ws, ws_bytes, qplan::ce_ws(T, D, V, chunk, dX != nullptr).total);
+}

@@ -24,3 +24,7 @@ int qv_mlp_fwd(const qlora_mlp* P, const void* X, int64_t M, const void* Y, cons
                size_t ws_bytes);
 int qv_mlp_bwd(const qlora_mlp* P, const void* dY, const void* X, const qlora_mlp_saved* S, int64_t M, const void* dX,
                const qlora_mlp_grads* G, const void* ws, size_t ws_bytes);
+size_t qv_linear_ce_ws(int64_t T, int64_t D, int64_t V, int64_t chunk, int32_t want_dx);
+int qv_linear_ce(const void* X, int64_t T, int64_t D, const void* W, int64_t V, const int32_t* targets,
+                 int64_t chunk, const float* loss, const float* token_loss, const void* dX, const void* ws,
+                 size_t ws_bytes);

@@ -200,6 +200,33 @@ def test_rmsnorm_rejections(lib):
     assert bwd(dw=FAKE + 4) == MISALIGNED
 
 
+def test_linear_ce_rejections(lib):
+    # every call below fails validation, so nothing reaches a device
+    ce = lambda T=16, D=64, V=128, chunk=8, X=FAKE, W=FAKE, t=FAKE, loss=FAKE, tl=None, dX=FAKE, ws=FAKE, \
+        wsb=1 << 30: lib.qlora_linear_ce(X, T, D, W, V, t, -100, chunk, loss, tl, dX, ws, wsb, None)
+    assert ce(D=96) == SHAPE
+    assert ce(V=100) == SHAPE
+    assert ce(D=0) == INVALID
+    assert ce(T=-1) == INVALID
+    assert ce(chunk=0) == INVALID
+    assert ce(loss=None) == INVALID
+    assert ce(X=None) == INVALID
+    assert ce(t=None) == INVALID
+    assert ce(W=FAKE + 2) == MISALIGNED
+    assert ce(dX=FAKE + 4) == MISALIGNED
+    assert ce(tl=FAKE + 4) == MISALIGNED
+    assert ce(wsb=16) == WS_SMALL
+    assert ce(dX=None, wsb=16) == WS_SMALL
+    assert ce(ws=FAKE + 4) == MISALIGNED
+    # workspace: chunk of logits + per-token losses (+ transposed head and partials with dX)
+    fwd_only = lib.qlora_linear_ce_workspace_bytes(16, 64, 128, 8, 0)
+    assert fwd_only == 256 + 256 + 8 * 128 * 2
+    with_dx = lib.qlora_linear_ce_workspace_bytes(16, 64, 128, 8, 1)
+    assert with_dx >= fwd_only + 128 * 64 * 2
+    assert lib.qlora_linear_ce_workspace_bytes(16, 96, 128, 8, 1) == 0
+    assert lib.qlora_linear_ce_workspace_bytes(4096, 4096, 128256, 1024, 0) == 256 + 4096 * 4 + 1024 * 128256 * 2
+
+
 def grouped(Ns=(64, 64), rs=(8, 8), N=None, K=128, G=None):
     Q = q.CGrouped()
     Q.W0 = nf4(sum(Ns) if N is None else N, K)
