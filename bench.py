@@ -14,7 +14,8 @@ the library's stream through qlora_trace_install), the CPU oracle timed on a
 bounded token sample of the same workload, and secondary lines for the
 single-linear workloads (Llama-3-8B q_proj, and the skinny M=64 gate_proj
 against the HBM roofline with its NF4 weights rotated to defeat the 256 MB
-last-level cache).
+last-level cache), the 16-bit merge, the packed q/k/v adapters, RMSNorm and
+the fused output head + cross-entropy.
 """
 import argparse
 import hashlib
@@ -41,9 +42,10 @@ def parse():
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="first run one plain device-to-device copy of this many MiB (the known-size kernel "
                          "that calibrates the FETCH_SIZE / WRITE_SIZE counters)")
-    ap.add_argument("--only", default=None, metavar="IDX|merge|rmsnorm|qkv",
+    ap.add_argument("--only", default=None, metavar="IDX|merge|rmsnorm|qkv|ce",
                     help="profiling aid: time only workload config IDX (0-4; the skinny linear with 4 rotated "
-                         "weight copies), the 16-bit merge, RMSNorm or the packed q/k/v adapters, and print its "
+                         "weight copies), the 16-bit merge, RMSNorm, the packed q/k/v adapters or the fused head + "
+                         "cross-entropy, and print its "
                          "own JSON line instead of the metric line")
     ap.add_argument("--summarize-traffic", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_MIB"),
                     help="no GPU: turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, "
@@ -405,6 +407,38 @@ def rmsnorm_bench(q, synth, steps, warmup, M=8192, D=4096, eps=1e-5):
                 bwd_frac_hbm_peak=bb / (b_ms * 1e-3) / 1e9 / HBM_PEAK_GBS)
 
 
+def ce_bench(q, synth, steps, warmup, T=4096, D=4096, V=128256, chunk=1024):
+    """qlora_linear_ce at the page's example (4096 tokens, hidden 4096, a 128256
+    class vocabulary): loss and dX in token chunks.  FLOPs: the logits and the
+    dX product, 2 T D V each.  Also reported: the call's workspace (one chunk of
+    bf16 logits, the transposed head, dX partials) against the [T, V] fp32 logit
+    matrix an unfused loss would hold."""
+    import torch
+    g = torch.Generator(device="cuda")
+    g.manual_seed(4242)
+    X = torch.randn(T, D, device="cuda", generator=g).bfloat16()
+    W = (torch.randn(V, D, device="cuda", generator=g) * (2.0 / D ** 0.5)).bfloat16()
+    t = torch.randint(0, V, (T,), device="cuda", generator=g, dtype=torch.int32)
+    dX = torch.empty_like(X)
+    nbytes = q.qlora_linear_ce_workspace_bytes(T, D, V, chunk, True)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    f = lambda: q.qlora_linear_ce(X, W, t, chunk=chunk, dX=dX, ws=ws)
+    for _ in range(warmup):
+        f()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        f()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    flops = 4.0 * T * D * V
+    return dict(workload="linear_ce_t%d_d%d_v%d_chunk%d" % (T, D, V, chunk), ms_per_call=ms,
+                tflops=flops / (ms * 1e-3) / 1e12, frac_bf16_peak=flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                tokens_per_s=T / (ms * 1e-3), workspace_gb=nbytes / 1e9, unfused_fp32_logits_gb=T * V * 4 / 1e9)
+
+
 def cpu_baseline(synth, target_s):
     """The oracle (fp64 numpy) on the first tokens of the same MLP workload."""
     import numpy as np
@@ -474,8 +508,8 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    if a.only in ("merge", "rmsnorm", "qkv"):
-        fn = {"merge": merge_bench, "rmsnorm": rmsnorm_bench, "qkv": grouped_bench}[a.only]
+    if a.only in ("merge", "rmsnorm", "qkv", "ce"):
+        fn = {"merge": merge_bench, "rmsnorm": rmsnorm_bench, "qkv": grouped_bench, "ce": ce_bench}[a.only]
         s = fn(q, synth, max(10, a.steps), a.warmup)
         print(json.dumps({k: (round(v, 4) if isinstance(v, float) else v) for k, v in s.items()}), flush=True)
         return
@@ -535,6 +569,9 @@ def main():
         sec.append({k: (round(v, 4) if isinstance(v, float) else v) for k, v in s.items()})
         log("secondary: rmsnorm")
         s = rmsnorm_bench(q, synth, max(20, a.steps), a.warmup)
+        sec.append({k: (round(v, 4) if isinstance(v, float) else v) for k, v in s.items()})
+        log("secondary: linear + cross-entropy")
+        s = ce_bench(q, synth, max(3, a.steps // 3), min(a.warmup, 2))
         sec.append({k: (round(v, 4) if isinstance(v, float) else v) for k, v in s.items()})
         out["secondary"] = sec
     out["cpu_baseline"] = None if a.no_cpu_baseline else cpu_baseline(synth, a.cpu_seconds)
