@@ -47,7 +47,7 @@ constexpr int TR_LD = 72;  // LDS row stride (elements)
 __global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __restrict__ in, int64_t V, int64_t D,
                                                              uint16_t* __restrict__ out) {
   __shared__ __attribute__((aligned(16))) uint16_t tile[64 * TR_LD];
-  const int64_t d0 = (int64_t)blockIdx.x * 64, v0 = (int64_t)blockIdx.y * 64;
+  const int64_t v0 = (int64_t)blockIdx.x * 64, d0 = (int64_t)blockIdx.y * 64;
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int c = threadIdx.x + 256 * j, row = c >> 3, ch = c & 7;
@@ -187,7 +187,7 @@ hipError_t launch_ce_count(const int32_t* targets, int64_t T, int64_t V, int32_t
 
 hipError_t launch_transpose_bf16(const uint16_t* in, int64_t V, int64_t D, uint16_t* out, hipStream_t st) {
   if (V == 0 || D == 0) return hipSuccess;
-  transpose_bf16_kernel<<<dim3((unsigned)(D / 64), (unsigned)(V / 64)), 256, 0, st>>>(in, V, D, out);
+  transpose_bf16_kernel<<<dim3((unsigned)(V / 64), (unsigned)(D / 64)), 256, 0, st>>>(in, V, D, out);
   return hipGetLastError();
 }
 
