@@ -26,7 +26,8 @@
  * - Gradients are written (overwritten), never accumulated.
  * - M (tokens) may be any value >= 0; M == 0 is a no-op that returns OK.
  * - Shapes: K % 64 == 0 and N % 64 == 0 (whole absmax blocks, whole tiles
- *   of 64), 1 <= r <= 128, blocksize == 64, dq_group in {0, 256}.
+ *   of 64), K, N <= 4194240 (a 256-row tile of a bf16 copy stays below
+ *   2 GiB), 1 <= r <= 128, blocksize == 64, dq_group in {0, 256}.
  */
 #ifndef QLORA_H
 #define QLORA_H
@@ -308,7 +309,7 @@ size_t qlora_linear_ce_workspace_bytes(int64_t T, int64_t D, int64_t V, int64_t 
  *   ws         ws_bytes >= qlora_linear_ce_workspace_bytes(T, D, V, chunk,
  *              dX != NULL); with dX the head is transposed into it once per
  *              call (V * D * 2 bytes)
- * D and V multiples of 64, D <= 65536, V <= 2^24
+ * D and V multiples of 64, D <= 65536, V <= 4194240
  * (QLORA_ERR_UNSUPPORTED_SHAPE otherwise).  T == 0 writes loss = 0 and needs
  * no workspace.  All pointers 16-byte aligned.  Results are bitwise
  * reproducible from run to run.

@@ -11,6 +11,8 @@
 
 namespace {
 
+constexpr int64_t kMaxDim = ((int64_t)1 << 22) - 64;  // 4194240
+
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 int check_nf4(const qlora_nf4* w) {
@@ -22,6 +24,9 @@ int check_nf4(const qlora_nf4* w) {
   if (w->dq_group != 0 && (!w->absmax_q || !w->absmax_scale)) return QLORA_ERR_INVALID_ARG;
   if (w->N == 0 || w->K == 0) return QLORA_ERR_UNSUPPORTED_SHAPE;
   if (w->K % 64 != 0 || w->N % 64 != 0) return QLORA_ERR_UNSUPPORTED_SHAPE;
+  // a 256-row tile of a bf16 row-major copy must stay below 2 GiB (32-bit
+  // buffer offsets of the GEMM's direct loads)
+  if (w->K > kMaxDim || w->N > kMaxDim) return QLORA_ERR_UNSUPPORTED_SHAPE;
   if (!aligned16(w->codes) || !aligned16(w->codebook)) return QLORA_ERR_MISALIGNED;
   if (w->dq_group == 0 && !aligned16(w->absmax)) return QLORA_ERR_MISALIGNED;
   if (w->dq_group != 0 && !aligned16(w->absmax_scale)) return QLORA_ERR_MISALIGNED;
@@ -246,7 +251,7 @@ int qv_linear_ce(const void* X, int64_t T, int64_t D, const void* W, int64_t V, 
                  int64_t chunk, const float* loss, const float* token_loss, const void* dX, const void* ws,
                  size_t ws_bytes) {
   if (T < 0 || D <= 0 || V <= 0 || chunk < 1) return QLORA_ERR_INVALID_ARG;
-  if (D % 64 != 0 || V % 64 != 0 || D > 65536 || V > ((int64_t)1 << 24)) return QLORA_ERR_UNSUPPORTED_SHAPE;
+  if (D % 64 != 0 || V % 64 != 0 || D > 65536 || V > kMaxDim) return QLORA_ERR_UNSUPPORTED_SHAPE;
   int st;
   if ((st = check_ptr(loss))) return st;
   if (token_loss && (st = check_ptr(token_loss))) return st;

@@ -76,6 +76,8 @@ def test_linear_fwd_rejections(lib):
     assert fwd(lib, linear(alpha=float("inf"))) == INVALID
     assert fwd(lib, linear(K=96)) == SHAPE
     assert fwd(lib, linear(N=100)) == SHAPE
+    assert fwd(lib, linear(N=1 << 22)) == SHAPE      # a 256-row bf16 tile must stay below 2 GiB
+    assert fwd(lib, linear(K=1 << 22)) == SHAPE
     assert fwd(lib, linear(r=0)) == SHAPE
     assert fwd(lib, linear(r=129)) == SHAPE
     assert fwd(lib, linear(blocksize=32)) == SHAPE
@@ -218,6 +220,7 @@ def test_linear_ce_rejections(lib):
     assert ce(wsb=16) == WS_SMALL
     assert ce(dX=None, wsb=16) == WS_SMALL
     assert ce(ws=FAKE + 4) == MISALIGNED
+    assert ce(V=(1 << 22)) == SHAPE               # 256 vocabulary rows of bf16 must stay below 2 GiB
     # workspace: chunk of logits + per-token losses (+ transposed head and partials with dX)
     fwd_only = lib.qlora_linear_ce_workspace_bytes(16, 64, 128, 8, 0)
     assert fwd_only == 256 + 256 + 8 * 128 * 2
