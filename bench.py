@@ -491,7 +491,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if a.gpus != 1 or world != 1:
         print("bench.py measures one MI355X: the QLoRA linear / MLP path here runs on a single GPU "
-              "(data-parallel sharding over tokens is described in DESIGN.md, not launched). "
+              "(data-parallel sharding over tokens is a design note of the repository, not launched). "
               "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
     import torch
