@@ -532,7 +532,7 @@ __global__ __launch_bounds__(512) void lora_down_kernel(const uint16_t* __restri
     const int j = 32 * jf + l32;
     wok[jf] = j < rt;
     wrow[jf] = (j < r0 ? W0 + (int64_t)j * Kred : W1 + (int64_t)(j - r0) * Kred) + 32 * h;
-    if (!wok[jf]) wrow[jf] = zrow;  // any valid address; the operand is zeroed
+    if (!wok[jf]) wrow[jf] = W0 + 32 * h;  // any valid address (one line for all such lanes); zeroed
   }
   const int64_t C = Kred / 64;
   const int64_t cb = (int64_t)blockIdx.y * chunks_per_split;
@@ -593,6 +593,102 @@ __global__ __launch_bounds__(512) void lora_down_kernel(const uint16_t* __restri
       V0[mm * r0 + j] = sum;
     } else {
       V1[mm * r1 + (j - r0)] = sum;
+    }
+  }
+}
+
+// One 16x16x32 bf16 MFMA: C[16x16] += A[16x32] B[32x16]; lane l holds
+// A[l%16][8(l/16) + i] and B[8(l/16) + i][l%16], accumulator v of lane l is
+// C[4(l/16) + v][l%16].
+__device__ __forceinline__ f32x4 mfma16k32(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                 0, 0, 0);
+}
+
+// The same down-projection when r0 + r1 <= 16, on 16x16x32 MFMAs: the W rows
+// are the 16 rows of the A operand (none wasted), and each token frag is 16
+// tokens.  Lane (c, q) (c = lane % 16, q = lane / 16) loads 16 bytes at
+// k0 + 32 s + 8 q of its token row for step s of a 64-wide chunk, so one load
+// instruction covers 64 contiguous bytes of 16 token rows (half lines; the
+// 32-wide form reads 32-byte pieces of 32 rows).  Workgroup: 32 tokens (two
+// frags), 8 waves taking the chunks of their split in turn; the 8 wave
+// partials are summed in LDS in wave order.
+__global__ __launch_bounds__(512) void lora_down16_kernel(const uint16_t* __restrict__ Z, int64_t M, int64_t Kred,
+                                                          const uint16_t* __restrict__ W0, int r0,
+                                                          const uint16_t* __restrict__ W1, int r1,
+                                                          float* __restrict__ V0, float* __restrict__ V1,
+                                                          int64_t chunks_per_split, float* __restrict__ part) {
+  __shared__ float red[8][2 * 4 * 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = lane & 15, q = lane >> 4;
+  const int rt = r0 + r1;
+  const int64_t m0 = (int64_t)blockIdx.x * 32;
+  const uint16_t* zrow[2];
+#pragma unroll
+  for (int f = 0; f < 2; ++f) {
+    const int64_t m = (m0 + 16 * f + c < M) ? m0 + 16 * f + c : M - 1;
+    zrow[f] = Z + m * Kred + 8 * q;
+  }
+  const bool wok = c < rt;
+  const uint16_t* wrow = wok ? (c < r0 ? W0 + (int64_t)c * Kred : W1 + (int64_t)(c - r0) * Kred) + 8 * q
+                             : W0 + 8 * q;  // any valid address; the operand is zeroed
+  const int64_t C = Kred / 64;
+  const int64_t cb = (int64_t)blockIdx.y * chunks_per_split;
+  const int64_t ce = (cb + chunks_per_split < C) ? cb + chunks_per_split : C;
+
+  f32x4 acc[2];
+#pragma unroll
+  for (int f = 0; f < 2; ++f) acc[f] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  u32x4 za[2][2], wa[2], zb[2][2], wb[2];
+  auto load = [&](int64_t ch, u32x4 (&z)[2][2], u32x4 (&w)[2]) {
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+#pragma unroll
+      for (int f = 0; f < 2; ++f) z[f][st] = *reinterpret_cast<const u32x4*>(zrow[f] + ch * 64 + 32 * st);
+      w[st] = *reinterpret_cast<const u32x4*>(wrow + ch * 64 + 32 * st);
+    }
+  };
+  auto mul = [&](const u32x4 (&z)[2][2], const u32x4 (&w)[2]) {
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      const u32x4 wz = wok ? w[st] : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int f = 0; f < 2; ++f) acc[f] = mfma16k32(wz, z[f][st], acc[f]);
+    }
+  };
+  int64_t ch = cb + wave;
+  if (ch < ce) load(ch, za, wa);
+  // two register sets alternate (a copy of a prefetch would wait for it)
+  for (; ch + 8 < ce; ch += 16) {
+    load(ch + 8, zb, wb);
+    mul(za, wa);
+    if (ch + 16 < ce) load(ch + 16, za, wa);
+    mul(zb, wb);
+  }
+  if (ch < ce) mul(za, wa);
+
+  // acc[f][v] = C[j = 4q + v][token m0 + 16 f + c]
+#pragma unroll
+  for (int f = 0; f < 2; ++f)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) red[wave][(f * 4 + v) * 64 + lane] = acc[f][v];
+  __syncthreads();
+  if (tid < 2 * 4 * 64) {
+    float sum = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) sum += red[w][tid];
+    const int ln = tid & 63, v = (tid >> 6) & 3, f = tid >> 8;
+    const int j = 4 * (ln >> 4) + v;
+    const int64_t mm = m0 + 16 * f + (ln & 15);
+    if (j < rt && mm < M) {
+      if (part) {
+        part[((int64_t)blockIdx.y * M + mm) * rt + j] = sum;
+      } else if (j < r0) {
+        V0[mm * r0 + j] = sum;
+      } else {
+        V1[mm * r1 + (j - r0)] = sum;
+      }
     }
   }
 }
@@ -803,11 +899,6 @@ __global__ __launch_bounds__(256) void lora_grad_kernel(const uint16_t* __restri
 // after the register transpose operand t holds, for row c, column
 // p0 + 8c + t of those 8 tokens, and the V operand holds V[token][j = c].
 // ------------------------------------------------------------------------
-__device__ __forceinline__ f32x4 mfma16k32(u32x4 a, u32x4 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
-                                                 0, 0, 0);
-}
-
 template <int ZMODE>
 __global__ __launch_bounds__(256) void lora_grad16_kernel(const uint16_t* __restrict__ Z0,
                                                           const uint16_t* __restrict__ Z1, int64_t M, int64_t P,
@@ -1020,8 +1111,13 @@ hipError_t launch_lora_down(const uint16_t* Z, int64_t M, int64_t Kred, const ui
   const int S = (int)((C + per - 1) / per);
   dim3 grid(grid1(M, 32), (unsigned)S);
   float* pp = S > 1 ? part : nullptr;
-  const int jf = (r0 + r1 + 31) / 32;
+  int jf = (r0 + r1 + 31) / 32;
+  if (r0 + r1 <= 16) {
+    lora_down16_kernel<<<grid, 512, 0, st>>>(Z, M, Kred, W0, r0, W1, r1, V0, V1, per, pp);
+    jf = 0;
+  }
   switch (jf) {
+    case 0: break;
     case 1: lora_down_kernel<1><<<grid, 512, 0, st>>>(Z, M, Kred, W0, r0, W1, r1, V0, V1, per, pp); break;
     case 2: lora_down_kernel<2><<<grid, 512, 0, st>>>(Z, M, Kred, W0, r0, W1, r1, V0, V1, per, pp); break;
     case 3: lora_down_kernel<3><<<grid, 512, 0, st>>>(Z, M, Kred, W0, r0, W1, r1, V0, V1, per, pp); break;
