@@ -522,7 +522,9 @@ int qlora_mlp_fwd(const qlora_mlp* P, const void* X, int64_t M, void* Y, const q
   const qplan::MlpWs w = qplan::mlp_ws(M, D, I, P->gate.r, P->up.r, P->down.r);
   uint16_t* H = reinterpret_cast<uint16_t*>(bytes(ws));
   float* down_part = reinterpret_cast<float*>(bytes(ws) + w.fwd_H);
-  uint16_t* wbuf = w.fwd_wbuf ? reinterpret_cast<uint16_t*>(bytes(ws) + w.fwd_H + w.fwd_down) : nullptr;
+  float* had_part = w.fwd_had ? reinterpret_cast<float*>(bytes(ws) + w.fwd_H + w.fwd_down) : nullptr;
+  uint16_t* wbuf =
+      w.fwd_wbuf ? reinterpret_cast<uint16_t*>(bytes(ws) + w.fwd_H + w.fwd_down + w.fwd_had) : nullptr;
 
   // XA_g | XA_u in one pass over X
   QHIP(launch_lora_down(u16(X), M, D, u16(P->gate.A), P->gate.r, u16(P->up.A), P->up.r, S->XA_g, S->XA_u,
@@ -548,14 +550,22 @@ int qlora_mlp_fwd(const qlora_mlp* P, const void* X, int64_t M, void* Y, const q
       a.wb = wbuf;
       a.ldw = D;
       a.wrows = qplan::pair_rows(I);
+      if (had_part) {  // HA_d from the GEMM's own H, as column-tile partials
+        a.had_A = u16(P->down.A);
+        a.had_r = P->down.r;
+        a.had_part = had_part;
+      }
       QHIP(traced_gemm_b(MODE_FWD_SWIGLU, a, st));
     } else {
       QHIP(traced_gemm_q(MODE_FWD_SWIGLU, a, qplan::plan_gemm(M, I, D, false), st));
     }
   }
   // HA_d = H A_d^T
-  QHIP(launch_lora_down(H, M, I, u16(P->down.A), P->down.r, nullptr, 0, S->HA_d, nullptr,
-                        qplan::plan_down_splits(M, I), down_part, st));
+  if (had_part)
+    QHIP(launch_had_finish(had_part, (int)qplan::cdiv(I, 128), M, P->down.r, S->HA_d, st));
+  else
+    QHIP(launch_lora_down(H, M, I, u16(P->down.A), P->down.r, nullptr, 0, S->HA_d, nullptr,
+                          qplan::plan_down_splits(M, I), down_part, st));
   // Y = H W_d^T + s_d HA_d B_d^T
   {
     GemmArgs a = gemm_args();

@@ -224,6 +224,54 @@ __device__ __forceinline__ void bg_epilogue(const GemmArgs& p, f32x16 (&acc)[BG_
   }
 }
 
+// SwiGLU forward, optional: the wave's share of H A^T (the down layer's
+// rank-r product, A [r, Nout] bf16) straight from the accumulators.  Lane
+// (token l32, g) holds H at columns cw + 8q + 4g + e (q, e < 4); taken as the
+// A operand of two 32x32x16 MFMAs, step s covers q = 2s, 2s + 1, and the B
+// operand reads A at the same columns, so no transpose is needed.  H is
+// rounded to bf16 exactly as the stored H.  The 128 x 32 fp32 result goes to
+// the wave's LDS region [token][j].
+template <int MODE>
+__device__ __forceinline__ void bg_had_wave(const GemmArgs& p, f32x16 (&acc)[BG_FM][2], int64_t n0, int wn,
+                                            int lane, float* reg) {
+  const int l32 = lane & 31, g = lane >> 5;
+  const int64_t cw = n0 + wn * 32;
+  const bool jok = l32 < p.had_r;
+  const uint16_t* arow = p.had_A + (int64_t)(jok ? l32 : 0) * p.Nout;
+  u32x4 bop[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const int64_t c0 = cw + 16 * s + 4 * g, c1 = c0 + 8;
+    const u32x2 lo = (jok && c0 < p.Nout) ? *reinterpret_cast<const u32x2*>(arow + c0) : u32x2{0u, 0u};
+    const u32x2 hi = (jok && c1 < p.Nout) ? *reinterpret_cast<const u32x2*>(arow + c1) : u32x2{0u, 0u};
+    bop[s] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+  }
+#pragma unroll
+  for (int i = 0; i < BG_FM; ++i) {
+    f32x16 h{};
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      uint32_t w[4];
+#pragma unroll
+      for (int hq = 0; hq < 2; ++hq) {
+        const int q = 2 * s + hq;
+        float H[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float Gv = acc[i][0][4 * q + e], Uv = acc[i][1][4 * q + e];
+          H[e] = Gv * sigmoid_fast(Gv) * Uv;
+        }
+        w[2 * hq] = pack_bf16x2(H[0], H[1]);
+        w[2 * hq + 1] = pack_bf16x2(H[2], H[3]);
+      }
+      h = mfma32(u32x4{w[0], w[1], w[2], w[3]}, bop[s], h);
+    }
+    // h[v] = C[token 8(v/4) + 4g + v%4 of frag i][j = l32]
+#pragma unroll
+    for (int v = 0; v < 16; ++v) reg[(i * 32 + 8 * (v >> 2) + 4 * g + (v & 3)) * 32 + l32] = h[v];
+  }
+}
+
 template <int MODE, bool WLEAD>
 __global__ __launch_bounds__(512) void bgemm_kernel(GemmArgs p) {
   constexpr int WN = BG_WN, FM = BG_FM, FN = BG_FN;
@@ -456,6 +504,29 @@ __global__ __launch_bounds__(512) void bgemm_kernel(GemmArgs p) {
   }
   uint16_t* buf = wave < 2 ? hb0 : wave < 4 ? hb1 : wave < 6 ? hb2 : hb3;
   bg_epilogue<MODE>(p, acc, m0, n0, wm, wn, lane, buf + (wave & 1) * 8192);
+  if constexpr (MODE == MODE_FWD_SWIGLU) {
+    if (p.had_part) {
+      // each wave's 128 tokens x 32 columns of H A^T into its region, then the
+      // four waves of a token half are added in column order
+      bg_had_wave<MODE>(p, acc, n0, wn, lane, reinterpret_cast<float*>(buf + (wave & 1) * 8192));
+      __syncthreads();
+      const int r = p.had_r;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const int e = tid + 512 * k;  // [half][token][j], 2 x 128 x 32
+        const int hf = e >> 12, t = (e >> 5) & 127, j = e & 31;
+        float sum = 0.0f;
+#pragma unroll
+        for (int w4 = 0; w4 < 4; ++w4) {
+          const int w = hf * 4 + w4;
+          const uint16_t* bw = w < 2 ? hb0 : w < 4 ? hb1 : w < 6 ? hb2 : hb3;
+          sum += reinterpret_cast<const float*>(bw + (w & 1) * 8192)[t * 32 + j];
+        }
+        const int64_t m = m0 + hf * 128 + t;
+        if (j < r && m < p.M) p.had_part[((int64_t)tn * p.M + m) * r + j] = sum;
+      }
+    }
+  }
 }
 
 // ------------------------------------------------------------------------
@@ -584,6 +655,31 @@ hipError_t launch_bgemm(int mode, const GemmArgs& a, hipStream_t st) {
     case MODE_BWD_DUAL: return run_bgemm<MODE_BWD_DUAL>(a, st);
     default: return hipErrorInvalidValue;
   }
+}
+
+// out[m, j] = sum over column tiles t of part[t][m][j], in tile order.
+__global__ __launch_bounds__(256) void had_finish_kernel(const float* __restrict__ part, int tiles, int64_t Mr,
+                                                         float* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= Mr) return;
+  float s = 0.0f;
+  int t = 0;
+  for (; t + 8 <= tiles; t += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = part[(int64_t)(t + u) * Mr + i];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s += v[u];
+  }
+  for (; t < tiles; ++t) s += part[(int64_t)t * Mr + i];
+  out[i] = s;
+}
+
+hipError_t launch_had_finish(const float* part, int tiles, int64_t M, int r, float* out, hipStream_t st) {
+  const int64_t n = M * r;
+  if (n == 0) return hipSuccess;
+  had_finish_kernel<<<dim3((unsigned)((n + 255) / 256)), 256, 0, st>>>(part, tiles, n, out);
+  return hipGetLastError();
 }
 
 hipError_t launch_dequant_rows(const Nf4Dev& w0, const Nf4Dev* w1, const float* codebook0, const float* codebook1,

@@ -54,6 +54,12 @@ struct GemmArgs {
   // contiguous along the reduction), row stride ldw, rows [0, wrows) valid
   const uint16_t* wb;
   int64_t ldw, wrows;
+  // bgemm_kernel, SwiGLU forward only: the rank-r product H A^T of the down
+  // layer computed from the epilogue's H (A bf16 [r, Nout], r <= 32), written
+  // as per-column-tile fp32 partials part[tiles_n][M][r] (null: not computed)
+  const uint16_t* had_A;
+  int32_t had_r;
+  float* had_part;
 };
 
 // Skinny-M forward GEMM (qlora_skinny.hip): out[m, n] = sum_k X[m, k]
@@ -137,6 +143,8 @@ hipError_t launch_rmsnorm_bwd(const uint16_t* dY, const uint16_t* X, const uint1
 hipError_t launch_nf4_dequantize(const Nf4Dev& w, const float* codebook, int out_f32, void* out, hipStream_t st);
 hipError_t launch_qgemm(int mode, const GemmArgs& a, const qplan::GemmPlan& pl, hipStream_t st);
 hipError_t launch_bgemm(int mode, const GemmArgs& a, hipStream_t st);
+// Sum of the H A^T partials of launch_bgemm (MODE_FWD_SWIGLU) in tile order.
+hipError_t launch_had_finish(const float* part, int tiles, int64_t M, int r, float* out, hipStream_t st);
 // Output head + cross-entropy helpers (qlora_ce.hip).
 hipError_t launch_ce_count(const int32_t* targets, int64_t T, int64_t V, int32_t ignore, int32_t* n_valid,
                            hipStream_t st);

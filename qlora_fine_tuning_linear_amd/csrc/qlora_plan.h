@@ -180,6 +180,7 @@ inline LinearWs linear_ws(int64_t M, int64_t N, int64_t K, int r) {
 struct MlpWs {
   size_t fwd_H, fwd_down;                            // H bf16 [M, I], down-proj partials
   size_t bwd_Td, bwd_dG, bwd_dU, bwd_Tg, bwd_Tu, bwd_BT, bwd_down, bwd_grad;
+  size_t fwd_had;                                    // H A_d^T column-tile partials (bgemm, r_d <= 32)
   size_t fwd_wbuf, bwd_wbuf;                         // bf16 weight copies (bgemm only), at the end
   size_t fwd_total, bwd_total, total;
 };
@@ -198,7 +199,8 @@ inline MlpWs mlp_ws(int64_t M, int64_t D, int64_t I, int rg, int ru, int rd) {
     w.fwd_wbuf = align256(gu > dn ? gu : dn);
     w.bwd_wbuf = align256((size_t)2 * I * D * 2);
   }
-  w.fwd_total = w.fwd_H + w.fwd_down + w.fwd_wbuf;
+  if (use_bgemm(M) && rd <= 32) w.fwd_had = align256((size_t)cdiv(I, 128) * M * rd * 4);
+  w.fwd_total = w.fwd_H + w.fwd_down + w.fwd_had + w.fwd_wbuf;
 
   w.bwd_Td = align256((size_t)M * rd * 4);
   w.bwd_dG = align256((size_t)M * I * 2);
