@@ -67,6 +67,12 @@ CASES = [
     synth.LinearCfg("m50_640x4096_r16", M=50, K=640, N=4096, r=16, alpha=16.0, dq_group=256),
     synth.LinearCfg("m7_8192x1024_r32", M=7, K=8192, N=1024, r=32, alpha=8.0, dq_group=0),
     synth.LinearCfg("m64_1024x512_r65", M=64, K=1024, N=512, r=65, alpha=13.0, dq_group=0),
+    # skinny forward with 4, 7 and 8 frags of 16 rows per workgroup: tile
+    # counts that are not a multiple of 4, ragged rows and tokens, and two
+    # reduction splits forced by the absmax staging limit (128 tiles > 124)
+    synth.LinearCfg("m64_640x9216_r32", M=64, K=640, N=9216, r=32, alpha=32.0, dq_group=0),
+    synth.LinearCfg("m40_1088x16448_r16", M=40, K=1088, N=16448, r=16, alpha=16.0, dq_group=256),
+    synth.LinearCfg("m16_8192x32768_r8_split", M=16, K=8192, N=32768, r=8, alpha=16.0, dq_group=0),
 ]
 
 
