@@ -9,6 +9,7 @@ The argument-validation unit is plain C++ compiled by the host compiler.
 import os
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
@@ -25,21 +26,24 @@ HIP_FLAGS = [
 ]
 
 
+SOURCES = ("qlora_kernels.hip", "qlora_bgemm.hip", "qlora_skinny.hip", "qlora_merge.hip", "qlora_rmsnorm.hip",
+           "qlora_ce.hip", "qlora_api.hip")
+
+
 def build(verbose: bool = False) -> str:
     bdir = os.path.join(HERE, "_build")
     os.makedirs(bdir, exist_ok=True)
-    objs = []
-    for src in ("qlora_kernels.hip", "qlora_bgemm.hip", "qlora_skinny.hip", "qlora_merge.hip", "qlora_rmsnorm.hip",
-                "qlora_ce.hip",
-                "qlora_api.hip"):
+    jobs = []
+    for src in SOURCES:
         obj = os.path.join(bdir, src + ".o")
-        cmd = ["hipcc", "-c"] + HIP_FLAGS + [os.path.join(CSRC, src), "-o", obj]
-        _run(cmd, verbose)
-        objs.append(obj)
+        jobs.append((["hipcc", "-c"] + HIP_FLAGS + [os.path.join(CSRC, src), "-o", obj], obj))
     vobj = os.path.join(bdir, "qlora_validate.o")
-    _run(["g++", "-c", "-O2", "-std=c++17", "-fPIC", "-Wall", "-I" + INCLUDE, "-I" + CSRC,
-          os.path.join(CSRC, "qlora_validate.cpp"), "-o", vobj], verbose)
-    objs.append(vobj)
+    jobs.append((["g++", "-c", "-O2", "-std=c++17", "-fPIC", "-Wall", "-I" + INCLUDE, "-I" + CSRC,
+                  os.path.join(CSRC, "qlora_validate.cpp"), "-o", vobj], vobj))
+    # one compiler process per source file, at most as many as there are CPUs
+    with ThreadPoolExecutor(max_workers=max(1, min(len(jobs), os.cpu_count() or 1, 16))) as ex:
+        list(ex.map(lambda j: _run(j[0], verbose), jobs))
+    objs = [o for _, o in jobs]
     tmp = LIB + ".tmp%d" % os.getpid()
     _run(["hipcc", "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs, verbose)
     os.replace(tmp, LIB)
