@@ -88,6 +88,9 @@ def stored_traffic(key):
 
 
 KIND_OF_MODE = {0: "fwd", 1: "fwd_swiglu", 2: "bwd_dx", 3: "bwd_dh_swiglu", 4: "bwd_dx_dual"}
+# committed rocprofv3 kernel statistics of each workload's bench command
+PROFILE_OF_WORKLOAD = {"llama3_8b_mlp_m8192_r16": "kernel_stats_mlp_llama3_8b_m8192.md",
+                       "llama3_70b_mlp_m4096_r64_dq": "kernel_stats_mlp_llama3_70b_m4096_dq.md"}
 
 
 def kernel_key(csv_name):
@@ -147,6 +150,49 @@ def summarize_traffic(fetch_csv, write_csv, copy_mib, command):
     return written
 
 
+def step_spread(fwd, bwd, n):
+    """Median and p10 / p90 of n steps, each timed on its own with HIP events
+    around the forward and the backward (after the K steps of the headline,
+    which are timed as one block)."""
+    import statistics
+    import torch
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n + 1)]
+    torch.cuda.synchronize()
+    for i in range(n):
+        ev[2 * i].record()
+        fwd()
+        ev[2 * i + 1].record()
+        bwd()
+    ev[2 * n].record()
+    torch.cuda.synchronize()
+    f = [ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(n)]
+    b = [ev[2 * i + 1].elapsed_time(ev[2 * i + 2]) for i in range(n)]
+    t = [x + y for x, y in zip(f, b)]
+
+    def pct(v):
+        q = statistics.quantiles(v, n=10, method="inclusive")
+        return {"median": round(statistics.median(v), 4), "p10": round(q[0], 4), "p90": round(q[-1], 4)}
+
+    return {"steps": n, "fwd_bwd_ms": pct(t), "fwd_ms": pct(f), "bwd_ms": pct(b)}
+
+
+def profiled_avg_ms(profile, kernel_prefix):
+    """Average duration (ms) of the kernel whose name starts with kernel_prefix
+    in a committed rocprofv3 kernel-statistics summary (profiles/*.md), or None."""
+    import re
+    path = os.path.join(ROOT, "profiles", profile)
+    if not os.path.exists(path):
+        return None
+    for line in open(path):
+        m = re.match(r"\|\s*`([^`]*)`\s*\|\s*(\d+)\s*\|\s*([0-9.]+)\s*\|", line)
+        if m and re.sub(r"^\w+::", "", m.group(1)).startswith(kernel_prefix):
+            return float(m.group(3)) / 1000.0
+    return None
+
+
+MODE_OF_KIND = {v: k for k, v in KIND_OF_MODE.items()}
+
+
 def gemm_flops(kind, M, D, I, r):
     """Algorithmic FLOPs of one launch of each GEMM kind of the MLP step
     (main product + the rank-r LoRA epilogue product)."""
@@ -203,6 +249,8 @@ def mlp_step_bench(q, synth, steps, warmup, idx=2):
         torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = e0.elapsed_time(e1) / steps
+    spread = step_spread(lambda: q.qlora_mlp_fwd(P, X, Y=Y, saved=S, ws=ws),
+                         lambda: q.qlora_mlp_bwd(P, dY, X, S, dX=dX, grads=grads, ws=ws), max(100, steps))
     per_kind, kname = {}, {}
     for kind, kernel, d in trace.launches():
         per_kind.setdefault(kind, []).append(d)
@@ -219,7 +267,7 @@ def mlp_step_bench(q, synth, steps, warmup, idx=2):
                                           "tflops": gemm_flops(k, M, D, I, r) / (sum(v) / len(v) * 1e-3) / 1e12}
                for k, v in per_kind.items()}
     return dict(cfg=cfg, ms=ms, wall=wall, flops=flops, dom=dom, dom_kernel=dom_kernel, dom_ms=dom_ms,
-                dom_flops=dom_flops, achieved=achieved, traffic=traffic, kernels=kernels)
+                dom_flops=dom_flops, achieved=achieved, traffic=traffic, kernels=kernels, spread=spread)
 
 
 def linear_bench(q, synth, idx, steps, warmup, rotate=1):
@@ -248,9 +296,14 @@ def linear_bench(q, synth, idx, steps, warmup, rotate=1):
     ws = torch.empty(q.qlora_linear_workspace_bytes(Ls[0], M), dtype=torch.uint8, device="cuda")
 
     def step(i):
-        L = Ls[i % len(Ls)]
-        q.qlora_linear_fwd(L, X, Y=Y, XA=XA, ws=ws)
-        q.qlora_linear_bwd(L, dY, X, XA, dX=dX, dA=dA, dB=dB, ws=ws)
+        # With several weight copies the forward and the backward of a step use
+        # different ones, and a copy comes back only after the others have
+        # streamed: nothing of it is left in the 256 MB last-level cache, as in
+        # training, where every other layer runs between a layer's forward and
+        # its backward.  The copies hold the same values.
+        Lf, Lb = Ls[(2 * i) % len(Ls)], Ls[(2 * i + 1) % len(Ls)]
+        q.qlora_linear_fwd(Lf, X, Y=Y, XA=XA, ws=ws)
+        q.qlora_linear_bwd(Lb, dY, X, XA, dX=dX, dA=dA, dB=dB, ws=ws)
 
     for i in range(warmup):
         step(i)
@@ -275,7 +328,9 @@ def linear_bench(q, synth, idx, steps, warmup, rotate=1):
                 frac_bf16_peak=flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
                 tokens_per_s=M / (ms * 1e-3), algorithmic_bytes=total_bytes,
                 hbm_gbs=total_bytes / (ms * 1e-3) / 1e9,
-                frac_hbm_peak=total_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, weight_copies=rotate)
+                frac_hbm_peak=total_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, weight_copies=rotate,
+                mall_defeated=("forward and backward on different weight copies, each reused after %d others"
+                               % (rotate - 1)) if rotate > 1 else None)
 
 
 def merge_bench(q, synth, steps, warmup, copies=3):
@@ -474,10 +529,32 @@ def cpu_baseline(synth, target_s):
     inp_rows = synth.mlp_inputs(cfg, synth.seed_of(2), M=m, with_weights=False)
     t = run(m)
     flops = 12 * m * cfg.D * cfg.I + 18 * m * cfg.r * (cfg.D + cfg.I)
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "cpu_model": model, "host_cpus": os.cpu_count(),
             "sample": "first %d of %d tokens of %s, fwd+bwd, fp64 numpy oracle (weights dequantized by the "
                       "oracle), %.1f s" % (m, cfg.M, cfg.name, t),
             "tokens_per_s": m / t}
+
+
+def mlp_line(cfg, r):
+    """Secondary line of an MLP workload: fwd+bwd time, TFLOP/s, fraction of
+    the bf16 peak, tokens/s, and its dominant GEMM kernel."""
+    return {"workload": cfg.name, "ms_per_step": round(r["ms"], 4),
+            "tflops": round(r["flops"] / (r["ms"] * 1e-3) / 1e12, 2),
+            "frac_bf16_peak": round(r["flops"] / (r["ms"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "tokens_per_s": round(cfg.M / (r["ms"] * 1e-3), 1),
+            "dominant_kernel": r["dom_kernel"], "dominant_avg_ms": round(r["dom_ms"], 4),
+            "dominant_frac_bf16_peak": round(r["achieved"] / BF16_PEAK_TFLOPS, 4),
+            "spread": r["spread"],
+            "kernels": {k: {kk: round(vv, 4) for kk, vv in v.items()} for k, v in r["kernels"].items()}}
 
 
 def main():
@@ -517,12 +594,7 @@ def main():
         a.only = int(a.only)
         cfg = synth.CONFIGS[a.only]
         if cfg.kind == "mlp":
-            r = mlp_step_bench(q, synth, a.steps, a.warmup, idx=a.only)
-            line = {"workload": cfg.name, "ms_per_step": round(r["ms"], 4),
-                    "tflops": round(r["flops"] / (r["ms"] * 1e-3) / 1e12, 2),
-                    "frac_bf16_peak": round(r["flops"] / (r["ms"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
-                    "tokens_per_s": round(cfg.M / (r["ms"] * 1e-3), 1),
-                    "kernels": {k: {kk: round(vv, 4) for kk, vv in v.items()} for k, v in r["kernels"].items()}}
+            line = mlp_line(cfg, mlp_step_bench(q, synth, a.steps, a.warmup, idx=a.only))
         else:
             s = linear_bench(q, synth, a.only, a.steps, a.warmup, rotate=4 if a.only == 4 else 1)
             line = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in s.items()}
@@ -553,11 +625,23 @@ def main():
                      "achieved": round(r["achieved"], 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(r["achieved"] / BF16_PEAK_TFLOPS, 4), "traffic": r["traffic"],
                      "flops_per_launch": r["dom_flops"], "avg_launch_ms": round(r["dom_ms"], 4)},
+        "spread": r["spread"],
         "kernels": {k: {kk: round(vv, 4) for kk, vv in v.items()} for k, v in r["kernels"].items()},
     }
+    # the same kernel's average in the committed rocprofv3 kernel statistics of
+    # this workload, and the fraction it gives
+    prof = profiled_avg_ms(PROFILE_OF_WORKLOAD.get(cfg.name, ""),
+                           "bgemm_kernel<%d," % MODE_OF_KIND[r["dom"]])
+    if prof:
+        out["roofline"]["profiled_avg_launch_ms"] = round(prof, 4)
+        out["roofline"]["profiled_frac"] = round(r["dom_flops"] / (prof * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)
+        out["roofline"]["profile"] = "profiles/" + PROFILE_OF_WORKLOAD[cfg.name]
     if not a.no_secondary:
         sec = []
-        for idx, steps, rot in ((1, max(5, a.steps), 1), (4, max(10, a.steps), 4)):
+        log("secondary: %s" % synth.CONFIGS[3].name)
+        sec.append(mlp_line(synth.CONFIGS[3], mlp_step_bench(q, synth, max(5, a.steps // 2), min(a.warmup, 3),
+                                                             idx=3)))
+        for idx, steps, rot in ((0, max(20, a.steps), 1), (1, max(5, a.steps), 1), (4, max(10, a.steps), 4)):
             log("secondary: %s" % synth.CONFIGS[idx].name)
             s = linear_bench(q, synth, idx, steps, a.warmup, rotate=rot)
             sec.append({k: (round(v, 4) if isinstance(v, float) else v) for k, v in s.items()})
