@@ -24,7 +24,10 @@
  *   surface on a later synchronisation and map to QLORA_ERR_HIP when a
  *   launch itself reports an error.
  * - Gradients are written (overwritten), never accumulated.
- * - M (tokens) may be any value >= 0; M == 0 is a no-op that returns OK.
+ * - M (tokens) may be any value in [0, 2^31 - 1] (QLORA_ERR_INVALID_ARG
+ *   below, QLORA_ERR_UNSUPPORTED_SHAPE above); M == 0 is a no-op that
+ *   returns OK.  The *_workspace_bytes queries return 0 for arguments the
+ *   matching call would reject.
  * - Shapes: K % 64 == 0 and N % 64 == 0 (whole absmax blocks, whole tiles
  *   of 64), K, N <= 4194240 (a 256-row tile of a bf16 copy stays below
  *   2 GiB), 1 <= r <= 128, blocksize == 64, dq_group in {0, 256}.
@@ -106,7 +109,8 @@ typedef struct qlora_linear {
  * ("MLP SwiGLU" among the hand-derived kernels, "LLM Fine-Tuning in 2026",
  * section 2).  gate and up must have the same dq_group
  * (QLORA_ERR_UNSUPPORTED_SHAPE otherwise); r, alpha and the codebook buffer
- * may differ per layer.
+ * may differ per layer.  I <= 2097088 (the backward holds [W_g^T | W_u^T]
+ * as one bf16 copy of row stride 2I; QLORA_ERR_UNSUPPORTED_SHAPE otherwise).
  */
 typedef struct qlora_mlp {
   qlora_linear gate;
@@ -279,7 +283,7 @@ int rmsnorm_bwd(const void* dY, const void* X, const void* w, const float* rstd,
 /*
  * Workspace bytes qlora_linear_ce needs for T tokens, hidden size D, V classes
  * and the given chunk (0 when the shape is not supported): one chunk of
- * logits (min(chunk, T) * V bf16), T per-token fp32 losses and, with
+ * logits (min(chunk, T) * V fp32), T per-token fp32 losses and, with
  * want_dx != 0, the head transposed (V * D bf16) plus the fp32 partials of
  * the dX product.
  */
@@ -293,7 +297,7 @@ size_t qlora_linear_ce_workspace_bytes(int64_t T, int64_t D, int64_t V, int64_t 
  * With n the number of tokens whose target is a class index in [0, V) other
  * than ignore_index (any other value marks a token without a target):
  *
- *   z_t   = W x_t                  V logits, fp32 accumulation, rounded to bf16
+ *   z_t   = W x_t                  V logits, fp32 accumulation, kept in fp32
  *   l_t   = logsumexp(z_t) - z_t[target_t]     (fp32; 0 without a target)
  *   loss  = (1/n) sum_t l_t                     (fixed-order sum; 0 if n == 0)
  *   dX_t  = sum_v g_tv W_v,  g_tv = bf16((softmax(z_t)_v - [v == target_t]) / n)
@@ -309,7 +313,7 @@ size_t qlora_linear_ce_workspace_bytes(int64_t T, int64_t D, int64_t V, int64_t 
  *   ws         ws_bytes >= qlora_linear_ce_workspace_bytes(T, D, V, chunk,
  *              dX != NULL); with dX the head is transposed into it once per
  *              call (V * D * 2 bytes)
- * D and V multiples of 64, D <= 65536, V <= 4194240
+ * D and V multiples of 64, D <= 65536, V <= 2097088
  * (QLORA_ERR_UNSUPPORTED_SHAPE otherwise).  T == 0 writes loss = 0 and needs
  * no workspace.  All pointers 16-byte aligned.  Results are bitwise
  * reproducible from run to run.
@@ -380,6 +384,17 @@ int qlora_mlp_fwd(const qlora_mlp* P, const void* X, int64_t M, void* Y,
 int qlora_mlp_bwd(const qlora_mlp* P, const void* dY, const void* X,
                   const qlora_mlp_saved* S, int64_t M, void* dX, const qlora_mlp_grads* G_out,
                   void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * qlora_debug_force_arch: a test aid for the device check.  With a non-NULL
+ * name, every entry point treats the current device as having that
+ * gcnArchName: any name other than "gfx950..." makes each call that would
+ * launch work return QLORA_ERR_UNSUPPORTED_DEVICE after validating its
+ * arguments and before enqueuing anything.  NULL restores the query of the
+ * real device.  Process-wide; set it while no other thread calls the library.
+ * Returns QLORA_ERR_INVALID_ARG for a name of 64 characters or more.
+ */
+int qlora_debug_force_arch(const char* gcn_arch_name);
 
 /*
  * qlora_trace_install: optional launch tracing, a profiling aid (off by

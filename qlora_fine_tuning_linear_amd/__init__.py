@@ -29,7 +29,7 @@ EXPORTED = (
     "qlora_mlp_workspace_bytes", "qlora_mlp_fwd", "qlora_mlp_bwd", "qlora_trace_install", "qlora_merge",
     "rmsnorm_fwd", "rmsnorm_bwd", "rmsnorm_bwd_workspace_bytes",
     "qlora_grouped_workspace_bytes", "qlora_grouped_fwd", "qlora_grouped_bwd",
-    "qlora_linear_ce_workspace_bytes", "qlora_linear_ce",
+    "qlora_linear_ce_workspace_bytes", "qlora_linear_ce", "qlora_debug_force_arch",
 )
 
 
@@ -108,6 +108,7 @@ def load_library(path: str = LIB_PATH):
         "qlora_grouped_bwd": (ctypes.c_int, [P(CGrouped), vp, vp, vp, i64, vp, vp, P(vp), vp, sz, vp]),
         "qlora_linear_ce_workspace_bytes": (sz, [i64, i64, i64, i64, i32]),
         "qlora_linear_ce": (ctypes.c_int, [vp, i64, i64, vp, i64, vp, i32, i64, vp, vp, vp, vp, sz, vp]),
+        "qlora_debug_force_arch": (ctypes.c_int, [ctypes.c_char_p]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -229,6 +230,12 @@ def qlora_linear_fwd(L: QLoraLinear, X: torch.Tensor, Y=None, XA=None, ws=None):
                               ws.numel(), _stream(dev))
     _check("qlora_linear_fwd", st)
     return Y, XA
+
+
+def debug_force_arch(name: Optional[str]):
+    """qlora_debug_force_arch: pretend every device is `name` (None: the real one)."""
+    _check("qlora_debug_force_arch",
+           load_library().qlora_debug_force_arch(None if name is None else name.encode()))
 
 
 def qlora_linear_bwd(L: QLoraLinear, dY: torch.Tensor, X: torch.Tensor, XA: torch.Tensor, dX=None, dA=None,

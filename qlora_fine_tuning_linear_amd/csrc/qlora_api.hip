@@ -14,11 +14,17 @@ namespace {
 
 // Per-device answer to "is this a gfx950": 0 unknown, 1 yes, 2 no.
 std::atomic<int> g_dev_ok[64];
+// qlora_debug_force_arch: when set, the architecture name every device is
+// taken to have (0: the device's own, the normal case).
+std::atomic<int> g_arch_forced{0};
+char g_arch_name[64];
 
 int check_device() {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return QLORA_ERR_HIP;
   if (dev < 0 || dev >= 64) return QLORA_ERR_UNSUPPORTED_DEVICE;
+  if (g_arch_forced.load(std::memory_order_acquire))
+    return strncmp(g_arch_name, "gfx950", 6) == 0 ? QLORA_OK : QLORA_ERR_UNSUPPORTED_DEVICE;
   int s = g_dev_ok[dev].load(std::memory_order_relaxed);
   if (s == 0) {
     hipDeviceProp_t prop;
@@ -155,6 +161,19 @@ int qlora_trace_install(void** begin_events, void** end_events, int32_t* kinds, 
   return QLORA_OK;
 }
 
+int qlora_debug_force_arch(const char* gcn_arch_name) {
+  if (!gcn_arch_name) {
+    g_arch_forced.store(0, std::memory_order_release);
+    return QLORA_OK;
+  }
+  if (strlen(gcn_arch_name) >= sizeof(g_arch_name)) return QLORA_ERR_INVALID_ARG;
+  g_arch_forced.store(0, std::memory_order_release);
+  strncpy(g_arch_name, gcn_arch_name, sizeof(g_arch_name) - 1);
+  g_arch_name[sizeof(g_arch_name) - 1] = 0;
+  g_arch_forced.store(1, std::memory_order_release);
+  return QLORA_OK;
+}
+
 int nf4_quantize(const float* W, int64_t N, int64_t K, const float* codebook16, int32_t blocksize, int32_t dq_group,
                  uint8_t* codes, float* absmax, uint8_t* absmax_q, float* absmax_scale, void* stream) {
   QTRY(qv_quantize(W, N, K, codebook16, blocksize, dq_group, codes, absmax, absmax_q, absmax_scale));
@@ -279,7 +298,7 @@ int qlora_linear_ce(const void* X, int64_t T, int64_t D, const void* W, int64_t 
   char* b = bytes(ws);
   int32_t* nvalid = reinterpret_cast<int32_t*>(b);
   float* tl = token_loss ? token_loss : reinterpret_cast<float*>(b + w.nvalid);
-  uint16_t* z = reinterpret_cast<uint16_t*>(b + w.nvalid + w.tloss);
+  float* z = reinterpret_cast<float*>(b + w.nvalid + w.tloss);
   uint16_t* wt = reinterpret_cast<uint16_t*>(b + w.nvalid + w.tloss + w.logits);
   float* part = reinterpret_cast<float*>(b + w.nvalid + w.tloss + w.logits + w.wt);
   QHIP(launch_ce_count(targets, T, V, ignore_index, nvalid, st));
@@ -287,7 +306,7 @@ int qlora_linear_ce(const void* X, int64_t T, int64_t D, const void* W, int64_t 
   if (want_dx) QHIP(launch_transpose_bf16(u16(W), V, D, wt, st));
   for (int64_t c0 = 0; c0 < T; c0 += w.C) {
     const int64_t C = (T - c0) < w.C ? (T - c0) : w.C;
-    // logits of the chunk: z = X_c W^T, bf16 [C, V]
+    // logits of the chunk: z = X_c W^T, fp32 [C, V]
     GemmArgs a = gemm_args();
     a.act0 = u16(X) + c0 * D;
     a.M = C;
@@ -296,14 +315,17 @@ int qlora_linear_ce(const void* X, int64_t T, int64_t D, const void* W, int64_t 
     a.wb = u16(W);
     a.ldw = D;
     a.wrows = V;
-    a.out0 = z;
+    a.partial = z;
+    a.out_f32 = 1;
     QHIP(traced_gemm_b(MODE_FWD, a, st));
-    // loss terms; with dX wanted, z becomes (softmax - onehot) / n
+    // loss terms; with dX wanted, each row of z becomes the bf16 row
+    // (softmax - onehot) / n (row stride 2V bf16 elements)
     QHIP(launch_ce_rows(z, C, V, targets + c0, ignore_index, nvalid, want_dx ? 1 : 0, tl + c0, st));
     if (!want_dx) continue;
-    // dX_c = z W, the vocabulary reduction split into fp32 partials
+    // dX_c = g W, the vocabulary reduction split into fp32 partials
     GemmArgs g = gemm_args();
-    g.act0 = z;
+    g.act0 = reinterpret_cast<const uint16_t*>(z);
+    g.lda = 2 * V;
     g.M = C;
     g.Nout = D;
     g.Kred0 = V;
@@ -526,9 +548,17 @@ int qlora_mlp_fwd(const qlora_mlp* P, const void* X, int64_t M, void* Y, const q
   uint16_t* wbuf =
       w.fwd_wbuf ? reinterpret_cast<uint16_t*>(bytes(ws) + w.fwd_H + w.fwd_down + w.fwd_had) : nullptr;
 
-  // XA_g | XA_u in one pass over X
-  QHIP(launch_lora_down(u16(X), M, D, u16(P->gate.A), P->gate.r, u16(P->up.A), P->up.r, S->XA_g, S->XA_u,
-                        qplan::plan_down_splits(M, D), down_part, st));
+  // XA_g | XA_u in one pass over X (the down-projection kernels take a
+  // combined rank of at most 128; above that, one pass per layer)
+  if (P->gate.r + P->up.r <= 128) {
+    QHIP(launch_lora_down(u16(X), M, D, u16(P->gate.A), P->gate.r, u16(P->up.A), P->up.r, S->XA_g, S->XA_u,
+                          qplan::plan_down_splits(M, D), down_part, st));
+  } else {
+    QHIP(launch_lora_down(u16(X), M, D, u16(P->gate.A), P->gate.r, nullptr, 0, S->XA_g, nullptr,
+                          qplan::plan_down_splits(M, D), down_part, st));
+    QHIP(launch_lora_down(u16(X), M, D, u16(P->up.A), P->up.r, nullptr, 0, S->XA_u, nullptr,
+                          qplan::plan_down_splits(M, D), down_part, st));
+  }
   // G, U = gate/up(X) and H = silu(G) * U in one dual GEMM
   {
     GemmArgs a = gemm_args();

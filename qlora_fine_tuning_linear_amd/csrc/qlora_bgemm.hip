@@ -297,6 +297,7 @@ __global__ __launch_bounds__(512) void bgemm_kernel(GemmArgs p) {
   const int64_t n0 = tn * BNO;  // first output column
   const int64_t wr0 = tn * BN;  // first weight row of the tile
   const int KT0 = (int)(p.Kred0 / 64);
+  const int64_t lda = p.lda > 0 ? p.lda : p.Kred0;  // activation row stride
   // Reduction split (plain forward mode only, gridDim.y > 1): workgroup
   // (x, y) takes reduction tiles [kb, kb + KT) and writes fp32 partials.
   const int kb = gridDim.y > 1 ? (int)blockIdx.y * p.ktiles_per_split : 0;
@@ -314,7 +315,7 @@ __global__ __launch_bounds__(512) void bgemm_kernel(GemmArgs p) {
     if (ra >= p.M) ra = p.M - 1;
     int64_t rb = wr0 + row;
     if (rb >= p.wrows) rb = p.wrows - 1;
-    aoff[i] = (uint32_t)((ra - m0) * p.Kred0) + (uint32_t)c * 8;
+    aoff[i] = (uint32_t)((ra - m0) * lda) + (uint32_t)c * 8;
     boff[i] = (uint32_t)((rb - wr0) * p.ldw) + (uint32_t)c * 8;
   }
   // Buffer resources over the tile's rows: the dual-reduction GEMM reads
@@ -325,9 +326,9 @@ __global__ __launch_bounds__(512) void bgemm_kernel(GemmArgs p) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0,
                                              (int)(bytes < 0x7FFFFFFF ? bytes : 0x7FFFFFFF), 0x00020000);
   };
-  const int64_t abytes = (p.M - m0) * p.Kred0 * 2;
-  const __amdgpu_buffer_rsrc_t ra0 = rsrc(p.act0 + m0 * p.Kred0, abytes);
-  const __amdgpu_buffer_rsrc_t ra1 = rsrc((p.act1 ? p.act1 : p.act0) + m0 * p.Kred0, abytes);
+  const int64_t abytes = (p.M - m0) * lda * 2;
+  const __amdgpu_buffer_rsrc_t ra0 = rsrc(p.act0 + m0 * lda, abytes);
+  const __amdgpu_buffer_rsrc_t ra1 = rsrc((p.act1 ? p.act1 : p.act0) + m0 * lda, abytes);
   const __amdgpu_buffer_rsrc_t rb = rsrc(p.wb + wr0 * p.ldw, (p.wrows - wr0) * p.ldw * 2);
 
   // 8 direct loads of one operand half of tile kt (clamped to the last tile:
@@ -497,7 +498,7 @@ __global__ __launch_bounds__(512) void bgemm_kernel(GemmArgs p) {
   }
   stage_barrier();  // every wave is done reading operands: LDS is free
   if constexpr (MODE == MODE_FWD) {
-    if (gridDim.y > 1) {
+    if (gridDim.y > 1 || p.out_f32) {  // fp32 split partials, or fp32 results (partial[0])
       gemm_epilogue<MODE, 2, WN, FM, FN, true>(p, acc, arow, m0, n0, wm, wn, l32, g);
       return;
     }

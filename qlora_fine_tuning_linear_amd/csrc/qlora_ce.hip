@@ -2,8 +2,8 @@
 // step of "LLM Fine-Tuning in 2026: Unsloth vs QLoRA vs Liger-Kernel"
 // (section 3), computed one token chunk at a time so that no [tokens, vocab]
 // logit matrix is ever held.  Per chunk the entry point runs the bf16 GEMM
-// for the chunk's logits, ce_rows_kernel for the loss terms and the logit
-// gradient (in place), and the bf16 GEMM again (reduction over the vocabulary,
+// for the chunk's fp32 logits, ce_rows_kernel for the loss terms and the
+// bf16 logit gradient (in place), and the bf16 GEMM again (reduction over the vocabulary,
 // split into fp32 partials) for dX.  The helpers here:
 //   * ce_count_kernel      - number of tokens that carry a target;
 //   * transpose_bf16_kernel - the head [V, D] -> [D, V], so that the dX product
@@ -80,36 +80,35 @@ __device__ __forceinline__ void lse_combine(float& m, float& s, float m2, float 
   m = mm;
 }
 
-// One workgroup of 256 threads per token row of the chunk's logits z [rows, V]
-// (bf16, V % 8 == 0).  Thread i takes the 16-byte chunks i, i + 256, ...;
-// partial (max, sum) pairs are combined across lanes with a fixed xor pattern
-// and across the four waves in wave order, so the result does not depend on
-// timing.  Then token_loss[row] = lse - z[target] (0 without a target) and,
-// with want_grad, z is overwritten by bf16((softmax(z) - onehot) / n) (0 rows
-// for tokens without a target).
-__global__ __launch_bounds__(256) void ce_rows_kernel(uint16_t* __restrict__ z, int64_t V,
+// One workgroup of 256 threads per token row of the chunk's logits z
+// [rows, V] (fp32, V % 8 == 0).  Thread i takes the 32-byte chunks i, i + 256,
+// ...; partial (max, sum) pairs are combined across lanes with a fixed xor
+// pattern and across the four waves in wave order, so the result does not
+// depend on timing.  Then token_loss[row] = lse - z[target] (0 without a
+// target) and, with want_grad, bf16((softmax(z) - onehot) / n) (0 rows for
+// tokens without a target) is written over the first half of the row's bytes
+// (a bf16 row of stride 2V elements).  That pass goes in rounds of 256 chunks
+// with a barrier between the reads and the writes of a round: the 16-byte
+// bf16 chunk c lands in bytes [16c, 16c + 16), inside fp32 chunks that every
+// thread has read by then (round k writes what rounds <= k read).
+__global__ __launch_bounds__(256) void ce_rows_kernel(float* __restrict__ z, int64_t V,
                                                       const int32_t* __restrict__ targets, int32_t ignore,
                                                       const int32_t* __restrict__ n_valid, int want_grad,
                                                       float* __restrict__ token_loss) {
   __shared__ float wm[4], wsum[4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t row = blockIdx.x;
-  uint16_t* zr = z + row * V;
+  float* zr = z + row * V;
   const int32_t tgt = targets[row];
   const bool valid = ce_valid(tgt, V, ignore);
-  // the target's logit, read before any thread overwrites the row
-  const float zt = valid ? bf16_to_f32(zr[tgt]) : 0.0f;
+  const float zt = valid ? zr[tgt] : 0.0f;
   const int64_t nch = V / 8;
 
   float m = 0.0f, s = 0.0f;
   for (int64_t c = tid; c < nch; c += 256) {
-    const u32x4 v = *reinterpret_cast<const u32x4*>(zr + c * 8);
-    float x[8];
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      x[2 * d] = bf16_lo(v[d]);
-      x[2 * d + 1] = bf16_hi(v[d]);
-    }
+    const f32x4 a = *reinterpret_cast<const f32x4*>(zr + c * 8);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(zr + c * 8 + 4);
+    const float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
     float cm = x[0];
 #pragma unroll
     for (int e = 1; e < 8; ++e) cm = fmaxf(cm, x[e]);
@@ -137,21 +136,30 @@ __global__ __launch_bounds__(256) void ce_rows_kernel(uint16_t* __restrict__ z, 
 
   const int32_t n = *n_valid;
   const float inv_n = (valid && n > 0) ? 1.0f / (float)n : 0.0f;
-  for (int64_t c = tid; c < nch; c += 256) {
-    const u32x4 v = *reinterpret_cast<const u32x4*>(zr + c * 8);
-    u32x4 o;
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      float g[2];
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const float x = e ? bf16_hi(v[d]) : bf16_lo(v[d]);
-        const int64_t col = c * 8 + 2 * d + e;
-        g[e] = (__expf(x - lse) - (col == tgt ? 1.0f : 0.0f)) * inv_n;
-      }
-      o[d] = pack_bf16x2(g[0], g[1]);
+  uint16_t* gr = reinterpret_cast<uint16_t*>(zr);
+  for (int64_t c0 = 0; c0 < nch; c0 += 256) {
+    const int64_t c = c0 + tid;
+    f32x4 a{}, b{};
+    if (c < nch) {
+      a = *reinterpret_cast<const f32x4*>(zr + c * 8);
+      b = *reinterpret_cast<const f32x4*>(zr + c * 8 + 4);
     }
-    *reinterpret_cast<u32x4*>(zr + c * 8) = o;
+    __syncthreads();  // every read of this round is done before its writes
+    if (c < nch) {
+      const float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+      u32x4 o;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        float g[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int64_t col = c * 8 + 2 * d + e;
+          g[e] = (__expf(x[2 * d + e] - lse) - (col == tgt ? 1.0f : 0.0f)) * inv_n;
+        }
+        o[d] = pack_bf16x2(g[0], g[1]);
+      }
+      *reinterpret_cast<u32x4*>(gr + c * 8) = o;
+    }
   }
 }
 
@@ -191,7 +199,7 @@ hipError_t launch_transpose_bf16(const uint16_t* in, int64_t V, int64_t D, uint1
   return hipGetLastError();
 }
 
-hipError_t launch_ce_rows(uint16_t* z, int64_t rows, int64_t V, const int32_t* targets, int32_t ignore,
+hipError_t launch_ce_rows(float* z, int64_t rows, int64_t V, const int32_t* targets, int32_t ignore,
                           const int32_t* n_valid, int want_grad, float* token_loss, hipStream_t st) {
   if (rows == 0) return hipSuccess;
   ce_rows_kernel<<<dim3((unsigned)rows), 256, 0, st>>>(z, V, targets, ignore, n_valid, want_grad, token_loss);

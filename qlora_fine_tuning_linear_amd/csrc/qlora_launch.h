@@ -60,6 +60,11 @@ struct GemmArgs {
   const uint16_t* had_A;
   int32_t had_r;
   float* had_part;
+  // bgemm_kernel only: row stride of act0 / act1 in elements (0: Kred0), and,
+  // in the plain forward mode, fp32 results written to partial as [M][Nout]
+  // instead of bf16 to out0
+  int64_t lda;
+  int32_t out_f32;
 };
 
 // Skinny-M forward GEMM (qlora_skinny.hip): out[m, n] = sum_k X[m, k]
@@ -149,7 +154,9 @@ hipError_t launch_had_finish(const float* part, int tiles, int64_t M, int r, flo
 hipError_t launch_ce_count(const int32_t* targets, int64_t T, int64_t V, int32_t ignore, int32_t* n_valid,
                            hipStream_t st);
 hipError_t launch_transpose_bf16(const uint16_t* in, int64_t V, int64_t D, uint16_t* out, hipStream_t st);
-hipError_t launch_ce_rows(uint16_t* z, int64_t rows, int64_t V, const int32_t* targets, int32_t ignore,
+// z: fp32 logits [rows][V]; with want_grad each row's first 2V bytes are
+// overwritten by the bf16 logit gradient (row stride 2V bf16 elements).
+hipError_t launch_ce_rows(float* z, int64_t rows, int64_t V, const int32_t* targets, int32_t ignore,
                           const int32_t* n_valid, int want_grad, float* token_loss, hipStream_t st);
 hipError_t launch_ce_loss(const float* token_loss, int64_t T, const int32_t* n_valid, float* loss, hipStream_t st);
 // bf16 copy of the dequantized weight(s) for bgemm_kernel.

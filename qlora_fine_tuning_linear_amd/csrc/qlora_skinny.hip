@@ -18,8 +18,8 @@
 //   * the activation tile of each reduction tile is read by exactly one wave
 //     (from L2, where the 64-token activation matrix stays resident) as the
 //     A operand (rows = tokens);
-//   * codes and activations of the next three tiles are in flight while the
-//     current one is expanded and multiplied (a ring of four register sets);
+//   * codes and activations of the next two tiles are in flight while the
+//     current one is expanded and multiplied (a ring of three register sets);
 //     the block absmax of the workgroup's rows and tiles is staged in LDS
 //     once, as fp32.
 // The four per-wave partial tiles are summed in LDS in wave order (results

@@ -12,6 +12,12 @@
 namespace {
 
 constexpr int64_t kMaxDim = ((int64_t)1 << 22) - 64;  // 4194240
+// The MLP backward reads [W_g^T | W_u^T] as one bf16 copy with row stride 2I,
+// and the cross-entropy's dX product its logit gradient with row stride 2V: a
+// 256-row tile of either must stay below 2 GiB as well.
+constexpr int64_t kMaxMlpI = (kMaxDim / 2) / 64 * 64;  // 2097088
+// Tokens per call: keeps every workspace size and launch grid in range.
+constexpr int64_t kMaxTokens = ((int64_t)1 << 31) - 1;
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -112,6 +118,7 @@ int qv_grouped_dB(const qlora_grouped* Q, void* const* dB) {
 
 static int check_rms(int64_t M, int64_t D) {
   if (M < 0) return QLORA_ERR_INVALID_ARG;
+  if (M > kMaxTokens) return QLORA_ERR_UNSUPPORTED_SHAPE;
   if (D < 8 || D > 8192 || D % 8 != 0) return QLORA_ERR_UNSUPPORTED_SHAPE;
   return QLORA_OK;
 }
@@ -155,6 +162,7 @@ int qv_linear_fwd(const qlora_linear* L, const void* X, int64_t M, const void* Y
   int st = check_linear(L);
   if (st) return st;
   if (M < 0) return QLORA_ERR_INVALID_ARG;
+  if (M > kMaxTokens) return QLORA_ERR_UNSUPPORTED_SHAPE;
   if (M == 0) return QLORA_OK;
   if ((st = check_ptr(X)) || (st = check_ptr(Y)) || (st = check_ptr(XA))) return st;
   const qplan::LinearWs w = qplan::linear_ws(M, L->W0.N, L->W0.K, L->r);
@@ -166,6 +174,7 @@ int qv_linear_bwd(const qlora_linear* L, const void* dY, const void* X, const fl
   int st = check_linear(L);
   if (st) return st;
   if (M < 0) return QLORA_ERR_INVALID_ARG;
+  if (M > kMaxTokens) return QLORA_ERR_UNSUPPORTED_SHAPE;
   if ((st = check_ptr(dA)) || (st = check_ptr(dB))) return st;
   if (M == 0) return QLORA_OK;
   if ((st = check_ptr(dY)) || (st = check_ptr(X)) || (st = check_ptr(XA)) || (st = check_ptr(dX))) return st;
@@ -181,6 +190,7 @@ static int check_mlp(const qlora_mlp* P) {
   if (P->up.W0.N != I || P->up.W0.K != D) return QLORA_ERR_UNSUPPORTED_SHAPE;
   if (P->down.W0.N != D || P->down.W0.K != I) return QLORA_ERR_UNSUPPORTED_SHAPE;
   if (P->gate.W0.dq_group != P->up.W0.dq_group) return QLORA_ERR_UNSUPPORTED_SHAPE;
+  if (I > kMaxMlpI) return QLORA_ERR_UNSUPPORTED_SHAPE;
   return QLORA_OK;
 }
 
@@ -189,6 +199,7 @@ int qv_mlp_fwd(const qlora_mlp* P, const void* X, int64_t M, const void* Y, cons
   int st = check_mlp(P);
   if (st) return st;
   if (M < 0 || !S) return QLORA_ERR_INVALID_ARG;
+  if (M > kMaxTokens) return QLORA_ERR_UNSUPPORTED_SHAPE;
   if (M == 0) return QLORA_OK;
   if ((st = check_ptr(X)) || (st = check_ptr(Y)) || (st = check_ptr(S->G)) || (st = check_ptr(S->U)) ||
       (st = check_ptr(S->XA_g)) || (st = check_ptr(S->XA_u)) || (st = check_ptr(S->HA_d)))
@@ -202,6 +213,7 @@ int qv_mlp_bwd(const qlora_mlp* P, const void* dY, const void* X, const qlora_ml
   int st = check_mlp(P);
   if (st) return st;
   if (M < 0 || !S || !G) return QLORA_ERR_INVALID_ARG;
+  if (M > kMaxTokens) return QLORA_ERR_UNSUPPORTED_SHAPE;
   if ((st = check_ptr(G->dA_g)) || (st = check_ptr(G->dB_g)) || (st = check_ptr(G->dA_u)) ||
       (st = check_ptr(G->dB_u)) || (st = check_ptr(G->dA_d)) || (st = check_ptr(G->dB_d)))
     return st;
@@ -231,19 +243,20 @@ const char* qlora_strerror(int status) {
 }
 
 size_t qlora_linear_workspace_bytes(const qlora_linear* L, int64_t M) {
-  if (!L || M <= 0 || L->r < 1) return 0;
+  if (!L || M <= 0 || M > kMaxTokens || check_linear(L)) return 0;
   return qplan::linear_ws(M, L->W0.N, L->W0.K, L->r).total;
 }
 
 size_t qlora_mlp_workspace_bytes(const qlora_mlp* P, int64_t M) {
-  if (!P || M <= 0) return 0;
+  if (!P || M <= 0 || M > kMaxTokens || check_mlp(P)) return 0;
   return qplan::mlp_ws(M, P->gate.W0.K, P->gate.W0.N, P->gate.r, P->up.r, P->down.r).total;
 }
 
 }  // extern "C"
 
 size_t qv_linear_ce_ws(int64_t T, int64_t D, int64_t V, int64_t chunk, int32_t want_dx) {
-  if (T < 0 || D <= 0 || V <= 0 || chunk < 1 || D % 64 != 0 || V % 64 != 0) return 0;
+  if (T < 0 || T > kMaxTokens || D <= 0 || V <= 0 || chunk < 1 || D % 64 != 0 || V % 64 != 0) return 0;
+  if (D > 65536 || V > kMaxMlpI) return 0;
   return qplan::ce_ws(T, D, V, chunk, want_dx != 0).total;
 }
 
@@ -251,7 +264,9 @@ int qv_linear_ce(const void* X, int64_t T, int64_t D, const void* W, int64_t V, 
                  int64_t chunk, const float* loss, const float* token_loss, const void* dX, const void* ws,
                  size_t ws_bytes) {
   if (T < 0 || D <= 0 || V <= 0 || chunk < 1) return QLORA_ERR_INVALID_ARG;
-  if (D % 64 != 0 || V % 64 != 0 || D > 65536 || V > kMaxDim) return QLORA_ERR_UNSUPPORTED_SHAPE;
+  // the logit gradient is read as bf16 rows of stride 2V: a 256-row tile of
+  // it stays below 2 GiB for V <= 2097088
+  if (D % 64 != 0 || V % 64 != 0 || D > 65536 || V > kMaxMlpI || T > kMaxTokens) return QLORA_ERR_UNSUPPORTED_SHAPE;
   int st;
   if ((st = check_ptr(loss))) return st;
   if (token_loss && (st = check_ptr(token_loss))) return st;

@@ -73,3 +73,36 @@ def make_linear(q, W, A_u16, B_u16, alpha, cb, dq):
     assert_codes_equal(qw, ow)
     L = q.QLoraLinear(qw, bf16_dev(A_u16), bf16_dev(B_u16), alpha)
     return L, onf4.dequantize(ow, cb).astype(np.float64)
+
+
+class Guarded:
+    """Output tensors for the parity tests, each carved out of its own buffer
+    between two guard bands of a fixed byte pattern; the output itself starts
+    with the same pattern.  ``check()`` (after the calls) asserts that no
+    kernel wrote outside its output: every guard byte must be unchanged."""
+
+    PAD = 4096   # bytes before and after each output (keeps 256-byte alignment)
+    FILL = 0xA5
+
+    def __init__(self, device="cuda"):
+        self.device = device
+        self.bufs = []
+
+    def empty(self, shape, dtype):
+        shape = tuple(int(d) for d in shape)
+        n = int(np.prod(shape)) * torch.empty((), dtype=dtype).element_size()
+        body = (n + 255) // 256 * 256
+        buf = torch.full((self.PAD + body + self.PAD,), self.FILL, dtype=torch.uint8, device=self.device)
+        self.bufs.append((buf, n))
+        return buf[self.PAD:self.PAD + n].view(dtype).view(shape)
+
+    def empty_like(self, t):
+        return self.empty(t.shape, t.dtype)
+
+    def check(self):
+        torch.cuda.synchronize()
+        for i, (buf, n) in enumerate(self.bufs):
+            head, tail = buf[:self.PAD], buf[self.PAD + n:]
+            assert bool((head == self.FILL).all()), "output %d: bytes written before its start" % i
+            assert bool((tail == self.FILL).all()), "output %d: bytes written past its end" % i
+

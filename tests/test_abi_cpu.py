@@ -90,6 +90,11 @@ def test_linear_fwd_rejections(lib):
     assert lib.qlora_linear_fwd(None, FAKE, 16, FAKE, FAKE, FAKE, 1 << 30, None) == INVALID
 
 
+def test_debug_force_arch_argument(lib):
+    assert lib.qlora_debug_force_arch(b"x" * 64) == INVALID
+    assert lib.qlora_debug_force_arch(None) == OK
+
+
 def test_linear_workspace_rule(lib):
     L = linear(N=28672, K=8192, r=16, dq=256)   # skinny M splits the reduction -> needs workspace
     need = lib.qlora_linear_workspace_bytes(ctypes.byref(L), 64)
@@ -157,6 +162,29 @@ def test_mlp_shape_rules(lib):
     assert lib.qlora_mlp_fwd(ctypes.byref(P), FAKE, 16, FAKE, ctypes.byref(S), FAKE, need, None) in (HIP, DEVICE)
 
 
+def test_mlp_intermediate_bound(lib):
+    """The backward's [W_g^T | W_u^T] bf16 copy has row stride 2I; a 256-row
+    tile of it must stay below 2 GiB, so I is capped at 2097088."""
+    S = q.CMlpSaved(FAKE, FAKE, FAKE, FAKE, FAKE)
+
+    def call(I):
+        P = q.CMlp(linear(N=I, K=64), linear(N=I, K=64), linear(N=64, K=I))
+        return lib.qlora_mlp_fwd(ctypes.byref(P), FAKE, 16, FAKE, ctypes.byref(S), FAKE, 1 << 50, None)
+
+    assert call(2097088 + 64) == SHAPE
+    assert call(2097088) in (HIP, DEVICE)
+
+
+def test_mlp_accepts_combined_rank_above_128(lib):
+    """r_g = r_u = 128 is valid (each layer's rank is at most 128; the forward
+    then projects X onto A_g and A_u in two passes)."""
+    P = q.CMlp(linear(N=256, K=128, r=128), linear(N=256, K=128, r=128), linear(N=128, K=256, r=128))
+    S = q.CMlpSaved(FAKE, FAKE, FAKE, FAKE, FAKE)
+    need = lib.qlora_mlp_workspace_bytes(ctypes.byref(P), 600)
+    assert need > 0
+    assert lib.qlora_mlp_fwd(ctypes.byref(P), FAKE, 600, FAKE, ctypes.byref(S), FAKE, need, None) in (HIP, DEVICE)
+
+
 def test_workspace_grows_with_tokens(lib):
     P = q.CMlp(linear(N=14336, K=4096, r=16), linear(N=14336, K=4096, r=16), linear(N=4096, K=14336, r=16))
     a = lib.qlora_mlp_workspace_bytes(ctypes.byref(P), 1024)
@@ -221,13 +249,14 @@ def test_linear_ce_rejections(lib):
     assert ce(dX=None, wsb=16) == WS_SMALL
     assert ce(ws=FAKE + 4) == MISALIGNED
     assert ce(V=(1 << 22)) == SHAPE               # 256 vocabulary rows of bf16 must stay below 2 GiB
-    # workspace: chunk of logits + per-token losses (+ transposed head and partials with dX)
+    assert ce(V=2097088 + 64) == SHAPE            # ... also as the logit gradient of row stride 2V
+    # workspace: chunk of fp32 logits + per-token losses (+ transposed head and partials with dX)
     fwd_only = lib.qlora_linear_ce_workspace_bytes(16, 64, 128, 8, 0)
-    assert fwd_only == 256 + 256 + 8 * 128 * 2
+    assert fwd_only == 256 + 256 + 8 * 128 * 4
     with_dx = lib.qlora_linear_ce_workspace_bytes(16, 64, 128, 8, 1)
     assert with_dx >= fwd_only + 128 * 64 * 2
     assert lib.qlora_linear_ce_workspace_bytes(16, 96, 128, 8, 1) == 0
-    assert lib.qlora_linear_ce_workspace_bytes(4096, 4096, 128256, 1024, 0) == 256 + 4096 * 4 + 1024 * 128256 * 2
+    assert lib.qlora_linear_ce_workspace_bytes(4096, 4096, 128256, 1024, 0) == 256 + 4096 * 4 + 1024 * 128256 * 4
 
 
 def grouped(Ns=(64, 64), rs=(8, 8), N=None, K=128, G=None):
@@ -259,3 +288,28 @@ def test_grouped_rejections(lib):
                                  None) == INVALID
     assert lib.qlora_grouped_workspace_bytes(ctypes.byref(grouped()), 64) > 0
     assert lib.qlora_grouped_workspace_bytes(ctypes.byref(grouped(G=0)), 64) == 0
+
+
+def test_validation_under_address_and_ub_sanitizers(tmp_path):
+    """qlora_validate.cpp (argument checks, workspace sizing; no HIP) built with
+    -fsanitize=address,undefined and driven over null, misaligned, negative,
+    zero and extreme arguments: no sanitizer report, no crash."""
+    import shutil
+    import subprocess
+    if shutil.which("g++") is None:
+        pytest.skip("no host C++ compiler")
+    csrc = os.path.join(ROOT, "qlora_fine_tuning_linear_amd", "csrc")
+    exe = str(tmp_path / "validate_san")
+    cmd = ["g++", "-std=c++17", "-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+           "-fno-sanitize-recover=all", "-I" + os.path.join(ROOT, "include"), "-I" + csrc,
+           os.path.join(csrc, "qlora_validate.cpp"), os.path.join(ROOT, "tests", "abi_validate_driver.cpp"),
+           "-o", exe]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0:abort_on_error=0", UBSAN_OPTIONS="print_stacktrace=1")
+    env.pop("LD_PRELOAD", None)
+    r = subprocess.run([exe], capture_output=True, text=True, env=env, timeout=300)
+    assert r.returncode == 0, r.stderr[-4000:]
+    assert "runtime error" not in r.stderr and "AddressSanitizer" not in r.stderr, r.stderr[-4000:]
+    assert "calls" in r.stdout.splitlines()[-1]
+

@@ -15,7 +15,7 @@ import torch
 import synth
 from oracle import qlora as oq
 
-from gpu_util import assert_close, bf16_dev, f64_host, make_linear
+from gpu_util import Guarded, assert_close, bf16_dev, f64_host, make_linear
 
 pytestmark = pytest.mark.gpu
 
@@ -36,9 +36,12 @@ def run_case(cfg, seed, codebook, zero_B=False, alpha=None):
         inp["B"] = np.zeros_like(inp["B"])
     L, Wh = make_linear(q, inp["W0"], inp["A"], inp["B"], alpha, codebook, cfg.dq_group)
     X, dY = bf16_dev(inp["X"]), bf16_dev(inp["dY"])
-    Y, XA = q.qlora_linear_fwd(L, X)
-    dX, dA, dB = q.qlora_linear_bwd(L, dY, X, XA)
-    torch.cuda.synchronize()
+    M, K, N, r = cfg.M, cfg.K, cfg.N, cfg.r
+    g = Guarded()
+    Y, XA = q.qlora_linear_fwd(L, X, Y=g.empty((M, N), torch.bfloat16), XA=g.empty((M, r), torch.float32))
+    dX, dA, dB = q.qlora_linear_bwd(L, dY, X, XA, dX=g.empty((M, K), torch.bfloat16),
+                                    dA=g.empty((r, K), torch.bfloat16), dB=g.empty((N, r), torch.bfloat16))
+    g.check()
     Yr, XAr = oq.linear_forward(inp["X"], Wh, inp["A"], inp["B"], alpha)
     dXr, dAr, dBr = oq.linear_backward(inp["dY"], inp["X"], Wh, inp["A"], inp["B"], alpha)
     return dict(Y=(Y, Yr), XA=(XA, XAr), dX=(dX, dXr), dA=(dA, dAr), dB=(dB, dBr)), L, X, dY

@@ -11,15 +11,19 @@ and dX): ragged chunks and token tiles, V that is not a multiple of the
 256-column tile, a vocabulary-split dX product (few tokens, V = 32000), the
 loss alone without dX, every target ignored, and no tokens.  The full-size
 case (T = 4096 tokens, D = 4096, V = 128256, the page's vocabulary) is checked
-on 24 sampled tokens: their per-token losses and dX rows against the oracle
-run on those tokens alone (its dX rescaled from their count to the count of
-all tokens with a target), and the mean loss against the GPU's own per-token
-terms.
+on 24 sampled tokens (their per-token losses and dX rows against the oracle
+run on those tokens alone, its dX rescaled from their count to the count of
+all tokens with a target), and its mean loss against the oracle's loss over
+all 4096 tokens (computed in token chunks, loss only).  The confident regime
+of late training is covered by logits of standard deviation about 10 with
+every target the largest logit (mean loss well below 0.5), where the loss is
+the small difference of two large numbers.
 
-Bars: the logits are rounded to bf16 before the softmax and (softmax -
-onehot)/n is rounded to bf16 before the dX product, so the per-token losses
-and the loss are held to 1e-3 (relative), dX to the 1e-2 relative Frobenius
-bar of every floating-point output.  Two calls give identical bits.
+Bars: the logits are fp32 (fp32 accumulation of exact bf16 products) and
+(softmax - onehot)/n is rounded to bf16 before the dX product, so the
+per-token losses and the loss are held to 1e-3 (relative), dX to the 1e-2
+relative Frobenius bar of every floating-point output.  Two calls give
+identical bits.
 """
 import numpy as np
 import pytest
@@ -42,9 +46,9 @@ def _gpu():
     q.load_library()
 
 
-def _inputs(T, D, V, seed, every):
+def _inputs(T, D, V, seed, every, logit_std=2.0):
     X = synth.normal_bf16(seed, 50, T * D).reshape(T, D)
-    W = synth.normal_bf16(seed, 51, V * D, 0.0, 2.0 / np.sqrt(D)).reshape(V, D)
+    W = synth.normal_bf16(seed, 51, V * D, 0.0, logit_std / np.sqrt(D)).reshape(V, D)
     t = synth.targets(seed, 52, T, V, ignore_every=every)
     return X, W, t
 
@@ -91,6 +95,26 @@ def test_linear_ce_matches_oracle(name, T, D, V, chunk, every, want_dx):
         assert torch.equal(dX.view(torch.int16), dX2.view(torch.int16))
 
 
+@pytest.mark.parametrize("T,D,V,chunk", [(300, 256, 2048, 128), (96, 1024, 32000, 64)])
+def test_linear_ce_confident_regime(T, D, V, chunk):
+    """Large logits (standard deviation about 10) with every target the
+    largest logit: the per-token losses are small differences of large
+    numbers, log-sum-exp minus the target logit."""
+    print("case confident T=%d D=%d V=%d" % (T, D, V), flush=True)
+    X, W, _ = _inputs(T, D, V, 4300 + V, 0, logit_std=10.0)
+    from oracle.qlora import as_f64
+    Z = as_f64(X) @ as_f64(W).T
+    t = Z.argmax(axis=1).astype(np.int32)
+    lr, tlr, dXr = olc.linear_ce(X, W, t)
+    assert lr < 0.5, lr  # the regime this case is for
+    Xd, Wd = bf16_dev(X), bf16_dev(W)
+    loss, tl, dX = q.qlora_linear_ce(Xd, Wd, torch.from_numpy(t).cuda(), chunk=chunk, want_token_loss=True)
+    torch.cuda.synchronize()
+    assert _rel(tl.cpu().numpy(), tlr) <= 1e-3, _rel(tl.cpu().numpy(), tlr)
+    assert abs(loss.item() - lr) <= 1e-3 * abs(lr), (loss.item(), lr)
+    assert rel_fro(dX, dXr) <= 1e-2, rel_fro(dX, dXr)
+
+
 def test_linear_ce_all_ignored_and_empty():
     T, D, V = 40, 64, 192
     X, W, _ = _inputs(T, D, V, 4100, 0)
@@ -115,8 +139,12 @@ def test_linear_ce_full_size_sampled():
     tl_h = tl.cpu().numpy().astype(np.float64)
     valid = t != olc.IGNORE_INDEX
     n = int(valid.sum())
-    # the mean of the GPU's own per-token terms
-    assert abs(loss.item() - tl_h.sum() / n) <= 1e-5 * abs(loss.item())
+    # the loss against the oracle's over every token (loss only, in chunks of
+    # tokens: the per-token terms do not depend on the other tokens)
+    tl_ref = np.concatenate([olc.linear_ce(X[c:c + 256], W, t[c:c + 256], want_grad=False)[1]
+                             for c in range(0, T, 256)])
+    loss_ref = tl_ref.sum() / n
+    assert abs(loss.item() - loss_ref) <= 1e-3 * abs(loss_ref), (loss.item(), loss_ref)
     rng = np.random.default_rng(7)
     idx = np.sort(rng.choice(T, 24, replace=False))
     lr, tlr, dXr = olc.linear_ce(X[idx], W, t[idx])

@@ -18,7 +18,7 @@ import torch
 import synth
 from oracle import qlora as oq
 
-from gpu_util import assert_close, bf16_dev, make_linear
+from gpu_util import Guarded, assert_close, bf16_dev, make_linear
 
 pytestmark = pytest.mark.gpu
 
@@ -53,6 +53,10 @@ SMALL = [
     synth.MlpCfg("m513_d256_i384_r64_dq", M=513, D=256, I=384, r=64, alpha=16.0, dq_group=256),
     synth.MlpCfg("m1100_d320_i448_r16", M=1100, D=320, I=448, r=16, alpha=16.0, dq_group=0),
     synth.MlpCfg("m1537_d192_i576_r32_dq", M=1537, D=192, I=576, r=32, alpha=32.0, dq_group=256),
+    # rank 128 on every layer: r_g + r_u = 256 exceeds one down-projection
+    # launch, below and above the 512-token switch to the bf16-copy GEMMs
+    synth.MlpCfg("m200_d256_i384_r128", M=200, D=256, I=384, r=128, alpha=16.0, dq_group=0),
+    synth.MlpCfg("m600_d256_i384_r128_dq", M=600, D=256, I=384, r=128, alpha=32.0, dq_group=256),
 ]
 
 
@@ -61,9 +65,17 @@ def test_mlp_parity_small(cfg, codebook):
     print("case", cfg.name, flush=True)
     P, W, inp = build(cfg, 3000 + cfg.M, codebook)
     X, dY = bf16_dev(inp["X"]), bf16_dev(inp["dY"])
-    Y, S = q.qlora_mlp_fwd(P, X)
-    dX, grads = q.qlora_mlp_bwd(P, dY, X, S)
-    torch.cuda.synchronize()
+    g = Guarded()
+    M, D, I = cfg.M, cfg.D, cfg.I
+    bf, f32 = torch.bfloat16, torch.float32
+    S0 = q.MlpSaved(g.empty((M, I), bf), g.empty((M, I), bf), g.empty((M, P.gate.r), f32),
+                    g.empty((M, P.up.r), f32), g.empty((M, P.down.r), f32))
+    Y, S = q.qlora_mlp_fwd(P, X, Y=g.empty((M, D), bf), saved=S0)
+    grads0 = {k: g.empty_like(getattr(P, lay).A if k[1] == "A" else getattr(P, lay).B)
+              for k, lay in (("dA_g", "gate"), ("dB_g", "gate"), ("dA_u", "up"), ("dB_u", "up"),
+                             ("dA_d", "down"), ("dB_d", "down"))}
+    dX, grads = q.qlora_mlp_bwd(P, dY, X, S, dX=g.empty((M, D), bf), grads=grads0)
+    g.check()
     f = oq.mlp_forward(inp["X"], *oracle_args(W, inp), cfg.alpha)
     b = oq.mlp_backward(inp["dY"], inp["X"], f["G"], f["U"], *oracle_args(W, inp), cfg.alpha)
     assert_close("Y", Y, f["Y"])
@@ -102,6 +114,7 @@ def test_mlp_parity_full_size_sampled(idx, codebook):
     assert_close("G", S.G[idx_t], f["G"])
     assert_close("U", S.U[idx_t], f["U"])
     assert_close("XA_g", S.XA_g[idx_t], f["XA_g"])
+    assert_close("XA_u", S.XA_u[idx_t], f["XA_u"])
     assert_close("HA_d", S.HA_d[idx_t], f["HA_d"])
     assert_close("dX", dX[idx_t], b["dX"])
     # rows outside the sample have dY == 0, hence dX == X-independent LoRA-free zero
@@ -110,3 +123,24 @@ def test_mlp_parity_full_size_sampled(idx, codebook):
     assert torch.count_nonzero(dX[others]) == 0
     for k in ("dA_g", "dB_g", "dA_u", "dB_u", "dA_d", "dB_d"):
         assert_close(k, grads[k], b[k])
+
+
+def test_mlp_parity_full_size_dense_llama3_8b(codebook):
+    """The Llama-3-8B-shaped block (M=8192, D=4096, I=14336, r=16) at full
+    size with dense dY: every LoRA gradient is a sum over all 8192 tokens,
+    compared with the oracle's whole-batch forward + backward (run in token
+    chunks; about 6 TFLOP of fp64 host work), and Y and dX on every row."""
+    cfg = synth.CONFIGS[2]
+    print("case", cfg.name, "dense", flush=True)
+    P, W, inp = build(cfg, synth.seed_of(2), codebook)
+    X, dY = bf16_dev(inp["X"]), bf16_dev(inp["dY"])
+    Y, S = q.qlora_mlp_fwd(P, X)
+    dX, grads = q.qlora_mlp_bwd(P, dY, X, S)
+    torch.cuda.synchronize()
+    ref = oq.mlp_forward_backward_rows(inp["X"], inp["dY"], *oracle_args(W, inp), cfg.alpha, chunk=1024,
+                                       keep=("Y", "dX"))
+    assert_close("Y", Y, ref["Y"])
+    assert_close("dX", dX, ref["dX"])
+    for k in ("dA_g", "dB_g", "dA_u", "dB_u", "dA_d", "dB_d"):
+        assert_close(k, grads[k], ref[k])
+
