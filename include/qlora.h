@@ -343,6 +343,28 @@ int qlora_linear_fwd(const qlora_linear* L, const void* X, int64_t M, void* Y,
                      float* XA_saved, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * qlora_linear_fwd_static: qlora_linear_fwd for callers that cannot allocate
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments and results as qlora_linear_fwd, but no
+ * workspace: the pass's scratch (split partials, down-projection partials,
+ * the bf16 weight copy from 512 tokens on) lives in a library-owned device
+ * array of QLORA_STATIC_SCRATCH_BYTES per GPU, which that GPU holds from the
+ * first call on it until the process ends.  The first call on a GPU looks up
+ * the array's device address; no call allocates or frees memory.
+ *   A pass that needs more scratch than that (qlora_linear_workspace_bytes
+ *   larger than QLORA_STATIC_SCRATCH_BYTES for the forward's share, e.g. a
+ *   bf16 copy of an 8192 x 8192 weight) returns QLORA_ERR_WORKSPACE_TOO_SMALL
+ *   and enqueues nothing.
+ * Every call on one GPU uses that GPU's one array and leaves the last call's
+ * contents there: calls that overlap on one GPU (several streams or host
+ * threads) race and must be ordered by the caller.  Nothing in the array
+ * needs to start at zero.  Other errors as for qlora_linear_fwd.
+ */
+#define QLORA_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+int qlora_linear_fwd_static(const qlora_linear* L, const void* X, int64_t M, void* Y, float* XA_saved,
+                            void* stream);
+
+/*
  * qlora_linear_bwd: gradients of <Y, dY> ("LLM Fine-Tuning in 2026",
  * section 2: analytic gradients instead of autograd; W0 is frozen).
  *   T  = dY B                      (fp32, in the workspace)

@@ -29,8 +29,9 @@ EXPORTED = (
     "qlora_mlp_workspace_bytes", "qlora_mlp_fwd", "qlora_mlp_bwd", "qlora_trace_install", "qlora_merge",
     "rmsnorm_fwd", "rmsnorm_bwd", "rmsnorm_bwd_workspace_bytes",
     "qlora_grouped_workspace_bytes", "qlora_grouped_fwd", "qlora_grouped_bwd",
-    "qlora_linear_ce_workspace_bytes", "qlora_linear_ce", "qlora_debug_force_arch",
+    "qlora_linear_ce_workspace_bytes", "qlora_linear_ce", "qlora_linear_fwd_static", "qlora_debug_force_arch",
 )
+QLORA_STATIC_SCRATCH_BYTES = 64 << 20
 
 
 class QloraError(RuntimeError):
@@ -108,6 +109,7 @@ def load_library(path: str = LIB_PATH):
         "qlora_grouped_bwd": (ctypes.c_int, [P(CGrouped), vp, vp, vp, i64, vp, vp, P(vp), vp, sz, vp]),
         "qlora_linear_ce_workspace_bytes": (sz, [i64, i64, i64, i64, i32]),
         "qlora_linear_ce": (ctypes.c_int, [vp, i64, i64, vp, i64, vp, i32, i64, vp, vp, vp, vp, sz, vp]),
+        "qlora_linear_fwd_static": (ctypes.c_int, [P(CLinear), vp, i64, vp, vp, vp]),
         "qlora_debug_force_arch": (ctypes.c_int, [ctypes.c_char_p]),
     }
     for name, (res, args) in sig.items():
@@ -229,6 +231,21 @@ def qlora_linear_fwd(L: QLoraLinear, X: torch.Tensor, Y=None, XA=None, ws=None):
     st = lib.qlora_linear_fwd(ctypes.byref(cl), X.data_ptr(), M, Y.data_ptr(), XA.data_ptr(), ws.data_ptr(),
                               ws.numel(), _stream(dev))
     _check("qlora_linear_fwd", st)
+    return Y, XA
+
+
+def qlora_linear_fwd_static(L: QLoraLinear, X: torch.Tensor, Y=None, XA=None):
+    """qlora_linear_fwd_static: as qlora_linear_fwd with the library's static
+    per-GPU scratch instead of a workspace; returns (Y, XA)."""
+    lib = load_library()
+    M = X.shape[0]
+    dev = X.device
+    _need(X, torch.bfloat16, (M, L.W0.K), "X")
+    Y = torch.empty(M, L.W0.N, dtype=torch.bfloat16, device=dev) if Y is None else Y
+    XA = torch.empty(M, L.r, dtype=torch.float32, device=dev) if XA is None else XA
+    cl = L.c()
+    _check("qlora_linear_fwd_static", lib.qlora_linear_fwd_static(ctypes.byref(cl), X.data_ptr(), M, Y.data_ptr(),
+                                                                  XA.data_ptr(), _stream(dev)))
     return Y, XA
 
 

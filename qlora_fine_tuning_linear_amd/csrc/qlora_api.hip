@@ -4,11 +4,18 @@
 #include <string.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "qlora.h"
 #include "qlora_launch.h"
 #include "qlora_plan.h"
 #include "qlora_validate.h"
+
+// Scratch of qlora_linear_fwd_static: one array per GPU, in this file's
+// device code object, held until the process ends.  In host code `scratch`
+// names a host-side stand-in, not device memory: never pass it to a kernel.
+constexpr size_t kStaticScratchBytes = QLORA_STATIC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
 
 namespace {
 
@@ -33,6 +40,32 @@ int check_device() {
     g_dev_ok[dev].store(s, std::memory_order_relaxed);
   }
   return s == 1 ? QLORA_OK : QLORA_ERR_UNSUPPORTED_DEVICE;
+}
+
+// Scratch of qlora_linear_fwd_static (the array itself is defined at file
+// scope above this namespace).  Its device address is looked up once per
+// device, with that device current, and only that address is ever handed to
+// kernels or host-side HIP calls.
+std::atomic<void*> g_scratch[64];
+std::mutex g_scratch_mu;
+
+int static_scratch(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return QLORA_ERR_HIP;
+  if (dev < 0 || dev >= 64) return QLORA_ERR_UNSUPPORTED_DEVICE;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      void* addr = nullptr;
+      if (hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)) != hipSuccess || !addr) return QLORA_ERR_HIP;
+      p = addr;
+      g_scratch[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return QLORA_OK;
 }
 
 inline int hip_status(hipError_t e) { return e == hipSuccess ? QLORA_OK : QLORA_ERR_HIP; }
@@ -416,6 +449,15 @@ int qlora_linear_fwd(const qlora_linear* L, const void* X, int64_t M, void* Y, f
   QHIP(traced_gemm_q(MODE_FWD, a, pl, st));
   if (pl.splits > 1) QHIP(launch_splitk_finish(part, pl.splits, M, N, u16m(Y), st));
   return QLORA_OK;
+}
+
+int qlora_linear_fwd_static(const qlora_linear* L, const void* X, int64_t M, void* Y, float* XA_saved, void* stream) {
+  QTRY(qv_linear_fwd_static(L, X, M, Y, XA_saved, kStaticScratchBytes));
+  if (M == 0) return QLORA_OK;
+  QTRY(check_device());
+  void* ws = nullptr;
+  QTRY(static_scratch(&ws));
+  return qlora_linear_fwd(L, X, M, Y, XA_saved, ws, kStaticScratchBytes, stream);
 }
 
 int qlora_linear_bwd(const qlora_linear* L, const void* dY, const void* X, const float* XA_saved, int64_t M, void* dX,

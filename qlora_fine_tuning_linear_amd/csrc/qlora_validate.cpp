@@ -169,6 +169,18 @@ int qv_linear_fwd(const qlora_linear* L, const void* X, int64_t M, const void* Y
   return check_ws(ws, ws_bytes, w.fwd_total);
 }
 
+int qv_linear_fwd_static(const qlora_linear* L, const void* X, int64_t M, const void* Y, const float* XA,
+                         size_t scratch_bytes) {
+  int st = check_linear(L);
+  if (st) return st;
+  if (M < 0) return QLORA_ERR_INVALID_ARG;
+  if (M > kMaxTokens) return QLORA_ERR_UNSUPPORTED_SHAPE;
+  if (M == 0) return QLORA_OK;
+  if ((st = check_ptr(X)) || (st = check_ptr(Y)) || (st = check_ptr(XA))) return st;
+  const qplan::LinearWs w = qplan::linear_ws(M, L->W0.N, L->W0.K, L->r);
+  return w.fwd_total > scratch_bytes ? QLORA_ERR_WORKSPACE_TOO_SMALL : QLORA_OK;
+}
+
 int qv_linear_bwd(const qlora_linear* L, const void* dY, const void* X, const float* XA, int64_t M, const void* dX,
                   const void* dA, const void* dB, const void* ws, size_t ws_bytes) {
   int st = check_linear(L);

@@ -18,6 +18,11 @@ int qv_rmsnorm_bwd(const void* dY, const void* X, const void* w, const float* rs
 int qv_merge(const qlora_linear* L, int32_t out_dtype, const void* out);
 int qv_linear_fwd(const qlora_linear* L, const void* X, int64_t M, const void* Y, const float* XA, const void* ws,
                   size_t ws_bytes);
+// qlora_linear_fwd_static: the arguments of qlora_linear_fwd without a
+// workspace; QLORA_ERR_WORKSPACE_TOO_SMALL when the pass needs more than
+// scratch_bytes of scratch.
+int qv_linear_fwd_static(const qlora_linear* L, const void* X, int64_t M, const void* Y, const float* XA,
+                         size_t scratch_bytes);
 int qv_linear_bwd(const qlora_linear* L, const void* dY, const void* X, const float* XA, int64_t M, const void* dX,
                   const void* dA, const void* dB, const void* ws, size_t ws_bytes);
 int qv_mlp_fwd(const qlora_mlp* P, const void* X, int64_t M, const void* Y, const qlora_mlp_saved* S, const void* ws,

@@ -56,9 +56,9 @@ int main() {
         for (int dq : {0, 256, 3}) {
           qlora_linear L = lin(N, K, r, dq);
           for (int64_t M : toks) {
-            printf("%d %d %zu %d\n", qv_linear_fwd(&L, P, M, P, F, P, SIZE_MAX),
+            printf("%d %d %zu %d %d\n", qv_linear_fwd(&L, P, M, P, F, P, SIZE_MAX),
                    qv_linear_bwd(&L, P, P, F, M, P, P, P, P, SIZE_MAX), qlora_linear_workspace_bytes(&L, M),
-                   qv_merge(&L, 0, P));
+                   qv_linear_fwd_static(&L, P, M, P, F, (size_t)64 << 20), qv_merge(&L, 0, P));
             qlora_mlp mp;
             mp.gate = lin(N, K, r, dq);
             mp.up = lin(N, K, r, dq);

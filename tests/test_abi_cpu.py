@@ -90,6 +90,23 @@ def test_linear_fwd_rejections(lib):
     assert lib.qlora_linear_fwd(None, FAKE, 16, FAKE, FAKE, FAKE, 1 << 30, None) == INVALID
 
 
+def test_linear_fwd_static_rejections(lib):
+    """The allocation-free forward validates like qlora_linear_fwd and refuses
+    a pass whose scratch exceeds the library's static array, before touching
+    the device."""
+    call = lambda L, M=16, X=FAKE, Y=FAKE, XA=FAKE: lib.qlora_linear_fwd_static(ctypes.byref(L), X, M, Y, XA, None)
+    assert call(linear(), X=None) == INVALID
+    assert call(linear(), Y=FAKE + 8) == MISALIGNED
+    assert call(linear(r=0)) == SHAPE
+    assert call(linear(), M=-1) == INVALID
+    assert call(linear(), M=0) == OK
+    # 4096 tokens of an 8192 x 8192 layer: a 128 MiB bf16 weight copy
+    assert call(linear(N=8192, K=8192, r=16), M=4096) == WS_SMALL
+    assert lib.qlora_linear_workspace_bytes(ctypes.byref(linear(N=8192, K=8192, r=16)), 4096) > q.QLORA_STATIC_SCRATCH_BYTES
+    # small enough: validation passes and the call stops at the device check
+    assert call(linear(N=2048, K=1024, r=16), M=40) in (HIP, DEVICE)
+
+
 def test_debug_force_arch_argument(lib):
     assert lib.qlora_debug_force_arch(b"x" * 64) == INVALID
     assert lib.qlora_debug_force_arch(None) == OK

@@ -39,6 +39,7 @@ def test_forced_other_arch_is_rejected_before_any_work(codebook):
     try:
         calls = [
             lambda: q.qlora_linear_fwd(L, X, Y=Y, XA=XA),
+            lambda: q.qlora_linear_fwd_static(L, X, Y=Y, XA=XA),
             lambda: q.qlora_linear_bwd(L, dY, X, XA, dX=dX),
             lambda: q.nf4_dequantize(L.W0, out=out),
             lambda: q.qlora_merge(L, out=out),
