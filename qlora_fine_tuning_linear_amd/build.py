@@ -26,8 +26,8 @@ HIP_FLAGS = [
 ]
 
 
-SOURCES = ("qlora_kernels.hip", "qlora_bgemm.hip", "qlora_skinny.hip", "qlora_merge.hip", "qlora_rmsnorm.hip",
-           "qlora_ce.hip", "qlora_api.hip")
+SOURCES = ("qlora_kernels.hip", "qlora_bgemm.hip", "qlora_skinny.hip", "qlora_skinny2.hip", "qlora_merge.hip",
+           "qlora_rmsnorm.hip", "qlora_ce.hip", "qlora_api.hip")
 
 
 def build(verbose: bool = False) -> str:

@@ -113,12 +113,13 @@ hipError_t trace_end(int32_t idx, hipError_t e, hipStream_t st) {
   return e;
 }
 
-// Skinny-M forward GEMM, traced as kind mode + 16.
+// Skinny-M forward GEMM (the streaming form when the activations were re-laid
+// out), traced as kind mode + 16.
 hipError_t traced_skinny_fwd(const SkinnyArgs& a, const qplan::SkinnyPlan& pl, hipStream_t st) {
   hipError_t e;
   const int32_t idx = trace_begin(MODE_FWD + 16, st, &e);
   if (e != hipSuccess) return e;
-  return trace_end(idx, launch_skinny_fwd(a, pl, st), st);
+  return trace_end(idx, a.Xt ? launch_skinny_fwd2(a, pl, st) : launch_skinny_fwd(a, pl, st), st);
 }
 
 // Skinny-M transposed product, traced as kind MODE_BWD + 16.
@@ -399,7 +400,8 @@ int qlora_linear_fwd(const qlora_linear* L, const void* X, int64_t M, void* Y, f
     const int ds = qplan::plan_down_splits(M, K);
     const int dsu = qplan::down_splits_used(K, ds);
     QHIP(launch_lora_down(u16(X), M, K, u16(L->A), L->r, nullptr, 0, XA_saved, nullptr, ds, down_part, st, false));
-    const qplan::SkinnyPlan sp = qplan::plan_skinny_fwd(N, K);
+    const bool stream2 = qplan::use_skinny_fwd2(M, N, K, L->r);
+    const qplan::SkinnyPlan sp = stream2 ? qplan::plan_skinny_fwd2(N, K) : qplan::plan_skinny_fwd(N, K);
     SkinnyArgs a;
     memset(&a, 0, sizeof(a));
     a.X = u16(X);
@@ -419,6 +421,12 @@ int qlora_linear_fwd(const qlora_linear* L, const void* X, int64_t M, void* Y, f
     a.out = u16m(Y);
     a.part = sp.splits > 1 ? part : nullptr;
     a.kps = sp.kps;
+    if (stream2) {
+      uint16_t* xt = reinterpret_cast<uint16_t*>(bytes(ws) + w.fwd_part + w.fwd_down);
+      a.Mp = qplan::skinny_mp(M);
+      a.Xt = xt;
+      QHIP(launch_xtile(u16(X), M, K, a.Mp, xt, st));
+    }
     QHIP(traced_skinny_fwd(a, sp, st));
     if (sp.splits > 1) QHIP(launch_splitk_finish(part, sp.splits, M, N, u16m(Y), st));
     return QLORA_OK;

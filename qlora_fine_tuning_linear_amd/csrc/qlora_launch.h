@@ -87,6 +87,10 @@ struct SkinnyArgs {
   uint16_t* out;
   float* part;
   int32_t kps;  // 64-wide reduction tiles per split
+  // streaming form (skinny_fwd2_kernel): the activations re-laid out as
+  // Xt[K/8][Mp][8] (Mp = M rounded up to 16, zero rows past M)
+  const uint16_t* Xt;
+  int32_t Mp;
 };
 
 // Skinny-M backward finish (qlora_skinny.hip): dX = sum of the split
@@ -171,6 +175,10 @@ hipError_t launch_dequant_trans(const Nf4Dev& w, const float* codebook, uint16_t
 hipError_t launch_splitk_finish(const float* part, int splits, int64_t M, int64_t Nout, uint16_t* out,
                                 hipStream_t st);
 bool skinny_fwd_supported(int64_t M, int r);
+bool skinny_fwd2_supported(int64_t M, int64_t N, int64_t K, int r);
+// Xt[j][m][0..7] = X[m][8j..8j+7] (zero for M <= m < Mp)
+hipError_t launch_xtile(const uint16_t* X, int64_t M, int64_t K, int Mp, uint16_t* Xt, hipStream_t st);
+hipError_t launch_skinny_fwd2(const SkinnyArgs& a, const qplan::SkinnyPlan& pl, hipStream_t st);
 bool skinny_finish_supported(int64_t M, int r);
 bool skinny_bwd_supported(int64_t M, int64_t N, int64_t K);
 hipError_t launch_skinny_bwd(const SkinnyBwdArgs& a, int splits, hipStream_t st);

@@ -116,6 +116,37 @@ inline SkinnyPlan plan_skinny_fwd(int64_t N, int64_t K) {
 }
 inline bool use_skinny_fwd(int64_t M, int r) { return M >= 1 && M <= 64 && r <= 64; }
 
+// Streaming skinny forward (M <= 64, K % 256 == 0): fn from {1, 2, 4, 7}, the
+// smallest that puts at most one workgroup on each CU; with fewer tiles than
+// CUs the reduction is split, each split a whole number of 4-tile groups and
+// keeping >= 4 groups.
+inline bool use_skinny_fwd2(int64_t M, int64_t N, int64_t K, int r) {
+  return M >= 1 && M <= 64 && r <= 64 && K % 256 == 0 && N * (K / 16) < ((int64_t)1 << 31) &&
+         K * 64 * 2 < ((int64_t)1 << 31);
+}
+inline int skinny_mp(int64_t M) { return (int)(16 * cdiv(M, 16)); }
+inline SkinnyPlan plan_skinny_fwd2(int64_t N, int64_t K) {
+  static const int kFn[] = {1, 2, 4, 7};
+  SkinnyPlan p{7, 1, 0};
+  for (int f : kFn)
+    if (cdiv(N, 16 * f) <= kNumCUs) {
+      p.fn = f;
+      break;
+    }
+  const int64_t tiles = cdiv(N, 16 * p.fn);
+  const int64_t groups = K / 256;
+  int64_t s = 1;
+  if (tiles < kNumCUs) {
+    s = kNumCUs / tiles;
+    const int64_t max_s = groups / 4 > 0 ? groups / 4 : 1;
+    if (s > max_s) s = max_s;
+  }
+  const int64_t per = cdiv(groups, s > 0 ? s : 1);  // groups per split
+  p.kps = (int)(4 * (per > 0 ? per : 1));
+  p.splits = (int)(groups > 0 ? cdiv(groups, per) : 1);
+  return p;
+}
+
 // Token splits of a LoRA-gradient reduction out[p, j] = sum_m Z[m, p] V[m, j].
 // Each split writes an fp32 [P, r] partial; keep the partials small next to Z.
 inline int plan_grad_msplits(int64_t M, int64_t P, int r) {
@@ -140,6 +171,7 @@ inline int64_t pair_rows(int64_t I) { return 256 * cdiv(I, 128); }
 
 struct LinearWs {
   size_t fwd_part, fwd_down;             // forward: split-K partials, down-proj partials
+  size_t fwd_xt;                         // skinny forward: the re-laid-out activations
   size_t bwd_T, bwd_BT, bwd_part, bwd_down, bwd_grad;
   size_t wbuf;                           // bf16 weight copy (bgemm only), at the end
   size_t fwd_total, bwd_total, total;
@@ -154,10 +186,15 @@ inline LinearWs linear_ws(int64_t M, int64_t N, int64_t K, int r) {
     const SkinnyPlan sp = plan_skinny_fwd(N, K);
     w.fwd_part = sp.splits > 1 ? align256((size_t)sp.splits * M * N * 4) : 0;
   }
+  if (use_skinny_fwd2(M, N, K, r)) {
+    const SkinnyPlan sp = plan_skinny_fwd2(N, K);
+    w.fwd_part = sp.splits > 1 ? align256((size_t)sp.splits * M * N * 4) : 0;
+    w.fwd_xt = align256((size_t)K * skinny_mp(M) * 2);
+  }
   const int ds = plan_down_splits(M, K);
   w.fwd_down = ds > 1 ? align256((size_t)ds * M * r * 4) : 0;
   w.wbuf = bg ? align256((size_t)N * K * 2) : 0;
-  w.fwd_total = w.fwd_part + w.fwd_down + w.wbuf;
+  w.fwd_total = w.fwd_part + w.fwd_down + w.fwd_xt + w.wbuf;
 
   GemmPlan pb = plan_gemm(M, K, N, true, true);
   w.bwd_T = align256((size_t)M * r * 4);

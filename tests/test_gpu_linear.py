@@ -76,6 +76,14 @@ CASES = [
     synth.LinearCfg("m64_640x9216_r32", M=64, K=640, N=9216, r=32, alpha=32.0, dq_group=0),
     synth.LinearCfg("m40_1088x16448_r16", M=40, K=1088, N=16448, r=16, alpha=16.0, dq_group=256),
     synth.LinearCfg("m16_8192x32768_r8_split", M=16, K=8192, N=32768, r=8, alpha=16.0, dq_group=0),
+    # streaming skinny forward (K a multiple of 256): 1-4 token frags, 1, 2
+    # and 7 frags of rows per workgroup, groups of 4 tiles dealt unevenly over
+    # the 4 waves (5 groups: 2, 2, 1, 0; 10 groups: 3, 3, 3, 1), reduction
+    # splits, ragged rows and tokens, both absmax forms
+    synth.LinearCfg("m48_2048x3072_r16", M=48, K=2048, N=3072, r=16, alpha=16.0, dq_group=0),
+    synth.LinearCfg("m24_1280x7168_r8_dq", M=24, K=1280, N=7168, r=8, alpha=8.0, dq_group=256),
+    synth.LinearCfg("m61_2560x28672_r16", M=61, K=2560, N=28672, r=16, alpha=16.0, dq_group=0),
+    synth.LinearCfg("m9_4096x28608_r64_dq", M=9, K=4096, N=28608, r=64, alpha=32.0, dq_group=256),
 ]
 
 
