@@ -552,7 +552,18 @@ int qlora_linear_bwd(const qlora_linear* L, const void* dY, const void* X, const
     tb.add(u16(L->A), r, K, AT);  // A [r, K] -> A^T [K, r]
     QHIP(launch_transpose_multi(tb.J, st));
   }
-  QHIP(launch_lora_down(u16(dY), M, N, BT, r, nullptr, 0, T, nullptr, qplan::plan_down_splits(M, N), down_part, st));
+  const bool pair = r <= 16;
+  if (pair) {
+    // T = dY B and dB = s dY^T XA from one pass over dY
+    PairArgs pa{};
+    plan_lora_pair(pa, M, N, r);
+    pa.njobs = 1;
+    pa.job[0] = PairJob{u16(dY), BT, XA_saved, r, s, grad_part, grad_part + (size_t)pa.nb * M * r, T, u16m(dB)};
+    QHIP(launch_lora_pair(pa, st));
+  } else {
+    QHIP(launch_lora_down(u16(dY), M, N, BT, r, nullptr, 0, T, nullptr, qplan::plan_down_splits(M, N), down_part,
+                          st));
+  }
   // dX = dY W0 + s T A
   GemmArgs a = gemm_args();
   a.act0 = u16(dY);
@@ -576,9 +587,10 @@ int qlora_linear_bwd(const qlora_linear* L, const void* dY, const void* X, const
     QHIP(traced_gemm_q(MODE_BWD, a, pl, st));
     if (pl.splits > 1) QHIP(launch_splitk_finish(part, pl.splits, M, K, u16m(dX), st));
   }
-  // dB = s dY^T XA  ([N, r]);  dA = s T^T X  ([r, K])
-  QHIP(launch_lora_grad(0, u16(dY), nullptr, M, N, XA_saved, r, s, qplan::plan_grad_msplits(M, N, r), grad_part, 0,
-                        u16m(dB), st));
+  // dB = s dY^T XA  ([N, r], unless done above);  dA = s T^T X  ([r, K])
+  if (!pair)
+    QHIP(launch_lora_grad(0, u16(dY), nullptr, M, N, XA_saved, r, s, qplan::plan_grad_msplits(M, N, r), grad_part,
+                          0, u16m(dB), st));
   QHIP(launch_lora_grad(0, u16(X), nullptr, M, K, T, r, s, qplan::plan_grad_msplits(M, K, r), grad_part, 1, u16m(dA),
                         st));
   return QLORA_OK;
@@ -714,7 +726,10 @@ int qlora_mlp_bwd(const qlora_mlp* P, const void* dY, const void* X, const qlora
   b += w.bwd_down;
   float* grad_part = reinterpret_cast<float*>(b);
   b += w.bwd_grad;
+  float* pair_part = reinterpret_cast<float*>(b);
+  b += w.bwd_pair;
   uint16_t* wbuf = w.bwd_wbuf ? reinterpret_cast<uint16_t*>(b) : nullptr;
+  const bool pair = qplan::use_lora_pair(rg, ru, rd);
 
   // Td = dY B_d
   {
@@ -727,8 +742,18 @@ int qlora_mlp_bwd(const qlora_mlp* P, const void* dY, const void* X, const qlora
     tb.add(u16(P->up.A), ru, D, AuT);
     QHIP(launch_transpose_multi(tb.J, st));
   }
-  QHIP(launch_lora_down(u16(dY), M, D, BdT, rd, nullptr, 0, Td, nullptr, qplan::plan_down_splits(M, D), down_part,
-                        st));
+  if (pair) {
+    // Td = dY B_d and dB_d = s_d dY^T HA_d from one pass over dY
+    PairArgs pa{};
+    plan_lora_pair(pa, M, D, rd);
+    pa.njobs = 1;
+    pa.job[0] = PairJob{u16(dY), BdT, S->HA_d, rd, sd, pair_part, pair_part + (size_t)pa.nb * M * rd, Td,
+                        u16m(G->dB_d)};
+    QHIP(launch_lora_pair(pa, st));
+  } else {
+    QHIP(launch_lora_down(u16(dY), M, D, BdT, rd, nullptr, 0, Td, nullptr, qplan::plan_down_splits(M, D),
+                          down_part, st));
+  }
   // dH = dY W_d + s_d Td A_d, with the SwiGLU backward in the epilogue -> dG, dU
   {
     GemmArgs a = gemm_args();
@@ -749,19 +774,39 @@ int qlora_mlp_bwd(const qlora_mlp* P, const void* dY, const void* X, const qlora
       a.wb = wbuf;
       a.ldw = D;
       a.wrows = I;
+      // dA_d = s_d Td^T H from the epilogue's own G, U (per-token-tile partials)
+      if (qplan::fuse_dad(rd)) a.dad_part = grad_part;
       QHIP(traced_gemm_b(MODE_BWD_SWIGLU, a, st));
+      if (qplan::fuse_dad(rd))
+        QHIP(launch_grad_finish(grad_part, (int)qplan::cdiv(M, 256), I, rd, sd, 1, u16m(G->dA_d), st));
     } else {
       QHIP(traced_gemm_q(MODE_BWD_SWIGLU, a, qplan::plan_gemm(M, I, D, false), st));
     }
   }
-  // down-layer LoRA gradients: dB_d = s_d dY^T HA_d, dA_d = s_d Td^T H (H recomputed)
-  QHIP(launch_lora_grad(0, u16(dY), nullptr, M, D, S->HA_d, rd, sd, qplan::plan_grad_msplits(M, D, rd), grad_part, 0,
-                        u16m(G->dB_d), st));
-  QHIP(launch_lora_grad(1, u16(S->G), u16(S->U), M, I, Td, rd, sd, qplan::plan_grad_msplits(M, I, rd), grad_part, 1,
-                        u16m(G->dA_d), st));
-  // Tg = dG B_g, Tu = dU B_u
-  QHIP(launch_lora_down(dG, M, I, BgT, rg, nullptr, 0, Tg, nullptr, qplan::plan_down_splits(M, I), down_part, st));
-  QHIP(launch_lora_down(dU, M, I, BuT, ru, nullptr, 0, Tu, nullptr, qplan::plan_down_splits(M, I), down_part, st));
+  // down-layer LoRA gradients: dB_d = s_d dY^T HA_d, dA_d = s_d Td^T H (H
+  // recomputed from G, U when the dH GEMM did not)
+  if (!pair)
+    QHIP(launch_lora_grad(0, u16(dY), nullptr, M, D, S->HA_d, rd, sd, qplan::plan_grad_msplits(M, D, rd), grad_part,
+                          0, u16m(G->dB_d), st));
+  if (!(wbuf && qplan::fuse_dad(rd)))
+    QHIP(launch_lora_grad(1, u16(S->G), u16(S->U), M, I, Td, rd, sd, qplan::plan_grad_msplits(M, I, rd), grad_part,
+                          1, u16m(G->dA_d), st));
+  if (pair) {
+    // Tg = dG B_g, dB_g = s_g dG^T XA_g, Tu = dU B_u, dB_u = s_u dU^T XA_u:
+    // one pass over dG and one over dU, in one launch
+    PairArgs pa{};
+    plan_lora_pair(pa, M, I, rg > ru ? rg : ru);
+    pa.njobs = 2;
+    float* pg = pair_part;
+    float* pu = pg + qplan::pair_part_floats(M, I, rg);
+    pa.job[0] = PairJob{dG, BgT, S->XA_g, rg, sg, pg, pg + (size_t)pa.nb * M * rg, Tg, u16m(G->dB_g)};
+    pa.job[1] = PairJob{dU, BuT, S->XA_u, ru, su, pu, pu + (size_t)pa.nb * M * ru, Tu, u16m(G->dB_u)};
+    QHIP(launch_lora_pair(pa, st));
+  } else {
+    // Tg = dG B_g, Tu = dU B_u
+    QHIP(launch_lora_down(dG, M, I, BgT, rg, nullptr, 0, Tg, nullptr, qplan::plan_down_splits(M, I), down_part, st));
+    QHIP(launch_lora_down(dU, M, I, BuT, ru, nullptr, 0, Tu, nullptr, qplan::plan_down_splits(M, I), down_part, st));
+  }
   // dX = dG W_g + dU W_u + s_g Tg A_g + s_u Tu A_u  (one GEMM, reduction over 2I)
   {
     GemmArgs a = gemm_args();
@@ -790,13 +835,15 @@ int qlora_mlp_bwd(const qlora_mlp* P, const void* dY, const void* X, const qlora
       QHIP(traced_gemm_q(MODE_BWD_DUAL, a, qplan::plan_gemm(M, D, 2 * I, false), st));
     }
   }
-  // gate / up LoRA gradients
-  QHIP(launch_lora_grad(0, dG, nullptr, M, I, S->XA_g, rg, sg, qplan::plan_grad_msplits(M, I, rg), grad_part, 0,
-                        u16m(G->dB_g), st));
+  // gate / up LoRA gradients (dB_g, dB_u already done by the single pass)
+  if (!pair)
+    QHIP(launch_lora_grad(0, dG, nullptr, M, I, S->XA_g, rg, sg, qplan::plan_grad_msplits(M, I, rg), grad_part, 0,
+                          u16m(G->dB_g), st));
   QHIP(launch_lora_grad(0, u16(X), nullptr, M, D, Tg, rg, sg, qplan::plan_grad_msplits(M, D, rg), grad_part, 1,
                         u16m(G->dA_g), st));
-  QHIP(launch_lora_grad(0, dU, nullptr, M, I, S->XA_u, ru, su, qplan::plan_grad_msplits(M, I, ru), grad_part, 0,
-                        u16m(G->dB_u), st));
+  if (!pair)
+    QHIP(launch_lora_grad(0, dU, nullptr, M, I, S->XA_u, ru, su, qplan::plan_grad_msplits(M, I, ru), grad_part, 0,
+                          u16m(G->dB_u), st));
   QHIP(launch_lora_grad(0, u16(X), nullptr, M, D, Tu, ru, su, qplan::plan_grad_msplits(M, D, ru), grad_part, 1,
                         u16m(G->dA_u), st));
   return QLORA_OK;

@@ -89,9 +89,24 @@ __device__ __forceinline__ void bg_tile(int64_t bid, int64_t tiles_m, int64_t ti
 // segments instead of 8-byte pieces of 32 different rows per instruction.
 // Chunk c of row r sits at c ^ (r mod #chunks), which keeps both the writes
 // and the row-chunk reads free of bank conflicts.
+__device__ __forceinline__ f32x4 bg_mfma16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                 0, 0, 0);
+}
+
+// Position of H[token t][column c] in a wave's transposed H block [64
+// columns][32 tokens] (bf16): the 16-byte chunk t / 8 of column c is stored at
+// chunk (t / 8) ^ hsw(c), which keeps the column-wise MFMA operand reads (8
+// columns per pass) and the token-wise writes of the epilogue off each
+// other's banks.
+__device__ __forceinline__ int bg_ht_index(int c, int t) {
+  const int hsw = ((c >> 1) ^ (c >> 3)) & 3;
+  return c * 32 + (((t >> 3) ^ hsw) << 3) + (t & 7);
+}
+
 template <int MODE>
 __device__ __forceinline__ void bg_epilogue(const GemmArgs& p, f32x16 (&acc)[BG_FM][2], int64_t m0, int64_t n0,
-                                             int wm, int wn, int lane, uint16_t* reg) {
+                                             int wm, int wn, int lane, uint16_t* reg, f32x4 (&dad)[2][4]) {
   constexpr int FM = BG_FM;
   const int l32 = lane & 31, g = lane >> 5;
   const int64_t mw = m0 + wm * 128;  // first token of the wave
@@ -157,6 +172,13 @@ __device__ __forceinline__ void bg_epilogue(const GemmArgs& p, f32x16 (&acc)[BG_
       }
     };
     float* lf = reinterpret_cast<float*>(reg);
+    // optional: the down layer's T^T H over this wave's 128 tokens x 64
+    // columns, one 32-token frag at a time, with H = silu(G) U rounded to
+    // bf16 and stored transposed after lf (T = l0.V, rank l0.r <= 32)
+    const bool with_dad = p.dad_part != nullptr;
+    const int dr = p.l0.r;
+    uint16_t* ht = reg + 4096;
+    const int l16 = lane & 15, kq = lane >> 4;
     load(0, 0);
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
@@ -189,6 +211,8 @@ __device__ __forceinline__ void bg_epilogue(const GemmArgs& p, f32x16 (&acc)[BG_
             const float h = dH[2 * d + e];
             dU2[e] = h * G * sg;
             dG2[e] = h * U * sg * (1.0f + G * (1.0f - sg));
+            if (with_dad)
+              ht[bg_ht_index(8 * c8 + 2 * d + e, row)] = (uint16_t)(pack_bf16x2(G * sg * U, 0.0f) & 0xFFFFu);
           }
           og[d] = pack_bf16x2(dG2[0], dG2[1]);
           ou[d] = pack_bf16x2(dU2[0], dU2[1]);
@@ -197,6 +221,30 @@ __device__ __forceinline__ void bg_epilogue(const GemmArgs& p, f32x16 (&acc)[BG_
         if (m < p.M && col_ok) {
           *reinterpret_cast<u32x4*>(p.out0 + m * p.Nout + ncol) = og;
           *reinterpret_cast<u32x4*>(p.out1 + m * p.Nout + ncol) = ou;
+        }
+      }
+      if (with_dad) {
+        // A operand: T^T, lane (j, kq) holds T[token 8 kq + e][j] (zero past
+        // M and past the rank); B operand: H^T rows, lane (column, kq) holds
+        // H[token 8 kq + e][column]; result lane (column, q): j = 4 q + v
+        u32x4 ta[2];
+#pragma unroll
+        for (int jf = 0; jf < 2; ++jf) {
+          const int j = 16 * jf + l16;
+          float t8[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int64_t m = mw + i * 32 + 8 * kq + e;
+            t8[e] = (j < dr && m < p.M) ? p.l0.V[m * dr + j] : 0.0f;
+          }
+          ta[jf] = u32x4{pack_bf16x2(t8[0], t8[1]), pack_bf16x2(t8[2], t8[3]), pack_bf16x2(t8[4], t8[5]),
+                         pack_bf16x2(t8[6], t8[7])};
+        }
+#pragma unroll
+        for (int cf = 0; cf < 4; ++cf) {
+          const u32x4 hop = *reinterpret_cast<const u32x4*>(ht + bg_ht_index(16 * cf + l16, 8 * kq));
+          dad[0][cf] = bg_mfma16(ta[0], hop, dad[0][cf]);
+          if (dr > 16) dad[1][cf] = bg_mfma16(ta[1], hop, dad[1][cf]);
         }
       }
     }
@@ -504,7 +552,45 @@ __global__ __launch_bounds__(512) void bgemm_kernel(GemmArgs p) {
     }
   }
   uint16_t* buf = wave < 2 ? hb0 : wave < 4 ? hb1 : wave < 6 ? hb2 : hb3;
-  bg_epilogue<MODE>(p, acc, m0, n0, wm, wn, lane, buf + (wave & 1) * 8192);
+  f32x4 dad[2][4];
+#pragma unroll
+  for (int jf = 0; jf < 2; ++jf)
+#pragma unroll
+    for (int cf = 0; cf < 4; ++cf) dad[jf][cf] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  bg_epilogue<MODE>(p, acc, m0, n0, wm, wn, lane, buf + (wave & 1) * 8192, dad);
+  if constexpr (MODE == MODE_BWD_SWIGLU) {
+    if (p.dad_part) {
+      // the two token halves of each 64-column strip are added (waves 4..7
+      // hand theirs to waves 0..3 through the fifth ring buffer) and written
+      // as this token tile's partial dad_part[tm][column][j]
+      float* xr = reinterpret_cast<float*>(hb4) + (wave & 3) * 2048;
+      if (wm == 1) {
+#pragma unroll
+        for (int jf = 0; jf < 2; ++jf)
+#pragma unroll
+          for (int cf = 0; cf < 4; ++cf)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) xr[((jf * 4 + cf) * 4 + v) * 64 + lane] = dad[jf][cf][v];
+      }
+      __syncthreads();
+      if (wm == 0) {
+        const int dr = p.l0.r;
+        const int l16 = lane & 15, kq = lane >> 4;
+#pragma unroll
+        for (int jf = 0; jf < 2; ++jf)
+#pragma unroll
+          for (int cf = 0; cf < 4; ++cf) {
+            const int64_t col = n0 + wn * 64 + 16 * cf + l16;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              const int j = 16 * jf + 4 * kq + v;
+              const float sum = dad[jf][cf][v] + xr[((jf * 4 + cf) * 4 + v) * 64 + lane];
+              if (j < dr && col < p.Nout) p.dad_part[((int64_t)tm * p.Nout + col) * dr + j] = sum;
+            }
+          }
+      }
+    }
+  }
   if constexpr (MODE == MODE_FWD_SWIGLU) {
     if (p.had_part) {
       // each wave's 128 tokens x 32 columns of H A^T into its region, then the

@@ -989,6 +989,178 @@ __global__ __launch_bounds__(256) void lora_grad16_kernel(const uint16_t* __rest
     }
 }
 
+// ------------------------------------------------------------------------
+// Both LoRA products of one gradient operand from a single pass over it
+// ("Speed Up Fine-Tuning 2x with Unsloth", item 2, the adapters' fused
+// backward): T = Z B (reduction over the P columns) and dB = s Z^T V
+// (reduction over the M tokens), r <= 16.  Workgroup (x, y, z): columns
+// [512 x, 512 x + 512) (wave w: 128 of them), token split y, job z.
+//   dB side: as lora_grad16_kernel (lane (c, q) loads 8 tokens x 8 columns,
+//     transposes them in registers, 8 MFMAs per 32-token slab against V).
+//   T side: the wave's 32 x 128 slab goes to its own LDS region as loaded
+//     (row-major, 16-byte chunk h of token row t at position h ^ (t % 16),
+//     so that the writes and the reads below hit distinct banks); lane
+//     (c, q) reads tokens 16 f + c at columns p0 + 32 s + 8 q, the B operand
+//     of 16x16x32 MFMAs whose A operand is Bt (rank j = c, loaded once); the
+//     four waves' 128-column sums of a slab are added in LDS in wave order
+//     and written as this column block's partial.
+// Z crosses HBM once; the operands never leave the CU.
+// ------------------------------------------------------------------------
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void lora_pair16_kernel(PairArgs a) {
+  __shared__ float tred[2][4][2 * 4 * 64];
+  __shared__ __attribute__((aligned(16))) uint16_t zs[4][32 * 128];
+  __shared__ u32x4 bts[4][4 * 64];
+  const PairJob& J = a.job[blockIdx.z];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = lane & 15, q = lane >> 4;
+  const int64_t M = a.M, P = a.P;
+  const int r = J.r;
+  const uint16_t* Z = J.Z;
+  const int64_t p0 = ((int64_t)blockIdx.x * 4 + wave) * 128;
+  const int64_t mb = (int64_t)blockIdx.y * a.m_per_split;
+  const int64_t me = min(M, mb + a.m_per_split);
+  int64_t pc = p0 + 8 * c;
+  if (pc > P - 8) pc = P - 8;
+  const int jv = c < r ? c : r - 1;
+  // T side: rank c of Bt at this lane's 4 column chunks (zero past P / r),
+  // kept in the wave's LDS slot [s][lane] (fewer live registers: two waves
+  // per SIMD)
+  u32x4* btw = bts[wave];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int64_t col = p0 + 32 * s + 8 * q;
+    btw[s * 64 + lane] = (c < r && col < P) ? *reinterpret_cast<const u32x4*>(J.Bt + (int64_t)c * P + col)
+                                            : u32x4{0u, 0u, 0u, 0u};
+  }
+  uint16_t* zw = zs[wave];
+
+  f32x4 acc[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  struct Slab {
+    u32x4 raw[8];
+    float x[8];
+  };
+  auto load = [&](int64_t ms, Slab& S) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      int64_t mm = ms + 8 * q + e;
+      if (mm >= me) mm = me - 1;
+      S.raw[e] = *reinterpret_cast<const u32x4*>(Z + mm * P + pc);
+      S.x[e] = J.V[mm * r + jv];
+    }
+  };
+  auto slab = [&](int64_t ms, const Slab& S, int buf) {
+    // the slab into this wave's region: token 8 q + e, chunk c
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int t = 8 * q + e;
+      *reinterpret_cast<u32x4*>(zw + t * 128 + ((c ^ (t & 15)) * 8)) = S.raw[e];
+    }
+    // dB side
+    u32x4 rows[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) rows[e] = (ms + 8 * q + e < me) ? S.raw[e] : u32x4{0u, 0u, 0u, 0u};
+    u32x4 aop[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const uint32_t sel = (t & 1) ? 0x07060302u : 0x05040100u;
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+        aop[t][d] = __builtin_amdgcn_perm(rows[2 * d + 1][t >> 1], rows[2 * d][t >> 1], sel);
+    }
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = (c < r && ms + 8 * q + e < me) ? S.x[e] : 0.0f;
+    const u32x4 vop{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
+                    pack_bf16x2(x[6], x[7])};
+#pragma unroll
+    for (int t = 0; t < 8; ++t) acc[t] = mfma16k32(aop[t], vop, acc[t]);
+    // T side: ta[f][v] = T partial [token ms + 16 f + c][j = 4 q + v]
+    f32x4 ta[2];
+#pragma unroll
+    for (int f = 0; f < 2; ++f) {
+      ta[f] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      const int t = 16 * f + c;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const u32x4 zt = *reinterpret_cast<const u32x4*>(zw + t * 128 + (((4 * s + q) ^ (t & 15)) * 8));
+        ta[f] = mfma16k32(btw[s * 64 + lane], zt, ta[f]);
+      }
+    }
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) tred[buf][wave][(f * 4 + v) * 64 + lane] = ta[f][v];
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int e = tid + 256 * k;  // (f, v, lane)
+      const float sum = tred[buf][0][e] + tred[buf][1][e] + tred[buf][2][e] + tred[buf][3][e];
+      const int ln = e & 63, v = (e >> 6) & 3, f = e >> 8;
+      const int64_t tok = ms + 16 * f + (ln & 15);
+      const int j = 4 * (ln >> 4) + v;
+      if (tok < me && j < r) J.tpart[((int64_t)blockIdx.x * M + tok) * r + j] = sum;
+    }
+  };
+  Slab ra, rb;
+  int64_t ms = mb;
+  if (ms < me) load(ms, ra);
+  for (; ms + 32 < me; ms += 64) {
+    load(ms + 32, rb);
+    slab(ms, ra, 0);
+    if (ms + 64 < me) load(ms + 64, ra);
+    slab(ms + 32, rb, 1);
+  }
+  if (ms < me) slab(ms, ra, 0);
+
+  // dB side: acc[t][v] = C[row 4q + v][j = c], column p = p0 + 8 (4q + v) + t
+  if (c >= r) return;
+#pragma unroll
+  for (int t = 0; t < 8; ++t)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int64_t pp = p0 + 8 * (4 * q + v) + t;
+      if (pp < P) J.gpart[((int64_t)blockIdx.y * P + pp) * r + c] = acc[t][v];
+    }
+}
+
+// sum_{i < n} src[i * stride], added in index order, 8 loads in flight
+__device__ __forceinline__ float ordered_sum(const float* __restrict__ src, int n, int64_t stride) {
+  float s = 0.0f;
+  int i = 0;
+  for (; i + 8 <= n; i += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = src[(int64_t)(i + u) * stride];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s += v[u];
+  }
+  for (; i < n; ++i) s += src[(int64_t)i * stride];
+  return s;
+}
+
+// T = sum_b tpart[b] (fp32, [M, r]) and dB = bf16(s sum_z gpart[z]) ([P, r])
+// of every job, each sum in fixed order.
+__global__ __launch_bounds__(256) void pair_finish_kernel(PairArgs a) {
+  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  for (int k = 0; k < a.njobs; ++k) {
+    const PairJob& J = a.job[k];
+    const int64_t nt = a.M * J.r, ng = a.P * J.r;
+    if (i < nt) {
+      J.T[i] = ordered_sum(J.tpart + i, a.nb, nt);
+      return;
+    }
+    i -= nt;
+    if (i < ng) {
+      J.dB[i] = (uint16_t)(pack_bf16x2(J.s * ordered_sum(J.gpart + i, a.S, ng), 0.0f) & 0xFFFFu);
+      return;
+    }
+    i -= ng;
+  }
+}
+
 // out = bf16(s * sum_z part[z]), layout [P, r] (dB) or [r, P] (dA).
 __global__ __launch_bounds__(256) void grad_finish_kernel(const float* __restrict__ part, int S, int64_t P, int r,
                                                           float s, int out_rp, uint16_t* __restrict__ out) {
@@ -1155,6 +1327,38 @@ hipError_t launch_transpose_multi(const TransposeJobs& J, hipStream_t st) {
 hipError_t launch_transpose_rn(const uint16_t* B, int64_t N, int r, uint16_t* BT, hipStream_t st) {
   if (N * r == 0) return hipSuccess;
   transpose_rn_kernel<<<grid1(N * r, 256), 256, 0, st>>>(B, N, r, BT);
+  return hipGetLastError();
+}
+
+void plan_lora_pair(PairArgs& a, int64_t M, int64_t P, int r) {
+  const int msplits = qplan::plan_grad_msplits(M, P, r);
+  const int64_t mps = (((M + msplits - 1) / msplits) + 31) / 32 * 32;
+  a.M = M;
+  a.P = P;
+  a.m_per_split = mps > 0 ? mps : 32;
+  a.S = (int)((M + a.m_per_split - 1) / a.m_per_split);
+  a.nb = (int)((P + 511) / 512);
+}
+
+hipError_t launch_lora_pair(const PairArgs& a, hipStream_t st) {
+  if (a.M == 0 || a.P == 0 || a.njobs < 1 || a.njobs > 2) return a.njobs < 1 || a.njobs > 2 ? hipErrorInvalidValue
+                                                                                              : hipSuccess;
+  for (int k = 0; k < a.njobs; ++k)
+    if (a.job[k].r < 1 || a.job[k].r > 16) return hipErrorInvalidValue;
+  if (a.P % 8 != 0) return hipErrorInvalidValue;
+  lora_pair16_kernel<<<dim3((unsigned)a.nb, (unsigned)a.S, (unsigned)a.njobs), 256, 0, st>>>(a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  int64_t n = 0;
+  for (int k = 0; k < a.njobs; ++k) n += (a.M + a.P) * a.job[k].r;
+  pair_finish_kernel<<<grid1(n, 256), 256, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_grad_finish(const float* part, int S, int64_t P, int r, float s, int out_rp, uint16_t* out,
+                              hipStream_t st) {
+  if (P * r == 0) return hipSuccess;
+  grad_finish_kernel<<<grid1(P * r, 256), 256, 0, st>>>(part, S, P, r, s, out_rp, out);
   return hipGetLastError();
 }
 

@@ -65,6 +65,11 @@ struct GemmArgs {
   // instead of bf16 to out0
   int64_t lda;
   int32_t out_f32;
+  // bgemm_kernel, SwiGLU backward only: the down layer's rank-r product
+  // T^T H (T = l0.V fp32 [M, r], r = l0.r <= 32; H = silu(in0) in1 rounded
+  // to bf16) as per-token-tile fp32 partials dad_part[tiles_m][Nout][r]
+  // (null: not computed)
+  float* dad_part;
 };
 
 // Skinny-M forward GEMM (qlora_skinny.hip): out[m, n] = sum_k X[m, k]
@@ -154,6 +159,10 @@ hipError_t launch_qgemm(int mode, const GemmArgs& a, const qplan::GemmPlan& pl, 
 hipError_t launch_bgemm(int mode, const GemmArgs& a, hipStream_t st);
 // Sum of the H A^T partials of launch_bgemm (MODE_FWD_SWIGLU) in tile order.
 hipError_t launch_had_finish(const float* part, int tiles, int64_t M, int r, float* out, hipStream_t st);
+// out = bf16(s * sum_z part[z]) over S fp32 partials [S][P][r], written as
+// [P, r] (out_rp = 0) or [r, P] (out_rp = 1)
+hipError_t launch_grad_finish(const float* part, int S, int64_t P, int r, float s, int out_rp, uint16_t* out,
+                              hipStream_t st);
 // Output head + cross-entropy helpers (qlora_ce.hip).
 hipError_t launch_ce_count(const int32_t* targets, int64_t T, int64_t V, int32_t ignore, int32_t* n_valid,
                            hipStream_t st);
@@ -192,6 +201,36 @@ hipError_t launch_lora_down(const uint16_t* Z, int64_t M, int64_t Kred, const ui
                             hipStream_t st, bool finish = true);
 // B [N, r] -> B^T [r, N]
 hipError_t launch_transpose_rn(const uint16_t* B, int64_t N, int r, uint16_t* BT, hipStream_t st);
+
+// Both LoRA products of one gradient-sized operand Z [M, P] (bf16) from a
+// single read of Z: T = Z Bt^T ([M, r] fp32, Bt = B^T [r, P] bf16) and
+// dB = s Z^T V ([P, r] bf16, V [M, r] fp32), r <= 16.  Up to two such jobs
+// of the same M and P run in one launch; the kernel writes T partials per
+// 512-column block (tpart [nb][M][r]) and dB partials per token split
+// (gpart [S][P][r]); the finish launch adds them in fixed order.
+struct PairJob {
+  const uint16_t* Z;
+  const uint16_t* Bt;
+  const float* V;
+  int32_t r;
+  float s;
+  float* tpart;
+  float* gpart;
+  float* T;
+  uint16_t* dB;
+};
+struct PairArgs {
+  PairJob job[2];
+  int32_t njobs;
+  int64_t M, P;
+  int64_t m_per_split;  // tokens per split (a multiple of 32)
+  int32_t S;            // token splits
+  int32_t nb;           // 512-column blocks
+};
+// Fills the split and block counts of a for M, P (r of the jobs <= 16);
+// the partial buffers need qplan::pair_part_floats(M, P, r) floats per job.
+void plan_lora_pair(PairArgs& a, int64_t M, int64_t P, int r);
+hipError_t launch_lora_pair(const PairArgs& a, hipStream_t st);
 // Several transposes in one launch: job k, src [rows, cols] -> dst [cols, rows].
 struct TransposeJobs {
   const uint16_t* src[6];

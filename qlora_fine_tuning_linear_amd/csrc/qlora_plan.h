@@ -169,6 +169,21 @@ inline bool use_bgemm(int64_t M) { return M >= kBgemmMinTokens; }
 // Rows of the bf16 gate|up workspace: blocks of 128 gate rows + 128 up rows.
 inline int64_t pair_rows(int64_t I) { return 256 * cdiv(I, 128); }
 
+// The MLP backward takes T = Z B and dB = s Z^T V of each layer from one
+// pass over Z (dY, dG, dU) when every rank is at most 16.  The pass splits
+// tokens like the gradient reduction (32-token multiples) and columns in
+// blocks of 512; its partials take nb M r + S P r floats per job.
+inline bool use_lora_pair(int rg, int ru, int rd) {
+  return rg >= 1 && rg <= 16 && ru >= 1 && ru <= 16 && rd >= 1 && rd <= 16;
+}
+inline size_t pair_part_floats(int64_t M, int64_t P, int r) {
+  const int msplits = plan_grad_msplits(M, P, r);
+  int64_t mps = (((M + msplits - 1) / msplits) + 31) / 32 * 32;
+  if (mps <= 0) mps = 32;
+  const int64_t S = cdiv(M, mps), nb = cdiv(P, 512);
+  return (size_t)nb * M * r + (size_t)S * P * r;
+}
+
 struct LinearWs {
   size_t fwd_part, fwd_down;             // forward: split-K partials, down-proj partials
   size_t fwd_xt;                         // skinny forward: the re-laid-out activations
@@ -208,16 +223,27 @@ inline LinearWs linear_ws(int64_t M, int64_t N, int64_t K, int r) {
   const int gs_a = plan_grad_msplits(M, K, r);
   size_t gb = align256((size_t)gs_b * N * r * 4), ga = align256((size_t)gs_a * K * r * 4);
   w.bwd_grad = gb > ga ? gb : ga;
+  // T = dY B and dB from one pass over dY (rank <= 16) share that region
+  if (r >= 1 && r <= 16) {
+    const size_t pp = align256(pair_part_floats(M, N, r) * 4);
+    if (pp > w.bwd_grad) w.bwd_grad = pp;
+  }
   w.bwd_total = w.bwd_T + w.bwd_BT + w.bwd_part + w.bwd_down + w.bwd_grad + w.wbuf;
   w.total = w.fwd_total > w.bwd_total ? w.fwd_total : w.bwd_total;
   if (w.total == 0) w.total = 256;
   return w;
 }
 
+// SwiGLU backward on the bf16 path: the down layer's dA = s T^T H is
+// computed in the dH GEMM's epilogue (from the G, U it reads anyway) for
+// ranks up to 32.
+inline bool fuse_dad(int rd) { return rd >= 1 && rd <= 32; }
+
 struct MlpWs {
   size_t fwd_H, fwd_down;                            // H bf16 [M, I], down-proj partials
   size_t bwd_Td, bwd_dG, bwd_dU, bwd_Tg, bwd_Tu, bwd_BT, bwd_down, bwd_grad;
   size_t fwd_had;                                    // H A_d^T column-tile partials (bgemm, r_d <= 32)
+  size_t bwd_pair;                                   // single-pass LoRA product partials (ranks <= 16)
   size_t fwd_wbuf, bwd_wbuf;                         // bf16 weight copies (bgemm only), at the end
   size_t fwd_total, bwd_total, total;
 };
@@ -259,9 +285,20 @@ inline MlpWs mlp_ws(int64_t M, int64_t D, int64_t I, int rg, int ru, int rd) {
     size_t b = align256((size_t)ms * Ps[i] * Rs[i] * 4);
     if (b > g) g = b;
   }
+  // the dH GEMM's per-token-tile partials of dA_d (bgemm, r_d <= 32)
+  if (use_bgemm(M) && fuse_dad(rd)) {
+    const size_t b = align256((size_t)cdiv(M, 256) * I * rd * 4);
+    if (b > g) g = b;
+  }
   w.bwd_grad = g;
+  if (use_lora_pair(rg, ru, rd)) {
+    // the dY job (Td, dB_d), then the dG and dU jobs together
+    const size_t a = pair_part_floats(M, D, rd);
+    const size_t b = pair_part_floats(M, I, rg) + pair_part_floats(M, I, ru);
+    w.bwd_pair = align256((a > b ? a : b) * 4);
+  }
   w.bwd_total = w.bwd_Td + w.bwd_dG + w.bwd_dU + w.bwd_Tg + w.bwd_Tu + w.bwd_BT + w.bwd_down + w.bwd_grad +
-                w.bwd_wbuf;
+                w.bwd_pair + w.bwd_wbuf;
   w.total = w.fwd_total > w.bwd_total ? w.fwd_total : w.bwd_total;
   if (w.total == 0) w.total = 256;
   return w;

@@ -53,6 +53,9 @@ SMALL = [
     synth.MlpCfg("m513_d256_i384_r64_dq", M=513, D=256, I=384, r=64, alpha=16.0, dq_group=256),
     synth.MlpCfg("m1100_d320_i448_r16", M=1100, D=320, I=448, r=16, alpha=16.0, dq_group=0),
     synth.MlpCfg("m1537_d192_i576_r32_dq", M=1537, D=192, I=576, r=32, alpha=32.0, dq_group=256),
+    # down rank 20: the dH GEMM's fused T^T H runs its second 16-rank frag
+    # with four live ranks; ragged token and column tiles
+    synth.MlpCfg("m777_d192_i320_r20", M=777, D=192, I=320, r=20, alpha=16.0, dq_group=0),
     # rank 128 on every layer: r_g + r_u = 256 exceeds one down-projection
     # launch, below and above the 512-token switch to the bf16-copy GEMMs
     synth.MlpCfg("m200_d256_i384_r128", M=200, D=256, I=384, r=128, alpha=16.0, dq_group=0),
