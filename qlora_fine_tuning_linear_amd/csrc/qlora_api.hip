@@ -836,14 +836,17 @@ int qlora_mlp_bwd(const qlora_mlp* P, const void* dY, const void* X, const qlora
     }
   }
   // gate / up LoRA gradients (dB_g, dB_u already done by the single pass)
-  if (!pair)
-    QHIP(launch_lora_grad(0, dG, nullptr, M, I, S->XA_g, rg, sg, qplan::plan_grad_msplits(M, I, rg), grad_part, 0,
-                          u16m(G->dB_g), st));
+  if (pair) {
+    // dA_g = s_g Tg^T X and dA_u = s_u Tu^T X from one pass over X
+    QHIP(launch_lora_grad2(u16(X), M, D, Tg, rg, sg, u16m(G->dA_g), Tu, ru, su, u16m(G->dA_u), grad_part, st));
+    return QLORA_OK;
+  }
+  QHIP(launch_lora_grad(0, dG, nullptr, M, I, S->XA_g, rg, sg, qplan::plan_grad_msplits(M, I, rg), grad_part, 0,
+                        u16m(G->dB_g), st));
   QHIP(launch_lora_grad(0, u16(X), nullptr, M, D, Tg, rg, sg, qplan::plan_grad_msplits(M, D, rg), grad_part, 1,
                         u16m(G->dA_g), st));
-  if (!pair)
-    QHIP(launch_lora_grad(0, dU, nullptr, M, I, S->XA_u, ru, su, qplan::plan_grad_msplits(M, I, ru), grad_part, 0,
-                          u16m(G->dB_u), st));
+  QHIP(launch_lora_grad(0, dU, nullptr, M, I, S->XA_u, ru, su, qplan::plan_grad_msplits(M, I, ru), grad_part, 0,
+                        u16m(G->dB_u), st));
   QHIP(launch_lora_grad(0, u16(X), nullptr, M, D, Tu, ru, su, qplan::plan_grad_msplits(M, D, ru), grad_part, 1,
                         u16m(G->dA_u), st));
   return QLORA_OK;

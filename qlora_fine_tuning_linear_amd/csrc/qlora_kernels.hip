@@ -899,11 +899,15 @@ __global__ __launch_bounds__(256) void lora_grad_kernel(const uint16_t* __restri
 // after the register transpose operand t holds, for row c, column
 // p0 + 8c + t of those 8 tokens, and the V operand holds V[token][j = c].
 // ------------------------------------------------------------------------
-template <int ZMODE>
-__global__ __launch_bounds__(256) void lora_grad16_kernel(const uint16_t* __restrict__ Z0,
+// NV = 2: a second V (V1, rank r1, partials part1) against the same Z, so
+// that two layers that share their input (gate and up) take their dA from one
+// pass over it.
+template <int ZMODE, int NV>
+__device__ __forceinline__ void lora_grad16_body(const uint16_t* __restrict__ Z0,
                                                           const uint16_t* __restrict__ Z1, int64_t M, int64_t P,
                                                           const float* __restrict__ V, int r, int64_t m_per_split,
-                                                          float* __restrict__ part) {
+                                                          float* __restrict__ part, const float* __restrict__ V1 = nullptr,
+                                                          int r1 = 0, float* __restrict__ part1 = nullptr) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = lane & 15, q = lane >> 4;
   const int64_t p0 = ((int64_t)blockIdx.x * 4 + wave) * 128;
@@ -914,15 +918,18 @@ __global__ __launch_bounds__(256) void lora_grad16_kernel(const uint16_t* __rest
   int64_t pc = p0 + 8 * c;
   if (pc > P - 8) pc = P - 8;
   const int jv = c < r ? c : r - 1;
+  const int jv1 = NV > 1 ? (c < r1 ? c : r1 - 1) : 0;
 
-  f32x4 acc[8];
+  f32x4 acc[NV][8];
 #pragma unroll
-  for (int t = 0; t < 8; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int k = 0; k < NV; ++k)
+#pragma unroll
+    for (int t = 0; t < 8; ++t) acc[k][t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
   constexpr int NZ = ZMODE == 0 ? 1 : 2;
   struct Slab {
     u32x4 raw[NZ][8];
-    float x[8];
+    float x[NV][8];
   };
   auto load = [&](int64_t ms, Slab& S) {
 #pragma unroll
@@ -931,7 +938,8 @@ __global__ __launch_bounds__(256) void lora_grad16_kernel(const uint16_t* __rest
       if (mm >= me) mm = me - 1;
       S.raw[0][e] = *reinterpret_cast<const u32x4*>(Z0 + mm * P + pc);
       if constexpr (ZMODE == 1) S.raw[NZ - 1][e] = *reinterpret_cast<const u32x4*>(Z1 + mm * P + pc);
-      S.x[e] = V[mm * r + jv];
+      S.x[0][e] = V[mm * r + jv];
+      if constexpr (NV > 1) S.x[NV - 1][e] = V1[mm * r1 + jv1];
     }
   };
   auto slab = [&](int64_t ms, const Slab& S) {
@@ -959,13 +967,17 @@ __global__ __launch_bounds__(256) void lora_grad16_kernel(const uint16_t* __rest
       for (int d = 0; d < 4; ++d)
         aop[t][d] = __builtin_amdgcn_perm(rows[2 * d + 1][t >> 1], rows[2 * d][t >> 1], sel);
     }
-    float x[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = (c < r && ms + 8 * q + e < me) ? S.x[e] : 0.0f;
-    const u32x4 vop{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
-                    pack_bf16x2(x[6], x[7])};
+    for (int k = 0; k < NV; ++k) {
+      const int rk = k == 0 ? r : r1;
+      float x[8];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) acc[t] = mfma16k32(aop[t], vop, acc[t]);
+      for (int e = 0; e < 8; ++e) x[e] = (c < rk && ms + 8 * q + e < me) ? S.x[k][e] : 0.0f;
+      const u32x4 vop{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
+                      pack_bf16x2(x[6], x[7])};
+#pragma unroll
+      for (int t = 0; t < 8; ++t) acc[k][t] = mfma16k32(aop[t], vop, acc[k][t]);
+    }
   };
   Slab ra, rb;
   int64_t ms = mb;
@@ -978,15 +990,36 @@ __global__ __launch_bounds__(256) void lora_grad16_kernel(const uint16_t* __rest
   }
   if (ms < me) slab(ms, ra);
 
-  // acc[t][v] = C[row 4q + v][j = c]: column p = p0 + 8 (4q + v) + t
-  if (c >= r) return;
+  // acc[k][t][v] = C[row 4q + v][j = c]: column p = p0 + 8 (4q + v) + t
 #pragma unroll
-  for (int t = 0; t < 8; ++t)
+  for (int k = 0; k < NV; ++k) {
+    const int rk = k == 0 ? r : r1;
+    float* pk = k == 0 ? part : part1;
+    if (c >= rk) continue;
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int64_t pp = p0 + 8 * (4 * q + v) + t;
-      if (pp < P) part[((int64_t)z * P + pp) * r + c] = acc[t][v];
-    }
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int64_t pp = p0 + 8 * (4 * q + v) + t;
+        if (pp < P) pk[((int64_t)z * P + pp) * rk + c] = acc[k][t][v];
+      }
+  }
+}
+
+template <int ZMODE>
+__global__ __launch_bounds__(256) void lora_grad16_kernel(const uint16_t* __restrict__ Z0,
+                                                          const uint16_t* __restrict__ Z1, int64_t M, int64_t P,
+                                                          const float* __restrict__ V, int r, int64_t m_per_split,
+                                                          float* __restrict__ part) {
+  lora_grad16_body<ZMODE, 1>(Z0, Z1, M, P, V, r, m_per_split, part);
+}
+
+// the two-V form, held to two waves per SIMD
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void lora_grad16x2_kernel(
+    const uint16_t* __restrict__ Z, int64_t M, int64_t P, const float* __restrict__ V0, int r0,
+    int64_t m_per_split, float* __restrict__ part0, const float* __restrict__ V1, int r1,
+    float* __restrict__ part1) {
+  lora_grad16_body<0, 2>(Z, nullptr, M, P, V0, r0, m_per_split, part0, V1, r1, part1);
 }
 
 // ------------------------------------------------------------------------
@@ -1359,6 +1392,57 @@ hipError_t launch_grad_finish(const float* part, int S, int64_t P, int r, float 
                               hipStream_t st) {
   if (P * r == 0) return hipSuccess;
   grad_finish_kernel<<<grid1(P * r, 256), 256, 0, st>>>(part, S, P, r, s, out_rp, out);
+  return hipGetLastError();
+}
+
+// Two finishes in one launch: out_k = bf16(s_k sum_z part_k[z]) as [r_k, P].
+__global__ __launch_bounds__(256) void grad_finish2_kernel(const float* __restrict__ part0, int r0, float s0,
+                                                           uint16_t* __restrict__ out0,
+                                                           const float* __restrict__ part1, int r1, float s1,
+                                                           uint16_t* __restrict__ out1, int S, int64_t P) {
+  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const float* part = part0;
+  int r = r0;
+  float s = s0;
+  uint16_t* out = out0;
+  if (i >= P * r0) {
+    i -= P * r0;
+    if (i >= P * r1) return;
+    part = part1;
+    r = r1;
+    s = s1;
+    out = out1;
+  }
+  float acc = 0.0f;
+  const int64_t stride = P * r;
+  int z = 0;
+  for (; z + 8 <= S; z += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = part[(int64_t)(z + u) * stride + i];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc += v[u];
+  }
+  for (; z < S; ++z) acc += part[(int64_t)z * stride + i];
+  const int64_t pp = i / r;
+  const int j = (int)(i % r);
+  out[(int64_t)j * P + pp] = (uint16_t)(pack_bf16x2(s * acc, 0.0f) & 0xFFFFu);
+}
+
+hipError_t launch_lora_grad2(const uint16_t* Z, int64_t M, int64_t P, const float* V0, int r0, float s0,
+                             uint16_t* out0, const float* V1, int r1, float s1, uint16_t* out1, float* part,
+                             hipStream_t st) {
+  if (M == 0 || P == 0) return hipSuccess;
+  if (r0 < 1 || r0 > 16 || r1 < 1 || r1 > 16 || P % 8 != 0) return hipErrorInvalidValue;
+  const int rmax = r0 > r1 ? r0 : r1;
+  const int msplits = qplan::plan_grad_msplits(M, P, rmax);
+  const int64_t mps = (((M + msplits - 1) / msplits) + 31) / 32 * 32;
+  const int S = (int)((M + mps - 1) / mps);
+  float* part1 = part + (size_t)S * P * r0;
+  lora_grad16x2_kernel<<<dim3(grid1(P, 512), (unsigned)S), 256, 0, st>>>(Z, M, P, V0, r0, mps, part, V1, r1, part1);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  grad_finish2_kernel<<<grid1(P * (r0 + r1), 256), 256, 0, st>>>(part, r0, s0, out0, part1, r1, s1, out1, S, P);
   return hipGetLastError();
 }
 

@@ -252,6 +252,12 @@ struct TransposeBatch {
   }
 };
 hipError_t launch_transpose_multi(const TransposeJobs& J, hipStream_t st);
+// dA of two layers that share their input Z [M, P] from one pass over it:
+// out_k = bf16(s_k V_k^T Z) as [r_k, P] (r_k <= 16, P % 8 == 0); part holds
+// the token-split partials of both (lora_grad2_part_floats of them).
+hipError_t launch_lora_grad2(const uint16_t* Z, int64_t M, int64_t P, const float* V0, int r0, float s0,
+                             uint16_t* out0, const float* V1, int r1, float s1, uint16_t* out1, float* part,
+                             hipStream_t st);
 hipError_t launch_lora_grad(int zmode, const uint16_t* Z0, const uint16_t* Z1, int64_t M, int64_t P,
                             const float* V, int r, float s, int msplits, float* part, int out_rp, uint16_t* out,
                             hipStream_t st);

@@ -292,6 +292,10 @@ inline MlpWs mlp_ws(int64_t M, int64_t D, int64_t I, int rg, int ru, int rd) {
   }
   w.bwd_grad = g;
   if (use_lora_pair(rg, ru, rd)) {
+    // dA_g and dA_u from one pass over X: both ranks' token-split partials
+    const int rm = rg > ru ? rg : ru;
+    const size_t b2 = align256((size_t)plan_grad_msplits(M, D, rm) * D * (rg + ru) * 4);
+    if (b2 > w.bwd_grad) w.bwd_grad = b2;
     // the dY job (Td, dB_d), then the dG and dU jobs together
     const size_t a = pair_part_floats(M, D, rd);
     const size_t b = pair_part_floats(M, I, rg) + pair_part_floats(M, I, ru);
