@@ -94,10 +94,16 @@ PROFILE_OF_WORKLOAD = {"llama3_8b_mlp_m8192_r16": "kernel_stats_mlp_llama3_8b_m8
 
 
 def kernel_key(csv_name):
-    """'void qk::bgemm_kernel<1>(GemmArgs)' -> 'bgemm_fwd_swiglu' (None for other kernels)."""
+    """'void qk::bgemm_kernel<1>(GemmArgs)' -> 'bgemm_fwd_swiglu', the skinny
+    GEMMs -> 'skinny_fwd' / 'skinny_bwd' (None for other kernels)."""
     import re
     m = re.search(r"\b([qb]gemm)_kernel<(\d+)", csv_name)
-    return None if not m else "%s_%s" % (m.group(1), KIND_OF_MODE[int(m.group(2))])
+    if m:
+        return "%s_%s" % (m.group(1), KIND_OF_MODE[int(m.group(2))])
+    m = re.search(r"\bskinny_(fwd2?|bwd)_kernel<", csv_name)
+    if m:
+        return "skinny_%s" % m.group(1).rstrip("2")
+    return None
 
 
 def summarize_traffic(fetch_csv, write_csv, copy_mib, command):
