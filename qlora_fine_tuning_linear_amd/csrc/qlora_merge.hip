@@ -21,7 +21,9 @@ namespace qk {
 // v_mfma_f32_32x32x16_bf16 steps (j past r is zero on both operands).
 // Accumulator v of lane l is then column k0 + 8(v/4) + 4(l/32) + v%4 of row
 // n0 + l%32, i.e. of the lane's own row, whose code bytes and absmax values
-// for the MG_COLS columns the lane loads up front.  The 16-bit results go to a
+// for the MG_COLS columns the lane loads up front.  A's columns are staged
+// once per workgroup in LDS, transposed (A^T rows of 16-byte rank chunks),
+// so that each MFMA A operand is one 16-byte LDS read.  The 16-bit results go to a
 // per-wave LDS tile (rows padded by 16 bytes) and leave as whole row segments
 // (2 * MG_COLS bytes), several rows per store instruction.
 // ------------------------------------------------------------------------
@@ -36,8 +38,11 @@ __global__ __launch_bounds__(256) void merge_kernel(Nf4Dev w, const float* __res
                                                     int r, float s, uint16_t* __restrict__ out) {
   __shared__ float cb[16];
   __shared__ __attribute__((aligned(16))) uint16_t tile[4][32 * MG_LD];
+  // A^T of the workgroup's columns, [MG_COLS][16 JS + 8] (ranks past r zero;
+  // the 16-byte pad keeps the 8-lane passes of the 16-byte reads and writes
+  // on distinct banks): dynamic, 16 JS + 8 elements per column
+  extern __shared__ __attribute__((aligned(16))) uint16_t at[];
   if (threadIdx.x < 16) cb[threadIdx.x] = codebook[threadIdx.x];
-  __syncthreads();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l32 = lane & 31, g = lane >> 5;
   const int64_t N = w.N, K = w.K;
@@ -47,7 +52,24 @@ __global__ __launch_bounds__(256) void merge_kernel(Nf4Dev w, const float* __res
   const int64_t kb = (int64_t)blockIdx.y * MG_COLS;
   const int ncols = (int)((K - kb) < MG_COLS ? (K - kb) : MG_COLS);  // multiple of 64
   const int JS = (r + 15) / 16;                               // 16-wide steps over the rank, <= 8
+  const int ald = 16 * JS + 8;                                 // A^T row stride, elements
   uint16_t* T = tile[wave];
+  {
+    // thread c: column kb + c of A, 8 ranks per 16-byte LDS store
+    const int c = threadIdx.x;
+    const bool cok = c < ncols;
+    for (int h = 0; h < 2 * JS; ++h) {
+      uint32_t v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int j = 8 * h + i;
+        v[i] = (cok && j < r) ? (uint32_t)A[(int64_t)j * K + kb + c] : 0u;
+      }
+      *reinterpret_cast<u32x4*>(at + c * ald + 8 * h) =
+          u32x4{v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16), v[6] | (v[7] << 16)};
+    }
+  }
+  __syncthreads();
 
   // the row's codes (32 columns per 16 bytes) and absmax (64 columns each)
   u32x4 cw[MG_T];
@@ -86,13 +108,7 @@ __global__ __launch_bounds__(256) void merge_kernel(Nf4Dev w, const float* __res
 #pragma unroll
     for (int js = 0; js < 8; ++js) {
       if (js >= JS) break;
-      uint32_t h[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int j = 16 * js + 8 * g + i;
-        h[i] = j < r ? (uint32_t)A[(int64_t)j * K + k0 + l32] : 0u;
-      }
-      const u32x4 aop{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+      const u32x4 aop = *reinterpret_cast<const u32x4*>(at + (32 * t + l32) * ald + 16 * js + 8 * g);
       acc = mfma32(aop, bop[js], acc);
     }
     const float a = am[t >> 1];
@@ -139,9 +155,10 @@ hipError_t launch_merge(const Nf4Dev& w, const float* codebook, const uint16_t* 
   if (w.N == 0 || w.K == 0) return hipSuccess;
   if (r < 1 || r > 128 || w.K % 64 != 0) return hipErrorInvalidValue;
   const dim3 grid((unsigned)((w.N + 127) / 128), (unsigned)((w.K + MG_COLS - 1) / MG_COLS));
+  const size_t at_bytes = (size_t)MG_COLS * (16 * ((r + 15) / 16) + 8) * 2;
   if (f16)
-    merge_kernel<true><<<grid, 256, 0, st>>>(w, codebook, A, B, r, s, out);
+    merge_kernel<true><<<grid, 256, at_bytes, st>>>(w, codebook, A, B, r, s, out);
   else
-    merge_kernel<false><<<grid, 256, 0, st>>>(w, codebook, A, B, r, s, out);
+    merge_kernel<false><<<grid, 256, at_bytes, st>>>(w, codebook, A, B, r, s, out);
   return hipGetLastError();
 }
