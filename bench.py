@@ -42,10 +42,10 @@ def parse():
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="first run one plain device-to-device copy of this many MiB (the known-size kernel "
                          "that calibrates the FETCH_SIZE / WRITE_SIZE counters)")
-    ap.add_argument("--only", default=None, metavar="IDX|merge|rmsnorm|qkv|ce",
+    ap.add_argument("--only", default=None, metavar="IDX|merge|rmsnorm|qkv|ce|rmsmlp",
                     help="profiling aid: time only workload config IDX (0-4; the skinny linear with 4 rotated "
-                         "weight copies), the 16-bit merge, RMSNorm, the packed q/k/v adapters or the fused head + "
-                         "cross-entropy, and print its "
+                         "weight copies), the 16-bit merge, RMSNorm, the packed q/k/v adapters, the fused head + "
+                         "cross-entropy or the RMSNorm + MLP forward (fused against two calls), and print its "
                          "own JSON line instead of the metric line")
     ap.add_argument("--summarize-traffic", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_MIB"),
                     help="no GPU: turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, "
@@ -468,6 +468,56 @@ def rmsnorm_bench(q, synth, steps, warmup, M=8192, D=4096, eps=1e-5):
                 bwd_frac_hbm_peak=bb / (b_ms * 1e-3) / 1e9 / HBM_PEAK_GBS)
 
 
+def rms_mlp_bench(q, synth, steps, warmup, idx=2, eps=1e-5):
+    """RMSNorm + MLP forward of the Llama-3-8B-shaped block: the two-call path
+    (rmsnorm_fwd writes the normalised input, qlora_mlp_fwd reads it) against
+    qlora_mlp_fwd_rmsnorm, with and without the normalised input kept."""
+    import torch
+    cfg = synth.CONFIGS[idx]
+    M, D = cfg.M, cfg.D
+    inp = synth.mlp_inputs(cfg, synth.seed_of(idx))
+    cb = torch.from_numpy(synth.nf4_codebook()).cuda()
+
+    def lin(W, A, B):
+        Wd = torch.from_numpy(W).cuda()
+        w = q.nf4_quantize(Wd, cb, dq_group=cfg.dq_group)
+        del Wd
+        return q.QLoraLinear(w, dev_bf16(A), dev_bf16(B), cfg.alpha)
+
+    P = q.QLoraMlp(lin(inp["Wg"], inp["Ag"], inp["Bg"]), lin(inp["Wu"], inp["Au"], inp["Bu"]),
+                   lin(inp["Wd"], inp["Ad"], inp["Bd"]))
+    X = dev_bf16(inp["X"])
+    del inp
+    w = dev_bf16(synth.normal_bf16(1, 42, D, 1.0, 0.1))
+    Y, Xn = torch.empty(M, D, dtype=torch.bfloat16, device="cuda"), torch.empty(M, D, dtype=torch.bfloat16,
+                                                                                device="cuda")
+    rstd = torch.empty(M, dtype=torch.float32, device="cuda")
+    S = q.alloc_mlp_saved(P, M, "cuda")
+    ws = torch.empty(max(q.qlora_mlp_workspace_bytes(P, M), q.qlora_mlp_rmsnorm_workspace_bytes(P, M)),
+                     dtype=torch.uint8, device="cuda")
+
+    def timed(f):
+        for _ in range(warmup):
+            f()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            f()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    def two_call():
+        q.rmsnorm_fwd(X, w, eps, Y=Xn, rstd=rstd)
+        q.qlora_mlp_fwd(P, Xn, Y=Y, saved=S, ws=ws)
+
+    t2 = timed(two_call)
+    tf = timed(lambda: q.qlora_mlp_fwd_rmsnorm(P, X, w, eps, Y=Y, saved=S, rstd=rstd, ws=ws))
+    tx = timed(lambda: q.qlora_mlp_fwd_rmsnorm(P, X, w, eps, Y=Y, saved=S, rstd=rstd, Xn=Xn, ws=ws))
+    return dict(workload="rmsnorm_mlp_fwd_%s" % cfg.name, two_call_ms=t2, fused_ms=tf, fused_keep_xn_ms=tx)
+
+
 def ce_bench(q, synth, steps, warmup, T=4096, D=4096, V=128256, chunk=1024):
     """qlora_linear_ce at the page's example (4096 tokens, hidden 4096, a 128256
     class vocabulary): loss and dX in token chunks.  FLOPs: the logits and the
@@ -591,8 +641,9 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    if a.only in ("merge", "rmsnorm", "qkv", "ce"):
-        fn = {"merge": merge_bench, "rmsnorm": rmsnorm_bench, "qkv": grouped_bench, "ce": ce_bench}[a.only]
+    if a.only in ("merge", "rmsnorm", "qkv", "ce", "rmsmlp"):
+        fn = {"merge": merge_bench, "rmsnorm": rmsnorm_bench, "qkv": grouped_bench, "ce": ce_bench,
+              "rmsmlp": rms_mlp_bench}[a.only]
         s = fn(q, synth, max(10, a.steps), a.warmup)
         print(json.dumps({k: (round(v, 4) if isinstance(v, float) else v) for k, v in s.items()}), flush=True)
         return
@@ -659,6 +710,9 @@ def main():
         sec.append({k: (round(v, 4) if isinstance(v, float) else v) for k, v in s.items()})
         log("secondary: rmsnorm")
         s = rmsnorm_bench(q, synth, max(20, a.steps), a.warmup)
+        sec.append({k: (round(v, 4) if isinstance(v, float) else v) for k, v in s.items()})
+        log("secondary: rmsnorm + MLP forward, fused and two-call")
+        s = rms_mlp_bench(q, synth, max(10, a.steps), a.warmup)
         sec.append({k: (round(v, 4) if isinstance(v, float) else v) for k, v in s.items()})
         log("secondary: linear + cross-entropy")
         s = ce_bench(q, synth, max(3, a.steps // 3), min(a.warmup, 2))

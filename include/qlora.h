@@ -394,6 +394,32 @@ size_t qlora_mlp_workspace_bytes(const qlora_mlp* P, int64_t M);
 int qlora_mlp_fwd(const qlora_mlp* P, const void* X, int64_t M, void* Y,
                   const qlora_mlp_saved* S, void* ws, size_t ws_bytes, void* stream);
 
+/* Workspace bytes qlora_mlp_fwd_rmsnorm needs (0 for a rejected shape). */
+size_t qlora_mlp_rmsnorm_workspace_bytes(const qlora_mlp* P, int64_t M);
+
+/*
+ * qlora_mlp_fwd_rmsnorm: the RMSNorm in front of the block fused into its
+ * forward ("LLM Fine-Tuning in 2026: Unsloth vs QLoRA vs Liger-Kernel",
+ * section 2, the fused RMSNorm): the results of rmsnorm_fwd(X, norm_w, eps)
+ * -> (Xn, rstd) followed by qlora_mlp_fwd(P, Xn, ...), without Xn between
+ * them.  From 512 tokens the norm weight is folded into the expanded gate/up
+ * weights (column k times norm_w[k]), the inverse RMS of each token scales
+ * the gate/up product, and XA_g, XA_u are rstd * X (A w)^T; below 512 the
+ * norm runs as its own pass.  Roundings differ from the two-call path only
+ * inside the bf16 operands (bf16(W w) instead of bf16(X rstd w)).
+ *   X      bf16 [M, D] pre-norm input     norm_w bf16 [D]    eps as rmsnorm_fwd
+ *   Y, S   as qlora_mlp_fwd (S->XA_g, S->XA_u are those of the normalised input)
+ *   rstd   fp32 [M] output (for rmsnorm_bwd)
+ *   Xn     bf16 [M, D] output, or NULL: the normalised input is written only
+ *          when Xn is given (qlora_mlp_bwd takes it as its X)
+ *   ws     ws_bytes >= qlora_mlp_rmsnorm_workspace_bytes(P, M)
+ * Errors: those of qlora_mlp_fwd and of rmsnorm_fwd for D = the block's
+ * hidden size.  M == 0 is a no-op.
+ */
+int qlora_mlp_fwd_rmsnorm(const qlora_mlp* P, const void* X, const void* norm_w, float eps, int64_t M, void* Y,
+                          const qlora_mlp_saved* S, float* rstd, void* Xn, void* ws, size_t ws_bytes,
+                          void* stream);
+
 /*
  * qlora_mlp_bwd: gradients of <Y, dY> with sigma, silu and H recomputed from
  * the saved G and U:

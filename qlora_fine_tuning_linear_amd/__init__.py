@@ -30,6 +30,7 @@ EXPORTED = (
     "rmsnorm_fwd", "rmsnorm_bwd", "rmsnorm_bwd_workspace_bytes",
     "qlora_grouped_workspace_bytes", "qlora_grouped_fwd", "qlora_grouped_bwd",
     "qlora_linear_ce_workspace_bytes", "qlora_linear_ce", "qlora_linear_fwd_static", "qlora_debug_force_arch",
+    "qlora_mlp_rmsnorm_workspace_bytes", "qlora_mlp_fwd_rmsnorm",
 )
 QLORA_STATIC_SCRATCH_BYTES = 64 << 20
 
@@ -97,6 +98,9 @@ def load_library(path: str = LIB_PATH):
         "qlora_linear_bwd": (ctypes.c_int, [P(CLinear), vp, vp, vp, i64, vp, vp, vp, vp, sz, vp]),
         "qlora_mlp_workspace_bytes": (sz, [P(CMlp), i64]),
         "qlora_mlp_fwd": (ctypes.c_int, [P(CMlp), vp, i64, vp, P(CMlpSaved), vp, sz, vp]),
+        "qlora_mlp_rmsnorm_workspace_bytes": (sz, [P(CMlp), i64]),
+        "qlora_mlp_fwd_rmsnorm": (ctypes.c_int, [P(CMlp), vp, vp, ctypes.c_float, i64, vp, P(CMlpSaved), vp, vp,
+                                                 vp, sz, vp]),
         "qlora_mlp_bwd": (ctypes.c_int, [P(CMlp), vp, vp, P(CMlpSaved), i64, vp, P(CMlpGrads), vp, sz,
                                          vp]),
         "qlora_trace_install": (ctypes.c_int, [P(vp), P(vp), P(i32), i32, P(i32)]),
@@ -467,6 +471,33 @@ def qlora_mlp_fwd(P: QLoraMlp, X: torch.Tensor, Y=None, saved: Optional[MlpSaved
                            ws.numel(), _stream(dev))
     _check("qlora_mlp_fwd", st)
     return Y, saved
+
+
+def qlora_mlp_rmsnorm_workspace_bytes(P: QLoraMlp, M: int) -> int:
+    cm = P.c()
+    return int(load_library().qlora_mlp_rmsnorm_workspace_bytes(ctypes.byref(cm), M))
+
+
+def qlora_mlp_fwd_rmsnorm(P: QLoraMlp, X: torch.Tensor, norm_w: torch.Tensor, eps: float, Y=None,
+                          saved: Optional[MlpSaved] = None, rstd=None, want_xn: bool = False, Xn=None, ws=None):
+    """qlora_mlp_fwd_rmsnorm: returns (Y, MlpSaved, rstd fp32 [M], Xn bf16 [M, D] or None)."""
+    lib = load_library()
+    M = X.shape[0]
+    dev = X.device
+    _need(X, torch.bfloat16, (M, P.D), "X")
+    _need(norm_w, torch.bfloat16, (P.D,), "norm_w")
+    Y = torch.empty(M, P.D, dtype=torch.bfloat16, device=dev) if Y is None else Y
+    saved = alloc_mlp_saved(P, M, dev) if saved is None else saved
+    rstd = torch.empty(M, dtype=torch.float32, device=dev) if rstd is None else rstd
+    if want_xn and Xn is None:
+        Xn = torch.empty(M, P.D, dtype=torch.bfloat16, device=dev)
+    ws = _workspace(qlora_mlp_rmsnorm_workspace_bytes(P, M), dev) if ws is None else ws
+    cm, cs = P.c(), saved.c()
+    st = lib.qlora_mlp_fwd_rmsnorm(ctypes.byref(cm), X.data_ptr(), norm_w.data_ptr(), float(eps), M, Y.data_ptr(),
+                                   ctypes.byref(cs), rstd.data_ptr(), None if Xn is None else Xn.data_ptr(),
+                                   ws.data_ptr(), ws.numel(), _stream(dev))
+    _check("qlora_mlp_fwd_rmsnorm", st)
+    return Y, saved, rstd, Xn
 
 
 def qlora_mlp_bwd(P: QLoraMlp, dY: torch.Tensor, X: torch.Tensor, saved: MlpSaved, dX=None, grads=None, ws=None):

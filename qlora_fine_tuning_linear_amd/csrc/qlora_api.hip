@@ -596,12 +596,21 @@ int qlora_linear_bwd(const qlora_linear* L, const void* dY, const void* X, const
   return QLORA_OK;
 }
 
-int qlora_mlp_fwd(const qlora_mlp* P, const void* X, int64_t M, void* Y, const qlora_mlp_saved* S, void* ws,
-                  size_t ws_bytes, void* stream) {
-  QTRY(qv_mlp_fwd(P, X, M, Y, S, ws, ws_bytes));
-  if (M == 0) return QLORA_OK;
-  QTRY(check_device());
-  hipStream_t st = static_cast<hipStream_t>(stream);
+// The RMSNorm in front of the block folded into its first GEMM: the norm
+// weight multiplies the expanded gate/up weights' columns, the inverse RMS of
+// each token row scales that GEMM's product (its LoRA term included, which
+// therefore uses the unscaled X (A w)^T).
+struct RmsFold {
+  const uint16_t* w;   // norm weight [D]
+  const float* rstd;   // [M]
+  const float* xa_g;   // X (A_g w)^T, fp32 [M, r_g]
+  const float* xa_u;   // X (A_u w)^T
+};
+
+// The MLP forward on validated arguments (X the block's input; with rf, the
+// pre-norm input and XA_g / XA_u already written by the caller).
+static int mlp_fwd_impl(const qlora_mlp* P, const void* X, int64_t M, void* Y, const qlora_mlp_saved* S, void* ws,
+                        hipStream_t st, const RmsFold* rf) {
   const int64_t I = P->gate.W0.N, D = P->gate.W0.K;
   const qplan::MlpWs w = qplan::mlp_ws(M, D, I, P->gate.r, P->up.r, P->down.r);
   uint16_t* H = reinterpret_cast<uint16_t*>(bytes(ws));
@@ -612,7 +621,9 @@ int qlora_mlp_fwd(const qlora_mlp* P, const void* X, int64_t M, void* Y, const q
 
   // XA_g | XA_u in one pass over X (the down-projection kernels take a
   // combined rank of at most 128; above that, one pass per layer)
-  if (P->gate.r + P->up.r <= 128) {
+  if (rf) {
+    // done by the caller
+  } else if (P->gate.r + P->up.r <= 128) {
     QHIP(launch_lora_down(u16(X), M, D, u16(P->gate.A), P->gate.r, u16(P->up.A), P->up.r, S->XA_g, S->XA_u,
                           qplan::plan_down_splits(M, D), down_part, st));
   } else {
@@ -632,13 +643,15 @@ int qlora_mlp_fwd(const qlora_mlp* P, const void* X, int64_t M, void* Y, const q
     a.w1 = to_dev(P->up.W0);
     a.codebook = P->gate.W0.codebook;
     a.codebook1 = P->up.W0.codebook;
-    a.l0 = side_B(P->gate, S->XA_g);
-    a.l1 = side_B(P->up, S->XA_u);
+    a.l0 = side_B(P->gate, rf ? rf->xa_g : S->XA_g);
+    a.l1 = side_B(P->up, rf ? rf->xa_u : S->XA_u);
+    if (rf) a.row_scale = rf->rstd;
     a.out0 = u16m(S->G);
     a.out1 = u16m(S->U);
     a.out2 = H;
     if (wbuf) {
-      QHIP(launch_dequant_rows(a.w0, &a.w1, a.codebook, a.codebook1, qplan::pair_rows(I), wbuf, st));
+      QHIP(launch_dequant_rows(a.w0, &a.w1, a.codebook, a.codebook1, qplan::pair_rows(I), wbuf, st,
+                               rf ? rf->w : nullptr));
       a.wb = wbuf;
       a.ldw = D;
       a.wrows = qplan::pair_rows(I);
@@ -680,6 +693,55 @@ int qlora_mlp_fwd(const qlora_mlp* P, const void* X, int64_t M, void* Y, const q
     }
   }
   return QLORA_OK;
+}
+
+int qlora_mlp_fwd(const qlora_mlp* P, const void* X, int64_t M, void* Y, const qlora_mlp_saved* S, void* ws,
+                  size_t ws_bytes, void* stream) {
+  QTRY(qv_mlp_fwd(P, X, M, Y, S, ws, ws_bytes));
+  if (M == 0) return QLORA_OK;
+  QTRY(check_device());
+  return mlp_fwd_impl(P, X, M, Y, S, ws, static_cast<hipStream_t>(stream), nullptr);
+}
+
+int qlora_mlp_fwd_rmsnorm(const qlora_mlp* P, const void* X, const void* norm_w, float eps, int64_t M, void* Y,
+                          const qlora_mlp_saved* S, float* rstd, void* Xn, void* ws, size_t ws_bytes, void* stream) {
+  QTRY(qv_mlp_fwd_rmsnorm(P, X, norm_w, eps, M, Y, S, rstd, Xn, ws, ws_bytes));
+  if (M == 0) return QLORA_OK;
+  QTRY(check_device());
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t I = P->gate.W0.N, D = P->gate.W0.K;
+  const int rg = P->gate.r, ru = P->up.r;
+  const qplan::MlpRmsWs w = qplan::mlp_rms_ws(M, D, I, rg, ru, P->down.r);
+  char* extra = bytes(ws) + w.base;
+  if (!qplan::use_bgemm(M)) {
+    // below the bf16-GEMM threshold the GEMM expands NF4 in its own tiles:
+    // the norm runs as its own pass into Xn (or the workspace)
+    uint16_t* xn = Xn ? u16m(Xn) : reinterpret_cast<uint16_t*>(extra + w.at_g + w.at_u + w.xa);
+    QHIP(launch_rmsnorm_fwd(u16(X), u16(norm_w), M, D, eps, xn, rstd, st));
+    return mlp_fwd_impl(P, xn, M, Y, S, ws, st, nullptr);
+  }
+  uint16_t* ag = reinterpret_cast<uint16_t*>(extra);
+  uint16_t* au = reinterpret_cast<uint16_t*>(extra + w.at_g);
+  float* xag = reinterpret_cast<float*>(extra + w.at_g + w.at_u);
+  float* xau = xag + (size_t)M * rg;
+  float* down_part = reinterpret_cast<float*>(bytes(ws) + qplan::mlp_ws(M, D, I, rg, ru, P->down.r).fwd_H);
+  // rstd (and Xn when the caller keeps it for the backward)
+  QHIP(launch_rmsnorm_fwd(u16(X), u16(norm_w), M, D, eps, Xn ? u16m(Xn) : nullptr, rstd, st));
+  // X (A w)^T, then XA = rstd * X (A w)^T for the backward
+  QHIP(launch_scale_cols(u16(P->gate.A), rg, D, u16(norm_w), ag, st));
+  QHIP(launch_scale_cols(u16(P->up.A), ru, D, u16(norm_w), au, st));
+  if (rg + ru <= 128) {
+    QHIP(launch_lora_down(u16(X), M, D, ag, rg, au, ru, xag, xau, qplan::plan_down_splits(M, D), down_part, st));
+  } else {
+    QHIP(launch_lora_down(u16(X), M, D, ag, rg, nullptr, 0, xag, nullptr, qplan::plan_down_splits(M, D), down_part,
+                          st));
+    QHIP(launch_lora_down(u16(X), M, D, au, ru, nullptr, 0, xau, nullptr, qplan::plan_down_splits(M, D), down_part,
+                          st));
+  }
+  QHIP(launch_scale_rows(xag, M, rg, rstd, S->XA_g, st));
+  QHIP(launch_scale_rows(xau, M, ru, rstd, S->XA_u, st));
+  const RmsFold rf{u16(norm_w), rstd, xag, xau};
+  return mlp_fwd_impl(P, X, M, Y, S, ws, st, &rf);
 }
 
 int qlora_mlp_bwd(const qlora_mlp* P, const void* dY, const void* X, const qlora_mlp_saved* S, int64_t M, void* dX,

@@ -551,6 +551,20 @@ __global__ __launch_bounds__(512) void bgemm_kernel(GemmArgs p) {
       return;
     }
   }
+  if constexpr (MODE == MODE_FWD_SWIGLU) {
+    if (p.row_scale) {
+      // RMSNorm folded in: every token row of the product (LoRA term included)
+      // times its inverse RMS; the norm weight is in the expanded weight
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const float rs = p.row_scale[arow[i]];
+#pragma unroll
+        for (int f = 0; f < FN; ++f)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) acc[i][f][v] *= rs;
+      }
+    }
+  }
   uint16_t* buf = wave < 2 ? hb0 : wave < 4 ? hb1 : wave < 6 ? hb2 : hb3;
   f32x4 dad[2][4];
 #pragma unroll
@@ -628,7 +642,8 @@ __global__ __launch_bounds__(512) void bgemm_kernel(GemmArgs p) {
 __global__ __launch_bounds__(256) void dequant_rows_kernel(Nf4Dev w0, Nf4Dev w1, int pair,
                                                            const float* __restrict__ codebook0,
                                                            const float* __restrict__ codebook1, uint32_t cpr,
-                                                           uint32_t nchunks, uint16_t* __restrict__ out) {
+                                                           uint32_t nchunks, const uint16_t* __restrict__ colw,
+                                                           uint16_t* __restrict__ out) {
   __shared__ float cb[32];  // tables of w0, w1
   if (threadIdx.x < 32) cb[threadIdx.x] = threadIdx.x < 16 ? codebook0[threadIdx.x] : codebook1[threadIdx.x & 15];
   __syncthreads();
@@ -653,7 +668,16 @@ __global__ __launch_bounds__(256) void dequant_rows_kernel(Nf4Dev w0, Nf4Dev w1,
       const uint32_t c = *reinterpret_cast<const uint32_t*>(w.codes + src * (K / 2) + k0 / 2);
       const int64_t blk = (src * K + k0) / 64;
       const float a = w.dq ? absmax_at<true>(w, blk) : absmax_at<false>(w, blk);
-      o = deq8(c, a, up ? cb + 16 : cb);
+      const float* t = up ? cb + 16 : cb;
+      if (colw) {
+        // column k scaled by colw[k]: fp32(fp32(codebook * absmax) * w), then bf16
+        const u32x4 wv = *reinterpret_cast<const u32x4*>(colw + k0);
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+          o[d] = pack_bf16x2(t[(c >> (8 * d)) & 15u] * a * bf16_lo(wv[d]), t[(c >> (8 * d + 4)) & 15u] * a * bf16_hi(wv[d]));
+      } else {
+        o = deq8(c, a, t);
+      }
     }
     *reinterpret_cast<u32x4*>(out + (int64_t)R * K + k0) = o;
   }
@@ -770,13 +794,13 @@ hipError_t launch_had_finish(const float* part, int tiles, int64_t M, int r, flo
 }
 
 hipError_t launch_dequant_rows(const Nf4Dev& w0, const Nf4Dev* w1, const float* codebook0, const float* codebook1,
-                               int64_t rows_out, uint16_t* out, hipStream_t st) {
+                               int64_t rows_out, uint16_t* out, hipStream_t st, const uint16_t* colw) {
   const int64_t cpr = w0.K / 8, chunks = rows_out * cpr;
   if (chunks == 0) return hipSuccess;
   if (chunks >= ((int64_t)1 << 32) - 1024) return hipErrorInvalidValue;  // 32-bit chunk index
   dequant_rows_kernel<<<dim3((unsigned)((chunks + 1023) / 1024)), 256, 0, st>>>(
       w0, w1 ? *w1 : w0, w1 ? 1 : 0, codebook0, codebook1 ? codebook1 : codebook0, (uint32_t)cpr, (uint32_t)chunks,
-      out);
+      colw, out);
   return hipGetLastError();
 }
 

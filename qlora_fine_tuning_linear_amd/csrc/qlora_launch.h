@@ -70,6 +70,10 @@ struct GemmArgs {
   // to bf16) as per-token-tile fp32 partials dad_part[tiles_m][Nout][r]
   // (null: not computed)
   float* dad_part;
+  // bgemm_kernel, SwiGLU forward only: every token row m of the product
+  // (LoRA term included) is multiplied by row_scale[m] before the epilogue
+  // (null: not scaled)
+  const float* row_scale;
 };
 
 // Skinny-M forward GEMM (qlora_skinny.hip): out[m, n] = sum_k X[m, k]
@@ -150,6 +154,11 @@ hipError_t launch_grouped_db(const GroupDesc& d, int Nt, int Rt, const uint16_t*
 // RMSNorm: Y = X rstd w (rstd saved per row) and its backward; D % 8 == 0,
 // D <= 8192.  The backward with dw needs part fp32 [rmsnorm_bwd_groups(M)][D].
 int rmsnorm_bwd_groups(int64_t M);
+// rows of A [rows, K] bf16 times w [K] bf16 -> out, bf16 (fp32 product rounded)
+hipError_t launch_scale_cols(const uint16_t* A, int64_t rows, int64_t K, const uint16_t* w, uint16_t* out,
+                             hipStream_t st);
+// out[m, j] = in[m, j] * s[m], fp32 [M, r]
+hipError_t launch_scale_rows(const float* in, int64_t M, int r, const float* s, float* out, hipStream_t st);
 hipError_t launch_rmsnorm_fwd(const uint16_t* X, const uint16_t* w, int64_t M, int64_t D, float eps, uint16_t* Y,
                               float* rstd, hipStream_t st);
 hipError_t launch_rmsnorm_bwd(const uint16_t* dY, const uint16_t* X, const uint16_t* w, const float* rstd,
@@ -178,7 +187,8 @@ hipError_t launch_ce_loss(const float* token_loss, int64_t T, const int32_t* n_v
 //          columns (rows past N are zero), else src(R) = R.
 //   trans: out[k, col0 + n] = deq(W)[n, k] (row stride ldo).
 hipError_t launch_dequant_rows(const Nf4Dev& w0, const Nf4Dev* w1, const float* codebook0, const float* codebook1,
-                               int64_t rows_out, uint16_t* out, hipStream_t st);
+                               int64_t rows_out, uint16_t* out, hipStream_t st,
+                               const uint16_t* colw = nullptr);
 hipError_t launch_dequant_trans(const Nf4Dev& w, const float* codebook, uint16_t* out, int64_t ldo, int64_t col0,
                                 hipStream_t st);
 hipError_t launch_splitk_finish(const float* part, int splits, int64_t M, int64_t Nout, uint16_t* out,

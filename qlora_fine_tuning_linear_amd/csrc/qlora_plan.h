@@ -308,6 +308,24 @@ inline MlpWs mlp_ws(int64_t M, int64_t D, int64_t I, int rg, int ru, int rd) {
   return w;
 }
 
+// MLP forward with the RMSNorm folded in (qlora_mlp_fwd_rmsnorm): the MLP
+// forward's workspace, then A_g w and A_u w (bf16), the unscaled X (A w)^T
+// (fp32 [M, r_g + r_u]) and, below the bf16-GEMM threshold (where the norm
+// runs as its own pass), the normalised input (bf16 [M, D]).
+struct MlpRmsWs {
+  size_t base, at_g, at_u, xa, xn, total;
+};
+inline MlpRmsWs mlp_rms_ws(int64_t M, int64_t D, int64_t I, int rg, int ru, int rd) {
+  MlpRmsWs w{};
+  w.base = mlp_ws(M, D, I, rg, ru, rd).fwd_total;
+  w.at_g = align256((size_t)rg * D * 2);
+  w.at_u = align256((size_t)ru * D * 2);
+  w.xa = align256((size_t)M * (rg + ru) * 4);
+  w.xn = use_bgemm(M) ? 0 : align256((size_t)M * D * 2);
+  w.total = w.base + w.at_g + w.at_u + w.xa + w.xn;
+  return w;
+}
+
 // Output head + cross-entropy: C tokens per chunk; the dX product of a chunk
 // ([C, V] x [V, D]) splits its vocabulary reduction so that tiles x splits
 // covers the chip about twice, with at least 32 vocabulary tiles per split.

@@ -61,6 +61,7 @@ __global__ __launch_bounds__(256) void rmsnorm_fwd_kernel(const uint16_t* __rest
   ss = wave_sum(ss);
   const float r = 1.0f / sqrtf(ss / (float)D + eps);
   if (lane == 0) rstd[m] = r;
+  if (!Y) return;  // rstd only (the norm folded into the next GEMM)
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     const int ch = lane + 64 * c;
@@ -252,10 +253,42 @@ int rmsnorm_bwd_groups(int64_t M) {
   return (int)(g < RN_BWD_WG ? (g > 0 ? g : 1) : RN_BWD_WG);
 }
 
+// out[j, k] = bf16(A[j, k] w[k]): a rank-r matrix with the norm weight folded in
+__global__ __launch_bounds__(256) void scale_cols_kernel(const uint16_t* __restrict__ A, int64_t n, int64_t K,
+                                                         const uint16_t* __restrict__ w, uint16_t* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const int64_t k = i % K;
+  out[i] = (uint16_t)(pack_bf16x2(bf16_lo(A[i]) * bf16_lo(w[k]), 0.0f) & 0xFFFFu);
+}
+
+// out[m, j] = in[m, j] s[m]
+__global__ __launch_bounds__(256) void scale_rows_kernel(const float* __restrict__ in, int64_t n, int r,
+                                                         const float* __restrict__ s, float* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  out[i] = in[i] * s[i / r];
+}
+
 static int rmsnorm_nc(int64_t D) {
   for (int nc = 1; nc <= 16; nc *= 2)
     if (512 * nc >= D) return nc;
   return 0;
+}
+
+hipError_t launch_scale_cols(const uint16_t* A, int64_t rows, int64_t K, const uint16_t* w, uint16_t* out,
+                             hipStream_t st) {
+  const int64_t n = rows * K;
+  if (n == 0) return hipSuccess;
+  scale_cols_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(A, n, K, w, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_scale_rows(const float* in, int64_t M, int r, const float* s, float* out, hipStream_t st) {
+  const int64_t n = M * r;
+  if (n == 0) return hipSuccess;
+  scale_rows_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(in, n, r, s, out);
+  return hipGetLastError();
 }
 
 hipError_t launch_rmsnorm_fwd(const uint16_t* X, const uint16_t* w, int64_t M, int64_t D, float eps, uint16_t* Y,

@@ -220,6 +220,25 @@ int qv_mlp_fwd(const qlora_mlp* P, const void* X, int64_t M, const void* Y, cons
   return check_ws(ws, ws_bytes, w.fwd_total);
 }
 
+int qv_mlp_fwd_rmsnorm(const qlora_mlp* P, const void* X, const void* norm_w, float eps, int64_t M, const void* Y,
+                       const qlora_mlp_saved* S, const float* rstd, const void* Xn, const void* ws, size_t ws_bytes) {
+  int st = check_mlp(P);
+  if (st) return st;
+  if (M < 0 || !S) return QLORA_ERR_INVALID_ARG;
+  if (M > kMaxTokens) return QLORA_ERR_UNSUPPORTED_SHAPE;
+  if ((st = check_rms(M, P->gate.W0.K))) return st;
+  if (!isfinite(eps) || eps < 0.0f) return QLORA_ERR_INVALID_ARG;
+  if (M == 0) return QLORA_OK;
+  if ((st = check_ptr(X)) || (st = check_ptr(norm_w)) || (st = check_ptr(Y)) || (st = check_ptr(rstd)) ||
+      (st = check_ptr(S->G)) || (st = check_ptr(S->U)) || (st = check_ptr(S->XA_g)) || (st = check_ptr(S->XA_u)) ||
+      (st = check_ptr(S->HA_d)))
+    return st;
+  if (Xn && (st = check_ptr(Xn))) return st;
+  const qplan::MlpRmsWs w =
+      qplan::mlp_rms_ws(M, P->gate.W0.K, P->gate.W0.N, P->gate.r, P->up.r, P->down.r);
+  return check_ws(ws, ws_bytes, w.total);
+}
+
 int qv_mlp_bwd(const qlora_mlp* P, const void* dY, const void* X, const qlora_mlp_saved* S, int64_t M, const void* dX,
                const qlora_mlp_grads* G, const void* ws, size_t ws_bytes) {
   int st = check_mlp(P);
@@ -262,6 +281,11 @@ size_t qlora_linear_workspace_bytes(const qlora_linear* L, int64_t M) {
 size_t qlora_mlp_workspace_bytes(const qlora_mlp* P, int64_t M) {
   if (!P || M <= 0 || M > kMaxTokens || check_mlp(P)) return 0;
   return qplan::mlp_ws(M, P->gate.W0.K, P->gate.W0.N, P->gate.r, P->up.r, P->down.r).total;
+}
+
+size_t qlora_mlp_rmsnorm_workspace_bytes(const qlora_mlp* P, int64_t M) {
+  if (!P || M <= 0 || M > kMaxTokens || check_mlp(P) || check_rms(M, P->gate.W0.K)) return 0;
+  return qplan::mlp_rms_ws(M, P->gate.W0.K, P->gate.W0.N, P->gate.r, P->up.r, P->down.r).total;
 }
 
 }  // extern "C"

@@ -27,6 +27,8 @@ int qv_linear_bwd(const qlora_linear* L, const void* dY, const void* X, const fl
                   const void* dA, const void* dB, const void* ws, size_t ws_bytes);
 int qv_mlp_fwd(const qlora_mlp* P, const void* X, int64_t M, const void* Y, const qlora_mlp_saved* S, const void* ws,
                size_t ws_bytes);
+int qv_mlp_fwd_rmsnorm(const qlora_mlp* P, const void* X, const void* norm_w, float eps, int64_t M, const void* Y,
+                       const qlora_mlp_saved* S, const float* rstd, const void* Xn, const void* ws, size_t ws_bytes);
 int qv_mlp_bwd(const qlora_mlp* P, const void* dY, const void* X, const qlora_mlp_saved* S, int64_t M, const void* dX,
                const qlora_mlp_grads* G, const void* ws, size_t ws_bytes);
 size_t qv_linear_ce_ws(int64_t T, int64_t D, int64_t V, int64_t chunk, int32_t want_dx);

@@ -179,6 +179,35 @@ def test_mlp_shape_rules(lib):
     assert lib.qlora_mlp_fwd(ctypes.byref(P), FAKE, 16, FAKE, ctypes.byref(S), FAKE, need, None) in (HIP, DEVICE)
 
 
+def test_mlp_rmsnorm_rules(lib):
+    """qlora_mlp_fwd_rmsnorm: the MLP forward's rules plus those of rmsnorm_fwd
+    (eps finite and >= 0, norm weight and rstd given); Xn is optional."""
+    P = q.CMlp(linear(N=256, K=128), linear(N=256, K=128), linear(N=128, K=256))
+    S = q.CMlpSaved(FAKE, FAKE, FAKE, FAKE, FAKE)
+    need = lib.qlora_mlp_rmsnorm_workspace_bytes(ctypes.byref(P), 16)
+    assert need > 16 * 256 * 2  # at least the transient H
+    assert lib.qlora_mlp_rmsnorm_workspace_bytes(ctypes.byref(P), 0) == 0
+
+    def call(M=16, X=FAKE, w=FAKE, eps=1e-5, rstd=FAKE, Xn=None, wsb=None, saved=True):
+        return lib.qlora_mlp_fwd_rmsnorm(ctypes.byref(P), X, w, eps, M, FAKE, ctypes.byref(S) if saved else None,
+                                         rstd, Xn, FAKE, need if wsb is None else wsb, None)
+
+    assert call(eps=-1.0) == INVALID
+    assert call(eps=float("nan")) == INVALID
+    assert call(w=None) == INVALID
+    assert call(rstd=None) == INVALID
+    assert call(X=None) == INVALID
+    assert call(saved=False) == INVALID
+    assert call(Xn=FAKE + 2) == MISALIGNED
+    assert call(wsb=need - 1) == WS_SMALL
+    assert call(M=0, X=None, rstd=None) == OK
+    # well-formed, with and without Xn: fails at the device check on a host without a GPU
+    assert call() in (HIP, DEVICE)
+    assert call(Xn=FAKE) in (HIP, DEVICE)
+    bad = q.CMlp(linear(N=256, K=8200), linear(N=256, K=8200), linear(N=8200, K=256))
+    assert lib.qlora_mlp_rmsnorm_workspace_bytes(ctypes.byref(bad), 16) == 0
+
+
 def test_mlp_intermediate_bound(lib):
     """The backward's [W_g^T | W_u^T] bf16 copy has row stride 2I; a 256-row
     tile of it must stay below 2 GiB, so I is capped at 2097088."""

@@ -147,3 +147,46 @@ def test_mlp_parity_full_size_dense_llama3_8b(codebook):
     for k in ("dA_g", "dB_g", "dA_u", "dB_u", "dA_d", "dB_d"):
         assert_close(k, grads[k], ref[k])
 
+
+
+# RMSNorm folded into the block's forward: from 512 tokens the norm weight is
+# in the expanded gate/up weights and the inverse RMS scales the gate/up
+# product; below, the norm runs as its own pass.  Ranks cover the fused HA_d
+# (r_d <= 32) and the separate one (r_d = 64, r_g + r_u = 128).
+RMS_CASES = [
+    synth.MlpCfg("rms_m600_d256_i384_r16", M=600, D=256, I=384, r=16, alpha=16.0, dq_group=0),
+    synth.MlpCfg("rms_m777_d192_i320_r20_dq", M=777, D=192, I=320, r=20, alpha=16.0, dq_group=256),
+    synth.MlpCfg("rms_m1100_d320_i448_r64", M=1100, D=320, I=448, r=64, alpha=16.0, dq_group=0),
+    synth.MlpCfg("rms_m300_d256_i512_r8", M=300, D=256, I=512, r=8, alpha=16.0, dq_group=0),
+]
+
+
+@pytest.mark.parametrize("want_xn", [False, True], ids=["no_xn", "xn"])
+@pytest.mark.parametrize("cfg", RMS_CASES, ids=[c.name for c in RMS_CASES])
+def test_mlp_rmsnorm_fused_forward(cfg, want_xn, codebook):
+    from oracle import rmsnorm as orn
+    print("case", cfg.name, want_xn, flush=True)
+    P, W, inp = build(cfg, 5000 + cfg.M, codebook)
+    M, D, I = cfg.M, cfg.D, cfg.I
+    wn = synth.normal_bf16(5000 + cfg.M, 42, D, 1.0, 0.1)
+    eps = 1e-5
+    X, wd = bf16_dev(inp["X"]), bf16_dev(wn)
+    g = Guarded()
+    bf, f32 = torch.bfloat16, torch.float32
+    S0 = q.MlpSaved(g.empty((M, I), bf), g.empty((M, I), bf), g.empty((M, P.gate.r), f32),
+                    g.empty((M, P.up.r), f32), g.empty((M, P.down.r), f32))
+    Y, S, rstd, Xn = q.qlora_mlp_fwd_rmsnorm(P, X, wd, eps, Y=g.empty((M, D), bf), saved=S0,
+                                             rstd=g.empty((M,), f32), want_xn=want_xn,
+                                             Xn=g.empty((M, D), bf) if want_xn else None)
+    g.check()
+    Xn_o, rstd_o = orn.rmsnorm_forward(inp["X"], wn, eps)
+    f = oq.mlp_forward(Xn_o, *oracle_args(W, inp), cfg.alpha)
+    assert_close("rstd", rstd, rstd_o, tol=1e-5)
+    if want_xn:
+        assert_close("Xn", Xn, Xn_o)
+    assert_close("Y", Y, f["Y"])
+    assert_close("G", S.G, f["G"])
+    assert_close("U", S.U, f["U"])
+    assert_close("XA_g", S.XA_g, f["XA_g"])
+    assert_close("XA_u", S.XA_u, f["XA_u"])
+    assert_close("HA_d", S.HA_d, f["HA_d"])
