@@ -284,8 +284,8 @@ int rmsnorm_bwd(const void* dY, const void* X, const void* w, const float* rstd,
  * Workspace bytes qlora_linear_ce needs for T tokens, hidden size D, V classes
  * and the given chunk (0 when the shape is not supported): one chunk of
  * logits (min(chunk, T) * V fp32), T per-token fp32 losses and, with
- * want_dx != 0, the head transposed (V * D bf16) plus the fp32 partials of
- * the dX product.
+ * want_dx != 0, the fp32 partials of the dX product (which reads the head as
+ * stored: no copy of it).
  */
 size_t qlora_linear_ce_workspace_bytes(int64_t T, int64_t D, int64_t V, int64_t chunk, int32_t want_dx);
 

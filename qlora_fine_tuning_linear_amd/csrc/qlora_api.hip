@@ -333,11 +333,8 @@ int qlora_linear_ce(const void* X, int64_t T, int64_t D, const void* W, int64_t 
   int32_t* nvalid = reinterpret_cast<int32_t*>(b);
   float* tl = token_loss ? token_loss : reinterpret_cast<float*>(b + w.nvalid);
   float* z = reinterpret_cast<float*>(b + w.nvalid + w.tloss);
-  uint16_t* wt = reinterpret_cast<uint16_t*>(b + w.nvalid + w.tloss + w.logits);
-  float* part = reinterpret_cast<float*>(b + w.nvalid + w.tloss + w.logits + w.wt);
+  float* part = reinterpret_cast<float*>(b + w.nvalid + w.tloss + w.logits);
   QHIP(launch_ce_count(targets, T, V, ignore_index, nvalid, st));
-  // the head as [D, V] rows, so that the dX product reduces over contiguous rows
-  if (want_dx) QHIP(launch_transpose_bf16(u16(W), V, D, wt, st));
   for (int64_t c0 = 0; c0 < T; c0 += w.C) {
     const int64_t C = (T - c0) < w.C ? (T - c0) : w.C;
     // logits of the chunk: z = X_c W^T, fp32 [C, V]
@@ -356,16 +353,18 @@ int qlora_linear_ce(const void* X, int64_t T, int64_t D, const void* W, int64_t 
     // (softmax - onehot) / n (row stride 2V bf16 elements)
     QHIP(launch_ce_rows(z, C, V, targets + c0, ignore_index, nvalid, want_dx ? 1 : 0, tl + c0, st));
     if (!want_dx) continue;
-    // dX_c = g W, the vocabulary reduction split into fp32 partials
+    // dX_c = g W, the vocabulary reduction split into fp32 partials; the head
+    // [V, D] is read K-major (rows of the reduction) as it is stored
     GemmArgs g = gemm_args();
     g.act0 = reinterpret_cast<const uint16_t*>(z);
     g.lda = 2 * V;
     g.M = C;
     g.Nout = D;
     g.Kred0 = V;
-    g.wb = wt;
-    g.ldw = V;
+    g.wb = u16(W);
+    g.ldw = D;
     g.wrows = D;
+    g.w_kmajor = 1;
     g.out0 = u16m(dX) + c0 * D;
     if (w.splits > 1) {
       g.partial = part;

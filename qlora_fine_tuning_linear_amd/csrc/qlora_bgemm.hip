@@ -320,7 +320,13 @@ __device__ __forceinline__ void bg_had_wave(const GemmArgs& p, f32x16 (&acc)[BG_
   }
 }
 
-template <int MODE, bool WLEAD>
+// KMAJ: the weight operand is stored K-major, wb[k ldw + n] (an output head
+// [V, D] read as the weight of the dX product, which reduces over V).  Its
+// half-tile then sits in LDS as [64 k][256 n] (whole 512-byte row segments by
+// direct loads; 16-byte chunk c of row k at c ^ 4 ((k / 8) % 2), so that the
+// two lane halves of a read, 8 rows apart, hit different banks), and each
+// A operand of the MFMA is gathered as 8 two-byte reads down a column.
+template <int MODE, bool WLEAD, bool KMAJ = false>
 __global__ __launch_bounds__(512) void bgemm_kernel(GemmArgs p) {
   constexpr int WN = BG_WN, FM = BG_FM, FN = BG_FN;
   constexpr int LPH = BG_LPH;
@@ -365,6 +371,13 @@ __global__ __launch_bounds__(512) void bgemm_kernel(GemmArgs p) {
     if (rb >= p.wrows) rb = p.wrows - 1;
     aoff[i] = (uint32_t)((ra - m0) * lda) + (uint32_t)c * 8;
     boff[i] = (uint32_t)((rb - wr0) * p.ldw) + (uint32_t)c * 8;
+    if constexpr (KMAJ) {
+      // load i of this wave: reduction rows 2 (4 wave + i) + lane / 32 of the
+      // tile, 16-byte chunk (lane % 32) ^ 4 ((row / 8) % 2) of its 256 columns
+      const int kr = 2 * (LPH * wave + i) + (lane >> 5);
+      const int kc = (lane & 31) ^ (((kr >> 3) & 1) * 4);
+      boff[i] = (uint32_t)(kr * p.ldw) + (uint32_t)kc * 8;
+    }
   }
   // Buffer resources over the tile's rows: the dual-reduction GEMM reads
   // act0 for the first KT0 tiles, then act1 (same row stride).  A direct load
@@ -377,7 +390,7 @@ __global__ __launch_bounds__(512) void bgemm_kernel(GemmArgs p) {
   const int64_t abytes = (p.M - m0) * lda * 2;
   const __amdgpu_buffer_rsrc_t ra0 = rsrc(p.act0 + m0 * lda, abytes);
   const __amdgpu_buffer_rsrc_t ra1 = rsrc((p.act1 ? p.act1 : p.act0) + m0 * lda, abytes);
-  const __amdgpu_buffer_rsrc_t rb = rsrc(p.wb + wr0 * p.ldw, (p.wrows - wr0) * p.ldw * 2);
+  const __amdgpu_buffer_rsrc_t rb = rsrc(p.wb + (KMAJ ? wr0 : wr0 * p.ldw), (p.wrows - wr0) * p.ldw * 2);
 
   // 8 direct loads of one operand half of tile kt (clamped to the last tile:
   // the tail re-loads it into a free buffer, which keeps vmcnt uniform)
@@ -397,9 +410,20 @@ __global__ __launch_bounds__(512) void bgemm_kernel(GemmArgs p) {
   };
   auto load_b = [&](uint16_t* buf, int kt) {
     kt = (kt < KT ? kt : KT - 1) + kb;
+    if constexpr (KMAJ) {
+      // tile kt is rows 64 kt .. 64 kt + 63 of the weight: a resource based
+      // at its first row (any weight size; offsets stay within the tile)
+      const int64_t k0 = (int64_t)kt * 64;
+      const __amdgpu_buffer_rsrc_t rk = rsrc(p.wb + k0 * p.ldw + wr0, ((p.Kred0 - k0) * p.ldw - wr0) * 2);
 #pragma unroll
-    for (int i = 0; i < LPH; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, LDS_PTR(buf + (LPH * wave + i) * 512), 16, boff[i], kt * 128, 0, 0);
+      for (int i = 0; i < LPH; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, LDS_PTR(buf + (LPH * wave + i) * 512), 16, boff[i], 0, 0, 0);
+    } else {
+#pragma unroll
+      for (int i = 0; i < LPH; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, LDS_PTR(buf + (LPH * wave + i) * 512), 16, boff[i], kt * 128, 0,
+                                                 0);
+    }
   };
 
   f32x16 acc[FM][FN];
@@ -424,6 +448,11 @@ __global__ __launch_bounds__(512) void bgemm_kernel(GemmArgs p) {
     const int row = frag_row<MODE, WN, FN>(wn, f) + l32;
 #pragma unroll
     for (int s = 0; s < 4; ++s) bro[f][s] = row * 64 + (((2 * s + g) ^ swz(row)) * 8);
+    if constexpr (KMAJ) {
+      // column `row` of the [64][256] half: element (k, row) for k = 16 s +
+      // 8 g + e lies at k 256 + bro[f][0] (chunk swizzle 4 g: (k / 8) % 2 = g)
+      bro[f][0] = (8 * g) * 256 + ((((row >> 3) ^ (4 * g)) << 3) | (row & 7));
+    }
   }
 
   // operands of 16-wide step s (0..3) of a tile held in halves (ha, hb)
@@ -445,8 +474,19 @@ __global__ __launch_bounds__(512) void bgemm_kernel(GemmArgs p) {
   auto rd = [&](const uint16_t* h1, const uint16_t* h2, int s, u32x4 (&xa)[FM], u32x4 (&wa)[FN]) {
     const uint16_t* ha = WLEAD ? h2 : h1;
     const uint16_t* hb = WLEAD ? h1 : h2;
+    if constexpr (KMAJ) {
 #pragma unroll
-    for (int f = 0; f < FN; ++f) wa[f] = *reinterpret_cast<const u32x4*>(hb + bro[f][s]);
+      for (int f = 0; f < FN; ++f) {
+        const uint16_t* col = hb + bro[f][0] + 16 * s * 256;
+        uint32_t h[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) h[e] = col[e * 256];
+        wa[f] = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+      }
+    } else {
+#pragma unroll
+      for (int f = 0; f < FN; ++f) wa[f] = *reinterpret_cast<const u32x4*>(hb + bro[f][s]);
+    }
 #pragma unroll
     for (int i = 0; i < FM; ++i) xa[i] = *reinterpret_cast<const u32x4*>(ha + aro[i][s]);
   };
@@ -750,7 +790,9 @@ static hipError_t run_bgemm(GemmArgs a, hipStream_t st) {
     const int64_t kt = (a.Kred0 + a.Kred1) / 64;
     splits = (unsigned)((kt + a.ktiles_per_split - 1) / a.ktiles_per_split);
   }
-  if (a.wrows > a.M)
+  if (MODE == MODE_FWD && a.w_kmajor)
+    bgemm_kernel<MODE, false, true><<<dim3((unsigned)n, splits), 512, 0, st>>>(a);
+  else if (a.wrows > a.M)
     bgemm_kernel<MODE, true><<<dim3((unsigned)n, splits), 512, 0, st>>>(a);
   else
     bgemm_kernel<MODE, false><<<dim3((unsigned)n, splits), 512, 0, st>>>(a);

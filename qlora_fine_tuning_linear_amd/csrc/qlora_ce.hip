@@ -4,10 +4,9 @@
 // logit matrix is ever held.  Per chunk the entry point runs the bf16 GEMM
 // for the chunk's fp32 logits, ce_rows_kernel for the loss terms and the
 // bf16 logit gradient (in place), and the bf16 GEMM again (reduction over the vocabulary,
-// split into fp32 partials) for dX.  The helpers here:
+// split into fp32 partials, reading the head [V, D] as stored: a K-major
+// weight operand) for dX.  The helpers here:
 //   * ce_count_kernel      - number of tokens that carry a target;
-//   * transpose_bf16_kernel - the head [V, D] -> [D, V], so that the dX product
-//     reduces over contiguous rows like every other GEMM of the library;
 //   * ce_rows_kernel       - one workgroup per token row of logits: log-sum-exp
 //     (one pass, running maximum), the token's loss term and, in a second pass,
 //     (softmax - onehot) / n rounded to bf16 in place of the logits;
@@ -38,33 +37,6 @@ __global__ __launch_bounds__(1024) void ce_count_kernel(const int32_t* __restric
     __syncthreads();
   }
   if (threadIdx.x == 0) *n_valid = red[0];
-}
-
-// out[d, v] = in[v, d] for a [V, D] bf16 matrix, 64 x 64 tiles through LDS
-// (rows read and written as 16-byte chunks).  V, D multiples of 64.
-constexpr int TR_LD = 72;  // LDS row stride (elements)
-
-__global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __restrict__ in, int64_t V, int64_t D,
-                                                             uint16_t* __restrict__ out) {
-  __shared__ __attribute__((aligned(16))) uint16_t tile[64 * TR_LD];
-  const int64_t v0 = (int64_t)blockIdx.x * 64, d0 = (int64_t)blockIdx.y * 64;
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int c = threadIdx.x + 256 * j, row = c >> 3, ch = c & 7;
-    *reinterpret_cast<u32x4*>(tile + row * TR_LD + ch * 8) =
-        *reinterpret_cast<const u32x4*>(in + (v0 + row) * D + d0 + ch * 8);
-  }
-  __syncthreads();
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int c = threadIdx.x + 256 * j, drow = c >> 3, vch = c & 7;
-    uint32_t w[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      w[e] = (uint32_t)tile[(vch * 8 + 2 * e) * TR_LD + drow] |
-             ((uint32_t)tile[(vch * 8 + 2 * e + 1) * TR_LD + drow] << 16);
-    *reinterpret_cast<u32x4*>(out + (d0 + drow) * V + v0 + vch * 8) = u32x4{w[0], w[1], w[2], w[3]};
-  }
 }
 
 // Running (max, sum of exp(x - max)) pairs, combined in a fixed order.
@@ -190,12 +162,6 @@ using namespace qk;
 hipError_t launch_ce_count(const int32_t* targets, int64_t T, int64_t V, int32_t ignore, int32_t* n_valid,
                            hipStream_t st) {
   ce_count_kernel<<<1, 1024, 0, st>>>(targets, T, V, ignore, n_valid);
-  return hipGetLastError();
-}
-
-hipError_t launch_transpose_bf16(const uint16_t* in, int64_t V, int64_t D, uint16_t* out, hipStream_t st) {
-  if (V == 0 || D == 0) return hipSuccess;
-  transpose_bf16_kernel<<<dim3((unsigned)(V / 64), (unsigned)(D / 64)), 256, 0, st>>>(in, V, D, out);
   return hipGetLastError();
 }
 

@@ -74,6 +74,9 @@ struct GemmArgs {
   // (LoRA term included) is multiplied by row_scale[m] before the epilogue
   // (null: not scaled)
   const float* row_scale;
+  // bgemm_kernel, plain forward only: the weight operand stored K-major,
+  // wb[k ldw + n] for k < Kred0, n < wrows (ldw >= wrows, a multiple of 8)
+  int32_t w_kmajor;
 };
 
 // Skinny-M forward GEMM (qlora_skinny.hip): out[m, n] = sum_k X[m, k]
@@ -175,7 +178,6 @@ hipError_t launch_grad_finish(const float* part, int S, int64_t P, int r, float 
 // Output head + cross-entropy helpers (qlora_ce.hip).
 hipError_t launch_ce_count(const int32_t* targets, int64_t T, int64_t V, int32_t ignore, int32_t* n_valid,
                            hipStream_t st);
-hipError_t launch_transpose_bf16(const uint16_t* in, int64_t V, int64_t D, uint16_t* out, hipStream_t st);
 // z: fp32 logits [rows][V]; with want_grad each row's first 2V bytes are
 // overwritten by the bf16 logit gradient (row stride 2V bf16 elements).
 hipError_t launch_ce_rows(float* z, int64_t rows, int64_t V, const int32_t* targets, int32_t ignore,

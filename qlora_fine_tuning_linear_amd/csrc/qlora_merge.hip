@@ -100,7 +100,6 @@ __global__ __launch_bounds__(256) void merge_kernel(Nf4Dev w, const float* __res
 #pragma unroll
   for (int t = 0; t < MG_T; ++t) {
     if (32 * t >= ncols) break;
-    const int64_t k0 = kb + 32 * t;
     // A operand of step js: lane (l32, g) holds A[16 js + 8 g + i][k0 + l32]
     f32x16 acc;
 #pragma unroll

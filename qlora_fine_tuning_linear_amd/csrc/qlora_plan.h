@@ -351,7 +351,7 @@ inline CeWs ce_ws(int64_t T, int64_t D, int64_t V, int64_t chunk, bool want_dx) 
   w.nvalid = 256;
   w.tloss = align256((size_t)T * 4);
   w.logits = align256((size_t)w.C * V * 4);  // fp32 logits; the bf16 gradient overwrites them
-  w.wt = want_dx ? align256((size_t)V * D * 2) : 0;
+  w.wt = 0;  // the dX product reads the head as stored (K-major weight operand)
   w.part = (want_dx && w.splits > 1) ? align256((size_t)w.splits * w.C * D * 4) : 0;
   w.total = w.nvalid + w.tloss + w.logits + w.wt + w.part;
   return w;
