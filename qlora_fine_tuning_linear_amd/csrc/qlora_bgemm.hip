@@ -790,9 +790,13 @@ static hipError_t run_bgemm(GemmArgs a, hipStream_t st) {
     const int64_t kt = (a.Kred0 + a.Kred1) / 64;
     splits = (unsigned)((kt + a.ktiles_per_split - 1) / a.ktiles_per_split);
   }
-  if (MODE == MODE_FWD && a.w_kmajor)
-    bgemm_kernel<MODE, false, true><<<dim3((unsigned)n, splits), 512, 0, st>>>(a);
-  else if (a.wrows > a.M)
+  if constexpr (MODE == MODE_FWD) {
+    if (a.w_kmajor) {
+      bgemm_kernel<MODE, false, true><<<dim3((unsigned)n, splits), 512, 0, st>>>(a);
+      return hipGetLastError();
+    }
+  }
+  if (a.wrows > a.M)
     bgemm_kernel<MODE, true><<<dim3((unsigned)n, splits), 512, 0, st>>>(a);
   else
     bgemm_kernel<MODE, false><<<dim3((unsigned)n, splits), 512, 0, st>>>(a);
