@@ -63,12 +63,24 @@ def dev_bf16(u16):
     return torch.from_numpy(np.ascontiguousarray(u16).view(np.int16)).view(torch.bfloat16).cuda()
 
 
-def kernel_source_sha():
+# the sources a kernel kind's code and launch arguments come from (besides
+# every header and the C ABI's launch code)
+KERNEL_SOURCES = {"bgemm": ("qlora_bgemm.hip",), "qgemm": ("qlora_kernels.hip",),
+                  "skinny": ("qlora_skinny.hip", "qlora_skinny2.hip")}
+
+
+def kernel_source_sha(key=None):
+    """Hash of the kernel sources: all of them, or those that build the kernel
+    kind of a traffic key ('bgemm_fwd_swiglu', 'skinny_fwd', ...)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "qlora_fine_tuning_linear_amd", "csrc")
+    own = KERNEL_SOURCES.get(key.split("_")[0]) if key else None
     for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".h", ".cpp")):
-            h.update(open(os.path.join(csrc, f), "rb").read())
+        if not f.endswith((".hip", ".h", ".cpp")):
+            continue
+        if own is not None and not (f.endswith(".h") or f == "qlora_api.hip" or f in own):
+            continue
+        h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
 
 
@@ -82,7 +94,7 @@ def stored_traffic(key):
         rec = json.loads("".join(l for l in open(path) if not l.startswith("#")))
     except ValueError:
         return None
-    if rec.get("source_sha") != kernel_source_sha():
+    if rec.get("source_sha") != kernel_source_sha(key):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -135,7 +147,6 @@ def summarize_traffic(fetch_csv, write_csv, copy_mib, command):
         return copy_kib / statistics.median(c)
 
     cf, cw = calib(f), calib(w)
-    sha = kernel_source_sha()
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
     written = []
     for name in sorted(set(f) & set(w)):
@@ -145,7 +156,7 @@ def summarize_traffic(fetch_csv, write_csv, copy_mib, command):
         fk, wk = statistics.median(f[name]), statistics.median(w[name])
         rec = {"kernel": name, "launches": len(f[name]), "fetch_kib_per_launch": fk, "write_kib_per_launch": wk,
                "copy_probe_mib": copy_mib, "calib_fetch": cf, "calib_write": cw,
-               "hbm_bytes_per_launch": int(round((fk * cf + wk * cw) * 1024)), "source_sha": sha}
+               "hbm_bytes_per_launch": int(round((fk * cf + wk * cw) * 1024)), "source_sha": kernel_source_sha(key)}
         path = os.path.join(ROOT, "profiles", "traffic_%s.txt" % key)
         with open(path, "w") as fh:
             fh.write("# HBM traffic per launch of %s (median over launches), from two rocprofv3 --pmc runs\n" % name)
