@@ -9,6 +9,8 @@
 // written; the rank-r product B A comes from the matrix cores.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "qlora_device.h"
 #include "qlora_gemm_common.h"
 #include "qlora_launch.h"
@@ -16,102 +18,121 @@
 namespace qk {
 
 // ------------------------------------------------------------------------
-// Workgroup: 128 weight rows x MG_COLS columns, 4 waves of 32 rows.  Per 32 x 32
-// tile the matrix cores give C[k][n] = sum_j A[j][k] B[n][j] over ceil(r/16)
-// v_mfma_f32_32x32x16_bf16 steps (j past r is zero on both operands).
-// Accumulator v of lane l is then column k0 + 8(v/4) + 4(l/32) + v%4 of row
-// n0 + l%32, i.e. of the lane's own row, whose code bytes and absmax values
-// for the MG_COLS columns the lane loads up front.  A's columns are staged
-// once per workgroup in LDS, transposed (A^T rows of 16-byte rank chunks),
-// so that each MFMA A operand is one 16-byte LDS read.  The 16-bit results go to a
-// per-wave LDS tile (rows padded by 16 bytes) and leave as whole row segments
-// (2 * MG_COLS bytes), several rows per store instruction.
+// Workgroup: one block of MG_COLS columns, walking `nb` blocks of 128 weight
+// rows (4 waves of 32 rows).  Per 32 x 32 tile the matrix cores give
+// C[k][n] = sum_j A[j][k] B[n][j] over ceil(r/16) v_mfma_f32_32x32x16_bf16
+// steps (j past r is zero on both operands).  Accumulator v of lane l is then
+// column k0 + 8(v/4) + 4(l/32) + v%4 of row n0 + l%32, i.e. of the lane's own
+// row, whose code bytes, absmax values and B row the lane loads one row block
+// ahead.  A's columns are staged once per workgroup in LDS, transposed (A^T
+// rows of 16-byte rank chunks), so that each MFMA A operand is one 16-byte LDS
+// read.  The 16-bit results go to a per-wave LDS tile (rows padded by 16
+// bytes) and leave as whole row segments (2 * MG_COLS bytes), four rows per
+// non-temporal store instruction.  Every global load and store of the
+// row-block loop is a buffer operation without a branch: rows past N and
+// columns past K fall outside the buffer ranges, so loads there read zeros and
+// stores there are dropped.  The number of memory operations in flight is
+// then the same on every path, and the wait for one block's operands leaves
+// the next block's loads and the previous block's stores in flight.
 // ------------------------------------------------------------------------
-constexpr int MG_COLS = 256;          // columns per workgroup
+constexpr int MG_COLS = 128;          // columns per workgroup
 constexpr int MG_LD = MG_COLS + 8;    // LDS row stride of the [32][MG_COLS] output tile, elements
 constexpr int MG_T = MG_COLS / 32;    // 32-column MFMA steps
 constexpr int MG_CH = MG_COLS / 8;    // 16-byte chunks per output row
-constexpr int MG_NB = 4;              // column blocks per workgroup
+constexpr uint32_t MG_OFF = 0x80000000u;  // a buffer offset past every range
+constexpr int64_t MG_TARGET_WG = 768;   // workgroups aimed for (three per CU)
+// cache policy of the output stores: non-temporal (the merged weight is not
+// read back by this pass; 35 us against 45.8 us with the default policy on the
+// 14336 x 4096 weight)
+constexpr int MG_NT = 2;
 
-template <bool F16>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t mg_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// JSX: 16-wide rank steps provided for (r <= 16 JSX); BV: B rows load as
+// 16-byte chunks (r % 8 == 0), else element by element; F16: fp16 output, else bf16
+template <int JSX, bool DQ, bool BV, bool F16>
 __global__ __launch_bounds__(256) void merge_kernel(Nf4Dev w, const float* __restrict__ codebook,
                                                     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
-                                                    int r, float s, uint16_t* __restrict__ out) {
+                                                    int r, float s, int nb, uint16_t* __restrict__ out) {
   __shared__ float cb[16];
   __shared__ __attribute__((aligned(16))) uint16_t tile[4][32 * MG_LD];
-  // A^T of the current column block, [MG_COLS][16 JS + 8] (ranks past r
-  // zero; the 16-byte pad keeps the 8-lane passes of the 16-byte reads and
-  // writes on distinct banks): dynamic, 16 JS + 8 elements per column
+  // A^T of the column block, [MG_COLS][16 JS + 8] (ranks past r zero; the
+  // 16-byte pad keeps the 8-lane passes of the 16-byte reads on distinct
+  // banks): dynamic, 16 JS + 8 elements per column
   extern __shared__ __attribute__((aligned(16))) uint16_t at[];
-  if (threadIdx.x < 16) cb[threadIdx.x] = codebook[threadIdx.x];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, g = lane >> 5;
   const int64_t N = w.N, K = w.K;
-  const int64_t nw = (int64_t)blockIdx.x * 128 + 32 * wave;  // the wave's first row
-  const int64_t n = nw + l32;                                  // the lane's row
-  const int64_t nr = n < N ? n : N - 1;
-  const int JS = (r + 15) / 16;                               // 16-wide steps over the rank, <= 8
-  const int ald = 16 * JS + 8;                                 // A^T row stride, elements
+  const int JS = (r + 15) / 16;  // <= JSX
+  const int ald = 16 * JS + 8;   // A^T row stride, elements
+  const int64_t kb = (int64_t)blockIdx.x * MG_COLS;
+  const int ncols = (int)((K - kb) < MG_COLS ? (K - kb) : MG_COLS);  // 64 or 128
+  const int64_t nrb = (N + 127) / 128;
+  const int64_t rb0 = (int64_t)blockIdx.y * nb;
+  const int64_t rb1 = (rb0 + nb) < nrb ? (rb0 + nb) : nrb;
   uint16_t* T = tile[wave];
-  // column blocks b0, b0 + 1, ... of this workgroup
-  const int64_t nblk = (K + MG_COLS - 1) / MG_COLS;
-  const int64_t b0 = (int64_t)blockIdx.y * MG_NB;
-  const int64_t b1 = (b0 + MG_NB) < nblk ? (b0 + MG_NB) : nblk;
 
-  // B operand of step js: lane (l32, g) holds B[nr][16 js + 8 g + i], i < 8 (0 past r)
-  u32x4 bop[8];
-#pragma unroll
-  for (int js = 0; js < 8; ++js) {
-    uint32_t h[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int j = 16 * js + 8 * g + i;
-      h[i] = (js < JS && j < r) ? (uint32_t)B[nr * r + j] : 0u;
-    }
-    bop[js] = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
-  }
-
-  // the row's codes (32 columns per 16 bytes) and absmax (64 columns each) of
-  // one block; the next block's are requested while this one is computed
-  u32x4 cw[MG_T], cwn[MG_T];
-  float am[MG_T / 2], amn[MG_T / 2];
-  auto load_codes = [&](int64_t blk, u32x4 (&c)[MG_T], float (&a)[MG_T / 2]) {
-    const int64_t kb = blk * MG_COLS;
-    const int nc = (int)((K - kb) < MG_COLS ? (K - kb) : MG_COLS);
+  // one row block's per-lane operands: codes (32 columns per 16 bytes), the
+  // absmax blocks, the B row as MFMA B operands
+  struct Blk {
+    u32x4 c[MG_T];
+    float am[MG_T / 2];
+    uint32_t aq[MG_T / 2];
+    float sc[MG_T / 2];
+    u32x4 b[JSX];
+  };
+  const int lrow = 32 * wave + l32;  // the lane's row within a row block
+  auto load_blk = [&](int64_t rb, Blk& d) __attribute__((always_inline)) {
+    const int64_t n0 = rb * 128;
+    const int64_t nrows = (N - n0) < 128 ? (N - n0) : 128;
+    const __amdgpu_buffer_rsrc_t crs = mg_rsrc(w.codes + n0 * (K / 2), nrows * (K / 2));
 #pragma unroll
     for (int t = 0; t < MG_T; ++t)
-      c[t] = 32 * t < nc ? *reinterpret_cast<const u32x4*>(w.codes + nr * (K / 2) + (kb + 32 * t) / 2)
-                         : u32x4{0u, 0u, 0u, 0u};
+      d.c[t] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(crs, (uint32_t)(lrow * (K / 2) + (kb + 32 * t) / 2), 0, 0));
+    const int64_t kblk = K / 64;
+    const int64_t blk0 = n0 * kblk;  // first absmax block of the row block
+    const uint32_t lb = (uint32_t)(lrow * kblk + kb / 64);
+    if constexpr (DQ) {
+      const __amdgpu_buffer_rsrc_t ars = mg_rsrc(w.absmax_q + blk0, nrows * kblk);
+      // the scales from the row block's first group to the end of the array
+      const __amdgpu_buffer_rsrc_t srs =
+          mg_rsrc(w.absmax_scale + (blk0 >> 8), ((N * kblk + 255) / 256 - (blk0 >> 8)) * 4);
 #pragma unroll
-    for (int b = 0; b < MG_T / 2; ++b) {
-      const int64_t bl = (nr * K + kb + 64 * (64 * b < nc ? b : 0)) / 64;
-      a[b] = w.dq ? absmax_at<true>(w, bl) : absmax_at<false>(w, bl);
+      for (int b = 0; b < MG_T / 2; ++b) {
+        d.aq[b] = __builtin_amdgcn_raw_buffer_load_b8(ars, lb + b, 0, 0);
+        d.sc[b] = __builtin_bit_cast(
+            float, __builtin_amdgcn_raw_buffer_load_b32(srs, (uint32_t)((((blk0 & 255) + lb + b) >> 8) * 4), 0, 0));
+      }
+    } else {
+      const __amdgpu_buffer_rsrc_t ars = mg_rsrc(w.absmax + blk0, nrows * kblk * 4);
+#pragma unroll
+      for (int b = 0; b < MG_T / 2; ++b)
+        d.am[b] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ars, (lb + b) * 4, 0, 0));
     }
-  };
-  if (b0 < b1) load_codes(b0, cw, am);
-
-  for (int64_t blk = b0; blk < b1; ++blk) {
-    const int64_t kb = blk * MG_COLS;
-    const int ncols = (int)((K - kb) < MG_COLS ? (K - kb) : MG_COLS);  // multiple of 64
-    if (blk + 1 < b1) load_codes(blk + 1, cwn, amn);
-    __syncthreads();  // every wave is done reading the previous block's A^T
-    {
-      // thread c: column kb + c of A, 8 ranks per 16-byte LDS store
-      const int c = threadIdx.x;
-      const bool cok = c < ncols;
-      for (int h = 0; h < 2 * JS; ++h) {
-        uint32_t v[8];
+    // lane (l32, g), step js: B[n][16 js + 8 g + i], i < 8
+    const __amdgpu_buffer_rsrc_t brs = mg_rsrc(B + n0 * r, nrows * r * 2);
+#pragma unroll
+    for (int js = 0; js < JSX; ++js) {
+      const int j0 = 16 * js + 8 * g;
+      if constexpr (BV) {
+        const uint32_t o = j0 < r ? (uint32_t)((lrow * r + j0) * 2) : MG_OFF;
+        d.b[js] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(brs, o, 0, 0));
+      } else {
+        uint32_t h[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          const int j = 8 * h + i;
-          v[i] = (cok && j < r) ? (uint32_t)A[(int64_t)j * K + kb + c] : 0u;
+          const uint32_t o = j0 + i < r ? (uint32_t)((lrow * r + j0 + i) * 2) : MG_OFF;
+          h[i] = __builtin_amdgcn_raw_buffer_load_b16(brs, o, 0, 0);
         }
-        *reinterpret_cast<u32x4*>(at + c * ald + 8 * h) =
-            u32x4{v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16), v[6] | (v[7] << 16)};
+        d.b[js] = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
       }
     }
-    __syncthreads();
+  };
 
+  auto step = [&](int64_t rb, const Blk& d) __attribute__((always_inline)) {
 #pragma unroll
     for (int t = 0; t < MG_T; ++t) {
       if (32 * t >= ncols) break;
@@ -120,20 +141,20 @@ __global__ __launch_bounds__(256) void merge_kernel(Nf4Dev w, const float* __res
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
 #pragma unroll
-      for (int js = 0; js < 8; ++js) {
+      for (int js = 0; js < JSX; ++js) {
         if (js >= JS) break;
         const u32x4 aop = *reinterpret_cast<const u32x4*>(at + (32 * t + l32) * ald + 16 * js + 8 * g);
-        acc = mfma32(aop, bop[js], acc);
+        acc = mfma32(aop, d.b[js], acc);
       }
-      const float a = am[t >> 1];
+      const float a = DQ ? (float)d.aq[t >> 1] * d.sc[t >> 1] : d.am[t >> 1];
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         // columns 32 t + 8 q4 + 4 g + b: nibbles 16 g + 4 b of code dword q4
         float x[4];
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-          const float d = cb[(cw[t][q4] >> (16 * g + 4 * b)) & 15u] * a;
-          x[b] = d + s * acc[4 * q4 + b];
+          const float dv = cb[(d.c[t][q4] >> (16 * g + 4 * b)) & 15u] * a;
+          x[b] = dv + s * acc[4 * q4 + b];
         }
         uint32_t p0, p1;
         if constexpr (F16) {
@@ -150,18 +171,46 @@ __global__ __launch_bounds__(256) void merge_kernel(Nf4Dev w, const float* __res
     }
     // the wave reads back only its own tile: LDS operations of a wave complete
     // in order, so no barrier is needed
+    const int64_t n0 = rb * 128;
+    const int64_t nrows = (N - n0) < 128 ? (N - n0) : 128;
+    const __amdgpu_buffer_rsrc_t ors = mg_rsrc(out + n0 * K, nrows * K * 2);
     constexpr int RPI = 64 / MG_CH;  // rows per store instruction
 #pragma unroll
     for (int i = 0; i < 32 / RPI; ++i) {
       const int row = RPI * i + lane / MG_CH, ch = lane % MG_CH;  // 16-byte chunk ch of the row
-      if (8 * ch < ncols && nw + row < N)
-        *reinterpret_cast<u32x4*>(out + (nw + row) * K + kb + 8 * ch) =
-            *reinterpret_cast<const u32x4*>(T + row * MG_LD + 8 * ch);
+      const uint32_t o = 8 * ch < ncols ? (uint32_t)(((32 * wave + row) * K + kb + 8 * ch) * 2) : MG_OFF;
+      __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4*>(T + row * MG_LD + 8 * ch), ors, o, 0,
+                                             MG_NT);
     }
+  };
+
+  // row blocks two at a time through two operand sets, each loaded one block
+  // ahead (past the end the last block is loaded again); the first block's
+  // operands are requested before A^T is staged
+  Blk b0, b1;
+  load_blk(rb0, b0);
+  if (tid < 16) cb[tid] = codebook[tid];
+  {
+    // (rank j, 8-column chunk ch) pairs; ranks past r and chunks past K read
+    // a valid address and store zeros
+    for (int idx = tid; idx < 16 * JS * MG_CH; idx += 256) {
+      const int j = idx / MG_CH, ch = idx % MG_CH;
+      const bool ok = j < r && 8 * ch < ncols;
+      const uint16_t* src = A + (int64_t)(ok ? j : 0) * K + kb + (ok ? 8 * ch : 0);
+      uint16_t v[8];
 #pragma unroll
-    for (int t = 0; t < MG_T; ++t) cw[t] = cwn[t];
+      for (int i = 0; i < 8; ++i) v[i] = src[i];
 #pragma unroll
-    for (int b = 0; b < MG_T / 2; ++b) am[b] = amn[b];
+      for (int i = 0; i < 8; ++i) at[(8 * ch + i) * ald + j] = ok ? v[i] : (uint16_t)0;
+    }
+  }
+  __syncthreads();
+  for (int64_t rb = rb0; rb < rb1; rb += 2) {
+    load_blk((rb + 1) < rb1 ? rb + 1 : rb1 - 1, b1);
+    step(rb, b0);
+    if (rb + 1 >= rb1) break;
+    load_blk((rb + 2) < rb1 ? rb + 2 : rb1 - 1, b0);
+    step(rb + 1, b1);
   }
 }
 
@@ -173,12 +222,26 @@ hipError_t launch_merge(const Nf4Dev& w, const float* codebook, const uint16_t* 
                         float s, int f16, uint16_t* out, hipStream_t st) {
   if (w.N == 0 || w.K == 0) return hipSuccess;
   if (r < 1 || r > 128 || w.K % 64 != 0) return hipErrorInvalidValue;
-  const int64_t nblk = (w.K + MG_COLS - 1) / MG_COLS;
-  const dim3 grid((unsigned)((w.N + 127) / 128), (unsigned)((nblk + MG_NB - 1) / MG_NB));
-  const size_t at_bytes = (size_t)MG_COLS * (16 * ((r + 15) / 16) + 8) * 2;
-  if (f16)
-    merge_kernel<true><<<grid, 256, at_bytes, st>>>(w, codebook, A, B, r, s, out);
-  else
-    merge_kernel<false><<<grid, 256, at_bytes, st>>>(w, codebook, A, B, r, s, out);
+  const int64_t ncb = (w.K + MG_COLS - 1) / MG_COLS, nrb = (w.N + 127) / 128;
+  // row blocks per workgroup: about MG_TARGET_WG workgroups in all
+  const int64_t nb = std::max<int64_t>(1, (ncb * nrb + MG_TARGET_WG - 1) / MG_TARGET_WG);
+  const dim3 grid((unsigned)ncb, (unsigned)((nrb + nb - 1) / nb));
+  const int js = (r + 15) / 16;
+  const size_t at_bytes = (size_t)MG_COLS * (16 * js + 8) * 2;
+  const bool dq = w.dq != 0, bv = r % 8 == 0;
+#define MG_LAUNCH(JSX, DQ, BV)                                                                             \
+  if (f16) merge_kernel<JSX, DQ, BV, true><<<grid, 256, at_bytes, st>>>(w, codebook, A, B, r, s, (int)nb, out); \
+  else merge_kernel<JSX, DQ, BV, false><<<grid, 256, at_bytes, st>>>(w, codebook, A, B, r, s, (int)nb, out)
+#define MG_BV(JSX, DQ) \
+  if (bv) { MG_LAUNCH(JSX, DQ, true); } else { MG_LAUNCH(JSX, DQ, false); }
+#define MG_DQ(JSX) \
+  if (dq) { MG_BV(JSX, true); } else { MG_BV(JSX, false); }
+  if (js == 1) { MG_DQ(1) }
+  else if (js == 2) { MG_DQ(2) }
+  else if (js <= 4) { MG_DQ(4) }
+  else { MG_DQ(8) }
+#undef MG_DQ
+#undef MG_BV
+#undef MG_LAUNCH
   return hipGetLastError();
 }

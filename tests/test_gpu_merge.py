@@ -21,7 +21,7 @@ import synth
 from oracle import nf4 as onf4
 from oracle import qlora as oq
 
-from gpu_util import bf16_dev, make_linear, u16_host
+from gpu_util import Guarded, bf16_dev, make_linear, u16_host
 
 pytestmark = pytest.mark.gpu
 
@@ -71,6 +71,10 @@ CASES = [
     ("r128_256x512_f16", 256, 512, 128, 0, 16.0, "f16", 32),
     ("1024x4096_r16_dq_f16", 1024, 4096, 16, 256, 32.0, "f16", 33),
     ("64x64_r1", 64, 64, 1, 0, 2.0, "bf16", 34),
+    # enough 128 x 128 blocks that a workgroup walks two row blocks, the last
+    # group one (31 row blocks), with a 64-column tail and ranks in 33..64
+    ("ragged_3968x4160_r50_dq_2blk", 3968, 4160, 50, 256, 16.0, "bf16", 35),
+    ("4096x4096_r32_2blk", 4096, 4096, 32, 0, 16.0, "bf16", 36),
 ]
 
 
@@ -79,8 +83,9 @@ def test_merge_matches_oracle(name, N, K, r, dq, alpha, dtype, seed, codebook):
     print("case", name, flush=True)
     W, A, B = _inputs(N, K, r, seed)
     L, Wh = make_linear(q, W, A, B, alpha, codebook, dq)
-    out = q.qlora_merge(L, torch.bfloat16 if dtype == "bf16" else torch.float16)
-    torch.cuda.synchronize()
+    g = Guarded()
+    out = q.qlora_merge(L, out=g.empty((N, K), torch.bfloat16 if dtype == "bf16" else torch.float16))
+    g.check()
     ref = oq.merge_16bit(Wh, A, B, alpha, dtype)
     _assert_merge_close(u16_host(out), ref, dtype)
 
