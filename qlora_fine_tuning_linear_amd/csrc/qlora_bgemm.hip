@@ -510,9 +510,15 @@ __global__ __launch_bounds__(512) void bgemm_kernel(GemmArgs p) {
   // tile kt in halves (ca, cb); tile kt+1 goes to (na, nb), and fb is the
   // fifth buffer, which takes the first half of kt+2.  nb and fb were freed
   // by the barrier of tile kt-1.
+  // The gate/up + SwiGLU kind raises its waves' priority over the three
+  // matrix phases before the barrier, so that a wave with MFMAs ready issues
+  // ahead of the other wave on its SIMD issuing loads (measured on the 8B
+  // MLP: 1662 -> 1618 us; no gain for the other kinds).
+  constexpr bool PRIO = ModeTraits<MODE>::swiglu_fwd;
   auto tile = [&](int kt, uint16_t* ca, uint16_t* cb, uint16_t* na, uint16_t* nb, uint16_t* fb) {
     rd(ca, cb, 1, x1, w1);
     load_second(nb, kt + 1);
+    if constexpr (PRIO) __builtin_amdgcn_s_setprio(1);
     mm(x0, w0);
     interleave_reads();
     rd(ca, cb, 2, x0, w0);
@@ -522,6 +528,7 @@ __global__ __launch_bounds__(512) void bgemm_kernel(GemmArgs p) {
     rd(ca, cb, 3, x1, w1);
     mm(x0, w0);
     interleave_reads();
+    if constexpr (PRIO) __builtin_amdgcn_s_setprio(0);
     wait_vmcnt<LPH>();  // tile kt+1 landed; the first half of kt+2 may be in flight
     stage_barrier();
     __builtin_amdgcn_sched_barrier(0);
