@@ -866,11 +866,15 @@ __global__ __launch_bounds__(256) void lora_grad_kernel(const uint16_t* __restri
   // two register sets alternate; the next slab is in flight during the current one
   Slab ra, rb;
   int64_t ms = mb;
-  if (ms < me) load(ms, ra);
+  // unconditional prefetches (rows past the split are clamped to its last
+  // row and masked), so that the compiler can count the loads in flight
+  load(ms, ra);
   for (; ms + 16 < me; ms += 32) {
     load(ms + 16, rb);
+    __builtin_amdgcn_sched_barrier(0);  // the prefetch is issued before the products
     slab(ms, ra);
-    if (ms + 32 < me) load(ms + 32, ra);
+    load(ms + 32, ra);
+    __builtin_amdgcn_sched_barrier(0);
     slab(ms + 16, rb);
   }
   if (ms < me) slab(ms, ra);
@@ -981,11 +985,15 @@ __device__ __forceinline__ void lora_grad16_body(const uint16_t* __restrict__ Z0
   };
   Slab ra, rb;
   int64_t ms = mb;
-  if (ms < me) load(ms, ra);
+  // unconditional prefetches (rows past the split are clamped to its last
+  // row and masked), so that the compiler can count the loads in flight
+  load(ms, ra);
   for (; ms + 32 < me; ms += 64) {
     load(ms + 32, rb);
+    __builtin_amdgcn_sched_barrier(0);  // the prefetch is issued before the products
     slab(ms, ra);
-    if (ms + 64 < me) load(ms + 64, ra);
+    load(ms + 64, ra);
+    __builtin_amdgcn_sched_barrier(0);
     slab(ms + 32, rb);
   }
   if (ms < me) slab(ms, ra);
@@ -1066,6 +1074,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void l
                                             : u32x4{0u, 0u, 0u, 0u};
   }
   uint16_t* zw = zs[wave];
+  // this workgroup's rows of the T partial (tokens [mb, me) of column block x)
+  const __amdgpu_buffer_rsrc_t trs = __builtin_amdgcn_make_buffer_rsrc(
+      J.tpart + ((int64_t)blockIdx.x * M + mb) * r, (short)0, (int)((me > mb ? me - mb : 0) * r * 4), 0x00020000);
 
   f32x4 acc[8];
 #pragma unroll
@@ -1134,16 +1145,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void l
       const int ln = e & 63, v = (e >> 6) & 3, f = e >> 8;
       const int64_t tok = ms + 16 * f + (ln & 15);
       const int j = 4 * (ln >> 4) + v;
-      if (tok < me && j < r) J.tpart[((int64_t)blockIdx.x * M + tok) * r + j] = sum;
+      // a buffer store without a branch (dropped out of range), so that the
+      // loads in flight stay countable
+      const uint32_t o = (tok < me && j < r) ? (uint32_t)(((tok - mb) * r + j) * 4) : 0x80000000u;
+      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, sum), trs, o, 0, 0);
     }
   };
   Slab ra, rb;
   int64_t ms = mb;
-  if (ms < me) load(ms, ra);
+  // unconditional prefetches (rows past the split are clamped to its last
+  // row and masked), so that the compiler can count the loads in flight
+  load(ms, ra);
   for (; ms + 32 < me; ms += 64) {
     load(ms + 32, rb);
+    __builtin_amdgcn_sched_barrier(0);  // the prefetch is issued before the products
     slab(ms, ra, 0);
-    if (ms + 64 < me) load(ms + 64, ra);
+    load(ms + 64, ra);
+    __builtin_amdgcn_sched_barrier(0);
     slab(ms + 32, rb, 1);
   }
   if (ms < me) slab(ms, ra, 0);
