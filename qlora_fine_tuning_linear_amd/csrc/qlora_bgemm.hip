@@ -104,7 +104,8 @@ __device__ __forceinline__ int bg_ht_index(int c, int t) {
   return c * 32 + (((t >> 3) ^ hsw) << 3) + (t & 7);
 }
 
-template <int MODE>
+// DAD: the SwiGLU backward also forms the dA_d partial (p.dad_part set)
+template <int MODE, bool DAD>
 __device__ __forceinline__ void bg_epilogue(const GemmArgs& p, f32x16 (&acc)[BG_FM][2], int64_t m0, int64_t n0,
                                              int wm, int wn, int lane, uint16_t* reg, f32x4 (&dad)[2][4]) {
   constexpr int FM = BG_FM;
@@ -162,6 +163,13 @@ __device__ __forceinline__ void bg_epilogue(const GemmArgs& p, f32x16 (&acc)[BG_
     const bool col_ok = ncol < p.Nout;
     const int64_t nc = col_ok ? ncol : p.Nout - 8;
     u32x4 gg[2][4], uu[2][4];
+    // optional: the down layer's T^T H over this wave's 128 tokens x 64
+    // columns, one 32-token frag at a time, with H = silu(G) U rounded to
+    // bf16 and stored transposed after lf (T = l0.V, rank l0.r <= 32)
+    constexpr bool with_dad = DAD;
+    const int dr = p.l0.r;
+    uint16_t* ht = reg + 4096;
+    const int l16 = lane & 15, kq = lane >> 4;
     auto load = [&](int i, int b) {
 #pragma unroll
       for (int it = 0; it < 4; ++it) {
@@ -171,17 +179,28 @@ __device__ __forceinline__ void bg_epilogue(const GemmArgs& p, f32x16 (&acc)[BG_
         uu[b][it] = *reinterpret_cast<const u32x4*>(p.in1 + m * p.Nout + nc);
       }
     };
+    // T operand values of frag i, [jf][e] = T[token 8 kq + e][j = 16 jf + l16]
+    // (zero past M and past the rank), requested at the start of the frag,
+    // before the next frag's G / U chunks, so that they arrive during the
+    // frag's dH work and their wait does not cover the next frag's loads
+    float tv[2][8];
+    auto load_t = [&](int i) {
+#pragma unroll
+      for (int jf = 0; jf < 2; ++jf) {
+        const int j = 16 * jf + l16;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int64_t m = mw + i * 32 + 8 * kq + e;
+          const float t = p.l0.V[(m < p.M ? m : p.M - 1) * dr + (j < dr ? j : dr - 1)];
+          tv[jf][e] = (j < dr && m < p.M) ? t : 0.0f;
+        }
+      }
+    };
     float* lf = reinterpret_cast<float*>(reg);
-    // optional: the down layer's T^T H over this wave's 128 tokens x 64
-    // columns, one 32-token frag at a time, with H = silu(G) U rounded to
-    // bf16 and stored transposed after lf (T = l0.V, rank l0.r <= 32)
-    const bool with_dad = p.dad_part != nullptr;
-    const int dr = p.l0.r;
-    uint16_t* ht = reg + 4096;
-    const int l16 = lane & 15, kq = lane >> 4;
     load(0, 0);
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
+      if constexpr (DAD) load_t(i);
       if (i + 1 < FM) load(i + 1, (i + 1) & 1);
       const int b = i & 1;
 #pragma unroll
@@ -230,13 +249,7 @@ __device__ __forceinline__ void bg_epilogue(const GemmArgs& p, f32x16 (&acc)[BG_
         u32x4 ta[2];
 #pragma unroll
         for (int jf = 0; jf < 2; ++jf) {
-          const int j = 16 * jf + l16;
-          float t8[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int64_t m = mw + i * 32 + 8 * kq + e;
-            t8[e] = (j < dr && m < p.M) ? p.l0.V[m * dr + j] : 0.0f;
-          }
+          const float* t8 = tv[jf];
           ta[jf] = u32x4{pack_bf16x2(t8[0], t8[1]), pack_bf16x2(t8[2], t8[3]), pack_bf16x2(t8[4], t8[5]),
                          pack_bf16x2(t8[6], t8[7])};
         }
@@ -326,7 +339,7 @@ __device__ __forceinline__ void bg_had_wave(const GemmArgs& p, f32x16 (&acc)[BG_
 // direct loads; 16-byte chunk c of row k at c ^ 4 ((k / 8) % 2), so that the
 // two lane halves of a read, 8 rows apart, hit different banks), and each
 // A operand of the MFMA is gathered as 8 two-byte reads down a column.
-template <int MODE, bool WLEAD, bool KMAJ = false>
+template <int MODE, bool WLEAD, bool KMAJ = false, bool DAD = false>
 __global__ __launch_bounds__(512) void bgemm_kernel(GemmArgs p) {
   constexpr int WN = BG_WN, FM = BG_FM, FN = BG_FN;
   constexpr int LPH = BG_LPH;
@@ -618,7 +631,7 @@ __global__ __launch_bounds__(512) void bgemm_kernel(GemmArgs p) {
   for (int jf = 0; jf < 2; ++jf)
 #pragma unroll
     for (int cf = 0; cf < 4; ++cf) dad[jf][cf] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  bg_epilogue<MODE>(p, acc, m0, n0, wm, wn, lane, buf + (wave & 1) * 8192, dad);
+  bg_epilogue<MODE, DAD>(p, acc, m0, n0, wm, wn, lane, buf + (wave & 1) * 8192, dad);
   if constexpr (MODE == MODE_BWD_SWIGLU) {
     if (p.dad_part) {
       // the two token halves of each 64-column strip are added (waves 4..7
@@ -800,6 +813,15 @@ static hipError_t run_bgemm(GemmArgs a, hipStream_t st) {
   if constexpr (MODE == MODE_FWD) {
     if (a.w_kmajor) {
       bgemm_kernel<MODE, false, true><<<dim3((unsigned)n, splits), 512, 0, st>>>(a);
+      return hipGetLastError();
+    }
+  }
+  if constexpr (MODE == MODE_BWD_SWIGLU) {
+    if (a.dad_part) {
+      if (a.wrows > a.M)
+        bgemm_kernel<MODE, true, false, true><<<dim3((unsigned)n, splits), 512, 0, st>>>(a);
+      else
+        bgemm_kernel<MODE, false, false, true><<<dim3((unsigned)n, splits), 512, 0, st>>>(a);
       return hipGetLastError();
     }
   }
