@@ -357,12 +357,35 @@ __global__ __launch_bounds__(256) void skinny_fwd2_kernel(SkinnyArgs p) {
   // also writes it out (the forward keeps X A^T)
   float* vs = reinterpret_cast<float*>(ring1);  // [M][r], r <= 64
   if (lora_here) {
+    // split z's partials are added in order z = 0, 1, ... for every entry;
+    // the loads of 8 splits x 4 entries are issued together (one load and
+    // its wait per split would put 4 x vsplits L2 round trips in a row)
     const int n = (int)p.M * p.r;
-    for (int e = tid; e < n; e += 256) {
-      float v = 0.0f;
-      for (int z = 0; z < p.vsplits; ++z) v += p.vpart[(int64_t)z * n + e];
-      vs[e] = v;
-      if (p.vout && blockIdx.x == 0) p.vout[e] = v;
+    for (int e0 = tid; e0 < n; e0 += 256 * 4) {
+      float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      for (int z0 = 0; z0 < p.vsplits; z0 += 8) {
+        float t[4][8];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int zz = 0; zz < 8; ++zz) {
+            const int e = min(e0 + 256 * j, n - 1), z = min(z0 + zz, p.vsplits - 1);
+            t[j][zz] = p.vpart[(int64_t)z * n + e];
+          }
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int zz = 0; zz < 8; ++zz)
+            if (z0 + zz < p.vsplits) v[j] += t[j][zz];
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int e = e0 + 256 * j;
+        if (e < n) {
+          vs[e] = v[j];
+          if (p.vout && blockIdx.x == 0) p.vout[e] = v[j];
+        }
+      }
     }
   }
   __syncthreads();
