@@ -227,6 +227,10 @@ int nf4_dequantize(const qlora_nf4* w, int32_t out_dtype, void* out, void* strea
 // ------------------------------------------------------------------ groups
 // The packed groups as one layer: W0 and the stacked A as given, B the
 // block-diagonal of bf16(s_g B_g) held in the workspace, s = 1.
+static int linear_bwd_impl(const qlora_linear* L, const void* dY, const void* X, const float* XA_saved, int64_t M,
+                           void* dX, void* dA, void* dB, const GroupDesc* grp, bool* grp_done, void* ws,
+                           size_t ws_bytes, void* stream);
+
 static qlora_linear grouped_layer(const qlora_grouped* Q, GroupDesc* d) {
   memset(d, 0, sizeof(*d));
   d->G = Q->G;
@@ -293,7 +297,10 @@ int qlora_grouped_bwd(const qlora_grouped* Q, const void* dY, const void* X, con
   uint16_t* dbcat = reinterpret_cast<uint16_t*>(bytes(ws) + bc);
   QHIP(launch_grouped_bcat(d, (int)Q->W0.N, L.r, bcat, st));
   L.B = bcat;
-  QTRY(qlora_linear_bwd(&L, dY, X, XA_saved, M, dX, dA, dbcat, bytes(ws) + 2 * bc, ws_bytes - 2 * bc, stream));
+  bool done = false;
+  QTRY(linear_bwd_impl(&L, dY, X, XA_saved, M, dX, dA, dbcat, &d, &done, bytes(ws) + 2 * bc, ws_bytes - 2 * bc,
+                       stream));
+  if (done) return QLORA_OK;
   return hip_status(launch_grouped_db(d, (int)Q->W0.N, L.r, dbcat, st));
 }
 
@@ -469,6 +476,16 @@ int qlora_linear_fwd_static(const qlora_linear* L, const void* X, int64_t M, voi
 
 int qlora_linear_bwd(const qlora_linear* L, const void* dY, const void* X, const float* XA_saved, int64_t M, void* dX,
                      void* dA, void* dB, void* ws, size_t ws_bytes, void* stream) {
+  return linear_bwd_impl(L, dY, X, XA_saved, M, dX, dA, dB, nullptr, nullptr, ws, ws_bytes, stream);
+}
+
+// grp: the layer is packed LoRA groups (B block-diagonal); when the dB
+// reduction can run per group (grouped_grad_ok), each group's dB is written
+// straight from dY and its own ranks of XA, dB is left alone and *grp_done
+// set; otherwise dB receives the [N, r] block-diagonal gradient.
+static int linear_bwd_impl(const qlora_linear* L, const void* dY, const void* X, const float* XA_saved, int64_t M,
+                           void* dX, void* dA, void* dB, const GroupDesc* grp, bool* grp_done, void* ws,
+                           size_t ws_bytes, void* stream) {
   QTRY(qv_linear_bwd(L, dY, X, XA_saved, M, dX, dA, dB, ws, ws_bytes));
   QTRY(check_device());
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -587,9 +604,16 @@ int qlora_linear_bwd(const qlora_linear* L, const void* dY, const void* X, const
     if (pl.splits > 1) QHIP(launch_splitk_finish(part, pl.splits, M, K, u16m(dX), st));
   }
   // dB = s dY^T XA  ([N, r], unless done above);  dA = s T^T X  ([r, K])
-  if (!pair)
+  const int64_t grp_cap = (int64_t)(w.bwd_grad / ((size_t)N * 64));  // [S][N][16] fp32 partials that fit
+  if (!pair && grp && grp_cap >= 1 && grouped_grad_ok(*grp, N)) {
+    int ms = qplan::plan_grad_msplits(M, N, 16);
+    if (ms > grp_cap) ms = (int)grp_cap;
+    QHIP(launch_grouped_grad(*grp, u16(dY), M, N, XA_saved, r, ms, grad_part, st));
+    *grp_done = true;
+  } else if (!pair) {
     QHIP(launch_lora_grad(0, u16(dY), nullptr, M, N, XA_saved, r, s, qplan::plan_grad_msplits(M, N, r), grad_part,
                           0, u16m(dB), st));
+  }
   QHIP(launch_lora_grad(0, u16(X), nullptr, M, K, T, r, s, qplan::plan_grad_msplits(M, K, r), grad_part, 1, u16m(dA),
                         st));
   return QLORA_OK;

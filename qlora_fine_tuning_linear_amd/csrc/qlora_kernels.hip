@@ -911,7 +911,11 @@ __device__ __forceinline__ void lora_grad16_body(const uint16_t* __restrict__ Z0
                                                           const uint16_t* __restrict__ Z1, int64_t M, int64_t P,
                                                           const float* __restrict__ V, int r, int64_t m_per_split,
                                                           float* __restrict__ part, const float* __restrict__ V1 = nullptr,
-                                                          int r1 = 0, float* __restrict__ part1 = nullptr) {
+                                                          int r1 = 0, float* __restrict__ part1 = nullptr,
+                                                          int vs = 0, int ps = 0) {
+  // vs: row stride of V (r unless V is a column slice of a wider matrix);
+  // ps: row stride of the partials (r unless set)
+  const int vstride = vs ? vs : r, pstride = ps ? ps : r;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = lane & 15, q = lane >> 4;
   const int64_t p0 = ((int64_t)blockIdx.x * 4 + wave) * 128;
@@ -942,7 +946,7 @@ __device__ __forceinline__ void lora_grad16_body(const uint16_t* __restrict__ Z0
       if (mm >= me) mm = me - 1;
       S.raw[0][e] = *reinterpret_cast<const u32x4*>(Z0 + mm * P + pc);
       if constexpr (ZMODE == 1) S.raw[NZ - 1][e] = *reinterpret_cast<const u32x4*>(Z1 + mm * P + pc);
-      S.x[0][e] = V[mm * r + jv];
+      S.x[0][e] = V[mm * vstride + jv];
       if constexpr (NV > 1) S.x[NV - 1][e] = V1[mm * r1 + jv1];
     }
   };
@@ -1001,7 +1005,7 @@ __device__ __forceinline__ void lora_grad16_body(const uint16_t* __restrict__ Z0
   // acc[k][t][v] = C[row 4q + v][j = c]: column p = p0 + 8 (4q + v) + t
 #pragma unroll
   for (int k = 0; k < NV; ++k) {
-    const int rk = k == 0 ? r : r1;
+    const int rk = k == 0 ? r : r1, sk = k == 0 ? pstride : r1;
     float* pk = k == 0 ? part : part1;
     if (c >= rk) continue;
 #pragma unroll
@@ -1009,7 +1013,7 @@ __device__ __forceinline__ void lora_grad16_body(const uint16_t* __restrict__ Z0
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int64_t pp = p0 + 8 * (4 * q + v) + t;
-        if (pp < P) pk[((int64_t)z * P + pp) * rk + c] = acc[k][t][v];
+        if (pp < P) pk[((int64_t)z * P + pp) * sk + c] = acc[k][t][v];
       }
   }
 }
@@ -1020,6 +1024,45 @@ __global__ __launch_bounds__(256) void lora_grad16_kernel(const uint16_t* __rest
                                                           const float* __restrict__ V, int r, int64_t m_per_split,
                                                           float* __restrict__ part) {
   lora_grad16_body<ZMODE, 1>(Z0, Z1, M, P, V, r, m_per_split, part);
+}
+
+// Packed LoRA groups (one layer whose B is block-diagonal): dB_g only needs
+// group g's own ranks of XA, so the wave over columns [p0, p0 + 128) (all of
+// one group, its boundaries being multiples of 128) reduces against the
+// column slice XA[:, roff_g .. roff_g + r_g) of the [M, Rt] matrix.  Partials
+// [S][P][16], rank j of column p at p * 16 + j.
+__global__ __launch_bounds__(256) void lora_grad16_grouped_kernel(GroupDesc d, const uint16_t* __restrict__ Z,
+                                                                  int64_t M, int64_t P, const float* __restrict__ V,
+                                                                  int Rt, int64_t m_per_split,
+                                                                  float* __restrict__ part) {
+  const int64_t p0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 128;
+  if (p0 >= P) return;
+  const int g = group_of(d, (int)p0);
+  lora_grad16_body<0, 1>(Z, nullptr, M, P, V + d.roff[g], d.roff[g + 1] - d.roff[g], m_per_split, part, nullptr, 0,
+                         nullptr, Rt, 16);
+}
+
+// dB_g = bf16(s_g sum_z part[z]) for the partials of lora_grad16_grouped_kernel
+__global__ __launch_bounds__(256) void grouped_grad_finish_kernel(GroupDesc d, const float* __restrict__ part, int S,
+                                                                  int64_t P) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= P * 16) return;
+  const int p = (int)(i >> 4), j = (int)(i & 15);
+  const int g = group_of(d, p);
+  const int rg = d.roff[g + 1] - d.roff[g];
+  if (j >= rg) return;
+  float acc = 0.0f;
+  const int64_t stride = P * 16;
+  int z = 0;
+  for (; z + 8 <= S; z += 8) {  // 8 loads in flight, added in split order
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = part[(int64_t)(z + u) * stride + i];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc += v[u];
+  }
+  for (; z < S; ++z) acc += part[(int64_t)z * stride + i];
+  d.dB[g][(int64_t)(p - d.noff[g]) * rg + j] = (uint16_t)(pack_bf16x2(d.s[g] * acc, 0.0f) & 0xFFFFu);
 }
 
 // the two-V form, held to two waves per SIMD
@@ -1461,6 +1504,27 @@ hipError_t launch_lora_grad2(const uint16_t* Z, int64_t M, int64_t P, const floa
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   grad_finish2_kernel<<<grid1(P * (r0 + r1), 256), 256, 0, st>>>(part, r0, s0, out0, part1, r1, s1, out1, S, P);
+  return hipGetLastError();
+}
+
+bool grouped_grad_ok(const GroupDesc& d, int64_t P) {
+  if (P % 8 != 0) return false;
+  for (int g = 0; g < d.G; ++g) {
+    if (d.roff[g + 1] - d.roff[g] > 16) return false;
+    if (g > 0 && d.noff[g] % 128 != 0) return false;
+  }
+  return true;
+}
+
+hipError_t launch_grouped_grad(const GroupDesc& d, const uint16_t* Z, int64_t M, int64_t P, const float* V, int Rt,
+                               int msplits, float* part, hipStream_t st) {
+  if (M == 0 || !grouped_grad_ok(d, P)) return hipErrorInvalidValue;
+  const int64_t mps = (((M + msplits - 1) / msplits) + 31) / 32 * 32;
+  const int S = (int)((M + mps - 1) / mps);
+  lora_grad16_grouped_kernel<<<dim3(grid1(P, 512), (unsigned)S), 256, 0, st>>>(d, Z, M, P, V, Rt, mps, part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  grouped_grad_finish_kernel<<<grid1(P * 16, 256), 256, 0, st>>>(d, part, S, P);
   return hipGetLastError();
 }
 

@@ -154,6 +154,13 @@ struct GroupDesc {
 hipError_t launch_grouped_bcat(const GroupDesc& d, int Nt, int Rt, uint16_t* out, hipStream_t st);
 // dB_g = bf16(s_g * diagonal block g of dbcat [Nt, Rt])
 hipError_t launch_grouped_db(const GroupDesc& d, int Nt, int Rt, const uint16_t* dbcat, hipStream_t st);
+// dB_g = bf16(s_g Z_g^T V[:, roff_g .. roff_g + r_g)) straight from Z [M, P]
+// (P = Nt columns, Z_g its group-g columns) and V fp32 [M, Rt], when every
+// r_g <= 16, P % 8 == 0 and every group boundary is a multiple of 128
+// (grouped_grad_ok); part fp32 [S][P][16] with S <= msplits.
+bool grouped_grad_ok(const GroupDesc& d, int64_t P);
+hipError_t launch_grouped_grad(const GroupDesc& d, const uint16_t* Z, int64_t M, int64_t P, const float* V, int Rt,
+                               int msplits, float* part, hipStream_t st);
 // RMSNorm: Y = X rstd w (rstd saved per row) and its backward; D % 8 == 0,
 // D <= 8192.  The backward with dw needs part fp32 [rmsnorm_bwd_groups(M)][D].
 int rmsnorm_bwd_groups(int64_t M);

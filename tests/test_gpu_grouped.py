@@ -10,8 +10,10 @@ are the concatenated Y and XA, the summed dX and the per-group dA, dB.
 Cases: the Llama-3-8B q/k/v shapes (K=4096, N = 4096 / 1024 / 1024, r=16) on
 both GEMM paths (256 and 1024 tokens); a ragged group set with different
 ranks and scales that are not powers of two (so the packed B is rounded);
-G = 1; the skinny path (33 tokens); M = 0.  Bar: relative Frobenius error
-1e-2 on every output.
+G = 1; the skinny path (33 tokens); ranks <= 16 with group boundaries on and
+off multiples of 128 rows (dB reduced per group, or as the whole
+block-diagonal gradient); M = 0.  Bar: relative Frobenius error 1e-2 on every
+output.
 """
 import numpy as np
 import pytest
@@ -86,6 +88,11 @@ CASES = [
     ("ragged_scales_dq", 512, [192, 64, 128], [8, 24, 5], [16.0, 8.0, 3.0], 70, 256, 3003),
     ("single_group", 256, [128], [12], [24.0], 100, 0, 3004),
     ("skinny_m33", 1024, [256, 256], [16, 16], [16.0, 32.0], 33, 256, 3005),
+    # ranks <= 16 and group boundaries on 128-row multiples: dB reduced per
+    # group against its own ranks of XA (last 128-column wave ragged, ragged
+    # token tail); then the same ranks with a boundary off the 128 grid
+    ("per_group_db_m777", 512, [256, 384, 192], [16, 5, 11], [16.0, 7.0, 3.0], 777, 0, 3007),
+    ("unaligned_groups_m300", 512, [192, 320], [16, 8], [16.0, 5.0], 300, 256, 3008),
 ]
 
 
