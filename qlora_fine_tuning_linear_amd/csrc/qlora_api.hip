@@ -639,8 +639,11 @@ static int mlp_fwd_impl(const qlora_mlp* P, const void* X, int64_t M, void* Y, c
   uint16_t* H = reinterpret_cast<uint16_t*>(bytes(ws));
   float* down_part = reinterpret_cast<float*>(bytes(ws) + w.fwd_H);
   float* had_part = w.fwd_had ? reinterpret_cast<float*>(bytes(ws) + w.fwd_H + w.fwd_down) : nullptr;
-  uint16_t* wbuf =
-      w.fwd_wbuf ? reinterpret_cast<uint16_t*>(bytes(ws) + w.fwd_H + w.fwd_down + w.fwd_had) : nullptr;
+  uint16_t* ext_act =
+      w.fwd_ext ? reinterpret_cast<uint16_t*>(bytes(ws) + w.fwd_H + w.fwd_down + w.fwd_had) : nullptr;
+  uint16_t* wbuf = w.fwd_wbuf
+                       ? reinterpret_cast<uint16_t*>(bytes(ws) + w.fwd_H + w.fwd_down + w.fwd_had + w.fwd_ext)
+                       : nullptr;
 
   // XA_g | XA_u in one pass over X (the down-projection kernels take a
   // combined rank of at most 128; above that, one pass per layer)
@@ -673,10 +676,20 @@ static int mlp_fwd_impl(const qlora_mlp* P, const void* X, int64_t M, void* Y, c
     a.out1 = u16m(S->U);
     a.out2 = H;
     if (wbuf) {
+      // the LoRA terms as extra reduction columns: [s_g XA_g | s_u XA_u]
+      // against [B_g | 0] (gate rows) and [0 | B_u] (up rows)
+      const int rg = P->gate.r, ru = P->up.r;
+      const int64_t ext = qplan::lora_ext_cols(rg, ru);
       QHIP(launch_dequant_rows(a.w0, &a.w1, a.codebook, a.codebook1, qplan::pair_rows(I), wbuf, st,
-                               rf ? rf->w : nullptr));
+                               rf ? rf->w : nullptr, D + ext));
+      QHIP(launch_lora_ext_cols(u16(P->gate.B), rg, u16(P->up.B), ru, I, qplan::pair_rows(I), D, D + ext, ext, wbuf,
+                                st));
+      QHIP(launch_lora_ext_act(a.l0.V, rg, a.l0.s, a.l1.V, ru, a.l1.s, M, ext, ext_act, st));
+      a.act1 = ext_act;
+      a.lda1 = ext;
+      a.Kred1 = ext;
       a.wb = wbuf;
-      a.ldw = D;
+      a.ldw = D + ext;
       a.wrows = qplan::pair_rows(I);
       if (had_part) {  // HA_d from the GEMM's own H, as column-tile partials
         a.had_A = u16(P->down.A);

@@ -365,6 +365,9 @@ __global__ __launch_bounds__(512) void bgemm_kernel(GemmArgs p) {
   const int64_t wr0 = tn * BN;  // first weight row of the tile
   const int KT0 = (int)(p.Kred0 / 64);
   const int64_t lda = p.lda > 0 ? p.lda : p.Kred0;  // activation row stride
+  const int64_t lda1 = p.lda1 > 0 ? p.lda1 : lda;   // act1's
+  // the SwiGLU forward's act1 (the LoRA extension) has its own row stride
+  constexpr bool A1 = ModeTraits<MODE>::swiglu_fwd;
   // Reduction split (plain forward mode only, gridDim.y > 1): workgroup
   // (x, y) takes reduction tiles [kb, kb + KT) and writes fp32 partials.
   const int kb = gridDim.y > 1 ? (int)blockIdx.y * p.ktiles_per_split : 0;
@@ -373,7 +376,7 @@ __global__ __launch_bounds__(512) void bgemm_kernel(GemmArgs p) {
 
   // direct load i (0..7) of this wave: tile rows 8 (8 wave + i) + lane/8,
   // physical chunk lane%8 <- logical chunk (lane%8) ^ swz(row)
-  uint32_t aoff[LPH], boff[LPH];
+  uint32_t aoff[LPH], boff[LPH], aoff1[A1 ? LPH : 1];
 #pragma unroll
   for (int i = 0; i < LPH; ++i) {
     const int row = 8 * (LPH * wave + i) + (lane >> 3);
@@ -383,6 +386,7 @@ __global__ __launch_bounds__(512) void bgemm_kernel(GemmArgs p) {
     int64_t rb = wr0 + row;
     if (rb >= p.wrows) rb = p.wrows - 1;
     aoff[i] = (uint32_t)((ra - m0) * lda) + (uint32_t)c * 8;
+    if constexpr (A1) aoff1[i] = (uint32_t)((ra - m0) * lda1) + (uint32_t)c * 8;
     boff[i] = (uint32_t)((rb - wr0) * p.ldw) + (uint32_t)c * 8;
     if constexpr (KMAJ) {
       // load i of this wave: reduction rows 2 (4 wave + i) + lane / 32 of the
@@ -402,7 +406,7 @@ __global__ __launch_bounds__(512) void bgemm_kernel(GemmArgs p) {
   };
   const int64_t abytes = (p.M - m0) * lda * 2;
   const __amdgpu_buffer_rsrc_t ra0 = rsrc(p.act0 + m0 * lda, abytes);
-  const __amdgpu_buffer_rsrc_t ra1 = rsrc((p.act1 ? p.act1 : p.act0) + m0 * lda, abytes);
+  const __amdgpu_buffer_rsrc_t ra1 = rsrc((p.act1 ? p.act1 : p.act0) + m0 * lda1, (p.M - m0) * lda1 * 2);
   const __amdgpu_buffer_rsrc_t rb = rsrc(p.wb + (KMAJ ? wr0 : wr0 * p.ldw), (p.wrows - wr0) * p.ldw * 2);
 
   // 8 direct loads of one operand half of tile kt (clamped to the last tile:
@@ -411,15 +415,19 @@ __global__ __launch_bounds__(512) void bgemm_kernel(GemmArgs p) {
   for (int i = 0; i < LPH; ++i) {
     aoff[i] *= 2;
     boff[i] *= 2;
+    if constexpr (A1) aoff1[i] *= 2;
   }
   auto load_a = [&](uint16_t* buf, int kt) {
     kt = (kt < KT ? kt : KT - 1) + kb;
     const bool second = kt >= KT0;
     const int so = (second ? kt - KT0 : kt) * 128;
 #pragma unroll
-    for (int i = 0; i < LPH; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(second ? ra1 : ra0, LDS_PTR(buf + (LPH * wave + i) * 512), 16, aoff[i],
+    for (int i = 0; i < LPH; ++i) {
+      uint32_t off = aoff[i];
+      if constexpr (A1) off = second ? aoff1[i] : off;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(second ? ra1 : ra0, LDS_PTR(buf + (LPH * wave + i) * 512), 16, off,
                                                so, 0, 0);
+    }
   };
   auto load_b = [&](uint16_t* buf, int kt) {
     kt = (kt < KT ? kt : KT - 1) + kb;
@@ -561,21 +569,28 @@ __global__ __launch_bounds__(512) void bgemm_kernel(GemmArgs p) {
     // the pipeline fill is issued (so the compiler's wait for it lets the
     // fill stay in flight) and applied after; remaining steps (rank > 16)
     // and the scalar form follow the fill.
-    const LoraSide* L[2];
-    int lo[2], hi[2];
-    const int ns = lora_sides<MODE, FN, true>(p, L, lo, hi);  // split runs: split 0 only
+    const LoraSide* L[2] = {&p.l0, &p.l0};
+    int lo[2] = {0, 0}, hi[2] = {0, 0};
+    // (none in the SwiGLU forward: it takes its LoRA terms as reduction
+    // columns, act1 against the weight rows' extension)
+    int ns = 0;
+    if constexpr (!A1) ns = lora_sides<MODE, FN, true>(p, L, lo, hi);  // split runs: split 0 only
     const bool fast = lora_fast(*L[0]) && (ns < 2 || lora_fast(*L[1]));
-    LoraRegs<FM, FN> R0, R1;
-    if (fast) {
-      if (ns > 0) lora_load<MODE, WN, FM, FN>(p, *L[0], 0, arow, n0, wn, l32, g, R0);
-      if (ns > 1) lora_load<MODE, WN, FM, FN>(p, *L[1], 0, arow, n0, wn, l32, g, R1);
-    }
+    // One side's operands in registers at a time: with both sides' loads in
+    // flight the prologue ran out of registers, and each spill store waited
+    // for its load, a chain of memory round trips per tile.
+    LoraRegs<FM, FN> R0;
+    if (fast && ns > 0) lora_load<MODE, WN, FM, FN>(p, *L[0], 0, arow, n0, wn, l32, g, R0);
     load_first(hb0, 0);
     load_second(hb1, 0);
     load_first(hb2, 1);  // the second half of tile 1 is requested by tile 0
     if (fast) {
       if (ns > 0) lora_apply<FM, FN>(*L[0], 0, g, lo[0], hi[0], acc, R0);
-      if (ns > 1) lora_apply<FM, FN>(*L[1], 0, g, lo[1], hi[1], acc, R1);
+      __builtin_amdgcn_sched_barrier(0);
+      if (ns > 1) {
+        lora_load<MODE, WN, FM, FN>(p, *L[1], 0, arow, n0, wn, l32, g, R0);
+        lora_apply<FM, FN>(*L[1], 0, g, lo[1], hi[1], acc, R0);
+      }
       for (int k = 0; k < ns; ++k)
         for (int t = 1; t < (L[k]->r + 15) / 16; ++t) {
           lora_load<MODE, WN, FM, FN>(p, *L[k], t, arow, n0, wn, l32, g, R0);
@@ -703,7 +718,7 @@ __global__ __launch_bounds__(256) void dequant_rows_kernel(Nf4Dev w0, Nf4Dev w1,
                                                            const float* __restrict__ codebook0,
                                                            const float* __restrict__ codebook1, uint32_t cpr,
                                                            uint32_t nchunks, const uint16_t* __restrict__ colw,
-                                                           uint16_t* __restrict__ out) {
+                                                           int64_t ldo, uint16_t* __restrict__ out) {
   __shared__ float cb[32];  // tables of w0, w1
   if (threadIdx.x < 32) cb[threadIdx.x] = threadIdx.x < 16 ? codebook0[threadIdx.x] : codebook1[threadIdx.x & 15];
   __syncthreads();
@@ -739,8 +754,56 @@ __global__ __launch_bounds__(256) void dequant_rows_kernel(Nf4Dev w0, Nf4Dev w1,
         o = deq8(c, a, t);
       }
     }
-    *reinterpret_cast<u32x4*>(out + (int64_t)R * K + k0) = o;
+    *reinterpret_cast<u32x4*>(out + (int64_t)R * ldo + k0) = o;
   }
+}
+
+// LoRA extension columns of the expanded SwiGLU pair rows: one thread per
+// 8-column chunk of a row's ext columns.
+__global__ __launch_bounds__(256) void lora_ext_cols_kernel(const uint16_t* __restrict__ Bg, int rg,
+                                                            const uint16_t* __restrict__ Bu, int ru, int64_t N,
+                                                            int64_t rows_out, int64_t K, int64_t ldo, int64_t ext,
+                                                            uint16_t* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t cpr = ext / 8;
+  if (i >= rows_out * cpr) return;
+  const int64_t R = i / cpr;
+  const int q = (int)(i - R * cpr);
+  const int64_t within = R & 255;
+  const bool up = within >= 128;
+  const int64_t src = (R >> 8) * 128 + (within & 127);
+  uint32_t h[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int j = 8 * q + e;
+    uint32_t v = 0u;
+    if (src < N) {
+      if (!up && j < rg) v = Bg[src * rg + j];
+      if (up && j >= rg && j < rg + ru) v = Bu[src * ru + (j - rg)];
+    }
+    h[e] = v;
+  }
+  *reinterpret_cast<u32x4*>(out + R * ldo + K + 8 * q) =
+      u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+}
+
+// [s_g XA_g | s_u XA_u | 0] rounded to bf16, one thread per 8-column chunk.
+__global__ __launch_bounds__(256) void lora_ext_act_kernel(const float* __restrict__ Vg, int rg, float sg,
+                                                           const float* __restrict__ Vu, int ru, float su, int64_t M,
+                                                           int64_t ext, uint16_t* __restrict__ act) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t cpr = ext / 8;
+  if (i >= M * cpr) return;
+  const int64_t m = i / cpr;
+  const int q = (int)(i - m * cpr);
+  float y[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int j = 8 * q + e;
+    y[e] = j < rg ? sg * Vg[m * rg + j] : (j < rg + ru ? su * Vu[m * ru + (j - rg)] : 0.0f);
+  }
+  *reinterpret_cast<u32x4*>(act + m * ext + 8 * q) =
+      u32x4{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]), pack_bf16x2(y[4], y[5]), pack_bf16x2(y[6], y[7])};
 }
 
 // ------------------------------------------------------------------------
@@ -804,6 +867,9 @@ static hipError_t run_bgemm(GemmArgs a, hipStream_t st) {
   a.tiles_n = (a.Nout + BNO - 1) / BNO;
   const int64_t n = a.tiles_m * a.tiles_n;
   if (n == 0) return hipSuccess;
+  // the SwiGLU forward has no register-path LoRA term: its ranks must come as
+  // act1 reduction columns
+  if (MODE == MODE_FWD_SWIGLU && (a.l0.V || a.l1.V) && (a.Kred1 <= 0 || !a.act1)) return hipErrorInvalidValue;
   // reduction splits (plain forward only): fp32 partials [splits][M][Nout]
   unsigned splits = 1;
   if (MODE == MODE_FWD && a.ktiles_per_split > 0 && a.partial) {
@@ -869,13 +935,33 @@ hipError_t launch_had_finish(const float* part, int tiles, int64_t M, int r, flo
 }
 
 hipError_t launch_dequant_rows(const Nf4Dev& w0, const Nf4Dev* w1, const float* codebook0, const float* codebook1,
-                               int64_t rows_out, uint16_t* out, hipStream_t st, const uint16_t* colw) {
+                               int64_t rows_out, uint16_t* out, hipStream_t st, const uint16_t* colw, int64_t ldo) {
   const int64_t cpr = w0.K / 8, chunks = rows_out * cpr;
   if (chunks == 0) return hipSuccess;
   if (chunks >= ((int64_t)1 << 32) - 1024) return hipErrorInvalidValue;  // 32-bit chunk index
+  if (ldo == 0) ldo = w0.K;
+  if (ldo < w0.K || ldo % 8 != 0) return hipErrorInvalidValue;
   dequant_rows_kernel<<<dim3((unsigned)((chunks + 1023) / 1024)), 256, 0, st>>>(
       w0, w1 ? *w1 : w0, w1 ? 1 : 0, codebook0, codebook1 ? codebook1 : codebook0, (uint32_t)cpr, (uint32_t)chunks,
-      colw, out);
+      colw, ldo, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_lora_ext_cols(const uint16_t* Bg, int rg, const uint16_t* Bu, int ru, int64_t N, int64_t rows_out,
+                                int64_t K, int64_t ldo, int64_t ext, uint16_t* out, hipStream_t st) {
+  if (ext % 8 != 0 || K % 8 != 0 || ldo % 8 != 0 || ldo < K + ext || rg + ru > ext) return hipErrorInvalidValue;
+  const int64_t n = rows_out * (ext / 8);
+  if (n == 0) return hipSuccess;
+  lora_ext_cols_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(Bg, rg, Bu, ru, N, rows_out, K, ldo, ext, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_lora_ext_act(const float* Vg, int rg, float sg, const float* Vu, int ru, float su, int64_t M,
+                               int64_t ext, uint16_t* act, hipStream_t st) {
+  if (ext % 8 != 0 || rg + ru > ext) return hipErrorInvalidValue;
+  const int64_t n = M * (ext / 8);
+  if (n == 0) return hipSuccess;
+  lora_ext_act_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(Vg, rg, sg, Vu, ru, su, M, ext, act);
   return hipGetLastError();
 }
 

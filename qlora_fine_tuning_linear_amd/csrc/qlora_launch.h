@@ -65,6 +65,11 @@ struct GemmArgs {
   // instead of bf16 to out0
   int64_t lda;
   int32_t out_f32;
+  // bgemm_kernel: row stride of act1 in elements when it differs from lda
+  // (0: lda).  In the SwiGLU forward a nonzero Kred1 means that the LoRA
+  // terms come as these extra reduction columns (act1 against columns
+  // Kred0 .. Kred0 + Kred1 of the weight rows) instead of l0 / l1.
+  int64_t lda1;
   // bgemm_kernel, SwiGLU backward only: the down layer's rank-r product
   // T^T H (T = l0.V fp32 [M, r], r = l0.r <= 32; H = silu(in0) in1 rounded
   // to bf16) as per-token-tile fp32 partials dad_part[tiles_m][Nout][r]
@@ -197,7 +202,16 @@ hipError_t launch_ce_loss(const float* token_loss, int64_t T, const int32_t* n_v
 //   trans: out[k, col0 + n] = deq(W)[n, k] (row stride ldo).
 hipError_t launch_dequant_rows(const Nf4Dev& w0, const Nf4Dev* w1, const float* codebook0, const float* codebook1,
                                int64_t rows_out, uint16_t* out, hipStream_t st,
-                               const uint16_t* colw = nullptr);
+                               const uint16_t* colw = nullptr, int64_t ldo = 0);
+// The LoRA extension of a SwiGLU pair's expanded rows (row stride ldo):
+// out[R, K + j] for j < ext = B_g[src(R), j] (j < rg) on gate rows,
+// B_u[src(R), j - rg] (rg <= j < rg + ru) on up rows, 0 elsewhere and past N.
+hipError_t launch_lora_ext_cols(const uint16_t* Bg, int rg, const uint16_t* Bu, int ru, int64_t N, int64_t rows_out,
+                                int64_t K, int64_t ldo, int64_t ext, uint16_t* out, hipStream_t st);
+// act [M, ext] bf16: bf16(sg Vg[m, j]) for j < rg, bf16(su Vu[m, j - rg]) for
+// rg <= j < rg + ru, 0 past that (V fp32 [M, r]).
+hipError_t launch_lora_ext_act(const float* Vg, int rg, float sg, const float* Vu, int ru, float su, int64_t M,
+                               int64_t ext, uint16_t* act, hipStream_t st);
 hipError_t launch_dequant_trans(const Nf4Dev& w, const float* codebook, uint16_t* out, int64_t ldo, int64_t col0,
                                 hipStream_t st);
 hipError_t launch_splitk_finish(const float* part, int splits, int64_t M, int64_t Nout, uint16_t* out,

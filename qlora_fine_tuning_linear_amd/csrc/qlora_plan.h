@@ -239,8 +239,15 @@ inline LinearWs linear_ws(int64_t M, int64_t N, int64_t K, int r) {
 // ranks up to 32.
 inline bool fuse_dad(int rd) { return rd >= 1 && rd <= 32; }
 
+// The gate/up GEMM on the bf16 path takes its LoRA terms as extra reduction
+// columns: [s_g XA_g | s_u XA_u] (bf16) against [B_g | 0] on the gate rows and
+// [0 | B_u] on the up rows of the expanded weight, zero-padded to whole
+// 64-column reduction tiles.
+inline int64_t lora_ext_cols(int rg, int ru) { return 64 * cdiv(rg + ru, 64); }
+
 struct MlpWs {
   size_t fwd_H, fwd_down;                            // H bf16 [M, I], down-proj partials
+  size_t fwd_ext;                                    // [s_g XA_g | s_u XA_u] bf16 [M, ext] (bgemm)
   size_t bwd_Td, bwd_dG, bwd_dU, bwd_Tg, bwd_Tu, bwd_BT, bwd_down, bwd_grad;
   size_t fwd_had;                                    // H A_d^T column-tile partials (bgemm, r_d <= 32)
   size_t bwd_pair;                                   // single-pass LoRA product partials (ranks <= 16)
@@ -258,12 +265,14 @@ inline MlpWs mlp_ws(int64_t M, int64_t D, int64_t I, int rg, int ru, int rd) {
   size_t d2 = s2 > 1 ? align256((size_t)s2 * M * rd * 4) : 0;
   w.fwd_down = d1 > d2 ? d1 : d2;
   if (use_bgemm(M)) {
-    const size_t gu = (size_t)pair_rows(I) * D * 2, dn = (size_t)D * I * 2;
+    const int64_t ext = lora_ext_cols(rg, ru);
+    const size_t gu = (size_t)pair_rows(I) * (D + ext) * 2, dn = (size_t)D * I * 2;
     w.fwd_wbuf = align256(gu > dn ? gu : dn);
+    w.fwd_ext = align256((size_t)M * ext * 2);
     w.bwd_wbuf = align256((size_t)2 * I * D * 2);
   }
   if (use_bgemm(M) && rd <= 32) w.fwd_had = align256((size_t)cdiv(I, 128) * M * rd * 4);
-  w.fwd_total = w.fwd_H + w.fwd_down + w.fwd_had + w.fwd_wbuf;
+  w.fwd_total = w.fwd_H + w.fwd_down + w.fwd_had + w.fwd_ext + w.fwd_wbuf;
 
   w.bwd_Td = align256((size_t)M * rd * 4);
   w.bwd_dG = align256((size_t)M * I * 2);
