@@ -826,6 +826,8 @@ int qlora_mlp_bwd(const qlora_mlp* P, const void* dY, const void* X, const qlora
   b += w.bwd_grad;
   float* pair_part = reinterpret_cast<float*>(b);
   b += w.bwd_pair;
+  uint16_t* tdt = reinterpret_cast<uint16_t*>(b);
+  b += w.bwd_tdt;
   uint16_t* wbuf = w.bwd_wbuf ? reinterpret_cast<uint16_t*>(b) : nullptr;
   const bool pair = qplan::use_lora_pair(rg, ru, rd);
 
@@ -872,8 +874,15 @@ int qlora_mlp_bwd(const qlora_mlp* P, const void* dY, const void* X, const qlora
       a.wb = wbuf;
       a.ldw = D;
       a.wrows = I;
-      // dA_d = s_d Td^T H from the epilogue's own G, U (per-token-tile partials)
-      if (qplan::fuse_dad(rd)) a.dad_part = grad_part;
+      // dA_d = s_d Td^T H from the epilogue's own G, U (per-token-tile
+      // partials), with Td^T in bf16 so that a lane's operand is one load
+      if (qplan::fuse_dad(rd)) {
+        const int64_t ld = 8 * qplan::cdiv(M, 8);
+        QHIP(launch_t_bf16_trans(Td, M, rd, ld, tdt, st));
+        a.dad_part = grad_part;
+        a.dad_tt = tdt;
+        a.dad_tt_ld = ld;
+      }
       QHIP(traced_gemm_b(MODE_BWD_SWIGLU, a, st));
       if (qplan::fuse_dad(rd))
         QHIP(launch_grad_finish(grad_part, (int)qplan::cdiv(M, 256), I, rd, sd, 1, u16m(G->dA_d), st));

@@ -155,14 +155,39 @@ __device__ __forceinline__ void bg_epilogue(const GemmArgs& p, f32x16 (&acc)[BG_
       }
     flush(lg, p.out2);
   } else if constexpr (MODE == MODE_BWD_SWIGLU) {
-    // dH (fp32) one token frag (32 rows x 64 columns, 8 KB) at a time; the
-    // G / U chunks of frag i+1 are loaded while frag i is finished
+    // dH (fp32) one token frag (32 rows x 64 columns, 8 KB) at a time through
+    // the wave's LDS region.  G / U stream in as 16 row chunks (8 rows x 64
+    // columns: one 16-byte piece per lane) kept LA = 6 chunks ahead of the chunk
+    // being finished; buffer loads read rows past M as zeros and buffer
+    // stores drop them (and columns past Nout), so that no memory operation
+    // sits under a branch and every wait covers only what it must.
     const int64_t cw = n0 + wn * 64;
     const int c8 = lane & 7;  // this lane's 8-column group
     const int64_t ncol = cw + 8 * c8;
     const bool col_ok = ncol < p.Nout;
     const int64_t nc = col_ok ? ncol : p.Nout - 8;
-    u32x4 gg[2][4], uu[2][4];
+    // resources over the tile's rows of G, U, dG, dU (at most 256 rows:
+    // below 2 GiB for every accepted Nout)
+    const int64_t tbytes = ((p.M - m0) < 256 ? (p.M - m0) : 256) * p.Nout * 2;
+    auto trs = [&](const uint16_t* base) {
+      return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base) + m0 * p.Nout, (short)0, (int)tbytes,
+                                               0x00020000);
+    };
+    const __amdgpu_buffer_rsrc_t rsg = trs(p.in0), rsu = trs(p.in1), rsdg = trs(p.out0), rsdu = trs(p.out1);
+    // byte offset of this lane's piece of chunk 0; chunk (i, it) adds the
+    // wave-uniform (32 i + 8 it) rows
+    const uint32_t lo = (uint32_t)(((int64_t)(wm * 128 + (lane >> 3)) * p.Nout + nc) * 2);
+    const uint32_t lso = col_ok ? lo : 0x80000000u;
+    auto chunk_so = [&](int c) { return (uint32_t)((32 * (c >> 2) + 8 * (c & 3)) * p.Nout * 2); };
+    constexpr int NCH = FM * 4, LA = 6, SL = LA + 1;
+    u32x4 gq[SL], uq[SL];
+    // the whole offset goes in the lane offset: the range check covers the
+    // lane offset only, not the scalar one
+    auto ld = [&](int c) {
+      const uint32_t o = lo + chunk_so(c);
+      gq[c % SL] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsg, o, 0, 0));
+      uq[c % SL] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsu, o, 0, 0));
+    };
     // optional: the down layer's T^T H over this wave's 128 tokens x 64
     // columns, one 32-token frag at a time, with H = silu(G) U rounded to
     // bf16 and stored transposed after lf (T = l0.V, rank l0.r <= 32)
@@ -170,39 +195,30 @@ __device__ __forceinline__ void bg_epilogue(const GemmArgs& p, f32x16 (&acc)[BG_
     const int dr = p.l0.r;
     uint16_t* ht = reg + 4096;
     const int l16 = lane & 15, kq = lane >> 4;
-    auto load = [&](int i, int b) {
-#pragma unroll
-      for (int it = 0; it < 4; ++it) {
-        int64_t m = mw + i * 32 + it * 8 + (lane >> 3);
-        if (m >= p.M) m = p.M - 1;
-        gg[b][it] = *reinterpret_cast<const u32x4*>(p.in0 + m * p.Nout + nc);
-        uu[b][it] = *reinterpret_cast<const u32x4*>(p.in1 + m * p.Nout + nc);
-      }
-    };
-    // T operand values of frag i, [jf][e] = T[token 8 kq + e][j = 16 jf + l16]
-    // (zero past M and past the rank), requested at the start of the frag,
-    // before the next frag's G / U chunks, so that they arrive during the
-    // frag's dH work and their wait does not cover the next frag's loads
-    float tv[2][8];
+    // T operand of frag i: ta[jf] = bf16 T[token 8 kq + e][j = 16 jf + l16]
+    // for e < 8, one 16-byte load from the transposed copy (tokens past M
+    // read as zeros: out-of-range offset; ranks past r masked at use)
+    u32x4 ta[2];
+    const __amdgpu_buffer_rsrc_t rst = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(p.dad_tt), (short)0, (int)(with_dad ? dr * p.dad_tt_ld * 2 : 0), 0x00020000);
     auto load_t = [&](int i) {
+      const int64_t m = mw + i * 32 + 8 * kq;
+      // bit 31 set past M: beyond the resource, reads zeros (arithmetic, not a
+      // select, so that the loads stay out of branches)
+      const uint32_t past = (uint32_t)(m >= p.M) << 31;
 #pragma unroll
       for (int jf = 0; jf < 2; ++jf) {
         const int j = 16 * jf + l16;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int64_t m = mw + i * 32 + 8 * kq + e;
-          const float t = p.l0.V[(m < p.M ? m : p.M - 1) * dr + (j < dr ? j : dr - 1)];
-          tv[jf][e] = (j < dr && m < p.M) ? t : 0.0f;
-        }
+        const uint32_t o = (uint32_t)(((j < dr ? j : dr - 1) * p.dad_tt_ld + (m < p.M ? m : 0)) * 2) | past;
+        ta[jf] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rst, o, 0, 0));
       }
     };
     float* lf = reinterpret_cast<float*>(reg);
-    load(0, 0);
+#pragma unroll
+    for (int c = 0; c < LA; ++c) ld(c);
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       if constexpr (DAD) load_t(i);
-      if (i + 1 < FM) load(i + 1, (i + 1) & 1);
-      const int b = i & 1;
 #pragma unroll
       for (int f = 0; f < 2; ++f)
 #pragma unroll
@@ -213,6 +229,9 @@ __device__ __forceinline__ void bg_epilogue(const GemmArgs& p, f32x16 (&acc)[BG_
         }
 #pragma unroll
       for (int it = 0; it < 4; ++it) {
+        const int ch = 4 * i + it;
+        if (ch + LA < NCH) ld(ch + LA);
+        const u32x4 gv = gq[ch % SL], uv = uq[ch % SL];
         const int row = it * 8 + (lane >> 3);
         const int c0 = 2 * c8;
         const f32x4 d0 = *reinterpret_cast<const f32x4*>(lf + row * 64 + ((c0 ^ (row & 15)) * 4));
@@ -224,8 +243,8 @@ __device__ __forceinline__ void bg_epilogue(const GemmArgs& p, f32x16 (&acc)[BG_
           float dG2[2], dU2[2];
 #pragma unroll
           for (int e = 0; e < 2; ++e) {
-            const float G = e ? bf16_hi(gg[b][it][d]) : bf16_lo(gg[b][it][d]);
-            const float U = e ? bf16_hi(uu[b][it][d]) : bf16_lo(uu[b][it][d]);
+            const float G = e ? bf16_hi(gv[d]) : bf16_lo(gv[d]);
+            const float U = e ? bf16_hi(uv[d]) : bf16_lo(uv[d]);
             const float sg = sigmoid_fast(G);
             const float h = dH[2 * d + e];
             dU2[e] = h * G * sg;
@@ -236,28 +255,26 @@ __device__ __forceinline__ void bg_epilogue(const GemmArgs& p, f32x16 (&acc)[BG_
           og[d] = pack_bf16x2(dG2[0], dG2[1]);
           ou[d] = pack_bf16x2(dU2[0], dU2[1]);
         }
-        const int64_t m = mw + i * 32 + row;
-        if (m < p.M && col_ok) {
-          *reinterpret_cast<u32x4*>(p.out0 + m * p.Nout + ncol) = og;
-          *reinterpret_cast<u32x4*>(p.out1 + m * p.Nout + ncol) = ou;
-        }
+        const uint32_t so = lso + chunk_so(ch);
+        __builtin_amdgcn_raw_buffer_store_b128(og, rsdg, so, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(ou, rsdu, so, 0, 0);
       }
       if (with_dad) {
         // A operand: T^T, lane (j, kq) holds T[token 8 kq + e][j] (zero past
         // M and past the rank); B operand: H^T rows, lane (column, kq) holds
         // H[token 8 kq + e][column]; result lane (column, q): j = 4 q + v
-        u32x4 ta[2];
+        u32x4 tb[2];
 #pragma unroll
         for (int jf = 0; jf < 2; ++jf) {
-          const float* t8 = tv[jf];
-          ta[jf] = u32x4{pack_bf16x2(t8[0], t8[1]), pack_bf16x2(t8[2], t8[3]), pack_bf16x2(t8[4], t8[5]),
-                         pack_bf16x2(t8[6], t8[7])};
+          const bool jok = 16 * jf + l16 < dr;
+#pragma unroll
+          for (int d = 0; d < 4; ++d) tb[jf][d] = jok ? ta[jf][d] : 0u;
         }
 #pragma unroll
         for (int cf = 0; cf < 4; ++cf) {
           const u32x4 hop = *reinterpret_cast<const u32x4*>(ht + bg_ht_index(16 * cf + l16, 8 * kq));
-          dad[0][cf] = bg_mfma16(ta[0], hop, dad[0][cf]);
-          if (dr > 16) dad[1][cf] = bg_mfma16(ta[1], hop, dad[1][cf]);
+          dad[0][cf] = bg_mfma16(tb[0], hop, dad[0][cf]);
+          if (dr > 16) dad[1][cf] = bg_mfma16(tb[1], hop, dad[1][cf]);
         }
       }
     }
@@ -661,7 +678,7 @@ __global__ __launch_bounds__(512) void bgemm_kernel(GemmArgs p) {
 #pragma unroll
             for (int v = 0; v < 4; ++v) xr[((jf * 4 + cf) * 4 + v) * 64 + lane] = dad[jf][cf][v];
       }
-      __syncthreads();
+      lds_barrier();  // an LDS exchange: the dG / dU stores need not land first
       if (wm == 0) {
         const int dr = p.l0.r;
         const int l16 = lane & 15, kq = lane >> 4;
@@ -685,7 +702,7 @@ __global__ __launch_bounds__(512) void bgemm_kernel(GemmArgs p) {
       // each wave's 128 tokens x 32 columns of H A^T into its region, then the
       // four waves of a token half are added in column order
       bg_had_wave<MODE>(p, acc, n0, wn, lane, reinterpret_cast<float*>(buf + (wave & 1) * 8192));
-      __syncthreads();
+      lds_barrier();  // an LDS exchange: the G / U / H stores need not land first
       const int r = p.had_r;
 #pragma unroll
       for (int k = 0; k < 16; ++k) {
@@ -806,6 +823,22 @@ __global__ __launch_bounds__(256) void lora_ext_act_kernel(const float* __restri
       u32x4{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]), pack_bf16x2(y[4], y[5]), pack_bf16x2(y[6], y[7])};
 }
 
+// T^T in bf16 for the dH epilogue's dA_d operand: out[j * ld + m] =
+// bf16(T[m, j]), zero for M <= m < ld; one thread per 8 tokens of a rank.
+__global__ __launch_bounds__(256) void t_bf16_trans_kernel(const float* __restrict__ T, int64_t M, int r,
+                                                           int64_t ld, uint16_t* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t per = ld / 8;
+  if (i >= (int64_t)r * per) return;
+  const int j = (int)(i / per);
+  const int64_t m0 = (i - (int64_t)j * per) * 8;
+  float v[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = m0 + e < M ? T[(m0 + e) * r + j] : 0.0f;
+  *reinterpret_cast<u32x4*>(out + (int64_t)j * ld + m0) =
+      u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
+}
+
 // ------------------------------------------------------------------------
 // Transposed weight expansion: out[k, col0 + n] = deq(W)[n, k].  Workgroup
 // -> 64 weight rows x 256 reduction columns.  Lane n of each wave expands
@@ -870,6 +903,9 @@ static hipError_t run_bgemm(GemmArgs a, hipStream_t st) {
   // the SwiGLU forward has no register-path LoRA term: its ranks must come as
   // act1 reduction columns
   if (MODE == MODE_FWD_SWIGLU && (a.l0.V || a.l1.V) && (a.Kred1 <= 0 || !a.act1)) return hipErrorInvalidValue;
+  // the dA_d product reads T through its transposed bf16 copy
+  if (MODE == MODE_BWD_SWIGLU && a.dad_part && (!a.dad_tt || a.dad_tt_ld < a.M || a.dad_tt_ld % 8 != 0))
+    return hipErrorInvalidValue;
   // reduction splits (plain forward only): fp32 partials [splits][M][Nout]
   unsigned splits = 1;
   if (MODE == MODE_FWD && a.ktiles_per_split > 0 && a.partial) {
@@ -944,6 +980,14 @@ hipError_t launch_dequant_rows(const Nf4Dev& w0, const Nf4Dev* w1, const float* 
   dequant_rows_kernel<<<dim3((unsigned)((chunks + 1023) / 1024)), 256, 0, st>>>(
       w0, w1 ? *w1 : w0, w1 ? 1 : 0, codebook0, codebook1 ? codebook1 : codebook0, (uint32_t)cpr, (uint32_t)chunks,
       colw, ldo, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_t_bf16_trans(const float* T, int64_t M, int r, int64_t ld, uint16_t* out, hipStream_t st) {
+  if (ld < M || ld % 8 != 0 || r < 1) return hipErrorInvalidValue;
+  const int64_t n = (int64_t)r * (ld / 8);
+  if (n == 0) return hipSuccess;
+  t_bf16_trans_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(T, M, r, ld, out);
   return hipGetLastError();
 }
 

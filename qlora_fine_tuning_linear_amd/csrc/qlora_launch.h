@@ -75,6 +75,10 @@ struct GemmArgs {
   // to bf16) as per-token-tile fp32 partials dad_part[tiles_m][Nout][r]
   // (null: not computed)
   float* dad_part;
+  // with dad_part: T as bf16 transposed, dad_tt[j * dad_tt_ld + m] (rows
+  // j < r, tokens m < dad_tt_ld, a multiple of 8; zero past M)
+  const uint16_t* dad_tt;
+  int64_t dad_tt_ld;
   // bgemm_kernel, SwiGLU forward only: every token row m of the product
   // (LoRA term included) is multiplied by row_scale[m] before the epilogue
   // (null: not scaled)
@@ -183,6 +187,9 @@ hipError_t launch_qgemm(int mode, const GemmArgs& a, const qplan::GemmPlan& pl, 
 hipError_t launch_bgemm(int mode, const GemmArgs& a, hipStream_t st);
 // Sum of the H A^T partials of launch_bgemm (MODE_FWD_SWIGLU) in tile order.
 hipError_t launch_had_finish(const float* part, int tiles, int64_t M, int r, float* out, hipStream_t st);
+// out [r][ld] bf16 = T^T for T fp32 [M, r] (ld >= M, a multiple of 8; zero for
+// M <= m < ld)
+hipError_t launch_t_bf16_trans(const float* T, int64_t M, int r, int64_t ld, uint16_t* out, hipStream_t st);
 // out = bf16(s * sum_z part[z]) over S fp32 partials [S][P][r], written as
 // [P, r] (out_rp = 0) or [r, P] (out_rp = 1)
 hipError_t launch_grad_finish(const float* part, int S, int64_t P, int r, float s, int out_rp, uint16_t* out,

@@ -251,6 +251,7 @@ struct MlpWs {
   size_t bwd_Td, bwd_dG, bwd_dU, bwd_Tg, bwd_Tu, bwd_BT, bwd_down, bwd_grad;
   size_t fwd_had;                                    // H A_d^T column-tile partials (bgemm, r_d <= 32)
   size_t bwd_pair;                                   // single-pass LoRA product partials (ranks <= 16)
+  size_t bwd_tdt;                                    // T_d^T bf16 for the dH epilogue's dA_d (bgemm)
   size_t fwd_wbuf, bwd_wbuf;                         // bf16 weight copies (bgemm only), at the end
   size_t fwd_total, bwd_total, total;
 };
@@ -294,10 +295,12 @@ inline MlpWs mlp_ws(int64_t M, int64_t D, int64_t I, int rg, int ru, int rd) {
     size_t b = align256((size_t)ms * Ps[i] * Rs[i] * 4);
     if (b > g) g = b;
   }
-  // the dH GEMM's per-token-tile partials of dA_d (bgemm, r_d <= 32)
+  // the dH GEMM's per-token-tile partials of dA_d (bgemm, r_d <= 32), and
+  // its T_d operand as bf16 [r_d][M rounded up to 8]
   if (use_bgemm(M) && fuse_dad(rd)) {
     const size_t b = align256((size_t)cdiv(M, 256) * I * rd * 4);
     if (b > g) g = b;
+    w.bwd_tdt = align256((size_t)rd * (size_t)(8 * cdiv(M, 8)) * 2);
   }
   w.bwd_grad = g;
   if (use_lora_pair(rg, ru, rd)) {
@@ -311,7 +314,7 @@ inline MlpWs mlp_ws(int64_t M, int64_t D, int64_t I, int rg, int ru, int rd) {
     w.bwd_pair = align256((a > b ? a : b) * 4);
   }
   w.bwd_total = w.bwd_Td + w.bwd_dG + w.bwd_dU + w.bwd_Tg + w.bwd_Tu + w.bwd_BT + w.bwd_down + w.bwd_grad +
-                w.bwd_pair + w.bwd_wbuf;
+                w.bwd_pair + w.bwd_tdt + w.bwd_wbuf;
   w.total = w.fwd_total > w.bwd_total ? w.fwd_total : w.bwd_total;
   if (w.total == 0) w.total = 256;
   return w;
