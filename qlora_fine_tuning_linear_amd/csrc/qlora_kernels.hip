@@ -1425,7 +1425,7 @@ hipError_t launch_transpose_rn(const uint16_t* B, int64_t N, int r, uint16_t* BT
 }
 
 void plan_lora_pair(PairArgs& a, int64_t M, int64_t P, int r) {
-  const int msplits = qplan::plan_grad_msplits(M, P, r);
+  const int msplits = qplan::plan_pair_msplits(M, P, r);
   const int64_t mps = (((M + msplits - 1) / msplits) + 31) / 32 * 32;
   a.M = M;
   a.P = P;

@@ -176,8 +176,16 @@ inline int64_t pair_rows(int64_t I) { return 256 * cdiv(I, 128); }
 inline bool use_lora_pair(int rg, int ru, int rd) {
   return rg >= 1 && rg <= 16 && ru >= 1 && ru <= 16 && rd >= 1 && rd <= 16;
 }
+// Token splits of the single-pass T + dB kernel: the gradient reduction's,
+// capped at about two workgroups per CU per job (fewer dB partials to write
+// and add).
+inline int plan_pair_msplits(int64_t M, int64_t P, int r) {
+  const int s = plan_grad_msplits(M, P, r);
+  const int64_t cap = cdiv(2 * kNumCUs, cdiv(P, 512));
+  return (int)(s < cap ? s : (cap < 1 ? 1 : cap));
+}
 inline size_t pair_part_floats(int64_t M, int64_t P, int r) {
-  const int msplits = plan_grad_msplits(M, P, r);
+  const int msplits = plan_pair_msplits(M, P, r);
   int64_t mps = (((M + msplits - 1) / msplits) + 31) / 32 * 32;
   if (mps <= 0) mps = 32;
   const int64_t S = cdiv(M, mps), nb = cdiv(P, 512);
