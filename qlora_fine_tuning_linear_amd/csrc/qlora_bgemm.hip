@@ -106,8 +106,11 @@ __device__ __forceinline__ int bg_ht_index(int c, int t) {
 
 // DAD: the SwiGLU backward also forms the dA_d partial (p.dad_part set)
 template <int MODE, bool DAD>
+// hp (SwiGLU forward): H of frag i at columns 8q + 4g .. + 3 as the two
+// bf16 words that are stored, kept for the H A^T product.
 __device__ __forceinline__ void bg_epilogue(const GemmArgs& p, f32x16 (&acc)[BG_FM][2], int64_t m0, int64_t n0,
-                                             int wm, int wn, int lane, uint16_t* reg, f32x4 (&dad)[2][4]) {
+                                             int wm, int wn, int lane, uint16_t* reg, f32x4 (&dad)[2][4],
+                                             u32x2 (&hp)[BG_FM][4]) {
   constexpr int FM = BG_FM;
   const int l32 = lane & 31, g = lane >> 5;
   const int64_t mw = m0 + wm * 128;  // first token of the wave
@@ -116,10 +119,12 @@ __device__ __forceinline__ void bg_epilogue(const GemmArgs& p, f32x16 (&acc)[BG_
     const int64_t cw = n0 + wn * 32;
     uint16_t* lg = reg;
     uint16_t* lu = reg + 128 * 32;
-    auto wr = [&](uint16_t* t, int i, int q, const float (&v)[4]) {
+    auto wrw = [&](uint16_t* t, int i, int q, u32x2 w) {
       const int row = i * 32 + l32;
-      *reinterpret_cast<u32x2*>(t + row * 32 + ((q ^ (row & 3)) * 8) + 4 * g) =
-          u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+      *reinterpret_cast<u32x2*>(t + row * 32 + ((q ^ (row & 3)) * 8) + 4 * g) = w;
+    };
+    auto wr = [&](uint16_t* t, int i, int q, const float (&v)[4]) {
+      wrw(t, i, q, u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])});
     };
     auto flush = [&](const uint16_t* t, uint16_t* out) {
 #pragma unroll
@@ -151,7 +156,8 @@ __device__ __forceinline__ void bg_epilogue(const GemmArgs& p, f32x16 (&acc)[BG_
           const float Gv = acc[i][0][4 * q + e], Uv = acc[i][1][4 * q + e];
           H[e] = Gv * sigmoid_fast(Gv) * Uv;
         }
-        wr(lg, i, q, H);
+        hp[i][q] = u32x2{pack_bf16x2(H[0], H[1]), pack_bf16x2(H[2], H[3])};
+        wrw(lg, i, q, hp[i][q]);
       }
     flush(lg, p.out2);
   } else if constexpr (MODE == MODE_BWD_SWIGLU) {
@@ -303,14 +309,14 @@ __device__ __forceinline__ void bg_epilogue(const GemmArgs& p, f32x16 (&acc)[BG_
 }
 
 // SwiGLU forward, optional: the wave's share of H A^T (the down layer's
-// rank-r product, A [r, Nout] bf16) straight from the accumulators.  Lane
-// (token l32, g) holds H at columns cw + 8q + 4g + e (q, e < 4); taken as the
-// A operand of two 32x32x16 MFMAs, step s covers q = 2s, 2s + 1, and the B
-// operand reads A at the same columns, so no transpose is needed.  H is
-// rounded to bf16 exactly as the stored H.  The 128 x 32 fp32 result goes to
-// the wave's LDS region [token][j].
+// rank-r product, A [r, Nout] bf16) from the bf16 H words the epilogue
+// stored (hp).  Lane (token l32, g) holds H at columns cw + 8q + 4g + e
+// (q, e < 4); taken as the A operand of two 32x32x16 MFMAs, step s covers
+// q = 2s, 2s + 1, and the B operand reads A at the same columns, so no
+// transpose is needed.  The 128 x 32 fp32 result goes to the wave's LDS
+// region [token][j].
 template <int MODE>
-__device__ __forceinline__ void bg_had_wave(const GemmArgs& p, f32x16 (&acc)[BG_FM][2], int64_t n0, int wn,
+__device__ __forceinline__ void bg_had_wave(const GemmArgs& p, const u32x2 (&hp)[BG_FM][4], int64_t n0, int wn,
                                             int lane, float* reg) {
   const int l32 = lane & 31, g = lane >> 5;
   const int64_t cw = n0 + wn * 32;
@@ -324,29 +330,19 @@ __device__ __forceinline__ void bg_had_wave(const GemmArgs& p, f32x16 (&acc)[BG_
     const u32x2 hi = (jok && c1 < p.Nout) ? *reinterpret_cast<const u32x2*>(arow + c1) : u32x2{0u, 0u};
     bop[s] = u32x4{lo[0], lo[1], hi[0], hi[1]};
   }
+  // ranks past 16 hold zeros when r <= 16: not written (nor read back)
+  const bool wj = l32 < (p.had_r <= 16 ? 16 : 32);
 #pragma unroll
   for (int i = 0; i < BG_FM; ++i) {
     f32x16 h{};
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      uint32_t w[4];
-#pragma unroll
-      for (int hq = 0; hq < 2; ++hq) {
-        const int q = 2 * s + hq;
-        float H[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float Gv = acc[i][0][4 * q + e], Uv = acc[i][1][4 * q + e];
-          H[e] = Gv * sigmoid_fast(Gv) * Uv;
-        }
-        w[2 * hq] = pack_bf16x2(H[0], H[1]);
-        w[2 * hq + 1] = pack_bf16x2(H[2], H[3]);
-      }
-      h = mfma32(u32x4{w[0], w[1], w[2], w[3]}, bop[s], h);
-    }
+    for (int s = 0; s < 2; ++s)
+      h = mfma32(u32x4{hp[i][2 * s][0], hp[i][2 * s][1], hp[i][2 * s + 1][0], hp[i][2 * s + 1][1]}, bop[s], h);
     // h[v] = C[token 8(v/4) + 4g + v%4 of frag i][j = l32]
+    if (wj) {
 #pragma unroll
-    for (int v = 0; v < 16; ++v) reg[(i * 32 + 8 * (v >> 2) + 4 * g + (v & 3)) * 32 + l32] = h[v];
+      for (int v = 0; v < 16; ++v) reg[(i * 32 + 8 * (v >> 2) + 4 * g + (v & 3)) * 32 + l32] = h[v];
+    }
   }
 }
 
@@ -663,7 +659,8 @@ __global__ __launch_bounds__(512) void bgemm_kernel(GemmArgs p) {
   for (int jf = 0; jf < 2; ++jf)
 #pragma unroll
     for (int cf = 0; cf < 4; ++cf) dad[jf][cf] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  bg_epilogue<MODE, DAD>(p, acc, m0, n0, wm, wn, lane, buf + (wave & 1) * 8192, dad);
+  u32x2 hp[FM][4];
+  bg_epilogue<MODE, DAD>(p, acc, m0, n0, wm, wn, lane, buf + (wave & 1) * 8192, dad, hp);
   if constexpr (MODE == MODE_BWD_SWIGLU) {
     if (p.dad_part) {
       // the two token halves of each 64-column strip are added (waves 4..7
@@ -701,13 +698,10 @@ __global__ __launch_bounds__(512) void bgemm_kernel(GemmArgs p) {
     if (p.had_part) {
       // each wave's 128 tokens x 32 columns of H A^T into its region, then the
       // four waves of a token half are added in column order
-      bg_had_wave<MODE>(p, acc, n0, wn, lane, reinterpret_cast<float*>(buf + (wave & 1) * 8192));
+      bg_had_wave<MODE>(p, hp, n0, wn, lane, reinterpret_cast<float*>(buf + (wave & 1) * 8192));
       lds_barrier();  // an LDS exchange: the G / U / H stores need not land first
       const int r = p.had_r;
-#pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const int e = tid + 512 * k;  // [half][token][j], 2 x 128 x 32
-        const int hf = e >> 12, t = (e >> 5) & 127, j = e & 31;
+      auto sum_out = [&](int hf, int t, int j) {
         float sum = 0.0f;
 #pragma unroll
         for (int w4 = 0; w4 < 4; ++w4) {
@@ -717,6 +711,19 @@ __global__ __launch_bounds__(512) void bgemm_kernel(GemmArgs p) {
         }
         const int64_t m = m0 + hf * 128 + t;
         if (j < r && m < p.M) p.had_part[((int64_t)tn * p.M + m) * r + j] = sum;
+      };
+      if (r <= 16) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int e = tid + 512 * k;  // [half][token][j < 16], 2 x 128 x 16
+          sum_out(e >> 11, (e >> 4) & 127, e & 15);
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+          const int e = tid + 512 * k;  // [half][token][j], 2 x 128 x 32
+          sum_out(e >> 12, (e >> 5) & 127, e & 31);
+        }
       }
     }
   }
