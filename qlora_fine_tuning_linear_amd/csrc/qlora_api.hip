@@ -405,9 +405,14 @@ int qlora_linear_fwd(const qlora_linear* L, const void* X, int64_t M, void* Y, f
     // XA partials; the skinny GEMM sums them, writes XA and adds s XA B^T
     const int ds = qplan::plan_down_splits(M, K);
     const int dsu = qplan::down_splits_used(K, ds);
-    QHIP(launch_lora_down(u16(X), M, K, u16(L->A), L->r, nullptr, 0, XA_saved, nullptr, ds, down_part, st, false));
     const bool stream2 = qplan::use_skinny_fwd2(M, N, K, L->r);
     const qplan::SkinnyPlan sp = stream2 ? qplan::plan_skinny_fwd2(N, K) : qplan::plan_skinny_fwd(N, K);
+    // the streaming form's activation re-layout comes from the same pass
+    // over X when the rank allows (<= 16), else from its own launch
+    uint16_t* xt = stream2 ? reinterpret_cast<uint16_t*>(bytes(ws) + w.fwd_part + w.fwd_down) : nullptr;
+    const bool xt_fused = stream2 && L->r <= 16;
+    QHIP(launch_lora_down(u16(X), M, K, u16(L->A), L->r, nullptr, 0, XA_saved, nullptr, ds, down_part, st, false,
+                          false, xt_fused ? xt : nullptr, xt_fused ? qplan::skinny_mp(M) : 0));
     SkinnyArgs a;
     memset(&a, 0, sizeof(a));
     a.X = u16(X);
@@ -428,10 +433,9 @@ int qlora_linear_fwd(const qlora_linear* L, const void* X, int64_t M, void* Y, f
     a.part = sp.splits > 1 ? part : nullptr;
     a.kps = sp.kps;
     if (stream2) {
-      uint16_t* xt = reinterpret_cast<uint16_t*>(bytes(ws) + w.fwd_part + w.fwd_down);
       a.Mp = qplan::skinny_mp(M);
       a.Xt = xt;
-      QHIP(launch_xtile(u16(X), M, K, a.Mp, xt, st));
+      if (!xt_fused) QHIP(launch_xtile(u16(X), M, K, a.Mp, xt, st));
     }
     QHIP(traced_skinny_fwd(a, sp, st));
     if (sp.splits > 1) QHIP(launch_splitk_finish(part, sp.splits, M, N, u16m(Y), st));
@@ -514,10 +518,15 @@ static int linear_bwd_impl(const qlora_linear* L, const void* dY, const void* X,
     // Skinny M: T partials, the split transposed product without its LoRA
     // term (the skinny kernel when the shape allows, else the dequant-staged
     // GEMM), then one finish launch for dX (+ s T A), dA and dB.
-    QHIP(launch_transpose_rn(u16(L->B), N, r, BT, st));
+    // T = dY B: B read as stored when the rank allows (<= 16), else B^T first
     const int ds = qplan::plan_down_splits(M, N);
     const int dsu = qplan::down_splits_used(N, ds);
-    QHIP(launch_lora_down(u16(dY), M, N, BT, r, nullptr, 0, T, nullptr, ds, down_part, st, false));
+    if (r <= 16) {
+      QHIP(launch_lora_down(u16(dY), M, N, u16(L->B), r, nullptr, 0, T, nullptr, ds, down_part, st, false, true));
+    } else {
+      QHIP(launch_transpose_rn(u16(L->B), N, r, BT, st));
+      QHIP(launch_lora_down(u16(dY), M, N, BT, r, nullptr, 0, T, nullptr, ds, down_part, st, false));
+    }
     if (sk_bwd) {
       SkinnyBwdArgs b;
       memset(&b, 0, sizeof(b));

@@ -613,11 +613,19 @@ __device__ __forceinline__ f32x4 mfma16k32(u32x4 a, u32x4 b, f32x4 c) {
 // 32-wide form reads 32-byte pieces of 32 rows).  Workgroup: 32 tokens (two
 // frags), 8 waves taking the chunks of their split in turn; the 8 wave
 // partials are summed in LDS in wave order.
+//
+// WNR: W0 is stored [Kred, r0] (a LoRA B read as stored, r1 = 0); the lane
+// gathers its 8 reduction rows of column c instead of one 16-byte load.
+// XT: every token chunk the kernel loads is also written to Xt[Kred/8][Mp][8]
+// (the skinny forward's activation layout; rows M..Mp-1 as zeros), so the
+// activations need no separate re-layout pass.
+template <bool WNR, bool XT>
 __global__ __launch_bounds__(512) void lora_down16_kernel(const uint16_t* __restrict__ Z, int64_t M, int64_t Kred,
                                                           const uint16_t* __restrict__ W0, int r0,
                                                           const uint16_t* __restrict__ W1, int r1,
                                                           float* __restrict__ V0, float* __restrict__ V1,
-                                                          int64_t chunks_per_split, float* __restrict__ part) {
+                                                          int64_t chunks_per_split, float* __restrict__ part,
+                                                          uint16_t* __restrict__ Xt, int Mp) {
   __shared__ float red[8][2 * 4 * 64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = lane & 15, q = lane >> 4;
@@ -632,6 +640,11 @@ __global__ __launch_bounds__(512) void lora_down16_kernel(const uint16_t* __rest
   const bool wok = c < rt;
   const uint16_t* wrow = wok ? (c < r0 ? W0 + (int64_t)c * Kred : W1 + (int64_t)(c - r0) * Kred) + 8 * q
                              : W0 + 8 * q;  // any valid address; the operand is zeroed
+  if constexpr (WNR) wrow = W0 + (wok ? c : 0) + (int64_t)(8 * q) * r0;
+  // the lane's token rows for the re-laid-out copy (rows past Mp: none)
+  int64_t xm[2];
+#pragma unroll
+  for (int f = 0; f < 2; ++f) xm[f] = m0 + 16 * f + c;
   const int64_t C = Kred / 64;
   const int64_t cb = (int64_t)blockIdx.y * chunks_per_split;
   const int64_t ce = (cb + chunks_per_split < C) ? cb + chunks_per_split : C;
@@ -646,15 +659,31 @@ __global__ __launch_bounds__(512) void lora_down16_kernel(const uint16_t* __rest
     for (int st = 0; st < 2; ++st) {
 #pragma unroll
       for (int f = 0; f < 2; ++f) z[f][st] = *reinterpret_cast<const u32x4*>(zrow[f] + ch * 64 + 32 * st);
-      w[st] = *reinterpret_cast<const u32x4*>(wrow + ch * 64 + 32 * st);
+      if constexpr (WNR) {
+        const uint16_t* src = wrow + (ch * 64 + 32 * st) * r0;
+        uint32_t h[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) h[e] = src[e * r0];
+        w[st] = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+      } else {
+        w[st] = *reinterpret_cast<const u32x4*>(wrow + ch * 64 + 32 * st);
+      }
     }
   };
-  auto mul = [&](const u32x4 (&z)[2][2], const u32x4 (&w)[2]) {
+  auto mul = [&](int64_t ch, const u32x4 (&z)[2][2], const u32x4 (&w)[2]) {
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
       const u32x4 wz = wok ? w[st] : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
       for (int f = 0; f < 2; ++f) acc[f] = mfma16k32(wz, z[f][st], acc[f]);
+      if constexpr (XT) {
+        // chunk ch * 8 + 4 st + q of token row xm[f]
+#pragma unroll
+        for (int f = 0; f < 2; ++f)
+          if (xm[f] < Mp)
+            *reinterpret_cast<u32x4*>(Xt + ((ch * 8 + 4 * st + q) * Mp + xm[f]) * 8) =
+                xm[f] < M ? z[f][st] : u32x4{0u, 0u, 0u, 0u};
+      }
     }
   };
   int64_t ch = cb + wave;
@@ -662,11 +691,11 @@ __global__ __launch_bounds__(512) void lora_down16_kernel(const uint16_t* __rest
   // two register sets alternate (a copy of a prefetch would wait for it)
   for (; ch + 8 < ce; ch += 16) {
     load(ch + 8, zb, wb);
-    mul(za, wa);
+    mul(ch, za, wa);
     if (ch + 16 < ce) load(ch + 16, za, wa);
-    mul(zb, wb);
+    mul(ch + 8, zb, wb);
   }
-  if (ch < ce) mul(za, wa);
+  if (ch < ce) mul(ch, za, wa);
 
   // acc[f][v] = C[j = 4q + v][token m0 + 16 f + c]
 #pragma unroll
@@ -1370,8 +1399,12 @@ hipError_t launch_splitk_finish(const float* part, int splits, int64_t M, int64_
 
 hipError_t launch_lora_down(const uint16_t* Z, int64_t M, int64_t Kred, const uint16_t* W0, int r0,
                             const uint16_t* W1, int r1, float* V0, float* V1, int splits, float* part,
-                            hipStream_t st, bool finish) {
+                            hipStream_t st, bool finish, bool w_nr, uint16_t* Xt, int Mp) {
   if (M == 0) return hipSuccess;
+  // the [Kred, r0] weight layout and the re-laid-out copy exist in the
+  // rank <= 16 form only, one at a time
+  if ((w_nr || Xt) && (r0 + r1 > 16 || (w_nr && (r1 != 0 || Xt)) || (Xt && (Mp < M || Mp > 32 * grid1(M, 32)))))
+    return hipErrorInvalidValue;
   const int64_t C = Kred / 64;
   const int64_t per = (C + splits - 1) / splits;
   const int S = (int)((C + per - 1) / per);
@@ -1379,7 +1412,13 @@ hipError_t launch_lora_down(const uint16_t* Z, int64_t M, int64_t Kred, const ui
   float* pp = S > 1 ? part : nullptr;
   int jf = (r0 + r1 + 31) / 32;
   if (r0 + r1 <= 16) {
-    lora_down16_kernel<<<grid, 512, 0, st>>>(Z, M, Kred, W0, r0, W1, r1, V0, V1, per, pp);
+    if (w_nr)
+      lora_down16_kernel<true, false><<<grid, 512, 0, st>>>(Z, M, Kred, W0, r0, W1, r1, V0, V1, per, pp, nullptr, 0);
+    else if (Xt)
+      lora_down16_kernel<false, true><<<grid, 512, 0, st>>>(Z, M, Kred, W0, r0, W1, r1, V0, V1, per, pp, Xt, Mp);
+    else
+      lora_down16_kernel<false, false><<<grid, 512, 0, st>>>(Z, M, Kred, W0, r0, W1, r1, V0, V1, per, pp, nullptr,
+                                                             0);
     jf = 0;
   }
   switch (jf) {

@@ -236,9 +236,13 @@ hipError_t launch_skinny_fwd(const SkinnyArgs& a, const qplan::SkinnyPlan& pl, h
 // V0 | V1 = Z W0^T | Z W1^T, W0 [r0, Kred], W1 [r1, Kred] (r0 + r1 <= 128).
 // With finish = false and more than one split (qplan::down_splits_used) the
 // fp32 partials stay in part[split][M][r0 + r1] for the consumer to sum.
+// Rank <= 16 only: w_nr reads W0 stored [Kred, r0] (r1 = 0), i.e. V0 = Z W0;
+// Xt (with Mp = M rounded up to 16) also receives Z re-laid out as
+// Xt[Kred/8][Mp][8], rows M..Mp-1 zero.
 hipError_t launch_lora_down(const uint16_t* Z, int64_t M, int64_t Kred, const uint16_t* W0, int r0,
                             const uint16_t* W1, int r1, float* V0, float* V1, int splits, float* part,
-                            hipStream_t st, bool finish = true);
+                            hipStream_t st, bool finish = true, bool w_nr = false, uint16_t* Xt = nullptr,
+                            int Mp = 0);
 // B [N, r] -> B^T [r, N]
 hipError_t launch_transpose_rn(const uint16_t* B, int64_t N, int r, uint16_t* BT, hipStream_t st);
 

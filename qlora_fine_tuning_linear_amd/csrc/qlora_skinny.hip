@@ -398,12 +398,16 @@ __global__ __launch_bounds__(256) void skinny_fwd_kernel(SkinnyArgs p) {
 //   dB[n, :] = s dY[:, n]^T XA
 // Every sum runs in fp32 in a fixed order.
 // ------------------------------------------------------------------------
+// LDS (dynamic, sized by the rank so that small ranks keep several
+// workgroups per CU): vs [64][r] T or XA, zs [64][68] a 64-column block of X
+// or dY (+4 pad), as [r][32] a 32-column block of A.
 __global__ __launch_bounds__(256) void skinny_bwd_finish_kernel(SkinnyFinishArgs p) {
-  __shared__ float vs[64 * 128];  // T or XA, [M][r]
-  __shared__ float zs[64 * 68];   // 64-column block of X or dY, [M][64] (+4 pad)
-  __shared__ float as[128 * 32];  // 32-column block of A, [r][32]
+  extern __shared__ float fin_smem[];
   const int tid = threadIdx.x;
   const int M = (int)p.M, r = p.r;
+  float* vs = fin_smem;
+  float* zs = vs + 64 * r;
+  float* as = zs + 64 * 68;
   const int nkb = (int)(p.K / 32);
   // bf16 [M][cols] block at src (row stride ld) -> zs as fp32, 8 columns per load
   auto stage_block = [&](const uint16_t* src, int64_t ld, int cols) {
@@ -421,6 +425,23 @@ __global__ __launch_bounds__(256) void skinny_bwd_finish_kernel(SkinnyFinishArgs
   };
   if ((int)blockIdx.x < nkb) {
     const int64_t k0 = (int64_t)blockIdx.x * 32;
+    // dX: 8 threads per row, 4 columns each, rows tid / 8 and tid / 8 + 32.
+    // With at most 8 splits the partials of both rows are requested first,
+    // so they are in flight while T, X and A are staged.
+    const int cq = (tid & 7) * 4;
+    constexpr int PZ = 8;
+    const bool early = p.splits <= PZ;
+    f32x4 pre[2][PZ];
+    if (early) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int m = min((tid >> 3) + 32 * h, M - 1);
+        const float* src = p.part + (int64_t)m * p.K + k0 + cq;
+#pragma unroll
+        for (int zz = 0; zz < PZ; ++zz)
+          pre[h][zz] = *reinterpret_cast<const f32x4*>(src + (int64_t)min(zz, p.splits - 1) * M * p.K);
+      }
+    }
     // T = sum_z tpart[z] (split order), loads of 8 splits in flight
     for (int e0 = tid; e0 < M * r; e0 += 256 * 4) {
       float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -452,20 +473,28 @@ __global__ __launch_bounds__(256) void skinny_bwd_finish_kernel(SkinnyFinishArgs
       }
     }
     __syncthreads();
-    // dX: 8 threads per row, 4 columns each; the split partials of a row
-    // are loaded 8 splits at a time and added in split order
-    const int cq = (tid & 7) * 4;
-    for (int m = tid >> 3; m < M; m += 32) {
+    // the split partials of a row are added in split order (loaded above,
+    // or here 8 splits at a time)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int m = (tid >> 3) + 32 * h;
+      if (m >= M) break;
       const float* src = p.part + (int64_t)m * p.K + k0 + cq;
       f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-      for (int z0 = 0; z0 < p.splits; z0 += 8) {
-        f32x4 t[8];
+      if (early) {
 #pragma unroll
-        for (int zz = 0; zz < 8; ++zz)
-          t[zz] = *reinterpret_cast<const f32x4*>(src + (int64_t)min(z0 + zz, p.splits - 1) * M * p.K);
+        for (int zz = 0; zz < PZ; ++zz)
+          if (zz < p.splits) acc += pre[h][zz];
+      } else {
+        for (int z0 = 0; z0 < p.splits; z0 += 8) {
+          f32x4 t[8];
 #pragma unroll
-        for (int zz = 0; zz < 8; ++zz)
-          if (z0 + zz < p.splits) acc += t[zz];
+          for (int zz = 0; zz < 8; ++zz)
+            t[zz] = *reinterpret_cast<const f32x4*>(src + (int64_t)min(z0 + zz, p.splits - 1) * M * p.K);
+#pragma unroll
+          for (int zz = 0; zz < 8; ++zz)
+            if (z0 + zz < p.splits) acc += t[zz];
+        }
       }
       float lo[4] = {0.0f, 0.0f, 0.0f, 0.0f};
       for (int j = 0; j < r; ++j) {
@@ -477,24 +506,51 @@ __global__ __launch_bounds__(256) void skinny_bwd_finish_kernel(SkinnyFinishArgs
           u32x2{pack_bf16x2(acc[0] + p.s * lo[0], acc[1] + p.s * lo[1]),
                 pack_bf16x2(acc[2] + p.s * lo[2], acc[3] + p.s * lo[3])};
     }
-    // dA[j, k0 + c] = s sum_m T[m, j] X[m, k0 + c]
+    // dA[j, k0 + c] = s sum_m T[m, j] X[m, k0 + c]; with an even rank each
+    // thread takes ranks j, j + 1 (one 8-byte read of T per token)
     const int c = tid & 31;
-    for (int j = tid >> 5; j < r; j += 8) {
-      float acc = 0.0f;
-      for (int m = 0; m < M; ++m) acc += vs[m * r + j] * zs[m * 68 + c];
-      p.dA[(int64_t)j * p.K + k0 + c] = (uint16_t)(pack_bf16x2(p.s * acc, 0.0f) & 0xFFFFu);
+    if ((r & 1) == 0) {
+      for (int j = 2 * (tid >> 5); j < r; j += 16) {
+        float a0 = 0.0f, a1 = 0.0f;
+        for (int m = 0; m < M; ++m) {
+          const float2 t = *reinterpret_cast<const float2*>(vs + m * r + j);
+          const float x = zs[m * 68 + c];
+          a0 += t.x * x;
+          a1 += t.y * x;
+        }
+        p.dA[(int64_t)j * p.K + k0 + c] = (uint16_t)(pack_bf16x2(p.s * a0, 0.0f) & 0xFFFFu);
+        p.dA[(int64_t)(j + 1) * p.K + k0 + c] = (uint16_t)(pack_bf16x2(p.s * a1, 0.0f) & 0xFFFFu);
+      }
+    } else {
+      for (int j = tid >> 5; j < r; j += 8) {
+        float acc = 0.0f;
+        for (int m = 0; m < M; ++m) acc += vs[m * r + j] * zs[m * 68 + c];
+        p.dA[(int64_t)j * p.K + k0 + c] = (uint16_t)(pack_bf16x2(p.s * acc, 0.0f) & 0xFFFFu);
+      }
     }
   } else {
     const int64_t n0 = (int64_t)(blockIdx.x - nkb) * 64;
     for (int e = tid; e < M * r; e += 256) vs[e] = p.XA[e];
     stage_block(p.dY + n0, p.N, 64);
     __syncthreads();
-    // consecutive threads write consecutive ranks of one row of dB
-    for (int e = tid; e < 64 * r; e += 256) {
-      const int nl = e / r, j = e - nl * r;
-      float acc = 0.0f;
-      for (int m = 0; m < M; ++m) acc += zs[m * 68 + nl] * vs[m * r + j];
-      p.dB[(n0 + nl) * r + j] = (uint16_t)(pack_bf16x2(p.s * acc, 0.0f) & 0xFFFFu);
+    if ((r & 3) == 0) {
+      // a thread takes 4 consecutive ranks of one row of dB (one 16-byte
+      // read of XA per token), consecutive threads the next 4
+      for (int e = 4 * tid; e < 64 * r; e += 1024) {
+        const int nl = e / r, j = e - nl * r;
+        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (int m = 0; m < M; ++m) acc += zs[m * 68 + nl] * *reinterpret_cast<const f32x4*>(vs + m * r + j);
+        *reinterpret_cast<u32x2*>(p.dB + (n0 + nl) * r + j) =
+            u32x2{pack_bf16x2(p.s * acc[0], p.s * acc[1]), pack_bf16x2(p.s * acc[2], p.s * acc[3])};
+      }
+    } else {
+      // consecutive threads write consecutive ranks of one row of dB
+      for (int e = tid; e < 64 * r; e += 256) {
+        const int nl = e / r, j = e - nl * r;
+        float acc = 0.0f;
+        for (int m = 0; m < M; ++m) acc += zs[m * 68 + nl] * vs[m * r + j];
+        p.dB[(n0 + nl) * r + j] = (uint16_t)(pack_bf16x2(p.s * acc, 0.0f) & 0xFFFFu);
+      }
     }
   }
 }
@@ -737,7 +793,8 @@ hipError_t launch_skinny_bwd_finish(const SkinnyFinishArgs& a, hipStream_t st) {
   if (!skinny_finish_supported(a.M, a.r) || a.K % 64 != 0 || a.N % 64 != 0) return hipErrorInvalidValue;
   const unsigned grid = (unsigned)(a.K / 32 + a.N / 64);
   if (grid == 0) return hipSuccess;
-  skinny_bwd_finish_kernel<<<grid, 256, 0, st>>>(a);
+  const size_t lds = (size_t)(64 * a.r + 64 * 68 + 32 * a.r) * sizeof(float);
+  skinny_bwd_finish_kernel<<<grid, 256, lds, st>>>(a);
   return hipGetLastError();
 }
 
