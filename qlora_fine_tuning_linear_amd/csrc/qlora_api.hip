@@ -403,7 +403,7 @@ int qlora_linear_fwd(const qlora_linear* L, const void* X, int64_t M, void* Y, f
 
   if (qplan::use_skinny_fwd(M, L->r)) {
     // XA partials; the skinny GEMM sums them, writes XA and adds s XA B^T
-    const int ds = qplan::plan_down_splits(M, K);
+    const int ds = qplan::plan_down_splits(M, K, L->r);
     const int dsu = qplan::down_splits_used(K, ds);
     const bool stream2 = qplan::use_skinny_fwd2(M, N, K, L->r);
     const qplan::SkinnyPlan sp = stream2 ? qplan::plan_skinny_fwd2(N, K) : qplan::plan_skinny_fwd(N, K);
@@ -443,7 +443,7 @@ int qlora_linear_fwd(const qlora_linear* L, const void* X, int64_t M, void* Y, f
   }
   // XA = X A^T (kept for the backward)
   QHIP(launch_lora_down(u16(X), M, K, u16(L->A), L->r, nullptr, 0, XA_saved, nullptr,
-                        qplan::plan_down_splits(M, K), down_part, st));
+                        qplan::plan_down_splits(M, K, L->r), down_part, st));
   // Y = X W0^T + s XA B^T
   const qplan::GemmPlan pl = qplan::plan_gemm(M, N, K, true);
   GemmArgs a = gemm_args();
@@ -519,7 +519,7 @@ static int linear_bwd_impl(const qlora_linear* L, const void* dY, const void* X,
     // term (the skinny kernel when the shape allows, else the dequant-staged
     // GEMM), then one finish launch for dX (+ s T A), dA and dB.
     // T = dY B: B read as stored when the rank allows (<= 16), else B^T first
-    const int ds = qplan::plan_down_splits(M, N);
+    const int ds = qplan::plan_down_splits(M, N, r);
     const int dsu = qplan::down_splits_used(N, ds);
     if (r <= 16) {
       QHIP(launch_lora_down(u16(dY), M, N, u16(L->B), r, nullptr, 0, T, nullptr, ds, down_part, st, false, true));
@@ -586,7 +586,7 @@ static int linear_bwd_impl(const qlora_linear* L, const void* dY, const void* X,
     pa.job[0] = PairJob{u16(dY), BT, XA_saved, r, s, grad_part, grad_part + (size_t)pa.nb * M * r, T, u16m(dB)};
     QHIP(launch_lora_pair(pa, st));
   } else {
-    QHIP(launch_lora_down(u16(dY), M, N, BT, r, nullptr, 0, T, nullptr, qplan::plan_down_splits(M, N), down_part,
+    QHIP(launch_lora_down(u16(dY), M, N, BT, r, nullptr, 0, T, nullptr, qplan::plan_down_splits(M, N, r), down_part,
                           st));
   }
   // dX = dY W0 + s T A
@@ -660,12 +660,12 @@ static int mlp_fwd_impl(const qlora_mlp* P, const void* X, int64_t M, void* Y, c
     // done by the caller
   } else if (P->gate.r + P->up.r <= 128) {
     QHIP(launch_lora_down(u16(X), M, D, u16(P->gate.A), P->gate.r, u16(P->up.A), P->up.r, S->XA_g, S->XA_u,
-                          qplan::plan_down_splits(M, D), down_part, st));
+                          qplan::plan_down_splits(M, D, P->gate.r + P->up.r), down_part, st));
   } else {
     QHIP(launch_lora_down(u16(X), M, D, u16(P->gate.A), P->gate.r, nullptr, 0, S->XA_g, nullptr,
-                          qplan::plan_down_splits(M, D), down_part, st));
+                          qplan::plan_down_splits(M, D, P->gate.r), down_part, st));
     QHIP(launch_lora_down(u16(X), M, D, u16(P->up.A), P->up.r, nullptr, 0, S->XA_u, nullptr,
-                          qplan::plan_down_splits(M, D), down_part, st));
+                          qplan::plan_down_splits(M, D, P->up.r), down_part, st));
   }
   // G, U = gate/up(X) and H = silu(G) * U in one dual GEMM
   {
@@ -715,7 +715,7 @@ static int mlp_fwd_impl(const qlora_mlp* P, const void* X, int64_t M, void* Y, c
     QHIP(launch_had_finish(had_part, (int)qplan::cdiv(I, 128), M, P->down.r, S->HA_d, st));
   else
     QHIP(launch_lora_down(H, M, I, u16(P->down.A), P->down.r, nullptr, 0, S->HA_d, nullptr,
-                          qplan::plan_down_splits(M, I), down_part, st));
+                          qplan::plan_down_splits(M, I, P->down.r), down_part, st));
   // Y = H W_d^T + s_d HA_d B_d^T
   {
     GemmArgs a = gemm_args();
@@ -776,11 +776,12 @@ int qlora_mlp_fwd_rmsnorm(const qlora_mlp* P, const void* X, const void* norm_w,
   QHIP(launch_scale_cols(u16(P->gate.A), rg, D, u16(norm_w), ag, st));
   QHIP(launch_scale_cols(u16(P->up.A), ru, D, u16(norm_w), au, st));
   if (rg + ru <= 128) {
-    QHIP(launch_lora_down(u16(X), M, D, ag, rg, au, ru, xag, xau, qplan::plan_down_splits(M, D), down_part, st));
-  } else {
-    QHIP(launch_lora_down(u16(X), M, D, ag, rg, nullptr, 0, xag, nullptr, qplan::plan_down_splits(M, D), down_part,
+    QHIP(launch_lora_down(u16(X), M, D, ag, rg, au, ru, xag, xau, qplan::plan_down_splits(M, D, rg + ru), down_part,
                           st));
-    QHIP(launch_lora_down(u16(X), M, D, au, ru, nullptr, 0, xau, nullptr, qplan::plan_down_splits(M, D), down_part,
+  } else {
+    QHIP(launch_lora_down(u16(X), M, D, ag, rg, nullptr, 0, xag, nullptr, qplan::plan_down_splits(M, D, rg), down_part,
+                          st));
+    QHIP(launch_lora_down(u16(X), M, D, au, ru, nullptr, 0, xau, nullptr, qplan::plan_down_splits(M, D, ru), down_part,
                           st));
   }
   QHIP(launch_scale_rows(xag, M, rg, rstd, S->XA_g, st));
@@ -860,7 +861,7 @@ int qlora_mlp_bwd(const qlora_mlp* P, const void* dY, const void* X, const qlora
                         u16m(G->dB_d)};
     QHIP(launch_lora_pair(pa, st));
   } else {
-    QHIP(launch_lora_down(u16(dY), M, D, BdT, rd, nullptr, 0, Td, nullptr, qplan::plan_down_splits(M, D),
+    QHIP(launch_lora_down(u16(dY), M, D, BdT, rd, nullptr, 0, Td, nullptr, qplan::plan_down_splits(M, D, rd),
                           down_part, st));
   }
   // dH = dY W_d + s_d Td A_d, with the SwiGLU backward in the epilogue -> dG, dU
@@ -920,8 +921,10 @@ int qlora_mlp_bwd(const qlora_mlp* P, const void* dY, const void* X, const qlora
     QHIP(launch_lora_pair(pa, st));
   } else {
     // Tg = dG B_g, Tu = dU B_u
-    QHIP(launch_lora_down(dG, M, I, BgT, rg, nullptr, 0, Tg, nullptr, qplan::plan_down_splits(M, I), down_part, st));
-    QHIP(launch_lora_down(dU, M, I, BuT, ru, nullptr, 0, Tu, nullptr, qplan::plan_down_splits(M, I), down_part, st));
+    QHIP(launch_lora_down(dG, M, I, BgT, rg, nullptr, 0, Tg, nullptr, qplan::plan_down_splits(M, I, rg), down_part,
+                          st));
+    QHIP(launch_lora_down(dU, M, I, BuT, ru, nullptr, 0, Tu, nullptr, qplan::plan_down_splits(M, I, ru), down_part,
+                          st));
   }
   // dX = dG W_g + dU W_u + s_g Tg A_g + s_u Tu A_u  (one GEMM, reduction over 2I)
   {

@@ -502,29 +502,36 @@ __global__ __launch_bounds__(256) void splitk_finish_kernel(const float* __restr
 // j < r0 come from W0 into V0, rows r0 <= j < r0 + r1 from W1 into V1 (gate |
 // up share one pass over Z).  Both W are [r, Kred] bf16, rows contiguous.
 //
-// Workgroup: 32 tokens, 8 waves taking the 64-wide reduction chunks of their
-// split in turn (consecutive chunks stream side by side).  Within a chunk
-// lane (token l32, half h) loads the 64 contiguous bytes k0 + 32h .. +31 of
-// its token row, and the W lane (row l32 of the frag, half h) the same
-// columns of its row: MFMA step t multiplies columns k0 + 32h + 8t + e, a
-// permutation of the chunk shared by both operands.  The next chunk's loads
-// are issued before the current chunk's MFMAs.  The 8 wave partials are
-// summed in LDS in wave order; with several splits (blockIdx.y) the sums go
-// to part[split][M][r0 + r1] for down_finish_kernel.
+// Workgroup: 32 TF tokens (TF token frags of 32), 8 waves taking the 64-wide
+// reduction chunks of their split in turn (consecutive chunks stream side by
+// side).  Within a chunk lane (token l32 of each frag, half h) loads the 64
+// contiguous bytes k0 + 32h .. +31 of its token row, and the W lane (row l32
+// of the frag, half h) the same columns of its row: MFMA step t multiplies
+// columns k0 + 32h + 8t + e, a permutation of the chunk shared by both
+// operands.  Every workgroup reads its split's W columns whole, so TF = 2
+// halves the W bytes per token (at ranks 33..64 they are twice the token
+// bytes with TF = 1).  The next chunk's loads are issued before the current
+// chunk's MFMAs.  The 8 wave partials are summed in LDS in wave order; with
+// several splits (blockIdx.y) the sums go to part[split][M][r0 + r1] for
+// down_finish_kernel.
 // ------------------------------------------------------------------------
-template <int JF>
+template <int JF, int TF>
 __global__ __launch_bounds__(512) void lora_down_kernel(const uint16_t* __restrict__ Z, int64_t M, int64_t Kred,
                                                         const uint16_t* __restrict__ W0, int r0,
                                                         const uint16_t* __restrict__ W1, int r1,
                                                         float* __restrict__ V0, float* __restrict__ V1,
                                                         int64_t chunks_per_split, float* __restrict__ part) {
-  __shared__ float red[8][JF * 16 * 64];
+  __shared__ float red[8][JF * TF * 16 * 64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, h = lane >> 5;
   const int rt = r0 + r1;
-  const int64_t m0 = (int64_t)blockIdx.x * 32;
-  const int64_t m = (m0 + l32 < M) ? m0 + l32 : M - 1;
-  const uint16_t* zrow = Z + m * Kred + 32 * h;
+  const int64_t m0 = (int64_t)blockIdx.x * 32 * TF;
+  const uint16_t* zrow[TF];
+#pragma unroll
+  for (int tf = 0; tf < TF; ++tf) {
+    const int64_t m = (m0 + 32 * tf + l32 < M) ? m0 + 32 * tf + l32 : M - 1;
+    zrow[tf] = Z + m * Kred + 32 * h;
+  }
   const uint16_t* wrow[JF];
   bool wok[JF];
 #pragma unroll
@@ -538,28 +545,33 @@ __global__ __launch_bounds__(512) void lora_down_kernel(const uint16_t* __restri
   const int64_t cb = (int64_t)blockIdx.y * chunks_per_split;
   const int64_t ce = (cb + chunks_per_split < C) ? cb + chunks_per_split : C;
 
-  f32x16 acc[JF];
+  f32x16 acc[JF][TF];
 #pragma unroll
   for (int jf = 0; jf < JF; ++jf)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) acc[jf][v] = 0.0f;
-
-  u32x4 za[4], wa[JF][4], zb[4], wb[JF][4];
-  auto load = [&](int64_t c, u32x4 (&z)[4], u32x4 (&w)[JF][4]) {
+    for (int tf = 0; tf < TF; ++tf)
 #pragma unroll
-    for (int t = 0; t < 4; ++t) z[t] = *reinterpret_cast<const u32x4*>(zrow + c * 64 + 8 * t);
+      for (int v = 0; v < 16; ++v) acc[jf][tf][v] = 0.0f;
+
+  u32x4 za[TF][4], wa[JF][4], zb[TF][4], wb[JF][4];
+  auto load = [&](int64_t c, u32x4 (&z)[TF][4], u32x4 (&w)[JF][4]) {
+#pragma unroll
+    for (int tf = 0; tf < TF; ++tf)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) z[tf][t] = *reinterpret_cast<const u32x4*>(zrow[tf] + c * 64 + 8 * t);
 #pragma unroll
     for (int jf = 0; jf < JF; ++jf)
 #pragma unroll
       for (int t = 0; t < 4; ++t) w[jf][t] = *reinterpret_cast<const u32x4*>(wrow[jf] + c * 64 + 8 * t);
   };
-  auto mul = [&](const u32x4 (&z)[4], const u32x4 (&w)[JF][4]) {
+  auto mul = [&](const u32x4 (&z)[TF][4], const u32x4 (&w)[JF][4]) {
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int jf = 0; jf < JF; ++jf) {
         const u32x4 wz = wok[jf] ? w[jf][t] : u32x4{0u, 0u, 0u, 0u};
-        acc[jf] = mfma32(wz, z[t], acc[jf]);
+#pragma unroll
+        for (int tf = 0; tf < TF; ++tf) acc[jf][tf] = mfma32(wz, z[tf][t], acc[jf][tf]);
       }
   };
   int64_t c = cb + wave;
@@ -573,19 +585,22 @@ __global__ __launch_bounds__(512) void lora_down_kernel(const uint16_t* __restri
   }
   if (c < ce) mul(za, wa);
 
-  // acc[jf][v] = C[j = 32 jf + 8(v/4) + 4h + v%4][token l32]
+  // acc[jf][tf][v] = C[j = 32 jf + 8(v/4) + 4h + v%4][token 32 tf + l32]
 #pragma unroll
   for (int jf = 0; jf < JF; ++jf)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) red[wave][(jf * 16 + v) * 64 + lane] = acc[jf][v];
+    for (int tf = 0; tf < TF; ++tf)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) red[wave][((jf * TF + tf) * 16 + v) * 64 + lane] = acc[jf][tf][v];
   __syncthreads();
-  for (int idx = tid; idx < JF * 16 * 64; idx += 512) {
+  for (int idx = tid; idx < JF * TF * 16 * 64; idx += 512) {
     float sum = 0.0f;
 #pragma unroll
     for (int w = 0; w < 8; ++w) sum += red[w][idx];
-    const int ln = idx & 63, vv = (idx >> 6) & 15, jf = idx >> 10;
+    const int ln = idx & 63, vv = (idx >> 6) & 15, jt = idx >> 10;
+    const int jf = jt / TF, tf = jt - jf * TF;
     const int j = 32 * jf + 8 * (vv >> 2) + 4 * (ln >> 5) + (vv & 3);
-    const int64_t mm = m0 + (ln & 31);
+    const int64_t mm = m0 + 32 * tf + (ln & 31);
     if (j >= rt || mm >= M) continue;
     if (part) {
       part[((int64_t)blockIdx.y * M + mm) * rt + j] = sum;
@@ -1408,7 +1423,9 @@ hipError_t launch_lora_down(const uint16_t* Z, int64_t M, int64_t Kred, const ui
   const int64_t C = Kred / 64;
   const int64_t per = (C + splits - 1) / splits;
   const int S = (int)((C + per - 1) / per);
-  dim3 grid(grid1(M, 32), (unsigned)S);
+  // tokens per workgroup as qplan::down_tokens, which the split plan assumed
+  const int tpw = qplan::down_tokens(r0 + r1);
+  dim3 grid(grid1(M, tpw), (unsigned)S);
   float* pp = S > 1 ? part : nullptr;
   int jf = (r0 + r1 + 31) / 32;
   if (r0 + r1 <= 16) {
@@ -1423,10 +1440,15 @@ hipError_t launch_lora_down(const uint16_t* Z, int64_t M, int64_t Kred, const ui
   }
   switch (jf) {
     case 0: break;
-    case 1: lora_down_kernel<1><<<grid, 512, 0, st>>>(Z, M, Kred, W0, r0, W1, r1, V0, V1, per, pp); break;
-    case 2: lora_down_kernel<2><<<grid, 512, 0, st>>>(Z, M, Kred, W0, r0, W1, r1, V0, V1, per, pp); break;
-    case 3: lora_down_kernel<3><<<grid, 512, 0, st>>>(Z, M, Kred, W0, r0, W1, r1, V0, V1, per, pp); break;
-    case 4: lora_down_kernel<4><<<grid, 512, 0, st>>>(Z, M, Kred, W0, r0, W1, r1, V0, V1, per, pp); break;
+    case 1: lora_down_kernel<1, 1><<<grid, 512, 0, st>>>(Z, M, Kred, W0, r0, W1, r1, V0, V1, per, pp); break;
+    case 2:
+      if (tpw == 64)
+        lora_down_kernel<2, 2><<<grid, 512, 0, st>>>(Z, M, Kred, W0, r0, W1, r1, V0, V1, per, pp);
+      else
+        lora_down_kernel<2, 1><<<grid, 512, 0, st>>>(Z, M, Kred, W0, r0, W1, r1, V0, V1, per, pp);
+      break;
+    case 3: lora_down_kernel<3, 1><<<grid, 512, 0, st>>>(Z, M, Kred, W0, r0, W1, r1, V0, V1, per, pp); break;
+    case 4: lora_down_kernel<4, 1><<<grid, 512, 0, st>>>(Z, M, Kred, W0, r0, W1, r1, V0, V1, per, pp); break;
     default: return hipErrorInvalidValue;
   }
   hipError_t e = hipGetLastError();

@@ -59,16 +59,38 @@ inline GemmPlan plan_gemm(int64_t M, int64_t Nout, int64_t Kred, bool allow_spli
   return p;
 }
 
-// Reduction splits of the LoRA down-projection V = Z W^T (M x r, reduce over
-// Kred): one 8-wave workgroup per 32 tokens and split; enough splits to put
-// one workgroup on every CU, each split keeping >= 2 64-wide chunks per wave.
-inline int plan_down_splits(int64_t M, int64_t Kred) {
-  const int64_t wgs = cdiv(M, 32);
+// Tokens per workgroup of the LoRA down-projection for a total rank rt: 64
+// at ranks 33..64 (every workgroup reads its split's W columns whole, and at
+// these ranks they are twice its token bytes with 32 tokens), else 32.
+inline int down_tokens(int rt) { return (rt > 32 && rt <= 64) ? 64 : 32; }
+
+// Reduction splits of the LoRA down-projection V = Z W^T (M x rt, reduce
+// over Kred): one 8-wave workgroup per down_tokens(rt) tokens and split;
+// enough splits to put one workgroup on every CU, each split keeping >= 2
+// 64-wide chunks per wave.
+inline int plan_down_splits(int64_t M, int64_t Kred, int rt) {
+  const int64_t wgs = cdiv(M, down_tokens(rt));
   if (wgs >= kNumCUs) return 1;
   int64_t s = cdiv(kNumCUs, wgs);
   const int64_t max_s = Kred / 1024 > 0 ? Kred / 1024 : 1;
   if (s > max_s) s = max_s;
   return (int)(s < 1 ? 1 : s);
+}
+
+// Floats of split partials that any down-projection of total rank <= rmax
+// over Kred may write (0: none).  The split count is not monotonic in the
+// rank (more splits from rank 33, with 64-token workgroups), so this bounds
+// both granularities.
+inline size_t down_part_floats(int64_t M, int64_t Kred, int rmax) {
+  size_t f = 0;
+  const int s32 = plan_down_splits(M, Kred, 1);
+  if (s32 > 1) f = (size_t)s32 * M * rmax;
+  if (rmax > 32) {
+    const int s64 = plan_down_splits(M, Kred, 64);
+    const size_t f64 = s64 > 1 ? (size_t)s64 * M * (rmax < 64 ? rmax : 64) : 0;
+    if (f64 > f) f = f64;
+  }
+  return f;
 }
 
 // Splits that launch_lora_down actually runs for a requested split count.
@@ -214,8 +236,7 @@ inline LinearWs linear_ws(int64_t M, int64_t N, int64_t K, int r) {
     w.fwd_part = sp.splits > 1 ? align256((size_t)sp.splits * M * N * 4) : 0;
     w.fwd_xt = align256((size_t)K * skinny_mp(M) * 2);
   }
-  const int ds = plan_down_splits(M, K);
-  w.fwd_down = ds > 1 ? align256((size_t)ds * M * r * 4) : 0;
+  w.fwd_down = align256(down_part_floats(M, K, r) * 4);
   w.wbuf = bg ? align256((size_t)N * K * 2) : 0;
   w.fwd_total = w.fwd_part + w.fwd_down + w.fwd_xt + w.wbuf;
 
@@ -225,8 +246,7 @@ inline LinearWs linear_ws(int64_t M, int64_t N, int64_t K, int r) {
   w.bwd_part = (!bg && pb.splits > 1) ? align256((size_t)pb.splits * M * K * 4) : 0;
   // skinny backward: the transposed product always writes split partials
   if (pb.cfg == CFG_SKINNY_TR) w.bwd_part = align256((size_t)pb.splits * M * K * 4);
-  const int ts = plan_down_splits(M, N);
-  w.bwd_down = ts > 1 ? align256((size_t)ts * M * r * 4) : 0;
+  w.bwd_down = align256(down_part_floats(M, N, r) * 4);
   const int gs_b = plan_grad_msplits(M, N, r);
   const int gs_a = plan_grad_msplits(M, K, r);
   size_t gb = align256((size_t)gs_b * N * r * 4), ga = align256((size_t)gs_a * K * r * 4);
@@ -269,9 +289,9 @@ inline MlpWs mlp_ws(int64_t M, int64_t D, int64_t I, int rg, int ru, int rd) {
   int rmax = rg > ru ? rg : ru;
   if (rd > rmax) rmax = rd;
   w.fwd_H = align256((size_t)M * I * 2);
-  const int s1 = plan_down_splits(M, D), s2 = plan_down_splits(M, I);
-  size_t d1 = s1 > 1 ? align256((size_t)s1 * M * (rg + ru) * 4) : 0;
-  size_t d2 = s2 > 1 ? align256((size_t)s2 * M * rd * 4) : 0;
+  // X [A_g | A_u]^T (or one layer at a time) over D, H A_d^T over I
+  size_t d1 = align256(down_part_floats(M, D, rg + ru) * 4);
+  size_t d2 = align256(down_part_floats(M, I, rd) * 4);
   w.fwd_down = d1 > d2 ? d1 : d2;
   if (use_bgemm(M)) {
     const int64_t ext = lora_ext_cols(rg, ru);
@@ -291,9 +311,9 @@ inline MlpWs mlp_ws(int64_t M, int64_t D, int64_t I, int rg, int ru, int rd) {
   // B_d^T [rd, D], B_g^T [rg, I], B_u^T [ru, I]; A_d^T [I, rd], A_g^T [D, rg], A_u^T [D, ru]
   w.bwd_BT = align256((size_t)rd * D * 2) + align256((size_t)rg * I * 2) + align256((size_t)ru * I * 2) +
              align256((size_t)I * rd * 2) + align256((size_t)D * rg * 2) + align256((size_t)D * ru * 2);
-  const int t1 = plan_down_splits(M, D), t2 = plan_down_splits(M, I);
-  size_t e1 = t1 > 1 ? align256((size_t)t1 * M * rd * 4) : 0;
-  size_t e2 = t2 > 1 ? align256((size_t)t2 * M * rmax * 4) : 0;
+  // dY B_d over D; dG B_g, dU B_u over I
+  size_t e1 = align256(down_part_floats(M, D, rd) * 4);
+  size_t e2 = align256(down_part_floats(M, I, rmax) * 4);
   w.bwd_down = e1 > e2 ? e1 : e2;
   size_t g = 0;
   const int64_t Ps[6] = {D, I, I, D, I, D};
