@@ -70,6 +70,9 @@ CASES = [
     synth.LinearCfg("m50_640x4096_r16", M=50, K=640, N=4096, r=16, alpha=16.0, dq_group=256),
     synth.LinearCfg("m7_8192x1024_r32", M=7, K=8192, N=1024, r=32, alpha=8.0, dq_group=0),
     synth.LinearCfg("m64_1024x512_r65", M=64, K=1024, N=512, r=65, alpha=13.0, dq_group=0),
+    # skinny backward finish at the largest rank it takes (its LDS is sized
+    # by the rank: 66.5 KB at r = 128)
+    synth.LinearCfg("m48_1024x2048_r128", M=48, K=1024, N=2048, r=128, alpha=32.0, dq_group=0),
     # skinny forward with 4, 7 and 8 frags of 16 rows per workgroup: tile
     # counts that are not a multiple of 4, ragged rows and tokens, and two
     # reduction splits forced by the absmax staging limit (128 tiles > 124)
