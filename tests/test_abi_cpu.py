@@ -362,3 +362,21 @@ def test_validation_under_address_and_ub_sanitizers(tmp_path):
     assert "runtime error" not in r.stderr and "AddressSanitizer" not in r.stderr, r.stderr[-4000:]
     assert "calls" in r.stdout.splitlines()[-1]
 
+
+def test_down_projection_partials_fit_the_workspace_bound(tmp_path):
+    """The split count of the LoRA down-projection depends on the rank (64
+    tokens per workgroup at ranks 33..64), so the workspace sizing uses a bound
+    over all ranks up to each site's maximum: checked on the host for token
+    counts, reduction lengths and ranks 1..256."""
+    import shutil
+    import subprocess
+    if shutil.which("g++") is None:
+        pytest.skip("no host C++ compiler")
+    csrc = os.path.join(ROOT, "qlora_fine_tuning_linear_amd", "csrc")
+    exe = str(tmp_path / "plan_bound")
+    cmd = ["g++", "-std=c++17", "-O1", "-I" + csrc, os.path.join(ROOT, "tests", "plan_bound_driver.cpp"), "-o", exe]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0 and r.stdout.startswith("ok"), r.stdout + r.stderr
+
