@@ -779,18 +779,41 @@ __global__ __launch_bounds__(256) void grouped_db_kernel(GroupDesc d, int Nt, in
   d.dB[g][(int64_t)(n - d.noff[g]) * rg + (j - d.roff[g])] = (uint16_t)(pack_bf16x2(v, 0.0f) & 0xFFFFu);
 }
 
-// Up to six transposes in one launch: job k turns src[k] [rows, cols] into
-// dst[k] [cols, rows]; the elements of all jobs are numbered one after the
-// other, job k owning [end[k-1], end[k]).
+// Several bf16 transposes in one launch: job k, src [rows, cols] -> dst
+// [cols, rows].  Workgroup: one 64 x 64 tile of one job (jobs in order, tiles
+// row-major within a job).  A wave instruction reads 64 consecutive elements
+// of a source row and writes 64 consecutive elements of a destination row;
+// the tile turns in LDS, whose rows are padded to 66 elements so that the
+// column reads of the write phase fall on 64 different banks.
 __global__ __launch_bounds__(256) void transpose_multi_kernel(TransposeJobs J) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  __shared__ uint16_t t[64 * 66];
+  int64_t b = blockIdx.x, tc = 1;
   int k = 0;
-  while (k < J.n - 1 && i >= J.end[k]) ++k;
-  if (i >= J.end[k]) return;
-  const int64_t li = i - (k ? J.end[k - 1] : 0);  // index into dst[k]
-  const int64_t R = J.rows[k];
-  const int64_t j = li / R, n = li % R;
-  J.dst[k][li] = J.src[k][n * J.cols[k] + j];
+  for (; k < J.n; ++k) {
+    tc = (J.cols[k] + 63) / 64;
+    const int64_t tiles = ((J.rows[k] + 63) / 64) * tc;
+    if (b < tiles) break;
+    b -= tiles;
+  }
+  if (k >= J.n) return;
+  const int64_t R = J.rows[k], Cn = J.cols[k];
+  const int64_t r0 = (b / tc) * 64, c0 = (b % tc) * 64;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const uint16_t* __restrict__ src = J.src[k];
+  uint16_t* __restrict__ dst = J.dst[k];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int row = 4 * i + wv;
+    const int64_t r = r0 + row, c = c0 + lane;
+    if (r < R && c < Cn) t[row * 66 + lane] = src[r * Cn + c];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int col = 4 * i + wv;
+    const int64_t c = c0 + col, r = r0 + lane;
+    if (c < Cn && r < R) dst[c * R + r] = t[lane * 66 + col];
+  }
 }
 
 // Sum of split partials [S][M][r0 + r1] in split order into V0 | V1.
@@ -1473,9 +1496,11 @@ hipError_t launch_grouped_db(const GroupDesc& d, int Nt, int Rt, const uint16_t*
 
 hipError_t launch_transpose_multi(const TransposeJobs& J, hipStream_t st) {
   if (J.n < 1 || J.n > 6) return hipErrorInvalidValue;
-  const int64_t total = J.end[J.n - 1];
-  if (total == 0) return hipSuccess;
-  transpose_multi_kernel<<<grid1(total, 256), 256, 0, st>>>(J);
+  int64_t tiles = 0;
+  for (int k = 0; k < J.n; ++k) tiles += ((J.rows[k] + 63) / 64) * ((J.cols[k] + 63) / 64);
+  if (tiles == 0) return hipSuccess;
+  if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
+  transpose_multi_kernel<<<(unsigned)tiles, 256, 0, st>>>(J);
   return hipGetLastError();
 }
 

@@ -281,7 +281,6 @@ struct TransposeJobs {
   uint16_t* dst[6];
   int64_t rows[6];
   int64_t cols[6];
-  int64_t end[6];  // running element count through job k
   int32_t n;
 };
 struct TransposeBatch {
@@ -292,7 +291,6 @@ struct TransposeBatch {
     J.dst[k] = dst;
     J.rows[k] = rows;
     J.cols[k] = cols;
-    J.end[k] = (k ? J.end[k - 1] : 0) + rows * cols;
   }
 };
 hipError_t launch_transpose_multi(const TransposeJobs& J, hipStream_t st);
