@@ -912,7 +912,7 @@ int qlora_mlp_bwd(const qlora_mlp* P, const void* dY, const void* X, const qlora
     // Tg = dG B_g, dB_g = s_g dG^T XA_g, Tu = dU B_u, dB_u = s_u dU^T XA_u:
     // one pass over dG and one over dU, in one launch
     PairArgs pa{};
-    plan_lora_pair(pa, M, I, rg > ru ? rg : ru);
+    plan_lora_pair(pa, M, I, rg > ru ? rg : ru, 2);
     pa.njobs = 2;
     float* pg = pair_part;
     float* pu = pg + qplan::pair_part_floats(M, I, rg);

@@ -1551,8 +1551,20 @@ hipError_t launch_transpose_rn(const uint16_t* B, int64_t N, int r, uint16_t* BT
   return hipGetLastError();
 }
 
-void plan_lora_pair(PairArgs& a, int64_t M, int64_t P, int r) {
-  const int msplits = qplan::plan_pair_msplits(M, P, r);
+void plan_lora_pair(PairArgs& a, int64_t M, int64_t P, int r, int njobs) {
+  int msplits = qplan::plan_pair_msplits(M, P, r);
+  // Whole rounds of workgroups: two fit on a CU (64 KB of LDS each), and a
+  // last round that is mostly empty leaves the chip idle for its duration
+  // (the dG / dU launch of the Llama-3-8B MLP: 2 x 28 x 19 = 1064 = two
+  // rounds and 40; with 18 splits, 1008: 118.7 -> 116.5 us).  Fewer splits
+  // only shrink the partials, so the buffers sized by
+  // qplan::pair_part_floats still hold them.
+  const int64_t nbk = (P + 511) / 512, per_round = 2 * qplan::kNumCUs;
+  const int64_t total = (int64_t)(njobs > 1 ? njobs : 1) * nbk * msplits;
+  if (total > per_round && total % per_round != 0) {
+    const int64_t s = (total / per_round) * per_round / ((njobs > 1 ? njobs : 1) * nbk);
+    if (s >= 1 && s < msplits) msplits = (int)s;
+  }
   const int64_t mps = (((M + msplits - 1) / msplits) + 31) / 32 * 32;
   a.M = M;
   a.P = P;

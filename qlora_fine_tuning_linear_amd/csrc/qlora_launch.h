@@ -271,9 +271,11 @@ struct PairArgs {
   int32_t S;            // token splits
   int32_t nb;           // 512-column blocks
 };
-// Fills the split and block counts of a for M, P (r of the jobs <= 16);
-// the partial buffers need qplan::pair_part_floats(M, P, r) floats per job.
-void plan_lora_pair(PairArgs& a, int64_t M, int64_t P, int r);
+// Fills the split and block counts of a for M, P (r of the jobs <= 16) and
+// njobs jobs in the launch; the partial buffers need
+// qplan::pair_part_floats(M, P, r) floats per job (an upper bound: the split
+// count may come out lower so that the launch fills whole rounds).
+void plan_lora_pair(PairArgs& a, int64_t M, int64_t P, int r, int njobs = 1);
 hipError_t launch_lora_pair(const PairArgs& a, hipStream_t st);
 // Several transposes in one launch: job k, src [rows, cols] -> dst [cols, rows].
 struct TransposeJobs {
