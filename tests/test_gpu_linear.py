@@ -62,6 +62,12 @@ CASES = [
     synth.LinearCfg("m520_1024x1088_r24", M=520, K=1024, N=1088, r=24, alpha=8.0, dq_group=0),
     synth.LinearCfg("m1300_384x448_r16", M=1300, K=384, N=448, r=16, alpha=16.0, dq_group=256),
     synth.LinearCfg("m2049_192x1216_r40", M=2049, K=192, N=1216, r=40, alpha=20.0, dq_group=0),
+    # LoRA-factor transposes above 2 M elements take the tiled form: 64 x 64
+    # tiles with 40 live columns (B [53312, 40]) or rows (A [40, 256]), 256 x 16
+    # tiles with 12 live columns and a partial last tile (B [200000, 12]), and
+    # 16 x 256 tiles (A [12, 256])
+    synth.LinearCfg("m300_256x53312_r40", M=300, K=256, N=53312, r=40, alpha=20.0, dq_group=0),
+    synth.LinearCfg("m300_256x200000_r12", M=300, K=256, N=200000, r=12, alpha=12.0, dq_group=256),
     # skinny (M <= 64) forward: reduction splits, ragged rows / tokens, wave
     # ranges that leave a partial load ring, the largest rank it takes
     synth.LinearCfg("m16_4096x192_r64", M=16, K=4096, N=192, r=64, alpha=16.0, dq_group=256),
