@@ -625,30 +625,31 @@ __device__ __forceinline__ f32x4 mfma16k32(u32x4 a, u32x4 b, f32x4 c) {
 // tokens.  Lane (c, q) (c = lane % 16, q = lane / 16) loads 16 bytes at
 // k0 + 32 s + 8 q of its token row for step s of a 64-wide chunk, so one load
 // instruction covers 64 contiguous bytes of 16 token rows (half lines; the
-// 32-wide form reads 32-byte pieces of 32 rows).  Workgroup: 32 tokens (two
-// frags), 8 waves taking the chunks of their split in turn; the 8 wave
-// partials are summed in LDS in wave order.
+// 32-wide form reads 32-byte pieces of 32 rows).  Workgroup: 16 NF tokens (NF
+// frags: 2, or 1 for at most 64 tokens, where two token blocks would leave
+// most CUs idle), 8 waves taking the chunks of their split in turn; the 8
+// wave partials are summed in LDS in wave order.
 //
 // WNR: W0 is stored [Kred, r0] (a LoRA B read as stored, r1 = 0); the lane
 // gathers its 8 reduction rows of column c instead of one 16-byte load.
 // XT: every token chunk the kernel loads is also written to Xt[Kred/8][Mp][8]
 // (the skinny forward's activation layout; rows M..Mp-1 as zeros), so the
 // activations need no separate re-layout pass.
-template <bool WNR, bool XT>
+template <bool WNR, bool XT, int NF>
 __global__ __launch_bounds__(512) void lora_down16_kernel(const uint16_t* __restrict__ Z, int64_t M, int64_t Kred,
                                                           const uint16_t* __restrict__ W0, int r0,
                                                           const uint16_t* __restrict__ W1, int r1,
                                                           float* __restrict__ V0, float* __restrict__ V1,
                                                           int64_t chunks_per_split, float* __restrict__ part,
                                                           uint16_t* __restrict__ Xt, int Mp) {
-  __shared__ float red[8][2 * 4 * 64];
+  __shared__ float red[8][NF * 4 * 64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = lane & 15, q = lane >> 4;
   const int rt = r0 + r1;
-  const int64_t m0 = (int64_t)blockIdx.x * 32;
-  const uint16_t* zrow[2];
+  const int64_t m0 = (int64_t)blockIdx.x * 16 * NF;
+  const uint16_t* zrow[NF];
 #pragma unroll
-  for (int f = 0; f < 2; ++f) {
+  for (int f = 0; f < NF; ++f) {
     const int64_t m = (m0 + 16 * f + c < M) ? m0 + 16 * f + c : M - 1;
     zrow[f] = Z + m * Kred + 8 * q;
   }
@@ -657,23 +658,23 @@ __global__ __launch_bounds__(512) void lora_down16_kernel(const uint16_t* __rest
                              : W0 + 8 * q;  // any valid address; the operand is zeroed
   if constexpr (WNR) wrow = W0 + (wok ? c : 0) + (int64_t)(8 * q) * r0;
   // the lane's token rows for the re-laid-out copy (rows past Mp: none)
-  int64_t xm[2];
+  int64_t xm[NF];
 #pragma unroll
-  for (int f = 0; f < 2; ++f) xm[f] = m0 + 16 * f + c;
+  for (int f = 0; f < NF; ++f) xm[f] = m0 + 16 * f + c;
   const int64_t C = Kred / 64;
   const int64_t cb = (int64_t)blockIdx.y * chunks_per_split;
   const int64_t ce = (cb + chunks_per_split < C) ? cb + chunks_per_split : C;
 
-  f32x4 acc[2];
+  f32x4 acc[NF];
 #pragma unroll
-  for (int f = 0; f < 2; ++f) acc[f] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int f = 0; f < NF; ++f) acc[f] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  u32x4 za[2][2], wa[2], zb[2][2], wb[2];
-  auto load = [&](int64_t ch, u32x4 (&z)[2][2], u32x4 (&w)[2]) {
+  u32x4 za[NF][2], wa[2], zb[NF][2], wb[2];
+  auto load = [&](int64_t ch, u32x4 (&z)[NF][2], u32x4 (&w)[2]) {
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
 #pragma unroll
-      for (int f = 0; f < 2; ++f) z[f][st] = *reinterpret_cast<const u32x4*>(zrow[f] + ch * 64 + 32 * st);
+      for (int f = 0; f < NF; ++f) z[f][st] = *reinterpret_cast<const u32x4*>(zrow[f] + ch * 64 + 32 * st);
       if constexpr (WNR) {
         const uint16_t* src = wrow + (ch * 64 + 32 * st) * r0;
         uint32_t h[8];
@@ -685,16 +686,16 @@ __global__ __launch_bounds__(512) void lora_down16_kernel(const uint16_t* __rest
       }
     }
   };
-  auto mul = [&](int64_t ch, const u32x4 (&z)[2][2], const u32x4 (&w)[2]) {
+  auto mul = [&](int64_t ch, const u32x4 (&z)[NF][2], const u32x4 (&w)[2]) {
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
       const u32x4 wz = wok ? w[st] : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-      for (int f = 0; f < 2; ++f) acc[f] = mfma16k32(wz, z[f][st], acc[f]);
+      for (int f = 0; f < NF; ++f) acc[f] = mfma16k32(wz, z[f][st], acc[f]);
       if constexpr (XT) {
         // chunk ch * 8 + 4 st + q of token row xm[f]
 #pragma unroll
-        for (int f = 0; f < 2; ++f)
+        for (int f = 0; f < NF; ++f)
           if (xm[f] < Mp)
             *reinterpret_cast<u32x4*>(Xt + ((ch * 8 + 4 * st + q) * Mp + xm[f]) * 8) =
                 xm[f] < M ? z[f][st] : u32x4{0u, 0u, 0u, 0u};
@@ -714,11 +715,11 @@ __global__ __launch_bounds__(512) void lora_down16_kernel(const uint16_t* __rest
 
   // acc[f][v] = C[j = 4q + v][token m0 + 16 f + c]
 #pragma unroll
-  for (int f = 0; f < 2; ++f)
+  for (int f = 0; f < NF; ++f)
 #pragma unroll
     for (int v = 0; v < 4; ++v) red[wave][(f * 4 + v) * 64 + lane] = acc[f][v];
   __syncthreads();
-  if (tid < 2 * 4 * 64) {
+  if (tid < NF * 4 * 64) {
     float sum = 0.0f;
 #pragma unroll
     for (int w = 0; w < 8; ++w) sum += red[w][tid];
@@ -1468,9 +1469,12 @@ hipError_t launch_lora_down(const uint16_t* Z, int64_t M, int64_t Kred, const ui
                             const uint16_t* W1, int r1, float* V0, float* V1, int splits, float* part,
                             hipStream_t st, bool finish, bool w_nr, uint16_t* Xt, int Mp) {
   if (M == 0) return hipSuccess;
+  // rank <= 16: 16-token workgroups for at most 64 tokens (same splits, so
+  // the partial layout [S][M][rt] is unchanged), else 32-token ones
+  const int nf = (r0 + r1 <= 16 && M <= 64) ? 1 : 2;
   // the [Kred, r0] weight layout and the re-laid-out copy exist in the
   // rank <= 16 form only, one at a time
-  if ((w_nr || Xt) && (r0 + r1 > 16 || (w_nr && (r1 != 0 || Xt)) || (Xt && (Mp < M || Mp > 32 * grid1(M, 32)))))
+  if ((w_nr || Xt) && (r0 + r1 > 16 || (w_nr && (r1 != 0 || Xt)) || (Xt && (Mp < M || Mp > 16 * nf * grid1(M, 16 * nf)))))
     return hipErrorInvalidValue;
   const int64_t C = Kred / 64;
   const int64_t per = (C + splits - 1) / splits;
@@ -1481,13 +1485,26 @@ hipError_t launch_lora_down(const uint16_t* Z, int64_t M, int64_t Kred, const ui
   float* pp = S > 1 ? part : nullptr;
   int jf = (r0 + r1 + 31) / 32;
   if (r0 + r1 <= 16) {
-    if (w_nr)
-      lora_down16_kernel<true, false><<<grid, 512, 0, st>>>(Z, M, Kred, W0, r0, W1, r1, V0, V1, per, pp, nullptr, 0);
-    else if (Xt)
-      lora_down16_kernel<false, true><<<grid, 512, 0, st>>>(Z, M, Kred, W0, r0, W1, r1, V0, V1, per, pp, Xt, Mp);
-    else
-      lora_down16_kernel<false, false><<<grid, 512, 0, st>>>(Z, M, Kred, W0, r0, W1, r1, V0, V1, per, pp, nullptr,
-                                                             0);
+    const dim3 g16(grid1(M, 16 * nf), (unsigned)S);
+    if (nf == 1) {
+      if (w_nr)
+        lora_down16_kernel<true, false, 1><<<g16, 512, 0, st>>>(Z, M, Kred, W0, r0, W1, r1, V0, V1, per, pp, nullptr,
+                                                                0);
+      else if (Xt)
+        lora_down16_kernel<false, true, 1><<<g16, 512, 0, st>>>(Z, M, Kred, W0, r0, W1, r1, V0, V1, per, pp, Xt, Mp);
+      else
+        lora_down16_kernel<false, false, 1><<<g16, 512, 0, st>>>(Z, M, Kred, W0, r0, W1, r1, V0, V1, per, pp,
+                                                                 nullptr, 0);
+    } else {
+      if (w_nr)
+        lora_down16_kernel<true, false, 2><<<g16, 512, 0, st>>>(Z, M, Kred, W0, r0, W1, r1, V0, V1, per, pp, nullptr,
+                                                                0);
+      else if (Xt)
+        lora_down16_kernel<false, true, 2><<<g16, 512, 0, st>>>(Z, M, Kred, W0, r0, W1, r1, V0, V1, per, pp, Xt, Mp);
+      else
+        lora_down16_kernel<false, false, 2><<<g16, 512, 0, st>>>(Z, M, Kred, W0, r0, W1, r1, V0, V1, per, pp,
+                                                                 nullptr, 0);
+    }
     jf = 0;
   }
   switch (jf) {
