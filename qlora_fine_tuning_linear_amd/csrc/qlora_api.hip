@@ -840,6 +840,10 @@ int qlora_mlp_bwd(const qlora_mlp* P, const void* dY, const void* X, const qlora
   b += w.bwd_tdt;
   uint16_t* wbuf = w.bwd_wbuf ? reinterpret_cast<uint16_t*>(b) : nullptr;
   const bool pair = qplan::use_lora_pair(rg, ru, rd);
+  // T_d^T in bf16 for the dH epilogue's dA_d (bf16-GEMM path): from the
+  // single-pass T + dB finish when it runs, else its own pass
+  const bool tt_in_pair = pair && wbuf && qplan::fuse_dad(rd);
+  const int64_t tt_ld = 8 * qplan::cdiv(M, 8);
 
   // Td = dY B_d
   {
@@ -859,6 +863,10 @@ int qlora_mlp_bwd(const qlora_mlp* P, const void* dY, const void* X, const qlora
     pa.njobs = 1;
     pa.job[0] = PairJob{u16(dY), BdT, S->HA_d, rd, sd, pair_part, pair_part + (size_t)pa.nb * M * rd, Td,
                         u16m(G->dB_d)};
+    if (tt_in_pair) {  // its finish also writes T_d^T in bf16 for the dH epilogue
+      pa.job[0].Tt = tdt;
+      pa.job[0].tt_ld = tt_ld;
+    }
     QHIP(launch_lora_pair(pa, st));
   } else {
     QHIP(launch_lora_down(u16(dY), M, D, BdT, rd, nullptr, 0, Td, nullptr, qplan::plan_down_splits(M, D, rd),
@@ -887,11 +895,10 @@ int qlora_mlp_bwd(const qlora_mlp* P, const void* dY, const void* X, const qlora
       // dA_d = s_d Td^T H from the epilogue's own G, U (per-token-tile
       // partials), with Td^T in bf16 so that a lane's operand is one load
       if (qplan::fuse_dad(rd)) {
-        const int64_t ld = 8 * qplan::cdiv(M, 8);
-        QHIP(launch_t_bf16_trans(Td, M, rd, ld, tdt, st));
+        if (!tt_in_pair) QHIP(launch_t_bf16_trans(Td, M, rd, tt_ld, tdt, st));
         a.dad_part = grad_part;
         a.dad_tt = tdt;
-        a.dad_tt_ld = ld;
+        a.dad_tt_ld = tt_ld;
       }
       QHIP(traced_gemm_b(MODE_BWD_SWIGLU, a, st));
       if (qplan::fuse_dad(rd))

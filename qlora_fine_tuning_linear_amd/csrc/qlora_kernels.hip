@@ -1340,7 +1340,16 @@ __global__ __launch_bounds__(256) void pair_finish_kernel(PairArgs a) {
     const PairJob& J = a.job[k];
     const int64_t nt = a.M * J.r, ng = a.P * J.r;
     if (i < nt) {
-      J.T[i] = ordered_sum(J.tpart + i, a.nb, nt);
+      const float v = ordered_sum(J.tpart + i, a.nb, nt);
+      J.T[i] = v;
+      if (J.Tt) {
+        const int64_t m = i / J.r;
+        const int j = (int)(i - m * J.r);
+        uint16_t* row = J.Tt + (int64_t)j * J.tt_ld;
+        row[m] = (uint16_t)(pack_bf16x2(v, 0.0f) & 0xFFFFu);
+        if (m == a.M - 1)
+          for (int64_t mm = a.M; mm < J.tt_ld; ++mm) row[mm] = 0;
+      }
       return;
     }
     i -= nt;

@@ -262,6 +262,10 @@ struct PairJob {
   float* gpart;
   float* T;
   uint16_t* dB;
+  // optional: T also as bf16 T^T [r][tt_ld] (tokens past M zero), the dH
+  // epilogue's dA_d operand
+  uint16_t* Tt;
+  int64_t tt_ld;
 };
 struct PairArgs {
   PairJob job[2];
